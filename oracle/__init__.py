@@ -1,0 +1,220 @@
+"""ctypes binding of the CPU oracle (``oracle/dspark_oracle.cpp``).
+
+Test infrastructure only: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``.  The product package never imports
+it.  Arrays are numpy; floating inputs are passed as float32 (bf16 values widen
+to float32 exactly) and widened to double inside the oracle.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dspark_oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+TAG_DRAFT_CHUNK, TAG_DRAFT_ELEM, TAG_ACCEPT = 1, 2, 3
+TAG_RESID_CHUNK, TAG_RESID_ELEM, TAG_BONUS_CHUNK, TAG_BONUS_ELEM = 4, 5, 6, 7
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with g++ (plain IEEE double, no contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
+               "-shared", "-fPIC", _SRC, "-o", _LIB + ".tmp"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = C.CDLL(_LIB)
+        P = C.c_void_p
+        i32, i64, u32, u64, f64 = C.c_int, C.c_int64, C.c_uint32, C.c_uint64, C.c_double
+        L.orc_philox4x32_10.argtypes = [P, P, P]
+        L.orc_stream_word.argtypes = [u64, u64, u32, u32, u32, u32]
+        L.orc_stream_word.restype = u32
+        L.orc_gumbel.argtypes = [u64, u64, u32, u32, u32, u32]
+        L.orc_gumbel.restype = f64
+        L.orc_chunk_width.restype = i64
+        L.orc_cgm.argtypes = [P, i64, u64, u64, u32, u32, u32, u32, P]
+        L.orc_cgm.restype = i64
+        L.orc_cgm_batch.argtypes = [P, i64, u64, u64, u32, u32, u32, i64, u32, P]
+        L.orc_draft_row.argtypes = [i64, i32, f64, P, P, P, C.c_int32, P]
+        L.orc_residual_row.argtypes = [i64, f64, P, P, f64, P]
+        L.orc_residual_row.restype = f64
+        L.orc_draft_markov.argtypes = [i32, i32, i64, i32, f64, u64, u64, P, P, P, P, P, P,
+                                       P, P, P, P]
+        L.orc_draft_markov.restype = i32
+        L.orc_confidence.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P]
+        L.orc_prefix_schedule.argtypes = [i32, i32, P, P, i32, i32, i32, P, P, P, P, P]
+        L.orc_prefix_schedule.restype = i32
+        L.orc_pack.argtypes = [i32, i32, P, P, P, P, P, P, P]
+        L.orc_verify.argtypes = [i32, i32, i64, i32, f64, u64, u64, P, P, P, i32, P, P, P,
+                                 P, P, P, P, P, P, P, P, P, P, P]
+        L.orc_verify.restype = i32
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+
+
+# ------------------------------------------------------------ random stream
+def philox4x32_10(ctr, key):
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib().orc_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def stream_word(seed, rnd, tag, req, k, idx):
+    return int(lib().orc_stream_word(seed, rnd, tag, req, k, idx))
+
+
+def gumbel(seed, rnd, tag, req, k, idx):
+    return float(lib().orc_gumbel(seed, rnd, tag, req, k, idx))
+
+
+def chunk_width():
+    return int(lib().orc_chunk_width())
+
+
+def cgm(score, seed, rnd, tag_chunk, tag_elem, req, k):
+    s = _f64(score)
+    mg = np.zeros(1)
+    j = lib().orc_cgm(_p(s), s.size, seed, rnd, tag_chunk, tag_elem, req, k, _p(mg))
+    return int(j), float(mg[0])
+
+
+def cgm_batch(score, seed, rnd, tag_chunk, tag_elem, req0, count, k):
+    s = _f64(score)
+    out = np.zeros(count, np.int64)
+    lib().orc_cgm_batch(_p(s), s.size, seed, rnd, tag_chunk, tag_elem, req0, count, k, _p(out))
+    return out
+
+
+# ------------------------------------------------------------ distributions
+def draft_row(Uk, W1, W2t, prev, T):
+    Uk = _f32(Uk)
+    rank = 0 if W1 is None else W1.shape[1]
+    p = np.zeros(Uk.size)
+    lib().orc_draft_row(Uk.size, rank, float(T), _p(Uk), _p(_f32(W1)), _p(_f32(W2t)),
+                        int(prev), _p(p))
+    return p
+
+
+def residual_row(t, s, lse_d, T):
+    t = _f32(t)
+    s = _f64(s)
+    q = np.zeros(t.size)
+    tot = lib().orc_residual_row(t.size, float(T), _p(t), _p(s), float(lse_d), _p(q))
+    return q, float(tot)
+
+
+# -------------------------------------------------------------- the stages
+def draft_markov(U, W1, W2t, x0, T, seed=0, rnd=0, req_ids=None, force_x=None):
+    """U [R][gamma][V]; W1, W2t [V][rank] or None; x0 [R]."""
+    U = _f32(U)
+    R, gamma, V = U.shape
+    rank = 0 if W1 is None else int(W1.shape[1])
+    W1c, W2c = _f32(W1), _f32(W2t)
+    x0 = _i32(x0)
+    x = np.zeros((R, gamma + 1), np.int32)
+    lp = np.zeros((R, gamma))
+    lse = np.zeros((R, gamma))
+    mg = np.zeros((R, gamma))
+    rc = lib().orc_draft_markov(R, gamma, V, rank, float(T), seed, rnd, _p(U), _p(W1c),
+                                _p(W2c), _p(x0), _p(_i32(req_ids)), _p(_i32(force_x)),
+                                _p(x), _p(lp), _p(lse), _p(mg))
+    assert rc == 0, rc
+    return x, lp, lse, mg
+
+
+def confidence(h, W1, w, x, sts_T=None):
+    h = _f32(h)
+    R, gamma, d = h.shape
+    rank = 0 if W1 is None else int(W1.shape[1])
+    c = np.zeros((R, gamma), np.float32)
+    z = np.zeros((R, gamma))
+    lib().orc_confidence(R, gamma, d, rank, _p(h), _p(_f32(W1)), _p(_f32(w)),
+                         _p(_f32(sts_T)), _p(_i32(x)), _p(c), _p(z))
+    return c, z
+
+
+def prefix_schedule(c, sps, N_max=None, enabled=True, mode=0):
+    c = _f32(c)
+    R, gamma = c.shape
+    sps = _f64(sps)
+    if N_max is None:
+        N_max = sps.size - 1
+    ell = np.zeros(R, np.int32)
+    a = np.zeros((R, gamma), np.float32)
+    N = np.zeros(1, np.int32)
+    th = np.zeros(1)
+    mg = np.zeros(1)
+    rc = lib().orc_prefix_schedule(R, gamma, _p(c), _p(sps), int(N_max), int(bool(enabled)),
+                                   int(mode), _p(ell), _p(a), _p(N), _p(th), _p(mg))
+    assert rc == 0, rc
+    return ell, a, int(N[0]), float(th[0]), float(mg[0])
+
+
+def pack(rows, lens):
+    rows = _i32(rows)
+    R, width = rows.shape
+    lens = _i32(lens)
+    cu = np.zeros(R + 1, np.int32)
+    flat = np.zeros(R * width, np.int32)
+    mr = np.zeros(R * width, np.int32)
+    mp = np.zeros(R * width, np.int32)
+    N = np.zeros(1, np.int32)
+    lib().orc_pack(R, width, _p(rows), _p(lens), _p(cu), _p(flat), _p(mr), _p(mp), _p(N))
+    return cu, flat, mr, mp, int(N[0])
+
+
+def verify(ell, cu, target, layout, x, logp_d, lse_d, U, W1, W2t, T, seed=0, rnd=0,
+           req_ids=None, force_m=None):
+    ell = _i32(ell)
+    R = ell.size
+    x = _i32(x)
+    gamma = x.shape[1] - 1
+    target = _f32(target)
+    V = target.shape[-1]
+    rank = 0 if W1 is None else int(W1.shape[1])
+    m = np.zeros(R, np.int32)
+    tau = np.zeros(R, np.int32)
+    em = np.zeros((R, gamma + 1), np.int32)
+    na = np.zeros(R, np.int32)
+    lpt = np.zeros((R, gamma))
+    mg = np.zeros(R)
+    rc = lib().orc_verify(R, gamma, V, rank, float(T), seed, rnd, _p(ell), _p(_i32(cu)),
+                          _p(target), int(layout), _p(x), _p(_f64(logp_d)), _p(_f64(lse_d)),
+                          _p(_f32(U)), _p(_f32(W1)), _p(_f32(W2t)), _p(_i32(req_ids)),
+                          _p(_i32(force_m)), _p(m), _p(tau), _p(em), _p(na), _p(lpt), _p(mg))
+    assert rc == 0, rc
+    return m, tau, em, na, lpt, mg
