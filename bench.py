@@ -1,0 +1,260 @@
+"""Benchmark: one DSpark round (draft -> confidence -> schedule -> pack ->
+verify -> pack) on one MI355X at the headline workload, R = 256 requests,
+block size 16, vocabulary 129280, Markov rank 256, hidden 4096, bf16, T = 1,
+scheduler on.
+
+Prints ONE JSON line.  `value` = verified draft tokens per second
+(sum of scheduled lengths ell over the timed rounds / their wall time), inputs
+resident in HBM before the timed region.  The `roofline` object covers the
+dominant kernel (the per-step Markov statistics kernel of the draft), timed
+live with HIP events recorded on the launch stream around each of its
+launches.  `cpu_baseline` is the single-threaded CPU oracle on a bounded
+sample of requests of the same workload, scaled to a full round.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--cpu-sample", type=int, default=4, help="requests in the oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+class HipEvents:
+    """Raw HIP events from the runtime torch already loaded."""
+
+    def __init__(self, n):
+        self.rt = C.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [C.c_void_p]
+        self.ev = (C.c_void_p * n)()
+        for i in range(n):
+            e = C.c_void_p()
+            assert self.rt.hipEventCreate(C.byref(e)) == 0
+            self.ev[i] = e
+        self.n = n
+
+    def array(self, start, count):
+        return C.cast(C.byref(self.ev, start * C.sizeof(C.c_void_p)), C.POINTER(C.c_void_p))
+
+    def elapsed_ms(self, a, b):
+        out = C.c_float()
+        rc = self.rt.hipEventElapsedTime(C.byref(out), self.ev[a], self.ev[b])
+        assert rc == 0, rc
+        return out.value
+
+    def close(self):
+        for i in range(self.n):
+            self.rt.hipEventDestroy(self.ev[i])
+
+
+def algorithmic_bytes(cfg, sum_tau, n_rej, N):
+    """Bytes the round must move (per round): U once, the target rows up to
+    the first rejection (or the bonus row), U rows of rejected positions, h,
+    W2 once and the gathered W1 rows, w, and the outputs."""
+    sU = sT = sh = sW = sw = 2 if cfg.dtype.itemsize == 2 else 4
+    R, G, V, r, d = cfg.R, cfg.gamma, cfg.V, cfg.rank, cfg.d
+    return (sU * R * G * V + sT * V * sum_tau + sU * V * n_rej + sh * R * G * d
+            + sW * (r * V + R * G * r) + sw * (d + r) + R * G * 16 + N * 12)
+
+
+def stats_kernel_bytes(cfg):
+    """Algorithmic bytes of one launch of the draft statistics kernel: one U_k
+    slab, the gathered W1 rows, the chunk statistics written, and W2 once per
+    round amortised over the gamma launches."""
+    s = cfg.dtype.itemsize
+    nch = (cfg.V + 127) // 128
+    return (s * cfg.R * cfg.V + s * cfg.R * cfg.rank + 4 * cfg.R * nch
+            + (s * cfg.rank * cfg.V) / cfg.gamma)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the round shards by requests; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import draft_verify_sampling_head_amd as D
+    from draft_verify_sampling_head_amd import _lib as L
+    from draft_verify_sampling_head_amd import round as RD
+    from draft_verify_sampling_head_amd import synth
+
+    dev = torch.device("cuda:0")
+    cfg = synth.config(args.config)
+    t0 = time.time()
+    inp = synth.make_inputs(cfg, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] config {args.config} ({cfg.name}) inputs ready in {time.time() - t0:.1f}s")
+    K, W = args.steps, args.warmup
+    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=dev)
+    ells = torch.empty(K + W, cfg.R, dtype=torch.int32, device=dev)
+    ms = torch.empty(K + W, cfg.R, dtype=torch.int32, device=dev)
+    Ns = torch.empty(K + W, dtype=torch.int32, device=dev)
+    Nouts = torch.empty(K + W, dtype=torch.int32, device=dev)
+    ev = HipEvents(2 * cfg.gamma * K)
+    stream = torch.cuda.current_stream()
+
+    def one_round(i, timed):
+        buf.ell, buf.m = ells[i], ms[i]
+        buf.N, buf.N_out = Ns[i:i + 1], Nouts[i:i + 1]
+        if timed:
+            j = (i - W) * 2 * cfg.gamma
+            L.draft_markov_profiled(inp["U"], inp["W1"], inp["W2t"], inp["x0"], cfg.T,
+                                    cfg.philox_seed, i, buf.x, buf.logp_d, buf.lse_d, buf.ws,
+                                    ev.array(j, cfg.gamma), ev.array(j + cfg.gamma, cfg.gamma))
+        else:
+            L.draft_markov(inp["U"], inp["W1"], inp["W2t"], inp["x0"], cfg.T, cfg.philox_seed, i,
+                           buf.x, buf.logp_d, buf.lse_d, buf.ws)
+        L.confidence(inp["h"], inp["W1"], inp["w"], buf.x, buf.c, V=cfg.V)
+        L.prefix_schedule(buf.c, inp["sps"], buf.ell, enabled=cfg.scheduler, a=buf.a, N_out=buf.N,
+                          theta_best=buf.theta)
+        L.pack(buf.x, buf.ell, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N,
+               ws=buf.ws)
+        L.verify(buf.ell, buf.cu, inp["target"], 1, buf.x, buf.logp_d, buf.lse_d, inp["U"],
+                 inp["W1"], inp["W2t"], cfg.T, cfg.philox_seed, i, buf.m, buf.tau, buf.emitted,
+                 buf.next_anchor, buf.ws, logp_t=buf.logp_t)
+        L.pack(buf.emitted, buf.tau, 0, buf.cu_out, buf.flat_out, N_out=buf.N_out, ws=buf.ws)
+
+    for i in range(W):
+        one_round(i, False)
+    torch.cuda.synchronize()
+    log(f"[bench] {W} warmup rounds done")
+    t_start = time.perf_counter()
+    for i in range(W, W + K):
+        one_round(i, True)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    status = D.get_status(buf.ws)
+    ms_per_step = 1e3 * t_total / K
+
+    ell_t = ells[W:].cpu().numpy().astype(np.int64)
+    m_t = ms[W:].cpu().numpy().astype(np.int64)
+    sum_ell = int(ell_t.sum())
+    sum_tau = int((m_t + 1).sum())
+    n_rej = int((m_t < ell_t).sum()) if cfg.T > 0 else 0
+    N_avg = float(Ns[W:].cpu().numpy().mean())
+    value = sum_ell / t_total
+    bytes_round = sum(algorithmic_bytes(cfg, int((m_t[i] + 1).sum()), int((m_t[i] < ell_t[i]).sum()),
+                                        int(Ns[W + i].item())) for i in range(K)) / K
+    hbm_frac_round = bytes_round / (t_total / K) / (HBM_PEAK_GBS * 1e9)
+
+    # dominant kernel: per-step draft statistics, events on the launch stream
+    durs = []
+    for i in range(K):
+        j = i * 2 * cfg.gamma
+        for k in range(cfg.gamma):
+            durs.append(ev.elapsed_ms(j + k, j + cfg.gamma + k))
+    ev.close()
+    avg_ms = float(np.mean(durs))
+    kb = stats_kernel_bytes(cfg)
+    achieved = kb / (avg_ms * 1e-3) / 1e9
+    kflops = 2.0 * cfg.R * cfg.rank * cfg.V
+    mfma_tf = kflops / (avg_ms * 1e-3) / 1e12
+    log(f"[bench] {K} rounds: {ms_per_step:.3f} ms/round, sum_ell={sum_ell}, sum_tau={sum_tau}, "
+        f"N_avg={N_avg:.1f}, n_rej={n_rej}, stats kernel {avg_ms * 1e3:.1f} us "
+        f"({achieved:.0f} GB/s, {mfma_tf:.0f} TFLOP/s), round HBM frac {hbm_frac_round:.3f}, "
+        f"status={status}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, inp, buf, args.cpu_sample, sum_ell / K, torch, np)
+    out = {
+        "metric": "verified draft tokens/s per round (B=256,γ=16,V=129280) + % peak HBM",
+        "value": value,
+        "unit": "verified draft tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"dspark-round config {args.config} ({cfg.name})", "R": cfg.R,
+                   "gamma": cfg.gamma, "V": cfg.V, "rank": cfg.rank, "d": cfg.d, "T": cfg.T,
+                   "scheduler": cfg.scheduler, "parallelism": "single-gpu"},
+        "hbm_frac_round": hbm_frac_round,
+        "round_bytes_alg": bytes_round,
+        "emitted_tokens_per_s": sum_tau / t_total,
+        "mean_ell": sum_ell / (K * cfg.R),
+        "mean_tau": sum_tau / (K * cfg.R),
+        "device_status": status,
+        "roofline": {"bound": "hbm", "kernel": "k_markov_mfma (draft statistics, per step)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "avg_launch_us": avg_ms * 1e3, "bytes_per_launch": kb,
+                     "mfma_tflops": mfma_tf, "mfma_frac": mfma_tf / MFMA_BF16_PEAK_TFLOPS},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, inp, buf, n_req, ell_per_round, torch, np):
+    """The oracle as it stands, on a bounded sample: draft + confidence +
+    verify for n_req requests, the scheduler and both packs on the full batch;
+    the per-request part is scaled to all R requests."""
+    import oracle as O
+    reqs = np.linspace(0, cfg.R - 1, n_req).round().astype(np.int32)
+    sel = torch.as_tensor(reqs, device=inp["U"].device).long()
+    f = lambda t: t.float().cpu().numpy()
+    U, tgt, h = f(inp["U"][sel]), f(inp["target"][sel]), f(inp["h"][sel])
+    W1, W2t, w = f(inp["W1"]), f(inp["W2t"]), f(inp["w"])
+    x0 = inp["x0"][sel].cpu().numpy()
+    sps = inp["sps"].cpu().numpy()
+    c_all = buf.c.cpu().numpy()
+    x_all = buf.x.cpu().numpy()
+    t0 = time.perf_counter()
+    x, lp, lse, _ = O.draft_markov(U, W1, W2t, x0, cfg.T, cfg.philox_seed, 0, req_ids=reqs)
+    c, _ = O.confidence(h, W1, w, x)
+    t1 = time.perf_counter()
+    c_all = c_all.copy()
+    c_all[reqs] = c
+    ell, _, N, _, _ = O.prefix_schedule(c_all, sps, enabled=cfg.scheduler)
+    O.pack(x_all, ell + 1)
+    t2 = time.perf_counter()
+    O.verify(ell[reqs], None, tgt, 1, x, lp, lse, U, W1, W2t, cfg.T, cfg.philox_seed, 0,
+             req_ids=reqs)
+    t3 = time.perf_counter()
+    O.pack(x_all, ell + 1)
+    t4 = time.perf_counter()
+    per_req = ((t1 - t0) + (t3 - t2)) / n_req
+    t_round = per_req * cfg.R + (t2 - t1) + (t4 - t3)
+    log(f"[bench] oracle: {per_req:.2f} s/request (draft+conf+verify), schedule+pack "
+        f"{(t2 - t1) + (t4 - t3):.3f} s, est. round {t_round:.1f} s")
+    return {"value": ell_per_round / t_round, "unit": "verified draft tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n_req} of {cfg.R} requests (draft+confidence+verify, {t3 - t0:.1f} s of "
+                      f"CPU) scaled to {cfg.R}; scheduler and packs on the full batch; tokens per "
+                      f"round = the GPU rounds' mean sum of ell ({ell_per_round:.1f})",
+            "est_round_s": t_round}
+
+
+if __name__ == "__main__":
+    main()

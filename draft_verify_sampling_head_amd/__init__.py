@@ -1,0 +1,16 @@
+"""MI355X-native hot path of one DSpark speculative-decoding round.
+
+The compute lives in libdspark.so (hand-written HIP kernels for gfx950, C ABI
+in include/dspark.h).  This package is its binding: `_lib` marshals arguments
+to the C entry points, `round` enqueues a whole round, `synth` draws seeded
+synthetic inputs.  Importing the package loads the library and fails if it is
+missing; there is no other execution path.
+"""
+from . import _lib
+from ._lib import (DsparkError, confidence, draft_markov, get_status, clear_status, pack,
+                   prefix_schedule, verify, workspace, workspace_bytes)
+
+_lib.load()
+
+__all__ = ["DsparkError", "confidence", "draft_markov", "get_status", "clear_status", "pack",
+           "prefix_schedule", "verify", "workspace", "workspace_bytes"]

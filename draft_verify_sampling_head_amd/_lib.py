@@ -1,0 +1,181 @@
+"""ctypes binding of libdspark.so: argument marshalling only.
+
+Each function takes torch tensors that already live on the GPU, passes their
+device pointers, sizes and dtype codes to the C entry point of the same name
+and raises on a non-OK status.  Every step of the round runs in the library's
+HIP kernels; nothing here computes.  There is no fallback: if the library is
+missing or fails to load, the import raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdspark.so")
+
+F32, BF16 = 0, 1
+STATUS = {0: "DSPARK_OK", 1: "DSPARK_E_INVALID", 2: "DSPARK_E_UNSUPPORTED",
+          3: "DSPARK_E_WORKSPACE", 4: "DSPARK_E_HIP"}
+FLAG_NONFINITE, FLAG_BAD_LEN, FLAG_BAD_TOKEN = 1, 2, 4
+CHUNK = 128
+EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
+           "dspark_clear_status", "dspark_get_status", "dspark_draft_markov",
+           "dspark_confidence", "dspark_prefix_schedule", "dspark_pack", "dspark_verify",
+           "dspark_draft_markov_profiled")
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} returned {STATUS.get(code, code)}")
+        self.code = code
+
+
+_lib = None
+
+
+def load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "or `python draft_verify_sampling_head_amd/build.py`")
+    L = C.CDLL(LIB_PATH)
+    P, i32, u64, f32, sz = C.c_void_p, C.c_int, C.c_uint64, C.c_float, C.c_size_t
+    L.dspark_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.dspark_workspace_bytes.restype = sz
+    L.dspark_status_string.argtypes = [i32]
+    L.dspark_status_string.restype = C.c_char_p
+    L.dspark_version.restype = C.c_char_p
+    L.dspark_clear_status.argtypes = [P, sz, P]
+    L.dspark_get_status.argtypes = [P, sz, P]
+    L.dspark_draft_markov.argtypes = [i32, i32, i32, i32, f32, u64, u64, P, i32, P, P, i32, P, P,
+                                      P, P, P, P, sz, P]
+    L.dspark_draft_markov_profiled.argtypes = L.dspark_draft_markov.argtypes + [P, P]
+    L.dspark_confidence.argtypes = [i32, i32, i32, i32, i32, P, i32, P, i32, P, i32, P, P, P, P]
+    L.dspark_prefix_schedule.argtypes = [i32, i32, P, P, i32, i32, P, P, P, P, P]
+    L.dspark_pack.argtypes = [i32, i32, P, P, i32, P, P, P, P, P, P, sz, P]
+    L.dspark_verify.argtypes = [i32, i32, i32, i32, f32, u64, u64, P, P, P, i32, i32, P, P, P, P,
+                                i32, P, P, i32, P, P, P, P, P, P, sz, P]
+    for fn in EXPORTS:
+        getattr(L, fn).restype = getattr(L, fn).restype or i32
+    L.dspark_workspace_bytes.restype = sz
+    L.dspark_status_string.restype = C.c_char_p
+    L.dspark_version.restype = C.c_char_p
+    _lib = L
+    return L
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _dt(t):
+    if t is None:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _check(fn, code):
+    if code != 0:
+        raise DsparkError(fn, code)
+
+
+def workspace_bytes(R, gamma, V, r=0, d=0):
+    return int(load().dspark_workspace_bytes(R, gamma, V, r, d))
+
+
+def workspace(R, gamma, V, device="cuda"):
+    """Allocate a workspace tensor (uint8) of the size the library asks for."""
+    return torch.empty(max(256, workspace_bytes(R, gamma, V)), dtype=torch.uint8, device=device)
+
+
+def version():
+    return load().dspark_version().decode()
+
+
+def clear_status(ws, stream=None):
+    _check("dspark_clear_status", load().dspark_clear_status(_ptr(ws), ws.numel(), _stream(stream)))
+
+
+def get_status(ws):
+    out = C.c_uint32(0)
+    _check("dspark_get_status", load().dspark_get_status(_ptr(ws), ws.numel(), C.byref(out)))
+    return int(out.value)
+
+
+def draft_markov(U, W1, W2t, x0, T, seed, rnd, x, logp_d, lse_d, ws, margin=None, stream=None):
+    R, gamma, V = U.shape
+    r = 0 if W1 is None else int(W1.shape[1])
+    code = load().dspark_draft_markov(R, gamma, V, r, float(T), seed, rnd, _ptr(U), _dt(U),
+                                      _ptr(W1), _ptr(W2t), _dt(W1), _ptr(x0), _ptr(x),
+                                      _ptr(logp_d), _ptr(lse_d), _ptr(margin), _ptr(ws),
+                                      ws.numel(), _stream(stream))
+    _check("dspark_draft_markov", code)
+
+
+def draft_markov_profiled(U, W1, W2t, x0, T, seed, rnd, x, logp_d, lse_d, ws, ev_begin, ev_end,
+                          margin=None, stream=None):
+    """As draft_markov, recording the caller's HIP events (ctypes arrays of
+    gamma hipEvent_t each) around every step's statistics kernel."""
+    R, gamma, V = U.shape
+    r = 0 if W1 is None else int(W1.shape[1])
+    code = load().dspark_draft_markov_profiled(R, gamma, V, r, float(T), seed, rnd, _ptr(U), _dt(U),
+                                               _ptr(W1), _ptr(W2t), _dt(W1), _ptr(x0), _ptr(x),
+                                               _ptr(logp_d), _ptr(lse_d), _ptr(margin), _ptr(ws),
+                                               ws.numel(), _stream(stream), ev_begin, ev_end)
+    _check("dspark_draft_markov_profiled", code)
+
+
+def confidence(h, W1, w, x, c, sts_T=None, V=None, stream=None):
+    R, gamma, d = h.shape
+    r = 0 if W1 is None else int(W1.shape[1])
+    V = int(W1.shape[0]) if (V is None and W1 is not None) else (V or 0)
+    code = load().dspark_confidence(R, gamma, d, r, V, _ptr(h), _dt(h), _ptr(W1), _dt(W1), _ptr(w),
+                                    _dt(w), _ptr(sts_T), _ptr(x), _ptr(c), _stream(stream))
+    _check("dspark_confidence", code)
+
+
+def prefix_schedule(c, sps, ell, enabled=True, N_max=None, a=None, N_out=None, theta_best=None,
+                    stream=None):
+    R, gamma = c.shape
+    N_max = sps.numel() - 1 if N_max is None else N_max
+    code = load().dspark_prefix_schedule(R, gamma, _ptr(c), _ptr(sps), int(N_max), int(bool(enabled)),
+                                         _ptr(ell), _ptr(a), _ptr(N_out), _ptr(theta_best),
+                                         _stream(stream))
+    _check("dspark_prefix_schedule", code)
+
+
+def pack(rows, lens, len_offset, cu, flat, marker_req=None, marker_pos=None, N_out=None, ws=None,
+         stream=None):
+    R, width = rows.shape
+    code = load().dspark_pack(R, width, _ptr(rows), _ptr(lens), int(len_offset), _ptr(cu), _ptr(flat),
+                              _ptr(marker_req), _ptr(marker_pos), _ptr(N_out), _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream(stream))
+    _check("dspark_pack", code)
+
+
+def verify(ell, cu, target, layout, x, logp_d, lse_d, U, W1, W2t, T, seed, rnd, m, tau, emitted,
+           next_anchor, ws, logp_t=None, stream=None):
+    R = ell.shape[0]
+    gamma = x.shape[1] - 1
+    V = target.shape[-1]
+    r = 0 if W1 is None else int(W1.shape[1])
+    code = load().dspark_verify(R, gamma, V, r, float(T), seed, rnd, _ptr(ell), _ptr(cu),
+                                _ptr(target), _dt(target), int(layout), _ptr(x), _ptr(logp_d),
+                                _ptr(lse_d), _ptr(U), _dt(U), _ptr(W1), _ptr(W2t), _dt(W1),
+                                _ptr(m), _ptr(tau), _ptr(emitted), _ptr(next_anchor),
+                                _ptr(logp_t), _ptr(ws), ws.numel(), _stream(stream))
+    _check("dspark_verify", code)

@@ -1,0 +1,198 @@
+// api.hip -- the C ABI of libdspark.so (declared in include/dspark.h).
+// Host-side argument checks, workspace sizing, then kernel enqueues.  No call
+// allocates, frees or synchronises (dspark_get_status aside, which reads the
+// status word with a blocking copy by design).
+#include "dspark.h"
+
+#include <cmath>
+
+#include "launch.hpp"
+#include "workspace.hpp"
+
+using namespace dspark;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool dtype_ok(dspark_dtype t) { return t == DSPARK_F32 || t == DSPARK_BF16; }
+
+dspark_status rank_check(int r) {
+  if (r < 0) return DSPARK_E_INVALID;
+  if (r > 512 || (r % 16) != 0) return DSPARK_E_UNSUPPORTED;
+  return DSPARK_OK;
+}
+
+dspark_status shape_check(int R, int gamma, int V) {
+  if (R < 0 || gamma < 1 || V < 1) return DSPARK_E_INVALID;
+  if (gamma > 32) return DSPARK_E_UNSUPPORTED;
+  return DSPARK_OK;
+}
+
+dspark_status hip_status(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_E_HIP; }
+
+__global__ void k_store_u32(uint32_t* p, uint32_t v) {
+  if (threadIdx.x == 0) *p = v;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dspark_workspace_bytes(int R, int gamma, int V, int r, int d) {
+  (void)r;
+  (void)d;
+  if (R < 0 || gamma < 1 || V < 1) return 0;
+  return ws_layout(R, gamma, V).total;
+}
+
+const char* dspark_status_string(dspark_status s) {
+  switch (s) {
+    case DSPARK_OK: return "DSPARK_OK";
+    case DSPARK_E_INVALID: return "DSPARK_E_INVALID";
+    case DSPARK_E_UNSUPPORTED: return "DSPARK_E_UNSUPPORTED";
+    case DSPARK_E_WORKSPACE: return "DSPARK_E_WORKSPACE";
+    case DSPARK_E_HIP: return "DSPARK_E_HIP";
+  }
+  return "DSPARK_E_UNKNOWN";
+}
+
+const char* dspark_version(void) { return "dspark-mi355x 0.1 (gfx950)"; }
+
+dspark_status dspark_clear_status(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws || ws_bytes < 256 || !aligned16(ws)) return DSPARK_E_INVALID;
+  hipLaunchKernelGGL(k_store_u32, dim3(1), dim3(64), 0, stream, reinterpret_cast<uint32_t*>(ws), 0u);
+  return hip_status(hipGetLastError());
+}
+
+dspark_status dspark_get_status(const void* ws, size_t ws_bytes, uint32_t* flags) {
+  if (!ws || !flags || ws_bytes < 256) return DSPARK_E_INVALID;
+  return hip_status(hipMemcpy(flags, ws, sizeof(uint32_t), hipMemcpyDeviceToHost));
+}
+
+static dspark_status draft_impl(int R, int gamma, int V, int r, float T, uint64_t seed,
+                                uint64_t round, const void* U, dspark_dtype U_dt, const void* W1,
+                                const void* W2t, dspark_dtype W_dt, const int32_t* x0, int32_t* x,
+                                float* logp_d, float* lse_d, float* margin, void* ws,
+                                size_t ws_bytes, hipStream_t stream, hipEvent_t* ev_begin,
+                                hipEvent_t* ev_end) {
+  dspark_status s = shape_check(R, gamma, V);
+  if (s != DSPARK_OK) return s;
+  if ((s = rank_check(r)) != DSPARK_OK) return s;
+  if (!(T >= 0.f) || !std::isfinite(T)) return DSPARK_E_INVALID;
+  if (!dtype_ok(U_dt) || !dtype_ok(W_dt)) return DSPARK_E_INVALID;
+  if (R == 0) return DSPARK_OK;
+  if (!U || !x0 || !x || !logp_d || !lse_d || !ws) return DSPARK_E_INVALID;
+  if (r > 0 && (!W1 || !W2t)) return DSPARK_E_INVALID;
+  if (r > 0 && (!aligned16(W1) || !aligned16(W2t))) return DSPARK_E_UNSUPPORTED;
+  if (!aligned16(ws)) return DSPARK_E_INVALID;
+  if (ws_bytes < ws_layout(R, gamma, V).total) return DSPARK_E_WORKSPACE;
+  return hip_status(launch_draft(R, gamma, V, r, T, seed, round, U, U_dt == DSPARK_BF16, W1, W2t,
+                                 W_dt == DSPARK_BF16, x0, x, logp_d, lse_d, margin, ws, stream,
+                                 ev_begin, ev_end));
+}
+
+dspark_status dspark_draft_markov(int R, int gamma, int V, int r, float T, uint64_t seed,
+                                  uint64_t round, const void* U, dspark_dtype U_dt, const void* W1,
+                                  const void* W2t, dspark_dtype W_dt, const int32_t* x0,
+                                  int32_t* x, float* logp_d, float* lse_d, float* margin, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  return draft_impl(R, gamma, V, r, T, seed, round, U, U_dt, W1, W2t, W_dt, x0, x, logp_d, lse_d,
+                    margin, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+dspark_status dspark_draft_markov_profiled(int R, int gamma, int V, int r, float T, uint64_t seed,
+                                           uint64_t round, const void* U, dspark_dtype U_dt,
+                                           const void* W1, const void* W2t, dspark_dtype W_dt,
+                                           const int32_t* x0, int32_t* x, float* logp_d,
+                                           float* lse_d, float* margin, void* ws, size_t ws_bytes,
+                                           hipStream_t stream, hipEvent_t* ev_begin,
+                                           hipEvent_t* ev_end) {
+  if (!ev_begin || !ev_end) return DSPARK_E_INVALID;
+  return draft_impl(R, gamma, V, r, T, seed, round, U, U_dt, W1, W2t, W_dt, x0, x, logp_d, lse_d,
+                    margin, ws, ws_bytes, stream, ev_begin, ev_end);
+}
+
+dspark_status dspark_confidence(int R, int gamma, int d, int r, int V, const void* h,
+                                dspark_dtype h_dt, const void* W1, dspark_dtype W_dt,
+                                const void* w, dspark_dtype w_dt, const float* sts_T,
+                                const int32_t* x, float* c, hipStream_t stream) {
+  if (R < 0 || gamma < 1 || d < 1) return DSPARK_E_INVALID;
+  if (gamma > 32) return DSPARK_E_UNSUPPORTED;
+  dspark_status s = rank_check(r);
+  if (s != DSPARK_OK) return s;
+  if (!dtype_ok(h_dt) || !dtype_ok(W_dt) || !dtype_ok(w_dt)) return DSPARK_E_INVALID;
+  if (R == 0) return DSPARK_OK;
+  if (!h || !w || !x || !c) return DSPARK_E_INVALID;
+  if (r > 0 && (!W1 || V < 1)) return DSPARK_E_INVALID;
+  ConfArgs a{};
+  a.R = R; a.gamma = gamma; a.d = d; a.rank = r; a.V = V; a.h = h; a.W1 = W1; a.w = w;
+  a.sts = sts_T; a.x = x; a.c = c; a.status = nullptr;
+  const size_t hs = h_dt == DSPARK_BF16 ? 2 : 4, ws_ = w_dt == DSPARK_BF16 ? 2 : 4;
+  const size_t es = W_dt == DSPARK_BF16 ? 2 : 4;
+  a.vec_h = aligned16(h) && aligned16(w) && ((size_t)d * hs) % 16 == 0 && hs == ws_;
+  a.vec_e = r > 0 && aligned16(W1) && aligned16(reinterpret_cast<const char*>(w) + (size_t)d * ws_) &&
+            ((size_t)r * es) % 16 == 0 && es == ws_;
+  return hip_status(launch_confidence(a, h_dt == DSPARK_BF16, W_dt == DSPARK_BF16,
+                                      w_dt == DSPARK_BF16, stream));
+}
+
+dspark_status dspark_prefix_schedule(int R, int gamma, const float* c, const double* sps,
+                                     int N_max, int enabled, int32_t* ell, float* a,
+                                     int32_t* N_out, double* theta_best, hipStream_t stream) {
+  if (R < 0 || gamma < 1) return DSPARK_E_INVALID;
+  if (gamma > 32) return DSPARK_E_UNSUPPORTED;
+  if (R == 0) return DSPARK_OK;
+  if (!c || !sps || !ell) return DSPARK_E_INVALID;
+  if (N_max < R) return DSPARK_E_INVALID;
+  if ((int64_t)R * gamma > 16384) return DSPARK_E_UNSUPPORTED;
+  SchedArgs sa{};
+  sa.R = R; sa.gamma = gamma; sa.N_max = N_max; sa.enabled = enabled ? 1 : 0;
+  sa.c = c; sa.sps = sps; sa.ell = ell; sa.a = a; sa.N_out = N_out; sa.theta = theta_best;
+  return hip_status(launch_schedule(sa, stream));
+}
+
+dspark_status dspark_pack(int R, int width, const int32_t* rows, const int32_t* len,
+                          int len_offset, int32_t* cu, int32_t* flat, int32_t* marker_req,
+                          int32_t* marker_pos, int32_t* N_out, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (R < 0 || width < 1) return DSPARK_E_INVALID;
+  if (R == 0) return DSPARK_OK;
+  if (!rows || !len || !cu || !flat) return DSPARK_E_INVALID;
+  if ((int64_t)R * width >= ((int64_t)1 << 31)) return DSPARK_E_UNSUPPORTED;
+  if (ws && (ws_bytes < 256 || !aligned16(ws))) return DSPARK_E_WORKSPACE;
+  PackArgs p{};
+  p.R = R; p.width = width; p.len_offset = len_offset; p.rows = rows; p.len = len; p.cu = cu;
+  p.flat = flat; p.marker_req = marker_req; p.marker_pos = marker_pos; p.N_out = N_out;
+  p.status = reinterpret_cast<uint32_t*>(ws);
+  return hip_status(launch_pack(p, stream));
+}
+
+dspark_status dspark_verify(int R, int gamma, int V, int r, float T, uint64_t seed, uint64_t round,
+                            const int32_t* ell, const int32_t* cu, const void* target,
+                            dspark_dtype t_dt, int target_layout, const int32_t* x,
+                            const float* logp_d, const float* lse_d, const void* U,
+                            dspark_dtype U_dt, const void* W1, const void* W2t, dspark_dtype W_dt,
+                            int32_t* m, int32_t* tau, int32_t* emitted, int32_t* next_anchor,
+                            float* logp_t, void* ws, size_t ws_bytes, hipStream_t stream) {
+  dspark_status s = shape_check(R, gamma, V);
+  if (s != DSPARK_OK) return s;
+  if ((s = rank_check(r)) != DSPARK_OK) return s;
+  if (!(T >= 0.f) || !std::isfinite(T)) return DSPARK_E_INVALID;
+  if (!dtype_ok(t_dt) || !dtype_ok(U_dt) || !dtype_ok(W_dt)) return DSPARK_E_INVALID;
+  if (target_layout != 0 && target_layout != 1) return DSPARK_E_INVALID;
+  if (R == 0) return DSPARK_OK;
+  if (t_dt != U_dt) return DSPARK_E_UNSUPPORTED;
+  if (!ell || !cu || !target || !x || !m || !tau || !emitted || !next_anchor || !ws)
+    return DSPARK_E_INVALID;
+  if (T > 0.f && (!logp_d || !lse_d || !U)) return DSPARK_E_INVALID;
+  if (T > 0.f && r > 0 && (!W1 || !W2t)) return DSPARK_E_INVALID;
+  if (r > 0 && T > 0.f && (!aligned16(W1) || !aligned16(W2t))) return DSPARK_E_UNSUPPORTED;
+  if (!aligned16(ws)) return DSPARK_E_INVALID;
+  if (ws_bytes < ws_layout(R, gamma, V).total) return DSPARK_E_WORKSPACE;
+  return hip_status(launch_verify(R, gamma, V, r, T, seed, round, ell, cu, target, target_layout,
+                                  x, logp_d, lse_d, U, U_dt == DSPARK_BF16, W1, W2t,
+                                  W_dt == DSPARK_BF16, m, tau, emitted, next_anchor, logp_t, ws,
+                                  stream));
+}
+
+}  // extern "C"

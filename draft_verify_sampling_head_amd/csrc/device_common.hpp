@@ -1,0 +1,159 @@
+// device_common.hpp -- device helpers shared by the libdspark kernels (gfx950).
+//
+// Random stream: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11, "Parallel
+// Random Numbers: As Easy as 1, 2, 3"): ten rounds of two 32x32->64 products
+// whose halves are cross-xored with the other counter words and the round key,
+// the key bumped by the two Weyl constants between rounds.  Key = the 64-bit
+// seed, counter = (idx/4, k | tag<<16, request, lo32 round), word = idx % 4.
+// A word y maps to u = (y + 1/2) 2^-32 and to a standard Gumbel -log(-log u);
+// for u > 1/2 the inner log is taken as log1p(-(1-u)) with 1-u = (~y + 1/2) 2^-32,
+// which keeps full float precision where u rounds towards 1.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+constexpr int kChunk = 128;        // vocabulary entries per Gumbel chunk
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
+
+enum : uint32_t {
+  kTagDraftChunk = 1, kTagDraftElem = 2, kTagAccept = 3,
+  kTagResidChunk = 4, kTagResidElem = 5, kTagBonusChunk = 6, kTagBonusElem = 7
+};
+
+enum : uint32_t { kFlagNonFinite = 1u, kFlagBadLen = 2u, kFlagBadToken = 4u };
+
+// ------------------------------------------------------------------ Philox
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// The four words of counter block idx4 (= idx / 4) of one stream.
+__device__ __forceinline__ uint4 stream_block(uint64_t seed, uint64_t round, uint32_t tag,
+                                              uint32_t req, uint32_t k, uint32_t idx4) {
+  return philox4x32_10(make_uint4(idx4, k | (tag << 16), req, (uint32_t)round),
+                       (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+__device__ __forceinline__ uint32_t word_of(uint4 b, uint32_t lane4) {
+  return lane4 == 0 ? b.x : lane4 == 1 ? b.y : lane4 == 2 ? b.z : b.w;
+}
+
+// log(u) for u = (y + 1/2) 2^-32, accurate for every word y.
+__device__ __forceinline__ float log_uniform(uint32_t y) {
+  if (y < 0x80000000u) {
+    return logf(fmaf((float)y, 0x1p-32f, 0x1p-33f));
+  }
+  return log1pf(-fmaf((float)(~y), 0x1p-32f, 0x1p-33f));
+}
+
+__device__ __forceinline__ float gumbel_of(uint32_t y) { return -logf(-log_uniform(y)); }
+
+// ------------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_at(const uint16_t* p, int64_t i) {
+  return __uint_as_float(((uint32_t)p[i]) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float get(const float* p, int64_t i) { return p[i]; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float get(const uint16_t* p, int64_t i) { return bf16_at(p, i); }
+};
+
+// ------------------------------------------------------------ reductions
+// DPP moves inside a row of 16 lanes (quad_perm xor1 / xor2, half-mirror,
+// mirror): four steps leave every lane of the row with the row's result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return v;
+}
+// (value, index) max with the lower index winning ties.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float vo, int io) {
+  if (vo > v || (vo == v && io < i)) { v = vo; i = io; }
+}
+template <int CTRL>
+__device__ __forceinline__ void row16_argmax_step(float& v, int& i) {
+  const float vo = dpp_f<CTRL>(v);
+  const int io = dpp_i<CTRL>(i);
+  argmax_merge(v, i, vo, io);
+}
+__device__ __forceinline__ void row16_argmax(float& v, int& i) {
+  row16_argmax_step<kDppXor1>(v, i);
+  row16_argmax_step<kDppXor2>(v, i);
+  row16_argmax_step<kDppHalfMirror>(v, i);
+  row16_argmax_step<kDppMirror>(v, i);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float vo = __shfl_xor(v, o);
+    const int io = __shfl_xor(i, o);
+    argmax_merge(v, i, vo, io);
+  }
+}
+
+// ln(sum exp) combine of (max, sum-of-exp2-relative-to-max) pairs in log2 units.
+__device__ __forceinline__ void lse2_merge(float& m, float& s, float mo, float so) {
+  const float mn = fmaxf(m, mo);
+  if (mn == -INFINITY) return;
+  s = s * exp2f(m - mn) + so * exp2f(mo - mn);
+  m = mn;
+}
+
+__device__ __forceinline__ void set_flag(uint32_t* status, uint32_t f) {
+  if (status) atomicOr(status, f);
+}
+
+}  // namespace dspark

@@ -1,0 +1,110 @@
+// launch.hpp -- internal host/device interface between the C ABI and kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace dspark {
+
+enum { kRowsDraft = 0, kRowsVerifyPacked = 1, kRowsVerifyDense = 2 };
+enum { kModeSample = 0, kModeGreedy = 1, kModeResid = 2 };
+
+// Streaming per-chunk statistics of rows with no bias.
+struct RowStatsArgs {
+  const void* base;        // U (draft) or target (verify)
+  int kind;                // kRows*
+  int R, gamma, k, V, nch;
+  const int32_t* cu;       // verify: offsets; N = cu[R]
+  int nrows_cap;           // draft: R; verify: R*(gamma+1)
+  float scale2;            // log2(e) / T (sampling) -- unused for greedy
+  bool vec_ok;             // rows are 16-byte aligned
+  float* L;                // [row][nch] log-masses (sample) or maxima (greedy)
+  float* M;
+  int* I;                  // [row][nch] argmax (greedy)
+  uint32_t* status;
+  uint32_t* zero_me;       // nullable: cleared by the first thread (work counter)
+  int segs, cps;           // filled by the launcher
+};
+
+// Per-chunk statistics of rows carrying the Markov bias (draft or residual).
+struct MarkovArgs {
+  int R, gamma, k, V, rank, nch, nrows_cap;
+  const void* U;
+  const void* W1v;
+  const void* W2tv;
+  const uint16_t* W1;      // bf16 views (MFMA path)
+  const uint16_t* W2t;
+  const int32_t* x0;       // draft anchors
+  const int32_t* x;        // [R][gamma+1]
+  float scale2;
+  bool u_vec_ok;
+  float* L;
+  float* M;
+  int* I;
+  // residual rows
+  const int32_t* rej_count;
+  const int4* rej;         // (request, position k, target row, -)
+  const void* target;
+  const float* lse_t;
+  const float* lse_d;
+  uint32_t* status;
+  // filled by the launcher
+  int cg, nrt, nrtg, ncg;
+};
+
+struct ConfArgs {
+  int R, gamma, d, rank, V;
+  const void* h;
+  const void* W1;
+  const void* w;
+  const float* sts;
+  const int32_t* x;
+  float* c;
+  bool vec_h, vec_e;
+  uint32_t* status;
+};
+
+struct PackArgs {
+  int R, width, len_offset;
+  const int32_t* rows;
+  const int32_t* len;
+  int32_t* cu;
+  int32_t* flat;
+  int32_t* marker_req;
+  int32_t* marker_pos;
+  int32_t* N_out;
+  uint32_t* status;
+};
+
+struct SchedArgs {
+  int R, gamma, N_max, enabled;
+  const float* c;
+  const double* sps;
+  int32_t* ell;
+  float* a;
+  int32_t* N_out;
+  double* theta;
+};
+
+hipError_t launch_row_stats(const RowStatsArgs& a, bool bf16, bool greedy, hipStream_t st);
+hipError_t launch_markov_stats(const MarkovArgs& a, bool u_bf16, bool w_bf16, int mode,
+                               hipStream_t st);
+
+hipError_t launch_confidence(const ConfArgs& a, bool h_bf16, bool w1_bf16, bool w_bf16,
+                             hipStream_t st);
+hipError_t launch_pack(const PackArgs& a, hipStream_t st);
+hipError_t launch_schedule(const SchedArgs& a, hipStream_t st);
+hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,
+                        const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
+                        const int32_t* x0, int32_t* x, float* logp_d, float* lse_d, float* margin,
+                        void* ws, hipStream_t st, hipEvent_t* ev_begin = nullptr,
+                        hipEvent_t* ev_end = nullptr);
+hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,
+                         const int32_t* ell, const int32_t* cu, const void* target, int layout,
+                         const int32_t* x, const float* logp_d, const float* lse_d,
+                         const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
+                         int32_t* m, int32_t* tau, int32_t* emitted, int32_t* next_anchor,
+                         float* logp_t, void* ws, hipStream_t st);
+
+}  // namespace dspark

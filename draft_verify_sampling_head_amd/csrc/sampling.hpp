@@ -1,0 +1,152 @@
+// sampling.hpp -- wave-level pieces of the chunked Gumbel-max sampler.
+//
+// Exact categorical sampling from softmax(score) over a vocabulary split into
+// chunks of kChunk consecutive entries: pick a chunk c by Gumbel-max over the
+// chunk log-masses L_c = ln sum_{v in c} exp(score_v), then an entry inside c
+// by Gumbel-max over score_v.  P(c) * P(v | c) = softmax(score)(v) (the
+// Gumbel-max theorem applied at both levels), so only ceil(V/kChunk) + kChunk
+// uniforms are drawn instead of V.  Keys are float32 sums; ties go to the
+// lower index.  With a single chunk no chunk-level uniform is drawn.
+#pragma once
+#include "device_common.hpp"
+
+namespace dspark {
+
+struct PickResult {
+  int idx;       // winner (-1 if nothing had mass)
+  float key;     // its key
+  float gap;     // best minus second-best key (only when asked for)
+};
+
+// Chunk-level Gumbel pick over L[0..nch) (natural-log chunk masses; -inf =
+// no mass).  One wave; lane l handles chunk blocks of four, one Philox block
+// per four chunks.
+__device__ inline PickResult pick_chunk(const float* L, int nch, uint64_t seed, uint64_t round,
+                                        uint32_t tag, uint32_t req, uint32_t k, bool want_gap) {
+  const int lane = threadIdx.x & 63;
+  PickResult r{-1, -INFINITY, INFINITY};
+  if (nch == 1) {
+    r.idx = (L[0] == -INFINITY) ? -1 : 0;
+    r.key = L[0];
+    return r;
+  }
+  float best = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int b = lane; b * 4 < nch; b += 64) {
+    const uint4 blk = stream_block(seed, round, tag, req, k, (uint32_t)b);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = b * 4 + w;
+      if (c < nch) {
+        const float l = L[c];
+        if (l != -INFINITY) {
+          const float key = l + gumbel_of(word_of(blk, (uint32_t)w));
+          argmax_merge(best, bi, key, c);
+        }
+      }
+    }
+  }
+  wave_argmax(best, bi);
+  r.idx = (best == -INFINITY) ? -1 : bi;
+  r.key = best;
+  if (want_gap && r.idx >= 0) {
+    float second = -INFINITY;
+    for (int b = lane; b * 4 < nch; b += 64) {
+      const uint4 blk = stream_block(seed, round, tag, req, k, (uint32_t)b);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int c = b * 4 + w;
+        if (c < nch && c != r.idx && L[c] != -INFINITY)
+          second = fmaxf(second, L[c] + gumbel_of(word_of(blk, (uint32_t)w)));
+      }
+    }
+    r.gap = best - wave_max(second);
+  }
+  return r;
+}
+
+// In-chunk Gumbel pick: lane l holds the scores of entries base+l and
+// base+64+l (-inf = excluded / outside the vocabulary).
+__device__ inline PickResult pick_in_chunk(float s0, float s1, int base, uint64_t seed,
+                                           uint64_t round, uint32_t tag, uint32_t req,
+                                           uint32_t k, bool want_gap) {
+  const int lane = threadIdx.x & 63;
+  const int v0 = base + lane, v1 = base + 64 + lane;
+  const uint4 b0 = stream_block(seed, round, tag, req, k, (uint32_t)v0 >> 2);
+  const uint4 b1 = stream_block(seed, round, tag, req, k, (uint32_t)v1 >> 2);
+  const float k0 = (s0 == -INFINITY) ? -INFINITY : s0 + gumbel_of(word_of(b0, (uint32_t)v0 & 3u));
+  const float k1 = (s1 == -INFINITY) ? -INFINITY : s1 + gumbel_of(word_of(b1, (uint32_t)v1 & 3u));
+  float best = k0;
+  int bi = v0;
+  argmax_merge(best, bi, k1, v1);
+  if (best == -INFINITY) bi = 0x7FFFFFFF;
+  wave_argmax(best, bi);
+  PickResult r{best == -INFINITY ? -1 : bi, best, INFINITY};
+  if (want_gap && r.idx >= 0) {
+    float second = -INFINITY;
+    if (v0 != r.idx) second = fmaxf(second, k0);
+    if (v1 != r.idx) second = fmaxf(second, k1);
+    r.gap = best - wave_max(second);
+  }
+  return r;
+}
+
+// Lowest-index argmax over per-chunk maxima M / argmaxes I (greedy).
+__device__ inline void argmax_chunks(const float* M, const int* I, int nch, float& v, int& idx) {
+  const int lane = threadIdx.x & 63;
+  v = -INFINITY;
+  idx = 0x7FFFFFFF;
+  for (int c = lane; c < nch; c += 64) argmax_merge(v, idx, M[c], I[c]);
+  wave_argmax(v, idx);
+}
+
+// ln sum_c exp(L_c) over a row of chunk log-masses (one wave).
+__device__ inline float lse_chunks(const float* L, int nch) {
+  const int lane = threadIdx.x & 63;
+  float m = -INFINITY;
+  for (int c = lane; c < nch; c += 64) m = fmaxf(m, L[c]);
+  m = wave_max(m);
+  if (m == -INFINITY) return -INFINITY;
+  float s = 0.f;
+  for (int c = lane; c < nch; c += 64) s += expf(L[c] - m);
+  s = wave_sum(s);
+  return m + logf(s);
+}
+
+// Markov bias W1[prev] . W2t[v] for one vocabulary entry: float32 FMA chain in
+// ascending i.  e is the gathered W1 row (the same address in every lane);
+// rank is a multiple of 16 and rows are 16-byte aligned.
+__device__ inline float markov_bias(const uint16_t* e, const uint16_t* W2t, int rank, int v) {
+  const uint4* w = reinterpret_cast<const uint4*>(W2t + (int64_t)v * rank);
+  const uint4* ev = reinterpret_cast<const uint4*>(e);
+  float b = 0.f;
+  for (int q = 0; q < rank / 8; ++q) {
+    const uint4 u = w[q];
+    const uint4 x = ev[q];
+    b = fmaf(bf16_lo(x.x), bf16_lo(u.x), b);
+    b = fmaf(bf16_hi(x.x), bf16_hi(u.x), b);
+    b = fmaf(bf16_lo(x.y), bf16_lo(u.y), b);
+    b = fmaf(bf16_hi(x.y), bf16_hi(u.y), b);
+    b = fmaf(bf16_lo(x.z), bf16_lo(u.z), b);
+    b = fmaf(bf16_hi(x.z), bf16_hi(u.z), b);
+    b = fmaf(bf16_lo(x.w), bf16_lo(u.w), b);
+    b = fmaf(bf16_hi(x.w), bf16_hi(u.w), b);
+  }
+  return b;
+}
+__device__ inline float markov_bias(const float* e, const float* W2t, int rank, int v) {
+  const float4* w = reinterpret_cast<const float4*>(W2t + (int64_t)v * rank);
+  const float4* ev = reinterpret_cast<const float4*>(e);
+  float b = 0.f;
+  for (int q = 0; q < rank / 4; ++q) {
+    const float4 u = w[q];
+    const float4 x = ev[q];
+    b = fmaf(x.x, u.x, b);
+    b = fmaf(x.y, u.y, b);
+    b = fmaf(x.z, u.z, b);
+    b = fmaf(x.w, u.w, b);
+  }
+  return b;
+}
+
+}  // namespace dspark

@@ -1,0 +1,275 @@
+// verify.hip -- lossless rejection-sampling verification.
+//
+// DSpark summary page, Background (x_k accepted with probability
+// min(1, p_t(x_k)/p_d(x_k)), left to right, the first rejection drops the
+// rest); MTP survey page, section 2.2 (resample the rejected position from
+// norm(max(0, p_t - p_d)); after a fully accepted prefix draw the bonus token
+// from the next target distribution; tau = m + 1; greedy reduction).
+// Launches, all sized by capacity so N, m and the rejections stay on device:
+//   1. k_row_stats over the N verify rows: chunk log-masses of t/T (or chunk
+//      maxima at T = 0); also clears the residual work counter.
+//   2. k_verify_scan, one wave per request: row normalisers, log p_t(x_k),
+//      the accept scan, and either the bonus draw (chunked Gumbel-max on the
+//      row after the accepted prefix) or a residual work item.
+//   3. residual chunk masses for the listed (request, position) rows: the
+//      draft scores are rebuilt with the Markov bias (MFMA) and combined with
+//      the target row into max(0, p_t - p_d) per chunk.
+//   4. k_resid_pick, one wave per work item: chunk pick and in-chunk pick on
+//      log max(0, p_t - p_d); zero mass falls back to p_t.
+#include "launch.hpp"
+#include "sampling.hpp"
+#include "workspace.hpp"
+
+namespace dspark {
+
+struct VerifyArgs {
+  int R, gamma, V, rank, nch, layout;
+  float invT;
+  bool greedy;
+  uint64_t seed, round;
+  const int32_t* ell;
+  const int32_t* cu;
+  const void* target;
+  const int32_t* x;
+  const float* logp_d;
+  const float* lse_d;
+  const void* U;
+  const void* W1;
+  const void* W2t;
+  int32_t* m;
+  int32_t* tau;
+  int32_t* emitted;
+  int32_t* next_anchor;
+  float* logp_t;
+  const float* vl;      // [q][nch] chunk log-masses / maxima of verify rows
+  const int* vi;        // [q][nch] chunk argmax (greedy)
+  float* lse_t;         // [q]
+  int32_t* rej_count;
+  int4* rej;            // (request, position, target row, verify row q)
+  const float* rl;      // [slot][nch] residual chunk log-masses
+  uint32_t* status;
+};
+
+__device__ __forceinline__ int64_t target_row(const VerifyArgs& a, int i, int j) {
+  return a.layout == 0 ? (int64_t)a.cu[i] + j : (int64_t)i * (a.gamma + 1) + j;
+}
+
+template <typename TT>
+__global__ __launch_bounds__(64) void k_verify_scan(VerifyArgs a) {
+  const int i = blockIdx.x;
+  const int lane = threadIdx.x;
+  int L = a.ell[i];
+  if (L < 0 || L > a.gamma) { set_flag(a.status, kFlagBadLen); L = L < 0 ? 0 : a.gamma; }
+  const int q0 = a.cu[i];
+  const int32_t* xi = a.x + (int64_t)i * (a.gamma + 1);
+  const TT* tgt = reinterpret_cast<const TT*>(a.target);
+  int m = L;
+  int y = -1;
+  bool rejected = false;
+  if (!a.greedy) {
+    for (int k = 1; k <= a.gamma; ++k)
+      if (a.logp_t && lane == 0) a.logp_t[(int64_t)i * a.gamma + (k - 1)] = 0.f;
+    float lse_row = 0.f;
+    for (int j = 0; j <= L; ++j) {
+      const int q = q0 + j;
+      const float lse = lse_chunks(a.vl + (int64_t)q * a.nch, a.nch);
+      if (lane == 0) a.lse_t[q] = lse;
+      if (j < L) {
+        const int k = j + 1;
+        int xk = xi[k];
+        if (xk < 0 || xk >= a.V) { set_flag(a.status, kFlagBadToken); xk = 0; }
+        const float lp = Elem<TT>::get(tgt + target_row(a, i, j) * a.V, xk) * a.invT - lse;
+        if (a.logp_t && lane == 0) a.logp_t[(int64_t)i * a.gamma + (k - 1)] = lp;
+        if (!rejected) {
+          const uint4 blk = stream_block(a.seed, a.round, kTagAccept, (uint32_t)i, (uint32_t)k, 0u);
+          const float lu = log_uniform(blk.x);
+          const float rhs = lp - a.logp_d[(int64_t)i * a.gamma + (k - 1)];
+          if (!(lu < rhs)) { rejected = true; m = k - 1; }
+        }
+      } else {
+        lse_row = lse;
+      }
+    }
+    if (!rejected) {
+      // bonus token from the target row after the accepted prefix
+      const int q = q0 + L;
+      const PickResult pc = pick_chunk(a.vl + (int64_t)q * a.nch, a.nch, a.seed, a.round,
+                                       kTagBonusChunk, (uint32_t)i, (uint32_t)(L + 1), false);
+      int c = pc.idx < 0 ? 0 : pc.idx;
+      if (pc.idx < 0) set_flag(a.status, kFlagNonFinite);
+      const TT* trow = tgt + target_row(a, i, L) * a.V;
+      float s[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int v = c * kChunk + h * 64 + lane;
+        s[h] = (v < a.V) ? Elem<TT>::get(trow, v) * a.invT : -INFINITY;
+      }
+      const PickResult pe = pick_in_chunk(s[0], s[1], c * kChunk, a.seed, a.round, kTagBonusElem,
+                                          (uint32_t)i, (uint32_t)(L + 1), false);
+      y = pe.idx < 0 ? c * kChunk : pe.idx;
+      (void)lse_row;
+    } else if (lane == 0) {
+      const int slot = atomicAdd(a.rej_count, 1);
+      a.rej[slot] = make_int4(i, m + 1, (int)target_row(a, i, m), q0 + m);
+    }
+  } else {
+    for (int k = 1; k <= a.gamma; ++k)
+      if (a.logp_t && lane == 0) a.logp_t[(int64_t)i * a.gamma + (k - 1)] = 0.f;
+    for (int k = 1; k <= L && !rejected; ++k) {
+      const int q = q0 + k - 1;
+      float v;
+      int am;
+      argmax_chunks(a.vl + (int64_t)q * a.nch, a.vi + (int64_t)q * a.nch, a.nch, v, am);
+      if (xi[k] != am) { rejected = true; m = k - 1; y = am; }
+    }
+    if (!rejected) {
+      const int q = q0 + L;
+      float v;
+      argmax_chunks(a.vl + (int64_t)q * a.nch, a.vi + (int64_t)q * a.nch, a.nch, v, y);
+    }
+    if (y < 0 || y >= a.V) { set_flag(a.status, kFlagNonFinite); y = 0; }
+  }
+  // outputs (y is wave-uniform; a rejected sampled position gets its token
+  // from k_resid_pick)
+  int32_t* em = a.emitted + (int64_t)i * (a.gamma + 1);
+  const bool have_y = a.greedy || !rejected;
+  for (int q = lane; q <= a.gamma; q += 64)
+    em[q] = (q < m) ? xi[q + 1] : ((q == m && have_y) ? y : -1);
+  if (lane == 0) {
+    a.m[i] = m;
+    a.tau[i] = m + 1;
+    if (have_y) a.next_anchor[i] = y;
+  }
+}
+
+template <typename UT, typename WT>
+__global__ __launch_bounds__(64) void k_resid_pick(VerifyArgs a) {
+  const int slot = blockIdx.x;
+  const int lane = threadIdx.x;
+  if (slot >= *a.rej_count) return;
+  const int4 e = a.rej[slot];
+  const int i = e.x, k = e.y, trow_i = e.z, q = e.w;
+  const UT* trow = reinterpret_cast<const UT*>(a.target) + (int64_t)trow_i * a.V;
+  const float* Lq = a.rl + (int64_t)slot * a.nch;
+  const float mass = lse_chunks(Lq, a.nch);
+  int y;
+  if (mass != -INFINITY) {
+    const PickResult pc = pick_chunk(Lq, a.nch, a.seed, a.round, kTagResidChunk, (uint32_t)i,
+                                     (uint32_t)k, false);
+    const int c = pc.idx < 0 ? 0 : pc.idx;
+    const UT* urow = reinterpret_cast<const UT*>(a.U) + ((int64_t)i * a.gamma + (k - 1)) * a.V;
+    int prev = a.x[(int64_t)i * (a.gamma + 1) + (k - 1)];
+    if (prev < 0 || prev >= a.V) prev = 0;
+    const WT* erow = reinterpret_cast<const WT*>(a.W1) + (int64_t)prev * a.rank;
+    const float lse_t = a.lse_t[q];
+    const float lse_d = a.lse_d[(int64_t)i * a.gamma + (k - 1)];
+    float s[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v = c * kChunk + h * 64 + lane;
+      s[h] = -INFINITY;
+      if (v < a.V) {
+        const float b = a.rank > 0 ? markov_bias(erow, reinterpret_cast<const WT*>(a.W2t), a.rank, v)
+                                   : 0.f;
+        const float sd = (Elem<UT>::get(urow, v) + b) * a.invT;
+        const float pt = expf(Elem<UT>::get(trow, v) * a.invT - lse_t);
+        const float pd = expf(sd - lse_d);
+        const float d = pt - pd;
+        s[h] = d > 0.f ? logf(d) : -INFINITY;
+      }
+    }
+    const PickResult pe = pick_in_chunk(s[0], s[1], c * kChunk, a.seed, a.round, kTagResidElem,
+                                        (uint32_t)i, (uint32_t)k, false);
+    y = pe.idx;
+    if (y < 0) {
+      // the chunk's mass vanished on re-evaluation: take its best target entry
+      set_flag(a.status, kFlagNonFinite);
+      y = c * kChunk;
+    }
+  } else {
+    // zero residual mass: sample p_t of the same row
+    const PickResult pc = pick_chunk(a.vl + (int64_t)q * a.nch, a.nch, a.seed, a.round,
+                                     kTagResidChunk, (uint32_t)i, (uint32_t)k, false);
+    const int c = pc.idx < 0 ? 0 : pc.idx;
+    float s[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int v = c * kChunk + h * 64 + lane;
+      s[h] = (v < a.V) ? Elem<UT>::get(trow, v) * a.invT : -INFINITY;
+    }
+    const PickResult pe = pick_in_chunk(s[0], s[1], c * kChunk, a.seed, a.round, kTagResidElem,
+                                        (uint32_t)i, (uint32_t)k, false);
+    y = pe.idx < 0 ? c * kChunk : pe.idx;
+  }
+  if (lane == 0) {
+    a.emitted[(int64_t)i * (a.gamma + 1) + (k - 1)] = y;
+    a.next_anchor[i] = y;
+  }
+}
+
+hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,
+                         const int32_t* ell, const int32_t* cu, const void* target, int layout,
+                         const int32_t* x, const float* logp_d, const float* lse_d,
+                         const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
+                         int32_t* m, int32_t* tau, int32_t* emitted, int32_t* next_anchor,
+                         float* logp_t, void* ws, hipStream_t st) {
+  const WsLayout L = ws_layout(R, gamma, V);
+  char* w = reinterpret_cast<char*>(ws);
+  uint32_t* hdr = reinterpret_cast<uint32_t*>(w + L.header);
+  const int nch = (V + kChunk - 1) / kChunk;
+  const bool greedy = (T == 0.f);
+  const size_t usz = u_bf16 ? 2 : 4;
+  const bool t_vec = ((reinterpret_cast<uintptr_t>(target) & 15) == 0) && (((size_t)V * usz) % 16 == 0);
+  const bool u_vec = ((reinterpret_cast<uintptr_t>(U) & 15) == 0) && (((size_t)V * usz) % 16 == 0);
+
+  RowStatsArgs rs{};
+  rs.base = target;
+  rs.kind = layout == 0 ? kRowsVerifyPacked : kRowsVerifyDense;
+  rs.R = R; rs.gamma = gamma; rs.k = 0; rs.V = V; rs.nch = nch; rs.cu = cu;
+  rs.nrows_cap = R * (gamma + 1);
+  rs.scale2 = greedy ? 1.f : kLog2e / T;
+  rs.vec_ok = t_vec;
+  rs.L = reinterpret_cast<float*>(w + L.ver_l);
+  rs.M = rs.L;
+  rs.I = reinterpret_cast<int*>(w + L.ver_i);
+  rs.status = hdr;
+  rs.zero_me = hdr + 1;
+  hipError_t e = launch_row_stats(rs, u_bf16, greedy, st);
+  if (e != hipSuccess) return e;
+
+  VerifyArgs a{};
+  a.R = R; a.gamma = gamma; a.V = V; a.rank = rank; a.nch = nch; a.layout = layout;
+  a.invT = greedy ? 1.f : 1.f / T; a.greedy = greedy; a.seed = seed; a.round = round;
+  a.ell = ell; a.cu = cu; a.target = target; a.x = x; a.logp_d = logp_d; a.lse_d = lse_d;
+  a.U = U; a.W1 = W1; a.W2t = W2t; a.m = m; a.tau = tau; a.emitted = emitted;
+  a.next_anchor = next_anchor; a.logp_t = logp_t;
+  a.vl = rs.L; a.vi = rs.I;
+  a.lse_t = reinterpret_cast<float*>(w + L.lse_t);
+  a.rej_count = reinterpret_cast<int32_t*>(hdr + 1);
+  a.rej = reinterpret_cast<int4*>(w + L.rej);
+  a.rl = reinterpret_cast<float*>(w + L.draft_l);
+  a.status = hdr;
+  if (u_bf16) hipLaunchKernelGGL((k_verify_scan<uint16_t>), dim3(R), dim3(64), 0, st, a);
+  else hipLaunchKernelGGL((k_verify_scan<float>), dim3(R), dim3(64), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || greedy) return e;
+
+  MarkovArgs ma{};
+  ma.R = R; ma.gamma = gamma; ma.k = 0; ma.V = V; ma.rank = rank; ma.nch = nch; ma.nrows_cap = R;
+  ma.U = U; ma.W1v = W1; ma.W2tv = W2t; ma.x0 = nullptr; ma.x = x; ma.scale2 = kLog2e / T;
+  ma.u_vec_ok = u_vec && t_vec;
+  ma.L = const_cast<float*>(a.rl); ma.M = ma.L; ma.I = nullptr;
+  ma.rej_count = a.rej_count; ma.rej = a.rej; ma.target = target; ma.lse_t = a.lse_t;
+  ma.lse_d = lse_d; ma.status = hdr;
+  e = launch_markov_stats(ma, u_bf16, w_bf16 && rank > 0, kModeResid, st);
+  if (e != hipSuccess) return e;
+#define DSPARK_RP(UT_, WT_) hipLaunchKernelGGL((k_resid_pick<UT_, WT_>), dim3(R), dim3(64), 0, st, a)
+  if (u_bf16 && w_bf16) DSPARK_RP(uint16_t, uint16_t);
+  else if (u_bf16) DSPARK_RP(uint16_t, float);
+  else if (w_bf16) DSPARK_RP(float, uint16_t);
+  else DSPARK_RP(float, float);
+#undef DSPARK_RP
+  return hipGetLastError();
+}
+
+}  // namespace dspark

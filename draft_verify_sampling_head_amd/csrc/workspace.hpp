@@ -1,0 +1,42 @@
+// workspace.hpp -- layout of the caller-provided workspace (host and device).
+//
+// One workspace serves every entry point of a round; the regions below are
+// carved at 256-byte boundaries.  All sizes follow the round's capacity
+// (R requests, gamma positions, V vocabulary), never the data-dependent
+// counts, so nothing has to visit the host.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dspark {
+
+struct WsLayout {
+  size_t header;       // uint32 words: [0] status flags, [1] residual count
+  size_t draft_l;      // float  [R][nch]   chunk log-masses / maxima (draft, residual)
+  size_t draft_i;      // int32  [R][nch]   chunk argmax (greedy)
+  size_t ver_l;        // float  [R*(gamma+1)][nch]  target-row chunk log-masses / maxima
+  size_t ver_i;        // int32  [R*(gamma+1)][nch]  target-row chunk argmax (greedy)
+  size_t lse_t;        // float  [R*(gamma+1)]       target-row log-normalisers
+  size_t rej;          // int32  [R][4]   residual work list: request, position, row, pad
+  size_t total;
+};
+
+inline size_t ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline WsLayout ws_layout(int R, int gamma, int V) {
+  const size_t nch = ((size_t)V + 127) / 128;
+  const size_t rows_v = (size_t)R * (size_t)(gamma + 1);
+  WsLayout L;
+  size_t off = 0;
+  L.header = off;  off += ws_align(256);
+  L.draft_l = off; off += ws_align((size_t)R * nch * 4);
+  L.draft_i = off; off += ws_align((size_t)R * nch * 4);
+  L.ver_l = off;   off += ws_align(rows_v * nch * 4);
+  L.ver_i = off;   off += ws_align(rows_v * nch * 4);
+  L.lse_t = off;   off += ws_align(rows_v * 4);
+  L.rej = off;     off += ws_align((size_t)R * 16);
+  L.total = off;
+  return L;
+}
+
+}  // namespace dspark

@@ -1,0 +1,63 @@
+"""One DSpark round on the GPU: the six C-ABI calls enqueued back to back.
+
+draft (Markov head) -> confidence -> prefix schedule -> pack the verify batch
+-> verify -> pack the emitted tokens.  This module only allocates the output
+tensors (torch is the memory allocator) and calls the library in order; the
+scheduled lengths, N, m and tau never leave the device.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+
+class RoundBuffers:
+    """Outputs and workspace of one round, allocated once and reused."""
+
+    def __init__(self, R, gamma, V, device="cuda"):
+        i32, f32 = torch.int32, torch.float32
+        dev = torch.device(device)
+        self.R, self.gamma, self.V = R, gamma, V
+        self.x = torch.empty(R, gamma + 1, dtype=i32, device=dev)
+        self.logp_d = torch.empty(R, gamma, dtype=f32, device=dev)
+        self.lse_d = torch.empty(R, gamma, dtype=f32, device=dev)
+        self.c = torch.empty(R, gamma, dtype=f32, device=dev)
+        self.ell = torch.empty(R, dtype=i32, device=dev)
+        self.a = torch.empty(R, gamma, dtype=f32, device=dev)
+        self.N = torch.empty(1, dtype=i32, device=dev)
+        self.theta = torch.empty(1, dtype=torch.float64, device=dev)
+        cap = R * (gamma + 1)
+        self.cu = torch.empty(R + 1, dtype=i32, device=dev)
+        self.flat = torch.empty(cap, dtype=i32, device=dev)
+        self.marker_req = torch.empty(cap, dtype=i32, device=dev)
+        self.marker_pos = torch.empty(cap, dtype=i32, device=dev)
+        self.m = torch.empty(R, dtype=i32, device=dev)
+        self.tau = torch.empty(R, dtype=i32, device=dev)
+        self.emitted = torch.empty(R, gamma + 1, dtype=i32, device=dev)
+        self.next_anchor = torch.empty(R, dtype=i32, device=dev)
+        self.logp_t = torch.empty(R, gamma, dtype=f32, device=dev)
+        self.cu_out = torch.empty(R + 1, dtype=i32, device=dev)
+        self.flat_out = torch.empty(cap, dtype=i32, device=dev)
+        self.N_out = torch.empty(1, dtype=i32, device=dev)
+        self.ws = L.workspace(R, gamma, V, device=dev)
+
+
+def run_round(inp, buf: RoundBuffers, T, seed, rnd, scheduler=True, layout=1, sts_T=None,
+              stream=None):
+    """Enqueue one full round on `stream` (default: torch's current stream).
+
+    `inp` holds U, W1, W2t, x0, h, w, sps and target (dense [R][gamma+1][V] for
+    layout 1; packed rows in verify order for layout 0)."""
+    L.draft_markov(inp["U"], inp["W1"], inp["W2t"], inp["x0"], T, seed, rnd, buf.x, buf.logp_d,
+                   buf.lse_d, buf.ws, stream=stream)
+    L.confidence(inp["h"], inp["W1"], inp["w"], buf.x, buf.c, sts_T=sts_T, V=buf.V, stream=stream)
+    L.prefix_schedule(buf.c, inp["sps"], buf.ell, enabled=scheduler, a=buf.a, N_out=buf.N,
+                      theta_best=buf.theta, stream=stream)
+    L.pack(buf.x, buf.ell, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N, ws=buf.ws,
+           stream=stream)
+    L.verify(buf.ell, buf.cu, inp["target"], layout, buf.x, buf.logp_d, buf.lse_d, inp["U"],
+             inp["W1"], inp["W2t"], T, seed, rnd, buf.m, buf.tau, buf.emitted, buf.next_anchor,
+             buf.ws, logp_t=buf.logp_t, stream=stream)
+    L.pack(buf.emitted, buf.tau, 0, buf.cu_out, buf.flat_out, N_out=buf.N_out, ws=buf.ws,
+           stream=stream)

@@ -1,0 +1,220 @@
+/*
+ * dspark.h -- C ABI of libdspark.so: the data-parallel hot path of one DSpark
+ * speculative-decoding round on an MI355X (gfx950) GPU.
+ *
+ * Method (the DSpark pages; cited by page and section):
+ *  [P3] papercache.org summary of "DSpark: Confidence-Scheduled Speculative
+ *       Decoding with Semi-Autoregressive Generation" (arXiv 2607.05147).
+ *  [P1] backyes.github.io "MTP algorithm survey", section 2.2 (rejection sampling).
+ *  [P2] bevisy.github.io DeepSpec analysis, section 2.2 (DFlash = rank 0).
+ *  [P4] modelscope/CSDN DSpark article, section 3.3 (flatten + marker tensors).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer is a DEVICE pointer unless marked (host).  The caller owns
+ *    all memory; no call allocates, frees or synchronises.  Each call checks
+ *    its scalar arguments on the host, then enqueues kernels on `stream` and
+ *    returns; outputs are valid once the stream reaches the call.
+ *  - A call that returns an error other than DSPARK_E_HIP has enqueued nothing.
+ *    DSPARK_E_HIP means a kernel launch failed; the stream state is then the
+ *    HIP runtime's.
+ *  - The library keeps no global state between calls.  Calls that share a
+ *    workspace must be ordered on one stream (or otherwise serialised).
+ *  - R = requests in the batch, gamma = block size (draft positions per
+ *    request), V = vocabulary, r = Markov rank, d = backbone hidden size,
+ *    T = sampling temperature (T == 0 selects greedy decoding).
+ *  - Row-major layouts.  Token ids are int32 in [0, V).
+ *  - Random numbers come from Philox4x32-10 (Salmon et al., SC'11) with
+ *    key (lo32 seed, hi32 seed) and counter (idx/4, k | tag<<16, request,
+ *    lo32 round); `round` must change between rounds that reuse a seed.
+ *    Sampling from softmax(score) uses the chunked Gumbel-max rule with
+ *    chunks of DSPARK_CHUNK consecutive vocabulary entries (exact sampling).
+ *  - Limits: 1 <= gamma <= 32; r == 0 or r a multiple of 16 up to 512;
+ *    1 <= V < 2^31; T >= 0 and finite; R * gamma <= 16384 for the scheduler.
+ *    R == 0 is a valid empty batch (nothing is enqueued).
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSPARK_CHUNK 128
+
+typedef enum {
+    DSPARK_OK = 0,
+    DSPARK_E_INVALID = 1,      /* null pointer, negative size, T < 0, bad layout  */
+    DSPARK_E_UNSUPPORTED = 2,  /* outside the limits above                         */
+    DSPARK_E_WORKSPACE = 3,    /* ws_bytes < dspark_workspace_bytes(...)           */
+    DSPARK_E_HIP = 4           /* a kernel launch failed                           */
+} dspark_status;
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+/* Device-side condition flags, OR-ed into the workspace status word. */
+#define DSPARK_FLAG_NONFINITE 1u   /* a non-finite logit or score was seen        */
+#define DSPARK_FLAG_BAD_LEN   2u   /* a pack length outside [0, width] was clamped */
+#define DSPARK_FLAG_BAD_TOKEN 4u   /* a token id outside [0, V) was read           */
+
+/* (host) Bytes of workspace every entry point below needs for these sizes. */
+size_t dspark_workspace_bytes(int R, int gamma, int V, int r, int d);
+
+/* (host) Human-readable name of a status code. */
+const char* dspark_status_string(dspark_status s);
+
+/* (host) Version string of the library build. */
+const char* dspark_version(void);
+
+/* Clears the workspace status word (enqueued on `stream`; no allocation). */
+dspark_status dspark_clear_status(void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* (host, synchronous) Reads the workspace status word into *flags (host).  Call
+ * after the stream has finished the calls of interest; it blocks on a copy. */
+dspark_status dspark_get_status(const void* ws, size_t ws_bytes, uint32_t* flags);
+
+/*
+ * Markov draft head over one block ([P3] Method details: causal block
+ * distribution p_k(v | x_0, x_<k) = softmax(U_k + B_k)(v); Markov head
+ * B(x_{k-1}, .) = W1[x_{k-1}] W2 with W1 in R^{V x r}, W2 in R^{r x V}; the
+ * anchor x_0 is the first predicted position's input).  For k = 1..gamma, in
+ * order: s = (U_k + W1[x_{k-1}] W2) / T over the whole vocabulary, an exact
+ * softmax, and x_k sampled from it; T == 0 takes the first argmax of
+ * U_k + W1[x_{k-1}] W2.  r == 0 is the DFlash case: independent per-position
+ * sampling from softmax(U_k / T) ([P2] 2.2).
+ *   U      [R][gamma][V]   base logits U_1..U_gamma (U_dt)
+ *   W1     [V][r]          embedding table (W_dt); unused if r == 0
+ *   W2t    [V][r]          W2 TRANSPOSED: W2t[v][i] = W2[i][v], the weight
+ *                          layout of a linear layer r -> V (W_dt)
+ *   x0     [R]             anchors
+ *   x      out [R][gamma+1]  x[i][0] = x0[i], x[i][k] = drafted token k
+ *   logp_d out [R][gamma]    log p_k(x_k) of the tempered draft (0 if T == 0)
+ *   lse_d  out [R][gamma]    log-normaliser of s (max score if T == 0)
+ *   margin out nullable [R][gamma]  gap between the two best Gumbel keys
+ *                          (debug; smaller of the chunk and in-chunk gaps)
+ * W_dt == DSPARK_BF16 runs the bias contraction on MFMA (fp32 accumulation);
+ * DSPARK_F32 weights run it on the vector ALU.
+ */
+dspark_status dspark_draft_markov(int R, int gamma, int V, int r, float T,
+                                  uint64_t seed, uint64_t round,
+                                  const void* U, dspark_dtype U_dt,
+                                  const void* W1, const void* W2t, dspark_dtype W_dt,
+                                  const int32_t* x0, int32_t* x, float* logp_d, float* lse_d,
+                                  float* margin, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Instrumented dspark_draft_markov for performance measurement: identical
+ * results; additionally records ev_begin[k-1] / ev_end[k-1] on `stream`
+ * immediately before / after the per-chunk statistics kernel of step k
+ * (the bias contraction and vocabulary stream, the draft's dominant kernel).
+ *   ev_begin, ev_end  (host) arrays of gamma events created by the caller
+ * Returns DSPARK_E_INVALID if either array is null.
+ */
+dspark_status dspark_draft_markov_profiled(int R, int gamma, int V, int r, float T,
+                                           uint64_t seed, uint64_t round,
+                                           const void* U, dspark_dtype U_dt,
+                                           const void* W1, const void* W2t, dspark_dtype W_dt,
+                                           const int32_t* x0, int32_t* x, float* logp_d,
+                                           float* lse_d, float* margin, void* ws, size_t ws_bytes,
+                                           hipStream_t stream, hipEvent_t* ev_begin,
+                                           hipEvent_t* ev_end);
+
+/*
+ * Confidence head ([P3] Method details, confidence head and STS calibration):
+ * c[i][k-1] = sigmoid((w_h . h_k + w_e . W1[x_{k-1}]) / t_k), k = 1..gamma.
+ *   h      [R][gamma][d]   backbone hidden states (h_dt)
+ *   W1     [V][r]          embedding table (W_dt); unused if r == 0
+ *   w      [d + r]         confidence vector [w_h ; w_e] (w_dt)
+ *   sts_T  nullable [gamma] per-position temperatures (default 1)
+ *   x      [R][gamma+1]    anchor + drafted tokens
+ *   c      out [R][gamma]  float32 confidences
+ */
+dspark_status dspark_confidence(int R, int gamma, int d, int r, int V,
+                                const void* h, dspark_dtype h_dt,
+                                const void* W1, dspark_dtype W_dt,
+                                const void* w, dspark_dtype w_dt,
+                                const float* sts_T, const int32_t* x, float* c,
+                                hipStream_t stream);
+
+/*
+ * Hardware-aware prefix scheduler ([P3] Method details, "greedy solution and
+ * causality", Algorithm 1).  a[i][j] = prod_{q<=j} c[i][q] (float32, left to
+ * right); candidates (i, j) with a > 0 are taken in order of a descending
+ * (ties: i, then j ascending); starting from B = R, tau = R,
+ * Theta_best = R * SPS(R), each candidate adds 1 to B and a to tau, and
+ * Theta = tau * SPS(B) must strictly improve or the scan stops (early stop).
+ * tau is summed in 2^-32 fixed point (exact, order-free); Theta is a double.
+ * B > N_max counts as Theta = 0 (capacity exceeded).
+ *   c          [R][gamma]   confidences
+ *   sps        [N_max+1]    SPS(B), engine steps per second at batch B (double)
+ *   enabled    0: ell = gamma for every request (static verification)
+ *   ell        out [R]      scheduled verify lengths in [0, gamma]
+ *   a          out nullable [R][gamma]  survival products
+ *   N_out      out nullable (device scalar)  sum_i (1 + ell_i)
+ *   theta_best out nullable (device scalar)  Theta of the returned schedule
+ * Needs R <= N_max and R * gamma <= 16384 (one workgroup, LDS-resident sort).
+ */
+dspark_status dspark_prefix_schedule(int R, int gamma, const float* c, const double* sps,
+                                     int N_max, int enabled, int32_t* ell, float* a,
+                                     int32_t* N_out, double* theta_best, hipStream_t stream);
+
+/*
+ * Ragged pack ([P3] Supplementary details, variable-length routing; [P4] 3.3):
+ * row i contributes its first len[i] + len_offset tokens; all of them are
+ * flattened back to back as independent elements, with offsets and marker
+ * tensors (owning request, position in the block).
+ *   rows       [R][width]   token rows (e.g. x with width gamma+1)
+ *   len        [R]          lengths (e.g. ell with len_offset 1, or tau with 0);
+ *                           an effective length outside [0, width] is clamped
+ *                           and flagged (DSPARK_FLAG_BAD_LEN) when ws != NULL
+ *   cu         out [R+1]    offsets, cu[0] = 0, cu[R] = N
+ *   flat       out [R*width] packed tokens; slots >= N hold -1
+ *   marker_req out nullable [R*width] owning request (-1 past N)
+ *   marker_pos out nullable [R*width] position inside the block (-1 past N)
+ *   N_out      out nullable (device scalar)
+ */
+dspark_status dspark_pack(int R, int width, const int32_t* rows, const int32_t* len,
+                          int len_offset, int32_t* cu, int32_t* flat, int32_t* marker_req,
+                          int32_t* marker_pos, int32_t* N_out, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
+ * Lossless rejection-sampling verification ([P3] Background: x_k accepted with
+ * probability min(1, p_t(x_k) / p_d(x_k)), left to right, the first rejection
+ * drops the rest; [P1] 2.2: at the first rejection a token is resampled from
+ * norm(max(0, p_t - p_d)), after a fully accepted prefix a bonus token is
+ * drawn from the next target distribution, tau = m + 1; at T == 0 the test is
+ * x_k == argmax p_t and the correction is the argmax).
+ * Request i verifies positions 1..ell[i].  Its verify row j (input token x_j,
+ * target distribution p_t^{j+1}), j = 0..ell[i], is read from
+ *   target_layout 0: packed [N][V], row cu[i] + j (cu from dspark_pack with
+ *                    rows = x, len = ell, len_offset = 1)
+ *   target_layout 1: dense [R][gamma+1][V], row i*(gamma+1) + j
+ * Accept test: log u < log p_t(x_k) - logp_d[i][k-1] with u in (0,1).
+ * Zero residual mass (p_t == p_d up to rounding) falls back to p_t.
+ *   x, logp_d, lse_d  the draft's outputs;  U, W1, W2t the draft's inputs
+ *                     (used to rebuild p_d at a rejected position)
+ *   m           out [R]        accepted draft tokens
+ *   tau         out [R]        m + 1 emitted tokens
+ *   emitted     out [R][gamma+1] x_1..x_m then the resampled / bonus token; -1 after
+ *   next_anchor out [R]        the last emitted token (next round's x_0)
+ *   logp_t      out nullable [R][gamma]  log p_t(x_k) for k <= ell[i], else 0
+ */
+dspark_status dspark_verify(int R, int gamma, int V, int r, float T,
+                            uint64_t seed, uint64_t round,
+                            const int32_t* ell, const int32_t* cu,
+                            const void* target, dspark_dtype t_dt, int target_layout,
+                            const int32_t* x, const float* logp_d, const float* lse_d,
+                            const void* U, dspark_dtype U_dt,
+                            const void* W1, const void* W2t, dspark_dtype W_dt,
+                            int32_t* m, int32_t* tau, int32_t* emitted, int32_t* next_anchor,
+                            float* logp_t, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

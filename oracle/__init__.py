@@ -55,7 +55,7 @@ def lib():
         L.orc_residual_row.argtypes = [i64, f64, P, P, f64, P]
         L.orc_residual_row.restype = f64
         L.orc_draft_markov.argtypes = [i32, i32, i64, i32, f64, u64, u64, P, P, P, P, P, P,
-                                       P, P, P, P]
+                                       P, P, P, P, P]
         L.orc_draft_markov.restype = i32
         L.orc_confidence.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.orc_prefix_schedule.argtypes = [i32, i32, P, P, i32, i32, i32, P, P, P, P, P]
@@ -138,8 +138,9 @@ def residual_row(t, s, lse_d, T):
 
 
 # -------------------------------------------------------------- the stages
-def draft_markov(U, W1, W2t, x0, T, seed=0, rnd=0, req_ids=None, force_x=None):
-    """U [R][gamma][V]; W1, W2t [V][rank] or None; x0 [R]."""
+def draft_markov(U, W1, W2t, x0, T, seed=0, rnd=0, req_ids=None, force_x=None, own=False):
+    """U [R][gamma][V]; W1, W2t [V][rank] or None; x0 [R].  With own=True also
+    returns the oracle's own choice at every position given the forced prefix."""
     U = _f32(U)
     R, gamma, V = U.shape
     rank = 0 if W1 is None else int(W1.shape[1])
@@ -149,10 +150,13 @@ def draft_markov(U, W1, W2t, x0, T, seed=0, rnd=0, req_ids=None, force_x=None):
     lp = np.zeros((R, gamma))
     lse = np.zeros((R, gamma))
     mg = np.zeros((R, gamma))
+    xo = np.zeros((R, gamma + 1), np.int32) if own else None
     rc = lib().orc_draft_markov(R, gamma, V, rank, float(T), seed, rnd, _p(U), _p(W1c),
                                 _p(W2c), _p(x0), _p(_i32(req_ids)), _p(_i32(force_x)),
-                                _p(x), _p(lp), _p(lse), _p(mg))
+                                _p(x), _p(lp), _p(lse), _p(mg), _p(xo))
     assert rc == 0, rc
+    if own:
+        return x, lp, lse, mg, xo
     return x, lp, lse, mg
 
 

@@ -262,19 +262,22 @@ double orc_residual_row(int64_t V, double T, const float* t, const double* s, do
 //  x0     [R]            anchors
 //  req_ids[R] nullable   request index used in the random stream (default i)
 //  force_x[R][gamma+1]   nullable; entries >= 0 replace the sample (lock-step)
-// Out: x [R][gamma+1] (x[i][0] = anchor), logp_d, lse_d, margin [R][gamma].
+// Out: x [R][gamma+1] (x[i][0] = anchor), logp_d, lse_d, margin [R][gamma];
+//      x_own [R][gamma+1] nullable: the oracle's own choice at each position
+//      given the (possibly forced) prefix.
 // T > 0: x_k ~ softmax(s), s = (U_k + bias) / T, logp_d = s(x_k) - lse_d.
 // T == 0: x_k = first argmax of U_k + bias; logp_d = 0; lse_d = max score.
 int orc_draft_markov(int R, int gamma, int64_t V, int rank, double T, uint64_t seed,
                      uint64_t round, const float* U, const float* W1, const float* W2t,
                      const int32_t* x0, const int32_t* req_ids, const int32_t* force_x,
-                     int32_t* x, double* logp_d, double* lse_d, double* margin) {
+                     int32_t* x, double* logp_d, double* lse_d, double* margin, int32_t* x_own) {
     if (R < 0 || gamma < 1 || V < 1 || rank < 0 || !(T >= 0.0)) return 1;
     std::vector<double> s(V);
     for (int i = 0; i < R; ++i) {
         const uint32_t rid = req_ids ? (uint32_t)req_ids[i] : (uint32_t)i;
         int32_t prev = x0[i];
         x[(int64_t)i * (gamma + 1)] = prev;
+        if (x_own) x_own[(int64_t)i * (gamma + 1)] = prev;
         for (int k = 1; k <= gamma; ++k) {
             const float* Uk = U + ((int64_t)i * gamma + (k - 1)) * V;
             markov_scores(V, rank, Uk, W1, W2t, prev, s.data());
@@ -285,11 +288,13 @@ int orc_draft_markov(int R, int gamma, int64_t V, int rank, double T, uint64_t s
                 lse = logsumexp(s.data(), V);
                 xk = cgm_sample(s.data(), V, seed, round, TAG_DRAFT_CHUNK, TAG_DRAFT_ELEM,
                                 rid, (uint32_t)k, &mg);
+                if (x_own) x_own[(int64_t)i * (gamma + 1) + k] = (int32_t)xk;
                 if (force_x && force_x[(int64_t)i * (gamma + 1) + k] >= 0)
                     xk = force_x[(int64_t)i * (gamma + 1) + k];
                 lp = s[xk] - lse;
             } else {
                 xk = argmax_f32_decision(s.data(), V, &mg);
+                if (x_own) x_own[(int64_t)i * (gamma + 1) + k] = (int32_t)xk;
                 if (force_x && force_x[(int64_t)i * (gamma + 1) + k] >= 0)
                     xk = force_x[(int64_t)i * (gamma + 1) + k];
                 double mx = NEG_INF;

@@ -1,0 +1,146 @@
+"""Lock-step parity of a GPU round against the CPU oracle (test infrastructure).
+
+Used by tests/, __graft_entry__.smoke() and nothing in the product path.
+Every stage is checked on the inputs the GPU stage itself consumed (the GPU's
+own upstream outputs), so each stage is compared in isolation:
+
+  draft       oracle re-runs the chain forced onto the GPU's tokens and reports
+              its own choice at every position; a different choice is allowed
+              only where the oracle's decision margin is below MARGIN (flagged)
+  confidence  float32 relative error <= TOL_REL
+  schedule    ell, a, N, Theta bit-exact on the GPU's float32 confidences
+  pack        bit-exact
+  verify      m, tau, emitted, next anchor bit-exact, except requests whose
+              oracle margin is below MARGIN (flagged); log p_t within TOL_LOG
+  commit pack bit-exact
+Probabilities are compared in log space: |d log p| <= 1e-5 is a relative error
+of 1e-5 on p.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle as O
+
+MARGIN = 1e-5
+TOL_REL = 1e-5
+TOL_LOG = 1e-5
+
+
+@dataclass
+class Report:
+    compared: int = 0
+    flagged: int = 0
+    errors: list = field(default_factory=list)
+    max_err: dict = field(default_factory=dict)
+
+    def err(self, msg):
+        self.errors.append(msg)
+
+    def note(self, key, val):
+        self.max_err[key] = max(self.max_err.get(key, 0.0), float(val))
+
+    def ok(self):
+        return not self.errors and self.flagged <= 0.001 * max(self.compared, 1) + 1
+
+    def summary(self):
+        return (f"compared={self.compared} flagged={self.flagged} errors={len(self.errors)} "
+                f"max_err={ {k: float(f'{v:.3g}') for k, v in self.max_err.items()} }"
+                + ("" if not self.errors else "\n  " + "\n  ".join(self.errors[:20])))
+
+
+def f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def check_draft(rep, U, W1, W2t, x0, T, seed, rnd, dev_x, dev_lp, dev_lse, reqs):
+    xo_f, lp, lse, mg, own = O.draft_markov(U, W1, W2t, x0, T, seed, rnd, req_ids=reqs,
+                                            force_x=dev_x, own=True)
+    g = dev_x.shape[1] - 1
+    diff = own[:, 1:] != dev_x[:, 1:]
+    rep.compared += diff.size
+    bad = diff & (mg >= MARGIN)
+    rep.flagged += int((diff & (mg < MARGIN)).sum())
+    for r, k in zip(*np.nonzero(bad)):
+        rep.err(f"draft req {reqs[r] if reqs is not None else r} pos {k + 1}: gpu {dev_x[r, k + 1]} "
+                f"oracle {own[r, k + 1]} margin {mg[r, k]:.3g}")
+    if (dev_x[:, 0] != np.asarray(x0)).any():
+        rep.err("draft: x[:, 0] is not the anchor")
+    e_lp = np.abs(dev_lp.astype(np.float64) - lp)
+    e_lse = np.abs(dev_lse.astype(np.float64) - lse)
+    rep.note("logp_d", e_lp.max())
+    rep.note("lse_d", e_lse.max())
+    if T > 0:
+        if e_lp.max() > TOL_LOG:
+            rep.err(f"draft logp_d max err {e_lp.max():.3g}")
+        if (e_lse / np.maximum(1.0, np.abs(lse))).max() > TOL_LOG:
+            rep.err(f"draft lse_d max err {e_lse.max():.3g}")
+    else:
+        if e_lse.max() > 1e-5 * max(1.0, np.abs(lse).max()):
+            rep.err(f"greedy lse_d (max score) err {e_lse.max():.3g}")
+    return lp, lse
+
+
+def check_confidence(rep, h, W1, w, dev_x, dev_c, sts=None):
+    c, _ = O.confidence(h, W1, w, dev_x, sts)
+    rel = np.abs(dev_c.astype(np.float64) - c) / np.maximum(np.abs(c.astype(np.float64)), 1e-30)
+    rep.note("c_rel", rel.max())
+    rep.compared += c.size
+    if rel.max() > TOL_REL:
+        rep.err(f"confidence max rel err {rel.max():.3g}")
+
+
+def check_schedule(rep, dev_c, sps, enabled, dev_ell, dev_a, dev_N, dev_theta):
+    ell, a, N, th, _ = O.prefix_schedule(dev_c, sps, enabled=enabled)
+    rep.compared += ell.size
+    if not np.array_equal(ell, dev_ell):
+        bad = np.nonzero(ell != dev_ell)[0]
+        rep.err(f"schedule ell differs at {bad[:10]} (gpu {dev_ell[bad[:10]]} oracle {ell[bad[:10]]})")
+    if dev_a is not None and not np.array_equal(a.view(np.uint32), f32(dev_a).view(np.uint32)):
+        rep.err("schedule survival products a differ")
+    if dev_N is not None and int(dev_N) != N:
+        rep.err(f"schedule N gpu {int(dev_N)} oracle {N}")
+    if dev_theta is not None and float(dev_theta) != th:
+        rep.err(f"schedule Theta gpu {float(dev_theta)!r} oracle {th!r}")
+    return ell
+
+
+def check_pack(rep, rows, lens, dev_cu, dev_flat, dev_mr, dev_mp, dev_N, what):
+    cu, flat, mr, mp, N = O.pack(rows, lens)
+    ok = np.array_equal(cu, dev_cu) and np.array_equal(flat, dev_flat) and int(dev_N) == N
+    if dev_mr is not None:
+        ok = ok and np.array_equal(mr, dev_mr) and np.array_equal(mp, dev_mp)
+    if not ok:
+        rep.err(f"pack ({what}) differs")
+    return cu
+
+
+def check_verify(rep, ell, cu, target, layout, x, dev_lp, dev_lse, U, W1, W2t, T, seed, rnd,
+                 dev_m, dev_tau, dev_em, dev_na, dev_lpt, reqs, full_R=None):
+    """reqs: request ids of the rows given (None: all); cu / target in the
+    layout the GPU consumed (for a subset, pass dense rows of the subset)."""
+    m, tau, em, na, lpt, mg = O.verify(ell, cu, target, layout, x, dev_lp.astype(np.float64),
+                                       dev_lse.astype(np.float64), U, W1, W2t, T, seed, rnd,
+                                       req_ids=reqs)
+    R = ell.size
+    rep.compared += R
+    for r in range(R):
+        same = (m[r] == dev_m[r] and tau[r] == dev_tau[r] and na[r] == dev_na[r]
+                and np.array_equal(em[r], dev_em[r]))
+        if not same:
+            if mg[r] < MARGIN:
+                rep.flagged += 1
+            else:
+                rid = reqs[r] if reqs is not None else r
+                rep.err(f"verify req {rid}: gpu m={dev_m[r]} y={dev_na[r]} oracle m={m[r]} "
+                        f"y={na[r]} margin {mg[r]:.3g}")
+    if T > 0 and dev_lpt is not None:
+        mask = np.arange(x.shape[1] - 1)[None, :] < ell[:, None]
+        e = np.abs(dev_lpt.astype(np.float64) - lpt)[mask]
+        if e.size:
+            rep.note("logp_t", e.max())
+            if e.max() > TOL_LOG:
+                rep.err(f"verify logp_t max err {e.max():.3g}")
+    return m, tau, em, na

@@ -1,0 +1,116 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every entry point
+declared in include/dspark.h, sizes its workspace, and rejects bad arguments
+on the host before touching a GPU (no compute call is made here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import draft_verify_sampling_head_amd as D
+from draft_verify_sampling_head_amd import _lib as L
+from draft_verify_sampling_head_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = C.c_void_p(0x100000)      # never dereferenced: every call below fails validation first
+
+
+def declared():
+    src = open(os.path.join(ROOT, "include", "dspark.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = L.load()
+    names = declared()
+    assert len(names) >= 10
+    for nm in names:
+        assert hasattr(lib, nm), nm
+    assert set(L.EXPORTS) == set(names)
+
+
+def test_workspace_and_strings():
+    assert D.workspace_bytes(0, 1, 1) >= 256
+    assert D.workspace_bytes(256, 16, 129280) > 256 * 1010 * 8
+    assert D.workspace_bytes(-1, 1, 1) == 0
+    lib = L.load()
+    for code, name in L.STATUS.items():
+        assert lib.dspark_status_string(code).decode() == name
+    assert "gfx950" in D._lib.version()
+
+
+def _draft(R=4, g=7, V=100, r=0, T=1.0, U=FAKE, W1=None, W2t=None, x0=FAKE, x=FAKE, lp=FAKE,
+           lse=FAKE, ws=FAKE, ws_bytes=1 << 30, udt=0, wdt=0):
+    return L.load().dspark_draft_markov(R, g, V, r, T, 0, 0, U, udt, W1, W2t, wdt, x0, x, lp, lse,
+                                        None, ws, ws_bytes, None)
+
+
+def test_draft_argument_checks():
+    assert _draft(R=-1) == INVALID
+    assert _draft(g=0) == INVALID
+    assert _draft(g=33) == UNSUPPORTED
+    assert _draft(V=0) == INVALID
+    assert _draft(r=-16) == INVALID
+    assert _draft(r=8) == UNSUPPORTED
+    assert _draft(r=528) == UNSUPPORTED
+    assert _draft(T=-0.5) == INVALID
+    assert _draft(T=float("inf")) == INVALID
+    assert _draft(T=float("nan")) == INVALID
+    assert _draft(U=None) == INVALID
+    assert _draft(r=16) == INVALID                      # rank > 0 needs W1 and W2t
+    assert _draft(r=16, W1=C.c_void_p(0x100008), W2t=FAKE) == UNSUPPORTED   # misaligned weights
+    assert _draft(ws_bytes=100) == WORKSPACE
+    assert _draft(udt=7) == INVALID
+    assert _draft(R=0, U=None, x0=None, x=None, lp=None, lse=None, ws=None) == OK  # empty batch
+
+
+def test_confidence_schedule_pack_verify_checks():
+    lib = L.load()
+    conf = lambda R=2, g=3, d=8, r=0, V=10, h=FAKE, w=FAKE, x=FAKE, c=FAKE: lib.dspark_confidence(
+        R, g, d, r, V, h, 0, None, 0, w, 0, None, x, c, None)
+    assert conf(d=0) == INVALID
+    assert conf(g=40) == UNSUPPORTED
+    assert conf(r=16) == INVALID                         # W1 missing
+    assert conf(h=None) == INVALID
+    assert conf(R=0, h=None) == OK
+    sched = lambda R=4, g=4, c=FAKE, sps=FAKE, N_max=100, ell=FAKE: lib.dspark_prefix_schedule(
+        R, g, c, sps, N_max, 1, ell, None, None, None, None)
+    assert sched(R=-2) == INVALID
+    assert sched(N_max=3) == INVALID                     # N_max < R
+    assert sched(R=1024, g=17, N_max=10**6) == UNSUPPORTED   # R * gamma > 16384
+    assert sched(c=None) == INVALID
+    pack = lambda R=4, width=3, rows=FAKE, ln=FAKE, cu=FAKE, flat=FAKE: lib.dspark_pack(
+        R, width, rows, ln, 0, cu, flat, None, None, None, None, 0, None)
+    assert pack(width=0) == INVALID
+    assert pack(rows=None) == INVALID
+    assert pack(R=1 << 20, width=1 << 12) == UNSUPPORTED
+    ver = lambda layout=1, tdt=1, udt=1, T=1.0, ws_bytes=1 << 30, ell=FAKE: lib.dspark_verify(
+        4, 3, 100, 0, T, 0, 0, ell, FAKE, FAKE, tdt, layout, FAKE, FAKE, FAKE, FAKE, udt, None,
+        None, 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_bytes, None)
+    assert ver(layout=2) == INVALID
+    assert ver(tdt=0, udt=1) == UNSUPPORTED
+    assert ver(T=-1.0) == INVALID
+    assert ver(ws_bytes=10) == WORKSPACE
+    assert ver(ell=None) == INVALID
+
+
+def test_synthetic_configs_shapes():
+    for idx in range(4):
+        cfg = synth.config(idx)
+        assert cfg.R * cfg.gamma <= 16384 and cfg.rank % 16 == 0
+    c4 = synth.config(4, R=512, gamma=16, rank=0)
+    assert c4.V == synth.VOCAB_DEEPSEEK and c4.rank == 0
+    small = synth.scaled(synth.config(3), R=10, gamma=4, V=300, d=16)
+    inp = synth.make_inputs(small, device="cpu")
+    assert inp["U"].shape == (10, 4, 300) and inp["target"].shape == (10, 5, 300)
+    assert int(inp["hard"].sum()) == 3
+    sps = synth.sps_table(synth.config(3), 3000)
+    assert sps[0] == sps[31] and sps[2049] == 0 and (sps[32:2049].diff() <= 0).all()
+
+
+@pytest.mark.parametrize("fn", ["draft_markov", "confidence", "prefix_schedule", "pack", "verify"])
+def test_binding_names_match_abi(fn):
+    assert callable(getattr(D, fn))
+    assert f"dspark_{fn}" in declared()

@@ -1,0 +1,265 @@
+"""GPU parity: every stage of the round through the C ABI against the oracle.
+
+Small cases span several chunks, several 32-row MFMA tiles and ragged tails
+(vocabularies that are not multiples of the 128-entry chunk, of 8, or below
+one chunk; row counts that are not multiples of 32).  Full-size cases run the
+benchmark's configurations and check a sample of requests one by one plus the
+whole schedule and both packs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import draft_verify_sampling_head_amd as D
+from draft_verify_sampling_head_amd import round as RD
+from draft_verify_sampling_head_amd import synth
+from oracle import parity as PC
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def n(t):
+    return t.detach().cpu().numpy()
+
+
+def f(t):
+    return None if t is None else t.detach().float().cpu().numpy()
+
+
+def to_dev(inp):
+    return {k: (v.to(DEV) if torch.is_tensor(v) and k != "hard" else v) for k, v in inp.items()}
+
+
+def run_and_check(cfg, inp_cpu=None, layout=1, rnd=0, reqs=None, inp_dev=None, sts=None):
+    """Run a full round on the GPU; check all stages (on `reqs` if given)."""
+    print(f"[case] {cfg.name} R={cfg.R} g={cfg.gamma} V={cfg.V} r={cfg.rank} T={cfg.T} "
+          f"layout={layout} reqs={None if reqs is None else list(reqs)}", flush=True)
+    if inp_dev is None:
+        inp_dev = to_dev(inp_cpu)
+    g = dict(inp_dev)
+    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV)
+    if layout == 0:
+        # the target model would produce rows in verify order: run the first
+        # four stages, gather the packed target rows, then verify
+        RD.run_round(g, buf, cfg.T, cfg.philox_seed, rnd, scheduler=cfg.scheduler, layout=1,
+                     sts_T=sts)
+        torch.cuda.synchronize()
+        N = int(n(buf.N)[0])
+        packed = g["target"][buf.marker_req[:N].long(), buf.marker_pos[:N].long()].contiguous()
+        g["target"] = packed
+        RD.run_round(g, buf, cfg.T, cfg.philox_seed, rnd, scheduler=cfg.scheduler, layout=0,
+                     sts_T=sts)
+    else:
+        RD.run_round(g, buf, cfg.T, cfg.philox_seed, rnd, scheduler=cfg.scheduler, layout=1,
+                     sts_T=sts)
+    torch.cuda.synchronize()
+    status = D.get_status(buf.ws)
+    rep = PC.Report()
+    sel = slice(None) if reqs is None else np.asarray(reqs)
+    src = inp_cpu if inp_cpu is not None else None
+
+    def host(key, rows=True):
+        t = (src[key] if src is not None else inp_dev[key])
+        if t is None:
+            return None
+        if rows and reqs is not None:
+            t = t[torch.as_tensor(np.asarray(reqs), device=t.device)]
+        return f(t) if t.is_floating_point() else n(t)
+
+    U, tgt, h = host("U"), host("target"), host("h")
+    W1, W2t, w = host("W1", False), host("W2t", False), host("w", False)
+    x0 = host("x0")
+    x = n(buf.x)[sel]
+    rq = None if reqs is None else np.asarray(reqs, np.int32)
+    PC.check_draft(rep, U, W1, W2t, x0, cfg.T, cfg.philox_seed, rnd, x, n(buf.logp_d)[sel],
+                   n(buf.lse_d)[sel], rq)
+    stsn = None if sts is None else n(sts)
+    PC.check_confidence(rep, h, W1, w, x, n(buf.c)[sel], stsn)
+    PC.check_schedule(rep, n(buf.c), n(inp_dev["sps"]), cfg.scheduler, n(buf.ell), n(buf.a),
+                      n(buf.N)[0], n(buf.theta)[0])
+    PC.check_pack(rep, n(buf.x), n(buf.ell) + 1, n(buf.cu), n(buf.flat), n(buf.marker_req),
+                  n(buf.marker_pos), n(buf.N)[0], "verify batch")
+    PC.check_verify(rep, n(buf.ell)[sel], None, tgt, 1, x, n(buf.logp_d)[sel], n(buf.lse_d)[sel],
+                    U, W1, W2t, cfg.T, cfg.philox_seed, rnd, n(buf.m)[sel], n(buf.tau)[sel],
+                    n(buf.emitted)[sel], n(buf.next_anchor)[sel], n(buf.logp_t)[sel], rq)
+    PC.check_pack(rep, n(buf.emitted), n(buf.tau), n(buf.cu_out), n(buf.flat_out), None, None,
+                  n(buf.N_out)[0], "emitted")
+    print(f"  {rep.summary()} status={status} sum_ell={int(n(buf.ell).sum())} "
+          f"sum_m={int(n(buf.m).sum())}", flush=True)
+    assert status == 0, f"device flags {status}"
+    assert rep.ok(), rep.summary()
+    return buf, rep
+
+
+# ------------------------------------------------------------- small cases
+SMALL = [
+    # (base config, overrides)
+    (0, {}),                                                            # config 0 itself
+    (2, dict(R=40, gamma=5, V=3000, d=256)),                             # bf16, rank 256
+    (2, dict(R=33, gamma=4, V=2000, d=64, rank=64)),
+    (2, dict(R=9, gamma=3, V=1500, d=64, rank=16)),
+    (2, dict(R=37, gamma=6, V=2600, d=64, rank=0)),                      # DFlash case
+    (2, dict(R=35, gamma=4, V=2000, d=64, rank=512)),
+    (1, dict(R=33, gamma=7, V=5000, d=128)),                             # greedy, no scheduler
+    (1, dict(R=20, gamma=5, V=3001, d=96, rank=0)),
+    (3, dict(R=70, gamma=6, V=2500, d=64)),                              # T = 0.7, hard/easy mix
+    (2, dict(R=5, gamma=3, V=100, d=32)),                                # one chunk
+    (2, dict(R=6, gamma=4, V=1001, d=40, rank=32)),                      # rows not 16-byte aligned
+    (2, dict(R=1, gamma=1, V=700, d=16)),
+    (2, dict(R=12, gamma=32, V=900, d=32, rank=32)),                     # longest block
+    (2, dict(R=24, gamma=4, V=1800, d=64, T=0.3)),
+    (2, dict(R=24, gamma=4, V=1800, d=64, T=2.0, scheduler=False)),
+]
+
+
+@pytest.mark.parametrize("base,over", SMALL, ids=[f"cfg{b}-{i}" for i, (b, _) in enumerate(SMALL)])
+def test_small_round_parity(base, over):
+    cfg = synth.scaled(synth.config(base), **over) if over else synth.config(base)
+    inp = synth.make_inputs(cfg, device="cpu")
+    run_and_check(cfg, inp)
+
+
+def test_packed_target_layout():
+    cfg = synth.scaled(synth.config(2), R=30, gamma=5, V=2100, d=64)
+    inp = synth.make_inputs(cfg, device="cpu")
+    run_and_check(cfg, inp, layout=0)
+
+
+def test_fp32_logits_bf16_weights():
+    cfg = synth.scaled(synth.config(2), R=34, gamma=4, V=1900, d=64)
+    inp = synth.make_inputs(cfg, device="cpu")
+    inp["U"] = inp["U"].float()
+    inp["target"] = inp["target"].float()
+    inp["h"] = inp["h"].float()
+    run_and_check(cfg, inp)
+
+
+def test_sts_temperatures_and_rounds():
+    cfg = synth.scaled(synth.config(2), R=16, gamma=4, V=1300, d=64)
+    inp = synth.make_inputs(cfg, device="cpu")
+    sts = torch.tensor([1.0, 1.5, 0.7, 2.0], dtype=torch.float32, device=DEV)
+    b1, _ = run_and_check(cfg, inp, rnd=5, sts=sts)
+    b2, _ = run_and_check(cfg, inp, rnd=6, sts=sts)
+    assert not torch.equal(b1.x, b2.x)   # the round counter changes the stream
+
+
+def test_determinism_bitwise():
+    cfg = synth.scaled(synth.config(2), R=64, gamma=6, V=4000, d=64)
+    inp = to_dev(synth.make_inputs(cfg, device="cpu"))
+    outs = []
+    for _ in range(2):
+        buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV)
+        RD.run_round(inp, buf, cfg.T, 0, 0, scheduler=True)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (buf.x, buf.logp_d, buf.lse_d, buf.c, buf.ell, buf.m,
+                                           buf.emitted, buf.flat_out)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_nonfinite_logits_are_flagged():
+    cfg = synth.scaled(synth.config(2), R=4, gamma=2, V=600, d=16)
+    inp = to_dev(synth.make_inputs(cfg, device="cpu"))
+    inp["U"][1, 0, 77] = float("nan")
+    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV)
+    D.clear_status(buf.ws)
+    RD.run_round(inp, buf, cfg.T, 0, 0)
+    torch.cuda.synchronize()
+    assert D.get_status(buf.ws) & D._lib.FLAG_NONFINITE
+
+
+# -------------------------------------------------------- stage: scheduler
+def _sched_case(c, sps, enabled=True, N_max=None):
+    R, g = c.shape
+    cd = torch.as_tensor(c, device=DEV)
+    spsd = torch.as_tensor(sps, device=DEV)
+    ell = torch.empty(R, dtype=torch.int32, device=DEV)
+    a = torch.empty(R, g, dtype=torch.float32, device=DEV)
+    N = torch.empty(1, dtype=torch.int32, device=DEV)
+    th = torch.empty(1, dtype=torch.float64, device=DEV)
+    D.prefix_schedule(cd, spsd, ell, enabled=enabled, N_max=N_max, a=a, N_out=N, theta_best=th)
+    torch.cuda.synchronize()
+    import oracle as O
+    e, ao, No, tho, _ = O.prefix_schedule(c, sps, N_max=N_max, enabled=enabled)
+    np.testing.assert_array_equal(n(ell), e)
+    np.testing.assert_array_equal(n(a).view(np.uint32), ao.view(np.uint32))
+    assert int(n(N)[0]) == No
+    assert float(n(th)[0]) == tho
+
+
+def test_scheduler_bitexact_random_and_ties():
+    rng = np.random.default_rng(0)
+    for it in range(40):
+        R, g = int(rng.integers(1, 300)), int(rng.integers(1, 33))
+        if R * g > 16384:
+            continue
+        c = rng.uniform(0, 1, (R, g)).astype(np.float32)
+        if it % 3 == 0:
+            c = rng.choice(np.array([0, 0.25, 0.5, 0.75, 1.0], np.float32), (R, g))
+        if it % 5 == 0:
+            c[:, :] = 1.0
+        B = np.arange(R * (g + 1) + 1, dtype=np.float64)
+        sps = [1.0 / (0.020 + 5e-5 * B), 1.0 / (0.02 + 0.002 * B),
+               1.0 / (0.015 + 4e-5 * B + 0.003 * (B // 7))][it % 3]
+        _sched_case(c, sps, N_max=None if it % 4 else int(rng.integers(R, R * (g + 1) + 1)))
+        _sched_case(c, sps, enabled=False)
+
+
+def test_scheduler_stress_size():
+    # 1024 requests x 15 positions with the tabulated, stepped SPS curve
+    cfg = synth.config(3)
+    rng = np.random.default_rng(3)
+    z = rng.normal(0, 3.2, (cfg.R, cfg.gamma))
+    c = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+    sps = synth.sps_table(cfg, cfg.R * (cfg.gamma + 1)).numpy()
+    _sched_case(c, sps)
+    c2 = rng.uniform(0.97, 1.0, (1024, 16)).astype(np.float32)
+    B = np.arange(1024 * 17 + 1, dtype=np.float64)
+    _sched_case(c2, 1.0 / (0.020 + 5e-6 * B))
+
+
+# ------------------------------------------------------------- stage: pack
+def test_pack_bitexact():
+    import oracle as O
+    rng = np.random.default_rng(1)
+    for R, width, off in [(1, 1, 0), (3000, 17, 1), (1025, 9, 0), (64, 33, 1)]:
+        rows = rng.integers(0, 100000, (R, width)).astype(np.int32)
+        lens = rng.integers(0, width + 1 - off, R).astype(np.int32)
+        rd, ld = torch.as_tensor(rows, device=DEV), torch.as_tensor(lens, device=DEV)
+        cu = torch.empty(R + 1, dtype=torch.int32, device=DEV)
+        flat = torch.empty(R * width, dtype=torch.int32, device=DEV)
+        mr, mp = torch.empty_like(flat), torch.empty_like(flat)
+        N = torch.empty(1, dtype=torch.int32, device=DEV)
+        D.pack(rd, ld, off, cu, flat, mr, mp, N)
+        torch.cuda.synchronize()
+        e = O.pack(rows, lens + off)
+        np.testing.assert_array_equal(n(cu), e[0])
+        np.testing.assert_array_equal(n(flat), e[1])
+        np.testing.assert_array_equal(n(mr), e[2])
+        np.testing.assert_array_equal(n(mp), e[3])
+        assert int(n(N)[0]) == e[4]
+
+
+# --------------------------------------------------------- full-size cases
+def _full(idx, reqs, **cell):
+    cfg = synth.config(idx, **cell)
+    inp = synth.make_inputs(cfg, device=DEV)
+    run_and_check(cfg, None, inp_dev=inp, reqs=reqs)
+
+
+def test_full_config2_sampled():
+    _full(2, [0, 131, 255])
+
+
+def test_full_config1_sampled():
+    _full(1, [0, 17, 63])
+
+
+def test_full_config3_sampled():
+    _full(3, [5, 600, 1023])
+
+
+@pytest.mark.parametrize("R,gamma,rank", [(1, 16, 256), (32, 4, 64), (512, 8, 0)])
+def test_full_config4_cells_sampled(R, gamma, rank):
+    _full(4, [0, R - 1] if R > 1 else [0], R=R, gamma=gamma, rank=rank)
