@@ -98,8 +98,9 @@ def workspace_bytes(R, gamma, V, r=0, d=0):
 
 
 def workspace(R, gamma, V, device="cuda"):
-    """Allocate a workspace tensor (uint8) of the size the library asks for."""
-    return torch.empty(max(256, workspace_bytes(R, gamma, V)), dtype=torch.uint8, device=device)
+    """Allocate a zeroed workspace tensor (uint8) of the size the library asks
+    for (the status word in its header must start at zero)."""
+    return torch.zeros(max(256, workspace_bytes(R, gamma, V)), dtype=torch.uint8, device=device)
 
 
 def version():

@@ -27,7 +27,7 @@ struct DraftPickArgs {
   float* logp_d;
   float* lse_d;
   float* margin;
-  const float* L;           // [R][nch] chunk log-masses (sample) or maxima (greedy)
+  const float2* L;          // [R][nch] chunk (max, scaled sum) or (max, -) when greedy
   const int* I;             // [R][nch] chunk argmax (greedy)
   uint32_t* status;
 };
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(64) void k_draft_pick(DraftPickArgs a) {
   const int k = a.k;
   const int64_t xo = (int64_t)i * (a.gamma + 1);
   const int prev = (k == 1) ? a.x0[i] : a.x[xo + k - 1];
-  const float* Lr = a.L + (int64_t)i * a.nch;
+  const float2* Lr = a.L + (int64_t)i * a.nch;
   int xk;
   float logp, lse, gap = INFINITY;
   if (GREEDY) {
@@ -49,10 +49,11 @@ __global__ __launch_bounds__(64) void k_draft_pick(DraftPickArgs a) {
     logp = 0.f;
     if (xk < 0 || xk >= a.V) { set_flag(a.status, kFlagNonFinite); xk = 0; }
   } else {
-    lse = lse_chunks(Lr, a.nch);
+    const RowNorm rn = row_norm(Lr, a.nch, a.invT);
+    lse = rn.m * a.invT + rn.lse_rel;
     const bool want_gap = a.margin != nullptr;
-    const PickResult pc = pick_chunk(Lr, a.nch, a.seed, a.round, kTagDraftChunk, (uint32_t)i,
-                                     (uint32_t)k, want_gap);
+    const PickResult pc = pick_chunk(Lr, a.nch, rn.m, a.invT, a.seed, a.round, kTagDraftChunk,
+                                     (uint32_t)i, (uint32_t)k, want_gap);
     int c = pc.idx;
     if (c < 0) { set_flag(a.status, kFlagNonFinite); c = 0; }
     const int base = c * kChunk;
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(64) void k_draft_pick(DraftPickArgs a) {
       if (v < a.V) {
         const float b = a.rank > 0 ? markov_bias(erow, reinterpret_cast<const WT*>(a.W2t), a.rank, v)
                                    : 0.f;
-        s[h] = (Elem<UT>::get(urow, v) + b) * a.invT;
+        s[h] = (Elem<UT>::get(urow, v) + b - rn.m) * a.invT;     // relative to the row maximum
       }
     }
     const PickResult pe = pick_in_chunk(s[0], s[1], base, a.seed, a.round, kTagDraftElem,
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(64) void k_draft_pick(DraftPickArgs a) {
     const int off = xk - base;
     const float sx0 = __shfl(s[0], off & 63);
     const float sx1 = __shfl(s[1], off & 63);
-    logp = ((off >= 64) ? sx1 : sx0) - lse;
+    logp = ((off >= 64) ? sx1 : sx0) - rn.lse_rel;
     gap = fminf(pc.gap, pe.gap);
   }
   if (lane == 0) {
@@ -97,7 +98,7 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
   const WsLayout L = ws_layout(R, gamma, V);
   char* w = reinterpret_cast<char*>(ws);
   uint32_t* status = reinterpret_cast<uint32_t*>(w + L.header);
-  float* Lc = reinterpret_cast<float*>(w + L.draft_l);
+  float2* Lc = reinterpret_cast<float2*>(w + L.draft_l);
   int* Ic = reinterpret_cast<int*>(w + L.draft_i);
   const int nch = (V + kChunk - 1) / kChunk;
   const bool greedy = (T == 0.f);
@@ -110,14 +111,14 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     if (rank == 0) {
       RowStatsArgs a{};
       a.base = U; a.kind = kRowsDraft; a.R = R; a.gamma = gamma; a.k = k; a.V = V; a.nch = nch;
-      a.nrows_cap = R; a.scale2 = scale2; a.vec_ok = u_vec; a.L = Lc; a.M = Lc; a.I = Ic;
+      a.nrows_cap = R; a.scale2 = scale2; a.vec_ok = u_vec; a.L = Lc; a.I = Ic;
       a.status = status;
       e = launch_row_stats(a, u_bf16, greedy, st);
     } else {
       MarkovArgs a{};
       a.R = R; a.gamma = gamma; a.k = k; a.V = V; a.rank = rank; a.nch = nch; a.nrows_cap = R;
       a.U = U; a.W1v = W1; a.W2tv = W2t; a.x0 = x0; a.x = x; a.scale2 = scale2; a.u_vec_ok = u_vec;
-      a.L = Lc; a.M = Lc; a.I = Ic; a.status = status;
+      a.L = Lc; a.I = Ic; a.status = status;
       e = launch_markov_stats(a, u_bf16, w_bf16, greedy ? kModeGreedy : kModeSample, st);
     }
     if (e != hipSuccess) return e;

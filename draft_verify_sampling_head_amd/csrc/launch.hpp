@@ -19,8 +19,7 @@ struct RowStatsArgs {
   int nrows_cap;           // draft: R; verify: R*(gamma+1)
   float scale2;            // log2(e) / T (sampling) -- unused for greedy
   bool vec_ok;             // rows are 16-byte aligned
-  float* L;                // [row][nch] log-masses (sample) or maxima (greedy)
-  float* M;
+  float2* L;               // [row][nch] (raw max M_c, sum exp((x - M_c)/T)); greedy: (M_c, -)
   int* I;                  // [row][nch] argmax (greedy)
   uint32_t* status;
   uint32_t* zero_me;       // nullable: cleared by the first thread (work counter)
@@ -39,14 +38,13 @@ struct MarkovArgs {
   const int32_t* x;        // [R][gamma+1]
   float scale2;
   bool u_vec_ok;
-  float* L;
-  float* M;
+  float2* L;               // [row][nch] as RowStatsArgs; residual: (0, sum max(0, p_t - p_d))
   int* I;
   // residual rows
   const int32_t* rej_count;
-  const int4* rej;         // (request, position k, target row, -)
+  const int4* rej;         // (request, position k, target row, verify row)
   const void* target;
-  const float* lse_t;
+  const float2* lse_t;     // [verify row] (raw max, log-normaliser relative to it)
   const float* lse_d;
   uint32_t* status;
   // filled by the launcher

@@ -18,16 +18,42 @@ struct PickResult {
   float gap;     // best minus second-best key (only when asked for)
 };
 
-// Chunk-level Gumbel pick over L[0..nch) (natural-log chunk masses; -inf =
-// no mass).  One wave; lane l handles chunk blocks of four, one Philox block
-// per four chunks.
-__device__ inline PickResult pick_chunk(const float* L, int nch, uint64_t seed, uint64_t round,
-                                        uint32_t tag, uint32_t req, uint32_t k, bool want_gap) {
+// Per-chunk statistics are (M_c, S_c): M_c the raw maximum of the row's scores
+// x over chunk c (before the temperature), S_c = sum_{v in c} exp((x_v - M_c)/T).
+// Chunk log-mass L_c = M_c/T + log S_c.  Everything below is kept relative to
+// the row maximum m, so log-probabilities stay accurate when x/T is large.
+struct RowNorm {
+  float m;        // raw row maximum (-inf: no mass)
+  float lse_rel;  // log sum_c S_c exp((M_c - m)/T)   (normaliser = m/T + lse_rel)
+};
+
+__device__ inline RowNorm row_norm(const float2* st, int nch, float invT) {
+  const int lane = threadIdx.x & 63;
+  float m = -INFINITY;
+  for (int c = lane; c < nch; c += 64) m = fmaxf(m, st[c].x);
+  m = wave_max(m);
+  if (m == -INFINITY) return RowNorm{-INFINITY, -INFINITY};
+  float s = 0.f;
+  for (int c = lane; c < nch; c += 64) {
+    const float2 v = st[c];
+    if (v.y > 0.f) s += v.y * expf((v.x - m) * invT);
+  }
+  s = wave_sum(s);
+  return RowNorm{m, s > 0.f ? logf(s) : -INFINITY};
+}
+
+// Chunk-level Gumbel pick: key_c = (M_c - m)/T + log S_c + G_c (chunks with
+// S_c == 0 carry no mass).  One wave; lane l handles chunk blocks of four,
+// one Philox block per four chunks.
+__device__ inline PickResult pick_chunk(const float2* st, int nch, float m, float invT,
+                                        uint64_t seed, uint64_t round, uint32_t tag, uint32_t req,
+                                        uint32_t k, bool want_gap) {
   const int lane = threadIdx.x & 63;
   PickResult r{-1, -INFINITY, INFINITY};
   if (nch == 1) {
-    r.idx = (L[0] == -INFINITY) ? -1 : 0;
-    r.key = L[0];
+    const float2 v = st[0];
+    r.idx = (v.y > 0.f) ? 0 : -1;
+    r.key = (v.y > 0.f) ? (v.x - m) * invT + logf(v.y) : -INFINITY;
     return r;
   }
   float best = -INFINITY;
@@ -38,9 +64,9 @@ __device__ inline PickResult pick_chunk(const float* L, int nch, uint64_t seed, 
     for (int w = 0; w < 4; ++w) {
       const int c = b * 4 + w;
       if (c < nch) {
-        const float l = L[c];
-        if (l != -INFINITY) {
-          const float key = l + gumbel_of(word_of(blk, (uint32_t)w));
+        const float2 v = st[c];
+        if (v.y > 0.f) {
+          const float key = (v.x - m) * invT + logf(v.y) + gumbel_of(word_of(blk, (uint32_t)w));
           argmax_merge(best, bi, key, c);
         }
       }
@@ -56,8 +82,11 @@ __device__ inline PickResult pick_chunk(const float* L, int nch, uint64_t seed, 
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const int c = b * 4 + w;
-        if (c < nch && c != r.idx && L[c] != -INFINITY)
-          second = fmaxf(second, L[c] + gumbel_of(word_of(blk, (uint32_t)w)));
+        if (c < nch && c != r.idx) {
+          const float2 v = st[c];
+          if (v.y > 0.f)
+            second = fmaxf(second, (v.x - m) * invT + logf(v.y) + gumbel_of(word_of(blk, (uint32_t)w)));
+        }
       }
     }
     r.gap = best - wave_max(second);
@@ -91,26 +120,13 @@ __device__ inline PickResult pick_in_chunk(float s0, float s1, int base, uint64_
   return r;
 }
 
-// Lowest-index argmax over per-chunk maxima M / argmaxes I (greedy).
-__device__ inline void argmax_chunks(const float* M, const int* I, int nch, float& v, int& idx) {
+// Lowest-index argmax over per-chunk maxima (st[c].x) / argmaxes I (greedy).
+__device__ inline void argmax_chunks(const float2* st, const int* I, int nch, float& v, int& idx) {
   const int lane = threadIdx.x & 63;
   v = -INFINITY;
   idx = 0x7FFFFFFF;
-  for (int c = lane; c < nch; c += 64) argmax_merge(v, idx, M[c], I[c]);
+  for (int c = lane; c < nch; c += 64) argmax_merge(v, idx, st[c].x, I[c]);
   wave_argmax(v, idx);
-}
-
-// ln sum_c exp(L_c) over a row of chunk log-masses (one wave).
-__device__ inline float lse_chunks(const float* L, int nch) {
-  const int lane = threadIdx.x & 63;
-  float m = -INFINITY;
-  for (int c = lane; c < nch; c += 64) m = fmaxf(m, L[c]);
-  m = wave_max(m);
-  if (m == -INFINITY) return -INFINITY;
-  float s = 0.f;
-  for (int c = lane; c < nch; c += 64) s += expf(L[c] - m);
-  s = wave_sum(s);
-  return m + logf(s);
 }
 
 // Markov bias W1[prev] . W2t[v] for one vocabulary entry: float32 FMA chain in

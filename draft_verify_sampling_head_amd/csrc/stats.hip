@@ -2,9 +2,10 @@
 //
 // Every sampler and every normaliser of the round works on per-chunk
 // summaries of a vocabulary row (kChunk = 128 consecutive entries):
-//   SAMPLE : L_c = ln sum_{v in c} exp(score_v)          (chunk log-mass)
-//   GREEDY : M_c = max_{v in c} score_v, I_c = its lowest argmax
-//   RESID  : L_c = ln sum_{v in c} max(0, p_t(v) - p_d(v))  (residual mass)
+//   SAMPLE : (M_c, S_c) = (max_{v in c} x_v, sum_{v in c} exp((x_v - M_c)/T)),
+//            x the raw score; the chunk log-mass is M_c/T + log S_c
+//   GREEDY : (M_c, -) and I_c = the lowest argmax
+//   RESID  : (0, sum_{v in c} max(0, p_t(v) - p_d(v)))   (residual mass)
 // Two producers:
 //   k_row_stats   : streams rows that need no bias (rank-0 draft rows, target
 //                   rows of the verify batch).  16-byte loads, a chunk spans
@@ -62,8 +63,7 @@ __device__ __forceinline__ void chunk_argmax(float& v, int& i) {
 // One wave: chunks [c0, c1) of one row.
 template <typename T, bool GREEDY>
 __device__ __forceinline__ void row_segment(const T* row, int V, int c0, int c1, float scale2,
-                                            bool vec_ok, float* L, float* M, int* I,
-                                            uint32_t* status) {
+                                            bool vec_ok, float2* L, int* I, uint32_t* status) {
   constexpr int VPL = 16 / sizeof(T);       // values per lane per 16-byte load
   constexpr int LPC = kChunk / VPL;         // lanes per chunk
   constexpr int CPI = 64 / LPC;             // chunks per wave-wide load
@@ -97,27 +97,23 @@ __device__ __forceinline__ void row_segment(const T* row, int V, int c0, int c1,
           if (x[u][e] > bv) { bv = x[u][e]; bi = v0 + e; }
         chunk_argmax<LPC>(bv, bi);
         if (sub == 0 && c < c1) {
-          M[c] = bv;
+          L[c] = make_float2(bv, 0.f);
           I[c] = bi;
           if (!(fabsf(bv) <= 3.0e38f)) set_flag(status, kFlagNonFinite);
         }
       } else {
         float m = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < VPL; ++e) {
-          x[u][e] *= scale2;
-          m = fmaxf(m, x[u][e]);
-        }
+        for (int e = 0; e < VPL; ++e) m = fmaxf(m, x[u][e]);
         m = chunk_max<LPC>(m);
         float s = 0.f;
         if (m != -INFINITY) {
 #pragma unroll
-          for (int e = 0; e < VPL; ++e) s += __builtin_amdgcn_exp2f(x[u][e] - m);
+          for (int e = 0; e < VPL; ++e) s += __builtin_amdgcn_exp2f((x[u][e] - m) * scale2);
         }
         s = chunk_sum<LPC>(s);
         if (sub == 0 && c < c1) {
-          const float lc = (m == -INFINITY) ? -INFINITY : (m + log2f(s)) * kLn2;
-          L[c] = lc;
+          L[c] = make_float2(m, s);
           if (!(s <= 3.0e38f) || m == INFINITY) set_flag(status, kFlagNonFinite);
         }
       }
@@ -152,8 +148,7 @@ __global__ __launch_bounds__(256) void k_row_stats(RowStatsArgs a) {
     const T* rp = reinterpret_cast<const T*>(a.base) + row * a.V;
     const int c0 = seg * a.cps, c1 = min(a.nch, c0 + a.cps);
     const int64_t o = (int64_t)q * a.nch;
-    row_segment<T, GREEDY>(rp, a.V, c0, c1, a.scale2, a.vec_ok, a.L + o, a.M + o, a.I + o,
-                           a.status);
+    row_segment<T, GREEDY>(rp, a.V, c0, c1, a.scale2, a.vec_ok, a.L + o, a.I + o, a.status);
   }
 }
 
@@ -206,11 +201,14 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
   }
   const UT* urow = reinterpret_cast<const UT*>(a.U) + ((int64_t)req * a.gamma + (kk - 1)) * a.V;
   const UT* tptr = reinterpret_cast<const UT*>(a.target) + (int64_t)trow * a.V;
-  float lse_t2 = 0.f, lse_d2 = 0.f;
+  float mt = 0.f, lrt2 = 0.f, lse_d = 0.f;
   if (MODE == kModeResid && valid) {
-    lse_t2 = a.lse_t[qrow] * kLog2e;
-    lse_d2 = a.lse_d[(int64_t)req * a.gamma + (kk - 1)] * kLog2e;
+    const float2 nt = a.lse_t[qrow];
+    mt = nt.x;
+    lrt2 = nt.y * kLog2e;
+    lse_d = a.lse_d[(int64_t)req * a.gamma + (kk - 1)];
   }
+  const float invT = a.scale2 * kLn2;
 
   // B operand: the gathered embedding rows, held for the whole wave
   const int nks = a.rank >> 4;
@@ -267,7 +265,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
           if (acc[t][j] > bv) { bv = acc[t][j]; bi = c * kChunk + t * 32 + 16 * half + j; }
       argmax_merge(bv, bi, __shfl_xor(bv, 32), __shfl_xor(bi, 32));
       if (half == 0 && valid) {
-        a.M[o] = bv;
+        a.L[o] = make_float2(bv, 0.f);
         a.I[o] = bi;
         if (!(fabsf(bv) <= 3.0e38f)) set_flag(a.status, kFlagNonFinite);
       }
@@ -276,21 +274,18 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          acc[t][j] *= a.scale2;
-          mx = fmaxf(mx, acc[t][j]);
-        }
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, acc[t][j]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       float sm = 0.f;
       if (mx != -INFINITY) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) sm += __builtin_amdgcn_exp2f(acc[t][j] - mx);
+          for (int j = 0; j < 16; ++j) sm += __builtin_amdgcn_exp2f((acc[t][j] - mx) * a.scale2);
       }
       sm += __shfl_xor(sm, 32);
       if (half == 0 && valid) {
-        a.L[o] = (mx == -INFINITY) ? -INFINITY : (mx + log2f(sm)) * kLn2;
+        a.L[o] = make_float2(mx, sm);
         if (!(sm <= 3.0e38f) || mx == INFINITY) set_flag(a.status, kFlagNonFinite);
       }
     } else {  // residual mass max(0, p_t - p_d) per chunk
@@ -306,14 +301,14 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const float pt = __builtin_amdgcn_exp2f(tv[j] * a.scale2 - lse_t2);
-          const float pd = __builtin_amdgcn_exp2f(acc[t][j] * a.scale2 - lse_d2);
+          const float pt = __builtin_amdgcn_exp2f((tv[j] - mt) * a.scale2 - lrt2);
+          const float pd = __builtin_amdgcn_exp2f((acc[t][j] * invT - lse_d) * kLog2e);
           sm += fmaxf(pt - pd, 0.f);
         }
       }
       sm += __shfl_xor(sm, 32);
       if (half == 0 && valid) {
-        a.L[o] = (sm > 0.f) ? logf(sm) : -INFINITY;
+        a.L[o] = make_float2(0.f, sm);
         if (!(sm <= 3.0e38f)) set_flag(a.status, kFlagNonFinite);
       }
     }
@@ -364,32 +359,35 @@ __global__ __launch_bounds__(256) void k_markov_valu(MarkovArgs a) {
       int bi = sv[0] == -INFINITY ? 0x7FFFFFFF : vv[0];
       argmax_merge(bv, bi, sv[1], sv[1] == -INFINITY ? 0x7FFFFFFF : vv[1]);
       wave_argmax(bv, bi);
-      if (lane == 0) { a.M[o] = bv; a.I[o] = bi; }
+      if (lane == 0) { a.L[o] = make_float2(bv, 0.f); a.I[o] = bi; }
     } else if (MODE == kModeSample) {
-      const float x0 = sv[0] * a.scale2, x1 = sv[1] * a.scale2;
-      const float mx = wave_max(fmaxf(x0, x1));
+      const float mx = wave_max(fmaxf(sv[0], sv[1]));
       float sm = 0.f;
-      if (mx != -INFINITY) sm = __builtin_amdgcn_exp2f(x0 - mx) + __builtin_amdgcn_exp2f(x1 - mx);
+      if (mx != -INFINITY)
+        sm = __builtin_amdgcn_exp2f((sv[0] - mx) * a.scale2) +
+             __builtin_amdgcn_exp2f((sv[1] - mx) * a.scale2);
       sm = wave_sum(sm);
       if (lane == 0) {
-        a.L[o] = (mx == -INFINITY) ? -INFINITY : (mx + log2f(sm)) * kLn2;
+        a.L[o] = make_float2(mx, sm);
         if (!(sm <= 3.0e38f) || mx == INFINITY) set_flag(a.status, kFlagNonFinite);
       }
     } else {
       const UT* tptr = reinterpret_cast<const UT*>(a.target) + (int64_t)trow * a.V;
-      const float lse_t2 = a.lse_t[qrow] * kLog2e;
-      const float lse_d2 = a.lse_d[(int64_t)req * a.gamma + (kk - 1)] * kLog2e;
+      const float2 nt = a.lse_t[qrow];
+      const float lse_d = a.lse_d[(int64_t)req * a.gamma + (kk - 1)];
+      const float invT = a.scale2 * kLn2;
       float sm = 0.f;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         if (vv[h] < a.V) {
-          const float pt = __builtin_amdgcn_exp2f(Elem<UT>::get(tptr, vv[h]) * a.scale2 - lse_t2);
-          const float pd = __builtin_amdgcn_exp2f(sv[h] * a.scale2 - lse_d2);
+          const float pt = __builtin_amdgcn_exp2f((Elem<UT>::get(tptr, vv[h]) - nt.x) * a.scale2
+                                                  - nt.y * kLog2e);
+          const float pd = __builtin_amdgcn_exp2f((sv[h] * invT - lse_d) * kLog2e);
           sm += fmaxf(pt - pd, 0.f);
         }
       }
       sm = wave_sum(sm);
-      if (lane == 0) a.L[o] = (sm > 0.f) ? logf(sm) : -INFINITY;
+      if (lane == 0) a.L[o] = make_float2(0.f, sm);
     }
   }
 }

@@ -41,12 +41,12 @@ struct VerifyArgs {
   int32_t* emitted;
   int32_t* next_anchor;
   float* logp_t;
-  const float* vl;      // [q][nch] chunk log-masses / maxima of verify rows
+  const float2* vl;     // [q][nch] chunk (max, scaled sum) of verify rows
   const int* vi;        // [q][nch] chunk argmax (greedy)
-  float* lse_t;         // [q]
+  float2* lse_t;        // [q] (raw row max, log-normaliser relative to it)
   int32_t* rej_count;
   int4* rej;            // (request, position, target row, verify row q)
-  const float* rl;      // [slot][nch] residual chunk log-masses
+  const float2* rl;     // [slot][nch] residual chunk masses (0, sum)
   uint32_t* status;
 };
 
@@ -69,16 +69,17 @@ __global__ __launch_bounds__(64) void k_verify_scan(VerifyArgs a) {
   if (!a.greedy) {
     for (int k = 1; k <= a.gamma; ++k)
       if (a.logp_t && lane == 0) a.logp_t[(int64_t)i * a.gamma + (k - 1)] = 0.f;
-    float lse_row = 0.f;
+    RowNorm last{0.f, 0.f};
     for (int j = 0; j <= L; ++j) {
       const int q = q0 + j;
-      const float lse = lse_chunks(a.vl + (int64_t)q * a.nch, a.nch);
-      if (lane == 0) a.lse_t[q] = lse;
+      const RowNorm rn = row_norm(a.vl + (int64_t)q * a.nch, a.nch, a.invT);
+      if (lane == 0) a.lse_t[q] = make_float2(rn.m, rn.lse_rel);
       if (j < L) {
         const int k = j + 1;
         int xk = xi[k];
         if (xk < 0 || xk >= a.V) { set_flag(a.status, kFlagBadToken); xk = 0; }
-        const float lp = Elem<TT>::get(tgt + target_row(a, i, j) * a.V, xk) * a.invT - lse;
+        const float lp = (Elem<TT>::get(tgt + target_row(a, i, j) * a.V, xk) - rn.m) * a.invT
+                         - rn.lse_rel;
         if (a.logp_t && lane == 0) a.logp_t[(int64_t)i * a.gamma + (k - 1)] = lp;
         if (!rejected) {
           const uint4 blk = stream_block(a.seed, a.round, kTagAccept, (uint32_t)i, (uint32_t)k, 0u);
@@ -87,14 +88,14 @@ __global__ __launch_bounds__(64) void k_verify_scan(VerifyArgs a) {
           if (!(lu < rhs)) { rejected = true; m = k - 1; }
         }
       } else {
-        lse_row = lse;
+        last = rn;
       }
     }
     if (!rejected) {
       // bonus token from the target row after the accepted prefix
       const int q = q0 + L;
-      const PickResult pc = pick_chunk(a.vl + (int64_t)q * a.nch, a.nch, a.seed, a.round,
-                                       kTagBonusChunk, (uint32_t)i, (uint32_t)(L + 1), false);
+      const PickResult pc = pick_chunk(a.vl + (int64_t)q * a.nch, a.nch, last.m, a.invT, a.seed,
+                                       a.round, kTagBonusChunk, (uint32_t)i, (uint32_t)(L + 1), false);
       int c = pc.idx < 0 ? 0 : pc.idx;
       if (pc.idx < 0) set_flag(a.status, kFlagNonFinite);
       const TT* trow = tgt + target_row(a, i, L) * a.V;
@@ -102,12 +103,11 @@ __global__ __launch_bounds__(64) void k_verify_scan(VerifyArgs a) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int v = c * kChunk + h * 64 + lane;
-        s[h] = (v < a.V) ? Elem<TT>::get(trow, v) * a.invT : -INFINITY;
+        s[h] = (v < a.V) ? (Elem<TT>::get(trow, v) - last.m) * a.invT : -INFINITY;
       }
       const PickResult pe = pick_in_chunk(s[0], s[1], c * kChunk, a.seed, a.round, kTagBonusElem,
                                           (uint32_t)i, (uint32_t)(L + 1), false);
       y = pe.idx < 0 ? c * kChunk : pe.idx;
-      (void)lse_row;
     } else if (lane == 0) {
       const int slot = atomicAdd(a.rej_count, 1);
       a.rej[slot] = make_int4(i, m + 1, (int)target_row(a, i, m), q0 + m);
@@ -150,18 +150,18 @@ __global__ __launch_bounds__(64) void k_resid_pick(VerifyArgs a) {
   const int4 e = a.rej[slot];
   const int i = e.x, k = e.y, trow_i = e.z, q = e.w;
   const UT* trow = reinterpret_cast<const UT*>(a.target) + (int64_t)trow_i * a.V;
-  const float* Lq = a.rl + (int64_t)slot * a.nch;
-  const float mass = lse_chunks(Lq, a.nch);
+  const float2* Lq = a.rl + (int64_t)slot * a.nch;
+  const RowNorm mass = row_norm(Lq, a.nch, 1.f);
+  const float2 nt = a.lse_t[q];
   int y;
-  if (mass != -INFINITY) {
-    const PickResult pc = pick_chunk(Lq, a.nch, a.seed, a.round, kTagResidChunk, (uint32_t)i,
-                                     (uint32_t)k, false);
+  if (mass.lse_rel != -INFINITY) {
+    const PickResult pc = pick_chunk(Lq, a.nch, 0.f, 1.f, a.seed, a.round, kTagResidChunk,
+                                     (uint32_t)i, (uint32_t)k, false);
     const int c = pc.idx < 0 ? 0 : pc.idx;
     const UT* urow = reinterpret_cast<const UT*>(a.U) + ((int64_t)i * a.gamma + (k - 1)) * a.V;
     int prev = a.x[(int64_t)i * (a.gamma + 1) + (k - 1)];
     if (prev < 0 || prev >= a.V) prev = 0;
     const WT* erow = reinterpret_cast<const WT*>(a.W1) + (int64_t)prev * a.rank;
-    const float lse_t = a.lse_t[q];
     const float lse_d = a.lse_d[(int64_t)i * a.gamma + (k - 1)];
     float s[2];
 #pragma unroll
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(64) void k_resid_pick(VerifyArgs a) {
         const float b = a.rank > 0 ? markov_bias(erow, reinterpret_cast<const WT*>(a.W2t), a.rank, v)
                                    : 0.f;
         const float sd = (Elem<UT>::get(urow, v) + b) * a.invT;
-        const float pt = expf(Elem<UT>::get(trow, v) * a.invT - lse_t);
+        const float pt = expf((Elem<UT>::get(trow, v) - nt.x) * a.invT - nt.y);
         const float pd = expf(sd - lse_d);
         const float d = pt - pd;
         s[h] = d > 0.f ? logf(d) : -INFINITY;
@@ -182,20 +182,20 @@ __global__ __launch_bounds__(64) void k_resid_pick(VerifyArgs a) {
                                         (uint32_t)i, (uint32_t)k, false);
     y = pe.idx;
     if (y < 0) {
-      // the chunk's mass vanished on re-evaluation: take its best target entry
+      // the chunk's mass vanished on re-evaluation (rounding): keep the chunk's first entry
       set_flag(a.status, kFlagNonFinite);
       y = c * kChunk;
     }
   } else {
     // zero residual mass: sample p_t of the same row
-    const PickResult pc = pick_chunk(a.vl + (int64_t)q * a.nch, a.nch, a.seed, a.round,
-                                     kTagResidChunk, (uint32_t)i, (uint32_t)k, false);
+    const PickResult pc = pick_chunk(a.vl + (int64_t)q * a.nch, a.nch, nt.x, a.invT, a.seed,
+                                     a.round, kTagResidChunk, (uint32_t)i, (uint32_t)k, false);
     const int c = pc.idx < 0 ? 0 : pc.idx;
     float s[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int v = c * kChunk + h * 64 + lane;
-      s[h] = (v < a.V) ? Elem<UT>::get(trow, v) * a.invT : -INFINITY;
+      s[h] = (v < a.V) ? (Elem<UT>::get(trow, v) - nt.x) * a.invT : -INFINITY;
     }
     const PickResult pe = pick_in_chunk(s[0], s[1], c * kChunk, a.seed, a.round, kTagResidElem,
                                         (uint32_t)i, (uint32_t)k, false);
@@ -229,8 +229,7 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
   rs.nrows_cap = R * (gamma + 1);
   rs.scale2 = greedy ? 1.f : kLog2e / T;
   rs.vec_ok = t_vec;
-  rs.L = reinterpret_cast<float*>(w + L.ver_l);
-  rs.M = rs.L;
+  rs.L = reinterpret_cast<float2*>(w + L.ver_l);
   rs.I = reinterpret_cast<int*>(w + L.ver_i);
   rs.status = hdr;
   rs.zero_me = hdr + 1;
@@ -244,10 +243,10 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
   a.U = U; a.W1 = W1; a.W2t = W2t; a.m = m; a.tau = tau; a.emitted = emitted;
   a.next_anchor = next_anchor; a.logp_t = logp_t;
   a.vl = rs.L; a.vi = rs.I;
-  a.lse_t = reinterpret_cast<float*>(w + L.lse_t);
+  a.lse_t = reinterpret_cast<float2*>(w + L.lse_t);
   a.rej_count = reinterpret_cast<int32_t*>(hdr + 1);
   a.rej = reinterpret_cast<int4*>(w + L.rej);
-  a.rl = reinterpret_cast<float*>(w + L.draft_l);
+  a.rl = reinterpret_cast<float2*>(w + L.draft_l);
   a.status = hdr;
   if (u_bf16) hipLaunchKernelGGL((k_verify_scan<uint16_t>), dim3(R), dim3(64), 0, st, a);
   else hipLaunchKernelGGL((k_verify_scan<float>), dim3(R), dim3(64), 0, st, a);
@@ -258,7 +257,7 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
   ma.R = R; ma.gamma = gamma; ma.k = 0; ma.V = V; ma.rank = rank; ma.nch = nch; ma.nrows_cap = R;
   ma.U = U; ma.W1v = W1; ma.W2tv = W2t; ma.x0 = nullptr; ma.x = x; ma.scale2 = kLog2e / T;
   ma.u_vec_ok = u_vec && t_vec;
-  ma.L = const_cast<float*>(a.rl); ma.M = ma.L; ma.I = nullptr;
+  ma.L = const_cast<float2*>(a.rl); ma.I = nullptr;
   ma.rej_count = a.rej_count; ma.rej = a.rej; ma.target = target; ma.lse_t = a.lse_t;
   ma.lse_d = lse_d; ma.status = hdr;
   e = launch_markov_stats(ma, u_bf16, w_bf16 && rank > 0, kModeResid, st);

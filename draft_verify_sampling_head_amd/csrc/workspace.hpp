@@ -12,11 +12,11 @@ namespace dspark {
 
 struct WsLayout {
   size_t header;       // uint32 words: [0] status flags, [1] residual count
-  size_t draft_l;      // float  [R][nch]   chunk log-masses / maxima (draft, residual)
+  size_t draft_l;      // float2 [R][nch]   chunk (max, scaled sum) / residual masses
   size_t draft_i;      // int32  [R][nch]   chunk argmax (greedy)
-  size_t ver_l;        // float  [R*(gamma+1)][nch]  target-row chunk log-masses / maxima
+  size_t ver_l;        // float2 [R*(gamma+1)][nch]  target-row chunk (max, scaled sum)
   size_t ver_i;        // int32  [R*(gamma+1)][nch]  target-row chunk argmax (greedy)
-  size_t lse_t;        // float  [R*(gamma+1)]       target-row log-normalisers
+  size_t lse_t;        // float2 [R*(gamma+1)]       target-row (max, log-normaliser above it)
   size_t rej;          // int32  [R][4]   residual work list: request, position, row, pad
   size_t total;
 };
@@ -29,11 +29,11 @@ inline WsLayout ws_layout(int R, int gamma, int V) {
   WsLayout L;
   size_t off = 0;
   L.header = off;  off += ws_align(256);
-  L.draft_l = off; off += ws_align((size_t)R * nch * 4);
+  L.draft_l = off; off += ws_align((size_t)R * nch * 8);
   L.draft_i = off; off += ws_align((size_t)R * nch * 4);
-  L.ver_l = off;   off += ws_align(rows_v * nch * 4);
+  L.ver_l = off;   off += ws_align(rows_v * nch * 8);
   L.ver_i = off;   off += ws_align(rows_v * nch * 4);
-  L.lse_t = off;   off += ws_align(rows_v * 4);
+  L.lse_t = off;   off += ws_align(rows_v * 8);
   L.rej = off;     off += ws_align((size_t)R * 16);
   L.total = off;
   return L;
