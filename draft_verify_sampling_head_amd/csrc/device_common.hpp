@@ -152,6 +152,12 @@ __device__ __forceinline__ void lse2_merge(float& m, float& s, float mo, float s
   m = mn;
 }
 
+// True for +-inf and NaN (exponent bits all ones); an integer test, so no
+// floating-point assumption can fold it away.
+__device__ __forceinline__ bool nonfinite(float x) {
+  return (__float_as_uint(x) & 0x7F800000u) == 0x7F800000u;
+}
+
 __device__ __forceinline__ void set_flag(uint32_t* status, uint32_t f) {
   if (status) atomicOr(status, f);
 }

@@ -32,10 +32,12 @@ struct DraftPickArgs {
   uint32_t* status;
 };
 
+// One 256-thread block per request.
 template <typename UT, typename WT, bool GREEDY>
-__global__ __launch_bounds__(64) void k_draft_pick(DraftPickArgs a) {
+__global__ __launch_bounds__(256) void k_draft_pick(DraftPickArgs a) {
+  __shared__ BlockScratch sh;
   const int i = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   const int k = a.k;
   const int64_t xo = (int64_t)i * (a.gamma + 1);
   const int prev = (k == 1) ? a.x0[i] : a.x[xo + k - 1];
@@ -43,45 +45,53 @@ __global__ __launch_bounds__(64) void k_draft_pick(DraftPickArgs a) {
   int xk;
   float logp, lse, gap = INFINITY;
   if (GREEDY) {
-    float v;
-    argmax_chunks(Lr, a.I + (int64_t)i * a.nch, a.nch, v, xk);
+    float v = -INFINITY;
+    int idx = 0x7FFFFFFF;
+    const int* Ir = a.I + (int64_t)i * a.nch;
+    for (int c = tid; c < a.nch; c += 256) argmax_merge(v, idx, Lr[c].x, Ir[c]);
+    block_argmax(v, idx, sh);
+    xk = idx;
     lse = v;
     logp = 0.f;
     if (xk < 0 || xk >= a.V) { set_flag(a.status, kFlagNonFinite); xk = 0; }
   } else {
-    const RowNorm rn = row_norm(Lr, a.nch, a.invT);
-    lse = rn.m * a.invT + rn.lse_rel;
+    float m = -INFINITY;
+    for (int c = tid; c < a.nch; c += 256) m = fmaxf(m, Lr[c].x);
+    m = block_max(m, sh);
     const bool want_gap = a.margin != nullptr;
-    const PickResult pc = pick_chunk(Lr, a.nch, rn.m, a.invT, a.seed, a.round, kTagDraftChunk,
-                                     (uint32_t)i, (uint32_t)k, want_gap);
+    float srel;
+    const PickResult pc = block_pick_chunk(Lr, a.nch, m, a.invT, a.seed, a.round, kTagDraftChunk,
+                                           (uint32_t)i, (uint32_t)k, want_gap, &srel, sh);
+    const float lse_rel = logf(srel);
+    lse = m * a.invT + lse_rel;
     int c = pc.idx;
     if (c < 0) { set_flag(a.status, kFlagNonFinite); c = 0; }
     const int base = c * kChunk;
-    const UT* urow = reinterpret_cast<const UT*>(a.U) + ((int64_t)i * a.gamma + (k - 1)) * a.V;
-    const int pv = (prev >= 0 && prev < a.V) ? prev : 0;
-    const WT* erow = reinterpret_cast<const WT*>(a.W1) + (int64_t)pv * a.rank;
-    float s[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int v = base + h * 64 + lane;
-      s[h] = -INFINITY;
-      if (v < a.V) {
-        const float b = a.rank > 0 ? markov_bias(erow, reinterpret_cast<const WT*>(a.W2t), a.rank, v)
-                                   : 0.f;
-        s[h] = (Elem<UT>::get(urow, v) + b - rn.m) * a.invT;     // relative to the row maximum
-      }
+    // rebuild the 128 scores of the chosen chunk: thread t covers entry
+    // base + t/2 and one half of the rank
+    const int v = base + (tid >> 1), h = tid & 1;
+    const bool in = v < a.V;
+    float b = 0.f;
+    if (a.rank > 0 && in) {
+      const int pv = (prev >= 0 && prev < a.V) ? prev : 0;
+      const WT* erow = reinterpret_cast<const WT*>(a.W1) + (int64_t)pv * a.rank;
+      b = markov_bias_half(erow, reinterpret_cast<const WT*>(a.W2t), a.rank, v, h);
     }
-    const PickResult pe = pick_in_chunk(s[0], s[1], base, a.seed, a.round, kTagDraftElem,
-                                        (uint32_t)i, (uint32_t)k, want_gap);
+    b += __shfl_xor(b, 1);
+    const UT* urow = reinterpret_cast<const UT*>(a.U) + ((int64_t)i * a.gamma + (k - 1)) * a.V;
+    const float s = in ? (Elem<UT>::get(urow, v) + b - m) * a.invT : -INFINITY;
+    const PickResult pe = block_pick_in_chunk(s, base, a.seed, a.round, kTagDraftElem,
+                                              (uint32_t)i, (uint32_t)k, want_gap, sh);
     xk = pe.idx;
     if (xk < 0) { set_flag(a.status, kFlagNonFinite); xk = base; }
-    const int off = xk - base;
-    const float sx0 = __shfl(s[0], off & 63);
-    const float sx1 = __shfl(s[1], off & 63);
-    logp = ((off >= 64) ? sx1 : sx0) - rn.lse_rel;
+    // the winner's score: held by thread 2*(xk - base)
+    __syncthreads();
+    if (tid == 2 * (xk - base)) sh.g[0] = s;
+    __syncthreads();
+    logp = sh.g[0] - lse_rel;
     gap = fminf(pc.gap, pe.gap);
   }
-  if (lane == 0) {
+  if (tid == 0) {
     if (k == 1) a.x[xo] = a.x0[i];
     a.x[xo + k] = xk;
     const int64_t o = (int64_t)i * a.gamma + (k - 1);
@@ -129,7 +139,7 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     p.U = U; p.W1 = W1; p.W2t = W2t; p.x0 = x0; p.x = x; p.logp_d = logp_d; p.lse_d = lse_d;
     p.margin = margin; p.L = Lc; p.I = Ic; p.status = status;
 #define DSPARK_PICK(UT_, WT_, G_) \
-    hipLaunchKernelGGL((k_draft_pick<UT_, WT_, G_>), dim3(R), dim3(64), 0, st, p)
+    hipLaunchKernelGGL((k_draft_pick<UT_, WT_, G_>), dim3(R), dim3(256), 0, st, p)
     if (u_bf16 && w_bf16) { if (greedy) DSPARK_PICK(uint16_t, uint16_t, true); else DSPARK_PICK(uint16_t, uint16_t, false); }
     else if (u_bf16)      { if (greedy) DSPARK_PICK(uint16_t, float, true);    else DSPARK_PICK(uint16_t, float, false); }
     else if (w_bf16)      { if (greedy) DSPARK_PICK(float, uint16_t, true);    else DSPARK_PICK(float, uint16_t, false); }

@@ -48,7 +48,7 @@ struct MarkovArgs {
   const float* lse_d;
   uint32_t* status;
   // filled by the launcher
-  int cg, nrt, nrtg, ncg;
+  int cg, nrg, ncg;        // chunks per workgroup, 256-row groups, chunk groups
 };
 
 struct ConfArgs {

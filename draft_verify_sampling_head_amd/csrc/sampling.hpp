@@ -165,4 +165,154 @@ __device__ inline float markov_bias(const float* e, const float* W2t, int rank, 
   return b;
 }
 
+// ------------------------------------------------ block-level (256 threads)
+// Reductions across the four waves of a 256-thread block through LDS; every
+// thread of the block must call them (they contain barriers).
+struct BlockScratch {
+  float f[4];
+  int i[4];
+  float g[4];
+};
+
+__device__ inline float block_max(float v, BlockScratch& sh) {
+  const int wv = threadIdx.x >> 6;
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.f[wv] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(sh.f[0], sh.f[1]), fmaxf(sh.f[2], sh.f[3]));
+}
+__device__ inline float block_sum(float v, BlockScratch& sh) {
+  const int wv = threadIdx.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.f[wv] = v;
+  __syncthreads();
+  return (sh.f[0] + sh.f[1]) + (sh.f[2] + sh.f[3]);
+}
+__device__ inline void block_argmax(float& v, int& idx, BlockScratch& sh) {
+  const int wv = threadIdx.x >> 6;
+  wave_argmax(v, idx);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { sh.f[wv] = v; sh.i[wv] = idx; }
+  __syncthreads();
+  v = sh.f[0];
+  idx = sh.i[0];
+  for (int q = 1; q < 4; ++q) argmax_merge(v, idx, sh.f[q], sh.i[q]);
+}
+
+// Chunk-level Gumbel pick by a 256-thread block: thread t scans chunk blocks
+// t, t+256, ... (four chunks per Philox block).  Returns the chunk and,
+// through *sum_rel, sum_c S_c exp((M_c - m)/T) (the row normaliser above m).
+__device__ inline PickResult block_pick_chunk(const float2* st, int nch, float m, float invT,
+                                              uint64_t seed, uint64_t round, uint32_t tag,
+                                              uint32_t req, uint32_t k, bool want_gap,
+                                              float* sum_rel, BlockScratch& sh) {
+  float best = -INFINITY, ssum = 0.f;
+  int bi = 0x7FFFFFFF;
+  const bool draw = nch > 1;
+  for (int b = threadIdx.x; b * 4 < nch; b += 256) {
+    uint4 blk = make_uint4(0, 0, 0, 0);
+    if (draw) blk = stream_block(seed, round, tag, req, k, (uint32_t)b);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = b * 4 + w;
+      if (c < nch) {
+        const float2 v = st[c];
+        if (v.y > 0.f) {
+          const float rel = (v.x - m) * invT;
+          ssum += v.y * expf(rel);
+          const float key = rel + logf(v.y) + (draw ? gumbel_of(word_of(blk, (uint32_t)w)) : 0.f);
+          argmax_merge(best, bi, key, c);
+        }
+      }
+    }
+  }
+  *sum_rel = block_sum(ssum, sh);
+  block_argmax(best, bi, sh);
+  PickResult r{best == -INFINITY ? -1 : bi, best, INFINITY};
+  if (want_gap && r.idx >= 0 && draw) {
+    float second = -INFINITY;
+    for (int b = threadIdx.x; b * 4 < nch; b += 256) {
+      const uint4 blk = stream_block(seed, round, tag, req, k, (uint32_t)b);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int c = b * 4 + w;
+        if (c < nch && c != r.idx) {
+          const float2 v = st[c];
+          if (v.y > 0.f)
+            second = fmaxf(second, (v.x - m) * invT + logf(v.y) + gumbel_of(word_of(blk, (uint32_t)w)));
+        }
+      }
+    }
+    r.gap = best - block_max(second, sh);
+  }
+  return r;
+}
+
+// In-chunk Gumbel pick by a 256-thread block: threads with (t & 1) == 0 hold
+// the score of entry base + t/2 (-inf = excluded).
+__device__ inline PickResult block_pick_in_chunk(float s, int base, uint64_t seed, uint64_t round,
+                                                 uint32_t tag, uint32_t req, uint32_t k,
+                                                 bool want_gap, BlockScratch& sh) {
+  const int t = threadIdx.x;
+  const int v = base + (t >> 1);
+  float key = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  if ((t & 1) == 0 && s != -INFINITY) {
+    const uint4 blk = stream_block(seed, round, tag, req, k, (uint32_t)v >> 2);
+    key = s + gumbel_of(word_of(blk, (uint32_t)v & 3u));
+    bi = v;
+  }
+  float best = key;
+  int bidx = bi;
+  block_argmax(best, bidx, sh);
+  PickResult r{best == -INFINITY ? -1 : bidx, best, INFINITY};
+  if (want_gap && r.idx >= 0) {
+    const float second = block_max((bi == r.idx) ? -INFINITY : key, sh);
+    r.gap = best - second;
+  }
+  return r;
+}
+
+// Half of the Markov bias dot product W1[prev] . W2t[v]: entries
+// [h*rank/2, (h+1)*rank/2), float32 FMA chain in ascending order.
+__device__ inline float markov_bias_half(const uint16_t* e, const uint16_t* W2t, int rank, int v,
+                                         int h) {
+  const int nq = rank / 16;                      // 8-value groups per half
+  const uint4* w = reinterpret_cast<const uint4*>(W2t + (int64_t)v * rank) + h * nq;
+  const uint4* ev = reinterpret_cast<const uint4*>(e) + h * nq;
+  float b = 0.f;
+#pragma unroll 8
+  for (int q = 0; q < nq; ++q) {
+    const uint4 u = w[q];
+    const uint4 x = ev[q];
+    b = fmaf(bf16_lo(x.x), bf16_lo(u.x), b);
+    b = fmaf(bf16_hi(x.x), bf16_hi(u.x), b);
+    b = fmaf(bf16_lo(x.y), bf16_lo(u.y), b);
+    b = fmaf(bf16_hi(x.y), bf16_hi(u.y), b);
+    b = fmaf(bf16_lo(x.z), bf16_lo(u.z), b);
+    b = fmaf(bf16_hi(x.z), bf16_hi(u.z), b);
+    b = fmaf(bf16_lo(x.w), bf16_lo(u.w), b);
+    b = fmaf(bf16_hi(x.w), bf16_hi(u.w), b);
+  }
+  return b;
+}
+__device__ inline float markov_bias_half(const float* e, const float* W2t, int rank, int v, int h) {
+  const int nq = rank / 8;                       // 4-value groups per half
+  const float4* w = reinterpret_cast<const float4*>(W2t + (int64_t)v * rank) + h * nq;
+  const float4* ev = reinterpret_cast<const float4*>(e) + h * nq;
+  float b = 0.f;
+#pragma unroll 8
+  for (int q = 0; q < nq; ++q) {
+    const float4 u = w[q];
+    const float4 x = ev[q];
+    b = fmaf(x.x, u.x, b);
+    b = fmaf(x.y, u.y, b);
+    b = fmaf(x.z, u.z, b);
+    b = fmaf(x.w, u.w, b);
+  }
+  return b;
+}
+
 }  // namespace dspark

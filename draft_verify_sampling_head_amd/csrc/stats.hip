@@ -19,12 +19,15 @@
 //                   vocabulary is the MFMA M dimension, arranged so each lane
 //                   ends with 16 consecutive entries of one row.
 //   k_markov_valu : the same with float32 weights on the vector ALU.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "sampling.hpp"
 
 namespace dspark {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // ===================================================================== rows
@@ -99,7 +102,7 @@ __device__ __forceinline__ void row_segment(const T* row, int V, int c0, int c1,
         if (sub == 0 && c < c1) {
           L[c] = make_float2(bv, 0.f);
           I[c] = bi;
-          if (!(fabsf(bv) <= 3.0e38f)) set_flag(status, kFlagNonFinite);
+          if (nonfinite(bv)) set_flag(status, kFlagNonFinite);
         }
       } else {
         float m = -INFINITY;
@@ -114,7 +117,7 @@ __device__ __forceinline__ void row_segment(const T* row, int V, int c0, int c1,
         s = chunk_sum<LPC>(s);
         if (sub == 0 && c < c1) {
           L[c] = make_float2(m, s);
-          if (!(s <= 3.0e38f) || m == INFINITY) set_flag(status, kFlagNonFinite);
+          if (nonfinite(s) || m == INFINITY) set_flag(status, kFlagNonFinite);
         }
       }
     }
@@ -169,149 +172,733 @@ __device__ __forceinline__ void load16(const T* p, bool vec, int v0, int V, floa
   }
 }
 
+// 16 consecutive logits of one row kept as raw words until they seed an
+// accumulator (bf16: 8 dwords, fp32: 16 dwords); -inf past the vocabulary.
+template <typename UT> struct URaw;
+template <> struct URaw<uint16_t> {
+  uint4 w[2];
+  __device__ __forceinline__ void fetch(const uint16_t* p, int v0, int V, bool vec, bool valid) {
+    if (valid && vec && v0 + 16 <= V) {
+      w[0] = *reinterpret_cast<const uint4*>(p + v0);
+      w[1] = *reinterpret_cast<const uint4*>(p + v0 + 8);
+    } else {
+      uint32_t d[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = (valid && v0 + 2 * e < V) ? p[v0 + 2 * e] : 0xFF80u;
+        const uint32_t hi = (valid && v0 + 2 * e + 1 < V) ? p[v0 + 2 * e + 1] : 0xFF80u;
+        d[e] = lo | (hi << 16);
+      }
+      w[0] = make_uint4(d[0], d[1], d[2], d[3]);
+      w[1] = make_uint4(d[4], d[5], d[6], d[7]);
+    }
+  }
+  __device__ __forceinline__ void unpack(f32x16_t& acc) const {
+    const uint32_t d[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[2 * e] = bf16_lo(d[e]);
+      acc[2 * e + 1] = bf16_hi(d[e]);
+    }
+  }
+};
+template <> struct URaw<float> {
+  float4 w[4];
+  __device__ __forceinline__ void fetch(const float* p, int v0, int V, bool vec, bool valid) {
+    if (valid && vec && v0 + 16 <= V) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = *reinterpret_cast<const float4*>(p + v0 + 4 * q);
+    } else {
+      float d[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) d[e] = (valid && v0 + e < V) ? p[v0 + e] : -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = make_float4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
+    }
+  }
+  __device__ __forceinline__ void unpack(f32x16_t& acc) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[4 * q] = w[q].x; acc[4 * q + 1] = w[q].y; acc[4 * q + 2] = w[q].z; acc[4 * q + 3] = w[q].w;
+    }
+  }
+};
+
+// LDS slot swizzle of a W2t tile row: spreads the 16-byte segments read by one
+// ds_read_b128 over distinct banks for the MFMA A-operand row order below.
+__device__ __forceinline__ int seg_swizzle(int r) { return (r & 7) | (((r >> 4) & 1) << 3); }
+
+// Markov statistics kernel.  One workgroup = 4 waves = 256 rows (each wave 64
+// rows as two 32-row MFMA column tiles, their gathered W1 rows held as B
+// operands for the whole kernel) x a contiguous range of vocabulary chunks.
+// The W2t tile (32 vocabulary rows x rank) of each step is loaded once per
+// workgroup into a double-buffered LDS ring (loads two tiles ahead) and read
+// by every wave as MFMA A operands; U is prefetched two tiles ahead and seeds
+// the accumulators; the epilogue of tile t-1 is issued after the MFMAs of
+// tile t so the vector ALU work overlaps the matrix pipe.
 template <typename UT, int KS, int MODE>
-__global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+__global__ __launch_bounds__(256) void k_markov_mfma_reg(MarkovArgs a) {
+  constexpr int SEGMAX = 2 * KS;                    // 16-byte segments per W2t row
+  constexpr int NLD = (32 * SEGMAX + 255) / 256;    // staging loads per thread per tile
+  __shared__ u32x4_t lds[2][32 * SEGMAX];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int b = blockIdx.x;
-  const int xcd = b & 7, s = b >> 3;
-  const int rtg = s % a.nrtg;
-  const int cg = (s / a.nrtg) * 8 + xcd;
-  const int rt = rtg * 4 + wv;
-  if (cg >= a.ncg || rt >= a.nrt) return;
+  const int xcd = b & 7, sb = b >> 3;
+  const int rg = sb % a.nrg;
+  const int cg = (sb / a.nrg) * 8 + xcd;
+  if (cg >= a.ncg) return;
   int nrows = a.R;
   if (MODE == kModeResid) nrows = *a.rej_count;
-  if (rt * 32 >= nrows) return;
-
-  const int n = lane & 31, half = lane >> 5;
-  const int row = rt * 32 + n;
-  const bool valid = row < nrows;
-  int req = 0, kk = a.k, trow = 0, qrow = 0;
-  if (valid && MODE == kModeResid) {
-    const int4 e = a.rej[row];
-    req = e.x; kk = e.y; trow = e.z; qrow = e.w;
-  } else if (valid) {
-    req = row;
-  }
-  int prev = 0;
-  if (valid) {
-    prev = (MODE != kModeResid && kk == 1) ? a.x0[req]
-                                           : a.x[(int64_t)req * (a.gamma + 1) + (kk - 1)];
-    if (prev < 0 || prev >= a.V) { set_flag(a.status, kFlagBadToken); prev = 0; }
-  }
-  const UT* urow = reinterpret_cast<const UT*>(a.U) + ((int64_t)req * a.gamma + (kk - 1)) * a.V;
-  const UT* tptr = reinterpret_cast<const UT*>(a.target) + (int64_t)trow * a.V;
-  float mt = 0.f, lrt2 = 0.f, lse_d = 0.f;
-  if (MODE == kModeResid && valid) {
-    const float2 nt = a.lse_t[qrow];
-    mt = nt.x;
-    lrt2 = nt.y * kLog2e;
-    lse_d = a.lse_d[(int64_t)req * a.gamma + (kk - 1)];
-  }
-  const float invT = a.scale2 * kLn2;
-
-  // B operand: the gathered embedding rows, held for the whole wave
-  const int nks = a.rank >> 4;
-  bf16x8_t Bf[KS];
-  const uint16_t* erow = a.W1 + (int64_t)prev * a.rank + half * 8;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    bf16x8_t z = {};
-    Bf[ks] = (valid && ks < nks) ? *reinterpret_cast<const bf16x8_t*>(erow + ks * 16) : z;
-  }
-  // A operand row of this lane: vocabulary offset inside a 32-entry tile such
-  // that accumulator j of lane (n, half) is entry 16*half + j.
-  const int m = lane & 31;
-  const int voff = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
-
+  if (rg * 256 >= nrows) return;
   const int c0 = cg * a.cg, c1 = min(a.nch, c0 + a.cg);
-  for (int c = c0; c < c1; ++c) {
-    f32x16_t acc[4];
+  const int T = (c1 - c0) * 4;
+  const int vbase = c0 * kChunk;
+  const int nseg = a.rank >> 3, nks = a.rank >> 4;   // nks <= KS
+  const int smask = ((nseg & (nseg - 1)) == 0) ? min(nseg, 16) - 1 : 0;
+  const bool wave_active = rg * 256 + wv * 64 < nrows;
+
+  // ---- the two rows of this lane (column n of each 32-row tile)
+  const int n = lane & 31, half = lane >> 5;
+  bool valid[2];
+  const UT* urow[2];
+  const UT* trow[2];
+  int prevs[2];
+  float mt[2], lrt2[2], lse_d[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float u[16];
-      const int vb = c * kChunk + t * 32 + 16 * half;
-      if (valid) load16<UT>(urow, a.u_vec_ok, vb, a.V, u);
-      else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) u[e] = -INFINITY;
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[t][e] = u[e];
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int va = c * kChunk + t * 32 + voff;
-      const uint16_t* arow = a.W2t + (int64_t)va * a.rank + half * 8;
-      const bool ok = va < a.V;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks < nks) {
-          bf16x8_t z = {};
-          const bf16x8_t A = ok ? *reinterpret_cast<const bf16x8_t*>(arow + ks * 16) : z;
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bf[ks], acc[t], 0, 0, 0);
-        }
+  for (int nt = 0; nt < 2; ++nt) {
+    const int row = rg * 256 + wv * 64 + nt * 32 + n;
+    valid[nt] = row < nrows;
+    int req = 0, kk = a.k, tr = 0, qr = 0;
+    if (valid[nt]) {
+      if (MODE == kModeResid) {
+        const int4 e = a.rej[row];
+        req = e.x; kk = e.y; tr = e.z; qr = e.w;
+      } else {
+        req = row;
       }
     }
-    // ---- epilogue: lane (n, half) holds entries c*128 + 32t + 16*half + j of row n
-    const int64_t o = (int64_t)row * a.nch + c;
-    if (MODE == kModeGreedy) {
-      float bv = -INFINITY;
-      int bi = 0x7FFFFFFF;
+    int prev = 0;
+    if (valid[nt]) {
+      prev = (MODE != kModeResid && kk == 1) ? a.x0[req]
+                                             : a.x[(int64_t)req * (a.gamma + 1) + (kk - 1)];
+      if (prev < 0 || prev >= a.V) { set_flag(a.status, kFlagBadToken); prev = 0; }
+    }
+    prevs[nt] = prev;
+    urow[nt] = reinterpret_cast<const UT*>(a.U) + ((int64_t)req * a.gamma + (kk - 1)) * a.V;
+    trow[nt] = reinterpret_cast<const UT*>(a.target) + (int64_t)tr * a.V;
+    mt[nt] = 0.f; lrt2[nt] = 0.f; lse_d[nt] = 0.f;
+    if (MODE == kModeResid && valid[nt]) {
+      const float2 nrm = a.lse_t[qr];
+      mt[nt] = nrm.x;
+      lrt2[nt] = nrm.y * kLog2e;
+      lse_d[nt] = a.lse_d[(int64_t)req * a.gamma + (kk - 1)];
+    }
+  }
+  // ---- B operands: gathered W1 rows for both column tiles, whole kernel
+  bf16x8_t Bf[2][KS];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+  for (int nt = 0; nt < 2; ++nt) {
+    const uint16_t* erow = a.W1 + (int64_t)prevs[nt] * a.rank + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t z = {};
+      Bf[nt][ks] = (valid[nt] && ks < nks) ? *reinterpret_cast<const bf16x8_t*>(erow + ks * 16) : z;
+    }
+  }
+  // A operand row of this lane inside a 32-entry tile, ordered so that
+  // accumulator j of lane (n, half) is vocabulary entry 16*half + j.
+  const int m = lane & 31;
+  const int arow = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+  const int aswz = seg_swizzle(arow) & smask;
+
+  // ---- staging of W2t tiles: thread tid owns segments tid + 256*i
+  u32x4_t st[2][NLD];
+  const int tile_segs = 32 * nseg;
+  // every staging load is unconditional (clamped address) so that the staged
+  // values stay in registers and their waits can be deferred to the LDS store
+  auto stage_load = [&](u32x4_t (&dst)[NLD], int t) __attribute__((always_inline)) {
+    const int vb = vbase + t * 32;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int j = min(tid + 256 * i, tile_segs - 1);
+      const int r = j / nseg, p = j - r * nseg;
+      const int q = p ^ (seg_swizzle(r) & smask);
+      const int v = min(vb + r, a.V - 1);
+      dst[i] = *reinterpret_cast<const u32x4_t*>(a.W2t + (int64_t)v * a.rank + q * 8);
+    }
+  };
+  auto stage_store = [&](const u32x4_t (&src)[NLD], int P) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int j = tid + 256 * i;
+      if (j < tile_segs) {
+        const int r = j / nseg;
+        lds[P][r * SEGMAX + (j - r * nseg)] = src[i];
+      }
+    }
+  };
+  // a rank below 16*KS leaves segments [nseg, SEGMAX) of every LDS row unused:
+  // zero them once so the padded MFMA steps (B is zero there too) add nothing
+  if (nseg < SEGMAX) {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    for (int j = tid; j < 2 * 32 * SEGMAX; j += 256) {
+      const int r = j / SEGMAX;
+      if (j - r * SEGMAX >= nseg) lds[r >> 5][(r & 31) * SEGMAX + (j - r * SEGMAX)] = z;
+    }
+  }
+
+  // ---- epilogue state
+  float Mr[2], Sr[2], Ms2[2];   // sample: running max, sum relative to Ms2, max * scale2 (rounded)
+  int Ir[2];                    // greedy argmax
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) { Mr[nt] = -INFINITY; Sr[nt] = 0.f; Ms2[nt] = -INFINITY; Ir[nt] = 0x7FFFFFFF; }
+  const float s2 = a.scale2;
+  const float invT = s2 * kLn2;
+
+  auto epilogue = [&](f32x16_t (&acc)[2], int t) __attribute__((always_inline)) {
+    const int vt = vbase + t * 32 + 16 * half;   // entry of accumulator 0
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      if (MODE == kModeGreedy) {
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (acc[t][j] > bv) { bv = acc[t][j]; bi = c * kChunk + t * 32 + 16 * half + j; }
-      argmax_merge(bv, bi, __shfl_xor(bv, 32), __shfl_xor(bi, 32));
-      if (half == 0 && valid) {
-        a.L[o] = make_float2(bv, 0.f);
-        a.I[o] = bi;
-        if (!(fabsf(bv) <= 3.0e38f)) set_flag(a.status, kFlagNonFinite);
-      }
-    } else if (MODE == kModeSample) {
-      float mx = -INFINITY;
+          if (acc[nt][j] > Mr[nt]) { Mr[nt] = acc[nt][j]; Ir[nt] = vt + j; }
+      } else if (MODE == kModeSample) {
+        float tm = acc[nt][0];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+        for (int j = 1; j < 16; ++j) tm = fmaxf(tm, acc[nt][j]);
+        if (tm != -INFINITY) {
+          if (tm > Mr[nt]) {
+            const float nms2 = tm * s2;
+            Sr[nt] *= __builtin_amdgcn_exp2f(Ms2[nt] - nms2);   // keeps a NaN sum NaN
+            Mr[nt] = tm;
+            Ms2[nt] = nms2;
+          }
+          float acc_s = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, acc[t][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      float sm = 0.f;
-      if (mx != -INFINITY) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) sm += __builtin_amdgcn_exp2f((acc[t][j] - mx) * a.scale2);
-      }
-      sm += __shfl_xor(sm, 32);
-      if (half == 0 && valid) {
-        a.L[o] = make_float2(mx, sm);
-        if (!(sm <= 3.0e38f) || mx == INFINITY) set_flag(a.status, kFlagNonFinite);
-      }
-    } else {  // residual mass max(0, p_t - p_d) per chunk
-      float sm = 0.f;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        float tv[16];
-        const int vb = c * kChunk + t * 32 + 16 * half;
-        if (valid) load16<UT>(tptr, a.u_vec_ok, vb, a.V, tv);
-        else {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) tv[e] = -INFINITY;
+          for (int j = 0; j < 16; ++j) acc_s += __builtin_amdgcn_exp2f(fmaf(acc[nt][j], s2, -Ms2[nt]));
+          Sr[nt] += acc_s;
         }
+      } else {
+        float tv[16];
+        load16<UT>(trow[nt], a.u_vec_ok && valid[nt], vt, valid[nt] ? a.V : 0, tv);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const float pt = __builtin_amdgcn_exp2f((tv[j] - mt) * a.scale2 - lrt2);
-          const float pd = __builtin_amdgcn_exp2f((acc[t][j] * invT - lse_d) * kLog2e);
-          sm += fmaxf(pt - pd, 0.f);
+          const float pt = __builtin_amdgcn_exp2f((tv[j] - mt[nt]) * s2 - lrt2[nt]);
+          const float pd = __builtin_amdgcn_exp2f((acc[nt][j] * invT - lse_d[nt]) * kLog2e);
+          Sr[nt] += fmaxf(pt - pd, 0.f);
         }
       }
-      sm += __shfl_xor(sm, 32);
-      if (half == 0 && valid) {
-        a.L[o] = make_float2(0.f, sm);
-        if (!(sm <= 3.0e38f)) set_flag(a.status, kFlagNonFinite);
+    }
+    if ((t & 3) == 3) {   // chunk complete: combine the two half-rows and write
+      const int c = c0 + (t >> 2);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int row = rg * 256 + wv * 64 + nt * 32 + n;
+        const int64_t o = (int64_t)row * a.nch + c;
+        if (MODE == kModeGreedy) {
+          float bv = Mr[nt];
+          int bi = Ir[nt];
+          argmax_merge(bv, bi, __shfl_xor(bv, 32), __shfl_xor(bi, 32));
+          if (half == 0 && valid[nt]) {
+            a.L[o] = make_float2(bv, 0.f);
+            a.I[o] = bi;
+            if (nonfinite(bv)) set_flag(a.status, kFlagNonFinite);
+          }
+          Mr[nt] = -INFINITY; Ir[nt] = 0x7FFFFFFF;
+        } else if (MODE == kModeSample) {
+          // sums were taken relative to Ms2 = round(M * s2): undo that rounding
+          if (valid[nt] && nonfinite(Sr[nt])) set_flag(a.status, kFlagNonFinite);
+          float S = Sr[nt];
+          if (S > 0.f) S *= __builtin_amdgcn_exp2f(-fmaf(Mr[nt], s2, -Ms2[nt]));
+          const float Mo = __shfl_xor(Mr[nt], 32);
+          const float So = __shfl_xor(S, 32);
+          const float Mn = fmaxf(Mr[nt], Mo);
+          float St = 0.f;
+          if (Mn != -INFINITY) {
+            if (S > 0.f) St += S * __builtin_amdgcn_exp2f((Mr[nt] - Mn) * s2);
+            if (So > 0.f) St += So * __builtin_amdgcn_exp2f((Mo - Mn) * s2);
+          }
+          if (half == 0 && valid[nt]) {
+            a.L[o] = make_float2(Mn, St);
+            if (nonfinite(St) || Mn == INFINITY) set_flag(a.status, kFlagNonFinite);
+          }
+          Mr[nt] = -INFINITY; Sr[nt] = 0.f; Ms2[nt] = -INFINITY;
+        } else {
+          const float St = Sr[nt] + __shfl_xor(Sr[nt], 32);
+          if (half == 0 && valid[nt]) {
+            a.L[o] = make_float2(0.f, St);
+            if (nonfinite(St)) set_flag(a.status, kFlagNonFinite);
+          }
+          Sr[nt] = 0.f;
+        }
       }
     }
+  };
+
+  URaw<UT> ub[2][2];
+  f32x16_t acc[2][2];
+  // ---- prologue: W2t tiles 0 and 1, U of tiles 0 and 1
+  stage_load(st[0], 0);
+  stage_load(st[1], 1);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    ub[0][nt].fetch(urow[nt], vbase + 16 * half, a.V, a.u_vec_ok, valid[nt]);
+    ub[1][nt].fetch(urow[nt], vbase + 32 + 16 * half, a.V, a.u_vec_ok, valid[nt]);
+  }
+
+  auto step = [&](auto Pc, int t) __attribute__((always_inline)) {
+    constexpr int P = decltype(Pc)::value;
+    stage_store(st[P], P);
+    // prefetch two tiles ahead (the last two prefetches repeat the final tile)
+    const int tp = min(t + 2, T - 1);
+    stage_load(st[P], tp);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) ub[P][nt].unpack(acc[P][nt]);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      ub[P][nt].fetch(urow[nt], vbase + tp * 32 + 16 * half, a.V, a.u_vec_ok, valid[nt]);
+    __syncthreads();
+    if (wave_active) {
+      const u32x4_t* tile = lds[P] + arow * SEGMAX;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4_t w = tile[(2 * ks + half) ^ aswz];
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, w);
+        acc[P][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bf[0][ks], acc[P][0], 0, 0, 0);
+        acc[P][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bf[1][ks], acc[P][1], 0, 0, 0);
+      }
+      if (t >= 1) epilogue(acc[1 - P], t - 1);
+    }
+  };
+  for (int t = 0; t < T; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < T) step(std::integral_constant<int, 1>{}, t + 1);
+  }
+  // T is a multiple of 4 (four tiles per chunk): the last tile used buffer 1
+  if (wave_active) epilogue(acc[1], T - 1);
+}
+
+// ------------------------------------------------ MFMA, LDS-DMA pipeline
+// Same contraction and epilogue as k_markov_mfma_reg, with both operands that
+// stream (the W2t tile and the 256 x 32 slab of U) moved by direct-to-LDS loads
+// (global_load_lds_dwordx4) into an NBUF-deep LDS ring: tile t+NBUF-1 is in
+// flight while tile t is computed, at no register cost.  Requirements: rank a
+// multiple of 64 (KS >= 4), U rows 16-byte aligned and V a multiple of the
+// elements per 16 bytes; other shapes use k_markov_mfma_reg.
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+__device__ __forceinline__ int u_swizzle(int rr) { return (rr >> 1) ^ (rr >> 3); }
+
+// gfx9 s_waitcnt immediate: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt_hi[15:14].  Waits until at most N vector-memory operations of this
+// wave are outstanding and all of its LDS operations are done.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+template <typename UT, int KS, int MODE, int NBUF>
+__global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
+  constexpr int SEGMAX = 2 * KS;                          // W2t row segments
+  constexpr int EPL = 16 / (int)sizeof(UT);               // U elements per segment
+  constexpr int SPR = 32 / EPL;                           // U segments per row of a tile
+  constexpr int USEG = 16 / EPL;                          // U segments read per lane (16 values)
+  constexpr int W2_SEGS = 32 * SEGMAX;
+  constexpr int SLOT = W2_SEGS + 256 * SPR;               // 16-byte units per ring slot
+  constexpr int NW = KS / 4;                              // W2 DMA ops per wave per tile
+  constexpr int NU = SPR;                                 // U DMA ops per wave per tile
+  constexpr int OPS = NW + NU;
+  static_assert(KS >= 4 && KS % 4 == 0, "DMA path needs rank >= 64");
+  static_assert(NBUF == 4, "ring depth");
+  __shared__ u32x4_t ring[NBUF * SLOT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, sb = b >> 3;
+  const int rg = sb % a.nrg;
+  const int cg = (sb / a.nrg) * 8 + xcd;
+  if (cg >= a.ncg) return;
+  int nrows = a.R;
+  if (MODE == kModeResid) nrows = *a.rej_count;
+  if (rg * 256 >= nrows) return;
+  const int c0 = cg * a.cg, c1 = min(a.nch, c0 + a.cg);
+  const int T = (c1 - c0) * 4;
+  const int vbase = c0 * kChunk;
+  const int nseg = a.rank >> 3;
+  const int smask = ((nseg & (nseg - 1)) == 0) ? min(nseg, 16) - 1 : 0;
+  const bool wave_active = rg * 256 + wv * 64 < nrows;
+
+  // ---- rows computed by this lane: column n of the wave's two 32-row tiles
+  const int n = lane & 31, half = lane >> 5;
+  bool valid[2];
+  const UT* trow[2];
+  int prevs[2];
+  float mt[2], lrt2[2], lse_d[2];
+  auto row_info = [&](int row, int& req, int& kk, int& tr, int& qr) __attribute__((always_inline)) {
+    req = 0; kk = a.k; tr = 0; qr = 0;
+    if (row < nrows) {
+      if (MODE == kModeResid) {
+        const int4 e = a.rej[row];
+        req = e.x; kk = e.y; tr = e.z; qr = e.w;
+      } else {
+        req = row;
+      }
+    }
+  };
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int row = rg * 256 + wv * 64 + nt * 32 + n;
+    valid[nt] = row < nrows;
+    int req, kk, tr, qr;
+    row_info(row, req, kk, tr, qr);
+    int prev = 0;
+    if (valid[nt]) {
+      prev = (MODE != kModeResid && kk == 1) ? a.x0[req]
+                                             : a.x[(int64_t)req * (a.gamma + 1) + (kk - 1)];
+      if (prev < 0 || prev >= a.V) { set_flag(a.status, kFlagBadToken); prev = 0; }
+    }
+    prevs[nt] = prev;
+    trow[nt] = reinterpret_cast<const UT*>(a.target) + (int64_t)tr * a.V;
+    mt[nt] = 0.f; lrt2[nt] = 0.f; lse_d[nt] = 0.f;
+    if (MODE == kModeResid && valid[nt]) {
+      const float2 nrm = a.lse_t[qr];
+      mt[nt] = nrm.x;
+      lrt2[nt] = nrm.y * kLog2e;
+      lse_d[nt] = a.lse_d[(int64_t)req * a.gamma + (kk - 1)];
+    }
+  }
+  bf16x8_t Bf[2][KS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const uint16_t* erow = a.W1 + (int64_t)prevs[nt] * a.rank + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t z = {};
+      Bf[nt][ks] = (valid[nt] && ks * 16 < a.rank) ? *reinterpret_cast<const bf16x8_t*>(erow + ks * 16) : z;
+    }
+  }
+  const int m = lane & 31;
+  const int arow = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+  const int aswz = seg_swizzle(arow) & smask;
+
+  // ---- DMA descriptors of this thread (fixed across tiles)
+  int w2_off[NW];
+  int w2_row[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int idx = (wv + 4 * i) * 64 + lane;
+    const int r = idx / SEGMAX, p = idx - r * SEGMAX;
+    w2_row[i] = r;
+    w2_off[i] = (p < nseg) ? (p ^ (seg_swizzle(r) & smask)) * 8 : -1;
+  }
+  const UT* u_ptr[NU];
+  int u_seg[NU];
+#pragma unroll
+  for (int i = 0; i < NU; ++i) {
+    const int idx = (wv + 4 * i) * 64 + lane;
+    const int rr = idx / SPR, sp = idx - rr * SPR;
+    u_seg[i] = (sp ^ (u_swizzle(rr) & (SPR - 1))) * EPL;
+    int req, kk, tr, qr;
+    const int row = rg * 256 + rr;
+    row_info(row < nrows ? row : rg * 256, req, kk, tr, qr);
+    u_ptr[i] = reinterpret_cast<const UT*>(a.U) + ((int64_t)req * a.gamma + (kk - 1)) * a.V;
+  }
+  const int vmax_seg = a.V - EPL;     // last in-range segment start (V % EPL == 0)
+  auto issue = [&](auto Sc, int t) __attribute__((always_inline)) {
+    constexpr int S = decltype(Sc)::value;
+    const int vb = vbase + min(t, T - 1) * 32;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int g = wv + 4 * i;
+      if (w2_off[i] >= 0) {
+        const int v = min(vb + w2_row[i], a.V - 1);
+        __builtin_amdgcn_global_load_lds(
+            (gvoid_t*)(a.W2t + (int64_t)v * a.rank + w2_off[i]),
+            (lvoid_t*)(ring + S * SLOT + g * 64), 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int g = wv + 4 * i;
+      const int v = min(vb + u_seg[i], vmax_seg);
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(u_ptr[i] + v),
+                                       (lvoid_t*)(ring + S * SLOT + W2_SEGS + g * 64), 16, 0, 0);
+    }
+  };
+  if (nseg < SEGMAX) {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    for (int j = tid; j < NBUF * W2_SEGS; j += 256) {
+      const int sl = j / W2_SEGS, u = j - sl * W2_SEGS;
+      if (u % SEGMAX >= nseg) ring[sl * SLOT + u] = z;
+    }
+  }
+  // A tile whose last entries lie past V: the U slots of those entries hold
+  // clamped (wrong) data; overwrite them with -inf after the DMA has landed.
+  auto mask_tail = [&](auto Sc, int t) __attribute__((always_inline)) {
+    constexpr int S = decltype(Sc)::value;
+    const int vb = vbase + t * 32;
+    if (vb + 32 > a.V) {
+      const uint32_t ninf = (EPL == 8) ? 0xFF80FF80u : 0xFF800000u;
+      const u32x4_t w = {ninf, ninf, ninf, ninf};
+      for (int j = tid; j < 256 * SPR; j += 256) {
+        const int rr = j / SPR, sp = j - rr * SPR;
+        const int seg = sp ^ (u_swizzle(rr) & (SPR - 1));
+        if (vb + seg * EPL >= a.V) ring[S * SLOT + W2_SEGS + j] = w;
+      }
+      // LDS writes done (lgkmcnt 0), no wait on vector memory (vmcnt 63)
+      __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+      __builtin_amdgcn_s_barrier();
+    }
+  };
+
+  // ---- epilogue state
+  float Mr[2], Sr[2], Ms2[2];
+  int Ir[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) { Mr[nt] = -INFINITY; Sr[nt] = 0.f; Ms2[nt] = -INFINITY; Ir[nt] = 0x7FFFFFFF; }
+  const float s2 = a.scale2;
+  const float invT = s2 * kLn2;
+
+  // straight-line part of the epilogue of one tile: x = acc + U, then the
+  // running (max, sum) or argmax update, branch-free
+  auto epi_hot = [&](f32x16_t (&acc)[2], const u32x4_t (&uw)[2][USEG], int t) __attribute__((always_inline)) {
+    const int vt = vbase + t * 32 + 16 * half;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float x[16];
+#pragma unroll
+      for (int e = 0; e < USEG; ++e) {
+        if (EPL == 8) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            x[8 * e + 2 * q] = acc[nt][8 * e + 2 * q] + bf16_lo(uw[nt][e][q]);
+            x[8 * e + 2 * q + 1] = acc[nt][8 * e + 2 * q + 1] + bf16_hi(uw[nt][e][q]);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) x[4 * e + q] = acc[nt][4 * e + q] + __uint_as_float(uw[nt][e][q]);
+        }
+      }
+      if (MODE == kModeGreedy) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const bool gt = x[j] > Mr[nt];
+          Mr[nt] = gt ? x[j] : Mr[nt];
+          Ir[nt] = gt ? vt + j : Ir[nt];
+        }
+      } else if (MODE == kModeSample) {
+        float tm = fmaxf(x[0], x[1]);
+#pragma unroll
+        for (int j = 2; j < 16; ++j) tm = fmaxf(tm, x[j]);
+        const float nM = fmaxf(Mr[nt], tm);
+        const float nMs2 = nM * s2;
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sum += __builtin_amdgcn_exp2f(fmaf(x[j], s2, -nMs2));
+        // rescale the running sum to the new maximum (exp2(-inf) = 0 while empty);
+        // a NaN sum stays NaN; an all -inf tile leaves the state unchanged
+        const float newS = Sr[nt] * __builtin_amdgcn_exp2f(Ms2[nt] - nMs2) + sum;
+        const bool empty = nM == -INFINITY;
+        Sr[nt] = empty ? Sr[nt] : newS;
+        Ms2[nt] = empty ? Ms2[nt] : nMs2;
+        Mr[nt] = nM;
+      } else {
+        float tv[16];
+        load16<UT>(trow[nt], a.u_vec_ok && valid[nt], vt, valid[nt] ? a.V : 0, tv);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float pt = __builtin_amdgcn_exp2f((tv[j] - mt[nt]) * s2 - lrt2[nt]);
+          const float pd = __builtin_amdgcn_exp2f((x[j] * invT - lse_d[nt]) * kLog2e);
+          Sr[nt] += fmaxf(pt - pd, 0.f);
+        }
+      }
+    }
+  };
+  // chunk completion after tile t: combine the two half-rows and write
+  auto epi_chunk = [&](int t) __attribute__((always_inline)) {
+    if ((t & 3) != 3) return;
+    const int c = c0 + (t >> 2);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int row = rg * 256 + wv * 64 + nt * 32 + n;
+      const int64_t o = (int64_t)row * a.nch + c;
+      if (MODE == kModeGreedy) {
+        float bv = Mr[nt];
+        int bi = Ir[nt];
+        argmax_merge(bv, bi, __shfl_xor(bv, 32), __shfl_xor(bi, 32));
+        if (half == 0 && valid[nt]) {
+          a.L[o] = make_float2(bv, 0.f);
+          a.I[o] = bi;
+          if (nonfinite(bv)) set_flag(a.status, kFlagNonFinite);
+        }
+        Mr[nt] = -INFINITY; Ir[nt] = 0x7FFFFFFF;
+      } else if (MODE == kModeSample) {
+        if (valid[nt] && nonfinite(Sr[nt])) set_flag(a.status, kFlagNonFinite);
+        float S = Sr[nt];
+        // sums were taken relative to Ms2 = round(M * s2): undo that rounding
+        if (S > 0.f) S *= __builtin_amdgcn_exp2f(-fmaf(Mr[nt], s2, -Ms2[nt]));
+        const float Mo = __shfl_xor(Mr[nt], 32);
+        const float So = __shfl_xor(S, 32);
+        const float Mn = fmaxf(Mr[nt], Mo);
+        float St = 0.f;
+        if (Mn != -INFINITY) {
+          if (S > 0.f) St += S * __builtin_amdgcn_exp2f((Mr[nt] - Mn) * s2);
+          if (So > 0.f) St += So * __builtin_amdgcn_exp2f((Mo - Mn) * s2);
+        }
+        if (half == 0 && valid[nt]) {
+          a.L[o] = make_float2(Mn, St);
+          if (nonfinite(St) || Mn == INFINITY) set_flag(a.status, kFlagNonFinite);
+        }
+        Mr[nt] = -INFINITY; Sr[nt] = 0.f; Ms2[nt] = -INFINITY;
+      } else {
+        const float St = Sr[nt] + __shfl_xor(Sr[nt], 32);
+        if (half == 0 && valid[nt]) {
+          a.L[o] = make_float2(0.f, St);
+          if (nonfinite(St)) set_flag(a.status, kFlagNonFinite);
+        }
+        Sr[nt] = 0.f;
+      }
+    }
+  };
+  auto read_u = [&](auto Sc, u32x4_t (&uw)[2][USEG]) __attribute__((always_inline)) {
+    constexpr int S = decltype(Sc)::value;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int rr = wv * 64 + nt * 32 + n;
+      const u32x4_t* ul = ring + S * SLOT + W2_SEGS + rr * SPR;
+      const int usw = u_swizzle(rr) & (SPR - 1);
+#pragma unroll
+      for (int e = 0; e < USEG; ++e) uw[nt][e] = ul[(USEG * half + e) ^ usw];
+    }
+  };
+
+  f32x16_t acc[2][2];
+  // Schedule of tile t (ring slot t % 4, accumulator buffer t % 2):
+  //   wait for tile t's DMA, barrier, DMA of tile t+2 into the slot of t-2,
+  //   then the MFMAs of tile t interleaved with the epilogue of tile t-1
+  //   (whose U values are still in slot (t-1) % 4).
+  auto step = [&](auto Sc, int t, bool with_epi) __attribute__((always_inline)) {
+    constexpr int S = decltype(Sc)::value;
+    constexpr int P = S & 1;
+    constexpr int SP = (S + 3) & 3;                 // slot of tile t-1
+    constexpr int SN = (S + 2) & 3;                 // slot of tile t+2 (= t-2)
+    wait_vm_lgkm0<OPS>();                           // tile t+1 may still be in flight
+    __builtin_amdgcn_s_barrier();
+    mask_tail(Sc, t);
+    issue(std::integral_constant<int, SN>{}, t + 2);
+    if (wave_active) {
+      const u32x4_t* tile = ring + S * SLOT + arow * SEGMAX;
+      u32x4_t aw[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) aw[ks] = tile[(2 * ks + half) ^ aswz];
+      u32x4_t uw[2][USEG];
+      if (with_epi) read_u(std::integral_constant<int, SP>{}, uw);
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x16_t zero = {};
+      // the epilogue of tile t-1 is cut into 2*KS slices, one after each MFMA:
+      // first half = x = acc + U with the running max (or argmax), second half
+      // = the exp sums relative to the new maximum
+      constexpr int NSL = 2 * KS;
+      constexpr int HALF_SL = NSL / 2;
+      constexpr int PER_A = (32 + HALF_SL - 1) / HALF_SL;
+      float x[2][16];
+      float tmx[2] = {-INFINITY, -INFINITY};
+      float ssum[2] = {0.f, 0.f};
+      float nM[2], nMs2[2];
+      const int vt = vbase + (t - 1) * 32 + 16 * half;
+#pragma unroll
+      for (int i = 0; i < NSL; ++i) {
+        const int ks = i >> 1, ntm = i & 1;
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, aw[ks]);
+        acc[P][ntm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bf[ntm][ks], ks ? acc[P][ntm] : zero, 0, 0, 0);
+        if (with_epi && MODE != kModeResid) {
+          if (i < HALF_SL) {
+#pragma unroll
+            for (int q = 0; q < PER_A; ++q) {
+              const int e = i * PER_A + q;
+              if (e < 32) {
+                const int nt = e >> 4, j = e & 15;
+                const uint32_t wd = uw[nt][j / EPL][(j % EPL) / (EPL / 4)];
+                const float u = (EPL == 8) ? ((j & 1) ? bf16_hi(wd) : bf16_lo(wd)) : __uint_as_float(wd);
+                x[nt][j] = acc[1 - P][nt][j] + u;
+                if (MODE == kModeGreedy) {
+                  const bool gt = x[nt][j] > Mr[nt];
+                  Mr[nt] = gt ? x[nt][j] : Mr[nt];
+                  Ir[nt] = gt ? vt + j : Ir[nt];
+                  asm volatile("" : "+v"(Mr[nt]), "+v"(Ir[nt]));
+                } else {
+                  tmx[nt] = fmaxf(tmx[nt], x[nt][j]);
+                  // keep this slice's work here (IR passes would sink it)
+                  asm volatile("" : "+v"(x[nt][j]), "+v"(tmx[nt]));
+                }
+              }
+            }
+          } else if (MODE == kModeSample) {
+            if (i == HALF_SL) {
+#pragma unroll
+              for (int nt = 0; nt < 2; ++nt) {
+                nM[nt] = fmaxf(Mr[nt], tmx[nt]);
+                nMs2[nt] = nM[nt] * s2;
+              }
+            }
+#pragma unroll
+            for (int q = 0; q < PER_A; ++q) {
+              const int e = (i - HALF_SL) * PER_A + q;
+              if (e < 32) {
+                const int nt = e >> 4, j = e & 15;
+                ssum[nt] += __builtin_amdgcn_exp2f(fmaf(x[nt][j], s2, -nMs2[nt]));
+                asm volatile("" : "+v"(ssum[nt]));
+              }
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (with_epi) {
+        if (MODE == kModeSample) {
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            // rescale the running sum to the new maximum; an all -inf tile
+            // leaves the state unchanged; a NaN sum stays NaN
+            const float newS = Sr[nt] * __builtin_amdgcn_exp2f(Ms2[nt] - nMs2[nt]) + ssum[nt];
+            const bool empty = nM[nt] == -INFINITY;
+            Sr[nt] = empty ? Sr[nt] : newS;
+            Ms2[nt] = empty ? Ms2[nt] : nMs2[nt];
+            Mr[nt] = nM[nt];
+          }
+        } else if (MODE == kModeResid) {
+          epi_hot(acc[1 - P], uw, t - 1);
+        }
+      }
+    }
+    if (with_epi && wave_active) epi_chunk(t - 1);
+  };
+  // prologue: tiles 0 and 1 in flight, then step 0 (no epilogue yet)
+  issue(std::integral_constant<int, 0>{}, 0);
+  issue(std::integral_constant<int, 1>{}, 1);
+  step(std::integral_constant<int, 0>{}, 0, false);
+  int t = 1;
+  for (; t + 3 < T; t += 4) {
+    step(std::integral_constant<int, 1>{}, t, true);
+    step(std::integral_constant<int, 2>{}, t + 1, true);
+    step(std::integral_constant<int, 3>{}, t + 2, true);
+    step(std::integral_constant<int, 0>{}, t + 3, true);
+  }
+  // T is a multiple of 4, so three steps remain (slots 1, 2, 3)
+  step(std::integral_constant<int, 1>{}, t, true);
+  step(std::integral_constant<int, 2>{}, t + 1, true);
+  step(std::integral_constant<int, 3>{}, t + 2, true);
+  // epilogue of the last tile (T-1, slot 3, accumulator buffer 1)
+  wait_vm_lgkm0<0>();
+  if (wave_active) {
+    u32x4_t uw[2][USEG];
+    read_u(std::integral_constant<int, 3>{}, uw);
+    epi_hot(acc[1], uw, T - 1);
+    epi_chunk(T - 1);
   }
 }
 
@@ -369,7 +956,7 @@ __global__ __launch_bounds__(256) void k_markov_valu(MarkovArgs a) {
       sm = wave_sum(sm);
       if (lane == 0) {
         a.L[o] = make_float2(mx, sm);
-        if (!(sm <= 3.0e38f) || mx == INFINITY) set_flag(a.status, kFlagNonFinite);
+        if (nonfinite(sm) || mx == INFINITY) set_flag(a.status, kFlagNonFinite);
       }
     } else {
       const UT* tptr = reinterpret_cast<const UT*>(a.target) + (int64_t)trow * a.V;
@@ -418,12 +1005,33 @@ hipError_t launch_row_stats(const RowStatsArgs& a0, bool bf16, bool greedy, hipS
 }
 
 template <typename UT, int MODE>
-static void launch_mfma_ks(MarkovArgs& a, int grid, hipStream_t st) {
+static void launch_mfma_ks(MarkovArgs& a, int grid, hipStream_t st, bool dma) {
   const int nks = a.rank / 16;
-  if (nks <= 4) hipLaunchKernelGGL((k_markov_mfma<UT, 4, MODE>), dim3(grid), dim3(256), 0, st, a);
-  else if (nks <= 8) hipLaunchKernelGGL((k_markov_mfma<UT, 8, MODE>), dim3(grid), dim3(256), 0, st, a);
-  else if (nks <= 16) hipLaunchKernelGGL((k_markov_mfma<UT, 16, MODE>), dim3(grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_markov_mfma<UT, 32, MODE>), dim3(grid), dim3(256), 0, st, a);
+  if (dma && nks >= 4) {
+    // ring depth: four slots when they fit in LDS, else two
+    constexpr int SPR = 32 * (int)sizeof(UT) / 16;
+#define DSPARK_DMA(KS_)                                                                          \
+    {                                                                                             \
+      constexpr int SLOTB = (32 * 2 * KS_ + 256 * SPR) * 16;                                      \
+      if (4 * SLOTB <= 160 * 1024) {                                                              \
+        hipLaunchKernelGGL((k_markov_mfma<UT, (4 * SLOTB <= 160 * 1024 ? KS_ : 4), MODE, 4>),    \
+                           dim3(grid), dim3(256), 0, st, a);                                      \
+        return;                                                                                   \
+      }                                                                                           \
+    }
+    if (nks <= 4) DSPARK_DMA(4)
+    else if (nks <= 8) DSPARK_DMA(8)
+    else if (nks <= 16) DSPARK_DMA(16)
+    else DSPARK_DMA(32)
+#undef DSPARK_DMA
+    // ring does not fit in LDS: register-staged kernel below
+  }
+  if (nks <= 1) hipLaunchKernelGGL((k_markov_mfma_reg<UT, 1, MODE>), dim3(grid), dim3(256), 0, st, a);
+  else if (nks <= 2) hipLaunchKernelGGL((k_markov_mfma_reg<UT, 2, MODE>), dim3(grid), dim3(256), 0, st, a);
+  else if (nks <= 4) hipLaunchKernelGGL((k_markov_mfma_reg<UT, 4, MODE>), dim3(grid), dim3(256), 0, st, a);
+  else if (nks <= 8) hipLaunchKernelGGL((k_markov_mfma_reg<UT, 8, MODE>), dim3(grid), dim3(256), 0, st, a);
+  else if (nks <= 16) hipLaunchKernelGGL((k_markov_mfma_reg<UT, 16, MODE>), dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_markov_mfma_reg<UT, 32, MODE>), dim3(grid), dim3(256), 0, st, a);
 }
 
 hipError_t launch_markov_stats(const MarkovArgs& a0, bool u_bf16, bool w_bf16, int mode,
@@ -432,23 +1040,25 @@ hipError_t launch_markov_stats(const MarkovArgs& a0, bool u_bf16, bool w_bf16, i
   if (w_bf16) {
     a.W1 = reinterpret_cast<const uint16_t*>(a.W1v);
     a.W2t = reinterpret_cast<const uint16_t*>(a.W2tv);
-    a.nrt = (a.nrows_cap + 31) / 32;
-    a.nrtg = (a.nrt + 3) / 4;
-    // chunks per wave: aim at about four waves per SIMD across the chip
-    const int64_t target_waves = 4096;
-    int cgw = (int)(((int64_t)a.nrt * a.nch + target_waves - 1) / target_waves);
+    a.nrg = (a.nrows_cap + 255) / 256;
+    // chunks per workgroup: about one workgroup per compute unit
+    int cgw = (int)(((int64_t)a.nrg * a.nch + 255) / 256);
     if (cgw < 1) cgw = 1;
     a.cg = cgw;
     a.ncg = (a.nch + cgw - 1) / cgw;
-    const int grid = a.nrtg * ((a.ncg + 7) / 8) * 8;
+    const int grid = a.nrg * ((a.ncg + 7) / 8) * 8;
+    // the LDS-DMA pipeline needs 16-byte aligned U rows (and target rows in
+    // residual mode) with V a multiple of the elements per 16 bytes
+    const int epl = u_bf16 ? 8 : 4;
+    const bool dma = a.u_vec_ok && (a.V % epl) == 0 && a.V >= epl;
     if (u_bf16) {
-      if (mode == kModeSample) launch_mfma_ks<uint16_t, kModeSample>(a, grid, st);
-      else if (mode == kModeGreedy) launch_mfma_ks<uint16_t, kModeGreedy>(a, grid, st);
-      else launch_mfma_ks<uint16_t, kModeResid>(a, grid, st);
+      if (mode == kModeSample) launch_mfma_ks<uint16_t, kModeSample>(a, grid, st, dma);
+      else if (mode == kModeGreedy) launch_mfma_ks<uint16_t, kModeGreedy>(a, grid, st, dma);
+      else launch_mfma_ks<uint16_t, kModeResid>(a, grid, st, dma);
     } else {
-      if (mode == kModeSample) launch_mfma_ks<float, kModeSample>(a, grid, st);
-      else if (mode == kModeGreedy) launch_mfma_ks<float, kModeGreedy>(a, grid, st);
-      else launch_mfma_ks<float, kModeResid>(a, grid, st);
+      if (mode == kModeSample) launch_mfma_ks<float, kModeSample>(a, grid, st, dma);
+      else if (mode == kModeGreedy) launch_mfma_ks<float, kModeGreedy>(a, grid, st, dma);
+      else launch_mfma_ks<float, kModeResid>(a, grid, st, dma);
     }
   } else {
     const int grid = grid_for((int64_t)a.nrows_cap * a.nch);
