@@ -37,8 +37,11 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=2)
-    p.add_argument("--cpu-sample", type=int, default=4, help="requests in the oracle sample")
+    p.add_argument("--cpu-sample", type=int, default=48, help="requests in the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="before the rounds, copy a buffer of this many MiB three times "
+                        "(device to device), the known-size reference for HBM byte counters")
     return p.parse_args()
 
 
@@ -87,8 +90,41 @@ def stats_kernel_bytes(cfg):
     round amortised over the gamma launches."""
     s = cfg.dtype.itemsize
     nch = (cfg.V + 127) // 128
-    return (s * cfg.R * cfg.V + s * cfg.R * cfg.rank + 4 * cfg.R * nch
+    return (s * cfg.R * cfg.V + s * cfg.R * cfg.rank + 8 * cfg.R * nch
             + (s * cfg.rank * cfg.V) / cfg.gamma)
+
+
+STATS_SOURCES = ("stats.hip", "launch.hpp", "device_common.hpp", "sampling.hpp", "workspace.hpp")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_markov_mfma_R256_g16_V129280_r256_counters.txt")
+
+
+def stats_source_sha():
+    """sha256 over the sources the draft statistics kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in STATS_SOURCES:
+        with open(os.path.join(ROOT, "draft_verify_sampling_head_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per launch of the statistics kernel from the committed
+    FETCH_SIZE / WRITE_SIZE summary, calibrated against a device copy of known
+    size; None when the file is missing or the kernel sources have changed
+    since the counters were taken."""
+    try:
+        kv = {}
+        with open(COUNTERS_FILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith((" ", "#", "|")):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_sha256") != stats_source_sha():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
@@ -106,6 +142,15 @@ def main():
     from draft_verify_sampling_head_amd import synth
 
     dev = torch.device("cuda:0")
+    if args.calib_copy_mib > 0:
+        nb = args.calib_copy_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: 3 x {nb} bytes")
+        del src, dst
     cfg = synth.config(args.config)
     t0 = time.time()
     inp = synth.make_inputs(cfg, device=dev)
@@ -208,7 +253,7 @@ def main():
         "device_status": status,
         "roofline": {"bound": "hbm", "kernel": "k_markov_mfma (draft statistics, per step)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(),
                      "avg_launch_us": avg_ms * 1e3, "bytes_per_launch": kb,
                      "mfma_tflops": mfma_tf, "mfma_frac": mfma_tf / MFMA_BF16_PEAK_TFLOPS},
         "cpu_baseline": cpu,
