@@ -94,37 +94,52 @@ def stats_kernel_bytes(cfg):
             + (s * cfg.rank * cfg.V) / cfg.gamma)
 
 
-STATS_SOURCES = ("stats.hip", "launch.hpp", "device_common.hpp", "sampling.hpp", "workspace.hpp")
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_markov_mfma_R256_g16_V129280_r256_counters.txt")
+# kernel -> (sources it is built from, committed counter summary)
+KERNELS = {
+    "k_markov_mfma": (("stats.hip", "launch.hpp", "device_common.hpp", "sampling.hpp", "workspace.hpp"),
+                      "k_markov_mfma_R256_g16_V129280_r256_counters.txt"),
+    "k_draft_persistent": (("draft.hip", "launch.hpp", "device_common.hpp", "sampling.hpp",
+                            "workspace.hpp"),
+                           "k_draft_persistent_R256_g16_V129280_r256_counters.txt"),
+}
 
 
-def stats_source_sha():
-    """sha256 over the sources the draft statistics kernel is built from."""
+def source_sha(kernel):
+    """sha256 over the sources a kernel is built from."""
     import hashlib
     h = hashlib.sha256()
-    for f in STATS_SOURCES:
+    for f in KERNELS[kernel][0]:
         with open(os.path.join(ROOT, "draft_verify_sampling_head_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def counter_traffic():
-    """HBM bytes per launch of the statistics kernel from the committed
-    FETCH_SIZE / WRITE_SIZE summary, calibrated against a device copy of known
-    size; None when the file is missing or the kernel sources have changed
-    since the counters were taken."""
+def counter_traffic(kernel):
+    """HBM bytes per launch of `kernel` from its committed FETCH_SIZE /
+    WRITE_SIZE summary, calibrated against a device copy of known size; None
+    when the file is missing or the kernel sources have changed since the
+    counters were taken."""
     try:
         kv = {}
-        with open(COUNTERS_FILE) as fh:
+        with open(os.path.join(ROOT, "profiles", KERNELS[kernel][1])) as fh:
             for line in fh:
                 if ":" in line and not line.startswith((" ", "#", "|")):
                     k, v = line.split(":", 1)
                     kv[k.strip()] = v.strip()
-        if kv.get("source_sha256") != stats_source_sha():
+        if kv.get("source_sha256") != source_sha(kernel):
             return None
         return float(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def draft_kernel_bytes(cfg):
+    """Algorithmic bytes of the persistent draft launch (all gamma steps): U
+    once, W2 once, the gathered W1 rows, the anchors and the outputs (x,
+    logp_d, lse_d)."""
+    s = cfg.dtype.itemsize
+    R, G, V, r = cfg.R, cfg.gamma, cfg.V, cfg.rank
+    return s * R * G * V + s * r * V + s * R * G * r + 4 * R + 12 * R * G
 
 
 def main():
@@ -165,14 +180,17 @@ def main():
     ev = HipEvents(2 * cfg.gamma * K)
     stream = torch.cuda.current_stream()
 
+    n_timed = [0]
+
     def one_round(i, timed):
         buf.ell, buf.m = ells[i], ms[i]
         buf.N, buf.N_out = Ns[i:i + 1], Nouts[i:i + 1]
         if timed:
             j = (i - W) * 2 * cfg.gamma
-            L.draft_markov_profiled(inp["U"], inp["W1"], inp["W2t"], inp["x0"], cfg.T,
-                                    cfg.philox_seed, i, buf.x, buf.logp_d, buf.lse_d, buf.ws,
-                                    ev.array(j, cfg.gamma), ev.array(j + cfg.gamma, cfg.gamma))
+            n_timed[0] = L.draft_markov_profiled(inp["U"], inp["W1"], inp["W2t"], inp["x0"], cfg.T,
+                                                 cfg.philox_seed, i, buf.x, buf.logp_d, buf.lse_d,
+                                                 buf.ws, ev.array(j, cfg.gamma),
+                                                 ev.array(j + cfg.gamma, cfg.gamma))
         else:
             L.draft_markov(inp["U"], inp["W1"], inp["W2t"], inp["x0"], cfg.T, cfg.philox_seed, i,
                            buf.x, buf.logp_d, buf.lse_d, buf.ws)
@@ -209,20 +227,30 @@ def main():
                                         int(Ns[W + i].item())) for i in range(K)) / K
     hbm_frac_round = bytes_round / (t_total / K) / (HBM_PEAK_GBS * 1e9)
 
-    # dominant kernel: per-step draft statistics, events on the launch stream
+    # dominant kernel, timed with events on its launch stream: the persistent
+    # draft (one launch per round) or the per-step draft statistics kernel
+    nt = n_timed[0]
     durs = []
     for i in range(K):
         j = i * 2 * cfg.gamma
-        for k in range(cfg.gamma):
+        for k in range(nt):
             durs.append(ev.elapsed_ms(j + k, j + cfg.gamma + k))
     ev.close()
     avg_ms = float(np.mean(durs))
-    kb = stats_kernel_bytes(cfg)
+    if nt == 1:
+        kernel = "k_draft_persistent"
+        kdesc = "k_draft_persistent (whole draft: gamma steps, one cooperative launch)"
+        kb = draft_kernel_bytes(cfg)
+        kflops = 2.0 * cfg.R * cfg.rank * cfg.V * cfg.gamma
+    else:
+        kernel = "k_markov_mfma"
+        kdesc = "k_markov_mfma (draft statistics, per step)"
+        kb = stats_kernel_bytes(cfg)
+        kflops = 2.0 * cfg.R * cfg.rank * cfg.V
     achieved = kb / (avg_ms * 1e-3) / 1e9
-    kflops = 2.0 * cfg.R * cfg.rank * cfg.V
     mfma_tf = kflops / (avg_ms * 1e-3) / 1e12
     log(f"[bench] {K} rounds: {ms_per_step:.3f} ms/round, sum_ell={sum_ell}, sum_tau={sum_tau}, "
-        f"N_avg={N_avg:.1f}, n_rej={n_rej}, stats kernel {avg_ms * 1e3:.1f} us "
+        f"N_avg={N_avg:.1f}, n_rej={n_rej}, {kernel} {avg_ms * 1e3:.1f} us/launch "
         f"({achieved:.0f} GB/s, {mfma_tf:.0f} TFLOP/s), round HBM frac {hbm_frac_round:.3f}, "
         f"status={status}")
 
@@ -251,9 +279,9 @@ def main():
         "mean_ell": sum_ell / (K * cfg.R),
         "mean_tau": sum_tau / (K * cfg.R),
         "device_status": status,
-        "roofline": {"bound": "hbm", "kernel": "k_markov_mfma (draft statistics, per step)",
+        "roofline": {"bound": "hbm", "kernel": kdesc,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(kernel),
                      "avg_launch_us": avg_ms * 1e3, "bytes_per_launch": kb,
                      "mfma_tflops": mfma_tf, "mfma_frac": mfma_tf / MFMA_BF16_PEAK_TFLOPS},
         "cpu_baseline": cpu,

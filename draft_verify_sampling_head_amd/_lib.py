@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libdspark.so")
 F32, BF16 = 0, 1
 STATUS = {0: "DSPARK_OK", 1: "DSPARK_E_INVALID", 2: "DSPARK_E_UNSUPPORTED",
           3: "DSPARK_E_WORKSPACE", 4: "DSPARK_E_HIP"}
-FLAG_NONFINITE, FLAG_BAD_LEN, FLAG_BAD_TOKEN = 1, 2, 4
+FLAG_NONFINITE, FLAG_BAD_LEN, FLAG_BAD_TOKEN, FLAG_BARRIER = 1, 2, 4, 8
 CHUNK = 128
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
            "dspark_clear_status", "dspark_get_status", "dspark_draft_markov",
@@ -54,7 +54,7 @@ def load():
     L.dspark_get_status.argtypes = [P, sz, P]
     L.dspark_draft_markov.argtypes = [i32, i32, i32, i32, f32, u64, u64, P, i32, P, P, i32, P, P,
                                       P, P, P, P, sz, P]
-    L.dspark_draft_markov_profiled.argtypes = L.dspark_draft_markov.argtypes + [P, P]
+    L.dspark_draft_markov_profiled.argtypes = L.dspark_draft_markov.argtypes + [P, P, P]
     L.dspark_confidence.argtypes = [i32, i32, i32, i32, i32, P, i32, P, i32, P, i32, P, P, P, P]
     L.dspark_prefix_schedule.argtypes = [i32, i32, P, P, i32, i32, P, P, P, P, P]
     L.dspark_pack.argtypes = [i32, i32, P, P, i32, P, P, P, P, P, P, sz, P]
@@ -130,14 +130,19 @@ def draft_markov(U, W1, W2t, x0, T, seed, rnd, x, logp_d, lse_d, ws, margin=None
 def draft_markov_profiled(U, W1, W2t, x0, T, seed, rnd, x, logp_d, lse_d, ws, ev_begin, ev_end,
                           margin=None, stream=None):
     """As draft_markov, recording the caller's HIP events (ctypes arrays of
-    gamma hipEvent_t each) around every step's statistics kernel."""
+    gamma hipEvent_t each) around the draft's dominant kernel; returns the
+    number of event pairs recorded (1: one persistent launch for all steps,
+    gamma: one statistics launch per step)."""
     R, gamma, V = U.shape
     r = 0 if W1 is None else int(W1.shape[1])
+    n_timed = C.c_int(0)
     code = load().dspark_draft_markov_profiled(R, gamma, V, r, float(T), seed, rnd, _ptr(U), _dt(U),
                                                _ptr(W1), _ptr(W2t), _dt(W1), _ptr(x0), _ptr(x),
                                                _ptr(logp_d), _ptr(lse_d), _ptr(margin), _ptr(ws),
-                                               ws.numel(), _stream(stream), ev_begin, ev_end)
+                                               ws.numel(), _stream(stream), ev_begin, ev_end,
+                                               C.byref(n_timed))
     _check("dspark_draft_markov_profiled", code)
+    return int(n_timed.value)
 
 
 def confidence(h, W1, w, x, c, sts_T=None, V=None, stream=None):

@@ -74,7 +74,7 @@ static dspark_status draft_impl(int R, int gamma, int V, int r, float T, uint64_
                                 const void* W2t, dspark_dtype W_dt, const int32_t* x0, int32_t* x,
                                 float* logp_d, float* lse_d, float* margin, void* ws,
                                 size_t ws_bytes, hipStream_t stream, hipEvent_t* ev_begin,
-                                hipEvent_t* ev_end) {
+                                hipEvent_t* ev_end, int* n_timed) {
   dspark_status s = shape_check(R, gamma, V);
   if (s != DSPARK_OK) return s;
   if ((s = rank_check(r)) != DSPARK_OK) return s;
@@ -88,7 +88,7 @@ static dspark_status draft_impl(int R, int gamma, int V, int r, float T, uint64_
   if (ws_bytes < ws_layout(R, gamma, V).total) return DSPARK_E_WORKSPACE;
   return hip_status(launch_draft(R, gamma, V, r, T, seed, round, U, U_dt == DSPARK_BF16, W1, W2t,
                                  W_dt == DSPARK_BF16, x0, x, logp_d, lse_d, margin, ws, stream,
-                                 ev_begin, ev_end));
+                                 ev_begin, ev_end, n_timed));
 }
 
 dspark_status dspark_draft_markov(int R, int gamma, int V, int r, float T, uint64_t seed,
@@ -97,7 +97,7 @@ dspark_status dspark_draft_markov(int R, int gamma, int V, int r, float T, uint6
                                   int32_t* x, float* logp_d, float* lse_d, float* margin, void* ws,
                                   size_t ws_bytes, hipStream_t stream) {
   return draft_impl(R, gamma, V, r, T, seed, round, U, U_dt, W1, W2t, W_dt, x0, x, logp_d, lse_d,
-                    margin, ws, ws_bytes, stream, nullptr, nullptr);
+                    margin, ws, ws_bytes, stream, nullptr, nullptr, nullptr);
 }
 
 dspark_status dspark_draft_markov_profiled(int R, int gamma, int V, int r, float T, uint64_t seed,
@@ -106,10 +106,11 @@ dspark_status dspark_draft_markov_profiled(int R, int gamma, int V, int r, float
                                            const int32_t* x0, int32_t* x, float* logp_d,
                                            float* lse_d, float* margin, void* ws, size_t ws_bytes,
                                            hipStream_t stream, hipEvent_t* ev_begin,
-                                           hipEvent_t* ev_end) {
+                                           hipEvent_t* ev_end, int* n_timed) {
   if (!ev_begin || !ev_end) return DSPARK_E_INVALID;
+  if (n_timed) *n_timed = 0;
   return draft_impl(R, gamma, V, r, T, seed, round, U, U_dt, W1, W2t, W_dt, x0, x, logp_d, lse_d,
-                    margin, ws, ws_bytes, stream, ev_begin, ev_end);
+                    margin, ws, ws_bytes, stream, ev_begin, ev_end, n_timed);
 }
 
 dspark_status dspark_confidence(int R, int gamma, int d, int r, int V, const void* h,

@@ -2,18 +2,35 @@
 //
 // DSpark summary page, Method details (causal block distribution, Markov
 // head): p_k(v | x_0, x_<k) = softmax(U_k + W1[x_{k-1}] W2)(v), sampled left to
-// right.  Each step k is two launches on the caller's stream:
-//   1. per-chunk statistics of s = (U_k + bias)/T for every row (stats.hip);
-//   2. k_draft_pick, one wave per request: the row normaliser from the chunk
-//      log-masses, the chunk-level Gumbel pick, then the in-chunk pick after
+// right.  Every step k has two phases:
+//   A. per-chunk statistics of s = (U_k + bias)/T for every request (the bias
+//      contraction on MFMA);
+//   B. the pick, one workgroup per request: the row normaliser from the chunk
+//      statistics, the chunk-level Gumbel pick, then the in-chunk pick after
 //      rebuilding the 128 scores of the chosen chunk (bias by FMA chain).
-// The next step's statistics read x_k written by step 1's pick, so stream
-// order is the only synchronisation; nothing returns to the host.
+// Two schedules of the same phases:
+//   persistent : one cooperative launch for all gamma steps (k_draft_persistent).
+//                Each workgroup owns a 512-entry vocabulary slice and keeps its
+//                W2 slice in registers as MFMA operands for the whole round, so
+//                W2 is read from memory once per round instead of once per
+//                step; U_k is streamed once; the W1 rows of the requests sit in
+//                LDS.  Phases are separated by grid barriers.
+//   steps      : two launches per step (stats.hip, then k_draft_pick); stream
+//                order is the only synchronisation.  Used for shapes the
+//                persistent kernel does not take (float32 data, rank other than
+//                64/128/256, vocabularies beyond 512 entries per compute unit).
+// Nothing returns to the host in either schedule.
+#include <cstdlib>
+#include <cstring>
+
 #include "launch.hpp"
 #include "sampling.hpp"
 #include "workspace.hpp"
 
 namespace dspark {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct DraftPickArgs {
   int R, gamma, k, V, rank, nch;
@@ -32,11 +49,10 @@ struct DraftPickArgs {
   uint32_t* status;
 };
 
-// One 256-thread block per request.
-template <typename UT, typename WT, bool GREEDY>
-__global__ __launch_bounds__(256) void k_draft_pick(DraftPickArgs a) {
-  __shared__ BlockScratch sh;
-  const int i = blockIdx.x;
+// Pick of step a.k for request i by an NT-thread block (NT in {256, 512}).
+template <typename UT, typename WT, bool GREEDY, int NT>
+__device__ __forceinline__ void pick_row(const DraftPickArgs& a, int i, BlockScratch& sh) {
+  constexpr int TPE = NT / kChunk;          // threads per rebuilt entry
   const int tid = threadIdx.x;
   const int k = a.k;
   const int64_t xo = (int64_t)i * (a.gamma + 1);
@@ -48,45 +64,47 @@ __global__ __launch_bounds__(256) void k_draft_pick(DraftPickArgs a) {
     float v = -INFINITY;
     int idx = 0x7FFFFFFF;
     const int* Ir = a.I + (int64_t)i * a.nch;
-    for (int c = tid; c < a.nch; c += 256) argmax_merge(v, idx, Lr[c].x, Ir[c]);
-    block_argmax(v, idx, sh);
+    for (int c = tid; c < a.nch; c += NT) argmax_merge(v, idx, Lr[c].x, Ir[c]);
+    block_argmax<NT>(v, idx, sh);
     xk = idx;
     lse = v;
     logp = 0.f;
     if (xk < 0 || xk >= a.V) { set_flag(a.status, kFlagNonFinite); xk = 0; }
   } else {
     float m = -INFINITY;
-    for (int c = tid; c < a.nch; c += 256) m = fmaxf(m, Lr[c].x);
-    m = block_max(m, sh);
+    for (int c = tid; c < a.nch; c += NT) m = fmaxf(m, Lr[c].x);
+    m = block_max<NT>(m, sh);
     const bool want_gap = a.margin != nullptr;
     float srel;
-    const PickResult pc = block_pick_chunk(Lr, a.nch, m, a.invT, a.seed, a.round, kTagDraftChunk,
-                                           (uint32_t)i, (uint32_t)k, want_gap, &srel, sh);
+    const PickResult pc = block_pick_chunk<NT>(Lr, a.nch, m, a.invT, a.seed, a.round,
+                                               kTagDraftChunk, (uint32_t)i, (uint32_t)k, want_gap,
+                                               &srel, sh);
     const float lse_rel = logf(srel);
     lse = m * a.invT + lse_rel;
     int c = pc.idx;
     if (c < 0) { set_flag(a.status, kFlagNonFinite); c = 0; }
     const int base = c * kChunk;
-    // rebuild the 128 scores of the chosen chunk: thread t covers entry
-    // base + t/2 and one half of the rank
-    const int v = base + (tid >> 1), h = tid & 1;
+    // rebuild the 128 scores of the chosen chunk: TPE threads per entry, each
+    // a 1/TPE part of the rank
+    const int v = base + tid / TPE, h = tid % TPE;
     const bool in = v < a.V;
     float b = 0.f;
     if (a.rank > 0 && in) {
       const int pv = (prev >= 0 && prev < a.V) ? prev : 0;
       const WT* erow = reinterpret_cast<const WT*>(a.W1) + (int64_t)pv * a.rank;
-      b = markov_bias_half(erow, reinterpret_cast<const WT*>(a.W2t), a.rank, v, h);
+      b = markov_bias_half<(NT > 256 ? 2 : 8)>(erow, reinterpret_cast<const WT*>(a.W2t), a.rank, v, h, TPE);
     }
-    b += __shfl_xor(b, 1);
+#pragma unroll
+    for (int o = 1; o < TPE; o *= 2) b += __shfl_xor(b, o);
     const UT* urow = reinterpret_cast<const UT*>(a.U) + ((int64_t)i * a.gamma + (k - 1)) * a.V;
     const float s = in ? (Elem<UT>::get(urow, v) + b - m) * a.invT : -INFINITY;
-    const PickResult pe = block_pick_in_chunk(s, base, a.seed, a.round, kTagDraftElem,
-                                              (uint32_t)i, (uint32_t)k, want_gap, sh);
+    const PickResult pe = block_pick_in_chunk<NT>(s, base, a.seed, a.round, kTagDraftElem,
+                                                  (uint32_t)i, (uint32_t)k, want_gap, sh);
     xk = pe.idx;
     if (xk < 0) { set_flag(a.status, kFlagNonFinite); xk = base; }
-    // the winner's score: held by thread 2*(xk - base)
+    // the winner's score: held by thread TPE * (xk - base)
     __syncthreads();
-    if (tid == 2 * (xk - base)) sh.g[0] = s;
+    if (tid == TPE * (xk - base)) sh.g[0] = s;
     __syncthreads();
     logp = sh.g[0] - lse_rel;
     gap = fminf(pc.gap, pe.gap);
@@ -99,12 +117,530 @@ __global__ __launch_bounds__(256) void k_draft_pick(DraftPickArgs a) {
     a.lse_d[o] = lse;
     if (a.margin) a.margin[o] = gap;
   }
+  __syncthreads();                          // sh is reused by the next call
+}
+
+// One 256-thread block per request.
+template <typename UT, typename WT, bool GREEDY>
+__global__ __launch_bounds__(256) void k_draft_pick(DraftPickArgs a) {
+  __shared__ BlockScratch sh;
+  pick_row<UT, WT, GREEDY, 256>(a, blockIdx.x, sh);
+}
+
+// ============================================================= persistent
+// Workgroup b (512 threads, eight waves) owns vocabulary slice [512 b, 512 b +
+// 512): wave w holds entries 512 b + 64 w + [0, 64) of W2 as the A operands of
+// v_mfma_f32_16x16x32_bf16 (four 16-entry M tiles x rank/32 k-steps, loaded
+// once).  Entry order inside a wave: lane (n, g) of a 16x16 result holds, in
+// accumulator slot j of M tile mt, entry 16 g + 4 mt + j of the wave's slice,
+// so each lane owns 16 consecutive entries of one request row (its U segment
+// is one contiguous 32-byte read) and a row's 64 entries sit in lanes n, n+16,
+// n+32, n+48.  The requests are the N dimension: 16-row tiles whose B
+// operands (W1[x_{k-1}] rows) are read from LDS.
+constexpr int kPThreads = 512;
+constexpr int kPWaves = 8;
+constexpr int kPSlice = 512;                // vocabulary entries per workgroup
+constexpr int kPRows = 256;                 // requests per row group (LDS-resident W1 rows)
+constexpr int kPMaxChunks = 1024;           // chunk statistics staged per pick
+constexpr uint32_t kBarrierSpins = 1u << 24;
+
+struct PersistArgs {
+  DraftPickArgs p;                          // pick view (k set per step)
+  float scale2;                             // log2(e)/T; 1 when greedy
+  int nslice;                               // vocabulary slices = ceil(V / 512)
+  uint32_t* bar;                            // grid-barrier counter, zero at launch
+  uint32_t spin_limit;                      // bounded wait per barrier
+};
+
+// Values that cross workgroups inside the launch (chunk statistics, chunk
+// argmaxes, drafted tokens) are stored and loaded with device-scope relaxed
+// atomics.  Those accesses are coherent across the XCDs' L2 caches by
+// themselves, so a grid barrier only has to order them: no L2 write-back or
+// invalidation (XCD-wide operations) is needed.
+__device__ __forceinline__ int ld_coh(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_coh2(const float2* p) {
+  const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float2*>(p)),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+}
+__device__ __forceinline__ void st_coh2(float2* p, float2 v) {
+  const uint64_t u = (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Grid-wide barrier number `epoch` (1-based) over gridDim.x co-resident
+// workgroups, in two levels so that no counter takes more than a few dozen
+// same-address atomics per barrier (they serialise where device-scope atomics
+// are performed): workgroup b arrives on group counter b % kBarGroups; the
+// last arrival of a group arrives on the top counter, which every workgroup
+// polls.  The workgroup barrier first completes every wave's memory
+// operations (it waits for vmcnt 0); the counters use relaxed device-scope
+// atomics.  The wait is bounded: past spin_limit polls the workgroup sets
+// kFlagBarrier and stops waiting, and every later barrier of the launch
+// returns at once, so the kernel always runs to its end.
+constexpr int kBarGroups = 16;
+constexpr int kBarStride = 16;              // uint32 words between counters (64 bytes)
+
+__device__ __forceinline__ void grid_barrier(uint32_t* bar, uint32_t epoch, uint32_t spin_limit,
+                                             uint32_t* status) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t G = gridDim.x, b = blockIdx.x;
+    const uint32_t g = b % kBarGroups;
+    const uint32_t in_group = (G - g + kBarGroups - 1) / kBarGroups;
+    const uint32_t groups = G < (uint32_t)kBarGroups ? G : (uint32_t)kBarGroups;
+    uint32_t* top = bar + kBarGroups * kBarStride;
+    const uint32_t old = __hip_atomic_fetch_add(bar + g * kBarStride, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == epoch * in_group)
+      __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t target = epoch * groups;
+    const bool broken =
+        (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kFlagBarrier) != 0;
+    if (!broken) {
+      uint32_t spins = 0;
+      while (__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins >= spin_limit) {
+          atomicOr(status, kFlagBarrier);
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt fields at their
+// maxima).  Placed where no useful load is in flight, it clears the
+// compiler's record of possibly pending loads, which otherwise merges across
+// the step loop into a full wait at the first LDS store of every tile.
+__device__ __forceinline__ void wait_vm_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// One direct-to-LDS load per lane: 16 bytes from gptr to lds_wave_base + 16 *
+// lane (global_load_lds_dwordx4; M0 holds the wave's LDS base).  Issued from
+// inline assembly so that the compiler, which does not see it, does not fence
+// every later LDS access of the kernel behind outstanding vector-memory loads;
+// the caller waits for it explicitly (wait_vm_zero) before the data is used.
+// Nothing else in this kernel uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* gptr, const void* lds_wave_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(l), "v"(gptr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Pick of step a.k for request i by the 512-thread workgroup of the persistent
+// launch (same arithmetic as pick_row).  The row's chunk statistics and
+// W1[x_{k-1}] are first staged in LDS; each of the four threads of an entry
+// then issues all of its W2t loads at once.
+template <int KS, bool GREEDY>
+__device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, BlockScratch& sh,
+                                           float2* Ls, int* Is, uint4* Es) {
+  constexpr int NT = kPThreads, TPE = NT / kChunk;
+  constexpr int SEG = 2 * KS, NQ = SEG / TPE;   // 16-byte pieces of the rank per thread
+  const int tid = threadIdx.x;
+  const int k = a.k;
+  const int64_t xo = (int64_t)i * (a.gamma + 1);
+  int prev = (k == 1) ? a.x0[i] : ld_coh(a.x + xo + k - 1);
+  if (prev < 0 || prev >= a.V) prev = 0;        // flagged when phase A read it
+  const float2* Lr = a.L + (int64_t)i * a.nch;
+  static_assert(kPMaxChunks <= 2 * NT, "two staged chunks per thread");
+  {
+    // both loads of a thread in flight before the LDS stores
+    const int c0 = tid, c1 = tid + NT;
+    float2 l0 = make_float2(0.f, 0.f), l1 = l0;
+    int i0 = 0, i1 = 0;
+    if (c0 < a.nch) { l0 = ld_coh2(Lr + c0); if (GREEDY) i0 = ld_coh(a.I + (int64_t)i * a.nch + c0); }
+    if (c1 < a.nch) { l1 = ld_coh2(Lr + c1); if (GREEDY) i1 = ld_coh(a.I + (int64_t)i * a.nch + c1); }
+    if (c0 < a.nch) { Ls[c0] = l0; if (GREEDY) Is[c0] = i0; }
+    if (c1 < a.nch) { Ls[c1] = l1; if (GREEDY) Is[c1] = i1; }
+  }
+  if (!GREEDY && tid < SEG)
+    Es[tid] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.W1) +
+                                              (int64_t)prev * a.rank + 8 * tid);
+  __syncthreads();
+  int xk;
+  float logp, lse, gap = INFINITY;
+  if (GREEDY) {
+    float v = -INFINITY;
+    int idx = 0x7FFFFFFF;
+    for (int c = tid; c < a.nch; c += NT) argmax_merge(v, idx, Ls[c].x, Is[c]);
+    block_argmax<NT>(v, idx, sh);
+    xk = idx;
+    lse = v;
+    logp = 0.f;
+    if (xk < 0 || xk >= a.V) { set_flag(a.status, kFlagNonFinite); xk = 0; }
+  } else {
+    float m = -INFINITY;
+    for (int c = tid; c < a.nch; c += NT) m = fmaxf(m, Ls[c].x);
+    m = block_max<NT>(m, sh);
+    const bool want_gap = a.margin != nullptr;
+    float srel;
+    const PickResult pc = block_pick_chunk<NT>(Ls, a.nch, m, a.invT, a.seed, a.round,
+                                               kTagDraftChunk, (uint32_t)i, (uint32_t)k, want_gap,
+                                               &srel, sh);
+    const float lse_rel = logf(srel);
+    lse = m * a.invT + lse_rel;
+    int c = pc.idx;
+    if (c < 0) { set_flag(a.status, kFlagNonFinite); c = 0; }
+    const int base = c * kChunk;
+    const int v = base + tid / TPE, h = tid % TPE;
+    const bool in = v < a.V;
+    float b = 0.f, u = 0.f;
+    if (in) {
+      const uint4* wr = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.W2t) +
+                                                       (int64_t)v * a.rank) + h * NQ;
+      u = bf16_at(reinterpret_cast<const uint16_t*>(a.U), ((int64_t)i * a.gamma + (k - 1)) * a.V + v);
+      // W2t loads in two halves (register budget: the W2 slice stays resident)
+      constexpr int NQH = NQ > 1 ? NQ / 2 : 1;
+#pragma unroll
+      for (int q0 = 0; q0 < NQ; q0 += NQH) {
+      uint4 wq[NQH];
+#pragma unroll
+      for (int q = 0; q < NQH; ++q) wq[q] = wr[q0 + q];
+#pragma unroll
+      for (int q = 0; q < NQH; ++q) {
+        const uint4 x = Es[h * NQ + q0 + q];
+        const uint4 w = wq[q];
+        b = fmaf(bf16_lo(x.x), bf16_lo(w.x), b);
+        b = fmaf(bf16_hi(x.x), bf16_hi(w.x), b);
+        b = fmaf(bf16_lo(x.y), bf16_lo(w.y), b);
+        b = fmaf(bf16_hi(x.y), bf16_hi(w.y), b);
+        b = fmaf(bf16_lo(x.z), bf16_lo(w.z), b);
+        b = fmaf(bf16_hi(x.z), bf16_hi(w.z), b);
+        b = fmaf(bf16_lo(x.w), bf16_lo(w.w), b);
+        b = fmaf(bf16_hi(x.w), bf16_hi(w.w), b);
+      }
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < TPE; o *= 2) b += __shfl_xor(b, o);
+    const float s = in ? (u + b - m) * a.invT : -INFINITY;
+    const PickResult pe = block_pick_in_chunk<NT>(s, base, a.seed, a.round, kTagDraftElem,
+                                                  (uint32_t)i, (uint32_t)k, want_gap, sh);
+    xk = pe.idx;
+    if (xk < 0) { set_flag(a.status, kFlagNonFinite); xk = base; }
+    __syncthreads();
+    if (tid == TPE * (xk - base)) sh.g[0] = s;
+    __syncthreads();
+    logp = sh.g[0] - lse_rel;
+    gap = fminf(pc.gap, pe.gap);
+  }
+  if (tid == 0) {
+    if (k == 1) st_coh(a.x + xo, a.x0[i]);
+    st_coh(a.x + xo + k, xk);
+    const int64_t o = (int64_t)i * a.gamma + (k - 1);
+    a.logp_d[o] = logp;
+    a.lse_d[o] = lse;
+    if (a.margin) a.margin[o] = gap;
+  }
+  wait_vm_zero();
+  __syncthreads();                          // LDS staging and sh are reused
+}
+
+template <int KS, bool GREEDY>
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_draft_persistent(PersistArgs P) {
+  constexpr int SEG = 2 * KS;               // 16-byte segments per W1 row (rank / 8)
+  static_assert(KS % 2 == 0, "rank must be a multiple of 32");
+  constexpr int ROWP = SEG + 1;             // padded LDS row: rows start 16 bytes apart in the
+                                            // bank space, so the 16 lanes of a ds_read_b128
+                                            // phase (16 rows, same segment) never collide
+  // LDS: the group's W1 rows; a union of the phase-A half-chunk statistics
+  // and the pick's staging; the group's tokens
+  constexpr int HS_BYTES = kPRows * kPWaves * 8, HI_BYTES = GREEDY ? kPRows * kPWaves * 4 : 0;
+  constexpr int PK_BYTES = kPMaxChunks * 8 + (GREEDY ? kPMaxChunks * 4 : 0) + SEG * 16;
+  constexpr int UA_BYTES = (HS_BYTES + HI_BYTES) > PK_BYTES ? (HS_BYTES + HI_BYTES) : PK_BYTES;
+  __shared__ uint4 E[kPRows * ROWP];
+  __shared__ uint4 UA[UA_BYTES / 16];
+  __shared__ int PV[kPRows];
+  __shared__ BlockScratch sh;
+  float2* HS = reinterpret_cast<float2*>(UA);                       // [row][wave]
+  int* HI = reinterpret_cast<int*>(reinterpret_cast<char*>(UA) + HS_BYTES);
+  float2* Ls = reinterpret_cast<float2*>(UA);                       // pick: chunk statistics
+  int* Is = reinterpret_cast<int*>(reinterpret_cast<char*>(UA) + kPMaxChunks * 8);
+  uint4* Es = reinterpret_cast<uint4*>(reinterpret_cast<char*>(UA) + kPMaxChunks * 8 +
+                                       (GREEDY ? kPMaxChunks * 4 : 0));
+
+  DraftPickArgs a = P.p;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = blockIdx.x;
+  const int V = a.V, R = a.R;
+  const int wslice = b * kPSlice + 64 * wv;
+  const bool slice_active = b < P.nslice;
+  const bool wave_active = slice_active && wslice < V;
+  const float s2 = P.scale2;
+  const uint16_t* U = reinterpret_cast<const uint16_t*>(a.U);
+  const uint16_t* W1 = reinterpret_cast<const uint16_t*>(a.W1);
+  const uint16_t* W2t = reinterpret_cast<const uint16_t*>(a.W2t);
+
+  // ---- W2 slice of this wave, resident for the whole launch
+  constexpr int KT = KS / 2;                // k-steps of 32
+  bf16x8_t Af[4][KT];
+  {
+    const int m = lane & 15, kg = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      int voc = wslice + 16 * (m >> 2) + 4 * mt + (m & 3);
+      voc = wave_active ? min(voc, V - 1) : 0;
+      const uint16_t* wr = W2t + (int64_t)voc * a.rank + 8 * kg;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) Af[mt][kt] = *reinterpret_cast<const bf16x8_t*>(wr + 32 * kt);
+    }
+  }
+  // this lane's 16 entries: two 16-byte pieces of U
+  const int ln = lane & 15, lg = lane >> 4;
+  const int ubase = wslice + 16 * lg;
+  bool uok[2];
+  int uoff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    uok[q] = wave_active && ubase + 8 * q + 8 <= V;
+    uoff[q] = uok[q] ? ubase + 8 * q : 0;
+  }
+
+  uint32_t epoch = 0;
+  const int ngroups = (R + kPRows - 1) / kPRows;
+  for (int k = 1; k <= a.gamma; ++k) {
+    a.k = k;
+    // ================= phase A: chunk statistics of step k for every request
+    for (int g = 0; g < ngroups; ++g) {
+      const int row0 = g * kPRows;
+      const int rows = min(kPRows, R - row0);
+      if (slice_active) {
+        // tokens x_{k-1} of the group, then the W1 rows: 16-byte piece p of E
+        // is segment p % ROWP of row p / ROWP (the pad piece stays unwritten).
+        // Ordinary loads, all issued before the LDS stores: direct-to-LDS
+        // loads would make the compiler fence every later LDS store of the
+        // kernel behind all outstanding vector-memory loads.
+        for (int rl = tid; rl < rows; rl += kPThreads) {
+          const int row = row0 + rl;
+          int prev = (k == 1) ? a.x0[row] : ld_coh(a.x + (int64_t)row * (a.gamma + 1) + (k - 1));
+          if (prev < 0 || prev >= V) { set_flag(a.status, kFlagBadToken); prev = 0; }
+          PV[rl] = prev;
+        }
+        __syncthreads();
+        // direct-to-LDS loads, one 1 KB run of 64 pieces per instruction;
+        // pieces past the group's rows re-read its last row and pad pieces
+        // re-read segment 0 (their slots are never read)
+        const int npieces = rows * ROWP;
+        for (int p0 = wv * 64; p0 < npieces; p0 += kPThreads) {
+          const int p = p0 + lane;
+          const int rl = min(p / ROWP, rows - 1), sp = p % ROWP;
+          lds_dma16(W1 + (int64_t)PV[rl] * a.rank + 8 * (sp < SEG ? sp : 0), E + p0);
+        }
+        wait_vm_zero();
+      }
+      wait_vm_zero();
+      __syncthreads();
+      if (wave_active) {
+        const int ntiles = (rows + 15) / 16;
+        const uint16_t* ustep = U + (int64_t)(k - 1) * V;
+        const int64_t rstride = (int64_t)a.gamma * V;
+        auto load_u = [&](uint4 (&dst)[2], int i) __attribute__((always_inline)) {
+          const int row = row0 + min(16 * i + ln, rows - 1);
+          const uint16_t* up = ustep + (int64_t)row * rstride;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) dst[q] = *reinterpret_cast<const uint4*>(up + uoff[q]);
+        };
+        // one 16-row tile: its U (in `un`) seeds the accumulators, then the
+        // slot is refilled with the tile two ahead
+        auto tile = [&](uint4 (&un)[2], int i) __attribute__((always_inline)) {
+          f32x4_t acc[4];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t wd[4] = {un[q].x, un[q].y, un[q].z, un[q].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int j = 8 * q + e;        // entry 16 lg + j = 16 lg + 4 mt + jj
+              acc[j >> 2][j & 3] = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
+            }
+          }
+          if (i + 2 < ntiles) load_u(un, i + 2);
+          const int rl = 16 * i + ln;
+          const uint4* erow = E + rl * ROWP + lg;   // segment 4 kt + lg at erow[4 kt]
+          // B operands through a three-deep register ring: the LDS read of
+          // k-step kt+2 is issued before the MFMAs of kt
+          bf16x8_t Bq[3];
+          Bq[0] = __builtin_bit_cast(bf16x8_t, erow[0]);
+          if (KT > 1) Bq[1] = __builtin_bit_cast(bf16x8_t, erow[4]);
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            if (kt + 2 < KT) Bq[(kt + 2) % 3] = __builtin_bit_cast(bf16x8_t, erow[4 * (kt + 2)]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[mt][kt], Bq[kt % 3], acc[mt], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // x = U + bias for the lane's 16 consecutive entries (invalid -> -inf)
+          float x[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) x[j] = uok[j >> 3] ? acc[j >> 2][j & 3] : -INFINITY;
+          const bool row_ok = rl < rows;
+          if (GREEDY) {
+            float bv = -INFINITY;
+            int bi = 0x7FFFFFFF;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const bool gt = x[j] > bv;
+              bv = gt ? x[j] : bv;
+              bi = gt ? ubase + j : bi;
+            }
+            argmax_merge(bv, bi, __shfl_xor(bv, 16), __shfl_xor(bi, 16));
+            argmax_merge(bv, bi, __shfl_xor(bv, 32), __shfl_xor(bi, 32));
+            if (lg == 0 && row_ok) { HS[rl * kPWaves + wv] = make_float2(bv, 0.f); HI[rl * kPWaves + wv] = bi; }
+          } else {
+            float M = x[0];
+#pragma unroll
+            for (int j = 1; j < 16; ++j) M = fmaxf(M, x[j]);
+            float S = 0.f;
+            if (M != -INFINITY) {
+              const float Ms2 = M * s2;
+#pragma unroll
+              for (int j = 0; j < 16; ++j) S += __builtin_amdgcn_exp2f(fmaf(x[j], s2, -Ms2));
+              // the sum is relative to Ms2 = round(M * s2): refer it to M exactly
+              S *= __builtin_amdgcn_exp2f(-fmaf(M, s2, -Ms2));
+            }
+            // combine the four lanes of the row (xor 16, then xor 32)
+#pragma unroll
+            for (int o = 16; o <= 32; o *= 2) {
+              const float Mo = __shfl_xor(M, o), So = __shfl_xor(S, o);
+              const float Mn = fmaxf(M, Mo);
+              float St = 0.f;
+              if (Mn != -INFINITY) {
+                if (__float_as_uint(S) != 0u) St += S * __builtin_amdgcn_exp2f((M - Mn) * s2);
+                if (__float_as_uint(So) != 0u) St += So * __builtin_amdgcn_exp2f((Mo - Mn) * s2);
+              }
+              M = Mn;
+              S = St;
+            }
+            if (lg == 0 && row_ok) HS[rl * kPWaves + wv] = make_float2(M, S);
+          }
+        };
+        uint4 ua[2], ub[2];
+        load_u(ua, 0);
+        if (ntiles > 1) load_u(ub, 1);
+        wait_vm_zero();
+        for (int i = 0; i < ntiles; i += 2) {
+          tile(ua, i);
+          if (i + 1 < ntiles) tile(ub, i + 1);
+        }
+      } else {
+        // no entries in this wave's slice: empty halves
+        for (int rl = lane; rl < rows; rl += 64) {
+          HS[rl * kPWaves + wv] = make_float2(-INFINITY, 0.f);
+          if (GREEDY) HI[rl * kPWaves + wv] = 0x7FFFFFFF;
+        }
+      }
+      __syncthreads();
+      // merge the two halves of each of the slice's four chunks and store
+      if (slice_active) {
+        for (int t = tid; t < rows * 4; t += kPThreads) {
+          const int rl = t >> 2, c = t & 3;
+          const int chunk = 4 * b + c;
+          if (chunk >= a.nch) continue;
+          const int row = row0 + rl;
+          const float2 s0 = HS[rl * kPWaves + 2 * c], s1 = HS[rl * kPWaves + 2 * c + 1];
+          float2* Lo = const_cast<float2*>(a.L) + (int64_t)row * a.nch + chunk;
+          if (GREEDY) {
+            float bv = s0.x;
+            int bi = HI[rl * kPWaves + 2 * c];
+            argmax_merge(bv, bi, s1.x, HI[rl * kPWaves + 2 * c + 1]);
+            st_coh2(Lo, make_float2(bv, 0.f));
+            st_coh(const_cast<int*>(a.I) + (int64_t)row * a.nch + chunk, bi);
+            if (nonfinite(bv)) set_flag(a.status, kFlagNonFinite);
+          } else {
+            const float Mn = fmaxf(s0.x, s1.x);
+            float St = 0.f;
+            if (Mn != -INFINITY) {
+              if (__float_as_uint(s0.y) != 0u) St += s0.y * __builtin_amdgcn_exp2f((s0.x - Mn) * s2);
+              if (__float_as_uint(s1.y) != 0u) St += s1.y * __builtin_amdgcn_exp2f((s1.x - Mn) * s2);
+            }
+            st_coh2(Lo, make_float2(Mn, St));
+            if (nonfinite(St) || Mn == INFINITY) set_flag(a.status, kFlagNonFinite);
+          }
+        }
+      }
+      __syncthreads();                      // E, PV and HS are rewritten by the next group
+    }
+    grid_barrier(P.bar, ++epoch, P.spin_limit, a.status);
+    // ================= phase B: the pick of step k, one request per workgroup
+    for (int i = b; i < R; i += gridDim.x) pick_row_p<KS, GREEDY>(a, i, sh, Ls, Is, Es);
+    if (k < a.gamma) grid_barrier(P.bar, ++epoch, P.spin_limit, a.status);
+  }
+}
+
+// Per-device facts for the persistent schedule (compute units; whether one
+// workgroup of each instance fits per compute unit).
+struct PersistInfo {
+  int cus = -1;
+  int fits[3][2] = {{-1, -1}, {-1, -1}, {-1, -1}};
+};
+static PersistInfo g_pinfo[64];
+
+template <int KS, bool G>
+static bool persist_fits(PersistInfo& pi, int ki) {
+  if (pi.fits[ki][G] < 0) {
+    int nb = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &nb, reinterpret_cast<const void*>(k_draft_persistent<KS, G>), kPThreads, 0);
+    pi.fits[ki][G] = (e == hipSuccess && nb >= 1) ? 1 : 0;
+    (void)hipGetLastError();
+  }
+  return pi.fits[ki][G] == 1;
+}
+
+template <int KS, bool G>
+static hipError_t launch_persist_ks(PersistArgs& P, int grid, hipStream_t st) {
+  void* args[] = {&P};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_draft_persistent<KS, G>),
+                                    dim3(grid), dim3(kPThreads), args, 0, st);
+}
+
+// The persistent schedule takes bf16 U and weights, rank 64/128/256, rows and
+// weight tables 16-byte aligned, V a multiple of 8 with at most 512 entries per
+// compute unit.  DSPARK_DRAFT_KERNEL=steps in the environment selects the
+// per-step schedule for every shape.
+static int persistent_grid(int V, int rank, bool u_bf16, bool w_bf16, bool u_vec, const void* W1,
+                           const void* W2t, bool greedy) {
+  const char* env = std::getenv("DSPARK_DRAFT_KERNEL");
+  if (env && std::strcmp(env, "steps") == 0) return 0;
+  if (!u_bf16 || !w_bf16 || !u_vec || (V % 8) != 0) return 0;
+  if (rank != 64 && rank != 128 && rank != 256) return 0;
+  if ((reinterpret_cast<uintptr_t>(W1) & 15) || (reinterpret_cast<uintptr_t>(W2t) & 15)) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  PersistInfo& pi = g_pinfo[dev];
+  if (pi.cus < 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    pi.cus = cus;
+  }
+  const int nslice = (V + kPSlice - 1) / kPSlice;
+  if (pi.cus < 1 || nslice > pi.cus || (V + kChunk - 1) / kChunk > kPMaxChunks) return 0;
+  bool fits;
+  if (rank == 64) fits = greedy ? persist_fits<4, true>(pi, 0) : persist_fits<4, false>(pi, 0);
+  else if (rank == 128) fits = greedy ? persist_fits<8, true>(pi, 1) : persist_fits<8, false>(pi, 1);
+  else fits = greedy ? persist_fits<16, true>(pi, 2) : persist_fits<16, false>(pi, 2);
+  return fits ? pi.cus : 0;
+}
+
+__global__ void k_zero_words(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
 }
 
 hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,
                         const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
                         const int32_t* x0, int32_t* x, float* logp_d, float* lse_d, float* margin,
-                        void* ws, hipStream_t st, hipEvent_t* ev_begin, hipEvent_t* ev_end) {
+                        void* ws, hipStream_t st, hipEvent_t* ev_begin, hipEvent_t* ev_end,
+                        int* n_timed) {
   const WsLayout L = ws_layout(R, gamma, V);
   char* w = reinterpret_cast<char*>(ws);
   uint32_t* status = reinterpret_cast<uint32_t*>(w + L.header);
@@ -115,6 +651,36 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
   const float scale2 = greedy ? 1.f : kLog2e / T;
   const size_t usz = u_bf16 ? 2 : 4;
   const bool u_vec = ((reinterpret_cast<uintptr_t>(U) & 15) == 0) && (((size_t)V * usz) % 16 == 0);
+
+  DraftPickArgs p{};
+  p.R = R; p.gamma = gamma; p.k = 1; p.V = V; p.rank = rank; p.nch = nch;
+  p.invT = greedy ? 1.f : 1.f / T; p.seed = seed; p.round = round;
+  p.U = U; p.W1 = W1; p.W2t = W2t; p.x0 = x0; p.x = x; p.logp_d = logp_d; p.lse_d = lse_d;
+  p.margin = margin; p.L = Lc; p.I = Ic; p.status = status;
+
+  const int grid = persistent_grid(V, rank, u_bf16, w_bf16, u_vec, W1, W2t, greedy);
+  if (grid > 0) {
+    PersistArgs P{};
+    P.p = p;
+    P.scale2 = scale2;
+    P.nslice = (V + kPSlice - 1) / kPSlice;
+    P.bar = reinterpret_cast<uint32_t*>(w + L.bar);
+    const char* sl = std::getenv("DSPARK_BARRIER_SPINS");
+    P.spin_limit = sl ? (uint32_t)std::strtoul(sl, nullptr, 10) : kBarrierSpins;
+    if (P.spin_limit == 0) P.spin_limit = 1;
+    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, st, P.bar, (kBarGroups + 1) * kBarStride);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ev_begin && (e = hipEventRecord(ev_begin[0], st)) != hipSuccess) return e;
+    if (rank == 64) e = greedy ? launch_persist_ks<4, true>(P, grid, st) : launch_persist_ks<4, false>(P, grid, st);
+    else if (rank == 128) e = greedy ? launch_persist_ks<8, true>(P, grid, st) : launch_persist_ks<8, false>(P, grid, st);
+    else e = greedy ? launch_persist_ks<16, true>(P, grid, st) : launch_persist_ks<16, false>(P, grid, st);
+    if (e != hipSuccess) return e;
+    if (ev_end && (e = hipEventRecord(ev_end[0], st)) != hipSuccess) return e;
+    if (n_timed) *n_timed = 1;
+    return hipSuccess;
+  }
+
   for (int k = 1; k <= gamma; ++k) {
     hipError_t e;
     if (ev_begin && (e = hipEventRecord(ev_begin[k - 1], st)) != hipSuccess) return e;
@@ -133,11 +699,7 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     }
     if (e != hipSuccess) return e;
     if (ev_end && (e = hipEventRecord(ev_end[k - 1], st)) != hipSuccess) return e;
-    DraftPickArgs p{};
-    p.R = R; p.gamma = gamma; p.k = k; p.V = V; p.rank = rank; p.nch = nch;
-    p.invT = greedy ? 1.f : 1.f / T; p.seed = seed; p.round = round;
-    p.U = U; p.W1 = W1; p.W2t = W2t; p.x0 = x0; p.x = x; p.logp_d = logp_d; p.lse_d = lse_d;
-    p.margin = margin; p.L = Lc; p.I = Ic; p.status = status;
+    p.k = k;
 #define DSPARK_PICK(UT_, WT_, G_) \
     hipLaunchKernelGGL((k_draft_pick<UT_, WT_, G_>), dim3(R), dim3(256), 0, st, p)
     if (u_bf16 && w_bf16) { if (greedy) DSPARK_PICK(uint16_t, uint16_t, true); else DSPARK_PICK(uint16_t, uint16_t, false); }
@@ -148,6 +710,7 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (n_timed) *n_timed = gamma;
   return hipSuccess;
 }
 

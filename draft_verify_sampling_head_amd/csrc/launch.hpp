@@ -97,7 +97,7 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
                         const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
                         const int32_t* x0, int32_t* x, float* logp_d, float* lse_d, float* margin,
                         void* ws, hipStream_t st, hipEvent_t* ev_begin = nullptr,
-                        hipEvent_t* ev_end = nullptr);
+                        hipEvent_t* ev_end = nullptr, int* n_timed = nullptr);
 hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,
                          const int32_t* ell, const int32_t* cu, const void* target, int layout,
                          const int32_t* x, const float* logp_d, const float* lse_d,

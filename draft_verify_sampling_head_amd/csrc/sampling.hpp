@@ -165,32 +165,49 @@ __device__ inline float markov_bias(const float* e, const float* W2t, int rank, 
   return b;
 }
 
-// ------------------------------------------------ block-level (256 threads)
-// Reductions across the four waves of a 256-thread block through LDS; every
-// thread of the block must call them (they contain barriers).
+// ------------------------------------------------------------ block-level
+// Reductions across the NT/64 waves of an NT-thread block (NT <= 512) through
+// LDS; every thread of the block must call them (they contain barriers).
 struct BlockScratch {
-  float f[4];
-  int i[4];
-  float g[4];
+  float f[8];
+  int i[8];
+  float g[8];
 };
 
+template <int NT = 256>
 __device__ inline float block_max(float v, BlockScratch& sh) {
+  constexpr int NWV = NT / 64;
   const int wv = threadIdx.x >> 6;
   v = wave_max(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sh.f[wv] = v;
   __syncthreads();
-  return fmaxf(fmaxf(sh.f[0], sh.f[1]), fmaxf(sh.f[2], sh.f[3]));
+  float r = sh.f[0];
+#pragma unroll
+  for (int q = 1; q < NWV; ++q) r = fmaxf(r, sh.f[q]);
+  return r;
 }
+template <int NT = 256>
 __device__ inline float block_sum(float v, BlockScratch& sh) {
+  constexpr int NWV = NT / 64;
   const int wv = threadIdx.x >> 6;
   v = wave_sum(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sh.f[wv] = v;
   __syncthreads();
-  return (sh.f[0] + sh.f[1]) + (sh.f[2] + sh.f[3]);
+  // pairwise, in wave order
+  float r[NWV];
+#pragma unroll
+  for (int q = 0; q < NWV; ++q) r[q] = sh.f[q];
+#pragma unroll
+  for (int w = 1; w < NWV; w *= 2)
+#pragma unroll
+    for (int q = 0; q + w < NWV; q += 2 * w) r[q] += r[q + w];
+  return r[0];
 }
+template <int NT = 256>
 __device__ inline void block_argmax(float& v, int& idx, BlockScratch& sh) {
+  constexpr int NWV = NT / 64;
   const int wv = threadIdx.x >> 6;
   wave_argmax(v, idx);
   __syncthreads();
@@ -198,12 +215,14 @@ __device__ inline void block_argmax(float& v, int& idx, BlockScratch& sh) {
   __syncthreads();
   v = sh.f[0];
   idx = sh.i[0];
-  for (int q = 1; q < 4; ++q) argmax_merge(v, idx, sh.f[q], sh.i[q]);
+#pragma unroll
+  for (int q = 1; q < NWV; ++q) argmax_merge(v, idx, sh.f[q], sh.i[q]);
 }
 
-// Chunk-level Gumbel pick by a 256-thread block: thread t scans chunk blocks
-// t, t+256, ... (four chunks per Philox block).  Returns the chunk and,
+// Chunk-level Gumbel pick by an NT-thread block: thread t scans chunk blocks
+// t, t+NT, ... (four chunks per Philox block).  Returns the chunk and,
 // through *sum_rel, sum_c S_c exp((M_c - m)/T) (the row normaliser above m).
+template <int NT = 256>
 __device__ inline PickResult block_pick_chunk(const float2* st, int nch, float m, float invT,
                                               uint64_t seed, uint64_t round, uint32_t tag,
                                               uint32_t req, uint32_t k, bool want_gap,
@@ -211,7 +230,7 @@ __device__ inline PickResult block_pick_chunk(const float2* st, int nch, float m
   float best = -INFINITY, ssum = 0.f;
   int bi = 0x7FFFFFFF;
   const bool draw = nch > 1;
-  for (int b = threadIdx.x; b * 4 < nch; b += 256) {
+  for (int b = threadIdx.x; b * 4 < nch; b += NT) {
     uint4 blk = make_uint4(0, 0, 0, 0);
     if (draw) blk = stream_block(seed, round, tag, req, k, (uint32_t)b);
 #pragma unroll
@@ -228,12 +247,12 @@ __device__ inline PickResult block_pick_chunk(const float2* st, int nch, float m
       }
     }
   }
-  *sum_rel = block_sum(ssum, sh);
-  block_argmax(best, bi, sh);
+  *sum_rel = block_sum<NT>(ssum, sh);
+  block_argmax<NT>(best, bi, sh);
   PickResult r{best == -INFINITY ? -1 : bi, best, INFINITY};
   if (want_gap && r.idx >= 0 && draw) {
     float second = -INFINITY;
-    for (int b = threadIdx.x; b * 4 < nch; b += 256) {
+    for (int b = threadIdx.x; b * 4 < nch; b += NT) {
       const uint4 blk = stream_block(seed, round, tag, req, k, (uint32_t)b);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -245,45 +264,49 @@ __device__ inline PickResult block_pick_chunk(const float2* st, int nch, float m
         }
       }
     }
-    r.gap = best - block_max(second, sh);
+    r.gap = best - block_max<NT>(second, sh);
   }
   return r;
 }
 
-// In-chunk Gumbel pick by a 256-thread block: threads with (t & 1) == 0 hold
-// the score of entry base + t/2 (-inf = excluded).
+// In-chunk Gumbel pick by an NT-thread block: NT/128 consecutive threads share
+// one entry; the first of them holds the score of entry base + t/(NT/128)
+// (-inf = excluded).
+template <int NT = 256>
 __device__ inline PickResult block_pick_in_chunk(float s, int base, uint64_t seed, uint64_t round,
                                                  uint32_t tag, uint32_t req, uint32_t k,
                                                  bool want_gap, BlockScratch& sh) {
+  constexpr int TPE = NT / kChunk;
   const int t = threadIdx.x;
-  const int v = base + (t >> 1);
+  const int v = base + t / TPE;
   float key = -INFINITY;
   int bi = 0x7FFFFFFF;
-  if ((t & 1) == 0 && s != -INFINITY) {
+  if ((t % TPE) == 0 && s != -INFINITY) {
     const uint4 blk = stream_block(seed, round, tag, req, k, (uint32_t)v >> 2);
     key = s + gumbel_of(word_of(blk, (uint32_t)v & 3u));
     bi = v;
   }
   float best = key;
   int bidx = bi;
-  block_argmax(best, bidx, sh);
+  block_argmax<NT>(best, bidx, sh);
   PickResult r{best == -INFINITY ? -1 : bidx, best, INFINITY};
   if (want_gap && r.idx >= 0) {
-    const float second = block_max((bi == r.idx) ? -INFINITY : key, sh);
+    const float second = block_max<NT>((bi == r.idx) ? -INFINITY : key, sh);
     r.gap = best - second;
   }
   return r;
 }
 
-// Half of the Markov bias dot product W1[prev] . W2t[v]: entries
-// [h*rank/2, (h+1)*rank/2), float32 FMA chain in ascending order.
+// Part h of nparts of the Markov bias dot product W1[prev] . W2t[v]: entries
+// [h*rank/nparts, (h+1)*rank/nparts), float32 FMA chain in ascending order.
+template <int UNR = 8>
 __device__ inline float markov_bias_half(const uint16_t* e, const uint16_t* W2t, int rank, int v,
-                                         int h) {
-  const int nq = rank / 16;                      // 8-value groups per half
+                                         int h, int nparts = 2) {
+  const int nq = rank / (8 * nparts);            // 8-value groups per part
   const uint4* w = reinterpret_cast<const uint4*>(W2t + (int64_t)v * rank) + h * nq;
   const uint4* ev = reinterpret_cast<const uint4*>(e) + h * nq;
   float b = 0.f;
-#pragma unroll 8
+#pragma unroll UNR
   for (int q = 0; q < nq; ++q) {
     const uint4 u = w[q];
     const uint4 x = ev[q];
@@ -298,12 +321,14 @@ __device__ inline float markov_bias_half(const uint16_t* e, const uint16_t* W2t,
   }
   return b;
 }
-__device__ inline float markov_bias_half(const float* e, const float* W2t, int rank, int v, int h) {
-  const int nq = rank / 8;                       // 4-value groups per half
+template <int UNR = 8>
+__device__ inline float markov_bias_half(const float* e, const float* W2t, int rank, int v, int h,
+                                         int nparts = 2) {
+  const int nq = rank / (4 * nparts);            // 4-value groups per part
   const float4* w = reinterpret_cast<const float4*>(W2t + (int64_t)v * rank) + h * nq;
   const float4* ev = reinterpret_cast<const float4*>(e) + h * nq;
   float b = 0.f;
-#pragma unroll 8
+#pragma unroll UNR
   for (int q = 0; q < nq; ++q) {
     const float4 u = w[q];
     const float4 x = ev[q];

@@ -17,8 +17,9 @@
  *  - A call that returns an error other than DSPARK_E_HIP has enqueued nothing.
  *    DSPARK_E_HIP means a kernel launch failed; the stream state is then the
  *    HIP runtime's.
- *  - The library keeps no global state between calls.  Calls that share a
- *    workspace must be ordered on one stream (or otherwise serialised).
+ *  - The library keeps no state between calls other than a per-device cache
+ *    of immutable device facts (compute-unit count, occupancy).  Calls that
+ *    share a workspace must be ordered on one stream (or otherwise serialised).
  *  - R = requests in the batch, gamma = block size (draft positions per
  *    request), V = vocabulary, r = Markov rank, d = backbone hidden size,
  *    T = sampling temperature (T == 0 selects greedy decoding).
@@ -59,6 +60,8 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 #define DSPARK_FLAG_NONFINITE 1u   /* a non-finite logit or score was seen        */
 #define DSPARK_FLAG_BAD_LEN   2u   /* a pack length outside [0, width] was clamped */
 #define DSPARK_FLAG_BAD_TOKEN 4u   /* a token id outside [0, V) was read           */
+#define DSPARK_FLAG_BARRIER   8u   /* a grid barrier of the persistent draft gave
+                                      up waiting (its outputs are then invalid)   */
 
 /* (host) Bytes of workspace every entry point below needs for these sizes. */
 size_t dspark_workspace_bytes(int R, int gamma, int V, int r, int d);
@@ -96,7 +99,14 @@ dspark_status dspark_get_status(const void* ws, size_t ws_bytes, uint32_t* flags
  *   margin out nullable [R][gamma]  gap between the two best Gumbel keys
  *                          (debug; smaller of the chunk and in-chunk gaps)
  * W_dt == DSPARK_BF16 runs the bias contraction on MFMA (fp32 accumulation);
- * DSPARK_F32 weights run it on the vector ALU.
+ * DSPARK_F32 weights run it on the vector ALU.  With bf16 U and weights,
+ * r in {64, 128, 256}, 16-byte aligned tables, V a multiple of 8 and at most
+ * 512 vocabulary entries per compute unit, all gamma steps run as one
+ * cooperative launch that keeps W2 on chip (grid barriers between steps;
+ * DSPARK_FLAG_BARRIER reports a barrier that gave up waiting); other shapes
+ * run two launches per step.  Both schedules give the same results.  The
+ * environment variable DSPARK_DRAFT_KERNEL=steps forces the per-step
+ * schedule.
  */
 dspark_status dspark_draft_markov(int R, int gamma, int V, int r, float T,
                                   uint64_t seed, uint64_t round,
@@ -107,10 +117,13 @@ dspark_status dspark_draft_markov(int R, int gamma, int V, int r, float T,
 
 /*
  * Instrumented dspark_draft_markov for performance measurement: identical
- * results; additionally records ev_begin[k-1] / ev_end[k-1] on `stream`
- * immediately before / after the per-chunk statistics kernel of step k
- * (the bias contraction and vocabulary stream, the draft's dominant kernel).
+ * results; additionally records events on `stream` around the draft's
+ * dominant kernel.  With the persistent schedule (one cooperative launch for
+ * all gamma steps) that is ev_begin[0] / ev_end[0] around the launch and
+ * *n_timed = 1; with the per-step schedule ev_begin[k-1] / ev_end[k-1] bracket
+ * the per-chunk statistics kernel of step k and *n_timed = gamma.
  *   ev_begin, ev_end  (host) arrays of gamma events created by the caller
+ *   n_timed           (host, nullable) number of event pairs recorded
  * Returns DSPARK_E_INVALID if either array is null.
  */
 dspark_status dspark_draft_markov_profiled(int R, int gamma, int V, int r, float T,
@@ -120,7 +133,7 @@ dspark_status dspark_draft_markov_profiled(int R, int gamma, int V, int r, float
                                            const int32_t* x0, int32_t* x, float* logp_d,
                                            float* lse_d, float* margin, void* ws, size_t ws_bytes,
                                            hipStream_t stream, hipEvent_t* ev_begin,
-                                           hipEvent_t* ev_end);
+                                           hipEvent_t* ev_end, int* n_timed);
 
 /*
  * Confidence head ([P3] Method details, confidence head and STS calibration):

@@ -110,6 +110,8 @@ SMALL = [
     (2, dict(R=12, gamma=32, V=900, d=32, rank=32)),                     # longest block
     (2, dict(R=24, gamma=4, V=1800, d=64, T=0.3)),
     (2, dict(R=24, gamma=4, V=1800, d=64, T=2.0, scheduler=False)),
+    (2, dict(R=300, gamma=3, V=2048, d=32, rank=128)),                   # two 256-row groups
+    (1, dict(R=260, gamma=3, V=4096, d=32, rank=64)),                    # greedy, two row groups
 ]
 
 
@@ -167,6 +169,60 @@ def test_nonfinite_logits_are_flagged():
     RD.run_round(inp, buf, cfg.T, 0, 0)
     torch.cuda.synchronize()
     assert D.get_status(buf.ws) & D._lib.FLAG_NONFINITE
+
+
+@pytest.fixture
+def draft_schedule(monkeypatch):
+    def set_to(name):
+        if name is None:
+            monkeypatch.delenv("DSPARK_DRAFT_KERNEL", raising=False)
+        else:
+            monkeypatch.setenv("DSPARK_DRAFT_KERNEL", name)
+    return set_to
+
+
+@pytest.mark.parametrize("base,rank", [(2, 256), (1, 128), (3, 64)])
+def test_draft_schedules_both_match_oracle(draft_schedule, base, rank):
+    # the persistent (one cooperative launch) and per-step schedules of the
+    # draft on the same inputs: both must match the oracle
+    cfg = synth.scaled(synth.config(base), R=45, gamma=4, V=3072, d=32, rank=rank)
+    inp = synth.make_inputs(cfg, device="cpu")
+    xs = []
+    for name in (None, "steps"):
+        draft_schedule(name)
+        buf, _ = run_and_check(cfg, inp)
+        xs.append(n(buf.x))
+    # decisions agree except where the oracle flags a near-tie
+    assert (xs[0] != xs[1]).mean() <= 0.01
+
+
+def test_barrier_wait_is_bounded(monkeypatch):
+    # a one-poll limit on the persistent draft's grid barriers: the launch must
+    # still finish; a barrier that gave up is reported through the status word
+    monkeypatch.setenv("DSPARK_BARRIER_SPINS", "1")
+    cfg = synth.scaled(synth.config(2), R=64, gamma=4, V=4096, d=32)
+    inp = to_dev(synth.make_inputs(cfg, device="cpu"))
+    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV)
+    D.clear_status(buf.ws)
+    D._lib.draft_markov(inp["U"], inp["W1"], inp["W2t"], inp["x0"], cfg.T, 0, 0, buf.x,
+                        buf.logp_d, buf.lse_d, buf.ws)
+    torch.cuda.synchronize()
+    st = D.get_status(buf.ws)
+    x = n(buf.x)
+    assert ((x >= 0) & (x < cfg.V)).all()
+    if not st & D._lib.FLAG_BARRIER:
+        # every barrier happened to complete within one poll: results are valid
+        rep = PC.Report()
+        f32 = lambda t: t.float().cpu().numpy()
+        PC.check_draft(rep, f32(inp["U"]), f32(inp["W1"]), f32(inp["W2t"]), n(inp["x0"]), cfg.T, 0,
+                       0, x, n(buf.logp_d), n(buf.lse_d), None)
+        assert rep.ok(), rep.summary()
+    monkeypatch.delenv("DSPARK_BARRIER_SPINS")
+    D.clear_status(buf.ws)
+    D._lib.draft_markov(inp["U"], inp["W1"], inp["W2t"], inp["x0"], cfg.T, 0, 0, buf.x,
+                        buf.logp_d, buf.lse_d, buf.ws)
+    torch.cuda.synchronize()
+    assert D.get_status(buf.ws) == 0
 
 
 # -------------------------------------------------------- stage: scheduler
