@@ -4,8 +4,10 @@
 // Algorithm 1).  Survival a_{r,j} = prod_{i<=j} c_{r,i} is a left-to-right
 // float32 running product per request.  Candidates (r, j) with a > 0 are
 // ordered by a descending, then r, then j ascending -- a total order -- by
-// sorting 64-bit keys (~bits(a) << 32 | r*32 + j-1) in LDS (bitonic network,
-// 1024 threads).  Admitting the q first candidates gives B = R + q and
+// sorting 64-bit keys (~bits(a) << 32 | r*32 + j-1) with a bitonic network
+// (1024 threads, each holding a run of consecutive positions in registers:
+// only the exchanges wider than a wave's span go through LDS).  Admitting the
+// q first candidates gives B = R + q and
 // tau_q = R + sum of their a; in 2^-32 fixed point the sums are exact, so a
 // block-wide prefix sum yields every tau_q at once, and
 // Theta_q = (tau_q * 2^-32) * SPS(B) is one double product (0 past N_max).
@@ -69,27 +71,94 @@ __device__ inline int block_min_i(int v, int* lds) {
   return t;
 }
 
-__global__ __launch_bounds__(kSchedThreads) void k_schedule(SchedArgs a) {
-  __shared__ uint64_t keys[kSchedMaxKeys];
-  __shared__ int64_t red64[kSchedThreads / 64];
-  __shared__ int red32[kSchedThreads / 64];
+// Compare-exchange for the bitonic network: `lower` is the element with the
+// smaller index of the pair; ascending blocks keep the smaller key there.
+__device__ __forceinline__ uint64_t bitonic_keep(uint64_t mine, uint64_t other, bool lower, bool up) {
+  const bool take_min = (lower == up);
+  return take_min ? (mine < other ? mine : other) : (mine < other ? other : mine);
+}
+
+// Thread t holds the EPT consecutive positions [t EPT, t EPT + EPT) in
+// registers.  Pairs closer than EPT are exchanged inside the thread, pairs
+// closer than 64 EPT across the wave (64-bit lane shuffles), wider pairs
+// through LDS with a workgroup barrier per stage.
+template <int EPT>
+__device__ __forceinline__ void bitonic_sort_regs(uint64_t (&v)[EPT], uint64_t* keys, int P) {
+  const int tid = threadIdx.x;
+  constexpr int WSPAN = 64 * EPT;
+  for (int kk = 2; kk <= P; kk <<= 1) {
+    int j = kk >> 1;
+    if (j >= WSPAN) {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) keys[tid * EPT + e] = v[e];
+      __syncthreads();
+      for (; j >= WSPAN; j >>= 1) {
+        for (int pi = tid; pi < P / 2; pi += kSchedThreads) {
+          const int i = (pi / j) * 2 * j + (pi % j);
+          const uint64_t x = keys[i], y = keys[i + j];
+          const bool up = (i & kk) == 0;
+          if ((x > y) == up) { keys[i] = y; keys[i + j] = x; }
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) v[e] = keys[tid * EPT + e];
+      __syncthreads();
+    }
+    for (; j >= EPT; j >>= 1) {
+      const int lx = j / EPT;                       // partner lane offset
+      const bool lower = (tid & lx) == 0;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int i = tid * EPT + e;
+        const uint64_t o = __shfl_xor(v[e], lx);
+        v[e] = bitonic_keep(v[e], o, lower, (i & kk) == 0);
+      }
+    }
+    // in-thread stages, unrolled over the compile-time distance jj (<= j)
+#pragma unroll
+    for (int jj = EPT / 2; jj >= 1; jj >>= 1) {
+      if (jj <= j) {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+          if ((e & jj) == 0) {
+            const int i = tid * EPT + e;
+            const bool up = (i & kk) == 0;
+            const uint64_t x = v[e], y = v[e | jj];
+            if ((x > y) == up) { v[e] = y; v[e | jj] = x; }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int EPT>
+__device__ __forceinline__ void schedule_body(const SchedArgs& a, uint64_t* keys, int64_t* red64, int* red32) {
   const int tid = threadIdx.x;
   const int R = a.R, G = a.gamma;
   const int n = R * G;
-  int P = 1;
-  while (P < n) P <<= 1;
+  const int P = kSchedThreads * EPT;
 
-  // survival products (left to right, float32) and sort keys
+  // survival products (left to right, float32) and sort keys; the G
+  // confidences of a request are loaded together
   int64_t part = 0;
   for (int r = tid; r < R; r += kSchedThreads) {
+    const float* cr = a.c + (int64_t)r * G;
+    float cv[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) cv[j] = (j < G) ? cr[j] : 0.f;
     float acc = 1.f;
-    for (int j = 1; j <= G; ++j) {
-      acc = __fmul_rn(acc, a.c[(int64_t)r * G + (j - 1)]);
-      if (a.a) a.a[(int64_t)r * G + (j - 1)] = acc;
-      keys[r * G + (j - 1)] = (acc > 0.f)
-          ? ((uint64_t)(0xFFFFFFFFu - __float_as_uint(acc)) << 32) | (uint32_t)(r * 32 + (j - 1))
-          : ~0ull;
-      part += fixed32(acc);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (j < G) {
+        acc = __fmul_rn(acc, cv[j]);
+        if (a.a) a.a[(int64_t)r * G + j] = acc;
+        keys[r * G + j] = (acc > 0.f)
+            ? ((uint64_t)(0xFFFFFFFFu - __float_as_uint(acc)) << 32) | (uint32_t)(r * 32 + j)
+            : ~0ull;
+        part += fixed32(acc);
+      }
     }
   }
   for (int q = n + tid; q < P; q += kSchedThreads) keys[q] = ~0ull;
@@ -106,45 +175,36 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(SchedArgs a) {
     return;
   }
 
-  // bitonic sort, ascending keys = a descending, then r, then j
-  for (int kk = 2; kk <= P; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P; i += kSchedThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t x = keys[i], y = keys[ixj];
-          const bool up = (i & kk) == 0;
-          if ((x > y) == up) { keys[i] = y; keys[ixj] = x; }
-        }
-      }
-      __syncthreads();
-    }
-  }
+  // sort ascending: a descending, then r, then j
+  uint64_t v[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) v[e] = keys[tid * EPT + e];
+  __syncthreads();
+  bitonic_sort_regs<EPT>(v, keys, P);
 
   // fixed-point prefix sums over the sorted order; thread t owns positions
-  // [t*PT, t*PT + PT)
-  const int PT = (P + kSchedThreads - 1) / kSchedThreads;
-  const int p0 = tid * PT;
+  // [t*EPT, t*EPT + EPT)
+  const int p0 = tid * EPT;
   int64_t local = 0;
-  for (int p = p0; p < p0 + PT && p < P; ++p) {
-    const uint64_t key = keys[p];
-    if (key != ~0ull) local += fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(key >> 32)));
-  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if (v[e] != ~0ull) local += fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(v[e] >> 32)));
   int64_t tau = ((int64_t)R << 32) + block_exscan_i64(local, red64);  // tau before p0
-  int first_stop = 0x7FFFFFFF;
-  for (int p = p0; p < p0 + PT && p < P; ++p) {
-    const uint64_t key = keys[p];
-    if (key == ~0ull) break;
-    const int64_t tau_next = tau + fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(key >> 32)));
-    const double before = theta_of(tau, R + p, a.N_max, a.sps);
-    const double after = theta_of(tau_next, R + p + 1, a.N_max, a.sps);
-    if (!(after > before)) { first_stop = p; break; }
-    tau = tau_next;
+  int first_stop = 0x7FFFFFFF, firstsent = 0x7FFFFFFF;
+  bool stopped = false;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int p = p0 + e;
+    if (v[e] == ~0ull) { if (firstsent == 0x7FFFFFFF) firstsent = p; stopped = true; }
+    if (!stopped) {
+      const int64_t tau_next = tau + fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(v[e] >> 32)));
+      const double before = theta_of(tau, R + p, a.N_max, a.sps);
+      const double after = theta_of(tau_next, R + p + 1, a.N_max, a.sps);
+      if (!(after > before)) { first_stop = p; stopped = true; }
+      tau = tau_next;
+    }
   }
   // number of candidates = position of the first sentinel key
-  int firstsent = 0x7FFFFFFF;
-  for (int p = p0; p < p0 + PT && p < P; ++p)
-    if (keys[p] == ~0ull) { firstsent = p; break; }
   int E = block_min_i(firstsent, red32);
   if (E > P) E = P;
   int admitted = block_min_i(first_stop, red32);
@@ -153,20 +213,32 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(SchedArgs a) {
   for (int r = tid; r < R; r += kSchedThreads) a.ell[r] = 0;
   __threadfence();
   __syncthreads();
-  for (int p = tid; p < admitted; p += kSchedThreads) {
-    const uint32_t lo = (uint32_t)keys[p];
-    atomicMax(&a.ell[lo >> 5], (int)(lo & 31u) + 1);
-  }
-  if (tid == 0) {
-    if (a.N_out) *a.N_out = R + admitted;
-  }
-  // Theta of the admitted prefix: the thread owning position admitted-1 knows
-  // tau there; recompute it from a block sum instead (exact integers).
   int64_t mine = 0;
-  for (int p = p0; p < p0 + PT && p < admitted; ++p)
-    mine += fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(keys[p] >> 32)));
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int p = p0 + e;
+    if (p < admitted) {
+      const uint32_t lo = (uint32_t)v[e];
+      atomicMax(&a.ell[lo >> 5], (int)(lo & 31u) + 1);
+      mine += fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(v[e] >> 32)));
+    }
+  }
+  if (tid == 0 && a.N_out) *a.N_out = R + admitted;
+  // Theta of the admitted prefix (exact integer sum)
   const int64_t tau_adm = ((int64_t)R << 32) + block_sum_i64(mine, red64);
   if (tid == 0 && a.theta) *a.theta = theta_of(tau_adm, R + admitted, a.N_max, a.sps);
+}
+
+__global__ __launch_bounds__(kSchedThreads) void k_schedule(SchedArgs a) {
+  __shared__ uint64_t keys[kSchedMaxKeys];
+  __shared__ int64_t red64[kSchedThreads / 64];
+  __shared__ int red32[kSchedThreads / 64];
+  const int n = a.R * a.gamma;
+  if (n <= kSchedThreads) schedule_body<1>(a, keys, red64, red32);
+  else if (n <= 2 * kSchedThreads) schedule_body<2>(a, keys, red64, red32);
+  else if (n <= 4 * kSchedThreads) schedule_body<4>(a, keys, red64, red32);
+  else if (n <= 8 * kSchedThreads) schedule_body<8>(a, keys, red64, red32);
+  else schedule_body<16>(a, keys, red64, red32);
 }
 
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t st) {

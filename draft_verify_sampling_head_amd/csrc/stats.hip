@@ -124,13 +124,24 @@ __device__ __forceinline__ void row_segment(const T* row, int V, int c0, int c1,
   }
 }
 
+constexpr int kCuLds = 2048;               // verify offsets staged in LDS up to this many
+
 template <typename T, bool GREEDY>
 __global__ __launch_bounds__(256) void k_row_stats(RowStatsArgs a) {
+  __shared__ int cus[kCuLds];
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * 4;
   if (a.zero_me && blockIdx.x == 0 && threadIdx.x == 0) *a.zero_me = 0u;
   int nrows = a.nrows_cap;
   if (a.kind != kRowsDraft) nrows = min(nrows, a.cu[a.R]);
+  // dense verify rows: the row of packed index q is found by binary search
+  // over the offsets, staged in LDS when they fit
+  const bool lds_cu = a.kind == kRowsVerifyDense && a.R + 1 <= kCuLds;
+  if (lds_cu) {
+    for (int t = threadIdx.x; t <= a.R; t += 256) cus[t] = a.cu[t];
+    __syncthreads();
+  }
+  const int* cu = lds_cu ? cus : a.cu;
   const int64_t items = (int64_t)nrows * a.segs;
   for (int64_t it = wave; it < items; it += nwaves) {
     const int q = (int)(it / a.segs);
@@ -144,9 +155,9 @@ __global__ __launch_bounds__(256) void k_row_stats(RowStatsArgs a) {
       int lo = 0, hi = a.R - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (a.cu[mid] <= q) lo = mid; else hi = mid - 1;
+        if (cu[mid] <= q) lo = mid; else hi = mid - 1;
       }
-      row = (int64_t)lo * (a.gamma + 1) + (q - a.cu[lo]);
+      row = (int64_t)lo * (a.gamma + 1) + (q - cu[lo]);
     }
     const T* rp = reinterpret_cast<const T*>(a.base) + row * a.V;
     const int c0 = seg * a.cps, c1 = min(a.nch, c0 + a.cps);

@@ -8,14 +8,18 @@
 // Launches, all sized by capacity so N, m and the rejections stay on device:
 //   1. k_row_stats over the N verify rows: chunk log-masses of t/T (or chunk
 //      maxima at T = 0); also clears the residual work counter.
-//   2. k_verify_scan, one wave per request: row normalisers, log p_t(x_k),
-//      the accept scan, and either the bonus draw (chunked Gumbel-max on the
-//      row after the accepted prefix) or a residual work item.
-//   3. residual chunk masses for the listed (request, position) rows: the
+//   2. k_row_norm, one wave per verify row: the row normaliser (raw maximum,
+//      log-sum above it) or, at T = 0, the row argmax.
+//   3. k_verify_scan, one workgroup per request: lane k-1 of the first wave
+//      evaluates position k (log p_t(x_k), its uniform, the accept test) for
+//      every k at once and a ballot finds the first rejection; then either the
+//      bonus draw (chunked Gumbel-max on the row after the accepted prefix)
+//      or a residual work item.
+//   4. residual chunk masses for the listed (request, position) rows: the
 //      draft scores are rebuilt with the Markov bias (MFMA) and combined with
 //      the target row into max(0, p_t - p_d) per chunk.
-//   4. k_resid_pick, one wave per work item: chunk pick and in-chunk pick on
-//      log max(0, p_t - p_d); zero mass falls back to p_t.
+//   5. k_resid_pick, one workgroup per work item: chunk pick and in-chunk pick
+//      on log max(0, p_t - p_d); zero mass falls back to p_t.
 #include "launch.hpp"
 #include "sampling.hpp"
 #include "workspace.hpp"
@@ -54,88 +58,99 @@ __device__ __forceinline__ int64_t target_row(const VerifyArgs& a, int i, int j)
   return a.layout == 0 ? (int64_t)a.cu[i] + j : (int64_t)i * (a.gamma + 1) + j;
 }
 
-template <typename TT>
-__global__ __launch_bounds__(64) void k_verify_scan(VerifyArgs a) {
-  const int i = blockIdx.x;
-  const int lane = threadIdx.x;
-  int L = a.ell[i];
-  if (L < 0 || L > a.gamma) { set_flag(a.status, kFlagBadLen); L = L < 0 ? 0 : a.gamma; }
-  const int q0 = a.cu[i];
-  const int32_t* xi = a.x + (int64_t)i * (a.gamma + 1);
-  const TT* tgt = reinterpret_cast<const TT*>(a.target);
-  int m = L;
-  int y = -1;
-  bool rejected = false;
-  if (!a.greedy) {
-    for (int k = 1; k <= a.gamma; ++k)
-      if (a.logp_t && lane == 0) a.logp_t[(int64_t)i * a.gamma + (k - 1)] = 0.f;
-    RowNorm last{0.f, 0.f};
-    for (int j = 0; j <= L; ++j) {
-      const int q = q0 + j;
-      const RowNorm rn = row_norm(a.vl + (int64_t)q * a.nch, a.nch, a.invT);
-      if (lane == 0) a.lse_t[q] = make_float2(rn.m, rn.lse_rel);
-      if (j < L) {
-        const int k = j + 1;
-        int xk = xi[k];
-        if (xk < 0 || xk >= a.V) { set_flag(a.status, kFlagBadToken); xk = 0; }
-        const float lp = (Elem<TT>::get(tgt + target_row(a, i, j) * a.V, xk) - rn.m) * a.invT
-                         - rn.lse_rel;
-        if (a.logp_t && lane == 0) a.logp_t[(int64_t)i * a.gamma + (k - 1)] = lp;
-        if (!rejected) {
-          const uint4 blk = stream_block(a.seed, a.round, kTagAccept, (uint32_t)i, (uint32_t)k, 0u);
-          const float lu = log_uniform(blk.x);
-          const float rhs = lp - a.logp_d[(int64_t)i * a.gamma + (k - 1)];
-          if (!(lu < rhs)) { rejected = true; m = k - 1; }
-        }
-      } else {
-        last = rn;
-      }
-    }
-    if (!rejected) {
-      // bonus token from the target row after the accepted prefix
-      const int q = q0 + L;
-      const PickResult pc = pick_chunk(a.vl + (int64_t)q * a.nch, a.nch, last.m, a.invT, a.seed,
-                                       a.round, kTagBonusChunk, (uint32_t)i, (uint32_t)(L + 1), false);
-      int c = pc.idx < 0 ? 0 : pc.idx;
-      if (pc.idx < 0) set_flag(a.status, kFlagNonFinite);
-      const TT* trow = tgt + target_row(a, i, L) * a.V;
-      float s[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int v = c * kChunk + h * 64 + lane;
-        s[h] = (v < a.V) ? (Elem<TT>::get(trow, v) - last.m) * a.invT : -INFINITY;
-      }
-      const PickResult pe = pick_in_chunk(s[0], s[1], c * kChunk, a.seed, a.round, kTagBonusElem,
-                                          (uint32_t)i, (uint32_t)(L + 1), false);
-      y = pe.idx < 0 ? c * kChunk : pe.idx;
-    } else if (lane == 0) {
-      const int slot = atomicAdd(a.rej_count, 1);
-      a.rej[slot] = make_int4(i, m + 1, (int)target_row(a, i, m), q0 + m);
-    }
-  } else {
-    for (int k = 1; k <= a.gamma; ++k)
-      if (a.logp_t && lane == 0) a.logp_t[(int64_t)i * a.gamma + (k - 1)] = 0.f;
-    for (int k = 1; k <= L && !rejected; ++k) {
-      const int q = q0 + k - 1;
+// Row normaliser of every verify row q < N: (raw max, log sum_c S_c
+// exp((M_c - max)/T)); at T = 0 (row max, bits of the first argmax).
+__global__ __launch_bounds__(256) void k_row_norm(VerifyArgs a) {
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nwaves = gridDim.x * 4;
+  const int N = min(a.cu[a.R], a.R * (a.gamma + 1));
+  for (int q = wave; q < N; q += nwaves) {
+    if (a.greedy) {
       float v;
       int am;
       argmax_chunks(a.vl + (int64_t)q * a.nch, a.vi + (int64_t)q * a.nch, a.nch, v, am);
-      if (xi[k] != am) { rejected = true; m = k - 1; y = am; }
+      if ((threadIdx.x & 63) == 0) a.lse_t[q] = make_float2(v, __int_as_float(am));
+    } else {
+      const RowNorm rn = row_norm(a.vl + (int64_t)q * a.nch, a.nch, a.invT);
+      if ((threadIdx.x & 63) == 0) a.lse_t[q] = make_float2(rn.m, rn.lse_rel);
     }
-    if (!rejected) {
-      const int q = q0 + L;
-      float v;
-      argmax_chunks(a.vl + (int64_t)q * a.nch, a.vi + (int64_t)q * a.nch, a.nch, v, y);
-    }
-    if (y < 0 || y >= a.V) { set_flag(a.status, kFlagNonFinite); y = 0; }
   }
-  // outputs (y is wave-uniform; a rejected sampled position gets its token
-  // from k_resid_pick)
+}
+
+template <typename TT>
+__global__ __launch_bounds__(256) void k_verify_scan(VerifyArgs a) {
+  __shared__ BlockScratch sh;
+  __shared__ int s_m, s_rej;
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  int L = a.ell[i];
+  if (L < 0 || L > a.gamma) { if (tid == 0) set_flag(a.status, kFlagBadLen); L = L < 0 ? 0 : a.gamma; }
+  const int q0 = a.cu[i];
+  const int32_t* xi = a.x + (int64_t)i * (a.gamma + 1);
+  const TT* tgt = reinterpret_cast<const TT*>(a.target);
+  if (tid < 64) {
+    // lane k-1 evaluates position k
+    const int k = lane + 1;
+    bool rej = false;
+    if (k <= L) {
+      const float2 nt = a.lse_t[q0 + k - 1];
+      int xk = xi[k];
+      if (xk < 0 || xk >= a.V) { set_flag(a.status, kFlagBadToken); xk = 0; }
+      if (a.greedy) {
+        rej = xk != __float_as_int(nt.y);
+        if (a.logp_t) a.logp_t[(int64_t)i * a.gamma + (k - 1)] = 0.f;
+      } else {
+        const float lp = (Elem<TT>::get(tgt + target_row(a, i, k - 1) * a.V, xk) - nt.x) * a.invT
+                         - nt.y;
+        if (a.logp_t) a.logp_t[(int64_t)i * a.gamma + (k - 1)] = lp;
+        const uint4 blk = stream_block(a.seed, a.round, kTagAccept, (uint32_t)i, (uint32_t)k, 0u);
+        const float lu = log_uniform(blk.x);
+        const float rhs = lp - a.logp_d[(int64_t)i * a.gamma + (k - 1)];
+        rej = !(lu < rhs);
+      }
+    } else if (k <= a.gamma && a.logp_t) {
+      a.logp_t[(int64_t)i * a.gamma + (k - 1)] = 0.f;
+    }
+    const uint64_t bal = __ballot(rej);
+    if (lane == 0) {
+      s_rej = bal != 0;
+      s_m = bal ? (__builtin_ctzll(bal)) : L;   // first rejected position k = m + 1
+    }
+  }
+  __syncthreads();
+  const int m = s_m;
+  const bool rejected = s_rej != 0;
+  int y = -1;
+  if (a.greedy) {
+    // correction: the argmax of the first mismatching row; bonus: of row L
+    y = __float_as_int(a.lse_t[q0 + m].y);
+    if (y < 0 || y >= a.V) { if (tid == 0) set_flag(a.status, kFlagNonFinite); y = 0; }
+  } else if (!rejected) {
+    // bonus token from the target row after the accepted prefix
+    const int q = q0 + L;
+    const float2 nt = a.lse_t[q];
+    float srel;
+    const PickResult pc = block_pick_chunk<256>(a.vl + (int64_t)q * a.nch, a.nch, nt.x, a.invT,
+                                                a.seed, a.round, kTagBonusChunk, (uint32_t)i,
+                                                (uint32_t)(L + 1), false, &srel, sh);
+    const int c = pc.idx < 0 ? 0 : pc.idx;
+    if (pc.idx < 0 && tid == 0) set_flag(a.status, kFlagNonFinite);
+    const TT* trow = tgt + target_row(a, i, L) * a.V;
+    const int v = c * kChunk + (tid >> 1);
+    const float s = (v < a.V) ? (Elem<TT>::get(trow, v) - nt.x) * a.invT : -INFINITY;
+    const PickResult pe = block_pick_in_chunk<256>(s, c * kChunk, a.seed, a.round, kTagBonusElem,
+                                                   (uint32_t)i, (uint32_t)(L + 1), false, sh);
+    y = pe.idx < 0 ? c * kChunk : pe.idx;
+  } else if (tid == 0) {
+    const int slot = atomicAdd(a.rej_count, 1);
+    a.rej[slot] = make_int4(i, m + 1, (int)target_row(a, i, m), q0 + m);
+  }
+  // outputs (a rejected sampled position gets its token from k_resid_pick)
   int32_t* em = a.emitted + (int64_t)i * (a.gamma + 1);
   const bool have_y = a.greedy || !rejected;
-  for (int q = lane; q <= a.gamma; q += 64)
+  for (int q = tid; q <= a.gamma; q += 256)
     em[q] = (q < m) ? xi[q + 1] : ((q == m && have_y) ? y : -1);
-  if (lane == 0) {
+  if (tid == 0) {
     a.m[i] = m;
     a.tau[i] = m + 1;
     if (have_y) a.next_anchor[i] = y;
@@ -143,65 +158,63 @@ __global__ __launch_bounds__(64) void k_verify_scan(VerifyArgs a) {
 }
 
 template <typename UT, typename WT>
-__global__ __launch_bounds__(64) void k_resid_pick(VerifyArgs a) {
+__global__ __launch_bounds__(256) void k_resid_pick(VerifyArgs a) {
+  __shared__ BlockScratch sh;
   const int slot = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   if (slot >= *a.rej_count) return;
   const int4 e = a.rej[slot];
   const int i = e.x, k = e.y, trow_i = e.z, q = e.w;
   const UT* trow = reinterpret_cast<const UT*>(a.target) + (int64_t)trow_i * a.V;
   const float2* Lq = a.rl + (int64_t)slot * a.nch;
-  const RowNorm mass = row_norm(Lq, a.nch, 1.f);
   const float2 nt = a.lse_t[q];
+  // chunk pick on the residual masses (keys log S_c + G_c); srel = total mass
+  float mass;
+  const PickResult pr = block_pick_chunk<256>(Lq, a.nch, 0.f, 1.f, a.seed, a.round, kTagResidChunk,
+                                              (uint32_t)i, (uint32_t)k, false, &mass, sh);
+  const int v_off = tid >> 1, h = tid & 1;
   int y;
-  if (mass.lse_rel != -INFINITY) {
-    const PickResult pc = pick_chunk(Lq, a.nch, 0.f, 1.f, a.seed, a.round, kTagResidChunk,
-                                     (uint32_t)i, (uint32_t)k, false);
-    const int c = pc.idx < 0 ? 0 : pc.idx;
+  if (mass > 0.f) {
+    const int c = pr.idx < 0 ? 0 : pr.idx;
+    const int v = c * kChunk + v_off;
     const UT* urow = reinterpret_cast<const UT*>(a.U) + ((int64_t)i * a.gamma + (k - 1)) * a.V;
     int prev = a.x[(int64_t)i * (a.gamma + 1) + (k - 1)];
     if (prev < 0 || prev >= a.V) prev = 0;
     const WT* erow = reinterpret_cast<const WT*>(a.W1) + (int64_t)prev * a.rank;
     const float lse_d = a.lse_d[(int64_t)i * a.gamma + (k - 1)];
-    float s[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int v = c * kChunk + h * 64 + lane;
-      s[h] = -INFINITY;
-      if (v < a.V) {
-        const float b = a.rank > 0 ? markov_bias(erow, reinterpret_cast<const WT*>(a.W2t), a.rank, v)
-                                   : 0.f;
-        const float sd = (Elem<UT>::get(urow, v) + b) * a.invT;
-        const float pt = expf((Elem<UT>::get(trow, v) - nt.x) * a.invT - nt.y);
-        const float pd = expf(sd - lse_d);
-        const float d = pt - pd;
-        s[h] = d > 0.f ? logf(d) : -INFINITY;
-      }
+    float b = 0.f;
+    if (a.rank > 0 && v < a.V) b = markov_bias_half(erow, reinterpret_cast<const WT*>(a.W2t), a.rank, v, h);
+    b += __shfl_xor(b, 1);
+    float s = -INFINITY;
+    if (v < a.V) {
+      const float sd = (Elem<UT>::get(urow, v) + b) * a.invT;
+      const float pt = expf((Elem<UT>::get(trow, v) - nt.x) * a.invT - nt.y);
+      const float pd = expf(sd - lse_d);
+      const float d = pt - pd;
+      s = d > 0.f ? logf(d) : -INFINITY;
     }
-    const PickResult pe = pick_in_chunk(s[0], s[1], c * kChunk, a.seed, a.round, kTagResidElem,
-                                        (uint32_t)i, (uint32_t)k, false);
+    const PickResult pe = block_pick_in_chunk<256>(s, c * kChunk, a.seed, a.round, kTagResidElem,
+                                                   (uint32_t)i, (uint32_t)k, false, sh);
     y = pe.idx;
     if (y < 0) {
       // the chunk's mass vanished on re-evaluation (rounding): keep the chunk's first entry
-      set_flag(a.status, kFlagNonFinite);
+      if (tid == 0) set_flag(a.status, kFlagNonFinite);
       y = c * kChunk;
     }
   } else {
     // zero residual mass: sample p_t of the same row
-    const PickResult pc = pick_chunk(a.vl + (int64_t)q * a.nch, a.nch, nt.x, a.invT, a.seed,
-                                     a.round, kTagResidChunk, (uint32_t)i, (uint32_t)k, false);
+    float srel;
+    const PickResult pc = block_pick_chunk<256>(a.vl + (int64_t)q * a.nch, a.nch, nt.x, a.invT,
+                                                a.seed, a.round, kTagResidChunk, (uint32_t)i,
+                                                (uint32_t)k, false, &srel, sh);
     const int c = pc.idx < 0 ? 0 : pc.idx;
-    float s[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int v = c * kChunk + h * 64 + lane;
-      s[h] = (v < a.V) ? (Elem<UT>::get(trow, v) - nt.x) * a.invT : -INFINITY;
-    }
-    const PickResult pe = pick_in_chunk(s[0], s[1], c * kChunk, a.seed, a.round, kTagResidElem,
-                                        (uint32_t)i, (uint32_t)k, false);
+    const int v = c * kChunk + v_off;
+    const float s = (v < a.V) ? (Elem<UT>::get(trow, v) - nt.x) * a.invT : -INFINITY;
+    const PickResult pe = block_pick_in_chunk<256>(s, c * kChunk, a.seed, a.round, kTagResidElem,
+                                                   (uint32_t)i, (uint32_t)k, false, sh);
     y = pe.idx < 0 ? c * kChunk : pe.idx;
   }
-  if (lane == 0) {
+  if (tid == 0) {
     a.emitted[(int64_t)i * (a.gamma + 1) + (k - 1)] = y;
     a.next_anchor[i] = y;
   }
@@ -248,8 +261,13 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
   a.rej = reinterpret_cast<int4*>(w + L.rej);
   a.rl = reinterpret_cast<float2*>(w + L.draft_l);
   a.status = hdr;
-  if (u_bf16) hipLaunchKernelGGL((k_verify_scan<uint16_t>), dim3(R), dim3(64), 0, st, a);
-  else hipLaunchKernelGGL((k_verify_scan<float>), dim3(R), dim3(64), 0, st, a);
+  {
+    const int rows = R * (gamma + 1);
+    const int grid = min(4096, (rows + 3) / 4);
+    hipLaunchKernelGGL(k_row_norm, dim3(grid), dim3(256), 0, st, a);
+  }
+  if (u_bf16) hipLaunchKernelGGL((k_verify_scan<uint16_t>), dim3(R), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_verify_scan<float>), dim3(R), dim3(256), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess || greedy) return e;
 
@@ -262,7 +280,7 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
   ma.lse_d = lse_d; ma.status = hdr;
   e = launch_markov_stats(ma, u_bf16, w_bf16 && rank > 0, kModeResid, st);
   if (e != hipSuccess) return e;
-#define DSPARK_RP(UT_, WT_) hipLaunchKernelGGL((k_resid_pick<UT_, WT_>), dim3(R), dim3(64), 0, st, a)
+#define DSPARK_RP(UT_, WT_) hipLaunchKernelGGL((k_resid_pick<UT_, WT_>), dim3(R), dim3(256), 0, st, a)
   if (u_bf16 && w_bf16) DSPARK_RP(uint16_t, uint16_t);
   else if (u_bf16) DSPARK_RP(uint16_t, float);
   else if (w_bf16) DSPARK_RP(float, uint16_t);
