@@ -237,6 +237,74 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, const void* lds_wave
 }
 #pragma clang diagnostic pop
 
+// The wave's 64-entry W2 slice as A operands of v_mfma_f32_16x16x32_bf16:
+// lane (m, kg) of M tile mt holds entry 16 (m >> 2) + 4 mt + (m & 3) of the
+// slice, k-values 32 kt + 8 kg + [0, 8).  Entries past V re-read entry V-1.
+template <int KT>
+__device__ __forceinline__ void load_w2_slice(bf16x8_t (&Af)[4][KT], const uint16_t* W2t, int rank,
+                                              int wslice, int V, bool active) {
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    int voc = wslice + 16 * (m >> 2) + 4 * mt + (m & 3);
+    voc = active ? min(voc, V - 1) : 0;
+    const uint16_t* wr = W2t + (int64_t)voc * rank + 8 * kg;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) Af[mt][kt] = *reinterpret_cast<const bf16x8_t*>(wr + 32 * kt);
+  }
+}
+
+// W1 rows of the tokens PV[0, rows) into LDS rows of ROWP 16-byte pieces:
+// piece p is segment p % ROWP of row p / ROWP (the pad piece of a row
+// re-reads its segment 0; pieces past the last row re-read it).  Direct-to-LDS
+// loads, one 1 KB run per wave instruction, waited for before returning.
+template <int SEG, int ROWP>
+__device__ __forceinline__ void gather_w1_rows(uint4* E, const int* PV, int rows, const uint16_t* W1,
+                                               int rank) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int npieces = rows * ROWP;
+  for (int p0 = wv * 64; p0 < npieces; p0 += (int)blockDim.x) {
+    const int p = p0 + lane;
+    const int rl = min(p / ROWP, rows - 1), sp = p % ROWP;
+    lds_dma16(W1 + (int64_t)PV[rl] * rank + 8 * (sp < SEG ? sp : 0), E + p0);
+  }
+  wait_vm_zero();
+}
+
+// MFMA chain of one 16-row tile: acc[mt] (seeded by the caller) += the wave's
+// W2 slice x the W1 rows of tile rows.  erow points at segment lg of the
+// lane's row; B operands pass through a three-deep register ring (the LDS
+// read of k-step kt+2 is issued before the MFMAs of kt).
+template <int KT>
+__device__ __forceinline__ void tile_mfma(f32x4_t (&acc)[4], const bf16x8_t (&Af)[4][KT],
+                                          const uint4* erow) {
+  bf16x8_t Bq[3];
+  Bq[0] = __builtin_bit_cast(bf16x8_t, erow[0]);
+  if (KT > 1) Bq[1] = __builtin_bit_cast(bf16x8_t, erow[4]);
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 2 < KT) Bq[(kt + 2) % 3] = __builtin_bit_cast(bf16x8_t, erow[4 * (kt + 2)]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[mt][kt], Bq[kt % 3], acc[mt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Seed four 4-value accumulators with 16 bf16 values (two 16-byte pieces).
+__device__ __forceinline__ void seed_acc(f32x4_t (&acc)[4], const uint4 (&un)[2]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t wd[4] = {un[q].x, un[q].y, un[q].z, un[q].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 8 * q + e;
+      acc[j >> 2][j & 3] = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
+    }
+  }
+}
+
 // Pick of step a.k for request i by the 512-thread workgroup of the persistent
 // launch (same arithmetic as pick_row).  The row's chunk statistics and
 // W1[x_{k-1}] are first staged in LDS; each of the four threads of an entry
@@ -384,17 +452,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   // ---- W2 slice of this wave, resident for the whole launch
   constexpr int KT = KS / 2;                // k-steps of 32
   bf16x8_t Af[4][KT];
-  {
-    const int m = lane & 15, kg = lane >> 4;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      int voc = wslice + 16 * (m >> 2) + 4 * mt + (m & 3);
-      voc = wave_active ? min(voc, V - 1) : 0;
-      const uint16_t* wr = W2t + (int64_t)voc * a.rank + 8 * kg;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) Af[mt][kt] = *reinterpret_cast<const bf16x8_t*>(wr + 32 * kt);
-    }
-  }
+  load_w2_slice<KT>(Af, W2t, a.rank, wslice, V, wave_active);
   // this lane's 16 entries: two 16-byte pieces of U
   const int ln = lane & 15, lg = lane >> 4;
   const int ubase = wslice + 16 * lg;
@@ -415,11 +473,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       const int row0 = g * kPRows;
       const int rows = min(kPRows, R - row0);
       if (slice_active) {
-        // tokens x_{k-1} of the group, then the W1 rows: 16-byte piece p of E
-        // is segment p % ROWP of row p / ROWP (the pad piece stays unwritten).
-        // Ordinary loads, all issued before the LDS stores: direct-to-LDS
-        // loads would make the compiler fence every later LDS store of the
-        // kernel behind all outstanding vector-memory loads.
+        // tokens x_{k-1} of the group (staged in LDS), then their W1 rows
         for (int rl = tid; rl < rows; rl += kPThreads) {
           const int row = row0 + rl;
           int prev = (k == 1) ? a.x0[row] : ld_coh(a.x + (int64_t)row * (a.gamma + 1) + (k - 1));
@@ -427,16 +481,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
           PV[rl] = prev;
         }
         __syncthreads();
-        // direct-to-LDS loads, one 1 KB run of 64 pieces per instruction;
-        // pieces past the group's rows re-read its last row and pad pieces
-        // re-read segment 0 (their slots are never read)
-        const int npieces = rows * ROWP;
-        for (int p0 = wv * 64; p0 < npieces; p0 += kPThreads) {
-          const int p = p0 + lane;
-          const int rl = min(p / ROWP, rows - 1), sp = p % ROWP;
-          lds_dma16(W1 + (int64_t)PV[rl] * a.rank + 8 * (sp < SEG ? sp : 0), E + p0);
-        }
-        wait_vm_zero();
+        gather_w1_rows<SEG, ROWP>(E, PV, rows, W1, a.rank);
       }
       wait_vm_zero();
       __syncthreads();
@@ -454,31 +499,10 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         // slot is refilled with the tile two ahead
         auto tile = [&](uint4 (&un)[2], int i) __attribute__((always_inline)) {
           f32x4_t acc[4];
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const uint32_t wd[4] = {un[q].x, un[q].y, un[q].z, un[q].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int j = 8 * q + e;        // entry 16 lg + j = 16 lg + 4 mt + jj
-              acc[j >> 2][j & 3] = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
-            }
-          }
+          seed_acc(acc, un);
           if (i + 2 < ntiles) load_u(un, i + 2);
           const int rl = 16 * i + ln;
-          const uint4* erow = E + rl * ROWP + lg;   // segment 4 kt + lg at erow[4 kt]
-          // B operands through a three-deep register ring: the LDS read of
-          // k-step kt+2 is issued before the MFMAs of kt
-          bf16x8_t Bq[3];
-          Bq[0] = __builtin_bit_cast(bf16x8_t, erow[0]);
-          if (KT > 1) Bq[1] = __builtin_bit_cast(bf16x8_t, erow[4]);
-#pragma unroll
-          for (int kt = 0; kt < KT; ++kt) {
-            if (kt + 2 < KT) Bq[(kt + 2) % 3] = __builtin_bit_cast(bf16x8_t, erow[4 * (kt + 2)]);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[mt][kt], Bq[kt % 3], acc[mt], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+          tile_mfma<KT>(acc, Af, E + rl * ROWP + lg);
           // x = U + bias for the lane's 16 consecutive entries (invalid -> -inf)
           float x[16];
 #pragma unroll
@@ -575,6 +599,157 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     for (int i = b; i < R; i += gridDim.x) pick_row_p<KS, GREEDY>(a, i, sh, Ls, Is, Es);
     if (k < a.gamma) grid_barrier(P.bar, ++epoch, P.spin_limit, a.status);
   }
+}
+
+// ================================================= residual statistics
+// Per-chunk residual mass sum_{v in c} max(0, p_t(v) - p_d(v)) of the rows in
+// the verify's residual work list (DSpark: resample the first rejected
+// position from norm(max(0, p_t - p_d))).  p_d is rebuilt exactly as the draft
+// computed it: U + W1[x_{k-1}] W2 over the whole vocabulary.  Same layout as
+// the persistent draft's phase A: workgroup b loads its 512-entry W2 slice
+// into registers once and computes every listed row in 16-row tiles, so W2 is
+// streamed once per call whatever the number of rejections.
+struct ResidArgs {
+  int R, gamma, V, rank, nch, nslice;
+  float scale2;                             // log2(e)/T
+  const uint16_t* U;
+  const uint16_t* W1;
+  const uint16_t* W2t;
+  const uint16_t* target;
+  const int32_t* x;
+  const int32_t* rej_count;
+  const int4* rej;                          // (request, position k, target row, verify row)
+  const float2* lse_t;                      // [verify row] (raw max, log-normaliser above it)
+  const float* lse_d;
+  float2* L;                                // out [slot][nch] (0, residual mass)
+  uint32_t* status;
+};
+
+template <int KS>
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_resid_stats(ResidArgs A) {
+  constexpr int SEG = 2 * KS, ROWP = SEG + 1, KT = KS / 2;
+  __shared__ uint4 E[kPRows * ROWP];
+  __shared__ float HS[kPRows * kPWaves];
+  __shared__ int PV[kPRows];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = blockIdx.x;
+  const int nrows = min(*A.rej_count, A.R);
+  if (nrows <= 0) return;
+  const int V = A.V;
+  const int wslice = b * kPSlice + 64 * wv;
+  const bool wave_active = wslice < V;
+  bf16x8_t Af[4][KT];
+  load_w2_slice<KT>(Af, A.W2t, A.rank, wslice, V, wave_active);
+  const int ln = lane & 15, lg = lane >> 4;
+  const int ubase = wslice + 16 * lg;
+  bool uok[2];
+  int uoff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    uok[q] = wave_active && ubase + 8 * q + 8 <= V;
+    uoff[q] = uok[q] ? ubase + 8 * q : 0;
+  }
+  const float s2 = A.scale2, invT = s2 * kLn2;
+  for (int row0 = 0; row0 < nrows; row0 += kPRows) {
+    const int rows = min(kPRows, nrows - row0);
+    for (int rl = tid; rl < rows; rl += kPThreads) {
+      const int4 e = A.rej[row0 + rl];
+      int prev = A.x[(int64_t)e.x * (A.gamma + 1) + (e.y - 1)];
+      if (prev < 0 || prev >= V) { set_flag(A.status, kFlagBadToken); prev = 0; }
+      PV[rl] = prev;
+    }
+    __syncthreads();
+    gather_w1_rows<SEG, ROWP>(E, PV, rows, A.W1, A.rank);
+    __syncthreads();
+    if (wave_active) {
+      const int ntiles = (rows + 15) / 16;
+      // per tile, this lane's row: its U and target pieces and normalisers
+      struct RowIn { uint4 u[2], t[2]; float2 nt; float ld; };
+      auto load_row = [&](RowIn& d, int i) __attribute__((always_inline)) {
+        const int4 e = A.rej[row0 + min(16 * i + ln, rows - 1)];
+        const uint16_t* up = A.U + ((int64_t)e.x * A.gamma + (e.y - 1)) * V;
+        const uint16_t* tp = A.target + (int64_t)e.z * V;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          d.u[q] = *reinterpret_cast<const uint4*>(up + uoff[q]);
+          d.t[q] = *reinterpret_cast<const uint4*>(tp + uoff[q]);
+        }
+        d.nt = A.lse_t[e.w];
+        d.ld = A.lse_d[(int64_t)e.x * A.gamma + (e.y - 1)];
+      };
+      RowIn cur, nxt;
+      load_row(nxt, 0);
+      for (int i = 0; i < ntiles; ++i) {
+        cur = nxt;
+        if (i + 1 < ntiles) load_row(nxt, i + 1);
+        f32x4_t acc[4];
+        seed_acc(acc, cur.u);
+        const int rl = 16 * i + ln;
+        tile_mfma<KT>(acc, Af, E + rl * ROWP + lg);
+        const float lrt2 = cur.nt.y * kLog2e;
+        float S = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (uok[j >> 3]) {
+            const uint32_t w = (j & 8) ? ((j & 4) ? ((j & 2) ? cur.t[1].w : cur.t[1].z)
+                                                  : ((j & 2) ? cur.t[1].y : cur.t[1].x))
+                                       : ((j & 4) ? ((j & 2) ? cur.t[0].w : cur.t[0].z)
+                                                  : ((j & 2) ? cur.t[0].y : cur.t[0].x));
+            const float tv = (j & 1) ? bf16_hi(w) : bf16_lo(w);
+            const float pt = __builtin_amdgcn_exp2f((tv - cur.nt.x) * s2 - lrt2);
+            const float pd = __builtin_amdgcn_exp2f((acc[j >> 2][j & 3] * invT - cur.ld) * kLog2e);
+            S += fmaxf(pt - pd, 0.f);
+          }
+        }
+        S += __shfl_xor(S, 16);
+        S += __shfl_xor(S, 32);
+        if (lg == 0 && rl < rows) HS[rl * kPWaves + wv] = S;
+      }
+    } else {
+      for (int rl = lane; rl < rows; rl += 64) HS[rl * kPWaves + wv] = 0.f;
+    }
+    __syncthreads();
+    for (int t = tid; t < rows * 4; t += kPThreads) {
+      const int rl = t >> 2, c = t & 3;
+      const int chunk = 4 * b + c;
+      if (chunk >= A.nch) continue;
+      const float St = HS[rl * kPWaves + 2 * c] + HS[rl * kPWaves + 2 * c + 1];
+      A.L[(int64_t)(row0 + rl) * A.nch + chunk] = make_float2(0.f, St);
+      if (nonfinite(St)) set_flag(A.status, kFlagNonFinite);
+    }
+    __syncthreads();
+  }
+}
+
+// Residual statistics on the W2-slice layout when the shape allows it
+// (bf16 data and weights, rank 64/128/256, 16-byte aligned rows, V a multiple
+// of 8); returns false to let the caller use the per-tile kernel.
+bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void* U,
+                         const void* W1, const void* W2t, const void* target, const int32_t* x,
+                         const int32_t* rej_count, const int4* rej, const float2* lse_t,
+                         const float* lse_d, float2* L, uint32_t* status, hipStream_t st,
+                         hipError_t* err) {
+  const char* env = std::getenv("DSPARK_DRAFT_KERNEL");
+  if (env && std::strcmp(env, "steps") == 0) return false;
+  if ((V % 8) != 0 || (rank != 64 && rank != 128 && rank != 256)) return false;
+  for (const void* p : {U, W1, W2t, target})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return false;
+  ResidArgs A{};
+  A.R = R; A.gamma = gamma; A.V = V; A.rank = rank; A.nch = (V + kChunk - 1) / kChunk;
+  A.nslice = (V + kPSlice - 1) / kPSlice;
+  A.scale2 = kLog2e / T;
+  A.U = reinterpret_cast<const uint16_t*>(U);
+  A.W1 = reinterpret_cast<const uint16_t*>(W1);
+  A.W2t = reinterpret_cast<const uint16_t*>(W2t);
+  A.target = reinterpret_cast<const uint16_t*>(target);
+  A.x = x; A.rej_count = rej_count; A.rej = rej; A.lse_t = lse_t; A.lse_d = lse_d; A.L = L;
+  A.status = status;
+  if (rank == 64) hipLaunchKernelGGL((k_resid_stats<4>), dim3(A.nslice), dim3(kPThreads), 0, st, A);
+  else if (rank == 128) hipLaunchKernelGGL((k_resid_stats<8>), dim3(A.nslice), dim3(kPThreads), 0, st, A);
+  else hipLaunchKernelGGL((k_resid_stats<16>), dim3(A.nslice), dim3(kPThreads), 0, st, A);
+  *err = hipGetLastError();
+  return true;
 }
 
 // Per-device facts for the persistent schedule (compute units; whether one

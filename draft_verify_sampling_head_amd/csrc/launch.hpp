@@ -98,6 +98,11 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
                         const int32_t* x0, int32_t* x, float* logp_d, float* lse_d, float* margin,
                         void* ws, hipStream_t st, hipEvent_t* ev_begin = nullptr,
                         hipEvent_t* ev_end = nullptr, int* n_timed = nullptr);
+bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void* U,
+                         const void* W1, const void* W2t, const void* target, const int32_t* x,
+                         const int32_t* rej_count, const int4* rej, const float2* lse_t,
+                         const float* lse_d, float2* L, uint32_t* status, hipStream_t st,
+                         hipError_t* err);
 hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,
                          const int32_t* ell, const int32_t* cu, const void* target, int layout,
                          const int32_t* x, const float* logp_d, const float* lse_d,

@@ -271,15 +271,22 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
   e = hipGetLastError();
   if (e != hipSuccess || greedy) return e;
 
-  MarkovArgs ma{};
-  ma.R = R; ma.gamma = gamma; ma.k = 0; ma.V = V; ma.rank = rank; ma.nch = nch; ma.nrows_cap = R;
-  ma.U = U; ma.W1v = W1; ma.W2tv = W2t; ma.x0 = nullptr; ma.x = x; ma.scale2 = kLog2e / T;
-  ma.u_vec_ok = u_vec && t_vec;
-  ma.L = const_cast<float2*>(a.rl); ma.I = nullptr;
-  ma.rej_count = a.rej_count; ma.rej = a.rej; ma.target = target; ma.lse_t = a.lse_t;
-  ma.lse_d = lse_d; ma.status = hdr;
-  e = launch_markov_stats(ma, u_bf16, w_bf16 && rank > 0, kModeResid, st);
-  if (e != hipSuccess) return e;
+  if (u_bf16 && w_bf16 && rank > 0 && u_vec && t_vec &&
+      launch_resid_slices(R, gamma, V, rank, T, U, W1, W2t, target, x, a.rej_count, a.rej,
+                          a.lse_t, lse_d, const_cast<float2*>(a.rl), hdr, st, &e)) {
+    if (e != hipSuccess) return e;
+  } else {
+    // per-tile kernel for the other shapes
+    MarkovArgs ma{};
+    ma.R = R; ma.gamma = gamma; ma.k = 0; ma.V = V; ma.rank = rank; ma.nch = nch; ma.nrows_cap = R;
+    ma.U = U; ma.W1v = W1; ma.W2tv = W2t; ma.x0 = nullptr; ma.x = x; ma.scale2 = kLog2e / T;
+    ma.u_vec_ok = u_vec && t_vec;
+    ma.L = const_cast<float2*>(a.rl); ma.I = nullptr;
+    ma.rej_count = a.rej_count; ma.rej = a.rej; ma.target = target; ma.lse_t = a.lse_t;
+    ma.lse_d = lse_d; ma.status = hdr;
+    e = launch_markov_stats(ma, u_bf16, w_bf16 && rank > 0, kModeResid, st);
+    if (e != hipSuccess) return e;
+  }
 #define DSPARK_RP(UT_, WT_) hipLaunchKernelGGL((k_resid_pick<UT_, WT_>), dim3(R), dim3(256), 0, st, a)
   if (u_bf16 && w_bf16) DSPARK_RP(uint16_t, uint16_t);
   else if (u_bf16) DSPARK_RP(uint16_t, float);
