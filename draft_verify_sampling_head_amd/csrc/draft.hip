@@ -174,44 +174,34 @@ __device__ __forceinline__ void st_coh2(float2* p, float2 v) {
 }
 
 // Grid-wide barrier number `epoch` (1-based) over gridDim.x co-resident
-// workgroups, in two levels so that no counter takes more than a few dozen
-// same-address atomics per barrier (they serialise where device-scope atomics
-// are performed): workgroup b arrives on group counter b % kBarGroups; the
-// last arrival of a group arrives on the top counter, which every workgroup
-// polls.  The workgroup barrier first completes every wave's memory
-// operations (it waits for vmcnt 0); the counters use relaxed device-scope
-// atomics.  The wait is bounded: past spin_limit polls the workgroup sets
-// kFlagBarrier and stops waiting, and every later barrier of the launch
-// returns at once, so the kernel always runs to its end.
-constexpr int kBarGroups = 16;
-constexpr int kBarStride = 16;              // uint32 words between counters (64 bytes)
+// workgroups, as a flag array: workgroup b stores `epoch` in its own word
+// flags[b] and polls all gridDim.x words until every one has reached `epoch`.
+// No word takes more than one store per barrier, so nothing serialises on a
+// shared counter.  The workgroup barrier first completes every wave's memory
+// operations (it waits for vmcnt 0); flags are written and read with relaxed
+// device-scope atomics.  The wait is bounded: past spin_limit polls the
+// workgroup sets kFlagBarrier and stops waiting, and every later barrier of
+// the launch returns at once, so the kernel always runs to its end.
+constexpr int kMaxGrid = 1024;              // flag words in the workspace
 
-__device__ __forceinline__ void grid_barrier(uint32_t* bar, uint32_t epoch, uint32_t spin_limit,
+__device__ __forceinline__ void grid_barrier(uint32_t* flags, uint32_t epoch, uint32_t spin_limit,
                                              uint32_t* status) {
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t G = gridDim.x, b = blockIdx.x;
-    const uint32_t g = b % kBarGroups;
-    const uint32_t in_group = (G - g + kBarGroups - 1) / kBarGroups;
-    const uint32_t groups = G < (uint32_t)kBarGroups ? G : (uint32_t)kBarGroups;
-    uint32_t* top = bar + kBarGroups * kBarStride;
-    const uint32_t old = __hip_atomic_fetch_add(bar + g * kBarStride, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1 == epoch * in_group)
-      __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t target = epoch * groups;
-    const bool broken =
-        (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kFlagBarrier) != 0;
-    if (!broken) {
-      uint32_t spins = 0;
-      while (__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins >= spin_limit) {
-          atomicOr(status, kFlagBarrier);
-          break;
-        }
-      }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(flags + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool broken =
+      (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kFlagBarrier) != 0;
+  if (broken) return;
+  for (uint32_t spins = 0;; ++spins) {
+    int ok = 1;
+    for (uint32_t t = threadIdx.x; t < gridDim.x; t += blockDim.x)
+      ok &= __hip_atomic_load(flags + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= epoch;
+    if (__syncthreads_and(ok)) break;
+    if (spins + 1 >= spin_limit) {
+      if (threadIdx.x == 0) atomicOr(status, kFlagBarrier);
+      break;
     }
+    __builtin_amdgcn_s_sleep(1);
   }
   __syncthreads();
 }
@@ -305,13 +295,41 @@ __device__ __forceinline__ void seed_acc(f32x4_t (&acc)[4], const uint4 (&un)[2]
   }
 }
 
+// (key, index) argmax with the lower index winning ties, and a sum.
+struct PickRed {
+  float key;
+  int idx;
+  float s;
+};
+// Reduction of PickRed over the 512 threads (every thread gets the result;
+// the sum is taken in a fixed order).
+__device__ __forceinline__ PickRed block_pick_reduce(PickRed v, PickRed* lds) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    argmax_merge(v.key, v.idx, __shfl_xor(v.key, o), __shfl_xor(v.idx, o));
+    v.s += __shfl_xor(v.s, o);
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+  __syncthreads();
+  PickRed r = lds[0];
+#pragma unroll
+  for (int q = 1; q < kPWaves; ++q) {
+    argmax_merge(r.key, r.idx, lds[q].key, lds[q].idx);
+    r.s += lds[q].s;
+  }
+  return r;
+}
+
 // Pick of step a.k for request i by the 512-thread workgroup of the persistent
-// launch (same arithmetic as pick_row).  The row's chunk statistics and
-// W1[x_{k-1}] are first staged in LDS; each of the four threads of an entry
-// then issues all of its W2t loads at once.
+// launch.  The row's chunk statistics and W1[x_{k-1}] are first staged in LDS.
+// Sampling: after the row maximum, one reduction gives both the chunk-level
+// Gumbel winner and the row normaliser; the chosen chunk's 128 scores
+// are rebuilt by four threads per entry (all W2t loads issued at once), and the
+// thread holding the in-chunk winner writes the outputs.
 template <int KS, bool GREEDY>
 __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, BlockScratch& sh,
-                                           float2* Ls, int* Is, uint4* Es) {
+                                           float2* Ls, int* Is, uint4* Es, PickRed* red) {
   constexpr int NT = kPThreads, TPE = NT / kChunk;
   constexpr int SEG = 2 * KS, NQ = SEG / TPE;   // 16-byte pieces of the rank per thread
   const int tid = threadIdx.x;
@@ -335,80 +353,126 @@ __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, BlockS
     Es[tid] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.W1) +
                                               (int64_t)prev * a.rank + 8 * tid);
   __syncthreads();
-  int xk;
-  float logp, lse, gap = INFINITY;
+  const int64_t o = (int64_t)i * a.gamma + (k - 1);
   if (GREEDY) {
     float v = -INFINITY;
     int idx = 0x7FFFFFFF;
     for (int c = tid; c < a.nch; c += NT) argmax_merge(v, idx, Ls[c].x, Is[c]);
     block_argmax<NT>(v, idx, sh);
-    xk = idx;
-    lse = v;
-    logp = 0.f;
+    int xk = idx;
     if (xk < 0 || xk >= a.V) { set_flag(a.status, kFlagNonFinite); xk = 0; }
+    if (tid == 0) {
+      if (k == 1) st_coh(a.x + xo, a.x0[i]);
+      st_coh(a.x + xo + k, xk);
+      a.logp_d[o] = 0.f;
+      a.lse_d[o] = v;
+      if (a.margin) a.margin[o] = INFINITY;
+    }
   } else {
-    float m = -INFINITY;
-    for (int c = tid; c < a.nch; c += NT) m = fmaxf(m, Ls[c].x);
-    m = block_max<NT>(m, sh);
+    // scores are kept relative to the raw row maximum m (accuracy at low T)
+    float mloc = -INFINITY;
+    for (int c = tid; c < a.nch; c += NT) mloc = fmaxf(mloc, Ls[c].x);
+    const float m = block_max<NT>(mloc, sh);
+    // chunk level: thread t owns chunks 4t..4t+3 (one Philox block); one
+    // reduction gives the Gumbel winner of (M_c - m)/T + log S_c + G_c and
+    // the normaliser sum_c S_c exp((M_c - m)/T)
+    const bool draw = a.nch > 1;
+    PickRed pr{-INFINITY, 0x7FFFFFFF, 0.f};
+    if (4 * tid < a.nch) {
+      uint4 blk = make_uint4(0, 0, 0, 0);
+      if (draw) blk = stream_block(a.seed, a.round, kTagDraftChunk, (uint32_t)i, (uint32_t)k, (uint32_t)tid);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int c = 4 * tid + w;
+        if (c < a.nch) {
+          const float2 v = Ls[c];
+          if (v.y > 0.f) {
+            const float rel = (v.x - m) * a.invT;
+            pr.s += v.y * expf(rel);
+            const float key = rel + logf(v.y) + (draw ? gumbel_of(word_of(blk, (uint32_t)w)) : 0.f);
+            argmax_merge(pr.key, pr.idx, key, c);
+          }
+        }
+      }
+    }
+    const PickRed rr = block_pick_reduce(pr, red);
+    const float lse_rel = logf(rr.s);
+    const float lse = m * a.invT + lse_rel;
+    int c = rr.key == -INFINITY ? -1 : rr.idx;
+    if (c < 0) { if (tid == 0) set_flag(a.status, kFlagNonFinite); c = 0; }
     const bool want_gap = a.margin != nullptr;
-    float srel;
-    const PickResult pc = block_pick_chunk<NT>(Ls, a.nch, m, a.invT, a.seed, a.round,
-                                               kTagDraftChunk, (uint32_t)i, (uint32_t)k, want_gap,
-                                               &srel, sh);
-    const float lse_rel = logf(srel);
-    lse = m * a.invT + lse_rel;
-    int c = pc.idx;
-    if (c < 0) { set_flag(a.status, kFlagNonFinite); c = 0; }
+    float cgap = INFINITY;
+    if (want_gap && draw) {
+      // second-best chunk key (debug output only)
+      float second = -INFINITY;
+      if (4 * tid < a.nch) {
+        const uint4 blk = stream_block(a.seed, a.round, kTagDraftChunk, (uint32_t)i, (uint32_t)k, (uint32_t)tid);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int cc = 4 * tid + w;
+          if (cc < a.nch && cc != c) {
+            const float2 v = Ls[cc];
+            if (v.y > 0.f)
+              second = fmaxf(second, (v.x - m) * a.invT + logf(v.y) + gumbel_of(word_of(blk, (uint32_t)w)));
+          }
+        }
+      }
+      cgap = rr.key - block_max<NT>(second, sh);
+    }
+    // in-chunk: entry base + tid / TPE, part tid % TPE of the rank
     const int base = c * kChunk;
     const int v = base + tid / TPE, h = tid % TPE;
     const bool in = v < a.V;
-    float b = 0.f, u = 0.f;
+    float bsum = 0.f, u = 0.f;
     if (in) {
       const uint4* wr = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.W2t) +
                                                        (int64_t)v * a.rank) + h * NQ;
+      uint4 wq[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) wq[q] = wr[q];
       u = bf16_at(reinterpret_cast<const uint16_t*>(a.U), ((int64_t)i * a.gamma + (k - 1)) * a.V + v);
-      // W2t loads in two halves (register budget: the W2 slice stays resident)
-      constexpr int NQH = NQ > 1 ? NQ / 2 : 1;
 #pragma unroll
-      for (int q0 = 0; q0 < NQ; q0 += NQH) {
-      uint4 wq[NQH];
-#pragma unroll
-      for (int q = 0; q < NQH; ++q) wq[q] = wr[q0 + q];
-#pragma unroll
-      for (int q = 0; q < NQH; ++q) {
-        const uint4 x = Es[h * NQ + q0 + q];
+      for (int q = 0; q < NQ; ++q) {
+        const uint4 x = Es[h * NQ + q];
         const uint4 w = wq[q];
-        b = fmaf(bf16_lo(x.x), bf16_lo(w.x), b);
-        b = fmaf(bf16_hi(x.x), bf16_hi(w.x), b);
-        b = fmaf(bf16_lo(x.y), bf16_lo(w.y), b);
-        b = fmaf(bf16_hi(x.y), bf16_hi(w.y), b);
-        b = fmaf(bf16_lo(x.z), bf16_lo(w.z), b);
-        b = fmaf(bf16_hi(x.z), bf16_hi(w.z), b);
-        b = fmaf(bf16_lo(x.w), bf16_lo(w.w), b);
-        b = fmaf(bf16_hi(x.w), bf16_hi(w.w), b);
-      }
+        bsum = fmaf(bf16_lo(x.x), bf16_lo(w.x), bsum);
+        bsum = fmaf(bf16_hi(x.x), bf16_hi(w.x), bsum);
+        bsum = fmaf(bf16_lo(x.y), bf16_lo(w.y), bsum);
+        bsum = fmaf(bf16_hi(x.y), bf16_hi(w.y), bsum);
+        bsum = fmaf(bf16_lo(x.z), bf16_lo(w.z), bsum);
+        bsum = fmaf(bf16_hi(x.z), bf16_hi(w.z), bsum);
+        bsum = fmaf(bf16_lo(x.w), bf16_lo(w.w), bsum);
+        bsum = fmaf(bf16_hi(x.w), bf16_hi(w.w), bsum);
       }
     }
 #pragma unroll
-    for (int o = 1; o < TPE; o *= 2) b += __shfl_xor(b, o);
-    const float s = in ? (u + b - m) * a.invT : -INFINITY;
-    const PickResult pe = block_pick_in_chunk<NT>(s, base, a.seed, a.round, kTagDraftElem,
-                                                  (uint32_t)i, (uint32_t)k, want_gap, sh);
-    xk = pe.idx;
-    if (xk < 0) { set_flag(a.status, kFlagNonFinite); xk = base; }
-    __syncthreads();
-    if (tid == TPE * (xk - base)) sh.g[0] = s;
-    __syncthreads();
-    logp = sh.g[0] - lse_rel;
-    gap = fminf(pc.gap, pe.gap);
-  }
-  if (tid == 0) {
-    if (k == 1) st_coh(a.x + xo, a.x0[i]);
-    st_coh(a.x + xo + k, xk);
-    const int64_t o = (int64_t)i * a.gamma + (k - 1);
-    a.logp_d[o] = logp;
-    a.lse_d[o] = lse;
-    if (a.margin) a.margin[o] = gap;
+    for (int oo = 1; oo < TPE; oo *= 2) bsum += __shfl_xor(bsum, oo);
+    const float sv = in ? (u + bsum - m) * a.invT : -INFINITY;   // score of entry v, minus m/T
+    float key = -INFINITY;
+    int kid = 0x7FFFFFFF;
+    if (h == 0 && in) {
+      const uint4 blk = stream_block(a.seed, a.round, kTagDraftElem, (uint32_t)i, (uint32_t)k, (uint32_t)v >> 2);
+      key = sv + gumbel_of(word_of(blk, (uint32_t)v & 3u));
+      kid = v;
+    }
+    float best = key;
+    int bidx = kid;
+    block_argmax<NT>(best, bidx, sh);
+    int xk = best == -INFINITY ? -1 : bidx;
+    float egap = INFINITY;
+    if (want_gap && xk >= 0) egap = best - block_max<NT>(kid == xk ? -INFINITY : key, sh);
+    if (xk < 0) {
+      if (tid == 0) set_flag(a.status, kFlagNonFinite);
+      xk = base;
+    }
+    // the thread holding the winner writes the outputs
+    if (tid == TPE * (xk - base)) {
+      if (k == 1) st_coh(a.x + xo, a.x0[i]);
+      st_coh(a.x + xo + k, xk);
+      a.logp_d[o] = sv - lse_rel;
+      a.lse_d[o] = lse;
+      if (a.margin) a.margin[o] = fminf(cgap, egap);
+    }
   }
   wait_vm_zero();
   __syncthreads();                          // LDS staging and sh are reused
@@ -430,6 +494,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   __shared__ uint4 UA[UA_BYTES / 16];
   __shared__ int PV[kPRows];
   __shared__ BlockScratch sh;
+  __shared__ PickRed pred[kPWaves];
   float2* HS = reinterpret_cast<float2*>(UA);                       // [row][wave]
   int* HI = reinterpret_cast<int*>(reinterpret_cast<char*>(UA) + HS_BYTES);
   float2* Ls = reinterpret_cast<float2*>(UA);                       // pick: chunk statistics
@@ -596,7 +661,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     }
     grid_barrier(P.bar, ++epoch, P.spin_limit, a.status);
     // ================= phase B: the pick of step k, one request per workgroup
-    for (int i = b; i < R; i += gridDim.x) pick_row_p<KS, GREEDY>(a, i, sh, Ls, Is, Es);
+    for (int i = b; i < R; i += gridDim.x) pick_row_p<KS, GREEDY>(a, i, sh, Ls, Is, Es, pred);
     if (k < a.gamma) grid_barrier(P.bar, ++epoch, P.spin_limit, a.status);
   }
 }
@@ -799,7 +864,8 @@ static int persistent_grid(int V, int rank, bool u_bf16, bool w_bf16, bool u_vec
     pi.cus = cus;
   }
   const int nslice = (V + kPSlice - 1) / kPSlice;
-  if (pi.cus < 1 || nslice > pi.cus || (V + kChunk - 1) / kChunk > kPMaxChunks) return 0;
+  if (pi.cus < 1 || pi.cus > kMaxGrid || nslice > pi.cus || (V + kChunk - 1) / kChunk > kPMaxChunks)
+    return 0;
   bool fits;
   if (rank == 64) fits = greedy ? persist_fits<4, true>(pi, 0) : persist_fits<4, false>(pi, 0);
   else if (rank == 128) fits = greedy ? persist_fits<8, true>(pi, 1) : persist_fits<8, false>(pi, 1);
@@ -843,7 +909,7 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     const char* sl = std::getenv("DSPARK_BARRIER_SPINS");
     P.spin_limit = sl ? (uint32_t)std::strtoul(sl, nullptr, 10) : kBarrierSpins;
     if (P.spin_limit == 0) P.spin_limit = 1;
-    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, st, P.bar, (kBarGroups + 1) * kBarStride);
+    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, st, P.bar, kMaxGrid);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev_begin && (e = hipEventRecord(ev_begin[0], st)) != hipSuccess) return e;

@@ -18,7 +18,7 @@ struct WsLayout {
   size_t ver_i;        // int32  [R*(gamma+1)][nch]  target-row chunk argmax (greedy)
   size_t lse_t;        // float2 [R*(gamma+1)]       target-row (max, log-normaliser above it)
   size_t rej;          // int32  [R][4]   residual work list: request, position, row, pad
-  size_t bar;          // uint32 grid-barrier counters of the persistent draft, 64 bytes apart
+  size_t bar;          // uint32 [1024] grid-barrier flags of the persistent draft, one per workgroup
   size_t total;
 };
 
@@ -36,7 +36,7 @@ inline WsLayout ws_layout(int R, int gamma, int V) {
   L.ver_i = off;   off += ws_align(rows_v * nch * 4);
   L.lse_t = off;   off += ws_align(rows_v * 8);
   L.rej = off;     off += ws_align((size_t)R * 16);
-  L.bar = off;     off += ws_align(64 * 17);
+  L.bar = off;     off += ws_align(4 * 1024);
   L.total = off;
   return L;
 }
