@@ -282,6 +282,216 @@ __device__ __forceinline__ void tile_mfma(f32x4_t (&acc)[4], const bf16x8_t (&Af
   }
 }
 
+// Cross-lane exchanges on the VALU (gfx950 v_permlane16_swap /
+// v_permlane32_swap with both operands the same register): afterwards every
+// lane holds {its own value, the value of lane ^ 16 (resp. ^ 32)} in some
+// order, so a symmetric merge of the pair gives the same bits on both lanes.
+__device__ __forceinline__ void xswap16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void xswap32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void iswap16(int v, int& a, int& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  a = (int)r[0];
+  b = (int)r[1];
+}
+__device__ __forceinline__ void iswap32(int v, int& a, int& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  a = (int)r[0];
+  b = (int)r[1];
+}
+
+// (max, sum of exp2((x - max) s2)) of two halves, symmetric in its operands;
+// branch-free (an empty half has max -inf and sum 0; a NaN sum stays NaN).
+__device__ __forceinline__ void ms_merge(float M0, float S0, float M1, float S1, float s2, float& M,
+                                         float& S) {
+  const float Mn = fmaxf(M0, M1);
+  const float Mr = (Mn == -INFINITY) ? 0.f : Mn;
+  S = S0 * __builtin_amdgcn_exp2f((M0 - Mr) * s2) + S1 * __builtin_amdgcn_exp2f((M1 - Mr) * s2);
+  M = Mn;
+}
+
+// Half-chunk statistics of a 16-row tile (sampling): the lane's 16 values,
+// then the four lanes of the row (xor 16, xor 32).  Every lane of the row
+// ends with the row's (max, sum relative to it) over the wave's 64 entries.
+__device__ __forceinline__ void epi_sample(const f32x4_t (&acc)[4], const bool (&uok)[2], float s2,
+                                           float& M, float& S) {
+  float x[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) x[j] = uok[j >> 3] ? acc[j >> 2][j & 3] : -INFINITY;
+  float m = fmaxf(fmaxf(x[0], x[1]), x[2]);
+#pragma unroll
+  for (int j = 3; j < 15; j += 2) m = fmaxf(fmaxf(m, x[j]), x[j + 1]);
+  m = fmaxf(m, x[15]);
+  const float mr = (m == -INFINITY) ? 0.f : m;
+  const float mr2 = mr * s2;
+  float sm = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sm += __builtin_amdgcn_exp2f(fmaf(x[j], s2, -mr2));
+  // the sum is relative to mr2 = round(mr * s2): refer it to mr exactly
+  sm *= __builtin_amdgcn_exp2f(-fmaf(mr, s2, -mr2));
+  float a0, a1, b0, b1;
+  xswap16(m, a0, a1);
+  xswap16(sm, b0, b1);
+  ms_merge(a0, b0, a1, b1, s2, m, sm);
+  xswap32(m, a0, a1);
+  xswap32(sm, b0, b1);
+  ms_merge(a0, b0, a1, b1, s2, M, S);
+}
+
+// Half-chunk argmax of a 16-row tile (greedy), lowest index on ties.
+__device__ __forceinline__ void epi_greedy(const f32x4_t (&acc)[4], const bool (&uok)[2], int ubase,
+                                           float& bv, int& bi) {
+  bv = -INFINITY;
+  bi = 0x7FFFFFFF;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float x = uok[j >> 3] ? acc[j >> 2][j & 3] : -INFINITY;
+    const bool gt = x > bv;
+    bv = gt ? x : bv;
+    bi = gt ? ubase + j : bi;
+  }
+  float v0, v1;
+  int i0, i1;
+  xswap16(bv, v0, v1);
+  iswap16(bi, i0, i1);
+  argmax_merge(v0, i0, v1, i1);
+  xswap32(v0, bv, v1);
+  iswap32(i0, bi, i1);
+  argmax_merge(bv, bi, v1, i1);
+}
+
+// MFMA chain of one 16-row tile without scheduling barriers (for the
+// software-pipelined tile loop, which interleaves it with an epilogue).
+template <int KT>
+__device__ __forceinline__ void tile_mfma_free(f32x4_t (&acc)[4], const bf16x8_t (&Af)[4][KT],
+                                               const uint4* erow) {
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const bf16x8_t B = __builtin_bit_cast(bf16x8_t, erow[4 * kt]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[mt][kt], B, acc[mt], 0, 0, 0);
+  }
+}
+
+// Epilogue of a 16-row tile split into 8 units so that it can be interleaved
+// with the MFMAs of the next tile (unit u runs after the MFMAs of the k-step
+// that owns it).  Sampling: units 0-1 masked maximum over the two halves of
+// the lane's 16 values, 2-5 the exp2 sums (4 values each), 6 the rounding
+// correction and the xor-16 lane merge, 7 the xor-32 merge.  Greedy: units
+// 0-1 argmax over the halves, 2 the xor-16 merge, 3 the xor-32 merge.
+struct EpiState {
+  float m, s, mr2, mr;
+  int bi;
+};
+template <bool GREEDY>
+__device__ __forceinline__ void epi_unit(int u, EpiState& st, const f32x4_t (&acc)[4],
+                                         const bool (&uok)[2], float s2, int ubase) {
+  auto xv = [&](int j) __attribute__((always_inline)) {
+    return uok[j >> 3] ? acc[j >> 2][j & 3] : -INFINITY;
+  };
+  if (GREEDY) {
+    if (u == 0 || u == 1) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = 8 * u + q;
+        const float x = xv(j);
+        const bool gt = x > st.m;
+        st.m = gt ? x : st.m;
+        st.bi = gt ? ubase + j : st.bi;
+      }
+    } else if (u == 2) {
+      float v0, v1;
+      int i0, i1;
+      xswap16(st.m, v0, v1);
+      iswap16(st.bi, i0, i1);
+      argmax_merge(v0, i0, v1, i1);
+      st.m = v0;
+      st.bi = i0;
+    } else if (u == 3) {
+      float v0, v1;
+      int i0, i1;
+      xswap32(st.m, v0, v1);
+      iswap32(st.bi, i0, i1);
+      argmax_merge(v0, i0, v1, i1);
+      st.m = v0;
+      st.bi = i0;
+    }
+  } else {
+    if (u == 0) {
+      float m = fmaxf(fmaxf(xv(0), xv(1)), xv(2));
+      m = fmaxf(fmaxf(m, xv(3)), xv(4));
+      m = fmaxf(fmaxf(m, xv(5)), xv(6));
+      st.m = fmaxf(m, xv(7));
+    } else if (u == 1) {
+      float m = fmaxf(fmaxf(st.m, xv(8)), xv(9));
+      m = fmaxf(fmaxf(m, xv(10)), xv(11));
+      m = fmaxf(fmaxf(m, xv(12)), xv(13));
+      m = fmaxf(fmaxf(m, xv(14)), xv(15));
+      st.m = m;
+      st.mr = (m == -INFINITY) ? 0.f : m;
+      st.mr2 = st.mr * s2;
+      st.s = 0.f;
+    } else if (u >= 2 && u <= 5) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        st.s += __builtin_amdgcn_exp2f(fmaf(xv(4 * (u - 2) + q), s2, -st.mr2));
+    } else if (u == 6) {
+      // the sum is relative to mr2 = round(mr * s2): refer it to mr exactly
+      st.s *= __builtin_amdgcn_exp2f(-fmaf(st.mr, s2, -st.mr2));
+      float a0, a1, b0, b1;
+      xswap16(st.m, a0, a1);
+      xswap16(st.s, b0, b1);
+      ms_merge(a0, b0, a1, b1, s2, st.m, st.s);
+    } else if (u == 7) {
+      float a0, a1, b0, b1;
+      xswap32(st.m, a0, a1);
+      xswap32(st.s, b0, b1);
+      ms_merge(a0, b0, a1, b1, s2, st.m, st.s);
+    }
+  }
+}
+
+// One pipelined tile step: the MFMA chain of the next tile (acc_next, already
+// seeded) interleaved k-step by k-step with the epilogue units of the current
+// tile (acc_cur).  B operands come through a three-deep register ring.
+template <int KT, bool GREEDY>
+__device__ __forceinline__ void mfma_with_epilogue(f32x4_t (&acc_next)[4], const bf16x8_t (&Af)[4][KT],
+                                                   const uint4* erow, const f32x4_t (&acc_cur)[4],
+                                                   const bool (&uok)[2], float s2, int ubase,
+                                                   EpiState& st) {
+  constexpr int NU = 8;                     // epilogue units
+  bf16x8_t Bq[3];
+  Bq[0] = __builtin_bit_cast(bf16x8_t, erow[0]);
+  if (KT > 1) Bq[1] = __builtin_bit_cast(bf16x8_t, erow[4]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 2 < KT) Bq[(kt + 2) % 3] = __builtin_bit_cast(bf16x8_t, erow[4 * (kt + 2)]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      acc_next[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[mt][kt], Bq[kt % 3], acc_next[mt], 0, 0, 0);
+#pragma unroll
+    for (int u = kt * NU / KT; u < (kt + 1) * NU / KT; ++u) epi_unit<GREEDY>(u, st, acc_cur, uok, s2, ubase);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The whole epilogue of a tile without MFMAs (last tile of a group).
+template <bool GREEDY>
+__device__ __forceinline__ void epilogue_all(EpiState& st, const f32x4_t (&acc)[4], const bool (&uok)[2],
+                                             float s2, int ubase) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) epi_unit<GREEDY>(u, st, acc, uok, s2, ubase);
+}
+
 // Seed four 4-value accumulators with 16 bf16 values (two 16-byte pieces).
 __device__ __forceinline__ void seed_acc(f32x4_t (&acc)[4], const uint4 (&un)[2]) {
 #pragma unroll
@@ -560,66 +770,57 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
           for (int q = 0; q < 2; ++q) dst[q] = *reinterpret_cast<const uint4*>(up + uoff[q]);
         };
-        // one 16-row tile: its U (in `un`) seeds the accumulators, then the
-        // slot is refilled with the tile two ahead
-        auto tile = [&](uint4 (&un)[2], int i) __attribute__((always_inline)) {
-          f32x4_t acc[4];
-          seed_acc(acc, un);
-          if (i + 2 < ntiles) load_u(un, i + 2);
+        // Software-pipelined tiles: while the MFMAs of tile i+1 run, the
+        // vector ALU works on the epilogue of tile i (their instructions are
+        // interleaved by the scheduling groups below).  U slots: slot
+        // (i+1) % 2 seeds tile i+1 and is then refilled with tile i+3.
+        auto store_stats = [&](int i, float M, float S, int bi) __attribute__((always_inline)) {
           const int rl = 16 * i + ln;
-          tile_mfma<KT>(acc, Af, E + rl * ROWP + lg);
-          // x = U + bias for the lane's 16 consecutive entries (invalid -> -inf)
-          float x[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) x[j] = uok[j >> 3] ? acc[j >> 2][j & 3] : -INFINITY;
-          const bool row_ok = rl < rows;
-          if (GREEDY) {
-            float bv = -INFINITY;
-            int bi = 0x7FFFFFFF;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const bool gt = x[j] > bv;
-              bv = gt ? x[j] : bv;
-              bi = gt ? ubase + j : bi;
-            }
-            argmax_merge(bv, bi, __shfl_xor(bv, 16), __shfl_xor(bi, 16));
-            argmax_merge(bv, bi, __shfl_xor(bv, 32), __shfl_xor(bi, 32));
-            if (lg == 0 && row_ok) { HS[rl * kPWaves + wv] = make_float2(bv, 0.f); HI[rl * kPWaves + wv] = bi; }
-          } else {
-            float M = x[0];
-#pragma unroll
-            for (int j = 1; j < 16; ++j) M = fmaxf(M, x[j]);
-            float S = 0.f;
-            if (M != -INFINITY) {
-              const float Ms2 = M * s2;
-#pragma unroll
-              for (int j = 0; j < 16; ++j) S += __builtin_amdgcn_exp2f(fmaf(x[j], s2, -Ms2));
-              // the sum is relative to Ms2 = round(M * s2): refer it to M exactly
-              S *= __builtin_amdgcn_exp2f(-fmaf(M, s2, -Ms2));
-            }
-            // combine the four lanes of the row (xor 16, then xor 32)
-#pragma unroll
-            for (int o = 16; o <= 32; o *= 2) {
-              const float Mo = __shfl_xor(M, o), So = __shfl_xor(S, o);
-              const float Mn = fmaxf(M, Mo);
-              float St = 0.f;
-              if (Mn != -INFINITY) {
-                if (__float_as_uint(S) != 0u) St += S * __builtin_amdgcn_exp2f((M - Mn) * s2);
-                if (__float_as_uint(So) != 0u) St += So * __builtin_amdgcn_exp2f((Mo - Mn) * s2);
-              }
-              M = Mn;
-              S = St;
-            }
-            if (lg == 0 && row_ok) HS[rl * kPWaves + wv] = make_float2(M, S);
+          if (lg == 0 && rl < rows) {
+            HS[rl * kPWaves + wv] = make_float2(M, S);
+            if (GREEDY) HI[rl * kPWaves + wv] = bi;
           }
         };
+        auto fresh = [&]() __attribute__((always_inline)) {
+          EpiState st;
+          st.m = -INFINITY; st.s = 0.f; st.mr = 0.f; st.mr2 = 0.f; st.bi = 0x7FFFFFFF;
+          return st;
+        };
+        // one pipelined iteration: epilogue of tile i (acc_cur) with the MFMAs
+        // of tile i+1 (acc_next, seeded from `un`)
+        auto step2 = [&](f32x4_t (&acc_cur)[4], f32x4_t (&acc_next)[4], uint4 (&un)[2], int i)
+            __attribute__((always_inline)) {
+          seed_acc(acc_next, un);
+          load_u(un, min(i + 3, ntiles - 1));   // unconditional: same loads in flight on every path
+          const int rln = 16 * (i + 1) + ln;
+          EpiState st = fresh();
+          mfma_with_epilogue<KT, GREEDY>(acc_next, Af, E + rln * ROWP + lg, acc_cur, uok, s2, ubase, st);
+          store_stats(i, st.m, st.s, st.bi);
+        };
+        auto last = [&](const f32x4_t (&acc)[4], int i) __attribute__((always_inline)) {
+          EpiState st = fresh();
+          epilogue_all<GREEDY>(st, acc, uok, s2, ubase);
+          store_stats(i, st.m, st.s, st.bi);
+        };
         uint4 ua[2], ub[2];
+        f32x4_t accA[4], accB[4];
         load_u(ua, 0);
-        if (ntiles > 1) load_u(ub, 1);
+        load_u(ub, min(1, ntiles - 1));
         wait_vm_zero();
-        for (int i = 0; i < ntiles; i += 2) {
-          tile(ua, i);
-          if (i + 1 < ntiles) tile(ub, i + 1);
+        // tile 0 alone
+        seed_acc(accA, ua);
+        load_u(ua, min(2, ntiles - 1));
+        tile_mfma<KT>(accA, Af, E + ln * ROWP + lg);
+        int i = 0;
+        for (; i + 2 < ntiles; i += 2) {
+          step2(accA, accB, ub, i);       // epilogue i, MFMA i+1 (seeded from ub)
+          step2(accB, accA, ua, i + 1);   // epilogue i+1, MFMA i+2 (seeded from ua)
+        }
+        if (i + 1 < ntiles) {
+          step2(accA, accB, ub, i);
+          last(accB, i + 1);
+        } else {
+          last(accA, i);
         }
       } else {
         // no entries in this wave's slice: empty halves
