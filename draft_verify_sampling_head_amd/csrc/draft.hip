@@ -20,6 +20,7 @@
 //                persistent kernel does not take (float32 data, rank other than
 //                64/128/256, vocabularies beyond 512 entries per compute unit).
 // Nothing returns to the host in either schedule.
+#include <cfloat>
 #include <cstdlib>
 #include <cstring>
 
@@ -131,12 +132,14 @@ __global__ __launch_bounds__(256) void k_draft_pick(DraftPickArgs a) {
 // Workgroup b (512 threads, eight waves) owns vocabulary slice [512 b, 512 b +
 // 512): wave w holds entries 512 b + 64 w + [0, 64) of W2 as the A operands of
 // v_mfma_f32_16x16x32_bf16 (four 16-entry M tiles x rank/32 k-steps, loaded
-// once).  Entry order inside a wave: lane (n, g) of a 16x16 result holds, in
-// accumulator slot j of M tile mt, entry 16 g + 4 mt + j of the wave's slice,
-// so each lane owns 16 consecutive entries of one request row (its U segment
-// is one contiguous 32-byte read) and a row's 64 entries sit in lanes n, n+16,
-// n+32, n+48.  The requests are the N dimension: 16-row tiles whose B
-// operands (W1[x_{k-1}] rows) are read from LDS.
+// once).  The requests are the N dimension: 16-row tiles whose B operands
+// (W1[x_{k-1}] rows) are read from LDS, and U seeds the accumulators.  Entry
+// order inside a wave (slice_entry): lane (n, g) of a 16x16 result holds two
+// runs of 8 consecutive entries of request row n, 8 g + [0, 8) and 32 + 8 g +
+// [0, 8), so the 16 rows x 4 lane groups of one U load instruction read 64
+// contiguous bytes per row.  Each lane keeps its own partial statistics (no
+// cross-lane work in the tile loop); a row's 8 partials per 128-entry chunk
+// are merged once the whole group is done.
 constexpr int kPThreads = 512;
 constexpr int kPWaves = 8;
 constexpr int kPSlice = 512;                // vocabulary entries per workgroup
@@ -227,9 +230,19 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, const void* lds_wave
 }
 #pragma clang diagnostic pop
 
+// Entry of the wave's 64-entry slice held by lane group lg (= lane / 16) in
+// value j of its 16 results (acc[j >> 2][j & 3], C-matrix row 4 lg + (j & 3)
+// of M tile j >> 2): values 0-7 and 8-15 are two runs of 8 consecutive
+// entries, so each run is one 16-byte piece of a U row and the four lane
+// groups of a row together read 64 contiguous bytes per load instruction.
+__device__ __forceinline__ constexpr int slice_entry(int lg, int j) {
+  return 32 * (j >> 3) + 8 * lg + (j & 7);
+}
+
 // The wave's 64-entry W2 slice as A operands of v_mfma_f32_16x16x32_bf16:
-// lane (m, kg) of M tile mt holds entry 16 (m >> 2) + 4 mt + (m & 3) of the
-// slice, k-values 32 kt + 8 kg + [0, 8).  Entries past V re-read entry V-1.
+// lane (m, kg) of M tile mt holds entry slice_entry(m >> 2, 4 mt + (m & 3)) of
+// the slice (C row m of M tile mt), k-values 32 kt + 8 kg + [0, 8).  Entries
+// past V re-read entry V-1.
 template <int KT>
 __device__ __forceinline__ void load_w2_slice(bf16x8_t (&Af)[4][KT], const uint16_t* W2t, int rank,
                                               int wslice, int V, bool active) {
@@ -237,7 +250,7 @@ __device__ __forceinline__ void load_w2_slice(bf16x8_t (&Af)[4][KT], const uint1
   const int m = lane & 15, kg = lane >> 4;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    int voc = wslice + 16 * (m >> 2) + 4 * mt + (m & 3);
+    int voc = wslice + slice_entry(m >> 2, 4 * mt + (m & 3));
     voc = active ? min(voc, V - 1) : 0;
     const uint16_t* wr = W2t + (int64_t)voc * rank + 8 * kg;
 #pragma unroll
@@ -285,187 +298,128 @@ __device__ __forceinline__ void tile_mfma(f32x4_t (&acc)[4], const bf16x8_t (&Af
 // Cross-lane exchanges on the VALU (gfx950 v_permlane16_swap /
 // v_permlane32_swap with both operands the same register): afterwards every
 // lane holds {its own value, the value of lane ^ 16 (resp. ^ 32)} in some
-// order, so a symmetric merge of the pair gives the same bits on both lanes.
-__device__ __forceinline__ void xswap16(float v, float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+// order, so a merge that is symmetric in the pair gives the same bits on both
+// lanes.
+template <int X>
+__device__ __forceinline__ void xswap(float v, float& a, float& b) {
+  const auto r = (X == 16)
+      ? __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+      : __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   a = __uint_as_float(r[0]);
   b = __uint_as_float(r[1]);
 }
-__device__ __forceinline__ void xswap32(float v, float& a, float& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  a = __uint_as_float(r[0]);
-  b = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void iswap16(int v, int& a, int& b) {
-  const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
-  a = (int)r[0];
-  b = (int)r[1];
-}
-__device__ __forceinline__ void iswap32(int v, int& a, int& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+template <int X>
+__device__ __forceinline__ void iswap(int v, int& a, int& b) {
+  const auto r = (X == 16) ? __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false)
+                           : __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
   a = (int)r[0];
   b = (int)r[1];
 }
 
-// (max, sum of exp2((x - max) s2)) of two halves, symmetric in its operands;
-// branch-free (an empty half has max -inf and sum 0; a NaN sum stays NaN).
-__device__ __forceinline__ void ms_merge(float M0, float S0, float M1, float S1, float s2, float& M,
-                                         float& S) {
-  const float Mn = fmaxf(M0, M1);
-  const float Mr = (Mn == -INFINITY) ? 0.f : Mn;
-  S = S0 * __builtin_amdgcn_exp2f((M0 - Mr) * s2) + S1 * __builtin_amdgcn_exp2f((M1 - Mr) * s2);
-  M = Mn;
+// Scaled reference of a partial with raw maximum m: fl(m s2), or -FLT_MAX
+// when the partial is empty (m = -inf), so that differences of references
+// are never NaN.
+__device__ __forceinline__ float scaled_ref(float m, float s2) {
+  return (m == -INFINITY) ? -FLT_MAX : m * s2;
 }
 
-// Half-chunk statistics of a 16-row tile (sampling): the lane's 16 values,
-// then the four lanes of the row (xor 16, xor 32).  Every lane of the row
-// ends with the row's (max, sum relative to it) over the wave's 64 entries.
-__device__ __forceinline__ void epi_sample(const f32x4_t (&acc)[4], const bool (&uok)[2], float s2,
-                                           float& M, float& S) {
-  float x[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) x[j] = uok[j >> 3] ? acc[j >> 2][j & 3] : -INFINITY;
-  float m = fmaxf(fmaxf(x[0], x[1]), x[2]);
-#pragma unroll
-  for (int j = 3; j < 15; j += 2) m = fmaxf(fmaxf(m, x[j]), x[j + 1]);
-  m = fmaxf(m, x[15]);
-  const float mr = (m == -INFINITY) ? 0.f : m;
-  const float mr2 = mr * s2;
-  float sm = 0.f;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) sm += __builtin_amdgcn_exp2f(fmaf(x[j], s2, -mr2));
-  // the sum is relative to mr2 = round(mr * s2): refer it to mr exactly
-  sm *= __builtin_amdgcn_exp2f(-fmaf(mr, s2, -mr2));
-  float a0, a1, b0, b1;
-  xswap16(m, a0, a1);
-  xswap16(sm, b0, b1);
-  ms_merge(a0, b0, a1, b1, s2, m, sm);
-  xswap32(m, a0, a1);
-  xswap32(sm, b0, b1);
-  ms_merge(a0, b0, a1, b1, s2, M, S);
-}
-
-// Half-chunk argmax of a 16-row tile (greedy), lowest index on ties.
-__device__ __forceinline__ void epi_greedy(const f32x4_t (&acc)[4], const bool (&uok)[2], int ubase,
-                                           float& bv, int& bi) {
-  bv = -INFINITY;
-  bi = 0x7FFFFFFF;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float x = uok[j >> 3] ? acc[j >> 2][j & 3] : -INFINITY;
-    const bool gt = x > bv;
-    bv = gt ? x : bv;
-    bi = gt ? ubase + j : bi;
-  }
-  float v0, v1;
-  int i0, i1;
-  xswap16(bv, v0, v1);
-  iswap16(bi, i0, i1);
-  argmax_merge(v0, i0, v1, i1);
-  xswap32(v0, bv, v1);
-  iswap32(i0, bi, i1);
-  argmax_merge(bv, bi, v1, i1);
-}
-
-// MFMA chain of one 16-row tile without scheduling barriers (for the
-// software-pipelined tile loop, which interleaves it with an epilogue).
-template <int KT>
-__device__ __forceinline__ void tile_mfma_free(f32x4_t (&acc)[4], const bf16x8_t (&Af)[4][KT],
-                                               const uint4* erow) {
-#pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    const bf16x8_t B = __builtin_bit_cast(bf16x8_t, erow[4 * kt]);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[mt][kt], B, acc[mt], 0, 0, 0);
-  }
-}
-
-// Epilogue of a 16-row tile split into 8 units so that it can be interleaved
-// with the MFMAs of the next tile (unit u runs after the MFMAs of the k-step
-// that owns it).  Sampling: units 0-1 masked maximum over the two halves of
-// the lane's 16 values, 2-5 the exp2 sums (4 values each), 6 the rounding
-// correction and the xor-16 lane merge, 7 the xor-32 merge.  Greedy: units
-// 0-1 argmax over the halves, 2 the xor-16 merge, 3 the xor-32 merge.
+// Statistics of one 16-row tile: every lane first reduces its 16 values of
+// one request row, then the four lanes of the row (xor 16, xor 32) merge.
+// The work is split into 8 units so that it can be interleaved with the MFMAs
+// of the next tile (unit u runs after the MFMAs of the k-step that owns it).
+//   sampling: raw maximum M, scaled reference m2 = scaled_ref(M), and
+//             S = sum_j exp2(x_j s2 - m2).  Merging two partials keeps the
+//             larger reference: S = S_big + S_small exp2(m2_small - m2_big)
+//             (one exponential, never above 1), and since fl(m s2) is
+//             monotone in m the merged m2 is again scaled_ref(merged M).
+//             Units 0-1 the maximum, 2-5 the exponentials (two partial
+//             sums), 6 the xor-16 merge, 7 the xor-32 merge.
+//   greedy:   the maximum and the lowest entry holding it (0x7FFFFFFF when
+//             the maximum is -inf).  Units 0-1 the maximum, 2-3 the index
+//             scan from j = 15 down, 4-5 the merges.
+// MASK: the lane's pieces past V (uok false) count as -inf.
 struct EpiState {
-  float m, s, mr2, mr;
+  float m, s0, s1, m2;
   int bi;
 };
-template <bool GREEDY>
+template <int X>
+__device__ __forceinline__ void merge_sample(EpiState& st) {
+  float m_a, m_b, r_a, r_b, s_a, s_b;
+  xswap<X>(st.m, m_a, m_b);
+  xswap<X>(st.m2, r_a, r_b);
+  xswap<X>(st.s0, s_a, s_b);
+  const bool a_big = r_a >= r_b;
+  const float hi = fmaxf(r_a, r_b), lo = fminf(r_a, r_b);
+  const float e = __builtin_amdgcn_exp2f(lo - hi);
+  st.s0 = fmaf(a_big ? s_b : s_a, e, a_big ? s_a : s_b);
+  st.m = fmaxf(m_a, m_b);
+  st.m2 = hi;
+}
+template <int X>
+__device__ __forceinline__ void merge_greedy(EpiState& st) {
+  float v0, v1;
+  int i0, i1;
+  xswap<X>(st.m, v0, v1);
+  iswap<X>(st.bi, i0, i1);
+  argmax_merge(v0, i0, v1, i1);
+  st.m = v0;
+  st.bi = i0;
+}
+template <bool GREEDY, bool MASK>
 __device__ __forceinline__ void epi_unit(int u, EpiState& st, const f32x4_t (&acc)[4],
-                                         const bool (&uok)[2], float s2, int ubase) {
+                                         const bool (&uok)[2], float s2, int gbase) {
   auto xv = [&](int j) __attribute__((always_inline)) {
-    return uok[j >> 3] ? acc[j >> 2][j & 3] : -INFINITY;
+    return (!MASK || uok[j >> 3]) ? acc[j >> 2][j & 3] : -INFINITY;
   };
-  if (GREEDY) {
-    if (u == 0 || u == 1) {
+  if (u == 0) {
+    float m = fmaxf(fmaxf(xv(0), xv(1)), xv(2));
+    m = fmaxf(fmaxf(m, xv(3)), xv(4));
+    m = fmaxf(fmaxf(m, xv(5)), xv(6));
+    st.m = fmaxf(m, xv(7));
+  } else if (u == 1) {
+    float m = fmaxf(fmaxf(st.m, xv(8)), xv(9));
+    m = fmaxf(fmaxf(m, xv(10)), xv(11));
+    m = fmaxf(fmaxf(m, xv(12)), xv(13));
+    m = fmaxf(fmaxf(m, xv(14)), xv(15));
+    st.m = m;
+    if (!GREEDY) st.m2 = scaled_ref(m, s2);
+  } else if (GREEDY) {
+    if (u == 2 || u == 3) {
+      int bl = (u == 2) ? 16 : st.bi;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int j = 8 * u + q;
-        const float x = xv(j);
-        const bool gt = x > st.m;
-        st.m = gt ? x : st.m;
-        st.bi = gt ? ubase + j : st.bi;
+      for (int q = 7; q >= 0; --q) {
+        const int j = 8 * (3 - u) + q;
+        bl = (xv(j) == st.m) ? j : bl;
       }
-    } else if (u == 2) {
-      float v0, v1;
-      int i0, i1;
-      xswap16(st.m, v0, v1);
-      iswap16(st.bi, i0, i1);
-      argmax_merge(v0, i0, v1, i1);
-      st.m = v0;
-      st.bi = i0;
-    } else if (u == 3) {
-      float v0, v1;
-      int i0, i1;
-      xswap32(st.m, v0, v1);
-      iswap32(st.bi, i0, i1);
-      argmax_merge(v0, i0, v1, i1);
-      st.m = v0;
-      st.bi = i0;
+      st.bi = bl;
+      if (u == 3)
+        st.bi = (st.m == -INFINITY || bl == 16) ? 0x7FFFFFFF : gbase + 32 * (bl >> 3) + (bl & 7);
+    } else if (u == 4) {
+      merge_greedy<16>(st);
+    } else if (u == 5) {
+      merge_greedy<32>(st);
     }
-  } else {
-    if (u == 0) {
-      float m = fmaxf(fmaxf(xv(0), xv(1)), xv(2));
-      m = fmaxf(fmaxf(m, xv(3)), xv(4));
-      m = fmaxf(fmaxf(m, xv(5)), xv(6));
-      st.m = fmaxf(m, xv(7));
-    } else if (u == 1) {
-      float m = fmaxf(fmaxf(st.m, xv(8)), xv(9));
-      m = fmaxf(fmaxf(m, xv(10)), xv(11));
-      m = fmaxf(fmaxf(m, xv(12)), xv(13));
-      m = fmaxf(fmaxf(m, xv(14)), xv(15));
-      st.m = m;
-      st.mr = (m == -INFINITY) ? 0.f : m;
-      st.mr2 = st.mr * s2;
-      st.s = 0.f;
-    } else if (u >= 2 && u <= 5) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        st.s += __builtin_amdgcn_exp2f(fmaf(xv(4 * (u - 2) + q), s2, -st.mr2));
-    } else if (u == 6) {
-      // the sum is relative to mr2 = round(mr * s2): refer it to mr exactly
-      st.s *= __builtin_amdgcn_exp2f(-fmaf(st.mr, s2, -st.mr2));
-      float a0, a1, b0, b1;
-      xswap16(st.m, a0, a1);
-      xswap16(st.s, b0, b1);
-      ms_merge(a0, b0, a1, b1, s2, st.m, st.s);
-    } else if (u == 7) {
-      float a0, a1, b0, b1;
-      xswap32(st.m, a0, a1);
-      xswap32(st.s, b0, b1);
-      ms_merge(a0, b0, a1, b1, s2, st.m, st.s);
-    }
+  } else if (u >= 2 && u <= 5) {
+    const int j0 = 4 * (u - 2);
+    st.s0 += __builtin_amdgcn_exp2f(fmaf(xv(j0), s2, -st.m2));
+    st.s1 += __builtin_amdgcn_exp2f(fmaf(xv(j0 + 1), s2, -st.m2));
+    st.s0 += __builtin_amdgcn_exp2f(fmaf(xv(j0 + 2), s2, -st.m2));
+    st.s1 += __builtin_amdgcn_exp2f(fmaf(xv(j0 + 3), s2, -st.m2));
+  } else if (u == 6) {
+    st.s0 += st.s1;
+    merge_sample<16>(st);
+  } else if (u == 7) {
+    merge_sample<32>(st);
   }
 }
 
 // One pipelined tile step: the MFMA chain of the next tile (acc_next, already
 // seeded) interleaved k-step by k-step with the epilogue units of the current
 // tile (acc_cur).  B operands come through a three-deep register ring.
-template <int KT, bool GREEDY>
+template <int KT, bool GREEDY, bool MASK>
 __device__ __forceinline__ void mfma_with_epilogue(f32x4_t (&acc_next)[4], const bf16x8_t (&Af)[4][KT],
                                                    const uint4* erow, const f32x4_t (&acc_cur)[4],
-                                                   const bool (&uok)[2], float s2, int ubase,
+                                                   const bool (&uok)[2], float s2, int gbase,
                                                    EpiState& st) {
   constexpr int NU = 8;                     // epilogue units
   bf16x8_t Bq[3];
@@ -479,17 +433,17 @@ __device__ __forceinline__ void mfma_with_epilogue(f32x4_t (&acc_next)[4], const
     for (int mt = 0; mt < 4; ++mt)
       acc_next[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[mt][kt], Bq[kt % 3], acc_next[mt], 0, 0, 0);
 #pragma unroll
-    for (int u = kt * NU / KT; u < (kt + 1) * NU / KT; ++u) epi_unit<GREEDY>(u, st, acc_cur, uok, s2, ubase);
+    for (int u = kt * NU / KT; u < (kt + 1) * NU / KT; ++u) epi_unit<GREEDY, MASK>(u, st, acc_cur, uok, s2, gbase);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // The whole epilogue of a tile without MFMAs (last tile of a group).
-template <bool GREEDY>
+template <bool GREEDY, bool MASK>
 __device__ __forceinline__ void epilogue_all(EpiState& st, const f32x4_t (&acc)[4], const bool (&uok)[2],
-                                             float s2, int ubase) {
+                                             float s2, int gbase) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) epi_unit<GREEDY>(u, st, acc, uok, s2, ubase);
+  for (int u = 0; u < 8; ++u) epi_unit<GREEDY, MASK>(u, st, acc, uok, s2, gbase);
 }
 
 // Seed four 4-value accumulators with 16 bf16 values (two 16-byte pieces).
@@ -502,6 +456,89 @@ __device__ __forceinline__ void seed_acc(f32x4_t (&acc)[4], const uint4 (&un)[2]
       const int j = 8 * q + e;
       acc[j >> 2][j & 3] = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
     }
+  }
+}
+
+// Phase A of one wave for one row group: 16-row tiles, software-pipelined so
+// that while the MFMAs of tile i+1 run, the vector ALU works on the epilogue
+// of tile i.  U pieces are prefetched two tiles ahead through a per-lane
+// pointer (tiles past the last re-read it).  The statistics of every tile row
+// over the wave's 64 entries go to HS[row][wave] (rows past `rows`, in the
+// ragged last tile, are never read).
+template <int KT, int ROWP, bool GREEDY, bool MASK>
+__device__ __forceinline__ void slice_tiles(const bf16x8_t (&Af)[4][KT], const uint4* E, float2* HS,
+                                            const uint16_t* ustep, int64_t rstride, int row0, int rows,
+                                            int wslice, const bool (&uok)[2], float s2) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  const int ntiles = (rows + 15) / 16;
+  // the lane's two 8-entry pieces; a piece past V re-reads the row's entry 0.
+  // Addresses are a wave-uniform tile base plus a 32-bit lane offset (the
+  // caller guarantees 16 rows of U fit in 4 GiB); lanes past the last row of
+  // a ragged last tile re-read that row.
+  const int e0 = (!MASK || uok[0]) ? wslice + slice_entry(lg, 0) : 0;
+  // byte distance from the first piece to the second (negative when only the
+  // second piece lies past V and re-reads entry 0)
+  const int d1 = MASK ? 2 * ((uok[1] ? wslice + slice_entry(lg, 8) : 0) - e0) : 64;
+  const uint32_t voff = (uint32_t)(2 * ((int64_t)ln * rstride + e0));
+  const int lrow_last = min(16 * (ntiles - 1) + ln, rows - 1) - 16 * (ntiles - 1);
+  const uint32_t voff_last = (uint32_t)(2 * ((int64_t)lrow_last * rstride + e0));
+  const char* tbase = reinterpret_cast<const char*>(ustep + (int64_t)row0 * rstride);
+  const int64_t tstep = 32 * rstride;         // bytes per 16 rows
+  int tn = 0;                                 // next tile to load
+  auto load_u = [&](uint4 (&dst)[2]) __attribute__((always_inline)) {
+    const int t = min(tn, ntiles - 1);
+    const char* p = tbase + t * tstep + (t == ntiles - 1 ? voff_last : voff);
+    dst[0] = *reinterpret_cast<const uint4*>(p);
+    dst[1] = *reinterpret_cast<const uint4*>(p + d1);
+    ++tn;
+  };
+  // after the merges every lane of a row holds the row's statistics over the
+  // wave's 64 entries; lane group 0 stores them (HS[row][wave])
+  float2* hs = HS + ln * kPWaves + wv;
+  const int gbase = wslice + 8 * lg;
+  auto store = [&](int i, const EpiState& st) __attribute__((always_inline)) {
+    if (lg == 0) hs[16 * kPWaves * i] = make_float2(st.m, GREEDY ? __int_as_float(st.bi) : st.s0);
+  };
+  auto fresh = [&]() __attribute__((always_inline)) {
+    EpiState st;
+    st.m = -INFINITY; st.s0 = 0.f; st.s1 = 0.f; st.m2 = -FLT_MAX; st.bi = 0x7FFFFFFF;
+    return st;
+  };
+  // epilogue of tile i (acc_cur) with the MFMAs of tile i+1 (acc_next, seeded
+  // from un, which is then refilled with tile i+3)
+  auto step2 = [&](f32x4_t (&acc_cur)[4], f32x4_t (&acc_next)[4], uint4 (&un)[2], int i)
+      __attribute__((always_inline)) {
+    seed_acc(acc_next, un);
+    load_u(un);
+    EpiState st = fresh();
+    mfma_with_epilogue<KT, GREEDY, MASK>(acc_next, Af, E + (16 * (i + 1) + ln) * ROWP + lg, acc_cur, uok,
+                                         s2, gbase, st);
+    store(i, st);
+  };
+  auto last = [&](const f32x4_t (&acc)[4], int i) __attribute__((always_inline)) {
+    EpiState st = fresh();
+    epilogue_all<GREEDY, MASK>(st, acc, uok, s2, gbase);
+    store(i, st);
+  };
+  uint4 ua[2], ub[2];
+  f32x4_t accA[4], accB[4];
+  load_u(ua);                                 // tile 0
+  load_u(ub);                                 // tile 1
+  wait_vm_zero();
+  seed_acc(accA, ua);
+  load_u(ua);                                 // tile 2
+  tile_mfma<KT>(accA, Af, E + ln * ROWP + lg);
+  int i = 0;
+  for (; i + 2 < ntiles; i += 2) {
+    step2(accA, accB, ub, i);                 // epilogue i, MFMA i+1 (seeded from ub)
+    step2(accB, accA, ua, i + 1);             // epilogue i+1, MFMA i+2 (seeded from ua)
+  }
+  if (i + 1 < ntiles) {
+    step2(accA, accB, ub, i);
+    last(accB, i + 1);
+  } else {
+    last(accA, i);
   }
 }
 
@@ -695,18 +732,17 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   constexpr int ROWP = SEG + 1;             // padded LDS row: rows start 16 bytes apart in the
                                             // bank space, so the 16 lanes of a ds_read_b128
                                             // phase (16 rows, same segment) never collide
-  // LDS: the group's W1 rows; a union of the phase-A half-chunk statistics
-  // and the pick's staging; the group's tokens
-  constexpr int HS_BYTES = kPRows * kPWaves * 8, HI_BYTES = GREEDY ? kPRows * kPWaves * 4 : 0;
+  // LDS: the group's W1 rows; a union of the phase-A statistics per (row,
+  // wave) and the pick's staging; the group's tokens
+  constexpr int HS_BYTES = kPRows * kPWaves * 8;
   constexpr int PK_BYTES = kPMaxChunks * 8 + (GREEDY ? kPMaxChunks * 4 : 0) + SEG * 16;
-  constexpr int UA_BYTES = (HS_BYTES + HI_BYTES) > PK_BYTES ? (HS_BYTES + HI_BYTES) : PK_BYTES;
+  constexpr int UA_BYTES = HS_BYTES > PK_BYTES ? HS_BYTES : PK_BYTES;
   __shared__ uint4 E[kPRows * ROWP];
   __shared__ uint4 UA[UA_BYTES / 16];
   __shared__ int PV[kPRows];
   __shared__ BlockScratch sh;
   __shared__ PickRed pred[kPWaves];
   float2* HS = reinterpret_cast<float2*>(UA);                       // [row][wave]
-  int* HI = reinterpret_cast<int*>(reinterpret_cast<char*>(UA) + HS_BYTES);
   float2* Ls = reinterpret_cast<float2*>(UA);                       // pick: chunk statistics
   int* Is = reinterpret_cast<int*>(reinterpret_cast<char*>(UA) + kPMaxChunks * 8);
   uint4* Es = reinterpret_cast<uint4*>(reinterpret_cast<char*>(UA) + kPMaxChunks * 8 +
@@ -728,16 +764,12 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   constexpr int KT = KS / 2;                // k-steps of 32
   bf16x8_t Af[4][KT];
   load_w2_slice<KT>(Af, W2t, a.rank, wslice, V, wave_active);
-  // this lane's 16 entries: two 16-byte pieces of U
-  const int ln = lane & 15, lg = lane >> 4;
-  const int ubase = wslice + 16 * lg;
+  // this lane's 16 entries: two 8-entry pieces of U, inside V or not
+  const int lg = lane >> 4;
   bool uok[2];
-  int uoff[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    uok[q] = wave_active && ubase + 8 * q + 8 <= V;
-    uoff[q] = uok[q] ? ubase + 8 * q : 0;
-  }
+  for (int q = 0; q < 2; ++q) uok[q] = wave_active && wslice + slice_entry(lg, 8 * q) + 8 <= V;
+  const bool wave_full = wave_active && wslice + 64 <= V;
 
   uint32_t epoch = 0;
   const int ngroups = (R + kPRows - 1) / kPRows;
@@ -761,98 +793,42 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       wait_vm_zero();
       __syncthreads();
       if (wave_active) {
-        const int ntiles = (rows + 15) / 16;
         const uint16_t* ustep = U + (int64_t)(k - 1) * V;
         const int64_t rstride = (int64_t)a.gamma * V;
-        auto load_u = [&](uint4 (&dst)[2], int i) __attribute__((always_inline)) {
-          const int row = row0 + min(16 * i + ln, rows - 1);
-          const uint16_t* up = ustep + (int64_t)row * rstride;
-#pragma unroll
-          for (int q = 0; q < 2; ++q) dst[q] = *reinterpret_cast<const uint4*>(up + uoff[q]);
-        };
-        // Software-pipelined tiles: while the MFMAs of tile i+1 run, the
-        // vector ALU works on the epilogue of tile i (their instructions are
-        // interleaved by the scheduling groups below).  U slots: slot
-        // (i+1) % 2 seeds tile i+1 and is then refilled with tile i+3.
-        auto store_stats = [&](int i, float M, float S, int bi) __attribute__((always_inline)) {
-          const int rl = 16 * i + ln;
-          if (lg == 0 && rl < rows) {
-            HS[rl * kPWaves + wv] = make_float2(M, S);
-            if (GREEDY) HI[rl * kPWaves + wv] = bi;
-          }
-        };
-        auto fresh = [&]() __attribute__((always_inline)) {
-          EpiState st;
-          st.m = -INFINITY; st.s = 0.f; st.mr = 0.f; st.mr2 = 0.f; st.bi = 0x7FFFFFFF;
-          return st;
-        };
-        // one pipelined iteration: epilogue of tile i (acc_cur) with the MFMAs
-        // of tile i+1 (acc_next, seeded from `un`)
-        auto step2 = [&](f32x4_t (&acc_cur)[4], f32x4_t (&acc_next)[4], uint4 (&un)[2], int i)
-            __attribute__((always_inline)) {
-          seed_acc(acc_next, un);
-          load_u(un, min(i + 3, ntiles - 1));   // unconditional: same loads in flight on every path
-          const int rln = 16 * (i + 1) + ln;
-          EpiState st = fresh();
-          mfma_with_epilogue<KT, GREEDY>(acc_next, Af, E + rln * ROWP + lg, acc_cur, uok, s2, ubase, st);
-          store_stats(i, st.m, st.s, st.bi);
-        };
-        auto last = [&](const f32x4_t (&acc)[4], int i) __attribute__((always_inline)) {
-          EpiState st = fresh();
-          epilogue_all<GREEDY>(st, acc, uok, s2, ubase);
-          store_stats(i, st.m, st.s, st.bi);
-        };
-        uint4 ua[2], ub[2];
-        f32x4_t accA[4], accB[4];
-        load_u(ua, 0);
-        load_u(ub, min(1, ntiles - 1));
-        wait_vm_zero();
-        // tile 0 alone
-        seed_acc(accA, ua);
-        load_u(ua, min(2, ntiles - 1));
-        tile_mfma<KT>(accA, Af, E + ln * ROWP + lg);
-        int i = 0;
-        for (; i + 2 < ntiles; i += 2) {
-          step2(accA, accB, ub, i);       // epilogue i, MFMA i+1 (seeded from ub)
-          step2(accB, accA, ua, i + 1);   // epilogue i+1, MFMA i+2 (seeded from ua)
-        }
-        if (i + 1 < ntiles) {
-          step2(accA, accB, ub, i);
-          last(accB, i + 1);
-        } else {
-          last(accA, i);
-        }
+        if (wave_full)
+          slice_tiles<KT, ROWP, GREEDY, false>(Af, E, HS, ustep, rstride, row0, rows, wslice, uok, s2);
+        else
+          slice_tiles<KT, ROWP, GREEDY, true>(Af, E, HS, ustep, rstride, row0, rows, wslice, uok, s2);
       } else {
-        // no entries in this wave's slice: empty halves
-        for (int rl = lane; rl < rows; rl += 64) {
-          HS[rl * kPWaves + wv] = make_float2(-INFINITY, 0.f);
-          if (GREEDY) HI[rl * kPWaves + wv] = 0x7FFFFFFF;
-        }
+        // no entries in this wave's slice: empty statistics
+        const float2 empty = make_float2(-INFINITY, GREEDY ? __int_as_float(0x7FFFFFFF) : 0.f);
+        for (int rl = lane; rl < rows; rl += 64) HS[rl * kPWaves + wv] = empty;
       }
       __syncthreads();
-      // merge the two halves of each of the slice's four chunks and store
+      // merge the two halves (waves 2c, 2c+1) of each of the slice's four
+      // chunks and store the chunk statistics: S relative to the raw maximum
       if (slice_active) {
         for (int t = tid; t < rows * 4; t += kPThreads) {
           const int rl = t >> 2, c = t & 3;
           const int chunk = 4 * b + c;
           if (chunk >= a.nch) continue;
           const int row = row0 + rl;
-          const float2 s0 = HS[rl * kPWaves + 2 * c], s1 = HS[rl * kPWaves + 2 * c + 1];
+          const float2 h0 = HS[rl * kPWaves + 2 * c], h1 = HS[rl * kPWaves + 2 * c + 1];
           float2* Lo = const_cast<float2*>(a.L) + (int64_t)row * a.nch + chunk;
           if (GREEDY) {
-            float bv = s0.x;
-            int bi = HI[rl * kPWaves + 2 * c];
-            argmax_merge(bv, bi, s1.x, HI[rl * kPWaves + 2 * c + 1]);
+            float bv = h0.x;
+            int bi = __float_as_int(h0.y);
+            argmax_merge(bv, bi, h1.x, __float_as_int(h1.y));
             st_coh2(Lo, make_float2(bv, 0.f));
             st_coh(const_cast<int*>(a.I) + (int64_t)row * a.nch + chunk, bi);
             if (nonfinite(bv)) set_flag(a.status, kFlagNonFinite);
           } else {
-            const float Mn = fmaxf(s0.x, s1.x);
-            float St = 0.f;
-            if (Mn != -INFINITY) {
-              if (__float_as_uint(s0.y) != 0u) St += s0.y * __builtin_amdgcn_exp2f((s0.x - Mn) * s2);
-              if (__float_as_uint(s1.y) != 0u) St += s1.y * __builtin_amdgcn_exp2f((s1.x - Mn) * s2);
-            }
+            // half h holds S_h relative to scaled_ref(M_h): refer it to Mr s2
+            // exactly (one rounding)
+            const float Mn = fmaxf(h0.x, h1.x);
+            const float Mr = (Mn == -INFINITY) ? 0.f : Mn;
+            const float St = h0.y * __builtin_amdgcn_exp2f(fmaf(-Mr, s2, scaled_ref(h0.x, s2))) +
+                             h1.y * __builtin_amdgcn_exp2f(fmaf(-Mr, s2, scaled_ref(h1.x, s2)));
             st_coh2(Lo, make_float2(Mn, St));
             if (nonfinite(St) || Mn == INFINITY) set_flag(a.status, kFlagNonFinite);
           }
@@ -908,13 +884,13 @@ void k_resid_stats(ResidArgs A) {
   bf16x8_t Af[4][KT];
   load_w2_slice<KT>(Af, A.W2t, A.rank, wslice, V, wave_active);
   const int ln = lane & 15, lg = lane >> 4;
-  const int ubase = wslice + 16 * lg;
   bool uok[2];
-  int uoff[2];
+  int uoff[2];                              // value j of the lane: entry uoff[j >> 3] + (j & 7)
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    uok[q] = wave_active && ubase + 8 * q + 8 <= V;
-    uoff[q] = uok[q] ? ubase + 8 * q : 0;
+    const int e = wslice + slice_entry(lg, 8 * q);
+    uok[q] = wave_active && e + 8 <= V;
+    uoff[q] = uok[q] ? e : 0;
   }
   const float s2 = A.scale2, invT = s2 * kLn2;
   for (int row0 = 0; row0 < nrows; row0 += kPRows) {
@@ -1047,13 +1023,15 @@ static hipError_t launch_persist_ks(PersistArgs& P, int grid, hipStream_t st) {
 
 // The persistent schedule takes bf16 U and weights, rank 64/128/256, rows and
 // weight tables 16-byte aligned, V a multiple of 8 with at most 512 entries per
-// compute unit.  DSPARK_DRAFT_KERNEL=steps in the environment selects the
-// per-step schedule for every shape.
-static int persistent_grid(int V, int rank, bool u_bf16, bool w_bf16, bool u_vec, const void* W1,
-                           const void* W2t, bool greedy) {
+// compute unit, and 16 request rows of U (16 gamma V entries) within 2 GiB (the
+// U loads use 32-bit lane offsets).  DSPARK_DRAFT_KERNEL=steps in the
+// environment selects the per-step schedule for every shape.
+static int persistent_grid(int gamma, int V, int rank, bool u_bf16, bool w_bf16, bool u_vec,
+                           const void* W1, const void* W2t, bool greedy) {
   const char* env = std::getenv("DSPARK_DRAFT_KERNEL");
   if (env && std::strcmp(env, "steps") == 0) return 0;
   if (!u_bf16 || !w_bf16 || !u_vec || (V % 8) != 0) return 0;
+  if ((int64_t)32 * gamma * V >= ((int64_t)1 << 31)) return 0;
   if (rank != 64 && rank != 128 && rank != 256) return 0;
   if ((reinterpret_cast<uintptr_t>(W1) & 15) || (reinterpret_cast<uintptr_t>(W2t) & 15)) return 0;
   int dev = 0;
@@ -1100,7 +1078,7 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
   p.U = U; p.W1 = W1; p.W2t = W2t; p.x0 = x0; p.x = x; p.logp_d = logp_d; p.lse_d = lse_d;
   p.margin = margin; p.L = Lc; p.I = Ic; p.status = status;
 
-  const int grid = persistent_grid(V, rank, u_bf16, w_bf16, u_vec, W1, W2t, greedy);
+  const int grid = persistent_grid(gamma, V, rank, u_bf16, w_bf16, u_vec, W1, W2t, greedy);
   if (grid > 0) {
     PersistArgs P{};
     P.p = p;
