@@ -59,7 +59,22 @@ __device__ __forceinline__ float log_uniform(uint32_t y) {
   return log1pf(-fmaf((float)(~y), 0x1p-32f, 0x1p-33f));
 }
 
-__device__ __forceinline__ float gumbel_of(uint32_t y) { return -logf(-log_uniform(y)); }
+// Standard Gumbel -ln(-ln u), u = (y + 1/2) 2^-32, from the hardware base-2
+// logarithm (v_log_f32, about one ulp) instead of the library logf/log1pf.
+// For u >= 1/2, -ln u = -log1p(x) with x = u - 1 taken exactly from y, and
+// log1p(x) = ln(1 + x) x / ((1 + x) - 1) (Goldberg's formula: the rounding of
+// 1 + x cancels), so small |x| keeps its relative accuracy.  Branch-free: both
+// halves are evaluated and one is selected.
+__device__ __forceinline__ float gumbel_of(uint32_t y) {
+  const float ulo = fmaf((float)y, 0x1p-32f, 0x1p-33f);            // u, for y < 2^31
+  const float nlo = -__builtin_amdgcn_logf(ulo) * kLn2;
+  const float x = -fmaf((float)(~y), 0x1p-32f, 0x1p-33f);          // u - 1, for y >= 2^31
+  const float u1 = 1.f + x;
+  const float r = __builtin_amdgcn_logf(u1) * kLn2 * __builtin_amdgcn_rcpf(u1 - 1.f);
+  const float nhi = (u1 == 1.f) ? -x : -(r * x);
+  const float nl = (y < 0x80000000u) ? nlo : nhi;                   // -ln u > 0
+  return -__builtin_amdgcn_logf(nl) * kLn2;
+}
 
 // ------------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -187,26 +187,41 @@ __device__ __forceinline__ void st_coh2(float2* p, float2 v) {
 // the launch returns at once, so the kernel always runs to its end.
 constexpr int kMaxGrid = 1024;              // flag words in the workspace
 
-__device__ __forceinline__ void grid_barrier(uint32_t* flags, uint32_t epoch, uint32_t spin_limit,
-                                             uint32_t* status) {
+// Arrival: every wave's memory operations are complete (the workgroup
+// barrier waits for them), then the workgroup's flag is raised.
+__device__ __forceinline__ void grid_arrive(uint32_t* flags, uint32_t epoch) {
   __syncthreads();
   if (threadIdx.x == 0)
     __hip_atomic_store(flags + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const bool broken =
+}
+// Wait until every workgroup has arrived at barrier `epoch` (bounded).  Every
+// decision to stop waiting is taken from a workgroup-barrier reduction, so all
+// waves of the workgroup take it together (a wave that left early would pair
+// its later barriers with the wrong ones of the others).
+__device__ __forceinline__ void grid_wait(uint32_t* flags, uint32_t epoch, uint32_t spin_limit,
+                                          uint32_t* status) {
+  // a barrier of this launch already gave up: do not wait
+  const int brk = threadIdx.x == 0 &&
       (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kFlagBarrier) != 0;
-  if (broken) return;
-  for (uint32_t spins = 0;; ++spins) {
-    int ok = 1;
-    for (uint32_t t = threadIdx.x; t < gridDim.x; t += blockDim.x)
-      ok &= __hip_atomic_load(flags + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= epoch;
-    if (__syncthreads_and(ok)) break;
-    if (spins + 1 >= spin_limit) {
-      if (threadIdx.x == 0) atomicOr(status, kFlagBarrier);
-      break;
+  if (!__syncthreads_or(brk)) {
+    for (uint32_t spins = 0;; ++spins) {
+      int ok = 1;
+      for (uint32_t t = threadIdx.x; t < gridDim.x; t += blockDim.x)
+        ok &= __hip_atomic_load(flags + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= epoch;
+      if (__syncthreads_and(ok)) break;
+      if (spins + 1 >= spin_limit) {
+        if (threadIdx.x == 0) atomicOr(status, kFlagBarrier);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
     }
-    __builtin_amdgcn_s_sleep(1);
   }
   __syncthreads();
+}
+__device__ __forceinline__ void grid_barrier(uint32_t* flags, uint32_t epoch, uint32_t spin_limit,
+                                             uint32_t* status) {
+  grid_arrive(flags, epoch);
+  grid_wait(flags, epoch, spin_limit, status);
 }
 
 // s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt fields at their
@@ -542,70 +557,149 @@ __device__ __forceinline__ void slice_tiles(const bf16x8_t (&Af)[4][KT], const u
   }
 }
 
+// Wave-wide reductions on the VALU alone: DPP steps inside rows of 16 lanes,
+// then the xor-16 and xor-32 swaps; every lane ends with the result, and each
+// combine is symmetric, so all lanes hold the same bits.
+__device__ __forceinline__ float wave_max_v(float v) {
+  v = row16_max(v);
+  float a, b;
+  xswap<16>(v, a, b);
+  v = fmaxf(a, b);
+  xswap<32>(v, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float wave_sum_v(float v) {
+  v = row16_sum(v);
+  float a, b;
+  xswap<16>(v, a, b);
+  v = a + b;
+  xswap<32>(v, a, b);
+  return a + b;
+}
+template <int X>
+__device__ __forceinline__ void argmax_swap(float& v, int& i) {
+  float v0, v1;
+  int i0, i1;
+  xswap<X>(v, v0, v1);
+  iswap<X>(i, i0, i1);
+  argmax_merge(v0, i0, v1, i1);
+  v = v0;
+  i = i0;
+}
+__device__ __forceinline__ void wave_argmax_v(float& v, int& i) {
+  row16_argmax(v, i);
+  argmax_swap<16>(v, i);
+  argmax_swap<32>(v, i);
+}
+
 // (key, index) argmax with the lower index winning ties, and a sum.
 struct PickRed {
   float key;
   int idx;
   float s;
 };
-// Reduction of PickRed over the 512 threads (every thread gets the result;
-// the sum is taken in a fixed order).
-__device__ __forceinline__ PickRed block_pick_reduce(PickRed v, PickRed* lds) {
+// Block-wide reductions over the 512 threads: wave results go through LDS
+// slots owned by one reduction each (so no barrier is needed before the
+// stores) and are combined in wave order.
+__device__ __forceinline__ float block_max_v(float v, float* slot) {
+  v = wave_max_v(v);
+  if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = slot[0];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    argmax_merge(v.key, v.idx, __shfl_xor(v.key, o), __shfl_xor(v.idx, o));
-    v.s += __shfl_xor(v.s, o);
-  }
+  for (int q = 1; q < kPWaves; ++q) r = fmaxf(r, slot[q]);
+  return r;
+}
+__device__ __forceinline__ PickRed block_pick_reduce(PickRed v, PickRed* slot) {
+  wave_argmax_v(v.key, v.idx);
+  v.s = wave_sum_v(v.s);
+  if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = v;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
-  __syncthreads();
-  PickRed r = lds[0];
+  PickRed r = slot[0];
 #pragma unroll
   for (int q = 1; q < kPWaves; ++q) {
-    argmax_merge(r.key, r.idx, lds[q].key, lds[q].idx);
-    r.s += lds[q].s;
+    argmax_merge(r.key, r.idx, slot[q].key, slot[q].idx);
+    r.s += slot[q].s;
   }
   return r;
 }
+__device__ __forceinline__ void block_argmax_v(float& v, int& idx, float* fslot, int* islot) {
+  wave_argmax_v(v, idx);
+  if ((threadIdx.x & 63) == 0) { fslot[threadIdx.x >> 6] = v; islot[threadIdx.x >> 6] = idx; }
+  __syncthreads();
+  v = fslot[0];
+  idx = islot[0];
+#pragma unroll
+  for (int q = 1; q < kPWaves; ++q) argmax_merge(v, idx, fslot[q], islot[q]);
+}
+
+// Gumbel noise of the chunk-level draw for request i at step k: thread t owns
+// chunks 4t..4t+3 (one Philox block).  Independent of the data, so it is
+// computed while the chunk statistics are being loaded.
+__device__ __forceinline__ void chunk_noise(const DraftPickArgs& a, int i, int k, float (&g)[4]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) g[w] = 0.f;
+  if (a.nch > 1 && 4 * t < a.nch) {
+    const uint4 blk = stream_block(a.seed, a.round, kTagDraftChunk, (uint32_t)i, (uint32_t)k, (uint32_t)t);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) g[w] = gumbel_of(word_of(blk, (uint32_t)w));
+  }
+}
+
+// LDS of the persistent pick: reduction slots and the W1 row of x_{k-1}.
+template <int SEG>
+struct PickLds {
+  float fmax[kPWaves];
+  float farg[kPWaves];
+  int iarg[kPWaves];
+  PickRed red[kPWaves];
+  uint4 E[SEG];
+};
 
 // Pick of step a.k for request i by the 512-thread workgroup of the persistent
-// launch.  The row's chunk statistics and W1[x_{k-1}] are first staged in LDS.
-// Sampling: after the row maximum, one reduction gives both the chunk-level
-// Gumbel winner and the row normaliser; the chosen chunk's 128 scores
-// are rebuilt by four threads per entry (all W2t loads issued at once), and the
-// thread holding the in-chunk winner writes the outputs.
+// launch.  Thread t keeps the statistics of chunks 4t..4t+3 in registers.
+// Sampling: the row maximum m, then one reduction gives both the chunk-level
+// Gumbel winner of (M_c - m)/T + ln S_c + G_c and the normaliser
+// sum_c S_c exp((M_c - m)/T); the chosen chunk's 128 scores are rebuilt by
+// four threads per entry (all W2t loads issued at once, the entry noise
+// computed while they are in flight), and the thread holding the in-chunk
+// winner writes the outputs.
 template <int KS, bool GREEDY>
-__device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, BlockScratch& sh,
-                                           float2* Ls, int* Is, uint4* Es, PickRed* red) {
+__device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, float s2, BlockScratch& sh,
+                                           PickLds<2 * KS>& pl) {
   constexpr int NT = kPThreads, TPE = NT / kChunk;
   constexpr int SEG = 2 * KS, NQ = SEG / TPE;   // 16-byte pieces of the rank per thread
+  static_assert(kPMaxChunks <= 4 * NT, "four chunks per thread");
   const int tid = threadIdx.x;
   const int k = a.k;
   const int64_t xo = (int64_t)i * (a.gamma + 1);
   int prev = (k == 1) ? a.x0[i] : ld_coh(a.x + xo + k - 1);
   if (prev < 0 || prev >= a.V) prev = 0;        // flagged when phase A read it
   const float2* Lr = a.L + (int64_t)i * a.nch;
-  static_assert(kPMaxChunks <= 2 * NT, "two staged chunks per thread");
-  {
-    // both loads of a thread in flight before the LDS stores
-    const int c0 = tid, c1 = tid + NT;
-    float2 l0 = make_float2(0.f, 0.f), l1 = l0;
-    int i0 = 0, i1 = 0;
-    if (c0 < a.nch) { l0 = ld_coh2(Lr + c0); if (GREEDY) i0 = ld_coh(a.I + (int64_t)i * a.nch + c0); }
-    if (c1 < a.nch) { l1 = ld_coh2(Lr + c1); if (GREEDY) i1 = ld_coh(a.I + (int64_t)i * a.nch + c1); }
-    if (c0 < a.nch) { Ls[c0] = l0; if (GREEDY) Is[c0] = i0; }
-    if (c1 < a.nch) { Ls[c1] = l1; if (GREEDY) Is[c1] = i1; }
+  // chunk statistics of this thread's four chunks (all loads in flight)
+  float2 Lv[4];
+  int Iv[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int c = 4 * tid + w;
+    Lv[w] = make_float2(-INFINITY, 0.f);
+    Iv[w] = 0x7FFFFFFF;
+    if (c < a.nch) {
+      Lv[w] = ld_coh2(Lr + c);
+      if (GREEDY) Iv[w] = ld_coh(a.I + (int64_t)i * a.nch + c);
+    }
   }
   if (!GREEDY && tid < SEG)
-    Es[tid] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.W1) +
-                                              (int64_t)prev * a.rank + 8 * tid);
-  __syncthreads();
+    pl.E[tid] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.W1) +
+                                                (int64_t)prev * a.rank + 8 * tid);
   const int64_t o = (int64_t)i * a.gamma + (k - 1);
   if (GREEDY) {
     float v = -INFINITY;
     int idx = 0x7FFFFFFF;
-    for (int c = tid; c < a.nch; c += NT) argmax_merge(v, idx, Ls[c].x, Is[c]);
-    block_argmax<NT>(v, idx, sh);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) argmax_merge(v, idx, Lv[w].x, Iv[w]);
+    block_argmax_v(v, idx, pl.farg, pl.iarg);
     int xk = idx;
     if (xk < 0 || xk >= a.V) { set_flag(a.status, kFlagNonFinite); xk = 0; }
     if (tid == 0) {
@@ -616,71 +710,51 @@ __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, BlockS
       if (a.margin) a.margin[o] = INFINITY;
     }
   } else {
+    // the chunk noise while the statistics are in flight
+    float g[4];
+    chunk_noise(a, i, k, g);
     // scores are kept relative to the raw row maximum m (accuracy at low T)
-    float mloc = -INFINITY;
-    for (int c = tid; c < a.nch; c += NT) mloc = fmaxf(mloc, Ls[c].x);
-    const float m = block_max<NT>(mloc, sh);
-    // chunk level: thread t owns chunks 4t..4t+3 (one Philox block); one
-    // reduction gives the Gumbel winner of (M_c - m)/T + log S_c + G_c and
-    // the normaliser sum_c S_c exp((M_c - m)/T)
-    const bool draw = a.nch > 1;
+    float mloc = fmaxf(fmaxf(Lv[0].x, Lv[1].x), fmaxf(Lv[2].x, Lv[3].x));
+    const float m = block_max_v(mloc, pl.fmax);
     PickRed pr{-INFINITY, 0x7FFFFFFF, 0.f};
-    if (4 * tid < a.nch) {
-      uint4 blk = make_uint4(0, 0, 0, 0);
-      if (draw) blk = stream_block(a.seed, a.round, kTagDraftChunk, (uint32_t)i, (uint32_t)k, (uint32_t)tid);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int c = 4 * tid + w;
-        if (c < a.nch) {
-          const float2 v = Ls[c];
-          if (v.y > 0.f) {
-            const float rel = (v.x - m) * a.invT;
-            pr.s += v.y * expf(rel);
-            const float key = rel + logf(v.y) + (draw ? gumbel_of(word_of(blk, (uint32_t)w)) : 0.f);
-            argmax_merge(pr.key, pr.idx, key, c);
-          }
-        }
+    for (int w = 0; w < 4; ++w) {
+      const float2 v = Lv[w];
+      if (v.y > 0.f) {
+        pr.s += v.y * __builtin_amdgcn_exp2f((v.x - m) * s2);
+        const float key = (v.x - m) * a.invT + __builtin_amdgcn_logf(v.y) * kLn2 + g[w];
+        argmax_merge(pr.key, pr.idx, key, 4 * tid + w);
       }
     }
-    const PickRed rr = block_pick_reduce(pr, red);
+    const PickRed rr = block_pick_reduce(pr, pl.red);
     const float lse_rel = logf(rr.s);
     const float lse = m * a.invT + lse_rel;
     int c = rr.key == -INFINITY ? -1 : rr.idx;
     if (c < 0) { if (tid == 0) set_flag(a.status, kFlagNonFinite); c = 0; }
-    const bool want_gap = a.margin != nullptr;
-    float cgap = INFINITY;
-    if (want_gap && draw) {
-      // second-best chunk key (debug output only)
-      float second = -INFINITY;
-      if (4 * tid < a.nch) {
-        const uint4 blk = stream_block(a.seed, a.round, kTagDraftChunk, (uint32_t)i, (uint32_t)k, (uint32_t)tid);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int cc = 4 * tid + w;
-          if (cc < a.nch && cc != c) {
-            const float2 v = Ls[cc];
-            if (v.y > 0.f)
-              second = fmaxf(second, (v.x - m) * a.invT + logf(v.y) + gumbel_of(word_of(blk, (uint32_t)w)));
-          }
-        }
-      }
-      cgap = rr.key - block_max<NT>(second, sh);
-    }
     // in-chunk: entry base + tid / TPE, part tid % TPE of the rank
     const int base = c * kChunk;
     const int v = base + tid / TPE, h = tid % TPE;
     const bool in = v < a.V;
-    float bsum = 0.f, u = 0.f;
+    uint4 wq[NQ];
+    float u = 0.f;
     if (in) {
       const uint4* wr = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.W2t) +
                                                        (int64_t)v * a.rank) + h * NQ;
-      uint4 wq[NQ];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) wq[q] = wr[q];
       u = bf16_at(reinterpret_cast<const uint16_t*>(a.U), ((int64_t)i * a.gamma + (k - 1)) * a.V + v);
+    }
+    // the entry's noise while the loads are in flight
+    float gel = 0.f;
+    if (h == 0 && in) {
+      const uint4 blk = stream_block(a.seed, a.round, kTagDraftElem, (uint32_t)i, (uint32_t)k, (uint32_t)v >> 2);
+      gel = gumbel_of(word_of(blk, (uint32_t)v & 3u));
+    }
+    float bsum = 0.f;
+    if (in) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        const uint4 x = Es[h * NQ + q];
+        const uint4 x = pl.E[h * NQ + q];
         const uint4 w = wq[q];
         bsum = fmaf(bf16_lo(x.x), bf16_lo(w.x), bsum);
         bsum = fmaf(bf16_hi(x.x), bf16_hi(w.x), bsum);
@@ -692,22 +766,36 @@ __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, BlockS
         bsum = fmaf(bf16_hi(x.w), bf16_hi(w.w), bsum);
       }
     }
-#pragma unroll
-    for (int oo = 1; oo < TPE; oo *= 2) bsum += __shfl_xor(bsum, oo);
+    static_assert(TPE == 4, "four threads per entry");
+    bsum += dpp_f<kDppXor1>(bsum);
+    bsum += dpp_f<kDppXor2>(bsum);
     const float sv = in ? (u + bsum - m) * a.invT : -INFINITY;   // score of entry v, minus m/T
     float key = -INFINITY;
     int kid = 0x7FFFFFFF;
     if (h == 0 && in) {
-      const uint4 blk = stream_block(a.seed, a.round, kTagDraftElem, (uint32_t)i, (uint32_t)k, (uint32_t)v >> 2);
-      key = sv + gumbel_of(word_of(blk, (uint32_t)v & 3u));
+      key = sv + gel;
       kid = v;
     }
     float best = key;
     int bidx = kid;
-    block_argmax<NT>(best, bidx, sh);
+    block_argmax_v(best, bidx, pl.farg, pl.iarg);
     int xk = best == -INFINITY ? -1 : bidx;
-    float egap = INFINITY;
-    if (want_gap && xk >= 0) egap = best - block_max<NT>(kid == xk ? -INFINITY : key, sh);
+    float gap = INFINITY;
+    if (a.margin != nullptr) {
+      // second-best keys (debug output only)
+      float second = -INFINITY;
+      if (a.nch > 1) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float2 lv = Lv[w];
+          if (4 * tid + w != c && lv.y > 0.f)
+            second = fmaxf(second, (lv.x - m) * a.invT + __builtin_amdgcn_logf(lv.y) * kLn2 + g[w]);
+        }
+      }
+      const float cgap = (a.nch > 1) ? rr.key - block_max<NT>(second, sh) : INFINITY;
+      const float egap = (xk >= 0) ? best - block_max<NT>(kid == xk ? -INFINITY : key, sh) : INFINITY;
+      gap = fminf(cgap, egap);
+    }
     if (xk < 0) {
       if (tid == 0) set_flag(a.status, kFlagNonFinite);
       xk = base;
@@ -718,11 +806,11 @@ __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, BlockS
       st_coh(a.x + xo + k, xk);
       a.logp_d[o] = sv - lse_rel;
       a.lse_d[o] = lse;
-      if (a.margin) a.margin[o] = fminf(cgap, egap);
+      if (a.margin) a.margin[o] = gap;
     }
   }
   wait_vm_zero();
-  __syncthreads();                          // LDS staging and sh are reused
+  __syncthreads();                          // LDS slots and the W1 row are reused
 }
 
 template <int KS, bool GREEDY>
@@ -732,21 +820,13 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   constexpr int ROWP = SEG + 1;             // padded LDS row: rows start 16 bytes apart in the
                                             // bank space, so the 16 lanes of a ds_read_b128
                                             // phase (16 rows, same segment) never collide
-  // LDS: the group's W1 rows; a union of the phase-A statistics per (row,
-  // wave) and the pick's staging; the group's tokens
-  constexpr int HS_BYTES = kPRows * kPWaves * 8;
-  constexpr int PK_BYTES = kPMaxChunks * 8 + (GREEDY ? kPMaxChunks * 4 : 0) + SEG * 16;
-  constexpr int UA_BYTES = HS_BYTES > PK_BYTES ? HS_BYTES : PK_BYTES;
+  // LDS: the group's W1 rows, the phase-A statistics per (row, wave), the
+  // group's tokens and the pick's slots
   __shared__ uint4 E[kPRows * ROWP];
-  __shared__ uint4 UA[UA_BYTES / 16];
+  __shared__ float2 HS[kPRows * kPWaves];   // [row][wave]
   __shared__ int PV[kPRows];
   __shared__ BlockScratch sh;
-  __shared__ PickRed pred[kPWaves];
-  float2* HS = reinterpret_cast<float2*>(UA);                       // [row][wave]
-  float2* Ls = reinterpret_cast<float2*>(UA);                       // pick: chunk statistics
-  int* Is = reinterpret_cast<int*>(reinterpret_cast<char*>(UA) + kPMaxChunks * 8);
-  uint4* Es = reinterpret_cast<uint4*>(reinterpret_cast<char*>(UA) + kPMaxChunks * 8 +
-                                       (GREEDY ? kPMaxChunks * 4 : 0));
+  __shared__ PickLds<SEG> pl;
 
   DraftPickArgs a = P.p;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -838,7 +918,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     }
     grid_barrier(P.bar, ++epoch, P.spin_limit, a.status);
     // ================= phase B: the pick of step k, one request per workgroup
-    for (int i = b; i < R; i += gridDim.x) pick_row_p<KS, GREEDY>(a, i, sh, Ls, Is, Es, pred);
+    for (int i = b; i < R; i += gridDim.x) pick_row_p<KS, GREEDY>(a, i, s2, sh, pl);
     if (k < a.gamma) grid_barrier(P.bar, ++epoch, P.spin_limit, a.status);
   }
 }
