@@ -6,9 +6,10 @@ scheduler on.
 Prints ONE JSON line.  `value` = verified draft tokens per second
 (sum of scheduled lengths ell over the timed rounds / their wall time), inputs
 resident in HBM before the timed region.  The `roofline` object covers the
-dominant kernel (the per-step Markov statistics kernel of the draft), timed
-live with HIP events recorded on the launch stream around each of its
-launches.  `cpu_baseline` is the single-threaded CPU oracle on a bounded
+dominant kernel (the persistent draft kernel: all gamma steps in one
+cooperative launch; the per-step statistics kernel when the shape takes the
+per-step schedule), timed live with HIP events recorded on the launch stream
+around each of its launches.  `cpu_baseline` is the single-threaded CPU oracle on a bounded
 sample of requests of the same workload, scaled to a full round.
 """
 from __future__ import annotations
