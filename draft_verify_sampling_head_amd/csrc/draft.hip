@@ -224,6 +224,25 @@ __device__ __forceinline__ void grid_barrier(uint32_t* flags, uint32_t epoch, ui
   grid_wait(flags, epoch, spin_limit, status);
 }
 
+// Token written by another workgroup's pick in this launch: x is -1 until
+// then (set before the launch).  Polled with relaxed device-scope loads; the
+// wait is bounded like the grid barrier's (past spin_limit polls, or once a
+// wait of this launch has given up, it returns -1 and kFlagBarrier is set).
+__device__ __forceinline__ int wait_token(const int* p, uint32_t spin_limit, uint32_t* status) {
+  int v = __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (v >= 0) return v;
+  if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kFlagBarrier) return -1;
+  for (uint32_t spins = 1;; ++spins) {
+    __builtin_amdgcn_s_sleep(1);
+    v = __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v >= 0) return v;
+    if (spins >= spin_limit) {
+      atomicOr(status, kFlagBarrier);
+      return -1;
+    }
+  }
+}
+
 // s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt fields at their
 // maxima).  Placed where no useful load is in flight, it clears the
 // compiler's record of possibly pending loads, which otherwise merges across
@@ -474,40 +493,53 @@ __device__ __forceinline__ void seed_acc(f32x4_t (&acc)[4], const uint4 (&un)[2]
   }
 }
 
+// U pieces of one wave for one row group, tile by tile.  The lane's two 8-entry
+// pieces (a piece past V re-reads the row's entry 0) are addressed as a
+// wave-uniform tile base plus a 32-bit lane offset (16 rows of U fit in 2 GiB,
+// checked on the host); lanes past the last row of a ragged last tile re-read
+// that row.
+struct UStream {
+  const char* tbase;
+  int64_t tstep;                              // bytes per 16 rows
+  uint32_t v0, v1, l0, l1;                    // lane offsets: full tiles, last tile
+  int ntiles;
+  __device__ __forceinline__ void init(const uint16_t* ustep, int64_t rstride, int row0, int rows,
+                                       int wslice, const bool (&uok)[2], bool full) {
+    const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
+    ntiles = (rows + 15) / 16;
+    const int e0 = (full || uok[0]) ? wslice + slice_entry(lg, 0) : 0;
+    const int e1 = (full || uok[1]) ? wslice + slice_entry(lg, 8) : 0;
+    const int lrow_last = min(16 * (ntiles - 1) + ln, rows - 1) - 16 * (ntiles - 1);
+    v0 = (uint32_t)(2 * ((int64_t)ln * rstride + e0));
+    v1 = (uint32_t)(2 * ((int64_t)ln * rstride + e1));
+    l0 = (uint32_t)(2 * ((int64_t)lrow_last * rstride + e0));
+    l1 = (uint32_t)(2 * ((int64_t)lrow_last * rstride + e1));
+    tbase = reinterpret_cast<const char*>(ustep + (int64_t)row0 * rstride);
+    tstep = 32 * rstride;
+  }
+  // tile i (past the last tile: the last one); i is wave-uniform
+  __device__ __forceinline__ void load(uint4 (&dst)[2], int i) const {
+    const int t = min(i, ntiles - 1);
+    const bool last = t == ntiles - 1;
+    const char* p = tbase + t * tstep;
+    dst[0] = *reinterpret_cast<const uint4*>(p + (last ? l0 : v0));
+    dst[1] = *reinterpret_cast<const uint4*>(p + (last ? l1 : v1));
+  }
+};
+
 // Phase A of one wave for one row group: 16-row tiles, software-pipelined so
 // that while the MFMAs of tile i+1 run, the vector ALU works on the epilogue
-// of tile i.  U pieces are prefetched two tiles ahead through a per-lane
-// pointer (tiles past the last re-read it).  The statistics of every tile row
-// over the wave's 64 entries go to HS[row][wave] (rows past `rows`, in the
-// ragged last tile, are never read).
+// of tile i.  U is prefetched two tiles ahead; the caller has already issued
+// the loads of tiles 0 and 1 (ua, ub) and waited for them.  The statistics of
+// every tile row over the wave's 64 entries go to HS[row][wave] (rows past
+// `rows`, in the ragged last tile, are never read).
 template <int KT, int ROWP, bool GREEDY, bool MASK>
 __device__ __forceinline__ void slice_tiles(const bf16x8_t (&Af)[4][KT], const uint4* E, float2* HS,
-                                            const uint16_t* ustep, int64_t rstride, int row0, int rows,
-                                            int wslice, const bool (&uok)[2], float s2) {
+                                            const UStream& us, uint4 (&ua)[2], uint4 (&ub)[2], int wslice,
+                                            const bool (&uok)[2], float s2) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int ln = lane & 15, lg = lane >> 4;
-  const int ntiles = (rows + 15) / 16;
-  // the lane's two 8-entry pieces; a piece past V re-reads the row's entry 0.
-  // Addresses are a wave-uniform tile base plus a 32-bit lane offset (the
-  // caller guarantees 16 rows of U fit in 4 GiB); lanes past the last row of
-  // a ragged last tile re-read that row.
-  const int e0 = (!MASK || uok[0]) ? wslice + slice_entry(lg, 0) : 0;
-  // byte distance from the first piece to the second (negative when only the
-  // second piece lies past V and re-reads entry 0)
-  const int d1 = MASK ? 2 * ((uok[1] ? wslice + slice_entry(lg, 8) : 0) - e0) : 64;
-  const uint32_t voff = (uint32_t)(2 * ((int64_t)ln * rstride + e0));
-  const int lrow_last = min(16 * (ntiles - 1) + ln, rows - 1) - 16 * (ntiles - 1);
-  const uint32_t voff_last = (uint32_t)(2 * ((int64_t)lrow_last * rstride + e0));
-  const char* tbase = reinterpret_cast<const char*>(ustep + (int64_t)row0 * rstride);
-  const int64_t tstep = 32 * rstride;         // bytes per 16 rows
-  int tn = 0;                                 // next tile to load
-  auto load_u = [&](uint4 (&dst)[2]) __attribute__((always_inline)) {
-    const int t = min(tn, ntiles - 1);
-    const char* p = tbase + t * tstep + (t == ntiles - 1 ? voff_last : voff);
-    dst[0] = *reinterpret_cast<const uint4*>(p);
-    dst[1] = *reinterpret_cast<const uint4*>(p + d1);
-    ++tn;
-  };
+  const int ntiles = us.ntiles;
   // after the merges every lane of a row holds the row's statistics over the
   // wave's 64 entries; lane group 0 stores them (HS[row][wave])
   float2* hs = HS + ln * kPWaves + wv;
@@ -525,7 +557,7 @@ __device__ __forceinline__ void slice_tiles(const bf16x8_t (&Af)[4][KT], const u
   auto step2 = [&](f32x4_t (&acc_cur)[4], f32x4_t (&acc_next)[4], uint4 (&un)[2], int i)
       __attribute__((always_inline)) {
     seed_acc(acc_next, un);
-    load_u(un);
+    us.load(un, i + 3);
     EpiState st = fresh();
     mfma_with_epilogue<KT, GREEDY, MASK>(acc_next, Af, E + (16 * (i + 1) + ln) * ROWP + lg, acc_cur, uok,
                                          s2, gbase, st);
@@ -536,13 +568,9 @@ __device__ __forceinline__ void slice_tiles(const bf16x8_t (&Af)[4][KT], const u
     epilogue_all<GREEDY, MASK>(st, acc, uok, s2, gbase);
     store(i, st);
   };
-  uint4 ua[2], ub[2];
   f32x4_t accA[4], accB[4];
-  load_u(ua);                                 // tile 0
-  load_u(ub);                                 // tile 1
-  wait_vm_zero();
-  seed_acc(accA, ua);
-  load_u(ua);                                 // tile 2
+  seed_acc(accA, ua);                         // tile 0
+  us.load(ua, 2);
   tile_mfma<KT>(accA, Af, E + ln * ROWP + lg);
   int i = 0;
   for (; i + 2 < ntiles; i += 2) {
@@ -859,12 +887,26 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     for (int g = 0; g < ngroups; ++g) {
       const int row0 = g * kPRows;
       const int rows = min(kPRows, R - row0);
+      // U of the group's first two tiles does not depend on the tokens: its
+      // loads are in flight while the tokens and W1 rows arrive
+      UStream us;
+      us.init(U + (int64_t)(k - 1) * V, (int64_t)a.gamma * V, row0, rows, wslice, uok, wave_full);
+      uint4 ua[2], ub[2];
+      if (wave_active) {
+        us.load(ua, 0);
+        us.load(ub, 1);
+      }
       if (slice_active) {
-        // tokens x_{k-1} of the group (staged in LDS), then their W1 rows
+        // tokens x_{k-1} of the group (staged in LDS), then their W1 rows.
+        // x_{k-1} is written by the picks of step k-1: waiting for each
+        // token to appear is the only synchronisation with them
         for (int rl = tid; rl < rows; rl += kPThreads) {
           const int row = row0 + rl;
-          int prev = (k == 1) ? a.x0[row] : ld_coh(a.x + (int64_t)row * (a.gamma + 1) + (k - 1));
-          if (prev < 0 || prev >= V) { set_flag(a.status, kFlagBadToken); prev = 0; }
+          int prev = (k == 1) ? a.x0[row]
+                              : wait_token(a.x + (int64_t)row * (a.gamma + 1) + (k - 1), P.spin_limit,
+                                           a.status);
+          if (prev >= V || (k == 1 && prev < 0)) set_flag(a.status, kFlagBadToken);
+          if (prev < 0 || prev >= V) prev = 0;
           PV[rl] = prev;
         }
         __syncthreads();
@@ -873,12 +915,10 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       wait_vm_zero();
       __syncthreads();
       if (wave_active) {
-        const uint16_t* ustep = U + (int64_t)(k - 1) * V;
-        const int64_t rstride = (int64_t)a.gamma * V;
         if (wave_full)
-          slice_tiles<KT, ROWP, GREEDY, false>(Af, E, HS, ustep, rstride, row0, rows, wslice, uok, s2);
+          slice_tiles<KT, ROWP, GREEDY, false>(Af, E, HS, us, ua, ub, wslice, uok, s2);
         else
-          slice_tiles<KT, ROWP, GREEDY, true>(Af, E, HS, ustep, rstride, row0, rows, wslice, uok, s2);
+          slice_tiles<KT, ROWP, GREEDY, true>(Af, E, HS, us, ua, ub, wslice, uok, s2);
       } else {
         // no entries in this wave's slice: empty statistics
         const float2 empty = make_float2(-INFINITY, GREEDY ? __int_as_float(0x7FFFFFFF) : 0.f);
@@ -917,9 +957,11 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       __syncthreads();                      // E, PV and HS are rewritten by the next group
     }
     grid_barrier(P.bar, ++epoch, P.spin_limit, a.status);
-    // ================= phase B: the pick of step k, one request per workgroup
+    // ================= phase B: the pick of step k, one request per workgroup.
+    // No barrier follows: phase A of step k+1 waits for the tokens it reads,
+    // and a token is written after its pick has read the chunk statistics
+    // that phase A of step k+1 overwrites.
     for (int i = b; i < R; i += gridDim.x) pick_row_p<KS, GREEDY>(a, i, s2, sh, pl);
-    if (k < a.gamma) grid_barrier(P.bar, ++epoch, P.spin_limit, a.status);
   }
 }
 
@@ -1136,6 +1178,20 @@ __global__ void k_zero_words(uint32_t* p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
 }
 
+// Before the persistent launch: barrier flags to zero, drafted positions
+// x[i][1..gamma] to -1 (not yet written), x[i][0] to the anchor.
+__global__ void k_draft_prep(uint32_t* flags, int nflags, int32_t* x, const int32_t* x0, int R, int gamma) {
+  const int t0 = blockIdx.x * blockDim.x + threadIdx.x, nt = gridDim.x * blockDim.x;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nflags; i += blockDim.x) flags[i] = 0u;
+  const int64_t n = (int64_t)R * (gamma + 1);
+  for (int64_t q = t0; q < n; q += nt) {
+    const int64_t i = q / (gamma + 1);
+    const int j = (int)(q - i * (gamma + 1));
+    x[q] = (j == 0) ? x0[i] : -1;
+  }
+}
+
 hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,
                         const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
                         const int32_t* x0, int32_t* x, float* logp_d, float* lse_d, float* margin,
@@ -1168,7 +1224,9 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     const char* sl = std::getenv("DSPARK_BARRIER_SPINS");
     P.spin_limit = sl ? (uint32_t)std::strtoul(sl, nullptr, 10) : kBarrierSpins;
     if (P.spin_limit == 0) P.spin_limit = 1;
-    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, st, P.bar, kMaxGrid);
+    const int prep_blocks = (int)std::min<int64_t>(64, ((int64_t)R * (gamma + 1) + 255) / 256);
+    hipLaunchKernelGGL(k_draft_prep, dim3(prep_blocks), dim3(256), 0, st, P.bar, kMaxGrid, x, x0, R,
+                       gamma);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev_begin && (e = hipEventRecord(ev_begin[0], st)) != hipSuccess) return e;
