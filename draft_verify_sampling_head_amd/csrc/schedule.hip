@@ -4,12 +4,16 @@
 // Algorithm 1).  Survival a_{r,j} = prod_{i<=j} c_{r,i} is a left-to-right
 // float32 running product per request.  Candidates (r, j) with a > 0 are
 // ordered by a descending, then r, then j ascending -- a total order -- by
-// sorting 64-bit keys (~bits(a) << 32 | r*32 + j-1) with a bitonic network
-// (1024 threads, each holding a run of consecutive positions in registers:
-// only the exchanges wider than a wave's span go through LDS).  Admitting the
-// q first candidates gives B = R + q and
-// tau_q = R + sum of their a; in 2^-32 fixed point the sums are exact, so a
-// block-wide prefix sum yields every tau_q at once, and
+// sorting 64-bit keys (~bits(a) << 32 | r*32 + j-1).  Since c <= 1 makes a
+// non-increasing in j, each request's keys are already an ascending run: the
+// sort is a bottom-up merge of the R runs (merge path: each thread finds its
+// output range by a binary search and merges it from LDS, keeping the result
+// in registers).  Runs that are not ascending (some c outside [0, 1]) and
+// shapes whose padded runs do not fit take a bitonic network instead (1024
+// threads holding runs of keys in registers; only exchanges wider than a
+// wave's span go through LDS).  Admitting the q first candidates gives
+// B = R + q and tau_q = R + sum of their a; in 2^-32 fixed point the sums are
+// exact, so a block-wide prefix sum yields every tau_q at once, and
 // Theta_q = (tau_q * 2^-32) * SPS(B) is one double product (0 past N_max).
 // The sequential rule "admit while Theta improves, stop at the first
 // non-improvement" admits exactly the candidates before the first q with
@@ -133,36 +137,97 @@ __device__ __forceinline__ void bitonic_sort_regs(uint64_t (&v)[EPT], uint64_t* 
   }
 }
 
+// Bottom-up merge of the ascending runs of length run0 (a power of two) in
+// keys[0, P); thread t ends with the sorted positions [t EPT, t EPT + EPT) in
+// v.  Per level, thread t's output range lies inside one pair of runs
+// (2 run >= EPT): a binary search over the merge path finds how many of its
+// first outputs come from the left run, then EPT steps merge from LDS (ties
+// take the left run).  The outputs are written back after a barrier.
 template <int EPT>
-__device__ __forceinline__ void schedule_body(const SchedArgs& a, uint64_t* keys, int64_t* red64, int* red32) {
+__device__ __forceinline__ void merge_sort_runs(uint64_t (&v)[EPT], uint64_t* keys, int P, int run0) {
+  const int o0 = threadIdx.x * EPT;
+  if (run0 >= P) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) v[e] = keys[o0 + e];
+    return;
+  }
+  for (int run = run0; run < P; run *= 2) {
+    const int base = o0 & ~(2 * run - 1);
+    const int d = o0 - base;
+    const uint64_t* A = keys + base;
+    const uint64_t* B = keys + base + run;
+    int lo = max(0, d - run), hi = min(d, run);
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (A[mid] <= B[d - mid - 1]) lo = mid + 1;
+      else hi = mid;
+    }
+    int i = lo, j = d - lo;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const uint64_t x = (i < run) ? A[i] : ~0ull;
+      const uint64_t y = (j < run) ? B[j] : ~0ull;
+      const bool ta = (j >= run) || (i < run && x <= y);
+      v[e] = ta ? x : y;
+      i += ta ? 1 : 0;
+      j += ta ? 0 : 1;
+    }
+    __syncthreads();
+    if (2 * run < P) {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) keys[o0 + e] = v[e];
+      __syncthreads();
+    }
+  }
+}
+
+template <int EPT>
+__device__ __forceinline__ void schedule_body(const SchedArgs& a, int G2, uint64_t* keys, int64_t* red64,
+                                              int* red32) {
   const int tid = threadIdx.x;
   const int R = a.R, G = a.gamma;
-  const int n = R * G;
   const int P = kSchedThreads * EPT;
+  // G2 > 0: request r's keys sit at r*G2 + j (runs padded to G2, a power of
+  // two); G2 == 0: packed at r*G + j (bitonic only)
+  const int stride = G2 > 0 ? G2 : G;
 
-  // survival products (left to right, float32) and sort keys; the G
-  // confidences of a request are loaded together
+  // survival products (left to right, float32) and sort keys
   int64_t part = 0;
+  int unsorted = 0;
+  const bool vec4 = (G % 4) == 0 && (reinterpret_cast<uintptr_t>(a.c) & 15) == 0;
   for (int r = tid; r < R; r += kSchedThreads) {
     const float* cr = a.c + (int64_t)r * G;
     float cv[32];
+    if (vec4) {
 #pragma unroll
-    for (int j = 0; j < 32; ++j) cv[j] = (j < G) ? cr[j] : 0.f;
+      for (int q = 0; q < 8; ++q) {
+        const float4 f = (4 * q < G) ? reinterpret_cast<const float4*>(cr)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        cv[4 * q] = f.x; cv[4 * q + 1] = f.y; cv[4 * q + 2] = f.z; cv[4 * q + 3] = f.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) cv[j] = (j < G) ? cr[j] : 0.f;
+    }
     float acc = 1.f;
+    uint64_t prevkey = 0;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       if (j < G) {
         acc = __fmul_rn(acc, cv[j]);
         if (a.a) a.a[(int64_t)r * G + j] = acc;
-        keys[r * G + j] = (acc > 0.f)
+        const uint64_t key = (acc > 0.f)
             ? ((uint64_t)(0xFFFFFFFFu - __float_as_uint(acc)) << 32) | (uint32_t)(r * 32 + j)
             : ~0ull;
+        unsorted |= key < prevkey;
+        prevkey = key;
+        keys[r * stride + j] = key;
         part += fixed32(acc);
       }
     }
+    for (int j = G; j < stride; ++j) keys[r * stride + j] = ~0ull;
   }
-  for (int q = n + tid; q < P; q += kSchedThreads) keys[q] = ~0ull;
-  __syncthreads();
+  for (int q = R * stride + tid; q < P; q += kSchedThreads) keys[q] = ~0ull;
+  unsorted = __syncthreads_or(unsorted);
 
   if (!a.enabled) {
     const int64_t tau = ((int64_t)R << 32) + block_sum_i64(part, red64);
@@ -177,10 +242,15 @@ __device__ __forceinline__ void schedule_body(const SchedArgs& a, uint64_t* keys
 
   // sort ascending: a descending, then r, then j
   uint64_t v[EPT];
+  if (G2 > 0 && !unsorted) {
+    merge_sort_runs<EPT>(v, keys, P, G2);
+  } else {
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) v[e] = keys[tid * EPT + e];
-  __syncthreads();
-  bitonic_sort_regs<EPT>(v, keys, P);
+    for (int e = 0; e < EPT; ++e) v[e] = keys[tid * EPT + e];
+    __syncthreads();
+    bitonic_sort_regs<EPT>(v, keys, P);
+  }
+  __syncthreads();                            // keys is reused below
 
   // fixed-point prefix sums over the sorted order; thread t owns positions
   // [t*EPT, t*EPT + EPT)
@@ -210,8 +280,10 @@ __device__ __forceinline__ void schedule_body(const SchedArgs& a, uint64_t* keys
   int admitted = block_min_i(first_stop, red32);
   if (admitted > E) admitted = E;
 
-  for (int r = tid; r < R; r += kSchedThreads) a.ell[r] = 0;
-  __threadfence();
+  // ell_r = largest admitted position of request r, by LDS atomics in the
+  // (now free) key buffer, then written out
+  int* ell_l = reinterpret_cast<int*>(keys);
+  for (int r = tid; r < R; r += kSchedThreads) ell_l[r] = 0;
   __syncthreads();
   int64_t mine = 0;
 #pragma unroll
@@ -219,13 +291,14 @@ __device__ __forceinline__ void schedule_body(const SchedArgs& a, uint64_t* keys
     const int p = p0 + e;
     if (p < admitted) {
       const uint32_t lo = (uint32_t)v[e];
-      atomicMax(&a.ell[lo >> 5], (int)(lo & 31u) + 1);
+      atomicMax(&ell_l[lo >> 5], (int)(lo & 31u) + 1);
       mine += fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(v[e] >> 32)));
     }
   }
   if (tid == 0 && a.N_out) *a.N_out = R + admitted;
   // Theta of the admitted prefix (exact integer sum)
-  const int64_t tau_adm = ((int64_t)R << 32) + block_sum_i64(mine, red64);
+  const int64_t tau_adm = ((int64_t)R << 32) + block_sum_i64(mine, red64);   // (has barriers)
+  for (int r = tid; r < R; r += kSchedThreads) a.ell[r] = ell_l[r];
   if (tid == 0 && a.theta) *a.theta = theta_of(tau_adm, R + admitted, a.N_max, a.sps);
 }
 
@@ -233,12 +306,16 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(SchedArgs a) {
   __shared__ uint64_t keys[kSchedMaxKeys];
   __shared__ int64_t red64[kSchedThreads / 64];
   __shared__ int red32[kSchedThreads / 64];
-  const int n = a.R * a.gamma;
-  if (n <= kSchedThreads) schedule_body<1>(a, keys, red64, red32);
-  else if (n <= 2 * kSchedThreads) schedule_body<2>(a, keys, red64, red32);
-  else if (n <= 4 * kSchedThreads) schedule_body<4>(a, keys, red64, red32);
-  else if (n <= 8 * kSchedThreads) schedule_body<8>(a, keys, red64, red32);
-  else schedule_body<16>(a, keys, red64, red32);
+  // runs padded to a power of two when they fit, else packed keys
+  int G2 = 1;
+  while (G2 < a.gamma) G2 *= 2;
+  int n = a.R * G2;
+  if (n > kSchedMaxKeys) { G2 = 0; n = a.R * a.gamma; }
+  if (n <= kSchedThreads) schedule_body<1>(a, G2, keys, red64, red32);
+  else if (n <= 2 * kSchedThreads) schedule_body<2>(a, G2, keys, red64, red32);
+  else if (n <= 4 * kSchedThreads) schedule_body<4>(a, G2, keys, red64, red32);
+  else if (n <= 8 * kSchedThreads) schedule_body<8>(a, G2, keys, red64, red32);
+  else schedule_body<16>(a, G2, keys, red64, red32);
 }
 
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t st) {

@@ -273,6 +273,12 @@ def test_scheduler_stress_size():
     c2 = rng.uniform(0.97, 1.0, (1024, 16)).astype(np.float32)
     B = np.arange(1024 * 17 + 1, dtype=np.float64)
     _sched_case(c2, 1.0 / (0.020 + 5e-6 * B))
+    # runs padded to 32 positions would exceed the key buffer: packed keys and
+    # the bitonic network instead of the run merge
+    for R, g in [(600, 17), (900, 17)]:
+        c3 = rng.uniform(0.6, 1.0, (R, g)).astype(np.float32)
+        B = np.arange(R * (g + 1) + 1, dtype=np.float64)
+        _sched_case(c3, 1.0 / (0.020 + 5e-5 * B))
 
 
 # ------------------------------------------------------------- stage: pack
