@@ -180,16 +180,26 @@ __device__ __forceinline__ void st_coh2(float2* p, float2 v) {
 // workgroups, as a flag array: workgroup b stores `epoch` in its own word
 // flags[b] and polls all gridDim.x words until every one has reached `epoch`.
 // No word takes more than one store per barrier, so nothing serialises on a
-// shared counter.  The workgroup barrier first completes every wave's memory
-// operations (it waits for vmcnt 0); flags are written and read with relaxed
+// shared counter.  Before the flag store every wave waits for its own memory
+// operations to complete; flags are written and read with relaxed
 // device-scope atomics.  The wait is bounded: past spin_limit polls the
 // workgroup sets kFlagBarrier and stops waiting, and every later barrier of
 // the launch returns at once, so the kernel always runs to its end.
 constexpr int kMaxGrid = 1024;              // flag words in the workspace
 
-// Arrival: every wave's memory operations are complete (the workgroup
-// barrier waits for them), then the workgroup's flag is raised.
+// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt fields at their
+// maxima).  Placed where no useful load is in flight, it clears the
+// compiler's record of possibly pending loads, which otherwise merges across
+// the step loop into a full wait at the first LDS store of every tile.
+__device__ __forceinline__ void wait_vm_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Arrival: every wave first waits until its own stores have completed (the
+// workgroup barrier alone does not wait for them), then the workgroup barrier,
+// then the workgroup's flag is raised.  The data the flag publishes is
+// written with device-coherent stores, so completion makes it visible to
+// every workgroup that later sees the flag.
 __device__ __forceinline__ void grid_arrive(uint32_t* flags, uint32_t epoch) {
+  wait_vm_zero();
   __syncthreads();
   if (threadIdx.x == 0)
     __hip_atomic_store(flags + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -243,11 +253,6 @@ __device__ __forceinline__ int wait_token(const int* p, uint32_t spin_limit, uin
   }
 }
 
-// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt fields at their
-// maxima).  Placed where no useful load is in flight, it clears the
-// compiler's record of possibly pending loads, which otherwise merges across
-// the step loop into a full wait at the first LDS store of every tile.
-__device__ __forceinline__ void wait_vm_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // One direct-to-LDS load per lane: 16 bytes from gptr to lds_wave_base + 16 *
 // lane (global_load_lds_dwordx4; M0 holds the wave's LDS base).  Issued from
