@@ -27,16 +27,35 @@ struct RowNorm {
   float lse_rel;  // log sum_c S_c exp((M_c - m)/T)   (normaliser = m/T + lse_rel)
 };
 
+// One wave; the chunk statistics are read 16 per lane at a time, all loads of
+// a batch in flight together.
 __device__ inline RowNorm row_norm(const float2* st, int nch, float invT) {
+  constexpr int B = 16;
   const int lane = threadIdx.x & 63;
   float m = -INFINITY;
-  for (int c = lane; c < nch; c += 64) m = fmaxf(m, st[c].x);
+  for (int c0 = 0; c0 < nch; c0 += 64 * B) {
+    float x[B];
+#pragma unroll
+    for (int t = 0; t < B; ++t) {
+      const int c = c0 + lane + 64 * t;
+      x[t] = c < nch ? st[c].x : -INFINITY;
+    }
+#pragma unroll
+    for (int t = 0; t < B; ++t) m = fmaxf(m, x[t]);
+  }
   m = wave_max(m);
   if (m == -INFINITY) return RowNorm{-INFINITY, -INFINITY};
   float s = 0.f;
-  for (int c = lane; c < nch; c += 64) {
-    const float2 v = st[c];
-    if (v.y > 0.f) s += v.y * expf((v.x - m) * invT);
+  for (int c0 = 0; c0 < nch; c0 += 64 * B) {
+    float2 v[B];
+#pragma unroll
+    for (int t = 0; t < B; ++t) {
+      const int c = c0 + lane + 64 * t;
+      v[t] = c < nch ? st[c] : make_float2(-INFINITY, 0.f);
+    }
+#pragma unroll
+    for (int t = 0; t < B; ++t)
+      if (v[t].y > 0.f) s += v[t].y * expf((v[t].x - m) * invT);
   }
   s = wave_sum(s);
   return RowNorm{m, s > 0.f ? logf(s) : -INFINITY};
@@ -122,10 +141,22 @@ __device__ inline PickResult pick_in_chunk(float s0, float s1, int base, uint64_
 
 // Lowest-index argmax over per-chunk maxima (st[c].x) / argmaxes I (greedy).
 __device__ inline void argmax_chunks(const float2* st, const int* I, int nch, float& v, int& idx) {
+  constexpr int B = 16;
   const int lane = threadIdx.x & 63;
   v = -INFINITY;
   idx = 0x7FFFFFFF;
-  for (int c = lane; c < nch; c += 64) argmax_merge(v, idx, st[c].x, I[c]);
+  for (int c0 = 0; c0 < nch; c0 += 64 * B) {
+    float x[B];
+    int ix[B];
+#pragma unroll
+    for (int t = 0; t < B; ++t) {
+      const int c = c0 + lane + 64 * t;
+      x[t] = c < nch ? st[c].x : -INFINITY;
+      ix[t] = c < nch ? I[c] : 0x7FFFFFFF;
+    }
+#pragma unroll
+    for (int t = 0; t < B; ++t) argmax_merge(v, idx, x[t], ix[t]);
+  }
   wave_argmax(v, idx);
 }
 

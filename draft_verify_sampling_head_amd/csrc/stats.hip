@@ -63,41 +63,60 @@ __device__ __forceinline__ void chunk_argmax(float& v, int& i) {
   if (LPC == 32) argmax_merge(v, i, __shfl_xor(v, 16), __shfl_xor(i, 16));
 }
 
-// One wave: chunks [c0, c1) of one row.
+// One wave: chunks [c0, c1) of one row.  UNR 16-byte loads per lane are in
+// flight at once; the data stays as raw words until it is used.
 template <typename T, bool GREEDY>
 __device__ __forceinline__ void row_segment(const T* row, int V, int c0, int c1, float scale2,
                                             bool vec_ok, float2* L, int* I, uint32_t* status) {
   constexpr int VPL = 16 / sizeof(T);       // values per lane per 16-byte load
   constexpr int LPC = kChunk / VPL;         // lanes per chunk
   constexpr int CPI = 64 / LPC;             // chunks per wave-wide load
-  constexpr int UNR = 4;                    // loads in flight per lane
+  constexpr int UNR = 8;                    // loads in flight per lane
   const int lane = threadIdx.x & 63;
   const int sub = lane % LPC;
   const int cl = lane / LPC;
   for (int cb = c0; cb < c1; cb += CPI * UNR) {
-    float x[UNR][VPL];
+    uint4 raw[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int c = cb + u * CPI + cl;
       const int v0 = c * kChunk + sub * VPL;
       if (c < c1 && vec_ok && v0 + VPL <= V) {
-        load_vec<T>(row + v0, x[u]);
+        raw[u] = *reinterpret_cast<const uint4*>(row + v0);
       } else {
+        // ragged tail: element loads, -inf past the segment or the vocabulary
+        uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < VPL; ++e)
-          x[u][e] = (c < c1 && v0 + e < V) ? Elem<T>::get(row, v0 + e) : -INFINITY;
+        for (int q = 0; q < 4; ++q) {
+          if (sizeof(T) == 2) {
+            const uint32_t lo = (c < c1 && v0 + 2 * q < V) ? reinterpret_cast<const uint16_t*>(row)[v0 + 2 * q] : 0xFF80u;
+            const uint32_t hi = (c < c1 && v0 + 2 * q + 1 < V) ? reinterpret_cast<const uint16_t*>(row)[v0 + 2 * q + 1] : 0xFF80u;
+            w[q] = lo | (hi << 16);
+          } else {
+            w[q] = (c < c1 && v0 + q < V) ? __float_as_uint(reinterpret_cast<const float*>(row)[v0 + q])
+                                          : __float_as_uint(-INFINITY);
+          }
+        }
+        raw[u] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int c = cb + u * CPI + cl;
       const int v0 = c * kChunk + sub * VPL;
+      float x[VPL];
+      {
+        const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+        for (int e = 0; e < VPL; ++e)
+          x[e] = (sizeof(T) == 2) ? ((e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1])) : __uint_as_float(w[e]);
+      }
       if (GREEDY) {
         float bv = -INFINITY;
         int bi = 0x7FFFFFFF;
 #pragma unroll
         for (int e = 0; e < VPL; ++e)
-          if (x[u][e] > bv) { bv = x[u][e]; bi = v0 + e; }
+          if (x[e] > bv) { bv = x[e]; bi = v0 + e; }
         chunk_argmax<LPC>(bv, bi);
         if (sub == 0 && c < c1) {
           L[c] = make_float2(bv, 0.f);
@@ -107,12 +126,12 @@ __device__ __forceinline__ void row_segment(const T* row, int V, int c0, int c1,
       } else {
         float m = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < VPL; ++e) m = fmaxf(m, x[u][e]);
+        for (int e = 0; e < VPL; ++e) m = fmaxf(m, x[e]);
         m = chunk_max<LPC>(m);
         float s = 0.f;
         if (m != -INFINITY) {
 #pragma unroll
-          for (int e = 0; e < VPL; ++e) s += __builtin_amdgcn_exp2f((x[u][e] - m) * scale2);
+          for (int e = 0; e < VPL; ++e) s += __builtin_amdgcn_exp2f((x[e] - m) * scale2);
         }
         s = chunk_sum<LPC>(s);
         if (sub == 0 && c < c1) {
@@ -1002,7 +1021,7 @@ hipError_t launch_row_stats(const RowStatsArgs& a0, bool bf16, bool greedy, hipS
   RowStatsArgs a = a0;
   const int vpl = bf16 ? 8 : 4;
   (void)vpl;
-  a.cps = 16;
+  a.cps = 32;
   a.segs = (a.nch + a.cps - 1) / a.cps;
   const int grid = grid_for((int64_t)a.nrows_cap * a.segs);
   if (bf16) {
