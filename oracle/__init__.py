@@ -60,6 +60,8 @@ def lib():
         L.orc_confidence.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.orc_prefix_schedule.argtypes = [i32, i32, P, P, i32, i32, i32, P, P, P, P, P]
         L.orc_prefix_schedule.restype = i32
+        L.orc_async_schedule.argtypes = [i32, i32, P, P, i32, i32, P, P, P, P, P, P]
+        L.orc_async_schedule.restype = i32
         L.orc_pack.argtypes = [i32, i32, P, P, P, P, P, P, P]
         L.orc_verify.argtypes = [i32, i32, i64, i32, f64, u64, u64, P, P, P, i32, P, P, P,
                                  P, P, P, P, P, P, P, P, P, P, P]
@@ -186,6 +188,27 @@ def prefix_schedule(c, sps, N_max=None, enabled=True, mode=0):
                                    int(mode), _p(ell), _p(a), _p(N), _p(th), _p(mg))
     assert rc == 0, rc
     return ell, a, int(N[0]), float(th[0]), float(mg[0])
+
+
+def async_schedule(c, sps, K_in, N_max=None):
+    """Production asynchronous scheduler: admit the K_in - R best candidates of
+    this round, plan the capacity of the round two rounds later.
+    Returns (ell, a, N, theta_admitted, K_plan, theta_plan)."""
+    c = _f32(c)
+    R, gamma = c.shape
+    sps = _f64(sps)
+    if N_max is None:
+        N_max = sps.size - 1
+    ell = np.zeros(R, np.int32)
+    a = np.zeros((R, gamma), np.float32)
+    N = np.zeros(1, np.int32)
+    th = np.zeros(1)
+    K = np.zeros(1, np.int32)
+    thp = np.zeros(1)
+    rc = lib().orc_async_schedule(R, gamma, _p(c), _p(sps), int(N_max), int(K_in), _p(ell), _p(a),
+                                  _p(N), _p(th), _p(K), _p(thp))
+    assert rc == 0, rc
+    return ell, a, int(N[0]), float(th[0]), int(K[0]), float(thp[0])
 
 
 def pack(rows, lens):

@@ -430,6 +430,82 @@ int orc_prefix_schedule(int R, int gamma, const float* c, const double* sps, int
     return 0;
 }
 
+// ------------------------------------------------ asynchronous scheduler ---
+// The scheduler as deployed in production ([P3] Supplementary details, the
+// hardware-aware prefix scheduler in production; [P1] 4.2.5 and 8.5).  Two
+// decisions per round, both on the candidate order of Algorithm 1 (a
+// descending, then r, then j ascending; a > 0 only):
+//  * admission: the verify batch holds at most K_in tokens, a capacity that
+//    was planned two rounds earlier.  The R anchors are always verified, so
+//    the min(K_in, N_max) - R best candidates of THIS round are admitted
+//    (dynamic top-K; clamped to [0, |E|]); Theta is not consulted.
+//  * planning: over THIS round's sorted candidates, the prefix length q* that
+//    maximises Theta_q = tau_q * SPS(R + q), q = 0..|E| (global search, no
+//    early stop; the first maximum wins; Theta = 0 past N_max), gives the
+//    capacity K_plan = R + q* that a round two rounds later admits with.
+// Reading: the capacity is counted in verify tokens, anchors included (the
+// pages call it the batch capacity); it is handed over as that token count.
+// tau and Theta are computed as in Algorithm 1 (2^-32 fixed point, one double
+// product).
+// Out: ell [R]; a [R][gamma] (nullable); N = sum(1 + ell); Theta of the
+//      admitted schedule; K_plan; Theta_{q*}.
+int orc_async_schedule(int R, int gamma, const float* c, const double* sps, int N_max, int K_in,
+                       int32_t* ell, float* a_out, int32_t* N_out, double* theta,
+                       int32_t* K_plan, double* theta_plan) {
+    if (R < 0 || gamma < 1 || N_max < R) return 1;
+    std::vector<float> a((size_t)R * gamma);
+    for (int r = 0; r < R; ++r) {
+        float acc = 1.0f;
+        for (int j = 1; j <= gamma; ++j) {
+            acc = acc * c[(int64_t)r * gamma + (j - 1)];   // float32 product
+            a[(size_t)r * gamma + (j - 1)] = acc;
+        }
+    }
+    if (a_out) std::memcpy(a_out, a.data(), a.size() * sizeof(float));
+    struct Cand { float a; int r; int j; };
+    std::vector<Cand> E;
+    for (int r = 0; r < R; ++r)
+        for (int j = 1; j <= gamma; ++j) {
+            const float av = a[(size_t)r * gamma + (j - 1)];
+            if (av > 0.0f) E.push_back({av, r, j});
+        }
+    std::sort(E.begin(), E.end(), [](const Cand& p, const Cand& q) {
+        if (p.a != q.a) return p.a > q.a;
+        if (p.r != q.r) return p.r < q.r;
+        return p.j < q.j;
+    });
+    auto fix = [](float av) -> int64_t { return (int64_t)std::llrint((double)av * 0x1p32); };
+    auto theta_of = [&](int64_t tau_fx, int64_t B) -> double {
+        if (B > N_max) return 0.0;
+        return ((double)tau_fx * 0x1p-32) * sps[B];
+    };
+    // tau_q for every prefix length q = 0..|E|
+    std::vector<int64_t> tau(E.size() + 1);
+    tau[0] = (int64_t)R << 32;
+    for (size_t q = 0; q < E.size(); ++q) tau[q + 1] = tau[q] + fix(E[q].a);
+
+    // admission: the best K_in - R candidates
+    const int64_t cap = std::min<int64_t>(K_in, N_max);
+    const int64_t take = std::max<int64_t>(0, std::min<int64_t>(cap - R, (int64_t)E.size()));
+    for (int r = 0; r < R; ++r) ell[r] = 0;
+    for (int64_t q = 0; q < take; ++q) ell[E[q].r] = std::max(ell[E[q].r], E[q].j);
+    int64_t N = 0;
+    for (int r = 0; r < R; ++r) N += 1 + ell[r];
+    if (N_out) *N_out = (int32_t)N;
+    if (theta) *theta = theta_of(tau[take], R + take);
+
+    // planning: global search over all prefix lengths
+    size_t qbest = 0;
+    double best = theta_of(tau[0], R);
+    for (size_t q = 1; q <= E.size(); ++q) {
+        const double th = theta_of(tau[q], R + (int64_t)q);
+        if (th > best) { best = th; qbest = q; }
+    }
+    if (K_plan) *K_plan = R + (int32_t)qbest;
+    if (theta_plan) *theta_plan = best;
+    return 0;
+}
+
 // ----------------------------------------------------------------- pack ---
 // Ragged pack ([P3] Supplementary details, variable-length routing; [P4] 3.3):
 // all requests' tokens flattened as independent elements with an offset array

@@ -436,6 +436,155 @@ def test_scheduler_invariants_and_disabled():
     assert N_c <= R + 10
 
 
+# ------------------------------------------------- asynchronous scheduler --
+def _survival_f32(c):
+    R, g = c.shape
+    a = np.ones((R, g), np.float32)
+    for r in range(R):
+        acc = np.float32(1.0)
+        for j in range(g):
+            acc = np.float32(acc * np.float32(c[r, j]))
+            a[r, j] = acc
+    return a
+
+
+def _theta_exact(a, ell, sps, n_max):
+    """Theta of an arbitrary prefix schedule ell, as an exact rational (the
+    2^-32 fixed-point amounts of a, no ordering involved)."""
+    R = a.shape[0]
+    B = R + int(sum(ell))
+    if B > n_max:
+        return Fraction(0)
+    tau = Fraction(R)
+    for r in range(R):
+        for j in range(int(ell[r])):
+            tau += Fraction(int(np.rint(np.float64(a[r, j]) * 2.0**32)), 2**32)
+    return tau * Fraction(sps[B])
+
+
+def test_async_appendix_a_plan():
+    # Appendix A: the capacity plan is the global search of that example.
+    gold = json.load(open(os.path.join(HERE, "golden", "appendix_a.json")))
+    sps = np.array(gold["sps"])
+    for case in gold["cases"]:
+        c = np.array([[gold["c1"], case["c2"]]], np.float32)
+        for K_in in range(0, 5):
+            ell, _, N, th, K, thp = O.async_schedule(c, sps, K_in)
+            assert K == 1 + case["ell_global"]
+            assert abs(thp - max(case["theta0"], case["theta1"], case["theta2"])) < 1e-6
+            npos = 2 if case["a2"] > 0 else 1
+            assert int(ell.sum()) == max(0, min(min(K_in, 3) - 1, npos))
+            assert N == 1 + int(ell.sum())
+    # c2 = 0.9 with the capacity planned on the same round admits ell = 2, which
+    # the early stop of Algorithm 1 never reaches (it stops at Theta_1 < Theta_0)
+    c = np.array([[gold["c1"], 0.9]], np.float32)
+    K = O.async_schedule(c, sps, 0)[4]
+    assert O.async_schedule(c, sps, K)[0][0] == 2
+    assert O.prefix_schedule(c, sps, mode=0)[0][0] == 0
+
+
+@pytest.mark.parametrize("R,g", [(1, 3), (2, 2), (2, 3), (3, 2), (3, 3)])
+def test_async_plan_is_optimum_over_all_prefix_schedules(R, g):
+    """The planned capacity is the best verify batch over EVERY per-request
+    prefix schedule (not only sorted prefixes): for a fixed batch size the
+    largest tau takes the largest survivals, and monotone a keeps them a
+    prefix.  Brute force over all (g+1)^R schedules, no sort involved."""
+    import itertools
+    rng = np.random.default_rng(100 * R + g)
+    n_max = R * (g + 1)
+    for it in range(150):
+        c = rng.uniform(0, 1, (R, g)).astype(np.float32)
+        c[rng.uniform(size=(R, g)) < 0.15] = 0.0
+        c[rng.uniform(size=(R, g)) < 0.15] = 1.0
+        sps = list(_sps_curves(n_max))[it % 4]
+        nm = int(rng.integers(R, n_max + 1))
+        a = _survival_f32(c)
+        best, bestB = None, None
+        for ell in itertools.product(range(g + 1), repeat=R):
+            th = _theta_exact(a, ell, sps, nm)
+            B = R + sum(ell)
+            if best is None or th > best or (th == best and B < bestB):
+                best, bestB = th, B
+        _, _, _, _, K, thp = O.async_schedule(c, sps, 0, N_max=nm)
+        assert thp == float(best)
+        assert K == bestB
+    # ties: with SPS(B) = 1/B and every c = 1, every schedule has Theta = 1;
+    # the first maximum is the smallest batch
+    Bv = np.arange(n_max + 1, dtype=np.float64)
+    sps = 1.0 / np.maximum(Bv, 1.0)
+    _, _, _, _, K, thp = O.async_schedule(np.ones((R, g), np.float32), sps, 0)
+    assert K == R and thp == 1.0
+
+
+def test_async_admission_is_topk():
+    """The admitted set holds exactly min(K, N_max) - R candidates (clamped to
+    [0, |E|]), every admitted survival precedes every rejected positive one in
+    the (a desc, r, j) order, it is prefix-closed per request, and Theta is the
+    admitted schedule's."""
+    rng = np.random.default_rng(21)
+    for it in range(1500):
+        R, g = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        c = rng.uniform(0, 1, (R, g)).astype(np.float32)
+        c[rng.uniform(size=(R, g)) < 0.1] = 0.0
+        c[rng.uniform(size=(R, g)) < 0.1] = 1.0
+        nm = int(rng.integers(R, R * (g + 1) + 3))
+        sps = list(_sps_curves(nm))[it % 4]
+        K_in = int(rng.integers(-2, R * (g + 1) + 4))
+        ell, a, N, th, _, _ = O.async_schedule(c, sps, K_in, N_max=nm)
+        np.testing.assert_array_equal(a, _survival_f32(c))
+        pos = [(-float(a[r, j]), r, j + 1) for r in range(R) for j in range(g) if a[r, j] > 0]
+        adm = [p for p in pos if p[2] <= ell[p[1]]]
+        rej = [p for p in pos if p[2] > ell[p[1]]]
+        assert len(adm) == int(ell.sum())            # every admitted position has a > 0
+        assert len(adm) == max(0, min(min(K_in, nm) - R, len(pos)))
+        if adm and rej:
+            assert max(adm) < min(rej)
+        assert N == R + len(adm) <= max(nm, R)
+        assert th == float(_theta_exact(a, ell, sps, nm))
+
+
+def test_async_reduces_to_algorithm1_and_global_search():
+    """Given the batch size Algorithm 1 chose, the top-K admission returns
+    Algorithm 1's schedule (it admits a prefix of the same order); given the
+    capacity planned on the same round, it returns the global search's."""
+    rng = np.random.default_rng(22)
+    for it in range(800):
+        R, g = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+        c = special.expit(rng.normal(1.0, 2.0, (R, g))).astype(np.float32)
+        sps = list(_sps_curves(R * (g + 1)))[it % 4]
+        ell1, _, N1, th1, _ = O.prefix_schedule(c, sps, mode=0)
+        ell, _, N, th, K, thp = O.async_schedule(c, sps, N1)
+        np.testing.assert_array_equal(ell, ell1)
+        assert N == N1 and th == th1
+        ellg, _, Ng, thg, _ = O.prefix_schedule(c, sps, mode=1)
+        ell2, _, N2, th2, _, _ = O.async_schedule(c, sps, K)
+        np.testing.assert_array_equal(ell2, ellg)
+        assert N2 == Ng == K and th2 == thg == thp
+        assert thp >= th1                           # the global search never does worse
+
+
+def test_async_causal_barrier_and_static_limits():
+    """The number of admitted tokens depends only on the capacity handed in
+    (and on how many candidates exist), never on this round's values; a
+    capacity of the whole block verifies everything, one of R verifies the
+    anchors only."""
+    rng = np.random.default_rng(23)
+    R, g = 12, 6
+    B = np.arange(R * (g + 1) + 1, dtype=np.float64)
+    sps = 1.0 / (0.015 + 4e-5 * B + 0.003 * (B // 5))
+    for it in range(200):
+        K_in = int(rng.integers(R, R * (g + 1) + 1))
+        c1 = rng.uniform(0.05, 1.0, (R, g)).astype(np.float32)
+        c2 = rng.uniform(0.05, 1.0, (R, g)).astype(np.float32)
+        n1 = int(O.async_schedule(c1, sps, K_in)[0].sum())
+        n2 = int(O.async_schedule(c2, sps, K_in)[0].sum())
+        assert n1 == n2 == K_in - R
+    c = rng.uniform(0.05, 1.0, (R, g)).astype(np.float32)
+    assert (O.async_schedule(c, sps, R * (g + 1))[0] == g).all()
+    assert (O.async_schedule(c, sps, R)[0] == 0).all()
+    assert (O.async_schedule(c, sps, 0)[0] == 0).all()
+
+
 # ------------------------------------------------------------------- pack --
 def test_pack_identities():
     rng = np.random.default_rng(16)
