@@ -1,7 +1,7 @@
 """Benchmark: one DSpark round (draft -> confidence -> schedule -> pack ->
 verify -> pack) on one MI355X at the headline workload, R = 256 requests,
 block size 16, vocabulary 129280, Markov rank 256, hidden 4096, bf16, T = 1,
-scheduler on.
+scheduler on (Algorithm 1; --scheduler async selects the asynchronous form).
 
 Prints ONE JSON line.  `value` = verified draft tokens per second
 (sum of scheduled lengths ell over the timed rounds / their wall time), inputs
@@ -38,6 +38,10 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=2)
+    p.add_argument("--scheduler", choices=["greedy", "async", "static"], default=None,
+                   help="Algorithm 1, the asynchronous production form (capacity planned two "
+                        "rounds earlier, top-K admission), or the static block; default: the "
+                        "configuration's (Algorithm 1, or static where it turns scheduling off)")
     p.add_argument("--cpu-sample", type=int, default=48, help="requests in the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -182,6 +186,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     n_timed = [0]
+    sched = args.scheduler or ("greedy" if cfg.scheduler else "static")
+    ring = RD.CapacityRing(cfg.R, cfg.gamma, inp["sps"].numel() - 1, device=dev)
 
     def one_round(i, timed):
         buf.ell, buf.m = ells[i], ms[i]
@@ -196,8 +202,13 @@ def main():
             L.draft_markov(inp["U"], inp["W1"], inp["W2t"], inp["x0"], cfg.T, cfg.philox_seed, i,
                            buf.x, buf.logp_d, buf.lse_d, buf.ws)
         L.confidence(inp["h"], inp["W1"], inp["w"], buf.x, buf.c, V=cfg.V)
-        L.prefix_schedule(buf.c, inp["sps"], buf.ell, enabled=cfg.scheduler, a=buf.a, N_out=buf.N,
-                          theta_best=buf.theta)
+        if sched == "async":
+            kin, kplan = ring.slots(i)
+            L.async_schedule(buf.c, inp["sps"], kin, kplan, buf.ell, a=buf.a, N_out=buf.N,
+                             theta=buf.theta)
+        else:
+            L.prefix_schedule(buf.c, inp["sps"], buf.ell, enabled=(sched == "greedy"), a=buf.a,
+                              N_out=buf.N, theta_best=buf.theta)
         L.pack(buf.x, buf.ell, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N,
                ws=buf.ws)
         L.verify(buf.ell, buf.cu, inp["target"], 1, buf.x, buf.logp_d, buf.lse_d, inp["U"],
@@ -257,7 +268,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, inp, buf, args.cpu_sample, sum_ell / K, torch, np)
+        cpu = cpu_baseline(cfg, inp, buf, args.cpu_sample, sum_ell / K, torch, np, sched,
+                           int(Ns[W + K - 1].item()))
     out = {
         "metric": "verified draft tokens/s per round (B=256,γ=16,V=129280) + % peak HBM",
         "value": value,
@@ -273,7 +285,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"dspark-round config {args.config} ({cfg.name})", "R": cfg.R,
                    "gamma": cfg.gamma, "V": cfg.V, "rank": cfg.rank, "d": cfg.d, "T": cfg.T,
-                   "scheduler": cfg.scheduler, "parallelism": "single-gpu"},
+                   "scheduler": sched, "parallelism": "single-gpu"},
         "hbm_frac_round": hbm_frac_round,
         "round_bytes_alg": bytes_round,
         "emitted_tokens_per_s": sum_tau / t_total,
@@ -290,7 +302,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(cfg, inp, buf, n_req, ell_per_round, torch, np):
+def cpu_baseline(cfg, inp, buf, n_req, ell_per_round, torch, np, sched="greedy", K_in=0):
     """The oracle as it stands, on a bounded sample: draft + confidence +
     verify for n_req requests, the scheduler and both packs on the full batch;
     the per-request part is scaled to all R requests."""
@@ -310,7 +322,10 @@ def cpu_baseline(cfg, inp, buf, n_req, ell_per_round, torch, np):
     t1 = time.perf_counter()
     c_all = c_all.copy()
     c_all[reqs] = c
-    ell, _, N, _, _ = O.prefix_schedule(c_all, sps, enabled=cfg.scheduler)
+    if sched == "async":
+        ell = O.async_schedule(c_all, sps, K_in)[0]
+    else:
+        ell = O.prefix_schedule(c_all, sps, enabled=(sched == "greedy"))[0]
     O.pack(x_all, ell + 1)
     t2 = time.perf_counter()
     O.verify(ell[reqs], None, tgt, 1, x, lp, lse, U, W1, W2t, cfg.T, cfg.philox_seed, 0,

@@ -7,10 +7,10 @@ synthetic inputs.  Importing the package loads the library and fails if it is
 missing; there is no other execution path.
 """
 from . import _lib
-from ._lib import (DsparkError, confidence, draft_markov, get_status, clear_status, pack,
-                   prefix_schedule, verify, workspace, workspace_bytes)
+from ._lib import (DsparkError, async_schedule, confidence, draft_markov, get_status,
+                   clear_status, pack, prefix_schedule, verify, workspace, workspace_bytes)
 
 _lib.load()
 
-__all__ = ["DsparkError", "confidence", "draft_markov", "get_status", "clear_status", "pack",
+__all__ = ["DsparkError", "async_schedule", "confidence", "draft_markov", "get_status", "clear_status", "pack",
            "prefix_schedule", "verify", "workspace", "workspace_bytes"]

@@ -24,7 +24,7 @@ CHUNK = 128
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
            "dspark_clear_status", "dspark_get_status", "dspark_draft_markov",
            "dspark_confidence", "dspark_prefix_schedule", "dspark_pack", "dspark_verify",
-           "dspark_draft_markov_profiled")
+           "dspark_draft_markov_profiled", "dspark_async_schedule")
 
 
 class DsparkError(RuntimeError):
@@ -57,6 +57,7 @@ def load():
     L.dspark_draft_markov_profiled.argtypes = L.dspark_draft_markov.argtypes + [P, P, P]
     L.dspark_confidence.argtypes = [i32, i32, i32, i32, i32, P, i32, P, i32, P, i32, P, P, P, P]
     L.dspark_prefix_schedule.argtypes = [i32, i32, P, P, i32, i32, P, P, P, P, P]
+    L.dspark_async_schedule.argtypes = [i32, i32, P, P, i32, P, P, P, P, P, P, P, P]
     L.dspark_pack.argtypes = [i32, i32, P, P, i32, P, P, P, P, P, P, sz, P]
     L.dspark_verify.argtypes = [i32, i32, i32, i32, f32, u64, u64, P, P, P, i32, i32, P, P, P, P,
                                 i32, P, P, i32, P, P, P, P, P, P, sz, P]
@@ -162,6 +163,16 @@ def prefix_schedule(c, sps, ell, enabled=True, N_max=None, a=None, N_out=None, t
                                          _ptr(ell), _ptr(a), _ptr(N_out), _ptr(theta_best),
                                          _stream(stream))
     _check("dspark_prefix_schedule", code)
+
+
+def async_schedule(c, sps, K_in, K_plan, ell, N_max=None, a=None, N_out=None, theta=None,
+                   theta_plan=None, stream=None):
+    R, gamma = c.shape
+    N_max = sps.numel() - 1 if N_max is None else N_max
+    code = load().dspark_async_schedule(R, gamma, _ptr(c), _ptr(sps), int(N_max), _ptr(K_in),
+                                        _ptr(K_plan), _ptr(ell), _ptr(a), _ptr(N_out), _ptr(theta),
+                                        _ptr(theta_plan), _stream(stream))
+    _check("dspark_async_schedule", code)
 
 
 def pack(rows, lens, len_offset, cu, flat, marker_req=None, marker_pos=None, N_out=None, ws=None,

@@ -77,12 +77,16 @@ struct PackArgs {
 
 struct SchedArgs {
   int R, gamma, N_max, enabled;
+  int mode;                 // 0: Algorithm 1 (early stop); 1: asynchronous (top-K + plan)
   const float* c;
   const double* sps;
   int32_t* ell;
   float* a;
   int32_t* N_out;
   double* theta;
+  const int32_t* K_in;      // mode 1: capacity planned two rounds earlier
+  int32_t* K_plan;          // mode 1: capacity planned from this round
+  double* theta_plan;       // mode 1 (nullable)
 };
 
 hipError_t launch_row_stats(const RowStatsArgs& a, bool bf16, bool greedy, hipStream_t st);

@@ -20,6 +20,15 @@
 // Theta_q <= Theta_{q-1}; a block-wide min finds that q.  ell_r is then the
 // largest admitted position of request r (admitted positions of a request are
 // always a prefix 1..ell_r, because a is non-increasing in j).
+//
+// The asynchronous form used in production (same page, Supplementary details,
+// the scheduler in production) sorts the same keys and takes two decisions
+// from the one sort: admission of the first min(K_in, N_max) - R candidates
+// (K_in = verify capacity in tokens planned two rounds earlier; clamped to
+// [0, |E|]; no Theta test), and the plan K_plan = R + q* where q* is the first
+// maximiser of Theta_q over q = 0..|E| (global search: every thread keeps the
+// first maximum of its own positions, then one block-wide (max Theta, min q)
+// reduction).
 #include "launch.hpp"
 
 namespace dspark {
@@ -61,6 +70,28 @@ __device__ inline int64_t block_exscan_i64(int64_t v, int64_t* lds) {
   for (int q = 0; q < wv; ++q) before += lds[q];
   __syncthreads();
   return before + inc - v;
+}
+
+// (max th, then min q) over the workgroup: the first maximum of Theta_q when
+// every thread holds the first maximum of its own ascending positions.
+__device__ inline void block_argmax_first(double& th, int& q, double* ldsd, int* ldsi) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const double oth = __shfl_xor(th, o);
+    const int oq = __shfl_xor(q, o);
+    if (oth > th || (oth == th && oq < q)) { th = oth; q = oq; }
+  }
+  if (lane == 0) { ldsd[wv] = th; ldsi[wv] = q; }
+  __syncthreads();
+  th = ldsd[0];
+  q = ldsi[0];
+  for (int w = 1; w < kSchedThreads / 64; ++w) {
+    const double oth = ldsd[w];
+    const int oq = ldsi[w];
+    if (oth > th || (oth == th && oq < q)) { th = oth; q = oq; }
+  }
+  __syncthreads();
 }
 
 __device__ inline int block_min_i(int v, int* lds) {
@@ -183,7 +214,7 @@ __device__ __forceinline__ void merge_sort_runs(uint64_t (&v)[EPT], uint64_t* ke
 
 template <int EPT>
 __device__ __forceinline__ void schedule_body(const SchedArgs& a, int G2, uint64_t* keys, int64_t* red64,
-                                              int* red32) {
+                                              int* red32, const int* kin_l) {
   const int tid = threadIdx.x;
   const int R = a.R, G = a.gamma;
   const int P = kSchedThreads * EPT;
@@ -261,6 +292,11 @@ __device__ __forceinline__ void schedule_body(const SchedArgs& a, int G2, uint64
     if (v[e] != ~0ull) local += fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(v[e] >> 32)));
   int64_t tau = ((int64_t)R << 32) + block_exscan_i64(local, red64);  // tau before p0
   int first_stop = 0x7FFFFFFF, firstsent = 0x7FFFFFFF;
+  // asynchronous form: first maximum of Theta_q over this thread's q = p + 1
+  // (thread 0 also holds q = 0)
+  double pbest = -__builtin_inf();
+  int pq = 0x7FFFFFFF;
+  if (a.mode == 1 && tid == 0) { pbest = theta_of((int64_t)R << 32, R, a.N_max, a.sps); pq = 0; }
   bool stopped = false;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
@@ -268,17 +304,33 @@ __device__ __forceinline__ void schedule_body(const SchedArgs& a, int G2, uint64
     if (v[e] == ~0ull) { if (firstsent == 0x7FFFFFFF) firstsent = p; stopped = true; }
     if (!stopped) {
       const int64_t tau_next = tau + fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(v[e] >> 32)));
-      const double before = theta_of(tau, R + p, a.N_max, a.sps);
       const double after = theta_of(tau_next, R + p + 1, a.N_max, a.sps);
-      if (!(after > before)) { first_stop = p; stopped = true; }
+      if (a.mode == 0) {
+        const double before = theta_of(tau, R + p, a.N_max, a.sps);
+        if (!(after > before)) { first_stop = p; stopped = true; }
+      } else if (after > pbest) {
+        pbest = after;
+        pq = p + 1;
+      }
       tau = tau_next;
     }
   }
   // number of candidates = position of the first sentinel key
   int E = block_min_i(firstsent, red32);
   if (E > P) E = P;
-  int admitted = block_min_i(first_stop, red32);
-  if (admitted > E) admitted = E;
+  int admitted;
+  if (a.mode == 0) {
+    admitted = block_min_i(first_stop, red32);
+    if (admitted > E) admitted = E;
+  } else {
+    const int cap = min(*kin_l, a.N_max);
+    admitted = max(0, min(cap - R, E));
+    block_argmax_first(pbest, pq, reinterpret_cast<double*>(red64), red32);
+    if (tid == 0) {
+      *a.K_plan = R + pq;
+      if (a.theta_plan) *a.theta_plan = pbest;
+    }
+  }
 
   // ell_r = largest admitted position of request r, by LDS atomics in the
   // (now free) key buffer, then written out
@@ -306,16 +358,19 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(SchedArgs a) {
   __shared__ uint64_t keys[kSchedMaxKeys];
   __shared__ int64_t red64[kSchedThreads / 64];
   __shared__ int red32[kSchedThreads / 64];
+  __shared__ int kin_l;
+  // K_in is read once, before K_plan (which may be the same address) is written
+  if (threadIdx.x == 0) kin_l = (a.mode == 1) ? *a.K_in : 0;
   // runs padded to a power of two when they fit, else packed keys
   int G2 = 1;
   while (G2 < a.gamma) G2 *= 2;
   int n = a.R * G2;
   if (n > kSchedMaxKeys) { G2 = 0; n = a.R * a.gamma; }
-  if (n <= kSchedThreads) schedule_body<1>(a, G2, keys, red64, red32);
-  else if (n <= 2 * kSchedThreads) schedule_body<2>(a, G2, keys, red64, red32);
-  else if (n <= 4 * kSchedThreads) schedule_body<4>(a, G2, keys, red64, red32);
-  else if (n <= 8 * kSchedThreads) schedule_body<8>(a, G2, keys, red64, red32);
-  else schedule_body<16>(a, G2, keys, red64, red32);
+  if (n <= kSchedThreads) schedule_body<1>(a, G2, keys, red64, red32, &kin_l);
+  else if (n <= 2 * kSchedThreads) schedule_body<2>(a, G2, keys, red64, red32, &kin_l);
+  else if (n <= 4 * kSchedThreads) schedule_body<4>(a, G2, keys, red64, red32, &kin_l);
+  else if (n <= 8 * kSchedThreads) schedule_body<8>(a, G2, keys, red64, red32, &kin_l);
+  else schedule_body<16>(a, G2, keys, red64, red32, &kin_l);
 }
 
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t st) {

@@ -1,6 +1,7 @@
 """One DSpark round on the GPU: the six C-ABI calls enqueued back to back.
 
-draft (Markov head) -> confidence -> prefix schedule -> pack the verify batch
+draft (Markov head) -> confidence -> prefix schedule (Algorithm 1, static, or
+the asynchronous form with a two-slot capacity ring) -> pack the verify batch
 -> verify -> pack the emitted tokens.  This module only allocates the output
 tensors (torch is the memory allocator) and calls the library in order; the
 scheduled lengths, N, m and tau never leave the device.
@@ -43,17 +44,42 @@ class RoundBuffers:
         self.ws = L.workspace(R, gamma, V, device=dev)
 
 
+class CapacityRing:
+    """Verify capacities of the asynchronous scheduler, two device slots.
+
+    The capacity that round t admits with was planned at round t - 2 from that
+    round's confidences, so slot t % 2 is read and rewritten by round t (the
+    scheduler reads its capacity before it writes the new plan).  Both slots
+    start at the static block, min(R (gamma + 1), N_max)."""
+
+    def __init__(self, R, gamma, N_max, device="cuda"):
+        self.K = torch.full((2,), min(R * (gamma + 1), N_max), dtype=torch.int32,
+                            device=torch.device(device))
+
+    def slots(self, rnd):
+        """(K_in, K_plan) of round `rnd`: the same device int."""
+        s = self.K[rnd % 2: rnd % 2 + 1]
+        return s, s
+
+
 def run_round(inp, buf: RoundBuffers, T, seed, rnd, scheduler=True, layout=1, sts_T=None,
-              stream=None):
+              stream=None, ring: CapacityRing = None):
     """Enqueue one full round on `stream` (default: torch's current stream).
 
     `inp` holds U, W1, W2t, x0, h, w, sps and target (dense [R][gamma+1][V] for
-    layout 1; packed rows in verify order for layout 0)."""
+    layout 1; packed rows in verify order for layout 0).  `scheduler`: True =
+    Algorithm 1, False = static block, "async" = the asynchronous scheduler
+    with capacities from `ring`."""
     L.draft_markov(inp["U"], inp["W1"], inp["W2t"], inp["x0"], T, seed, rnd, buf.x, buf.logp_d,
                    buf.lse_d, buf.ws, stream=stream)
     L.confidence(inp["h"], inp["W1"], inp["w"], buf.x, buf.c, sts_T=sts_T, V=buf.V, stream=stream)
-    L.prefix_schedule(buf.c, inp["sps"], buf.ell, enabled=scheduler, a=buf.a, N_out=buf.N,
-                      theta_best=buf.theta, stream=stream)
+    if scheduler == "async":
+        kin, kplan = ring.slots(rnd)
+        L.async_schedule(buf.c, inp["sps"], kin, kplan, buf.ell, a=buf.a, N_out=buf.N,
+                         theta=buf.theta, stream=stream)
+    else:
+        L.prefix_schedule(buf.c, inp["sps"], buf.ell, enabled=bool(scheduler), a=buf.a,
+                          N_out=buf.N, theta_best=buf.theta, stream=stream)
     L.pack(buf.x, buf.ell, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N, ws=buf.ws,
            stream=stream)
     L.verify(buf.ell, buf.cu, inp["target"], layout, buf.x, buf.logp_d, buf.lse_d, inp["U"],

@@ -175,6 +175,40 @@ dspark_status dspark_prefix_schedule(int R, int gamma, const float* c, const dou
                                      int32_t* N_out, double* theta_best, hipStream_t stream);
 
 /*
+ * Asynchronous prefix scheduler, the production form ([P3] Supplementary
+ * details, the hardware-aware prefix scheduler in production; [P1] 4.2.5 and
+ * 8.5).  The candidates and their order are those of dspark_prefix_schedule.
+ * One sort of this round's candidates serves two decisions:
+ *   admission  the first min(*K_in, N_max) - R candidates are admitted
+ *              (dynamic top-K: none if that count is <= 0, all if it exceeds
+ *              their number); no Theta test, no early stop.
+ *   planning   q* = the first q in 0..|E| maximising Theta_q = tau_q SPS(R + q)
+ *              over the sorted candidates (global search; Theta = 0 past
+ *              N_max); *K_plan = R + q*.  A round two rounds later passes it
+ *              back as K_in.
+ * Because the capacity a round admits with was fixed from confidences two
+ * rounds old, the batch size does not depend on this round's tokens, and the
+ * host can read it (copied asynchronously) before the round is enqueued.
+ *   c, sps, N_max   as for dspark_prefix_schedule; SPS values finite, >= 0
+ *   K_in       (device scalar) verify capacity in tokens, anchors included;
+ *              the caller seeds the first two rounds (e.g. with
+ *              min(R (gamma + 1), N_max), the static block)
+ *   K_plan     out (device scalar) the capacity planned from this round.  May
+ *              be the same address as K_in: K_in is read before K_plan is
+ *              written (a two-slot ring indexed by round parity works).
+ *   ell        out [R]  scheduled verify lengths (admitted prefix per request)
+ *   a          out nullable [R][gamma] survival products
+ *   N_out      out nullable (device scalar) sum_i (1 + ell_i)
+ *   theta      out nullable (device scalar) Theta of the admitted schedule
+ *   theta_plan out nullable (device scalar) Theta_{q*}
+ * Needs R <= N_max and R * gamma <= 16384, like dspark_prefix_schedule.
+ */
+dspark_status dspark_async_schedule(int R, int gamma, const float* c, const double* sps,
+                                    int N_max, const int32_t* K_in, int32_t* K_plan, int32_t* ell,
+                                    float* a, int32_t* N_out, double* theta, double* theta_plan,
+                                    hipStream_t stream);
+
+/*
  * Ragged pack ([P3] Supplementary details, variable-length routing; [P4] 3.3):
  * row i contributes its first len[i] + len_offset tokens; all of them are
  * flattened back to back as independent elements, with offsets and marker

@@ -81,6 +81,14 @@ def test_confidence_schedule_pack_verify_checks():
     assert sched(N_max=3) == INVALID                     # N_max < R
     assert sched(R=1024, g=17, N_max=10**6) == UNSUPPORTED   # R * gamma > 16384
     assert sched(c=None) == INVALID
+    asch = lambda R=4, g=4, N_max=100, kin=FAKE, kp=FAKE, ell=FAKE: lib.dspark_async_schedule(
+        R, g, FAKE, FAKE, N_max, kin, kp, ell, None, None, None, None, None)
+    assert asch(R=-1) == INVALID
+    assert asch(N_max=3) == INVALID
+    assert asch(kin=None) == INVALID and asch(kp=None) == INVALID
+    assert asch(g=33) == UNSUPPORTED
+    assert asch(R=1024, g=17, N_max=10**6) == UNSUPPORTED
+    assert asch(R=0, kin=None) == OK
     pack = lambda R=4, width=3, rows=FAKE, ln=FAKE, cu=FAKE, flat=FAKE: lib.dspark_pack(
         R, width, rows, ln, 0, cu, flat, None, None, None, None, 0, None)
     assert pack(width=0) == INVALID
@@ -110,7 +118,8 @@ def test_synthetic_configs_shapes():
     assert sps[0] == sps[31] and sps[2049] == 0 and (sps[32:2049].diff() <= 0).all()
 
 
-@pytest.mark.parametrize("fn", ["draft_markov", "confidence", "prefix_schedule", "pack", "verify"])
+@pytest.mark.parametrize("fn", ["draft_markov", "confidence", "prefix_schedule", "async_schedule",
+                                "pack", "verify"])
 def test_binding_names_match_abi(fn):
     assert callable(getattr(D, fn))
     assert f"dspark_{fn}" in declared()

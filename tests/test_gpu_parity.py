@@ -281,6 +281,88 @@ def test_scheduler_stress_size():
         _sched_case(c3, 1.0 / (0.020 + 5e-5 * B))
 
 
+def _async_case(c, sps, K_in, N_max=None, alias=False):
+    import oracle as O
+    R, g = c.shape
+    cd = torch.as_tensor(c, device=DEV)
+    spsd = torch.as_tensor(sps, device=DEV)
+    ell = torch.empty(R, dtype=torch.int32, device=DEV)
+    a = torch.empty(R, g, dtype=torch.float32, device=DEV)
+    N = torch.empty(1, dtype=torch.int32, device=DEV)
+    th = torch.empty(1, dtype=torch.float64, device=DEV)
+    thp = torch.empty(1, dtype=torch.float64, device=DEV)
+    Kin = torch.full((1,), K_in, dtype=torch.int32, device=DEV)
+    Kp = Kin if alias else torch.empty(1, dtype=torch.int32, device=DEV)
+    D.async_schedule(cd, spsd, Kin, Kp, ell, N_max=N_max, a=a, N_out=N, theta=th, theta_plan=thp)
+    torch.cuda.synchronize()
+    e, ao, No, tho, Ko, thpo = O.async_schedule(c, sps, K_in, N_max=N_max)
+    np.testing.assert_array_equal(n(ell), e)
+    np.testing.assert_array_equal(n(a).view(np.uint32), ao.view(np.uint32))
+    assert int(n(N)[0]) == No
+    assert float(n(th)[0]) == tho
+    assert int(n(Kp)[0]) == Ko
+    assert float(n(thp)[0]) == thpo
+
+
+def test_async_scheduler_bitexact_random_and_ties():
+    rng = np.random.default_rng(5)
+    for it in range(40):
+        R, g = int(rng.integers(1, 300)), int(rng.integers(1, 33))
+        if R * g > 16384:
+            continue
+        c = rng.uniform(0, 1, (R, g)).astype(np.float32)
+        if it % 3 == 0:
+            c = rng.choice(np.array([0, 0.25, 0.5, 0.75, 1.0], np.float32), (R, g))
+        if it % 5 == 0:
+            c[:, :] = 1.0
+        B = np.arange(R * (g + 1) + 1, dtype=np.float64)
+        sps = [1.0 / (0.020 + 5e-5 * B), 1.0 / (0.02 + 0.002 * B),
+               1.0 / (0.015 + 4e-5 * B + 0.003 * (B // 7)), 1.0 / np.maximum(B, 1.0)][it % 4]
+        N_max = None if it % 4 else int(rng.integers(R, R * (g + 1) + 1))
+        for K_in in [int(rng.integers(R, R * (g + 1) + 1)), 0, R, R * (g + 1) + 5]:
+            _async_case(c, sps, K_in, N_max=N_max, alias=(it % 2 == 0))
+
+
+def test_async_scheduler_stress_size():
+    cfg = synth.config(3)
+    rng = np.random.default_rng(4)
+    z = rng.normal(0, 3.2, (cfg.R, cfg.gamma))
+    c = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+    sps = synth.sps_table(cfg, cfg.R * (cfg.gamma + 1)).numpy()
+    for K_in in [cfg.R, cfg.R + 3000, cfg.R * (cfg.gamma + 1)]:
+        _async_case(c, sps, K_in)
+    for R, g in [(600, 17), (900, 17)]:
+        c3 = rng.uniform(0.6, 1.0, (R, g)).astype(np.float32)
+        B = np.arange(R * (g + 1) + 1, dtype=np.float64)
+        _async_case(c3, 1.0 / (0.015 + 4e-5 * B + 0.003 * (B // 64)), R + 4000)
+
+
+def test_async_scheduler_two_round_pipeline():
+    """Rounds t = 0..7 through the round driver's two-slot capacity ring: the
+    capacity round t admits with is the one planned at round t - 2 (the seed
+    for t < 2), in the same stream order as a live decode loop."""
+    import oracle as O
+    rng = np.random.default_rng(6)
+    R, g = 48, 7
+    B = np.arange(R * (g + 1) + 1, dtype=np.float64)
+    sps = 1.0 / (0.015 + 4e-5 * B + 0.003 * (B // 16))
+    spsd = torch.as_tensor(sps, device=DEV)
+    ring = RD.CapacityRing(R, g, len(sps) - 1, device=DEV)
+    ell = torch.empty(R, dtype=torch.int32, device=DEV)
+    cs = [(1.0 / (1.0 + np.exp(-rng.normal(1.5, 2.5, (R, g))))).astype(np.float32) for _ in range(8)]
+    outs = []
+    for t, c in enumerate(cs):
+        kin, kplan = ring.slots(t)
+        D.async_schedule(torch.as_tensor(c, device=DEV), spsd, kin, kplan, ell)
+        outs.append(n(ell).copy())
+    torch.cuda.synchronize()
+    hist = [min(R * (g + 1), len(sps) - 1)] * 2
+    for t, c in enumerate(cs):
+        e, _, _, _, Kp, _ = O.async_schedule(c, sps, hist[t])
+        np.testing.assert_array_equal(outs[t], e)
+        hist.append(Kp)
+
+
 # ------------------------------------------------------------- stage: pack
 def test_pack_bitexact():
     import oracle as O
