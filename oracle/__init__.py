@@ -224,6 +224,51 @@ def pack(rows, lens):
     return cu, flat, mr, mp, int(N[0])
 
 
+def pack_tiered(rows, lens, tiers, pad_token, slots=None):
+    """Ragged pack padded to a captured graph tier (bevisy.github.io DeepSpec
+    analysis, section 5.4, DSpark in SGLang: ragged verify packs the requests
+    into one compact buffer whose total is rounded up to a captured CUDA-graph
+    tier).  The pack itself is `pack`; N_pad = the smallest tier >= N (N itself,
+    flagged, when no tier holds N); slots [N, N_pad) hold pad_token with
+    markers -1, slots from N_pad to `slots` hold -1.
+    Returns (cu, flat, marker_req, marker_pos, N, N_pad, overflow)."""
+    rows = _i32(rows)
+    R, width = rows.shape
+    slots = R * width if slots is None else int(slots)
+    assert all(0 < int(t) <= slots for t in tiers) and slots >= R * width
+    cu, flat, mr, mp, N = pack(rows, lens)
+    fits = [int(t) for t in tiers if int(t) >= N]
+    N_pad = min(fits) if fits else N
+    out = np.full(slots, -1, np.int32)
+    omr, omp = np.full(slots, -1, np.int32), np.full(slots, -1, np.int32)
+    out[:N], omr[:N], omp[:N] = flat[:N], mr[:N], mp[:N]
+    out[N:N_pad] = pad_token
+    return cu, out, omr, omp, N, N_pad, not fits
+
+
+def verify_cap_accept(ell, cap, cu, target, layout, x, logp_d, lse_d, U, W1, W2t, T, seed=0,
+                      rnd=0, req_ids=None):
+    """Cap-accept verification (bevisy.github.io DeepSpec analysis, section
+    5.4, DSpark in SGLang, the verify modes: verify the whole window, commit
+    only the scheduler's truncated window).  Request i is verified over its window ell[i] exactly
+    as in `verify`; of the token sequence that produces (m accepted drafts,
+    then the correction or bonus), the first min(m, c) + 1 tokens are
+    committed, c = cap[i] clamped to [0, ell[i]].  When m > c the committed
+    token at position c + 1 is the accepted draft x_{c+1} itself.
+    Returns (m, tau, emitted, next_anchor, logp_t, margin, m_full)."""
+    m_full, _, em_full, _, lpt, mg = verify(ell, cu, target, layout, x, logp_d, lse_d, U, W1, W2t,
+                                            T, seed, rnd, req_ids=req_ids)
+    ell = _i32(ell)
+    c = np.clip(_i32(cap), 0, ell)
+    m = np.minimum(m_full, c).astype(np.int32)
+    tau = m + 1
+    em = np.full_like(em_full, -1)
+    for i in range(ell.size):
+        em[i, :tau[i]] = em_full[i, :tau[i]]
+    na = em[np.arange(ell.size), tau - 1].astype(np.int32)
+    return m, tau.astype(np.int32), em, na, lpt, mg, m_full
+
+
 def verify(ell, cu, target, layout, x, logp_d, lse_d, U, W1, W2t, T, seed=0, rnd=0,
            req_ids=None, force_m=None):
     ell = _i32(ell)

@@ -194,3 +194,96 @@ def test_monte_carlo_sampled_path_lossless(T):
     bc[-1] += cc
     chi = stats.chisquare(bc, be)
     assert chi.pvalue > 1e-4, chi
+
+
+def _enumerate_cap_accept(U, W1, W2t, h, w, tl, T, sps, anchor):
+    """Law of the committed tokens of a cap-accept round: every position of
+    the block is verified, the commit window is Algorithm 1's ell; when more
+    than ell drafts were accepted the committed tokens are x_1..x_{ell+1}."""
+    emitted_law = {}
+    for xs in itertools.product(range(V), repeat=G):
+        x = (anchor,) + xs
+        pd = [O.draft_row(U[k - 1], W1, W2t, x[k - 1], T) for k in range(1, G + 1)]
+        p_draft = np.prod([pd[k - 1][x[k]] for k in range(1, G + 1)])
+        c, _ = O.confidence(h[None], W1, w, np.array([x]))
+        cap = int(O.prefix_schedule(c, sps, mode=0)[0][0])
+        p_reach = 1.0
+        outcomes = []
+        for k in range(1, G + 1):
+            pt = _pt(tl, x[1:k], T)
+            alpha = min(1.0, pt[x[k]] / pd[k - 1][x[k]])
+            q, _ = O.residual_row(tl[tuple(x[1:k])], np.log(pd[k - 1]), 0.0, T)
+            outcomes.append((k - 1, p_reach * (1.0 - alpha), q))
+            p_reach *= alpha
+        outcomes.append((G, p_reach, _pt(tl, x[1:G + 1], T)))
+        for m, pm, ydist in outcomes:
+            if pm == 0.0:
+                continue
+            if m > cap:
+                e = tuple(int(t) for t in x[1:cap + 2])
+                emitted_law[e] = emitted_law.get(e, 0.0) + p_draft * pm
+                continue
+            for y in range(V):
+                e = tuple(int(t) for t in x[1:m + 1]) + (y,)
+                emitted_law[e] = emitted_law.get(e, 0.0) + p_draft * pm * ydist[y]
+    return _complete(tl, emitted_law, T)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_exact_enumeration_cap_accept_lossless(T):
+    U, W1, W2t, h, w, tl = _setup(31)
+    law = _enumerate_cap_accept(U, W1, W2t, h, w, tl, T, _sps_dynamic(), anchor=5)
+    ref = _target_law(tl, T)
+    assert abs(sum(law.values()) - 1.0) < 1e-12
+    tv = 0.5 * sum(abs(law.get(s, 0.0) - p) for s, p in ref.items())
+    assert tv < 1e-12, tv
+
+
+def test_monte_carlo_cap_accept_lossless():
+    """The oracle's sampled cap-accept path (full-block verify, commit within
+    Algorithm 1's window) against the target law."""
+    T = 1.0
+    U, W1, W2t, h, w, tl = _setup(31)
+    n = 120_000
+    anchor = 5
+    Ub = np.broadcast_to(U, (n, G, V))
+    x, lp, lse, _ = O.draft_markov(Ub, W1, W2t, np.full(n, anchor), T, seed=78, rnd=4)
+    c, _ = O.confidence(np.broadcast_to(h, (n, G, D)), W1, w, x)
+    sps = _sps_dynamic()
+    cap = np.array([O.prefix_schedule(c[i:i + 1], sps)[0][0] for i in range(n)], np.int32)
+    keys = list(tl.keys())
+    index = {k: i for i, k in enumerate(keys)}
+    table = np.stack([tl[k] for k in keys])
+    rows = np.zeros((n, G + 1), np.int64)
+    for j in range(G + 1):
+        rows[:, j] = [index[tuple(x[i, 1:j + 1])] for i in range(n)]
+    tgt = table[rows]
+    full = np.full(n, G, np.int32)
+    m, tau, em, na, _, _, m_full = O.verify_cap_accept(full, cap, None, tgt, 1, x, lp, lse, Ub,
+                                                       W1, W2t, T, seed=78, rnd=4)
+    assert (m_full > cap).any() and (m == np.minimum(m_full, cap)).all()
+    rng = np.random.default_rng(98)
+    seqs = np.full((n, G + 1), -1, np.int64)
+    for i in range(n):
+        s = list(em[i, :tau[i]])
+        while len(s) < G + 1:
+            s.append(int(rng.choice(V, p=_pt(tl, s, T))))
+        seqs[i] = s
+    codes = (seqs * (V ** np.arange(G, -1, -1))).sum(1)
+    counts = np.bincount(codes, minlength=V ** (G + 1))
+    probs = np.zeros(V ** (G + 1))
+    for s, p in _target_law(tl, T).items():
+        probs[int(sum(v * V ** (G - j) for j, v in enumerate(s)))] = p
+    order = np.argsort(probs)
+    be, bc, ce, cc = [], [], 0.0, 0
+    for i in order:
+        ce += probs[i] * n
+        cc += counts[i]
+        if ce >= 10:
+            be.append(ce)
+            bc.append(cc)
+            ce, cc = 0.0, 0
+    be[-1] += ce
+    bc[-1] += cc
+    chi = stats.chisquare(bc, be)
+    assert chi.pvalue > 1e-4, chi

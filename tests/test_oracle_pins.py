@@ -652,6 +652,62 @@ def test_verify_bookkeeping_and_layouts():
             assert abs(lpt[r, k - 1] - ref) < 1e-10
 
 
+def test_verify_cap_accept_invariants():
+    """Cap-accept commits a prefix of the full-window verification: m =
+    min(m_full, cap), the committed tokens are the first m + 1 of the full
+    window's, a cap at or above the window is plain verification, and at T = 0
+    the committed tokens follow the target's argmax chain."""
+    R, g, V, rank = 30, 6, 400, 16
+    U, W1, W2t, tgt, x0 = _markov_case(19, R, g, V, rank, sig_t=0.3)
+    rng = np.random.default_rng(2)
+    for T in [1.0, 0.0]:
+        x, lp, lse, _ = O.draft_markov(U, W1, W2t, x0, T, seed=6)
+        ell = np.full(R, g, np.int32)
+        cap = rng.integers(-1, g + 2, R).astype(np.int32)
+        full = O.verify(ell, None, tgt, 1, x, lp, lse, U, W1, W2t, T, seed=6)
+        m, tau, em, na, lpt, _, m_full = O.verify_cap_accept(ell, cap, None, tgt, 1, x, lp, lse, U,
+                                                             W1, W2t, T, seed=6)
+        np.testing.assert_array_equal(m_full, full[0])
+        c = np.clip(cap, 0, g)
+        np.testing.assert_array_equal(m, np.minimum(full[0], c))
+        assert (tau == m + 1).all()
+        np.testing.assert_array_equal(lpt, full[4])
+        for r in range(R):
+            np.testing.assert_array_equal(em[r, :tau[r]], full[2][r, :tau[r]])
+            assert (em[r, tau[r]:] == -1).all() and na[r] == em[r, tau[r] - 1]
+            if full[0][r] > c[r]:
+                assert na[r] == x[r, c[r] + 1]          # the accepted draft closes the window
+            if T == 0.0:
+                am = tgt[r].argmax(-1)
+                np.testing.assert_array_equal(em[r, :tau[r]], am[:tau[r]])
+        same = O.verify_cap_accept(ell, np.full(R, g + 3), None, tgt, 1, x, lp, lse, U, W1, W2t,
+                                   T, seed=6)
+        for p_, q_ in zip(same[:5], full[:5]):
+            np.testing.assert_array_equal(p_, q_)
+
+
+def test_pack_tiered():
+    rng = np.random.default_rng(3)
+    for it in range(300):
+        R, width = int(rng.integers(1, 20)), int(rng.integers(1, 9))
+        rows = rng.integers(0, 1000, (R, width)).astype(np.int32)
+        lens = rng.integers(0, width + 1, R).astype(np.int32)
+        slots = R * width + int(rng.integers(0, 100))
+        tiers = [t for t in [8, 16, 32, 64, 128] if t <= slots]
+        cu, flat, mr, mp, N, N_pad, over = O.pack_tiered(rows, lens, tiers, 7, slots=slots)
+        cu0, flat0, mr0, mp0, N0 = O.pack(rows, lens)
+        assert N == N0 == int(lens.sum())
+        np.testing.assert_array_equal(cu, cu0)
+        np.testing.assert_array_equal(flat[:N], flat0[:N])
+        np.testing.assert_array_equal(mr[:N], mr0[:N])
+        np.testing.assert_array_equal(mp[:N], mp0[:N])
+        bigger = [t for t in tiers if t >= N]
+        assert over == (not bigger)
+        assert N_pad == (bigger[0] if bigger else N)
+        assert (flat[N:N_pad] == 7).all() and (flat[N_pad:] == -1).all() and flat.size == slots
+        assert (mr[N:] == -1).all() and (mp[N:] == -1).all()
+
+
 def test_verify_first_position_acceptance_rate():
     # P(accept x_1) = sum_v min(p_d, p_t) = 1 - TV(p_d, p_t)  (the confidence
     # head's training label c* on the DSpark summary page)
