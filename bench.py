@@ -42,6 +42,9 @@ def parse():
                    help="Algorithm 1, the asynchronous production form (capacity planned two "
                         "rounds earlier, top-K admission), or the static block; default: the "
                         "configuration's (Algorithm 1, or static where it turns scheduling off)")
+    p.add_argument("--verify-mode", choices=["compact", "cap-accept"], default="compact",
+                   help="verify the scheduled window (default) or the whole block, committed "
+                        "within the scheduled window")
     p.add_argument("--cpu-sample", type=int, default=48, help="requests in the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -178,6 +181,7 @@ def main():
     log(f"[bench] config {args.config} ({cfg.name}) inputs ready in {time.time() - t0:.1f}s")
     K, W = args.steps, args.warmup
     buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=dev)
+    vmode = args.verify_mode
     ells = torch.empty(K + W, cfg.R, dtype=torch.int32, device=dev)
     ms = torch.empty(K + W, cfg.R, dtype=torch.int32, device=dev)
     Ns = torch.empty(K + W, dtype=torch.int32, device=dev)
@@ -209,11 +213,18 @@ def main():
         else:
             L.prefix_schedule(buf.c, inp["sps"], buf.ell, enabled=(sched == "greedy"), a=buf.a,
                               N_out=buf.N, theta_best=buf.theta)
-        L.pack(buf.x, buf.ell, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N,
+        win = buf.full if vmode == "cap-accept" else buf.ell
+        L.pack(buf.x, win, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N,
                ws=buf.ws)
-        L.verify(buf.ell, buf.cu, inp["target"], 1, buf.x, buf.logp_d, buf.lse_d, inp["U"],
-                 inp["W1"], inp["W2t"], cfg.T, cfg.philox_seed, i, buf.m, buf.tau, buf.emitted,
-                 buf.next_anchor, buf.ws, logp_t=buf.logp_t)
+        if vmode == "cap-accept":
+            L.verify_cap_accept(buf.full, buf.ell, buf.cu, inp["target"], 1, buf.x, buf.logp_d,
+                                buf.lse_d, inp["U"], inp["W1"], inp["W2t"], cfg.T, cfg.philox_seed,
+                                i, buf.m, buf.tau, buf.emitted, buf.next_anchor, buf.ws,
+                                m_full=buf.m_full, logp_t=buf.logp_t)
+        else:
+            L.verify(buf.ell, buf.cu, inp["target"], 1, buf.x, buf.logp_d, buf.lse_d, inp["U"],
+                     inp["W1"], inp["W2t"], cfg.T, cfg.philox_seed, i, buf.m, buf.tau,
+                     buf.emitted, buf.next_anchor, buf.ws, logp_t=buf.logp_t)
         L.pack(buf.emitted, buf.tau, 0, buf.cu_out, buf.flat_out, N_out=buf.N_out, ws=buf.ws)
 
     for i in range(W):
@@ -285,7 +296,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"dspark-round config {args.config} ({cfg.name})", "R": cfg.R,
                    "gamma": cfg.gamma, "V": cfg.V, "rank": cfg.rank, "d": cfg.d, "T": cfg.T,
-                   "scheduler": sched, "parallelism": "single-gpu"},
+                   "scheduler": sched, "verify_mode": vmode, "parallelism": "single-gpu"},
         "hbm_frac_round": hbm_frac_round,
         "round_bytes_alg": bytes_round,
         "emitted_tokens_per_s": sum_tau / t_total,

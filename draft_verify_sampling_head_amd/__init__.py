@@ -8,9 +8,11 @@ missing; there is no other execution path.
 """
 from . import _lib
 from ._lib import (DsparkError, async_schedule, confidence, draft_markov, get_status,
-                   clear_status, pack, prefix_schedule, verify, workspace, workspace_bytes)
+                   clear_status, pack, pack_tiered, prefix_schedule, verify, verify_cap_accept,
+                   workspace, workspace_bytes)
 
 _lib.load()
 
-__all__ = ["DsparkError", "async_schedule", "confidence", "draft_markov", "get_status", "clear_status", "pack",
-           "prefix_schedule", "verify", "workspace", "workspace_bytes"]
+__all__ = ["DsparkError", "async_schedule", "confidence", "draft_markov", "get_status",
+           "clear_status", "pack", "pack_tiered", "prefix_schedule", "verify", "verify_cap_accept",
+           "workspace", "workspace_bytes"]

@@ -19,12 +19,13 @@ LIB_PATH = os.path.join(_PKG, "libdspark.so")
 F32, BF16 = 0, 1
 STATUS = {0: "DSPARK_OK", 1: "DSPARK_E_INVALID", 2: "DSPARK_E_UNSUPPORTED",
           3: "DSPARK_E_WORKSPACE", 4: "DSPARK_E_HIP"}
-FLAG_NONFINITE, FLAG_BAD_LEN, FLAG_BAD_TOKEN, FLAG_BARRIER = 1, 2, 4, 8
+FLAG_NONFINITE, FLAG_BAD_LEN, FLAG_BAD_TOKEN, FLAG_BARRIER, FLAG_TIER = 1, 2, 4, 8, 16
 CHUNK = 128
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
            "dspark_clear_status", "dspark_get_status", "dspark_draft_markov",
            "dspark_confidence", "dspark_prefix_schedule", "dspark_pack", "dspark_verify",
-           "dspark_draft_markov_profiled", "dspark_async_schedule")
+           "dspark_draft_markov_profiled", "dspark_async_schedule", "dspark_pack_tiered",
+           "dspark_verify_cap_accept")
 
 
 class DsparkError(RuntimeError):
@@ -59,6 +60,10 @@ def load():
     L.dspark_prefix_schedule.argtypes = [i32, i32, P, P, i32, i32, P, P, P, P, P]
     L.dspark_async_schedule.argtypes = [i32, i32, P, P, i32, P, P, P, P, P, P, P, P]
     L.dspark_pack.argtypes = [i32, i32, P, P, i32, P, P, P, P, P, P, sz, P]
+    L.dspark_pack_tiered.argtypes = [i32, i32, P, P, i32, P, i32, i32, C.c_int64, P, P, P, P, P,
+                                     P, P, sz, P]
+    L.dspark_verify_cap_accept.argtypes = [i32, i32, i32, i32, f32, u64, u64, P, P, P, P, i32, i32,
+                                           P, P, P, P, i32, P, P, i32, P, P, P, P, P, P, P, sz, P]
     L.dspark_verify.argtypes = [i32, i32, i32, i32, f32, u64, u64, P, P, P, i32, i32, P, P, P, P,
                                 i32, P, P, i32, P, P, P, P, P, P, sz, P]
     for fn in EXPORTS:
@@ -182,6 +187,35 @@ def pack(rows, lens, len_offset, cu, flat, marker_req=None, marker_pos=None, N_o
                               _ptr(marker_req), _ptr(marker_pos), _ptr(N_out), _ptr(ws),
                               0 if ws is None else ws.numel(), _stream(stream))
     _check("dspark_pack", code)
+
+
+def pack_tiered(rows, lens, len_offset, tiers, pad_token, cu, flat, marker_req=None,
+                marker_pos=None, N_out=None, N_pad=None, ws=None, stream=None):
+    """`tiers` is a host sequence of ints; `flat` (and the markers) may be longer
+    than rows.numel(): their length is the slot count."""
+    R, width = rows.shape
+    t = (C.c_int32 * max(1, len(tiers)))(*[int(v) for v in tiers])
+    code = load().dspark_pack_tiered(R, width, _ptr(rows), _ptr(lens), int(len_offset),
+                                     C.cast(t, C.c_void_p), len(tiers), int(pad_token),
+                                     int(flat.numel()), _ptr(cu), _ptr(flat), _ptr(marker_req),
+                                     _ptr(marker_pos), _ptr(N_out), _ptr(N_pad), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(stream))
+    _check("dspark_pack_tiered", code)
+
+
+def verify_cap_accept(ell, cap, cu, target, layout, x, logp_d, lse_d, U, W1, W2t, T, seed, rnd, m,
+                      tau, emitted, next_anchor, ws, m_full=None, logp_t=None, stream=None):
+    R = ell.shape[0]
+    gamma = x.shape[1] - 1
+    V = target.shape[-1]
+    r = 0 if W1 is None else int(W1.shape[1])
+    code = load().dspark_verify_cap_accept(R, gamma, V, r, float(T), seed, rnd, _ptr(ell),
+                                           _ptr(cap), _ptr(cu), _ptr(target), _dt(target),
+                                           int(layout), _ptr(x), _ptr(logp_d), _ptr(lse_d), _ptr(U),
+                                           _dt(U), _ptr(W1), _ptr(W2t), _dt(W1), _ptr(m), _ptr(tau),
+                                           _ptr(emitted), _ptr(next_anchor), _ptr(m_full),
+                                           _ptr(logp_t), _ptr(ws), ws.numel(), _stream(stream))
+    _check("dspark_verify_cap_accept", code)
 
 
 def verify(ell, cu, target, layout, x, logp_d, lse_d, U, W1, W2t, T, seed, rnd, m, tau, emitted,

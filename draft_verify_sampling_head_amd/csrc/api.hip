@@ -182,16 +182,44 @@ dspark_status dspark_pack(int R, int width, const int32_t* rows, const int32_t* 
   p.R = R; p.width = width; p.len_offset = len_offset; p.rows = rows; p.len = len; p.cu = cu;
   p.flat = flat; p.marker_req = marker_req; p.marker_pos = marker_pos; p.N_out = N_out;
   p.status = reinterpret_cast<uint32_t*>(ws);
+  p.slots = (int64_t)R * width;
   return hip_status(launch_pack(p, stream));
 }
 
-dspark_status dspark_verify(int R, int gamma, int V, int r, float T, uint64_t seed, uint64_t round,
-                            const int32_t* ell, const int32_t* cu, const void* target,
-                            dspark_dtype t_dt, int target_layout, const int32_t* x,
-                            const float* logp_d, const float* lse_d, const void* U,
-                            dspark_dtype U_dt, const void* W1, const void* W2t, dspark_dtype W_dt,
-                            int32_t* m, int32_t* tau, int32_t* emitted, int32_t* next_anchor,
-                            float* logp_t, void* ws, size_t ws_bytes, hipStream_t stream) {
+dspark_status dspark_pack_tiered(int R, int width, const int32_t* rows, const int32_t* len,
+                                 int len_offset, const int32_t* tiers, int n_tiers, int pad_token,
+                                 int64_t slots, int32_t* cu, int32_t* flat, int32_t* marker_req,
+                                 int32_t* marker_pos, int32_t* N_out, int32_t* N_pad, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  if (R < 0 || width < 1) return DSPARK_E_INVALID;
+  if (n_tiers < 0 || (n_tiers > 0 && !tiers)) return DSPARK_E_INVALID;
+  if (n_tiers > kMaxTiers) return DSPARK_E_UNSUPPORTED;
+  if (slots < (int64_t)R * width) return DSPARK_E_INVALID;
+  for (int k = 0; k < n_tiers; ++k) {
+    if (tiers[k] < 1 || tiers[k] > slots) return DSPARK_E_INVALID;
+    if (k > 0 && tiers[k] <= tiers[k - 1]) return DSPARK_E_INVALID;
+  }
+  if (R == 0) return DSPARK_OK;
+  if (!rows || !len || !cu || !flat) return DSPARK_E_INVALID;
+  if (slots >= ((int64_t)1 << 31)) return DSPARK_E_UNSUPPORTED;
+  if (ws && (ws_bytes < 256 || !aligned16(ws))) return DSPARK_E_WORKSPACE;
+  PackArgs p{};
+  p.R = R; p.width = width; p.len_offset = len_offset; p.rows = rows; p.len = len; p.cu = cu;
+  p.flat = flat; p.marker_req = marker_req; p.marker_pos = marker_pos; p.N_out = N_out;
+  p.status = reinterpret_cast<uint32_t*>(ws);
+  p.slots = slots; p.ntiers = n_tiers; p.pad_token = pad_token; p.N_pad = N_pad;
+  for (int k = 0; k < n_tiers; ++k) p.tiers[k] = tiers[k];
+  return hip_status(launch_pack(p, stream));
+}
+
+static dspark_status verify_impl(int R, int gamma, int V, int r, float T, uint64_t seed,
+                                 uint64_t round, const int32_t* ell, const int32_t* cu,
+                                 const void* target, dspark_dtype t_dt, int target_layout,
+                                 const int32_t* x, const float* logp_d, const float* lse_d,
+                                 const void* U, dspark_dtype U_dt, const void* W1, const void* W2t,
+                                 dspark_dtype W_dt, int32_t* m, int32_t* tau, int32_t* emitted,
+                                 int32_t* next_anchor, float* logp_t, void* ws, size_t ws_bytes,
+                                 hipStream_t stream, const int32_t* cap, int32_t* m_full) {
   dspark_status s = shape_check(R, gamma, V);
   if (s != DSPARK_OK) return s;
   if ((s = rank_check(r)) != DSPARK_OK) return s;
@@ -210,7 +238,34 @@ dspark_status dspark_verify(int R, int gamma, int V, int r, float T, uint64_t se
   return hip_status(launch_verify(R, gamma, V, r, T, seed, round, ell, cu, target, target_layout,
                                   x, logp_d, lse_d, U, U_dt == DSPARK_BF16, W1, W2t,
                                   W_dt == DSPARK_BF16, m, tau, emitted, next_anchor, logp_t, ws,
-                                  stream));
+                                  stream, cap, m_full));
+}
+
+dspark_status dspark_verify(int R, int gamma, int V, int r, float T, uint64_t seed, uint64_t round,
+                            const int32_t* ell, const int32_t* cu, const void* target,
+                            dspark_dtype t_dt, int target_layout, const int32_t* x,
+                            const float* logp_d, const float* lse_d, const void* U,
+                            dspark_dtype U_dt, const void* W1, const void* W2t, dspark_dtype W_dt,
+                            int32_t* m, int32_t* tau, int32_t* emitted, int32_t* next_anchor,
+                            float* logp_t, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return verify_impl(R, gamma, V, r, T, seed, round, ell, cu, target, t_dt, target_layout, x,
+                     logp_d, lse_d, U, U_dt, W1, W2t, W_dt, m, tau, emitted, next_anchor, logp_t,
+                     ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+dspark_status dspark_verify_cap_accept(int R, int gamma, int V, int r, float T, uint64_t seed,
+                                       uint64_t round, const int32_t* ell, const int32_t* cap,
+                                       const int32_t* cu, const void* target, dspark_dtype t_dt,
+                                       int target_layout, const int32_t* x, const float* logp_d,
+                                       const float* lse_d, const void* U, dspark_dtype U_dt,
+                                       const void* W1, const void* W2t, dspark_dtype W_dt,
+                                       int32_t* m, int32_t* tau, int32_t* emitted,
+                                       int32_t* next_anchor, int32_t* m_full, float* logp_t,
+                                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (R > 0 && !cap) return DSPARK_E_INVALID;
+  return verify_impl(R, gamma, V, r, T, seed, round, ell, cu, target, t_dt, target_layout, x,
+                     logp_d, lse_d, U, U_dt, W1, W2t, W_dt, m, tau, emitted, next_anchor, logp_t,
+                     ws, ws_bytes, stream, cap, m_full);
 }
 
 }  // extern "C"

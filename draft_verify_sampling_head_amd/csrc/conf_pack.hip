@@ -151,13 +151,25 @@ __global__ __launch_bounds__(1024) void k_pack(PackArgs a) {
     }
     carry += tot;
   }
+  // graph-tier padding: the smallest tier that holds the packed total
+  int npad = carry;
+  if (a.ntiers > 0) {
+    int t = -1;
+    for (int k = 0; k < a.ntiers; ++k)
+      if (a.tiers[k] >= carry) { t = a.tiers[k]; break; }
+    if (t < 0) {
+      if (tid == 0) set_flag(a.status, kFlagTier);
+      t = carry;
+    }
+    npad = t;
+  }
   if (tid == 0) {
     a.cu[a.R] = carry;
     if (a.N_out) *a.N_out = carry;
+    if (a.N_pad) *a.N_pad = npad;
   }
-  const int64_t cap = (int64_t)a.R * a.width;
-  for (int64_t q = carry + tid; q < cap; q += 1024) {
-    a.flat[q] = -1;
+  for (int64_t q = carry + tid; q < a.slots; q += 1024) {
+    a.flat[q] = q < npad ? a.pad_token : -1;
     if (a.marker_req) a.marker_req[q] = -1;
     if (a.marker_pos) a.marker_pos[q] = -1;
   }

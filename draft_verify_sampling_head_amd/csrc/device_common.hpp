@@ -23,7 +23,8 @@ enum : uint32_t {
   kTagResidChunk = 4, kTagResidElem = 5, kTagBonusChunk = 6, kTagBonusElem = 7
 };
 
-enum : uint32_t { kFlagNonFinite = 1u, kFlagBadLen = 2u, kFlagBadToken = 4u, kFlagBarrier = 8u };
+enum : uint32_t { kFlagNonFinite = 1u, kFlagBadLen = 2u, kFlagBadToken = 4u, kFlagBarrier = 8u,
+                  kFlagTier = 16u };
 
 // ------------------------------------------------------------------ Philox
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {

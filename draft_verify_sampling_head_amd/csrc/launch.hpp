@@ -63,6 +63,8 @@ struct ConfArgs {
   uint32_t* status;
 };
 
+constexpr int kMaxTiers = 32;
+
 struct PackArgs {
   int R, width, len_offset;
   const int32_t* rows;
@@ -73,6 +75,11 @@ struct PackArgs {
   int32_t* marker_pos;
   int32_t* N_out;
   uint32_t* status;
+  int64_t slots;            // length of flat / markers (>= R * width)
+  int ntiers;               // 0: no tier padding
+  int pad_token;
+  int32_t* N_pad;           // nullable
+  int tiers[kMaxTiers];     // ascending
 };
 
 struct SchedArgs {
@@ -112,6 +119,7 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
                          const int32_t* x, const float* logp_d, const float* lse_d,
                          const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
                          int32_t* m, int32_t* tau, int32_t* emitted, int32_t* next_anchor,
-                         float* logp_t, void* ws, hipStream_t st);
+                         float* logp_t, void* ws, hipStream_t st, const int32_t* cap = nullptr,
+                         int32_t* m_full = nullptr);
 
 }  // namespace dspark

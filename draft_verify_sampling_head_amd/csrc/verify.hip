@@ -14,7 +14,10 @@
 //      evaluates position k (log p_t(x_k), its uniform, the accept test) for
 //      every k at once and a ballot finds the first rejection; then either the
 //      bonus draw (chunked Gumbel-max on the row after the accepted prefix)
-//      or a residual work item.
+//      or a residual work item.  Cap-accept (DeepSpec analysis page, section
+//      5.4, DSpark in SGLang: the verify modes): with a commit window C below
+//      the accepted count m, the first C + 1 tokens of the sequence are
+//      committed, the last being the accepted draft x_{C+1}; no draw is made.
 //   4. residual chunk masses for the listed (request, position) rows: the
 //      draft scores are rebuilt with the Markov bias (MFMA) and combined with
 //      the target row into max(0, p_t - p_d) per chunk.
@@ -45,6 +48,8 @@ struct VerifyArgs {
   int32_t* emitted;
   int32_t* next_anchor;
   float* logp_t;
+  const int32_t* cap;   // nullable: commit window per request (cap-accept)
+  int32_t* m_full;      // nullable: accepted count over the whole window
   const float2* vl;     // [q][nch] chunk (max, scaled sum) of verify rows
   const int* vi;        // [q][nch] chunk argmax (greedy)
   float2* lse_t;        // [q] (raw row max, log-normaliser relative to it)
@@ -118,10 +123,27 @@ __global__ __launch_bounds__(256) void k_verify_scan(VerifyArgs a) {
     }
   }
   __syncthreads();
-  const int m = s_m;
-  const bool rejected = s_rej != 0;
+  int m = s_m;
+  bool rejected = s_rej != 0;
   int y = -1;
-  if (a.greedy) {
+  // cap-accept: when more drafts were accepted than the commit window holds,
+  // the window closes on the accepted draft x_{C+1} (no correction, no bonus)
+  bool closed = false;
+  if (a.cap) {
+    int C = a.cap[i];
+    if (C < 0) { if (tid == 0) set_flag(a.status, kFlagBadLen); C = 0; }
+    if (C > L) C = L;
+    if (tid == 0 && a.m_full) a.m_full[i] = m;
+    if (m > C) {
+      closed = true;
+      m = C;
+      rejected = false;
+    }
+  }
+  if (closed) {
+    y = xi[m + 1];                      // the accepted draft that closes the window
+    if (y < 0 || y >= a.V) y = 0;       // (flagged by the scan above)
+  } else if (a.greedy) {
     // correction: the argmax of the first mismatching row; bonus: of row L
     y = __float_as_int(a.lse_t[q0 + m].y);
     if (y < 0 || y >= a.V) { if (tid == 0) set_flag(a.status, kFlagNonFinite); y = 0; }
@@ -147,7 +169,7 @@ __global__ __launch_bounds__(256) void k_verify_scan(VerifyArgs a) {
   }
   // outputs (a rejected sampled position gets its token from k_resid_pick)
   int32_t* em = a.emitted + (int64_t)i * (a.gamma + 1);
-  const bool have_y = a.greedy || !rejected;
+  const bool have_y = closed || a.greedy || !rejected;
   for (int q = tid; q <= a.gamma; q += 256)
     em[q] = (q < m) ? xi[q + 1] : ((q == m && have_y) ? y : -1);
   if (tid == 0) {
@@ -225,7 +247,8 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
                          const int32_t* x, const float* logp_d, const float* lse_d,
                          const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
                          int32_t* m, int32_t* tau, int32_t* emitted, int32_t* next_anchor,
-                         float* logp_t, void* ws, hipStream_t st) {
+                         float* logp_t, void* ws, hipStream_t st, const int32_t* cap,
+                         int32_t* m_full) {
   const WsLayout L = ws_layout(R, gamma, V);
   char* w = reinterpret_cast<char*>(ws);
   uint32_t* hdr = reinterpret_cast<uint32_t*>(w + L.header);
@@ -254,7 +277,7 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
   a.invT = greedy ? 1.f : 1.f / T; a.greedy = greedy; a.seed = seed; a.round = round;
   a.ell = ell; a.cu = cu; a.target = target; a.x = x; a.logp_d = logp_d; a.lse_d = lse_d;
   a.U = U; a.W1 = W1; a.W2t = W2t; a.m = m; a.tau = tau; a.emitted = emitted;
-  a.next_anchor = next_anchor; a.logp_t = logp_t;
+  a.next_anchor = next_anchor; a.logp_t = logp_t; a.cap = cap; a.m_full = m_full;
   a.vl = rs.L; a.vi = rs.I;
   a.lse_t = reinterpret_cast<float2*>(w + L.lse_t);
   a.rej_count = reinterpret_cast<int32_t*>(hdr + 1);

@@ -2,7 +2,9 @@
 
 draft (Markov head) -> confidence -> prefix schedule (Algorithm 1, static, or
 the asynchronous form with a two-slot capacity ring) -> pack the verify batch
--> verify -> pack the emitted tokens.  This module only allocates the output
+(optionally padded to a graph tier) -> verify (compact: the scheduled window;
+cap-accept: the whole block, committed within the scheduled window) -> pack
+the emitted tokens.  This module only allocates the output
 tensors (torch is the memory allocator) and calls the library in order; the
 scheduled lengths, N, m and tau never leave the device.
 """
@@ -16,7 +18,7 @@ from . import _lib as L
 class RoundBuffers:
     """Outputs and workspace of one round, allocated once and reused."""
 
-    def __init__(self, R, gamma, V, device="cuda"):
+    def __init__(self, R, gamma, V, device="cuda", slots=None):
         i32, f32 = torch.int32, torch.float32
         dev = torch.device(device)
         self.R, self.gamma, self.V = R, gamma, V
@@ -29,10 +31,14 @@ class RoundBuffers:
         self.N = torch.empty(1, dtype=i32, device=dev)
         self.theta = torch.empty(1, dtype=torch.float64, device=dev)
         cap = R * (gamma + 1)
+        vs = max(cap, slots or 0)            # verify-batch slots (a graph tier may exceed cap)
         self.cu = torch.empty(R + 1, dtype=i32, device=dev)
-        self.flat = torch.empty(cap, dtype=i32, device=dev)
-        self.marker_req = torch.empty(cap, dtype=i32, device=dev)
-        self.marker_pos = torch.empty(cap, dtype=i32, device=dev)
+        self.flat = torch.empty(vs, dtype=i32, device=dev)
+        self.marker_req = torch.empty(vs, dtype=i32, device=dev)
+        self.marker_pos = torch.empty(vs, dtype=i32, device=dev)
+        self.N_pad = torch.empty(1, dtype=i32, device=dev)
+        self.full = torch.full((R,), gamma, dtype=i32, device=dev)
+        self.m_full = torch.empty(R, dtype=i32, device=dev)
         self.m = torch.empty(R, dtype=i32, device=dev)
         self.tau = torch.empty(R, dtype=i32, device=dev)
         self.emitted = torch.empty(R, gamma + 1, dtype=i32, device=dev)
@@ -63,13 +69,17 @@ class CapacityRing:
 
 
 def run_round(inp, buf: RoundBuffers, T, seed, rnd, scheduler=True, layout=1, sts_T=None,
-              stream=None, ring: CapacityRing = None):
+              stream=None, ring: CapacityRing = None, verify_mode="compact", tiers=None,
+              pad_token=0):
     """Enqueue one full round on `stream` (default: torch's current stream).
 
     `inp` holds U, W1, W2t, x0, h, w, sps and target (dense [R][gamma+1][V] for
     layout 1; packed rows in verify order for layout 0).  `scheduler`: True =
     Algorithm 1, False = static block, "async" = the asynchronous scheduler
-    with capacities from `ring`."""
+    with capacities from `ring`.  `verify_mode` "cap-accept" packs and verifies
+    the whole block and commits within the scheduled window.  `tiers` (host
+    ints, ascending) pads the verify batch to the smallest tier that holds it
+    (`buf.N_pad`; the buffers need slots >= the largest tier)."""
     L.draft_markov(inp["U"], inp["W1"], inp["W2t"], inp["x0"], T, seed, rnd, buf.x, buf.logp_d,
                    buf.lse_d, buf.ws, stream=stream)
     L.confidence(inp["h"], inp["W1"], inp["w"], buf.x, buf.c, sts_T=sts_T, V=buf.V, stream=stream)
@@ -80,10 +90,21 @@ def run_round(inp, buf: RoundBuffers, T, seed, rnd, scheduler=True, layout=1, st
     else:
         L.prefix_schedule(buf.c, inp["sps"], buf.ell, enabled=bool(scheduler), a=buf.a,
                           N_out=buf.N, theta_best=buf.theta, stream=stream)
-    L.pack(buf.x, buf.ell, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N, ws=buf.ws,
-           stream=stream)
-    L.verify(buf.ell, buf.cu, inp["target"], layout, buf.x, buf.logp_d, buf.lse_d, inp["U"],
-             inp["W1"], inp["W2t"], T, seed, rnd, buf.m, buf.tau, buf.emitted, buf.next_anchor,
-             buf.ws, logp_t=buf.logp_t, stream=stream)
+    win = buf.full if verify_mode == "cap-accept" else buf.ell
+    if tiers:
+        L.pack_tiered(buf.x, win, 1, tiers, pad_token, buf.cu, buf.flat, buf.marker_req,
+                      buf.marker_pos, buf.N, buf.N_pad, ws=buf.ws, stream=stream)
+    else:
+        L.pack(buf.x, win, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N, ws=buf.ws,
+               stream=stream)
+    if verify_mode == "cap-accept":
+        L.verify_cap_accept(buf.full, buf.ell, buf.cu, inp["target"], layout, buf.x, buf.logp_d,
+                            buf.lse_d, inp["U"], inp["W1"], inp["W2t"], T, seed, rnd, buf.m,
+                            buf.tau, buf.emitted, buf.next_anchor, buf.ws, m_full=buf.m_full,
+                            logp_t=buf.logp_t, stream=stream)
+    else:
+        L.verify(buf.ell, buf.cu, inp["target"], layout, buf.x, buf.logp_d, buf.lse_d, inp["U"],
+                 inp["W1"], inp["W2t"], T, seed, rnd, buf.m, buf.tau, buf.emitted, buf.next_anchor,
+                 buf.ws, logp_t=buf.logp_t, stream=stream)
     L.pack(buf.emitted, buf.tau, 0, buf.cu_out, buf.flat_out, N_out=buf.N_out, ws=buf.ws,
            stream=stream)

@@ -8,6 +8,8 @@
  *  [P1] backyes.github.io "MTP algorithm survey", section 2.2 (rejection sampling).
  *  [P2] bevisy.github.io DeepSpec analysis, section 2.2 (DFlash = rank 0).
  *  [P4] modelscope/CSDN DSpark article, section 3.3 (flatten + marker tensors).
+ *       Section 5.4 of that page (DSpark in SGLang): verify modes static /
+ *       compact / cap-accept, ragged verify padded to captured graph tiers.
  *
  * Conventions shared by every entry point
  *  - Every pointer is a DEVICE pointer unless marked (host).  The caller owns
@@ -62,6 +64,8 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 #define DSPARK_FLAG_BAD_TOKEN 4u   /* a token id outside [0, V) was read           */
 #define DSPARK_FLAG_BARRIER   8u   /* a grid barrier of the persistent draft gave
                                       up waiting (its outputs are then invalid)   */
+#define DSPARK_FLAG_TIER     16u   /* a tiered pack's total exceeded every tier
+                                      (N_pad = N)                                 */
 
 /* (host) Bytes of workspace every entry point below needs for these sizes. */
 size_t dspark_workspace_bytes(int R, int gamma, int V, int r, int d);
@@ -229,6 +233,25 @@ dspark_status dspark_pack(int R, int width, const int32_t* rows, const int32_t* 
                           hipStream_t stream);
 
 /*
+ * Ragged pack padded to a captured graph tier ([P2] 5.4, DSpark in SGLang: ragged verify packs the
+ * requests into one compact buffer whose total is rounded up to a captured
+ * CUDA-graph tier, so a fixed graph replays a batch of any smaller size).
+ * The pack is dspark_pack's; then N_pad = the smallest tier >= N, or N when
+ * no tier holds it (DSPARK_FLAG_TIER, when ws != NULL).  Slots [N, N_pad)
+ * hold pad_token with markers -1; slots [N_pad, slots) hold -1.
+ *   tiers      (host) [n_tiers] strictly ascending, each in [1, slots];
+ *              copied into the launch (at most 32)
+ *   slots      length of flat / marker_req / marker_pos, >= R * width
+ *   N_pad      out nullable (device scalar)
+ *   other arguments as for dspark_pack
+ */
+dspark_status dspark_pack_tiered(int R, int width, const int32_t* rows, const int32_t* len,
+                                 int len_offset, const int32_t* tiers, int n_tiers, int pad_token,
+                                 int64_t slots, int32_t* cu, int32_t* flat, int32_t* marker_req,
+                                 int32_t* marker_pos, int32_t* N_out, int32_t* N_pad, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/*
  * Lossless rejection-sampling verification ([P3] Background: x_k accepted with
  * probability min(1, p_t(x_k) / p_d(x_k)), left to right, the first rejection
  * drops the rest; [P1] 2.2: at the first rejection a token is resampled from
@@ -259,6 +282,34 @@ dspark_status dspark_verify(int R, int gamma, int V, int r, float T,
                             const void* W1, const void* W2t, dspark_dtype W_dt,
                             int32_t* m, int32_t* tau, int32_t* emitted, int32_t* next_anchor,
                             float* logp_t, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Cap-accept verification ([P2] 5.4, DSpark in SGLang, the verify modes:
+ * verify the whole window, commit only the scheduler's truncated window; used
+ * to observe the acceptance a schedule leaves on the table).  Request i is
+ * verified over its window ell[i] exactly as by dspark_verify (same random
+ * streams, same accept tests), giving m_full accepted drafts.  With
+ * C = cap[i] clamped to [0, ell[i]] (a negative cap is flagged
+ * DSPARK_FLAG_BAD_LEN), the committed sequence is the first min(m_full, C) + 1
+ * tokens of the verification's sequence: when m_full > C those are
+ * x_1..x_{C+1}, the last being an accepted draft, and no correction or bonus
+ * token is drawn; otherwise the outputs equal dspark_verify's.  A prefix of a
+ * lossless sequence, so the committed tokens keep the target's law.
+ *   ell      [R] verified window (typically gamma: the static block)
+ *   cap      [R] commit window (typically the scheduler's ell)
+ *   m, tau, emitted, next_anchor  the committed result (m = min(m_full, C))
+ *   m_full   out nullable [R] accepted drafts over the whole window
+ *   other arguments as for dspark_verify (logp_t covers the whole window)
+ */
+dspark_status dspark_verify_cap_accept(int R, int gamma, int V, int r, float T, uint64_t seed,
+                                       uint64_t round, const int32_t* ell, const int32_t* cap,
+                                       const int32_t* cu, const void* target, dspark_dtype t_dt,
+                                       int target_layout, const int32_t* x, const float* logp_d,
+                                       const float* lse_d, const void* U, dspark_dtype U_dt,
+                                       const void* W1, const void* W2t, dspark_dtype W_dt,
+                                       int32_t* m, int32_t* tau, int32_t* emitted,
+                                       int32_t* next_anchor, int32_t* m_full, float* logp_t,
+                                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -144,3 +144,28 @@ def check_verify(rep, ell, cu, target, layout, x, dev_lp, dev_lse, U, W1, W2t, T
             if e.max() > TOL_LOG:
                 rep.err(f"verify logp_t max err {e.max():.3g}")
     return m, tau, em, na
+
+
+def check_verify_cap_accept(rep, ell, cap, cu, target, layout, x, dev_lp, dev_lse, U, W1, W2t, T,
+                            seed, rnd, dev_m, dev_tau, dev_em, dev_na, dev_mfull, reqs):
+    """Cap-accept verify: the committed result and the whole-window accepted
+    count, bit-exact except requests whose oracle margin is below MARGIN."""
+    m, tau, em, na, lpt, mg, mfull = O.verify_cap_accept(ell, cap, cu, target, layout, x,
+                                                         dev_lp.astype(np.float64),
+                                                         dev_lse.astype(np.float64), U, W1, W2t,
+                                                         T, seed, rnd, req_ids=reqs)
+    R = ell.size
+    rep.compared += R
+    for r in range(R):
+        same = (m[r] == dev_m[r] and tau[r] == dev_tau[r] and na[r] == dev_na[r]
+                and np.array_equal(em[r], dev_em[r])
+                and (dev_mfull is None or mfull[r] == dev_mfull[r]))
+        if not same:
+            if mg[r] < MARGIN:
+                rep.flagged += 1
+            else:
+                rid = reqs[r] if reqs is not None else r
+                rep.err(f"cap-accept req {rid}: gpu m={dev_m[r]} y={dev_na[r]} oracle m={m[r]} "
+                        f"y={na[r]} m_full gpu {None if dev_mfull is None else dev_mfull[r]} "
+                        f"oracle {mfull[r]} margin {mg[r]:.3g}")
+    return m, mfull

@@ -102,6 +102,22 @@ def test_confidence_schedule_pack_verify_checks():
     assert ver(T=-1.0) == INVALID
     assert ver(ws_bytes=10) == WORKSPACE
     assert ver(ell=None) == INVALID
+    capv = lambda cap=FAKE, R=4: lib.dspark_verify_cap_accept(
+        R, 3, 100, 0, 1.0, 0, 0, FAKE, cap, FAKE, FAKE, 1, 1, FAKE, FAKE, FAKE, FAKE, 1, None,
+        None, 1, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 30, None)
+    assert capv(cap=None) == INVALID
+    assert capv(cap=None, R=0) == OK
+    tiers = (C.c_int32 * 3)(4, 8, 8)
+    ptier = lambda n=3, slots=16, t=tiers, R=4: lib.dspark_pack_tiered(
+        R, 3, FAKE, FAKE, 0, C.cast(t, C.c_void_p), n, 0, slots, FAKE, FAKE, None, None,
+        None, None, None, 0, None)
+    assert ptier() == INVALID                            # tiers not strictly ascending
+    assert ptier(n=2, slots=11) == INVALID               # slots < R * width
+    assert ptier(n=2, slots=7) == INVALID
+    assert ptier(n=33) == UNSUPPORTED
+    big = (C.c_int32 * 2)(4, 20)
+    assert ptier(n=2, t=big) == INVALID                  # a tier beyond the slots
+    assert ptier(n=-1) == INVALID
 
 
 def test_synthetic_configs_shapes():
@@ -119,7 +135,7 @@ def test_synthetic_configs_shapes():
 
 
 @pytest.mark.parametrize("fn", ["draft_markov", "confidence", "prefix_schedule", "async_schedule",
-                                "pack", "verify"])
+                                "pack", "pack_tiered", "verify", "verify_cap_accept"])
 def test_binding_names_match_abi(fn):
     assert callable(getattr(D, fn))
     assert f"dspark_{fn}" in declared()

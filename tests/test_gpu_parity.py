@@ -363,7 +363,153 @@ def test_async_scheduler_two_round_pipeline():
         hist.append(Kp)
 
 
+# ------------------------------------------------------- verify: cap-accept
+CAP = [
+    (2, dict(R=40, gamma=5, V=3000, d=64), "sched", 1),        # bf16, rank 256, sampled
+    (2, dict(R=33, gamma=6, V=2600, d=64, rank=0), "random", 1),
+    (1, dict(R=33, gamma=7, V=5000, d=128), "random", 1),      # greedy
+    (0, {}, "random", 1),                                       # fp32
+    (2, dict(R=24, gamma=4, V=1800, d=64, T=0.3), "sched", 0),  # packed target rows
+    (3, dict(R=70, gamma=6, V=2500, d=64), "sched", 1),
+]
+
+
+@pytest.mark.parametrize("base,over,capk,layout", CAP, ids=[f"cap{i}" for i in range(len(CAP))])
+def test_cap_accept_parity(base, over, capk, layout):
+    """Whole-block verification committed within a window: the scheduler's
+    ell (Algorithm 1) or random windows, against the oracle's cap-accept."""
+    cfg = synth.scaled(synth.config(base), **over) if over else synth.config(base)
+    print(f"[case] cap-accept {cfg.name} R={cfg.R} g={cfg.gamma} V={cfg.V} r={cfg.rank} T={cfg.T} "
+          f"cap={capk} layout={layout}", flush=True)
+    inp = synth.make_inputs(cfg, device="cpu")
+    g = to_dev(inp)
+    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV)
+    D.draft_markov(g["U"], g["W1"], g["W2t"], g["x0"], cfg.T, cfg.philox_seed, 2, buf.x,
+                   buf.logp_d, buf.lse_d, buf.ws)
+    D.confidence(g["h"], g["W1"], g["w"], buf.x, buf.c, V=cfg.V)
+    D.prefix_schedule(buf.c, g["sps"], buf.ell, N_out=buf.N)
+    full = torch.full((cfg.R,), cfg.gamma, dtype=torch.int32, device=DEV)
+    D.pack(buf.x, full, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N, ws=buf.ws)
+    if capk == "sched":
+        cap = buf.ell.clone()
+    else:
+        rng = np.random.default_rng(cfg.R)
+        cap = torch.as_tensor(rng.integers(0, cfg.gamma + 3, cfg.R).astype(np.int32), device=DEV)
+    tgt = g["target"]
+    if layout == 0:
+        torch.cuda.synchronize()
+        Np = int(n(buf.N)[0])
+        tgt = g["target"][buf.marker_req[:Np].long(), buf.marker_pos[:Np].long()].contiguous()
+    mfull = torch.empty(cfg.R, dtype=torch.int32, device=DEV)
+    D.verify_cap_accept(full, cap, buf.cu, tgt, layout, buf.x, buf.logp_d, buf.lse_d, g["U"],
+                        g["W1"], g["W2t"], cfg.T, cfg.philox_seed, 2, buf.m, buf.tau, buf.emitted,
+                        buf.next_anchor, buf.ws, m_full=mfull, logp_t=buf.logp_t)
+    torch.cuda.synchronize()
+    status = D.get_status(buf.ws)
+    rep = PC.Report()
+    W1, W2t = f(inp["W1"]), f(inp["W2t"])
+    tg = f(tgt) if layout == 0 else f(inp["target"])
+    m, mf = PC.check_verify_cap_accept(rep, n(full), n(cap), n(buf.cu), tg, layout, n(buf.x),
+                                       n(buf.logp_d), n(buf.lse_d), f(inp["U"]), W1, W2t, cfg.T,
+                                       cfg.philox_seed, 2, n(buf.m), n(buf.tau), n(buf.emitted),
+                                       n(buf.next_anchor), n(mfull), None)
+    print(f"  {rep.summary()} status={status} sum_m={int(m.sum())} sum_m_full={int(mf.sum())} "
+          f"closed_by_draft={int((mf > np.minimum(n(cap), cfg.gamma)).sum())}", flush=True)
+    assert status == 0, f"device flags {status}"
+    assert rep.ok(), rep.summary()
+    assert (mf >= m).all()
+
+
+def test_round_driver_async_cap_accept_tiers():
+    """The round driver with the production options together: asynchronous
+    scheduler (two-slot ring), whole-block verify committed within the window,
+    verify batch padded to a tier; every stage against the oracle."""
+    import oracle as O
+    cfg = synth.scaled(synth.config(2), R=48, gamma=5, V=2600, d=64)
+    inp = synth.make_inputs(cfg, device="cpu")
+    g = to_dev(inp)
+    tiers = [64, 128, 192, 256, 320]
+    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV, slots=320)
+    nmax = g["sps"].numel() - 1
+    ring = RD.CapacityRing(cfg.R, cfg.gamma, nmax, device=DEV)
+    hist = [min(cfg.R * (cfg.gamma + 1), nmax)] * 2
+    for rnd in range(4):
+        print(f"[case] driver round {rnd}", flush=True)
+        D.clear_status(buf.ws)
+        RD.run_round(g, buf, cfg.T, cfg.philox_seed, rnd, scheduler="async", ring=ring,
+                     verify_mode="cap-accept", tiers=tiers, pad_token=7)
+        torch.cuda.synchronize()
+        assert D.get_status(buf.ws) == 0
+        c = n(buf.c)
+        e, _, Ne, _, Kp, _ = O.async_schedule(c, n(g["sps"]), hist[rnd])
+        hist.append(Kp)
+        np.testing.assert_array_equal(n(buf.ell), e)
+        pk = O.pack_tiered(n(buf.x), np.full(cfg.R, cfg.gamma + 1), tiers, 7, slots=320)
+        np.testing.assert_array_equal(n(buf.flat), pk[1])
+        assert int(n(buf.N)[0]) == pk[4] and int(n(buf.N_pad)[0]) == pk[5]
+        rep = PC.Report()
+        PC.check_verify_cap_accept(rep, n(buf.full), e, None, f(inp["target"]), 1, n(buf.x),
+                                   n(buf.logp_d), n(buf.lse_d), f(inp["U"]), f(inp["W1"]),
+                                   f(inp["W2t"]), cfg.T, cfg.philox_seed, rnd, n(buf.m),
+                                   n(buf.tau), n(buf.emitted), n(buf.next_anchor), n(buf.m_full),
+                                   None)
+        assert rep.ok(), rep.summary()
+        PC.check_pack(rep, n(buf.emitted), n(buf.tau), n(buf.cu_out), n(buf.flat_out), None, None,
+                      n(buf.N_out)[0], "emitted")
+        assert rep.ok(), rep.summary()
+
+
+def test_cap_accept_negative_window_is_flagged():
+    cfg = synth.scaled(synth.config(2), R=8, gamma=3, V=700, d=16)
+    inp = synth.make_inputs(cfg, device="cpu")
+    g = to_dev(inp)
+    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV)
+    D.clear_status(buf.ws)
+    D.draft_markov(g["U"], g["W1"], g["W2t"], g["x0"], cfg.T, 1, 0, buf.x, buf.logp_d, buf.lse_d,
+                   buf.ws)
+    full = torch.full((cfg.R,), cfg.gamma, dtype=torch.int32, device=DEV)
+    D.pack(buf.x, full, 1, buf.cu, buf.flat, ws=buf.ws)
+    cap = torch.full((cfg.R,), -3, dtype=torch.int32, device=DEV)
+    D.verify_cap_accept(full, cap, buf.cu, g["target"], 1, buf.x, buf.logp_d, buf.lse_d, g["U"],
+                        g["W1"], g["W2t"], cfg.T, 1, 0, buf.m, buf.tau, buf.emitted,
+                        buf.next_anchor, buf.ws)
+    torch.cuda.synchronize()
+    assert D.get_status(buf.ws) & D._lib.FLAG_BAD_LEN
+    assert (n(buf.m) == 0).all() and (n(buf.tau) == 1).all()
+
+
 # ------------------------------------------------------------- stage: pack
+def test_pack_tiered_bitexact():
+    import oracle as O
+    rng = np.random.default_rng(2)
+    for R, width, off, tiers, extra in [(300, 17, 1, [512, 1024, 2048, 4096, 8192], 100),
+                                        (5, 4, 0, [1, 2, 4, 8, 16], 0),
+                                        (2000, 9, 0, [64, 128], 7),       # no tier holds N
+                                        (1, 1, 0, [1], 0),
+                                        (700, 6, 1, list(range(128, 4200, 128)), 0)]:
+        slots = R * width + extra
+        tiers = [t for t in tiers if t <= slots][:32]       # every tier fits the slots
+        rows = rng.integers(0, 100000, (R, width)).astype(np.int32)
+        lens = rng.integers(0, width + 1 - off, R).astype(np.int32)
+        rd, ld = torch.as_tensor(rows, device=DEV), torch.as_tensor(lens, device=DEV)
+        cu = torch.empty(R + 1, dtype=torch.int32, device=DEV)
+        flat = torch.empty(slots, dtype=torch.int32, device=DEV)
+        mr, mp = torch.empty_like(flat), torch.empty_like(flat)
+        N = torch.empty(1, dtype=torch.int32, device=DEV)
+        Np = torch.empty(1, dtype=torch.int32, device=DEV)
+        ws = D.workspace(1, 1, 1, device=DEV)
+        D.clear_status(ws)
+        D.pack_tiered(rd, ld, off, tiers, 99, cu, flat, mr, mp, N, Np, ws=ws)
+        torch.cuda.synchronize()
+        e = O.pack_tiered(rows, lens + off, tiers, 99, slots=slots)
+        np.testing.assert_array_equal(n(cu), e[0])
+        np.testing.assert_array_equal(n(flat), e[1])
+        np.testing.assert_array_equal(n(mr), e[2])
+        np.testing.assert_array_equal(n(mp), e[3])
+        assert int(n(N)[0]) == e[4] and int(n(Np)[0]) == e[5]
+        assert bool(D.get_status(ws) & D._lib.FLAG_TIER) == e[6]
+
+
 def test_pack_bitexact():
     import oracle as O
     rng = np.random.default_rng(1)
