@@ -62,6 +62,10 @@ def lib():
         L.orc_prefix_schedule.restype = i32
         L.orc_async_schedule.argtypes = [i32, i32, P, P, i32, i32, P, P, P, P, P, P]
         L.orc_async_schedule.restype = i32
+        L.orc_acceptance_rate.argtypes = [i32, i32, i64, i32, f64, P, P, P, P, P, P, P]
+        L.orc_acceptance_rate.restype = i32
+        L.orc_sts_fit.argtypes = [i32, i32, P, P, P, i32, i32, P, P, P, P]
+        L.orc_sts_fit.restype = i32
         L.orc_pack.argtypes = [i32, i32, P, P, P, P, P, P, P]
         L.orc_verify.argtypes = [i32, i32, i64, i32, f64, u64, u64, P, P, P, i32, P, P, P,
                                  P, P, P, P, P, P, P, P, P, P, P]
@@ -222,6 +226,36 @@ def pack(rows, lens):
     N = np.zeros(1, np.int32)
     lib().orc_pack(R, width, _p(rows), _p(lens), _p(cu), _p(flat), _p(mr), _p(mp), _p(N))
     return cu, flat, mr, mp, int(N[0])
+
+
+def acceptance_rate(target, x, U, W1, W2t, T):
+    """c*_k = sum_v min(p_d^k, p_t^k) for every request and position (dense
+    target [R][gamma+1][V]).  Returns (c_star [R][gamma], margin)."""
+    target = _f32(target)
+    R, g1, V = target.shape
+    gamma = g1 - 1
+    rank = 0 if W1 is None else int(W1.shape[1])
+    cs = np.zeros((R, gamma))
+    mg = np.zeros((R, gamma))
+    rc = lib().orc_acceptance_rate(R, gamma, V, rank, float(T), _p(target), _p(_i32(x)),
+                                   _p(_f32(U)), _p(_f32(W1)), _p(_f32(W2t)), _p(cs), _p(mg))
+    assert rc == 0, rc
+    return cs, mg
+
+
+def sts_fit(z, m, grid, nbins=15, force_t=None):
+    """Sequential temperature scaling on held-out logits z [n][gamma] and
+    accepted counts m [n].  Returns (t [gamma] float32, ece [gamma], margin)."""
+    z = _f32(z)
+    n, gamma = z.shape
+    grid = _f32(grid)
+    t = np.zeros(gamma, np.float32)
+    ece = np.zeros(gamma)
+    mg = np.zeros(gamma)
+    rc = lib().orc_sts_fit(n, gamma, _p(z), _p(_i32(m)), _p(grid), grid.size, int(nbins),
+                           _p(None if force_t is None else _f32(force_t)), _p(t), _p(ece), _p(mg))
+    assert rc == 0, rc
+    return t, ece, mg
 
 
 def pack_tiered(rows, lens, tiers, pad_token, slots=None):

@@ -647,4 +647,105 @@ int orc_verify(int R, int gamma, int64_t V, int rank, double T, uint64_t seed, u
     return 0;
 }
 
+// ------------------------------------------- single-step acceptance rate ---
+// The confidence head's supervision target ([P3] Method details, confidence
+// head): c*_k = 1 - TV(p_d^k, p_t^k) = sum_v min(p_d^k(v), p_t^k(v)), the
+// probability that the rejection test accepts position k given the prefix.
+// For every request i and k = 1..gamma: p_d^k is the tempered draft
+// distribution of position k given x_{k-1} (scores (U_k + W1[x_{k-1}] W2) / T,
+// normalised here), p_t^k = softmax(row / T) of the dense target row
+// i*(gamma+1) + k-1 (verify row k-1, input x_{k-1}).
+// T == 0 (point masses): c*_k = 1 if x_k (the greedy draft's pick) is the first
+// argmax of the target row, else 0; the argmax is decided on float32 values
+// and its gap is the margin.
+// Out: c_star [R][gamma]; margin [R][gamma] (nullable; +inf when T > 0).
+int orc_acceptance_rate(int R, int gamma, int64_t V, int rank, double T, const float* target,
+                        const int32_t* x, const float* U, const float* W1, const float* W2t,
+                        double* c_star, double* margin) {
+    if (R < 0 || gamma < 1 || V < 1 || !(T >= 0.0)) return 1;
+    std::vector<double> s(V), lt(V);
+    for (int i = 0; i < R; ++i) {
+        const int32_t* xi = x + (int64_t)i * (gamma + 1);
+        for (int k = 1; k <= gamma; ++k) {
+            const float* t = target + ((int64_t)i * (gamma + 1) + (k - 1)) * V;
+            double cs, mg = POS_INF;
+            if (T > 0.0) {
+                markov_scores(V, rank, U + ((int64_t)i * gamma + (k - 1)) * V, W1, W2t, xi[k - 1],
+                              s.data());
+                for (int64_t v = 0; v < V; ++v) { s[v] /= T; lt[v] = (double)t[v] / T; }
+                const double lse_d = logsumexp(s.data(), V);
+                const double lse_t = logsumexp(lt.data(), V);
+                cs = 0.0;
+                for (int64_t v = 0; v < V; ++v)
+                    cs += std::min(std::exp(s[v] - lse_d), std::exp(lt[v] - lse_t));
+            } else {
+                for (int64_t v = 0; v < V; ++v) lt[v] = (double)t[v];
+                const int64_t am = argmax_f32_decision(lt.data(), V, &mg);
+                cs = (xi[k] == am) ? 1.0 : 0.0;
+            }
+            c_star[(int64_t)i * gamma + (k - 1)] = cs;
+            if (margin) margin[(int64_t)i * gamma + (k - 1)] = mg;
+        }
+    }
+    return 0;
+}
+
+// ------------------------------------------------------------- STS fit ---
+// Sequential temperature scaling ([P3] Method details, post-hoc calibration;
+// [P1] 4.2.3).  Held-out data: n blocks with raw confidence logits z [n][gamma]
+// (c_k = sigmoid(z_k / t_k)) and the number m [n] of drafts the target
+// accepted; the label of position k is "the prefix 1..k was accepted",
+// y_k = [m >= k].  Left to right, k = 1..gamma, earlier temperatures fixed:
+// for every candidate t of the grid (in its order),
+//   A_k(t) = A_{k-1} * sigmoid(z_k / t)          (A_0 = 1; cumulative product)
+//   ECE(t) = (1/n) sum_b | sum_{i in bin b} (A_k,i - y_k,i) |
+// over nbins equal-width bins of [0, 1], bin = min(floor(A nbins), nbins - 1)
+// (the expected calibration error: bin weight n_b/n times |mean A - mean y|);
+// t_k = the first grid value with the smallest ECE.  All in double.
+// force_t (nullable, [gamma]): entries > 0 replace the chosen temperature
+// (lock-step checking); the ECE reported is then that of the forced value.
+// Out: t [gamma] (float, the grid's value); ece [gamma]; margin [gamma] = the
+// smaller of (second-smallest ECE - smallest ECE) and the closest distance of
+// any A nbins to a bin edge (both nullable-safe: margin may be null).
+int orc_sts_fit(int n, int gamma, const float* z, const int32_t* m, const float* grid, int G,
+                int nbins, const float* force_t, float* t_out, double* ece_out, double* margin) {
+    if (n < 1 || gamma < 1 || G < 1 || nbins < 1) return 1;
+    std::vector<double> A(n, 1.0), Ak(n), d(nbins);
+    for (int k = 1; k <= gamma; ++k) {
+        double best = POS_INF, second = POS_INF, edge = POS_INF;
+        int gbest = 0;
+        std::vector<double> eces(G);
+        for (int g = 0; g < G; ++g) {
+            const double t = (double)grid[g];
+            std::fill(d.begin(), d.end(), 0.0);
+            for (int i = 0; i < n; ++i) {
+                const double c = 1.0 / (1.0 + std::exp(-(double)z[(int64_t)i * gamma + (k - 1)] / t));
+                const double a = A[i] * c;
+                const double pos = a * nbins;
+                int b = (int)std::floor(pos);
+                if (b > nbins - 1) b = nbins - 1;
+                if (b < 0) b = 0;
+                edge = std::min(edge, std::fabs(pos - std::nearbyint(pos)));
+                d[b] += a - (m[i] >= k ? 1.0 : 0.0);
+            }
+            double e = 0.0;
+            for (int b = 0; b < nbins; ++b) e += std::fabs(d[b]);
+            e /= n;
+            eces[g] = e;
+            if (e < best) { second = best; best = e; gbest = g; }
+            else if (e < second) second = e;
+        }
+        if (force_t && force_t[k - 1] > 0.0f) {
+            for (int g = 0; g < G; ++g) if (grid[g] == force_t[k - 1]) { gbest = g; break; }
+        }
+        const double t = (double)grid[gbest];
+        for (int i = 0; i < n; ++i)
+            A[i] *= 1.0 / (1.0 + std::exp(-(double)z[(int64_t)i * gamma + (k - 1)] / t));
+        t_out[k - 1] = grid[gbest];
+        if (ece_out) ece_out[k - 1] = eces[gbest];
+        if (margin) margin[k - 1] = std::min(second - best, edge);
+    }
+    return 0;
+}
+
 }  // extern "C"

@@ -745,3 +745,130 @@ def test_residual_row_closed_form():
     q, tot = O.residual_row(t, t.astype(np.float64), special.logsumexp(t.astype(np.float64)), 1.0)
     assert tot < 1e-15
     np.testing.assert_allclose(q, special.softmax(t.astype(np.float64)), atol=1e-15)
+
+
+# ------------------------------------------------ acceptance rate c* --
+def test_acceptance_rate_closed_forms():
+    rng = np.random.default_rng(30)
+    R, g, V = 3, 4, 500
+    U = rng.normal(0, 2, (R, g, V)).astype(np.float32)
+    x = np.concatenate([rng.integers(0, V, (R, 1)), rng.integers(0, V, (R, g))], 1)
+    # rank 0, target row k-1 = U_k: identical distributions, c* = 1
+    tgt = np.concatenate([U, U[:, :1]], axis=1)
+    cs, _ = O.acceptance_rate(tgt, x, U, None, None, 1.0)
+    np.testing.assert_allclose(cs, 1.0, rtol=0, atol=1e-12)
+    # disjoint supports: c* = 0
+    U2 = U.copy()
+    U2[:, :, : V // 2] = -1e4
+    tgt2 = np.full((R, g + 1, V), -1e4, np.float32)
+    tgt2[:, :, : V // 2] = U[:, :1, : V // 2]            # target mass where the draft has none
+    cs, _ = O.acceptance_rate(tgt2, x, U2, None, None, 0.8)
+    assert np.abs(cs).max() == 0.0
+    # rank 16: 1 - TV by scipy softmax of an independently computed bias
+    rank = 16
+    W1 = rng.normal(0, 0.4, (V, rank)).astype(np.float32)
+    W2t = rng.normal(0, 0.4, (V, rank)).astype(np.float32)
+    tgt3 = (np.concatenate([U, U[:, :1]], 1) + rng.normal(0, 1, (R, g + 1, V))).astype(np.float32)
+    for T in [1.0, 0.6]:
+        cs, _ = O.acceptance_rate(tgt3, x, U, W1, W2t, T)
+        for i in range(R):
+            for k in range(1, g + 1):
+                bias = W2t.astype(np.float64) @ W1[x[i, k - 1]].astype(np.float64)
+                pd = special.softmax((U[i, k - 1].astype(np.float64) + bias) / T)
+                pt = special.softmax(tgt3[i, k - 1].astype(np.float64) / T)
+                assert abs(cs[i, k - 1] - (1 - 0.5 * np.abs(pd - pt).sum())) < 1e-12
+    # T = 0: x_k against the target row's argmax
+    cs, mg = O.acceptance_rate(tgt3, x, U, W1, W2t, 0.0)
+    ref = (x[:, 1:] == tgt3[:, :g].argmax(-1)).astype(np.float64)
+    np.testing.assert_array_equal(cs, ref)
+    x2 = x.copy()
+    x2[:, 1:] = tgt3[:, :g].argmax(-1)
+    assert (O.acceptance_rate(tgt3, x2, U, W1, W2t, 0.0)[0] == 1.0).all()
+
+
+def test_acceptance_rate_is_the_verify_acceptance_probability():
+    """c*_1 is the probability that the oracle's rejection test accepts x_1."""
+    rng = np.random.default_rng(31)
+    V, rank, n = 300, 16, 40000
+    Uk = rng.normal(0, 2, V).astype(np.float32)
+    W1 = rng.normal(0, 0.3, (V, rank)).astype(np.float32)
+    W2t = rng.normal(0, 0.3, (V, rank)).astype(np.float32)
+    t1 = (Uk + rng.normal(0, 0.8, V)).astype(np.float32)
+    U = np.broadcast_to(Uk, (n, 1, V))
+    x, lp, lse, _ = O.draft_markov(U, W1, W2t, np.full(n, 7), 1.0, seed=3)
+    tgt = np.broadcast_to(np.stack([t1, t1]), (n, 2, V))
+    m, *_ = O.verify(np.ones(n, np.int32), None, tgt, 1, x, lp, lse, U, W1, W2t, 1.0, seed=3)
+    cs, _ = O.acceptance_rate(tgt[:1], x[:1], U[:1], W1, W2t, 1.0)
+    alpha = cs[0, 0]
+    emp = (m == 1).mean()
+    assert abs(emp - alpha) < 4 * np.sqrt(alpha * (1 - alpha) / n), (emp, alpha)
+
+
+# ----------------------------------------------------------- STS fit --
+def test_sts_fit_hand_example():
+    # four blocks, one position, logit 0 (c = 0.5, bin 7 of 15), three accepted:
+    # ECE = |4 * 0.5 - 3| / 4 = 0.25 at every temperature; the first grid value wins
+    z = np.zeros((4, 1), np.float32)
+    m = np.array([1, 1, 1, 0])
+    t, ece, _ = O.sts_fit(z, m, [2.0, 1.0, 0.5])
+    assert t[0] == 2.0 and ece[0] == 0.25
+    # two positions by hand: z = (ln 3, 0): c_1 = 0.75, A_2 = 0.375 (bins 11 and 5)
+    z = np.array([[np.log(3.0), 0.0]] * 4, np.float32)
+    m = np.array([2, 1, 1, 0])
+    t, ece, _ = O.sts_fit(z, m, [1.0])
+    c1 = 1 / (1 + np.exp(-np.float64(np.float32(np.log(3.0)))))
+    assert abs(ece[0] - abs(4 * c1 - 3) / 4) < 1e-15
+    assert abs(ece[1] - abs(4 * c1 * 0.5 - 1) / 4) < 1e-15
+    # two bins whose errors cancel in total: c = 0.75, 0.75 (bin 11) never
+    # accepted, c = 0.25, 0.25 (bin 3) always accepted -> ECE = (1.5 + 1.5) / 4
+    z = np.array([[np.log(3.0)], [np.log(3.0)], [-np.log(3.0)], [-np.log(3.0)]], np.float32)
+    t, ece, _ = O.sts_fit(z, np.array([0, 0, 1, 1]), [1.0])
+    assert abs(ece[0] - 0.75) < 1e-7
+    # the top two bins kept apart: c = 0.9 (bin 13) always accepted, c = 0.98
+    # (bin 14) never: ECE = (|1.8 - 2| + |1.96 - 0|) / 4
+    z = np.array([[np.log(9.0)]] * 2 + [[np.log(49.0)]] * 2, np.float32)
+    t, ece, _ = O.sts_fit(z, np.array([1, 1, 0, 0]), [1.0])
+    assert abs(ece[0] - 0.54) < 1e-6
+
+
+def _sts_data(rng, n, t_true, mu=1.5, sd=2.0):
+    """Blocks whose true prefix-acceptance law is prod_j sigmoid(z_j / t*_j):
+    position k is accepted (given the prefix) with probability sigmoid(z_k / t*_k)."""
+    g = len(t_true)
+    z = rng.normal(mu, sd, (n, g)).astype(np.float32)
+    p = 1.0 / (1.0 + np.exp(-z.astype(np.float64) / np.asarray(t_true)))
+    acc = rng.uniform(size=(n, g)) < p
+    m = np.where(acc.all(1), g, np.argmin(acc, axis=1))
+    return z, m
+
+
+def test_sts_fit_recovers_true_temperatures():
+    rng = np.random.default_rng(32)
+    grid = np.round(np.arange(0.4, 3.01, 0.2), 6).astype(np.float32)
+    t_true = [grid[3], grid[6], grid[10], grid[1], grid[8]]
+    z, m = _sts_data(rng, 300_000, t_true)
+    t, ece, _ = O.sts_fit(z, m, grid)
+    np.testing.assert_array_equal(t, np.asarray(t_true, np.float32))
+    assert (ece < 0.01).all()
+    # an uncalibrated head (t = 1 everywhere) has a larger ECE at every
+    # position whose true temperature is not 1
+    t1, ece1, _ = O.sts_fit(z, m, [1.0])
+    assert (ece1[1:] > 3 * ece[1:]).all() and ece1[0] == ece[0]   # t*_1 = 1.0
+
+
+def test_sts_fit_left_to_right_freezing():
+    """t_1..t_k depend only on labels of positions 1..k: accepted counts above
+    k may change without moving them."""
+    rng = np.random.default_rng(33)
+    grid = np.linspace(0.5, 2.0, 16).astype(np.float32)
+    z, m = _sts_data(rng, 20_000, [1.3, 0.7, 1.0, 1.6])
+    t, _, _ = O.sts_fit(z, m, grid)
+    for k in range(1, 4):
+        m2 = np.where(m > k, k + rng.integers(0, 4 - k + 1, m.size), m)
+        m2 = np.minimum(m2, 4)
+        t2, _, _ = O.sts_fit(z, m2, grid)
+        np.testing.assert_array_equal(t2[:k], t[:k])
+    # order preservation: calibrated confidences rank as the raw logits do
+    for k in range(4):
+        c = 1 / (1 + np.exp(-z[:, k].astype(np.float64) / t[k]))
+        assert (np.argsort(c, kind="stable") == np.argsort(z[:, k], kind="stable")).all()
