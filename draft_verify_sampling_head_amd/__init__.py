@@ -7,12 +7,13 @@ synthetic inputs.  Importing the package loads the library and fails if it is
 missing; there is no other execution path.
 """
 from . import _lib
-from ._lib import (DsparkError, async_schedule, confidence, draft_markov, get_status,
-                   clear_status, pack, pack_tiered, prefix_schedule, verify, verify_cap_accept,
-                   workspace, workspace_bytes)
+from ._lib import (DsparkError, acceptance_rate, async_schedule, confidence, confidence_logits,
+                   draft_markov, get_status, clear_status, pack, pack_tiered, prefix_schedule,
+                   sts_fit, sts_workspace, verify, verify_cap_accept, workspace, workspace_bytes)
 
 _lib.load()
 
-__all__ = ["DsparkError", "async_schedule", "confidence", "draft_markov", "get_status",
-           "clear_status", "pack", "pack_tiered", "prefix_schedule", "verify", "verify_cap_accept",
-           "workspace", "workspace_bytes"]
+__all__ = ["DsparkError", "acceptance_rate", "async_schedule", "confidence", "confidence_logits",
+           "draft_markov", "get_status", "clear_status", "pack", "pack_tiered", "prefix_schedule",
+           "sts_fit", "sts_workspace", "verify", "verify_cap_accept", "workspace",
+           "workspace_bytes"]

@@ -25,7 +25,8 @@ EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
            "dspark_clear_status", "dspark_get_status", "dspark_draft_markov",
            "dspark_confidence", "dspark_prefix_schedule", "dspark_pack", "dspark_verify",
            "dspark_draft_markov_profiled", "dspark_async_schedule", "dspark_pack_tiered",
-           "dspark_verify_cap_accept")
+           "dspark_verify_cap_accept", "dspark_acceptance_rate", "dspark_sts_fit",
+           "dspark_sts_workspace_bytes", "dspark_confidence_logits")
 
 
 class DsparkError(RuntimeError):
@@ -60,6 +61,12 @@ def load():
     L.dspark_prefix_schedule.argtypes = [i32, i32, P, P, i32, i32, P, P, P, P, P]
     L.dspark_async_schedule.argtypes = [i32, i32, P, P, i32, P, P, P, P, P, P, P, P]
     L.dspark_pack.argtypes = [i32, i32, P, P, i32, P, P, P, P, P, P, sz, P]
+    L.dspark_sts_workspace_bytes.argtypes = [i32]
+    L.dspark_sts_workspace_bytes.restype = sz
+    L.dspark_sts_fit.argtypes = [i32, i32, P, P, P, i32, i32, P, P, P, sz, P]
+    L.dspark_confidence_logits.argtypes = [i32, i32, i32, i32, i32, P, i32, P, i32, P, i32, P, P, P]
+    L.dspark_acceptance_rate.argtypes = [i32, i32, i32, i32, f32, P, i32, P, P, P, i32, P, P, i32,
+                                         P, P, sz, P]
     L.dspark_pack_tiered.argtypes = [i32, i32, P, P, i32, P, i32, i32, C.c_int64, P, P, P, P, P,
                                      P, P, sz, P]
     L.dspark_verify_cap_accept.argtypes = [i32, i32, i32, i32, f32, u64, u64, P, P, P, P, i32, i32,
@@ -69,6 +76,7 @@ def load():
     for fn in EXPORTS:
         getattr(L, fn).restype = getattr(L, fn).restype or i32
     L.dspark_workspace_bytes.restype = sz
+    L.dspark_sts_workspace_bytes.restype = sz
     L.dspark_status_string.restype = C.c_char_p
     L.dspark_version.restype = C.c_char_p
     _lib = L
@@ -216,6 +224,42 @@ def verify_cap_accept(ell, cap, cu, target, layout, x, logp_d, lse_d, U, W1, W2t
                                            _ptr(emitted), _ptr(next_anchor), _ptr(m_full),
                                            _ptr(logp_t), _ptr(ws), ws.numel(), _stream(stream))
     _check("dspark_verify_cap_accept", code)
+
+
+def confidence_logits(h, W1, w, x, z, V=None, stream=None):
+    R, gamma, d = h.shape
+    r = 0 if W1 is None else int(W1.shape[1])
+    V = int(W1.shape[0]) if (V is None and W1 is not None) else (V or 0)
+    code = load().dspark_confidence_logits(R, gamma, d, r, V, _ptr(h), _dt(h), _ptr(W1), _dt(W1),
+                                           _ptr(w), _dt(w), _ptr(x), _ptr(z), _stream(stream))
+    _check("dspark_confidence_logits", code)
+
+
+def sts_workspace(n, device="cuda"):
+    return torch.zeros(int(load().dspark_sts_workspace_bytes(int(n))), dtype=torch.uint8,
+                       device=device)
+
+
+def sts_fit(z, m, grid, t_out, ws, nbins=15, ece_out=None, stream=None):
+    """z [n][gamma] float32 logits, m [n] int32 accepted counts (device);
+    grid: host sequence of candidate temperatures."""
+    n, gamma = z.shape
+    g = (C.c_float * max(1, len(grid)))(*[float(v) for v in grid])
+    code = load().dspark_sts_fit(n, gamma, _ptr(z), _ptr(m), C.cast(g, C.c_void_p), len(grid),
+                                 int(nbins), _ptr(t_out), _ptr(ece_out), _ptr(ws), ws.numel(),
+                                 _stream(stream))
+    _check("dspark_sts_fit", code)
+
+
+def acceptance_rate(target, x, lse_d, U, W1, W2t, T, c_star, ws, stream=None):
+    """target dense [R][gamma+1][V]; c_star out [R][gamma]."""
+    R, g1, V = target.shape
+    r = 0 if W1 is None else int(W1.shape[1])
+    code = load().dspark_acceptance_rate(R, g1 - 1, V, r, float(T), _ptr(target), _dt(target),
+                                         _ptr(x), _ptr(lse_d), _ptr(U), _dt(U), _ptr(W1),
+                                         _ptr(W2t), _dt(W1), _ptr(c_star), _ptr(ws), ws.numel(),
+                                         _stream(stream))
+    _check("dspark_acceptance_rate", code)
 
 
 def verify(ell, cu, target, layout, x, logp_d, lse_d, U, W1, W2t, T, seed, rnd, m, tau, emitted,

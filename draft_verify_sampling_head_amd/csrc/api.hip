@@ -113,10 +113,10 @@ dspark_status dspark_draft_markov_profiled(int R, int gamma, int V, int r, float
                     margin, ws, ws_bytes, stream, ev_begin, ev_end, n_timed);
 }
 
-dspark_status dspark_confidence(int R, int gamma, int d, int r, int V, const void* h,
-                                dspark_dtype h_dt, const void* W1, dspark_dtype W_dt,
-                                const void* w, dspark_dtype w_dt, const float* sts_T,
-                                const int32_t* x, float* c, hipStream_t stream) {
+static dspark_status confidence_impl(int R, int gamma, int d, int r, int V, const void* h,
+                                     dspark_dtype h_dt, const void* W1, dspark_dtype W_dt,
+                                     const void* w, dspark_dtype w_dt, const float* sts_T,
+                                     const int32_t* x, float* c, bool logits, hipStream_t stream) {
   if (R < 0 || gamma < 1 || d < 1) return DSPARK_E_INVALID;
   if (gamma > 32) return DSPARK_E_UNSUPPORTED;
   dspark_status s = rank_check(r);
@@ -127,7 +127,7 @@ dspark_status dspark_confidence(int R, int gamma, int d, int r, int V, const voi
   if (r > 0 && (!W1 || V < 1)) return DSPARK_E_INVALID;
   ConfArgs a{};
   a.R = R; a.gamma = gamma; a.d = d; a.rank = r; a.V = V; a.h = h; a.W1 = W1; a.w = w;
-  a.sts = sts_T; a.x = x; a.c = c; a.status = nullptr;
+  a.sts = sts_T; a.x = x; a.c = c; a.status = nullptr; a.logits = logits;
   const size_t hs = h_dt == DSPARK_BF16 ? 2 : 4, ws_ = w_dt == DSPARK_BF16 ? 2 : 4;
   const size_t es = W_dt == DSPARK_BF16 ? 2 : 4;
   a.vec_h = aligned16(h) && aligned16(w) && ((size_t)d * hs) % 16 == 0 && hs == ws_;
@@ -135,6 +135,22 @@ dspark_status dspark_confidence(int R, int gamma, int d, int r, int V, const voi
             ((size_t)r * es) % 16 == 0 && es == ws_;
   return hip_status(launch_confidence(a, h_dt == DSPARK_BF16, W_dt == DSPARK_BF16,
                                       w_dt == DSPARK_BF16, stream));
+}
+
+dspark_status dspark_confidence(int R, int gamma, int d, int r, int V, const void* h,
+                                dspark_dtype h_dt, const void* W1, dspark_dtype W_dt,
+                                const void* w, dspark_dtype w_dt, const float* sts_T,
+                                const int32_t* x, float* c, hipStream_t stream) {
+  return confidence_impl(R, gamma, d, r, V, h, h_dt, W1, W_dt, w, w_dt, sts_T, x, c, false,
+                         stream);
+}
+
+dspark_status dspark_confidence_logits(int R, int gamma, int d, int r, int V, const void* h,
+                                       dspark_dtype h_dt, const void* W1, dspark_dtype W_dt,
+                                       const void* w, dspark_dtype w_dt, const int32_t* x,
+                                       float* z, hipStream_t stream) {
+  return confidence_impl(R, gamma, d, r, V, h, h_dt, W1, W_dt, w, w_dt, nullptr, x, z, true,
+                         stream);
 }
 
 dspark_status dspark_prefix_schedule(int R, int gamma, const float* c, const double* sps,
@@ -239,6 +255,55 @@ static dspark_status verify_impl(int R, int gamma, int V, int r, float T, uint64
                                   x, logp_d, lse_d, U, U_dt == DSPARK_BF16, W1, W2t,
                                   W_dt == DSPARK_BF16, m, tau, emitted, next_anchor, logp_t, ws,
                                   stream, cap, m_full));
+}
+
+size_t dspark_sts_workspace_bytes(int n) {
+  return n < 0 ? 0 : 256 + ws_align((size_t)n * 8) + (size_t)kStsMaxGrid * 8;
+}
+
+dspark_status dspark_sts_fit(int n, int gamma, const float* z, const int32_t* m, const float* grid,
+                             int G, int nbins, float* t_out, double* ece_out, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  if (n < 0 || gamma < 1 || G < 1 || nbins < 1) return DSPARK_E_INVALID;
+  if (G > kStsMaxGrid || nbins > kStsMaxBins) return DSPARK_E_UNSUPPORTED;
+  if (!grid) return DSPARK_E_INVALID;
+  for (int g = 0; g < G; ++g)
+    if (!(grid[g] > 0.f) || !std::isfinite(grid[g])) return DSPARK_E_INVALID;
+  if (n == 0) return DSPARK_E_INVALID;      // nothing to calibrate on
+  if (!z || !m || !t_out || !ws) return DSPARK_E_INVALID;
+  if (!aligned16(ws)) return DSPARK_E_INVALID;
+  if (ws_bytes < dspark_sts_workspace_bytes(n)) return DSPARK_E_WORKSPACE;
+  StsArgs a{};
+  a.n = n; a.gamma = gamma; a.G = G; a.nbins = nbins; a.z = z; a.m = m;
+  char* w = reinterpret_cast<char*>(ws);
+  a.A = reinterpret_cast<double*>(w + 256);
+  a.ece_g = reinterpret_cast<double*>(w + 256 + ws_align((size_t)n * 8));
+  a.t_out = t_out; a.ece_out = ece_out;
+  for (int g = 0; g < G; ++g) a.grid[g] = grid[g];
+  return hip_status(launch_sts_fit(a, stream));
+}
+
+dspark_status dspark_acceptance_rate(int R, int gamma, int V, int r, float T, const void* target,
+                                     dspark_dtype t_dt, const int32_t* x, const float* lse_d,
+                                     const void* U, dspark_dtype U_dt, const void* W1,
+                                     const void* W2t, dspark_dtype W_dt, float* c_star, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  dspark_status s = shape_check(R, gamma, V);
+  if (s != DSPARK_OK) return s;
+  if ((s = rank_check(r)) != DSPARK_OK) return s;
+  if (!(T >= 0.f) || !std::isfinite(T)) return DSPARK_E_INVALID;
+  if (!dtype_ok(t_dt) || !dtype_ok(U_dt) || !dtype_ok(W_dt)) return DSPARK_E_INVALID;
+  if (R == 0) return DSPARK_OK;
+  if (t_dt != U_dt) return DSPARK_E_UNSUPPORTED;
+  if (!target || !x || !c_star || !ws) return DSPARK_E_INVALID;
+  if (T > 0.f && (!lse_d || !U)) return DSPARK_E_INVALID;
+  if (T > 0.f && r > 0 && (!W1 || !W2t)) return DSPARK_E_INVALID;
+  if (r > 0 && T > 0.f && (!aligned16(W1) || !aligned16(W2t))) return DSPARK_E_UNSUPPORTED;
+  if (!aligned16(ws)) return DSPARK_E_INVALID;
+  if (ws_bytes < ws_layout(R, gamma, V).total) return DSPARK_E_WORKSPACE;
+  return hip_status(launch_acceptance_rate(R, gamma, V, r, T, target, x, lse_d, U,
+                                           U_dt == DSPARK_BF16, W1, W2t, W_dt == DSPARK_BF16,
+                                           c_star, ws, stream));
 }
 
 dspark_status dspark_verify(int R, int gamma, int V, int r, float T, uint64_t seed, uint64_t round,

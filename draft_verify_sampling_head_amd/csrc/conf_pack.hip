@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void k_confidence(ConfArgs a) {
   z = wave_sum(z);
   if ((threadIdx.x & 63) == 0) {
     const float t = a.sts ? a.sts[k - 1] : 1.f;
-    a.c[item] = 1.f / (1.f + expf(-z / t));
+    a.c[item] = a.logits ? z : 1.f / (1.f + expf(-z / t));
   }
 }
 

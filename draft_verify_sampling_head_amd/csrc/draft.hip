@@ -973,7 +973,8 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // ================================================= residual statistics
 // Per-chunk residual mass sum_{v in c} max(0, p_t(v) - p_d(v)) of the rows in
 // the verify's residual work list (DSpark: resample the first rejected
-// position from norm(max(0, p_t - p_d))).  p_d is rebuilt exactly as the draft
+// position from norm(max(0, p_t - p_d))), or with OVERLAP the overlap mass
+// sum_{v in c} min(p_t(v), p_d(v)) (the acceptance rate c* of a position).  p_d is rebuilt exactly as the draft
 // computed it: U + W1[x_{k-1}] W2 over the whole vocabulary.  Same layout as
 // the persistent draft's phase A: workgroup b loads its 512-entry W2 slice
 // into registers once and computes every listed row in 16-row tiles, so W2 is
@@ -994,7 +995,7 @@ struct ResidArgs {
   uint32_t* status;
 };
 
-template <int KS>
+template <int KS, bool OVERLAP>
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_resid_stats(ResidArgs A) {
   constexpr int SEG = 2 * KS, ROWP = SEG + 1, KT = KS / 2;
@@ -1068,7 +1069,7 @@ void k_resid_stats(ResidArgs A) {
             const float tv = (j & 1) ? bf16_hi(w) : bf16_lo(w);
             const float pt = __builtin_amdgcn_exp2f((tv - cur.nt.x) * s2 - lrt2);
             const float pd = __builtin_amdgcn_exp2f((acc[j >> 2][j & 3] * invT - cur.ld) * kLog2e);
-            S += fmaxf(pt - pd, 0.f);
+            S += OVERLAP ? fminf(pt, pd) : fmaxf(pt - pd, 0.f);
           }
         }
         S += __shfl_xor(S, 16);
@@ -1098,7 +1099,7 @@ bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void*
                          const void* W1, const void* W2t, const void* target, const int32_t* x,
                          const int32_t* rej_count, const int4* rej, const float2* lse_t,
                          const float* lse_d, float2* L, uint32_t* status, hipStream_t st,
-                         hipError_t* err) {
+                         hipError_t* err, bool overlap) {
   const char* env = std::getenv("DSPARK_DRAFT_KERNEL");
   if (env && std::strcmp(env, "steps") == 0) return false;
   if ((V % 8) != 0 || (rank != 64 && rank != 128 && rank != 256)) return false;
@@ -1114,9 +1115,13 @@ bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void*
   A.target = reinterpret_cast<const uint16_t*>(target);
   A.x = x; A.rej_count = rej_count; A.rej = rej; A.lse_t = lse_t; A.lse_d = lse_d; A.L = L;
   A.status = status;
-  if (rank == 64) hipLaunchKernelGGL((k_resid_stats<4>), dim3(A.nslice), dim3(kPThreads), 0, st, A);
-  else if (rank == 128) hipLaunchKernelGGL((k_resid_stats<8>), dim3(A.nslice), dim3(kPThreads), 0, st, A);
-  else hipLaunchKernelGGL((k_resid_stats<16>), dim3(A.nslice), dim3(kPThreads), 0, st, A);
+#define DSPARK_RS(KS_, OV_) hipLaunchKernelGGL((k_resid_stats<KS_, OV_>), dim3(A.nslice), dim3(kPThreads), 0, st, A)
+  if (overlap) {
+    if (rank == 64) DSPARK_RS(4, true); else if (rank == 128) DSPARK_RS(8, true); else DSPARK_RS(16, true);
+  } else {
+    if (rank == 64) DSPARK_RS(4, false); else if (rank == 128) DSPARK_RS(8, false); else DSPARK_RS(16, false);
+  }
+#undef DSPARK_RS
   *err = hipGetLastError();
   return true;
 }

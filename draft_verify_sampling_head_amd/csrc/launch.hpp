@@ -7,7 +7,7 @@
 
 namespace dspark {
 
-enum { kRowsDraft = 0, kRowsVerifyPacked = 1, kRowsVerifyDense = 2 };
+enum { kRowsDraft = 0, kRowsVerifyPacked = 1, kRowsVerifyDense = 2, kRowsAll = 3 };
 enum { kModeSample = 0, kModeGreedy = 1, kModeResid = 2 };
 
 // Streaming per-chunk statistics of rows with no bias.
@@ -46,6 +46,7 @@ struct MarkovArgs {
   const void* target;
   const float2* lse_t;     // [verify row] (raw max, log-normaliser relative to it)
   const float* lse_d;
+  bool overlap;            // residual rows: sum min(p_t, p_d) instead of max(0, p_t - p_d)
   uint32_t* status;
   // filled by the launcher
   int cg, nrg, ncg;        // chunks per workgroup, 256-row groups, chunk groups
@@ -58,8 +59,8 @@ struct ConfArgs {
   const void* w;
   const float* sts;
   const int32_t* x;
-  float* c;
-  bool vec_h, vec_e;
+  float* c;                // sigmoid(z / t), or z itself when logits is set
+  bool vec_h, vec_e, logits;
   uint32_t* status;
 };
 
@@ -96,6 +97,21 @@ struct SchedArgs {
   double* theta_plan;       // mode 1 (nullable)
 };
 
+constexpr int kStsMaxBins = 64;
+constexpr int kStsMaxGrid = 256;
+
+struct StsArgs {
+  int n, gamma, G, nbins;
+  const float* z;            // [n][gamma] raw confidence logits
+  const int32_t* m;          // [n] accepted drafts
+  double* A;                 // [n] workspace: cumulative product of earlier positions
+  double* ece_g;             // [G] workspace: ECE of every candidate at the current position
+  float* t_out;              // [gamma]
+  double* ece_out;           // [gamma] nullable
+  float grid[kStsMaxGrid];   // candidate temperatures, in search order
+};
+
+hipError_t launch_sts_fit(const StsArgs& a, hipStream_t st);
 hipError_t launch_row_stats(const RowStatsArgs& a, bool bf16, bool greedy, hipStream_t st);
 hipError_t launch_markov_stats(const MarkovArgs& a, bool u_bf16, bool w_bf16, int mode,
                                hipStream_t st);
@@ -113,7 +129,11 @@ bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void*
                          const void* W1, const void* W2t, const void* target, const int32_t* x,
                          const int32_t* rej_count, const int4* rej, const float2* lse_t,
                          const float* lse_d, float2* L, uint32_t* status, hipStream_t st,
-                         hipError_t* err);
+                         hipError_t* err, bool overlap = false);
+hipError_t launch_acceptance_rate(int R, int gamma, int V, int rank, float T, const void* target,
+                                  const int32_t* x, const float* lse_d, const void* U, bool u_bf16,
+                                  const void* W1, const void* W2t, bool w_bf16, float* c_star,
+                                  void* ws, hipStream_t st);
 hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,
                          const int32_t* ell, const int32_t* cu, const void* target, int layout,
                          const int32_t* x, const float* logp_d, const float* lse_d,

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void k_row_stats(RowStatsArgs a) {
   const int nwaves = gridDim.x * 4;
   if (a.zero_me && blockIdx.x == 0 && threadIdx.x == 0) *a.zero_me = 0u;
   int nrows = a.nrows_cap;
-  if (a.kind != kRowsDraft) nrows = min(nrows, a.cu[a.R]);
+  if (a.kind != kRowsDraft && a.kind != kRowsAll) nrows = min(nrows, a.cu[a.R]);
   // dense verify rows: the row of packed index q is found by binary search
   // over the offsets, staged in LDS when they fit
   const bool lds_cu = a.kind == kRowsVerifyDense && a.R + 1 <= kCuLds;
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void k_row_stats(RowStatsArgs a) {
     int64_t row;
     if (a.kind == kRowsDraft) {
       row = (int64_t)q * a.gamma + (a.k - 1);
-    } else if (a.kind == kRowsVerifyPacked) {
+    } else if (a.kind == kRowsVerifyPacked || a.kind == kRowsAll) {
       row = q;
     } else {
       int lo = 0, hi = a.R - 1;
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma_reg(MarkovArgs a) {
         for (int j = 0; j < 16; ++j) {
           const float pt = __builtin_amdgcn_exp2f((tv[j] - mt[nt]) * s2 - lrt2[nt]);
           const float pd = __builtin_amdgcn_exp2f((acc[nt][j] * invT - lse_d[nt]) * kLog2e);
-          Sr[nt] += fmaxf(pt - pd, 0.f);
+          Sr[nt] += a.overlap ? fminf(pt, pd) : fmaxf(pt - pd, 0.f);
         }
       }
     }
@@ -743,7 +743,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
         for (int j = 0; j < 16; ++j) {
           const float pt = __builtin_amdgcn_exp2f((tv[j] - mt[nt]) * s2 - lrt2[nt]);
           const float pd = __builtin_amdgcn_exp2f((x[j] * invT - lse_d[nt]) * kLog2e);
-          Sr[nt] += fmaxf(pt - pd, 0.f);
+          Sr[nt] += a.overlap ? fminf(pt, pd) : fmaxf(pt - pd, 0.f);
         }
       }
     }
@@ -1000,7 +1000,7 @@ __global__ __launch_bounds__(256) void k_markov_valu(MarkovArgs a) {
           const float pt = __builtin_amdgcn_exp2f((Elem<UT>::get(tptr, vv[h]) - nt.x) * a.scale2
                                                   - nt.y * kLog2e);
           const float pd = __builtin_amdgcn_exp2f((sv[h] * invT - lse_d) * kLog2e);
-          sm += fmaxf(pt - pd, 0.f);
+          sm += a.overlap ? fminf(pt, pd) : fmaxf(pt - pd, 0.f);
         }
       }
       sm = wave_sum(sm);

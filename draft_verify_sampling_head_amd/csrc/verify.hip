@@ -31,6 +31,7 @@ namespace dspark {
 
 struct VerifyArgs {
   int R, gamma, V, rank, nch, layout;
+  bool all_rows;        // every dense row R*(gamma+1), not cu[R] (acceptance-rate pass)
   float invT;
   bool greedy;
   uint64_t seed, round;
@@ -68,7 +69,7 @@ __device__ __forceinline__ int64_t target_row(const VerifyArgs& a, int i, int j)
 __global__ __launch_bounds__(256) void k_row_norm(VerifyArgs a) {
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * 4;
-  const int N = min(a.cu[a.R], a.R * (a.gamma + 1));
+  const int N = a.all_rows ? a.R * (a.gamma + 1) : min(a.cu[a.R], a.R * (a.gamma + 1));
   for (int q = wave; q < N; q += nwaves) {
     if (a.greedy) {
       float v;
@@ -240,6 +241,127 @@ __global__ __launch_bounds__(256) void k_resid_pick(VerifyArgs a) {
     a.emitted[(int64_t)i * (a.gamma + 1) + (k - 1)] = y;
     a.next_anchor[i] = y;
   }
+}
+
+// ------------------------------------------------- acceptance rate c*
+// c*_k = sum_v min(p_d^k(v), p_t^k(v)) for every request and block position
+// (DSpark summary page, Method details: the confidence head's supervision
+// target, one minus the total variation between draft and target).  One pass
+// over every dense target row gives the row normalisers; then one launch of
+// the residual kernels in overlap mode covers a work list of all R * gamma
+// (request, position) rows (p_d rebuilt from U and the Markov bias exactly as
+// for a rejection; W2 is streamed once), and one wave per row adds the chunk
+// masses.  The list and the masses reuse the target-row statistics buffers,
+// which are free once the normalisers exist.  At T == 0 the distributions
+// are point masses: c* = [x_k == argmax of target row k-1].
+// items q0 .. q0+n-1, q = i * gamma + (k - 1): request i, position k, target row
+// i*(gamma+1) + k-1
+__global__ __launch_bounds__(256) void k_cstar_list(int gamma, int q0, int n, int4* list,
+                                                     int32_t* count) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j < n) {
+    const int q = q0 + j;
+    const int i = q / gamma, k = q % gamma + 1;
+    const int row = i * (gamma + 1) + (k - 1);
+    list[j] = make_int4(i, k, row, row);
+  }
+  if (j == 0) *count = n;
+}
+
+__global__ __launch_bounds__(256) void k_cstar_sum(int items, int nch, const float2* L,
+                                                    float* c_star) {
+  const int q = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (q >= items) return;
+  const int lane = threadIdx.x & 63;
+  float s = 0.f;
+  for (int c = lane; c < nch; c += 64) s += L[(int64_t)q * nch + c].y;
+  s = wave_sum(s);
+  if (lane == 0) c_star[q] = s;
+}
+
+__global__ __launch_bounds__(256) void k_cstar_greedy(int R, int gamma, int V, const int32_t* x,
+                                                       const float2* lse_t, float* c_star,
+                                                       uint32_t* status) {
+  const int item = blockIdx.x * 256 + threadIdx.x;
+  if (item >= R * gamma) return;
+  const int i = item / gamma, k = item % gamma + 1;
+  const int am = __float_as_int(lse_t[i * (gamma + 1) + (k - 1)].y);
+  const int xk = x[(int64_t)i * (gamma + 1) + k];
+  if (xk < 0 || xk >= V) set_flag(status, kFlagBadToken);
+  c_star[item] = (xk == am) ? 1.f : 0.f;
+}
+
+hipError_t launch_acceptance_rate(int R, int gamma, int V, int rank, float T, const void* target,
+                                  const int32_t* x, const float* lse_d, const void* U, bool u_bf16,
+                                  const void* W1, const void* W2t, bool w_bf16, float* c_star,
+                                  void* ws, hipStream_t st) {
+  const WsLayout L = ws_layout(R, gamma, V);
+  char* w = reinterpret_cast<char*>(ws);
+  uint32_t* hdr = reinterpret_cast<uint32_t*>(w + L.header);
+  const int nch = (V + kChunk - 1) / kChunk;
+  const bool greedy = (T == 0.f);
+  const size_t usz = u_bf16 ? 2 : 4;
+  const bool t_vec = ((reinterpret_cast<uintptr_t>(target) & 15) == 0) && (((size_t)V * usz) % 16 == 0);
+  const bool u_vec = ((reinterpret_cast<uintptr_t>(U) & 15) == 0) && (((size_t)V * usz) % 16 == 0);
+  const int rows = R * (gamma + 1);
+
+  RowStatsArgs rs{};
+  rs.base = target; rs.kind = kRowsAll;
+  rs.R = R; rs.gamma = gamma; rs.k = 0; rs.V = V; rs.nch = nch; rs.cu = nullptr;
+  rs.nrows_cap = rows;
+  rs.scale2 = greedy ? 1.f : kLog2e / T;
+  rs.vec_ok = t_vec;
+  rs.L = reinterpret_cast<float2*>(w + L.ver_l);
+  rs.I = reinterpret_cast<int*>(w + L.ver_i);
+  rs.status = hdr;
+  rs.zero_me = nullptr;
+  hipError_t e = launch_row_stats(rs, u_bf16, greedy, st);
+  if (e != hipSuccess) return e;
+
+  VerifyArgs a{};
+  a.R = R; a.gamma = gamma; a.V = V; a.rank = rank; a.nch = nch; a.layout = 1; a.all_rows = true;
+  a.invT = greedy ? 1.f : 1.f / T; a.greedy = greedy;
+  a.vl = rs.L; a.vi = rs.I;
+  a.lse_t = reinterpret_cast<float2*>(w + L.lse_t);
+  a.status = hdr;
+  hipLaunchKernelGGL(k_row_norm, dim3(min(4096, (rows + 3) / 4)), dim3(256), 0, st, a);
+  if (greedy) {
+    hipLaunchKernelGGL(k_cstar_greedy, dim3((R * gamma + 255) / 256), dim3(256), 0, st, R, gamma,
+                       V, x, a.lse_t, c_star, hdr);
+    return hipGetLastError();
+  }
+  // the list takes the argmax buffer (unused at T > 0) and the masses the
+  // chunk statistics (read by k_row_norm only): all R*gamma items at once when
+  // the list fits (at least 4 chunks), else in batches of what fits
+  const int items = R * gamma;
+  int32_t* count = reinterpret_cast<int32_t*>(hdr + 1);
+  int4* list = reinterpret_cast<int4*>(w + L.ver_i);
+  float2* rl = reinterpret_cast<float2*>(w + L.ver_l);
+  const int cap = (int)std::min<size_t>((size_t)items, (L.lse_t - L.ver_i) / sizeof(int4));
+  for (int q0 = 0; q0 < items; q0 += cap) {
+    const int n = std::min(cap, items - q0);
+    hipLaunchKernelGGL(k_cstar_list, dim3((n + 255) / 256), dim3(256), 0, st, gamma, q0, n, list,
+                       count);
+    if (u_bf16 && w_bf16 && rank > 0 && u_vec && t_vec &&
+        launch_resid_slices(n, gamma, V, rank, T, U, W1, W2t, target, x, count, list, a.lse_t,
+                            lse_d, rl, hdr, st, &e, true)) {
+      if (e != hipSuccess) return e;
+    } else {
+      MarkovArgs ma{};
+      ma.R = R; ma.gamma = gamma; ma.k = 0; ma.V = V; ma.rank = rank; ma.nch = nch;
+      ma.nrows_cap = n;
+      ma.U = U; ma.W1v = W1; ma.W2tv = W2t; ma.x0 = nullptr; ma.x = x; ma.scale2 = kLog2e / T;
+      ma.u_vec_ok = u_vec && t_vec;
+      ma.L = rl; ma.I = nullptr;
+      ma.rej_count = count; ma.rej = list; ma.target = target; ma.lse_t = a.lse_t;
+      ma.lse_d = lse_d; ma.status = hdr; ma.overlap = true;
+      e = launch_markov_stats(ma, u_bf16, w_bf16 && rank > 0, kModeResid, st);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_cstar_sum, dim3((n + 3) / 4), dim3(256), 0, st, n, nch, rl,
+                       c_star + q0);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,

@@ -284,6 +284,63 @@ dspark_status dspark_verify(int R, int gamma, int V, int r, float T,
                             float* logp_t, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Single-step acceptance rate of every block position, a diagnostic pass
+ * over the whole block ([P3] Method details, confidence head: the head is
+ * supervised with c*_k = 1 - TV(p_d^k, p_t^k)):
+ *   c*_k = sum_v min(p_d^k(v), p_t^k(v)),  k = 1..gamma,
+ * with p_d^k the tempered draft distribution of position k given x_{k-1}
+ * (rebuilt from U, W1, W2t and normalised by lse_d, as at a rejection) and
+ * p_t^k = softmax(row / T) of dense target row i*(gamma+1) + k-1.  T == 0:
+ * point masses, c*_k = 1 if x_k is the first argmax of that target row, else 0.
+ *   target   dense [R][gamma+1][V] (t_dt, equal to U_dt); rows 0..gamma-1 are read
+ *   x, lse_d the draft's outputs; U, W1, W2t the draft's inputs
+ *   c_star   out [R][gamma] float32
+ * Uses the workspace like dspark_verify (same size); enqueues about 3 gamma
+ * kernels.
+ */
+dspark_status dspark_acceptance_rate(int R, int gamma, int V, int r, float T, const void* target,
+                                     dspark_dtype t_dt, const int32_t* x, const float* lse_d,
+                                     const void* U, dspark_dtype U_dt, const void* W1,
+                                     const void* W2t, dspark_dtype W_dt, float* c_star, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Sequential temperature scaling fit of the confidence head ([P3] Method
+ * details, post-hoc calibration; [P1] 4.2.3).  Held-out data: n blocks with
+ * raw confidence logits z (c_k = sigmoid(z_k / t_k); e.g. from
+ * dspark_confidence_logits) and the number m of drafts the target accepted
+ * under whole-block verification.  Left to right, k = 1..gamma, with t_1..t_{k-1}
+ * fixed: for every candidate t of the grid the cumulative product
+ * A_k = A_{k-1} sigmoid(z_k / t) (A_0 = 1) is scored by its expected
+ * calibration error against y_k = [m >= k],
+ *   ECE = (1/n) sum_b | sum_{i in bin b} (A_i - y_i) |,
+ * nbins equal-width bins of [0, 1], bin = min(floor(A nbins), nbins - 1);
+ * t_k = the first grid value with the smallest ECE.  Evaluated in double,
+ * deterministic.  The result feeds dspark_confidence's sts_T.
+ *   z        [n][gamma] float32 logits;  m  [n] int32
+ *   grid     (host) [G] candidate temperatures, each > 0 and finite, G <= 256
+ *   nbins    1..64 (15 is the usual choice)
+ *   t_out    out [gamma] float32 (a grid value per position)
+ *   ece_out  out nullable [gamma] double: ECE at the chosen temperature
+ *   ws       workspace of dspark_sts_workspace_bytes(n) bytes, 16-byte aligned
+ */
+size_t dspark_sts_workspace_bytes(int n);
+dspark_status dspark_sts_fit(int n, int gamma, const float* z, const int32_t* m, const float* grid,
+                             int G, int nbins, float* t_out, double* ece_out, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Confidence logits: z_k = w . [h_k ; W1[x_{k-1}]] (dspark_confidence before the
+ * temperature and the sigmoid), the input of the STS fit.  Arguments as for
+ * dspark_confidence; z out [R][gamma] float32.
+ */
+dspark_status dspark_confidence_logits(int R, int gamma, int d, int r, int V,
+                                       const void* h, dspark_dtype h_dt,
+                                       const void* W1, dspark_dtype W_dt,
+                                       const void* w, dspark_dtype w_dt,
+                                       const int32_t* x, float* z, hipStream_t stream);
+
+/*
  * Cap-accept verification ([P2] 5.4, DSpark in SGLang, the verify modes:
  * verify the whole window, commit only the scheduler's truncated window; used
  * to observe the acceptance a schedule leaves on the table).  Request i is

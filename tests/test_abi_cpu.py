@@ -102,6 +102,17 @@ def test_confidence_schedule_pack_verify_checks():
     assert ver(T=-1.0) == INVALID
     assert ver(ws_bytes=10) == WORKSPACE
     assert ver(ell=None) == INVALID
+    grid = (C.c_float * 3)(0.5, 1.0, 2.0)
+    sts = lambda n=10, g=3, G=3, nb=15, gr=grid, wsb=1 << 20: lib.dspark_sts_fit(
+        n, g, FAKE, FAKE, C.cast(gr, C.c_void_p), G, nb, FAKE, None, FAKE, wsb, None)
+    assert sts(n=0) == INVALID and sts(G=0) == INVALID and sts(nb=0) == INVALID
+    assert sts(G=257) == UNSUPPORTED and sts(nb=65) == UNSUPPORTED
+    assert sts(gr=(C.c_float * 3)(0.5, -1.0, 2.0)) == INVALID
+    assert sts(wsb=64) == WORKSPACE
+    assert lib.dspark_sts_workspace_bytes(1000) >= 8000
+    acc = lambda T=1.0, R=4, tdt=1: lib.dspark_acceptance_rate(
+        R, 3, 100, 0, T, FAKE, tdt, FAKE, FAKE, FAKE, 1, None, None, 1, FAKE, FAKE, 1 << 30, None)
+    assert acc(T=-1.0) == INVALID and acc(tdt=0) == UNSUPPORTED and acc(R=0) == OK
     capv = lambda cap=FAKE, R=4: lib.dspark_verify_cap_accept(
         R, 3, 100, 0, 1.0, 0, 0, FAKE, cap, FAKE, FAKE, 1, 1, FAKE, FAKE, FAKE, FAKE, 1, None,
         None, 1, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 30, None)
@@ -135,7 +146,8 @@ def test_synthetic_configs_shapes():
 
 
 @pytest.mark.parametrize("fn", ["draft_markov", "confidence", "prefix_schedule", "async_schedule",
-                                "pack", "pack_tiered", "verify", "verify_cap_accept"])
+                                "pack", "pack_tiered", "verify", "verify_cap_accept",
+                                "acceptance_rate", "sts_fit", "confidence_logits"])
 def test_binding_names_match_abi(fn):
     assert callable(getattr(D, fn))
     assert f"dspark_{fn}" in declared()

@@ -478,6 +478,100 @@ def test_cap_accept_negative_window_is_flagged():
     assert (n(buf.m) == 0).all() and (n(buf.tau) == 1).all()
 
 
+# ------------------------------------------- diagnostics: c*, STS fit
+CSTAR = [
+    (2, dict(R=40, gamma=5, V=3000, d=64)),               # bf16 rank 256: W2-slice kernel
+    (2, dict(R=33, gamma=4, V=2000, d=64, rank=64)),
+    (2, dict(R=37, gamma=6, V=2600, d=64, rank=0)),       # no bias: per-tile kernel
+    (0, {}),                                               # fp32
+    (1, dict(R=33, gamma=7, V=5000, d=128)),               # T = 0
+    (2, dict(R=5, gamma=3, V=300, d=32, rank=16)),         # 3 chunks: batched work list
+    (3, dict(R=70, gamma=6, V=2500, d=64)),
+]
+
+
+@pytest.mark.parametrize("base,over", CSTAR, ids=[f"cstar{i}" for i in range(len(CSTAR))])
+def test_acceptance_rate_parity(base, over):
+    import oracle as O
+    cfg = synth.scaled(synth.config(base), **over) if over else synth.config(base)
+    print(f"[case] c* {cfg.name} R={cfg.R} g={cfg.gamma} V={cfg.V} r={cfg.rank} T={cfg.T}",
+          flush=True)
+    inp = synth.make_inputs(cfg, device="cpu")
+    g = to_dev(inp)
+    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV)
+    D.draft_markov(g["U"], g["W1"], g["W2t"], g["x0"], cfg.T, cfg.philox_seed, 1, buf.x,
+                   buf.logp_d, buf.lse_d, buf.ws)
+    cs = torch.empty(cfg.R, cfg.gamma, dtype=torch.float32, device=DEV)
+    D.acceptance_rate(g["target"], buf.x, buf.lse_d, g["U"], g["W1"], g["W2t"], cfg.T, cs, buf.ws)
+    torch.cuda.synchronize()
+    assert D.get_status(buf.ws) == 0
+    ref, mg = O.acceptance_rate(f(inp["target"]), n(buf.x), f(inp["U"]), f(inp["W1"]),
+                                f(inp["W2t"]), cfg.T)
+    got = n(cs).astype(np.float64)
+    if cfg.T > 0:
+        rel = np.abs(got - ref) / np.maximum(ref, 1e-30)
+        print(f"  c* max rel err {rel.max():.3g}, range [{ref.min():.3g}, {ref.max():.3g}]",
+              flush=True)
+        assert rel.max() <= 1e-5
+    else:
+        bad = (got != ref) & (mg >= 1e-5)
+        assert not bad.any() and (got != ref).sum() <= 0.001 * got.size + 1
+
+
+def test_confidence_logits_parity():
+    import oracle as O
+    for base, over in [(2, dict(R=40, gamma=5, V=3000, d=256)), (0, {}),
+                       (2, dict(R=9, gamma=3, V=1500, d=64, rank=0))]:
+        cfg = synth.scaled(synth.config(base), **over) if over else synth.config(base)
+        inp = synth.make_inputs(cfg, device="cpu")
+        g = to_dev(inp)
+        rng = np.random.default_rng(cfg.R)
+        x = np.concatenate([n(inp["x0"])[:, None], rng.integers(0, cfg.V, (cfg.R, cfg.gamma))], 1)
+        xd = torch.as_tensor(x.astype(np.int32), device=DEV)
+        z = torch.empty(cfg.R, cfg.gamma, dtype=torch.float32, device=DEV)
+        D.confidence_logits(g["h"], g["W1"], g["w"], xd, z, V=cfg.V)
+        torch.cuda.synchronize()
+        _, zo = O.confidence(f(inp["h"]), f(inp["W1"]), f(inp["w"]), x)
+        err = np.abs(n(z).astype(np.float64) - zo) / (1.0 + np.abs(zo))
+        assert err.max() <= 1e-5, err.max()
+
+
+def _sts_case(n_, g_, grid, nbins, seed, t_true=None):
+    import oracle as O
+    rng = np.random.default_rng(seed)
+    t_true = t_true or list(rng.choice(grid, g_))
+    zc = rng.normal(1.5, 2.0, (n_, g_)).astype(np.float32)
+    p = 1.0 / (1.0 + np.exp(-zc.astype(np.float64) / np.asarray(t_true)))
+    acc = rng.uniform(size=(n_, g_)) < p
+    m = np.where(acc.all(1), g_, np.argmin(acc, axis=1)).astype(np.int32)
+    zd, md = torch.as_tensor(zc, device=DEV), torch.as_tensor(m, device=DEV)
+    t = torch.empty(g_, dtype=torch.float32, device=DEV)
+    e = torch.empty(g_, dtype=torch.float64, device=DEV)
+    ws = D.sts_workspace(n_, device=DEV)
+    D.sts_fit(zd, md, grid, t, ws, nbins=nbins, ece_out=e)
+    torch.cuda.synchronize()
+    tg, eg = n(t), n(e)
+    # lock-step: a differing choice is allowed only where the oracle's margin
+    # (ECE gap to the runner-up, or a value on a bin edge) is below 1e-9
+    to, eo, mo = O.sts_fit(zc, m, grid, nbins=nbins, force_t=tg)
+    t_own, _, _ = O.sts_fit(zc, m, grid, nbins=nbins)
+    for k in range(g_):
+        if tg[k] != t_own[k]:
+            assert mo[k] < 1e-9, (k, tg[k], t_own[k], mo[k])
+    np.testing.assert_allclose(eg, eo, rtol=1e-12, atol=1e-15)
+    return tg, eg
+
+
+def test_sts_fit_parity():
+    grid = np.round(np.linspace(0.3, 3.0, 28), 6).astype(np.float32)
+    _sts_case(20000, 6, grid, 15, 1)
+    _sts_case(777, 3, grid, 7, 2)
+    _sts_case(1, 2, grid, 1, 3)                           # one block, one bin
+    _sts_case(5000, 4, grid[:1], 64, 4)                   # one candidate, 64 bins
+    tg, _ = _sts_case(200_000, 5, grid, 15, 5, t_true=[grid[3], grid[9], grid[17], grid[5], grid[12]])
+    np.testing.assert_array_equal(tg, grid[[3, 9, 17, 5, 12]])
+
+
 # ------------------------------------------------------------- stage: pack
 def test_pack_tiered_bitexact():
     import oracle as O
