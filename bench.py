@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--verify-mode", choices=["compact", "cap-accept"], default="compact",
                    help="verify the scheduled window (default) or the whole block, committed "
                         "within the scheduled window")
+    p.add_argument("--diagnostics", action="store_true",
+                   help="also time the acceptance-rate (c*) pass on the last round and an STS "
+                        "fit on synthetic held-out blocks")
     p.add_argument("--cpu-sample", type=int, default=48, help="requests in the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -277,6 +280,8 @@ def main():
         f"({achieved:.0f} GB/s, {mfma_tf:.0f} TFLOP/s), round HBM frac {hbm_frac_round:.3f}, "
         f"status={status}")
 
+    diag = diagnostics(cfg, inp, buf, torch, np, D) if args.diagnostics else None
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, inp, buf, args.cpu_sample, sum_ell / K, torch, np, sched,
@@ -310,7 +315,48 @@ def main():
                      "mfma_tflops": mfma_tf, "mfma_frac": mfma_tf / MFMA_BF16_PEAK_TFLOPS},
         "cpu_baseline": cpu,
     }
+    if diag is not None:
+        out["diagnostics"] = diag
     print(json.dumps(out), flush=True)
+
+
+def diagnostics(cfg, inp, buf, torch, np, D):
+    """Times (torch events on the launch stream) of the acceptance-rate pass
+    over the whole block of the last round and of an STS fit on synthetic
+    held-out blocks (n = 1024 rounds of R requests, 64 temperatures, 15 bins)."""
+    dev = inp["U"].device
+    cs = torch.empty(cfg.R, cfg.gamma, dtype=torch.float32, device=dev)
+    run_c = lambda: D.acceptance_rate(inp["target"], buf.x, buf.lse_d, inp["U"], inp["W1"],
+                                      inp["W2t"], cfg.T, cs, buf.ws)
+    n = 1024 * cfg.R
+    g = torch.Generator(device="cpu").manual_seed(7)
+    z = (torch.randn(n, cfg.gamma, generator=g) * 2.0 + 1.5).to(dev)
+    m = torch.randint(0, cfg.gamma + 1, (n,), generator=g, dtype=torch.int32).to(dev)
+    grid = [0.25 + 0.05 * i for i in range(64)]
+    t = torch.empty(cfg.gamma, dtype=torch.float32, device=dev)
+    ws = D.sts_workspace(n, device=dev)
+    run_s = lambda: D.sts_fit(z, m, grid, t, ws, nbins=15)
+    res = {}
+    for name, fn, reps in [("acceptance_rate", run_c, 5), ("sts_fit", run_s, 3)]:
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name + "_ms"] = e0.elapsed_time(e1) / reps
+    s = cfg.dtype.itemsize
+    alg = 2.0 * s * cfg.R * cfg.gamma * cfg.V + s * cfg.rank * cfg.V
+    res["acceptance_rate_alg_bytes"] = alg
+    res["acceptance_rate_hbm_frac"] = alg / (res["acceptance_rate_ms"] * 1e-3) / (HBM_PEAK_GBS * 1e9)
+    res["sts_fit_shape"] = {"n": n, "gamma": cfg.gamma, "grid": len(grid), "nbins": 15}
+    res["sts_sigmoids_per_s"] = cfg.gamma * len(grid) * n / (res["sts_fit_ms"] * 1e-3)
+    log(f"[bench] diagnostics: c* pass {res['acceptance_rate_ms']:.3f} ms "
+        f"({res['acceptance_rate_hbm_frac']:.3f} of HBM peak on U + target + W2), STS fit "
+        f"{res['sts_fit_ms']:.3f} ms for n={n}")
+    return res
 
 
 def cpu_baseline(cfg, inp, buf, n_req, ell_per_round, torch, np, sched="greedy", K_in=0):

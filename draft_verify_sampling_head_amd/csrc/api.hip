@@ -258,7 +258,9 @@ static dspark_status verify_impl(int R, int gamma, int V, int r, float T, uint64
 }
 
 size_t dspark_sts_workspace_bytes(int n) {
-  return n < 0 ? 0 : 256 + ws_align((size_t)n * 8) + (size_t)kStsMaxGrid * 8;
+  return n < 0 ? 0
+               : 256 + ws_align((size_t)n * 8) +
+                     (size_t)kStsMaxGrid * kStsMaxSlices * kStsMaxBins * sizeof(double);
 }
 
 dspark_status dspark_sts_fit(int n, int gamma, const float* z, const int32_t* m, const float* grid,
@@ -277,7 +279,9 @@ dspark_status dspark_sts_fit(int n, int gamma, const float* z, const int32_t* m,
   a.n = n; a.gamma = gamma; a.G = G; a.nbins = nbins; a.z = z; a.m = m;
   char* w = reinterpret_cast<char*>(ws);
   a.A = reinterpret_cast<double*>(w + 256);
-  a.ece_g = reinterpret_cast<double*>(w + 256 + ws_align((size_t)n * 8));
+  a.part = reinterpret_cast<double*>(w + 256 + ws_align((size_t)n * 8));
+  // slices of at least 2048 examples (16 per thread), at most 32 per temperature
+  a.S = std::max(1, std::min(kStsMaxSlices, (n + 2047) / 2048));
   a.t_out = t_out; a.ece_out = ece_out;
   for (int g = 0; g < G; ++g) a.grid[g] = grid[g];
   return hip_status(launch_sts_fit(a, stream));

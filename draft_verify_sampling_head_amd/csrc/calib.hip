@@ -10,11 +10,14 @@
 // ECE over nbins equal-width bins of [0, 1] (bin = min(floor(A nbins),
 // nbins - 1)):  ECE = (1/n) sum_b | sum_{i in b} (A_i - y_i) |.
 // Everything is evaluated in double.  Per position k, three launches:
-//   k_sts_ece    one 128-thread workgroup per grid temperature: each thread
-//                accumulates its examples' (A - y) into its own LDS column of
-//                bins; the columns are then added in a fixed order, so the
-//                result does not depend on scheduling.
-//   k_sts_pick   the first grid index with the smallest ECE.
+//   k_sts_ece    a (slice, temperature) grid of 128-thread workgroups: each
+//                thread accumulates its examples' (A - y) into its own LDS
+//                column of bins, the columns are added in a fixed order and
+//                the slice's signed bin sums are written out.
+//   k_sts_pick   per temperature, the slices' bin sums added in slice order,
+//                then |.| summed over bins; the first grid index with the
+//                smallest ECE.  Fixed orders throughout: the result does not
+//                depend on scheduling.
 //   k_sts_apply  A_i *= sigmoid(z_ik / t_k) for the next position.
 #include "launch.hpp"
 
@@ -26,13 +29,14 @@ __device__ __forceinline__ double sigmoid_d(double x) { return 1.0 / (1.0 + exp(
 
 __global__ __launch_bounds__(kStsThreads) void k_sts_ece(StsArgs a, int k) {
   __shared__ double D[kStsMaxBins * kStsThreads];
-  __shared__ double part[kStsMaxBins];
   const int tid = threadIdx.x;
-  const int g = blockIdx.x;
+  const int sl = blockIdx.x, g = blockIdx.y;
   const double t = (double)a.grid[g];
   const int nb = a.nbins;
+  const int per = (a.n + a.S - 1) / a.S;
+  const int i0 = sl * per, i1 = min(a.n, i0 + per);
   for (int b = 0; b < nb; ++b) D[b * kStsThreads + tid] = 0.0;
-  for (int i = tid; i < a.n; i += kStsThreads) {
+  for (int i = i0 + tid; i < i1; i += kStsThreads) {
     const double prev = (k == 1) ? 1.0 : a.A[i];
     const double A = prev * sigmoid_d((double)a.z[(int64_t)i * a.gamma + (k - 1)] / t);
     int b = (int)floor(A * nb);
@@ -43,23 +47,36 @@ __global__ __launch_bounds__(kStsThreads) void k_sts_ece(StsArgs a, int k) {
   if (tid < nb) {
     double s = 0.0;
     for (int q = 0; q < kStsThreads; ++q) s += D[tid * kStsThreads + q];
-    part[tid] = fabs(s);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    double e = 0.0;
-    for (int b = 0; b < nb; ++b) e += part[b];
-    a.ece_g[g] = e / (double)a.n;
+    a.part[((int64_t)g * nb + tid) * a.S + sl] = s;
   }
 }
 
-__global__ __launch_bounds__(64) void k_sts_pick(StsArgs a, int k) {
-  if (threadIdx.x != 0) return;
+constexpr int kStsPickThreads = 1024;
+
+__global__ __launch_bounds__(kStsPickThreads) void k_sts_pick(StsArgs a, int k) {
+  __shared__ double absb[kStsMaxGrid * kStsMaxBins];
+  __shared__ double ece[kStsMaxGrid];
+  const int tid = threadIdx.x;
+  const int nb = a.nbins;
+  // |sum over slices| per (temperature, bin), slices added in order
+  for (int p = tid; p < a.G * nb; p += kStsPickThreads) {
+    const double* q = a.part + (int64_t)p * a.S;
+    double s = 0.0;
+    for (int sl = 0; sl < a.S; ++sl) s += q[sl];
+    absb[p] = fabs(s);
+  }
+  __syncthreads();
+  if (tid < a.G) {
+    double e = 0.0;
+    for (int b = 0; b < nb; ++b) e += absb[tid * nb + b];
+    ece[tid] = e / (double)a.n;
+  }
+  __syncthreads();
+  if (tid != 0) return;
   int best = 0;
-  double be = a.ece_g[0];
-  for (int g = 1; g < a.G; ++g) {
-    const double e = a.ece_g[g];
-    if (e < be) { be = e; best = g; }
+  double be = ece[0];
+  for (int q = 1; q < a.G; ++q) {
+    if (ece[q] < be) { be = ece[q]; best = q; }
   }
   a.t_out[k - 1] = a.grid[best];
   if (a.ece_out) a.ece_out[k - 1] = be;
@@ -75,8 +92,8 @@ __global__ __launch_bounds__(256) void k_sts_apply(StsArgs a, int k) {
 
 hipError_t launch_sts_fit(const StsArgs& a, hipStream_t st) {
   for (int k = 1; k <= a.gamma; ++k) {
-    hipLaunchKernelGGL(k_sts_ece, dim3(a.G), dim3(kStsThreads), 0, st, a, k);
-    hipLaunchKernelGGL(k_sts_pick, dim3(1), dim3(64), 0, st, a, k);
+    hipLaunchKernelGGL(k_sts_ece, dim3(a.S, a.G), dim3(kStsThreads), 0, st, a, k);
+    hipLaunchKernelGGL(k_sts_pick, dim3(1), dim3(kStsPickThreads), 0, st, a, k);
     if (k < a.gamma)
       hipLaunchKernelGGL(k_sts_apply, dim3((a.n + 255) / 256), dim3(256), 0, st, a, k);
   }

@@ -99,13 +99,15 @@ struct SchedArgs {
 
 constexpr int kStsMaxBins = 64;
 constexpr int kStsMaxGrid = 256;
+constexpr int kStsMaxSlices = 32;
 
 struct StsArgs {
   int n, gamma, G, nbins;
+  int S;                     // example slices per temperature (1..kStsMaxSlices)
   const float* z;            // [n][gamma] raw confidence logits
   const int32_t* m;          // [n] accepted drafts
   double* A;                 // [n] workspace: cumulative product of earlier positions
-  double* ece_g;             // [G] workspace: ECE of every candidate at the current position
+  double* part;              // [G][nbins][S] workspace: per-slice signed bin sums
   float* t_out;              // [gamma]
   double* ece_out;           // [gamma] nullable
   float grid[kStsMaxGrid];   // candidate temperatures, in search order

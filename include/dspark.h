@@ -322,7 +322,8 @@ dspark_status dspark_acceptance_rate(int R, int gamma, int V, int r, float T, co
  *   nbins    1..64 (15 is the usual choice)
  *   t_out    out [gamma] float32 (a grid value per position)
  *   ece_out  out nullable [gamma] double: ECE at the chosen temperature
- *   ws       workspace of dspark_sts_workspace_bytes(n) bytes, 16-byte aligned
+ *   ws       workspace of dspark_sts_workspace_bytes(n) bytes (8 n + 4 MiB and a
+ *            little), 16-byte aligned
  */
 size_t dspark_sts_workspace_bytes(int n);
 dspark_status dspark_sts_fit(int n, int gamma, const float* z, const int32_t* m, const float* grid,
