@@ -68,7 +68,10 @@ def lib():
         L.orc_sts_fit.restype = i32
         L.orc_pack.argtypes = [i32, i32, P, P, P, P, P, P, P]
         L.orc_verify.argtypes = [i32, i32, i64, i32, f64, u64, u64, P, P, P, i32, P, P, P,
-                                 P, P, P, P, P, P, P, P, P, P, P]
+                                 P, P, P, P, P, P, P, P, P, P, P, P]
+        L.orc_draft_rnn.argtypes = [i32, i32, i64, i32, i32, f64, u64, u64, P, P, P, P, P, P, P,
+                                    P, P, i32, P, P, P, P, P, P, P, P]
+        L.orc_draft_rnn.restype = i32
         L.orc_verify.restype = i32
         _lib = L
     return _lib
@@ -144,6 +147,30 @@ def residual_row(t, s, lse_d, T):
 
 
 # -------------------------------------------------------------- the stages
+def draft_rnn(U, W1, W2t, Wr, h, x0, T, seed=0, rnd=0, req_ids=None, force_x=None,
+              force_e=None, bf16_e=True):
+    """RNN draft head.  U [R][gamma][V]; W1, W2t [V][r]; Wr [3r][2r+d]; h
+    [R][gamma][d]; x0 [R].  Returns (x, logp_d, lse_d, margin, x_own, e, s,
+    e_margin)."""
+    U = _f32(U)
+    R, gamma, V = U.shape
+    rank = int(W1.shape[1])
+    h = _f32(h)
+    d = h.shape[-1]
+    x = np.zeros((R, gamma + 1), np.int32)
+    lp, lse, mg = np.zeros((R, gamma)), np.zeros((R, gamma)), np.zeros((R, gamma))
+    xo = np.zeros((R, gamma + 1), np.int32)
+    e = np.zeros((R, gamma, rank))
+    s = np.zeros((R, gamma, rank))
+    em = np.zeros((R, gamma, rank))
+    rc = lib().orc_draft_rnn(R, gamma, V, rank, d, float(T), seed, rnd, _p(U), _p(_f32(W1)),
+                             _p(_f32(W2t)), _p(_f32(Wr)), _p(h), _p(_i32(x0)), _p(_i32(req_ids)),
+                             _p(_i32(force_x)), _p(_f32(force_e)), int(bool(bf16_e)), _p(x),
+                             _p(lp), _p(lse), _p(mg), _p(xo), _p(e), _p(s), _p(em))
+    assert rc == 0, rc
+    return x, lp, lse, mg, xo, e, s, em
+
+
 def draft_markov(U, W1, W2t, x0, T, seed=0, rnd=0, req_ids=None, force_x=None, own=False):
     """U [R][gamma][V]; W1, W2t [V][rank] or None; x0 [R].  With own=True also
     returns the oracle's own choice at every position given the forced prefix."""
@@ -304,7 +331,7 @@ def verify_cap_accept(ell, cap, cu, target, layout, x, logp_d, lse_d, U, W1, W2t
 
 
 def verify(ell, cu, target, layout, x, logp_d, lse_d, U, W1, W2t, T, seed=0, rnd=0,
-           req_ids=None, force_m=None):
+           req_ids=None, force_m=None, feat=None):
     ell = _i32(ell)
     R = ell.size
     x = _i32(x)
@@ -321,6 +348,7 @@ def verify(ell, cu, target, layout, x, logp_d, lse_d, U, W1, W2t, T, seed=0, rnd
     rc = lib().orc_verify(R, gamma, V, rank, float(T), seed, rnd, _p(ell), _p(_i32(cu)),
                           _p(target), int(layout), _p(x), _p(_f64(logp_d)), _p(_f64(lse_d)),
                           _p(_f32(U)), _p(_f32(W1)), _p(_f32(W2t)), _p(_i32(req_ids)),
-                          _p(_i32(force_m)), _p(m), _p(tau), _p(em), _p(na), _p(lpt), _p(mg))
+                          _p(_i32(force_m)), _p(m), _p(tau), _p(em), _p(na), _p(lpt), _p(mg),
+                          _p(_f32(feat)))
     assert rc == 0, rc
     return m, tau, em, na, lpt, mg

@@ -313,6 +313,119 @@ int orc_draft_markov(int R, int gamma, int64_t V, int rank, double T, uint64_t s
     return 0;
 }
 
+// -------------------------------------------------------------- RNN head ---
+// RNN draft head ([P3] Method details, RNN head): a recurrent state carries
+// the whole in-block prefix.  With z_k = [s_{k-1} ; W1[x_{k-1}] ; h_k] (length
+// 2r + d, s_0 = 0) and one projection Wr [3r][2r + d] whose rows are the gate,
+// candidate and output parts (no bias terms),
+//   g = sigmoid(Wr_g z_k),  s_k = g * s_{k-1} + (1 - g) * tanh(Wr_c z_k),
+//   e_k = tanh(Wr_o z_k),   bias_k(v) = sum_j e_k[j] W2t[v][j]  (= W2^T e_k),
+// then x_k is sampled from softmax((U_k + bias_k) / T) as for the Markov head
+// (same random stream).  Reading: e_k is the activation handed to the W2
+// projection in the model's dtype; with bf16_e it is rounded to bf16 (round to
+// nearest even), and e_margin reports, per element, the distance of the
+// unrounded value to the nearest bf16 rounding boundary relative to its size
+// (+inf when not rounded).  force_e (nullable, [R][gamma][r]) replaces e_k
+// after rounding (lock-step checking); force_x as for the Markov head.
+// Out: x, logp_d, lse_d, margin, x_own as orc_draft_markov; e [R][gamma][r]
+//      (the features used), s [R][gamma][r] (states s_1..s_gamma), e_margin.
+static double bf16_round(double v, double* rel_margin) {
+    // round to bf16 (8 significant bits) with ties to even, from the exact value
+    if (v == 0.0 || !std::isfinite(v)) { if (rel_margin) *rel_margin = POS_INF; return v; }
+    int ex;
+    const double m = std::frexp(std::fabs(v), &ex);     // |v| = m 2^ex, m in [0.5, 1)
+    const double scaled = m * 256.0;                     // 8 bits: [128, 256)
+    const double fl = std::floor(scaled);
+    const double frac = scaled - fl;
+    double r = fl;
+    if (frac > 0.5 || (frac == 0.5 && std::fmod(fl, 2.0) != 0.0)) r = fl + 1.0;
+    if (rel_margin) *rel_margin = std::fabs(frac - 0.5) / scaled;
+    return std::copysign(std::ldexp(r / 256.0, ex), v);
+}
+
+int orc_draft_rnn(int R, int gamma, int64_t V, int rank, int d, double T, uint64_t seed,
+                  uint64_t round, const float* U, const float* W1, const float* W2t,
+                  const float* Wr, const float* h, const int32_t* x0, const int32_t* req_ids,
+                  const int32_t* force_x, const float* force_e, int bf16_e, int32_t* x,
+                  double* logp_d, double* lse_d, double* margin, int32_t* x_own, double* e_out,
+                  double* s_out, double* e_margin) {
+    if (R < 0 || gamma < 1 || V < 1 || rank < 1 || d < 1 || !(T >= 0.0)) return 1;
+    const int nz = 2 * rank + d;
+    std::vector<double> sc(V), z(nz), st(rank), e(rank);
+    for (int i = 0; i < R; ++i) {
+        const uint32_t rid = req_ids ? (uint32_t)req_ids[i] : (uint32_t)i;
+        int32_t prev = x0[i];
+        x[(int64_t)i * (gamma + 1)] = prev;
+        if (x_own) x_own[(int64_t)i * (gamma + 1)] = prev;
+        std::fill(st.begin(), st.end(), 0.0);
+        for (int k = 1; k <= gamma; ++k) {
+            const int64_t o = (int64_t)i * gamma + (k - 1);
+            for (int j = 0; j < rank; ++j) z[j] = st[j];
+            for (int j = 0; j < rank; ++j) z[rank + j] = (double)W1[(int64_t)prev * rank + j];
+            for (int j = 0; j < d; ++j) z[2 * rank + j] = (double)h[o * d + j];
+            std::vector<double> gs(rank);
+            for (int j = 0; j < rank; ++j) {
+                double pg = 0.0, pc = 0.0, po = 0.0;
+                const float* rg = Wr + (int64_t)j * nz;
+                const float* rc = Wr + (int64_t)(rank + j) * nz;
+                const float* ro = Wr + (int64_t)(2 * rank + j) * nz;
+                for (int q = 0; q < nz; ++q) {
+                    pg += (double)rg[q] * z[q];
+                    pc += (double)rc[q] * z[q];
+                    po += (double)ro[q] * z[q];
+                }
+                const double g = 1.0 / (1.0 + std::exp(-pg));
+                gs[j] = g * st[j] + (1.0 - g) * std::tanh(pc);
+                double mgn = POS_INF;
+                double ev = std::tanh(po);
+                if (bf16_e) ev = bf16_round(ev, &mgn);
+                if (force_e) ev = (double)force_e[o * rank + j];
+                e[j] = ev;
+                if (e_margin) e_margin[o * rank + j] = mgn;
+            }
+            st = gs;
+            for (int j = 0; j < rank; ++j) {
+                if (e_out) e_out[o * rank + j] = e[j];
+                if (s_out) s_out[o * rank + j] = st[j];
+            }
+            const float* Uk = U + o * V;
+            for (int64_t v = 0; v < V; ++v) {
+                double b = 0.0;
+                const float* w = W2t + v * rank;
+                for (int j = 0; j < rank; ++j) b += e[j] * (double)w[j];
+                sc[v] = (double)Uk[v] + b;
+            }
+            int64_t xk;
+            double lp, lse, mg;
+            if (T > 0.0) {
+                for (int64_t v = 0; v < V; ++v) sc[v] /= T;
+                lse = logsumexp(sc.data(), V);
+                xk = cgm_sample(sc.data(), V, seed, round, TAG_DRAFT_CHUNK, TAG_DRAFT_ELEM, rid,
+                                (uint32_t)k, &mg);
+                if (x_own) x_own[(int64_t)i * (gamma + 1) + k] = (int32_t)xk;
+                if (force_x && force_x[(int64_t)i * (gamma + 1) + k] >= 0)
+                    xk = force_x[(int64_t)i * (gamma + 1) + k];
+                lp = sc[xk] - lse;
+            } else {
+                xk = argmax_f32_decision(sc.data(), V, &mg);
+                if (x_own) x_own[(int64_t)i * (gamma + 1) + k] = (int32_t)xk;
+                if (force_x && force_x[(int64_t)i * (gamma + 1) + k] >= 0)
+                    xk = force_x[(int64_t)i * (gamma + 1) + k];
+                double mx = NEG_INF;
+                for (int64_t v = 0; v < V; ++v) mx = std::max(mx, sc[v]);
+                lp = 0.0;
+                lse = mx;
+            }
+            x[(int64_t)i * (gamma + 1) + k] = (int32_t)xk;
+            if (logp_d) logp_d[o] = lp;
+            if (lse_d) lse_d[o] = lse;
+            if (margin) margin[o] = mg;
+            prev = (int32_t)xk;
+        }
+    }
+    return 0;
+}
+
 // ----------------------------------------------------------- confidence ---
 // c_k = sigmoid(w^T [h_k ; W1[x_{k-1}]] / t_k)  ([P3] Method details, confidence
 // head; optional per-position STS temperatures t_k, default 1).  The result is
@@ -543,6 +656,8 @@ void orc_pack(int R, int width, const int32_t* rows, const int32_t* len, int32_t
 //  x [R][gamma+1]; logp_d, lse_d [R][gamma] (the draft's outputs).
 //  U, W1, W2t as in the draft (used to rebuild p_d at a rejected position).
 //  force_m [R] nullable; entries >= 0 force the accepted count (lock-step).
+//  feat [R][gamma][rank] nullable: bias features of each position (the RNN
+//  head's e_k); when given they replace W1[x_{k-1}] in rebuilding p_d.
 // Out: m, tau [R]; emitted [R][gamma+1] (-1 past tau); next_anchor [R];
 //      logp_t [R][gamma] (log p_t(x_k) for k <= ell, else 0; 0 when T == 0);
 //      margin [R] (smallest decision margin of the request).
@@ -553,7 +668,7 @@ int orc_verify(int R, int gamma, int64_t V, int rank, double T, uint64_t seed, u
                const float* U, const float* W1, const float* W2t,
                const int32_t* req_ids, const int32_t* force_m,
                int32_t* m_out, int32_t* tau_out, int32_t* emitted, int32_t* next_anchor,
-               double* logp_t, double* margin) {
+               double* logp_t, double* margin, const float* feat) {
     if (R < 0 || gamma < 1 || V < 1 || !(T >= 0.0)) return 1;
     std::vector<double> lt(V), s(V), q(V), sc(V);
     for (int i = 0; i < R; ++i) {
@@ -595,8 +710,19 @@ int orc_verify(int R, int gamma, int64_t V, int rank, double T, uint64_t seed, u
                 const int k = m + 1;
                 const float* t = row(k - 1);
                 for (int64_t v = 0; v < V; ++v) lt[v] = (double)t[v] / T;
-                markov_scores(V, rank, U + ((int64_t)i * gamma + (k - 1)) * V, W1, W2t,
-                              xi[k - 1], s.data());
+                if (feat) {
+                    // the draft's bias features of this position (RNN head)
+                    const float* e = feat + ((int64_t)i * gamma + (k - 1)) * rank;
+                    const float* Uk = U + ((int64_t)i * gamma + (k - 1)) * V;
+                    for (int64_t v = 0; v < V; ++v) {
+                        double b = 0.0;
+                        for (int j = 0; j < rank; ++j) b += (double)e[j] * (double)W2t[v * rank + j];
+                        s[v] = (double)Uk[v] + b;
+                    }
+                } else {
+                    markov_scores(V, rank, U + ((int64_t)i * gamma + (k - 1)) * V, W1, W2t,
+                                  xi[k - 1], s.data());
+                }
                 for (int64_t v = 0; v < V; ++v) s[v] /= T;
                 const double tot = residual_weights(V, lt.data(), lse_t[k - 1], s.data(),
                                                     lse_d[(int64_t)i * gamma + (k - 1)], q.data());

@@ -287,3 +287,57 @@ def test_monte_carlo_cap_accept_lossless():
     bc[-1] += cc
     chi = stats.chisquare(bc, be)
     assert chi.pvalue > 1e-4, chi
+
+
+def test_monte_carlo_rnn_draft_lossless():
+    """Sampled RNN-head drafts verified with the residual rebuilt from the
+    draft's features: the emitted law is the target's."""
+    T = 1.0
+    U, W1, W2t, h, w, tl = _setup(31)
+    rng = np.random.default_rng(5)
+    Wr = rng.normal(0, 0.6, (3 * RANK, 2 * RANK + D)).astype(np.float32)
+    n = 120_000
+    anchor = 5
+    Ub = np.broadcast_to(U, (n, G, V))
+    hb = np.broadcast_to(h, (n, G, D))
+    x, lp, lse, _, _, e, _, _ = O.draft_rnn(Ub, W1, W2t, Wr, hb, np.full(n, anchor), T, seed=79,
+                                            rnd=5)
+    keys = list(tl.keys())
+    index = {k: i for i, k in enumerate(keys)}
+    table = np.stack([tl[k] for k in keys])
+    rows = np.zeros((n, G + 1), np.int64)
+    for j in range(G + 1):
+        rows[:, j] = [index[tuple(x[i, 1:j + 1])] for i in range(n)]
+    tgt = table[rows]
+    ell = np.full(n, G, np.int32)
+    m, tau, em, na, _, _ = O.verify(ell, None, tgt, 1, x, lp, lse, Ub, W1, W2t, T, seed=79, rnd=5,
+                                    feat=e)
+    rng2 = np.random.default_rng(97)
+    seqs = np.full((n, G + 1), -1, np.int64)
+    for i in range(n):
+        s = list(em[i, :tau[i]])
+        while len(s) < G + 1:
+            s.append(int(rng2.choice(V, p=_pt(tl, s, T))))
+        seqs[i] = s
+    codes = (seqs * (V ** np.arange(G, -1, -1))).sum(1)
+    counts = np.bincount(codes, minlength=V ** (G + 1))
+    probs = np.zeros(V ** (G + 1))
+    for s_, p in _target_law(tl, T).items():
+        probs[int(sum(v * V ** (G - j) for j, v in enumerate(s_)))] = p
+    order = np.argsort(probs)
+    be, bc, ce, cc = [], [], 0.0, 0
+    for i in order:
+        ce += probs[i] * n
+        cc += counts[i]
+        if ce >= 10:
+            be.append(ce)
+            bc.append(cc)
+            ce, cc = 0.0, 0
+    be[-1] += ce
+    bc[-1] += cc
+    chi = stats.chisquare(bc, be)
+    assert chi.pvalue > 1e-4, chi
+    # the same drafts verified as if they came from a Markov head (features
+    # ignored) emit a different law
+    m2, tau2, em2, *_ = O.verify(ell, None, tgt, 1, x, lp, lse, Ub, W1, W2t, T, seed=79, rnd=5)
+    assert (em2 != em).any()

@@ -872,3 +872,88 @@ def test_sts_fit_left_to_right_freezing():
     for k in range(4):
         c = 1 / (1 + np.exp(-z[:, k].astype(np.float64) / t[k]))
         assert (np.argsort(c, kind="stable") == np.argsort(z[:, k], kind="stable")).all()
+
+
+# --------------------------------------------------------------- RNN head --
+def _rnn_case(seed, R, g, V, rank, d):
+    rng = np.random.default_rng(seed)
+    U = rng.normal(0, 2, (R, g, V)).astype(np.float32)
+    W1 = rng.normal(0, 0.5, (V, rank)).astype(np.float32)
+    W2t = rng.normal(0, 0.3, (V, rank)).astype(np.float32)
+    Wr = rng.normal(0, 0.3, (3 * rank, 2 * rank + d)).astype(np.float32)
+    h = rng.normal(0, 1, (R, g, d)).astype(np.float32)
+    x0 = rng.integers(0, V, R)
+    return U, W1, W2t, Wr, h, x0
+
+
+def test_rnn_zero_projection_is_the_rank0_draft():
+    # Wr = 0: every feature is tanh(0) = 0, the bias vanishes (DFlash case)
+    U, W1, W2t, Wr, h, x0 = _rnn_case(40, 4, 5, 600, 16, 8)
+    for T in [1.0, 0.0]:
+        a = O.draft_rnn(U, W1, W2t, np.zeros_like(Wr), h, x0, T, seed=3)
+        b = O.draft_markov(U, None, None, x0, T, seed=3)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-12)
+        assert np.abs(a[5]).max() == 0.0 and np.abs(a[6]).max() == 0.0
+
+
+def test_rnn_closed_gate_is_a_markov_head_on_tanh_embeddings():
+    """Gate saturated open-state (g = 1 exactly: s stays 0) and an output part
+    that reads only the embedding: e_k = tanh(W1[x_{k-1}]), so the head is the
+    Markov head with the table tanh(W1) (computed here by numpy)."""
+    R, g, V, rank, d = 6, 5, 700, 16, 4
+    U, W1, W2t, Wr, h, x0 = _rnn_case(41, R, g, V, rank, d)
+    h[:, :, 0] = 1.0                                   # a constant feature
+    Wr = np.zeros_like(Wr)
+    Wr[:rank, 2 * rank] = 60.0                         # gate: sigmoid(60) == 1 in double
+    Wr[rank:2 * rank] = np.random.default_rng(1).normal(0, 1, (rank, 2 * rank + d))
+    Wr[2 * rank:, rank:2 * rank] = np.eye(rank)        # output: the embedding part
+    W1t = np.tanh(W1.astype(np.float64)).astype(np.float32)
+    for T in [1.0, 0.7, 0.0]:
+        a = O.draft_rnn(U, W1, W2t, Wr, h, x0, T, seed=4, bf16_e=False)
+        b = O.draft_markov(U, W1t, W2t, x0, T, seed=4, own=True)
+        assert np.abs(a[6]).max() == 0.0               # the state never moves
+        close = (b[3] > 1e-6)                          # decisions away from a tie
+        assert (a[0][:, 1:][close] == b[0][:, 1:][close]).all()
+        if T > 0:
+            np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-6)
+
+
+def test_rnn_state_and_features_layout():
+    """Rows [0, r) of Wr are the gate, [r, 2r) the candidate, [2r, 3r) the
+    output; z = [s ; W1[x] ; h].  Checked at k = 1 and k = 2 against numpy."""
+    from scipy import special as sp
+    R, g, V, rank, d = 3, 2, 200, 8, 5
+    U, W1, W2t, Wr, h, x0 = _rnn_case(42, R, g, V, rank, d)
+    x, _, _, _, _, e, s, _ = O.draft_rnn(U, W1, W2t, Wr, h, x0, 1.0, seed=5, bf16_e=False)
+    W = Wr.astype(np.float64)
+    for i in range(R):
+        st = np.zeros(rank)
+        for k in range(1, g + 1):
+            z = np.concatenate([st, W1[x[i, k - 1]].astype(np.float64), h[i, k - 1]])
+            gt = sp.expit(W[:rank] @ z)
+            st = gt * st + (1 - gt) * np.tanh(W[rank:2 * rank] @ z)
+            np.testing.assert_allclose(s[i, k - 1], st, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(e[i, k - 1], np.tanh(W[2 * rank:] @ z), rtol=0, atol=1e-12)
+
+
+def test_rnn_bf16_features_and_memory():
+    R, g, V, rank, d = 5, 4, 300, 16, 6
+    U, W1, W2t, Wr, h, x0 = _rnn_case(43, R, g, V, rank, d)
+    x, lp, lse, mg, xo, e, s, em = O.draft_rnn(U, W1, W2t, Wr, h, x0, 1.0, seed=6)
+    xr, _, _, _, _, er, _, _ = O.draft_rnn(U, W1, W2t, Wr, h, x0, 1.0, seed=6, bf16_e=False)
+    np.testing.assert_array_equal(x[:, :2], xr[:, :2])
+    # e is the bf16 rounding (nearest even) of the unrounded feature: torch's
+    # float32 -> bfloat16 conversion agrees wherever no float32 rounding sits
+    # between the two
+    import torch
+    ref = torch.tensor(er[:, :1], dtype=torch.float32).to(torch.bfloat16).double().numpy()
+    ok = em[:, :1] > 1e-6
+    assert ok.mean() > 0.99
+    np.testing.assert_array_equal(e[:, :1][ok], ref[ok])
+    # memory: e_3 depends on x_1 with x_2 held fixed (a Markov head cannot)
+    f1 = x.copy()
+    f1[:, 1] = (x[:, 1] + 1) % V
+    f1[:, 3:] = -1
+    _, _, _, _, _, e2, _, _ = O.draft_rnn(U, W1, W2t, Wr, h, x0, 1.0, seed=6, force_x=f1)
+    assert (np.abs(e2[:, 2] - e[:, 2]).max(axis=1) > 0).all()
