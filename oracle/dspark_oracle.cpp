@@ -323,15 +323,17 @@ int orc_draft_markov(int R, int gamma, int64_t V, int rank, double T, uint64_t s
 // then x_k is sampled from softmax((U_k + bias_k) / T) as for the Markov head
 // (same random stream).  Reading: e_k is the activation handed to the W2
 // projection in the model's dtype; with bf16_e it is rounded to bf16 (round to
-// nearest even), and e_margin reports, per element, the distance of the
-// unrounded value to the nearest bf16 rounding boundary relative to its size
+// nearest even), and e_margin reports, per element, the absolute distance of
+// the unrounded value to the nearest bf16 rounding boundary (the same absolute
+// scale as the other decision margins: an error in the pre-activation moves e
+// by an absolute amount whatever its size)
 // (+inf when not rounded).  force_e (nullable, [R][gamma][r]) replaces e_k
 // after rounding (lock-step checking); force_x as for the Markov head.
 // Out: x, logp_d, lse_d, margin, x_own as orc_draft_markov; e [R][gamma][r]
 //      (the features used), s [R][gamma][r] (states s_1..s_gamma), e_margin.
-static double bf16_round(double v, double* rel_margin) {
+static double bf16_round(double v, double* abs_margin) {
     // round to bf16 (8 significant bits) with ties to even, from the exact value
-    if (v == 0.0 || !std::isfinite(v)) { if (rel_margin) *rel_margin = POS_INF; return v; }
+    if (v == 0.0 || !std::isfinite(v)) { if (abs_margin) *abs_margin = POS_INF; return v; }
     int ex;
     const double m = std::frexp(std::fabs(v), &ex);     // |v| = m 2^ex, m in [0.5, 1)
     const double scaled = m * 256.0;                     // 8 bits: [128, 256)
@@ -339,7 +341,7 @@ static double bf16_round(double v, double* rel_margin) {
     const double frac = scaled - fl;
     double r = fl;
     if (frac > 0.5 || (frac == 0.5 && std::fmod(fl, 2.0) != 0.0)) r = fl + 1.0;
-    if (rel_margin) *rel_margin = std::fabs(frac - 0.5) / scaled;
+    if (abs_margin) *abs_margin = std::ldexp(std::fabs(frac - 0.5), ex - 8);   // in units of v
     return std::copysign(std::ldexp(r / 256.0, ex), v);
 }
 

@@ -947,6 +947,12 @@ def test_rnn_bf16_features_and_memory():
     # float32 -> bfloat16 conversion agrees wherever no float32 rounding sits
     # between the two
     import torch
+    # the reported margin is the absolute distance of the unrounded feature to
+    # the midpoint between its two neighbouring bf16 values (8 significant bits)
+    a = np.abs(er[:, :1])
+    ulp = np.exp2(np.floor(np.log2(a)) - 7)
+    mid = np.floor(a / ulp) * ulp + ulp / 2
+    np.testing.assert_allclose(em[:, :1], np.abs(a - mid), rtol=1e-9, atol=0)
     ref = torch.tensor(er[:, :1], dtype=torch.float32).to(torch.bfloat16).double().numpy()
     ok = em[:, :1] > 1e-6
     assert ok.mean() > 0.99
