@@ -26,7 +26,8 @@ EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
            "dspark_confidence", "dspark_prefix_schedule", "dspark_pack", "dspark_verify",
            "dspark_draft_markov_profiled", "dspark_async_schedule", "dspark_pack_tiered",
            "dspark_verify_cap_accept", "dspark_acceptance_rate", "dspark_sts_fit",
-           "dspark_sts_workspace_bytes", "dspark_confidence_logits")
+           "dspark_sts_workspace_bytes", "dspark_confidence_logits", "dspark_rnn_workspace_bytes",
+           "dspark_draft_rnn", "dspark_verify_features")
 
 
 class DsparkError(RuntimeError):
@@ -73,10 +74,16 @@ def load():
                                            P, P, P, P, i32, P, P, i32, P, P, P, P, P, P, P, sz, P]
     L.dspark_verify.argtypes = [i32, i32, i32, i32, f32, u64, u64, P, P, P, i32, i32, P, P, P, P,
                                 i32, P, P, i32, P, P, P, P, P, P, sz, P]
+    L.dspark_rnn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.dspark_rnn_workspace_bytes.restype = sz
+    L.dspark_draft_rnn.argtypes = [i32, i32, i32, i32, i32, f32, u64, u64, P, i32, P, P, i32, P, P,
+                                   i32, P, P, P, P, P, P, P, P, sz, P]
+    L.dspark_verify_features.argtypes = L.dspark_verify.argtypes
     for fn in EXPORTS:
         getattr(L, fn).restype = getattr(L, fn).restype or i32
     L.dspark_workspace_bytes.restype = sz
     L.dspark_sts_workspace_bytes.restype = sz
+    L.dspark_rnn_workspace_bytes.restype = sz
     L.dspark_status_string.restype = C.c_char_p
     L.dspark_version.restype = C.c_char_p
     _lib = L
@@ -274,3 +281,44 @@ def verify(ell, cu, target, layout, x, logp_d, lse_d, U, W1, W2t, T, seed, rnd, 
                                 _ptr(m), _ptr(tau), _ptr(emitted), _ptr(next_anchor),
                                 _ptr(logp_t), _ptr(ws), ws.numel(), _stream(stream))
     _check("dspark_verify", code)
+
+
+def rnn_workspace_bytes(R, gamma, V, r, d):
+    return int(load().dspark_rnn_workspace_bytes(R, gamma, V, r, d))
+
+
+def rnn_workspace(R, gamma, V, r, d, device="cuda"):
+    """Zeroed workspace for dspark_draft_rnn (its head is the shared layout,
+    so the same buffer serves the rest of the round)."""
+    return torch.zeros(max(256, rnn_workspace_bytes(R, gamma, V, r, d)), dtype=torch.uint8,
+                       device=device)
+
+
+def draft_rnn(U, W1, W2t, Wr, h, x0, T, seed, rnd, x, logp_d, lse_d, feat, ws, state=None,
+              margin=None, stream=None):
+    """U [R][gamma][V]; W1, W2t [V][r]; Wr [3r][2r+d]; h [R][gamma][d]; feat out
+    [R][gamma][r] in the weights' dtype; state out (nullable) [R][gamma][r] fp32."""
+    R, gamma, V = U.shape
+    r = int(W1.shape[1])
+    d = int(h.shape[-1])
+    code = load().dspark_draft_rnn(R, gamma, V, r, d, float(T), seed, rnd, _ptr(U), _dt(U),
+                                   _ptr(W1), _ptr(W2t), _dt(W1), _ptr(Wr), _ptr(h), _dt(h),
+                                   _ptr(x0), _ptr(x), _ptr(logp_d), _ptr(lse_d), _ptr(margin),
+                                   _ptr(feat), _ptr(state), _ptr(ws), ws.numel(), _stream(stream))
+    _check("dspark_draft_rnn", code)
+
+
+def verify_features(ell, cu, target, layout, x, logp_d, lse_d, U, feat, W2t, T, seed, rnd, m, tau,
+                    emitted, next_anchor, ws, logp_t=None, stream=None):
+    """dspark_verify with the draft's per-position features feat [R][gamma][r]."""
+    R = ell.shape[0]
+    gamma = x.shape[1] - 1
+    V = target.shape[-1]
+    r = int(feat.shape[-1])
+    code = load().dspark_verify_features(R, gamma, V, r, float(T), seed, rnd, _ptr(ell), _ptr(cu),
+                                         _ptr(target), _dt(target), int(layout), _ptr(x),
+                                         _ptr(logp_d), _ptr(lse_d), _ptr(U), _dt(U), _ptr(feat),
+                                         _ptr(W2t), _dt(feat), _ptr(m), _ptr(tau), _ptr(emitted),
+                                         _ptr(next_anchor), _ptr(logp_t), _ptr(ws), ws.numel(),
+                                         _stream(stream))
+    _check("dspark_verify_features", code)

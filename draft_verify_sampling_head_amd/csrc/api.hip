@@ -113,6 +113,46 @@ dspark_status dspark_draft_markov_profiled(int R, int gamma, int V, int r, float
                     margin, ws, ws_bytes, stream, ev_begin, ev_end, n_timed);
 }
 
+size_t dspark_rnn_workspace_bytes(int R, int gamma, int V, int r, int d) {
+  (void)d;
+  if (R < 0 || gamma < 1 || V < 1 || r < 0) return 0;
+  return rnn_ws_layout(R, gamma, V, r).total;
+}
+
+dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, int d, float T, uint64_t seed,
+                               uint64_t round, const void* U, dspark_dtype U_dt, const void* W1,
+                               const void* W2t, dspark_dtype W_dt, const void* Wr, const void* h,
+                               dspark_dtype h_dt, const int32_t* x0, int32_t* x, float* logp_d,
+                               float* lse_d, float* margin, void* feat, float* state, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  dspark_status s = shape_check(R, gamma, V);
+  if (s != DSPARK_OK) return s;
+  if (d < 1) return DSPARK_E_INVALID;
+  if ((s = rank_check(r)) != DSPARK_OK) return s;
+  if (r == 0) return DSPARK_E_UNSUPPORTED;
+  if (!(T >= 0.f) || !std::isfinite(T)) return DSPARK_E_INVALID;
+  if (!dtype_ok(U_dt) || !dtype_ok(W_dt) || !dtype_ok(h_dt)) return DSPARK_E_INVALID;
+  if (R == 0) return DSPARK_OK;
+  if (!U || !W1 || !W2t || !Wr || !h || !x0 || !x || !logp_d || !lse_d || !feat || !ws)
+    return DSPARK_E_INVALID;
+  if (!aligned16(W1) || !aligned16(W2t) || !aligned16(feat)) return DSPARK_E_UNSUPPORTED;
+  if (!aligned16(ws)) return DSPARK_E_INVALID;
+  const RnnWsLayout RL = rnn_ws_layout(R, gamma, V, r);
+  if (ws_bytes < RL.total) return DSPARK_E_WORKSPACE;
+  char* w = reinterpret_cast<char*>(ws);
+  RnnArgs a{};
+  a.R = R; a.gamma = gamma; a.V = V; a.rank = r; a.d = d;
+  a.W1 = W1; a.Wr = Wr; a.h = h; a.w_bf16 = W_dt == DSPARK_BF16; a.h_bf16 = h_dt == DSPARK_BF16;
+  a.x0 = x0; a.x = x;
+  a.P = reinterpret_cast<float*>(w + RL.P);
+  a.state = state ? state : reinterpret_cast<float*>(w + RL.state);
+  a.feat = feat;
+  a.status = reinterpret_cast<uint32_t*>(w + ws_layout(R, gamma, V).header);
+  return hip_status(launch_draft(R, gamma, V, r, T, seed, round, U, U_dt == DSPARK_BF16, W1, W2t,
+                                 W_dt == DSPARK_BF16, x0, x, logp_d, lse_d, margin, ws, stream,
+                                 nullptr, nullptr, nullptr, &a));
+}
+
 static dspark_status confidence_impl(int R, int gamma, int d, int r, int V, const void* h,
                                      dspark_dtype h_dt, const void* W1, dspark_dtype W_dt,
                                      const void* w, dspark_dtype w_dt, const float* sts_T,
@@ -235,7 +275,8 @@ static dspark_status verify_impl(int R, int gamma, int V, int r, float T, uint64
                                  const void* U, dspark_dtype U_dt, const void* W1, const void* W2t,
                                  dspark_dtype W_dt, int32_t* m, int32_t* tau, int32_t* emitted,
                                  int32_t* next_anchor, float* logp_t, void* ws, size_t ws_bytes,
-                                 hipStream_t stream, const int32_t* cap, int32_t* m_full) {
+                                 hipStream_t stream, const int32_t* cap, int32_t* m_full,
+                                 const void* feat = nullptr) {
   dspark_status s = shape_check(R, gamma, V);
   if (s != DSPARK_OK) return s;
   if ((s = rank_check(r)) != DSPARK_OK) return s;
@@ -254,7 +295,7 @@ static dspark_status verify_impl(int R, int gamma, int V, int r, float T, uint64
   return hip_status(launch_verify(R, gamma, V, r, T, seed, round, ell, cu, target, target_layout,
                                   x, logp_d, lse_d, U, U_dt == DSPARK_BF16, W1, W2t,
                                   W_dt == DSPARK_BF16, m, tau, emitted, next_anchor, logp_t, ws,
-                                  stream, cap, m_full));
+                                  stream, cap, m_full, feat));
 }
 
 size_t dspark_sts_workspace_bytes(int n) {
@@ -320,6 +361,22 @@ dspark_status dspark_verify(int R, int gamma, int V, int r, float T, uint64_t se
   return verify_impl(R, gamma, V, r, T, seed, round, ell, cu, target, t_dt, target_layout, x,
                      logp_d, lse_d, U, U_dt, W1, W2t, W_dt, m, tau, emitted, next_anchor, logp_t,
                      ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+dspark_status dspark_verify_features(int R, int gamma, int V, int r, float T, uint64_t seed,
+                                     uint64_t round, const int32_t* ell, const int32_t* cu,
+                                     const void* target, dspark_dtype t_dt, int target_layout,
+                                     const int32_t* x, const float* logp_d, const float* lse_d,
+                                     const void* U, dspark_dtype U_dt, const void* feat,
+                                     const void* W2t, dspark_dtype W_dt, int32_t* m, int32_t* tau,
+                                     int32_t* emitted, int32_t* next_anchor, float* logp_t,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (r == 0 && R > 0) return DSPARK_E_UNSUPPORTED;
+  if (R > 0 && !feat) return DSPARK_E_INVALID;
+  // the features take W1's place in the argument checks
+  return verify_impl(R, gamma, V, r, T, seed, round, ell, cu, target, t_dt, target_layout, x,
+                     logp_d, lse_d, U, U_dt, feat, W2t, W_dt, m, tau, emitted, next_anchor,
+                     logp_t, ws, ws_bytes, stream, nullptr, nullptr, feat);
 }
 
 dspark_status dspark_verify_cap_accept(int R, int gamma, int V, int r, float T, uint64_t seed,

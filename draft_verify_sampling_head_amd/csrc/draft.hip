@@ -40,6 +40,7 @@ struct DraftPickArgs {
   const void* U;
   const void* W1;
   const void* W2t;
+  const void* feat;         // nullable: per-position bias features [R][gamma][rank] (RNN head)
   const int32_t* x0;
   int32_t* x;
   float* logp_d;
@@ -92,7 +93,8 @@ __device__ __forceinline__ void pick_row(const DraftPickArgs& a, int i, BlockScr
     float b = 0.f;
     if (a.rank > 0 && in) {
       const int pv = (prev >= 0 && prev < a.V) ? prev : 0;
-      const WT* erow = reinterpret_cast<const WT*>(a.W1) + (int64_t)pv * a.rank;
+      const WT* erow = a.feat ? reinterpret_cast<const WT*>(a.feat) + ((int64_t)i * a.gamma + (k - 1)) * a.rank
+                              : reinterpret_cast<const WT*>(a.W1) + (int64_t)pv * a.rank;
       b = markov_bias_half<(NT > 256 ? 2 : 8)>(erow, reinterpret_cast<const WT*>(a.W2t), a.rank, v, h, TPE);
     }
 #pragma unroll
@@ -993,6 +995,7 @@ struct ResidArgs {
   const float* lse_d;
   float2* L;                                // out [slot][nch] (0, residual mass)
   uint32_t* status;
+  bool feat_rows;                           // W1 holds per-position features [R][gamma][rank]
 };
 
 template <int KS, bool OVERLAP>
@@ -1025,8 +1028,13 @@ void k_resid_stats(ResidArgs A) {
     const int rows = min(kPRows, nrows - row0);
     for (int rl = tid; rl < rows; rl += kPThreads) {
       const int4 e = A.rej[row0 + rl];
-      int prev = A.x[(int64_t)e.x * (A.gamma + 1) + (e.y - 1)];
-      if (prev < 0 || prev >= V) { set_flag(A.status, kFlagBadToken); prev = 0; }
+      int prev;
+      if (A.feat_rows) {
+        prev = e.x * A.gamma + (e.y - 1);
+      } else {
+        prev = A.x[(int64_t)e.x * (A.gamma + 1) + (e.y - 1)];
+        if (prev < 0 || prev >= V) { set_flag(A.status, kFlagBadToken); prev = 0; }
+      }
       PV[rl] = prev;
     }
     __syncthreads();
@@ -1099,7 +1107,7 @@ bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void*
                          const void* W1, const void* W2t, const void* target, const int32_t* x,
                          const int32_t* rej_count, const int4* rej, const float2* lse_t,
                          const float* lse_d, float2* L, uint32_t* status, hipStream_t st,
-                         hipError_t* err, bool overlap) {
+                         hipError_t* err, bool overlap, bool feat_rows) {
   const char* env = std::getenv("DSPARK_DRAFT_KERNEL");
   if (env && std::strcmp(env, "steps") == 0) return false;
   if ((V % 8) != 0 || (rank != 64 && rank != 128 && rank != 256)) return false;
@@ -1115,6 +1123,7 @@ bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void*
   A.target = reinterpret_cast<const uint16_t*>(target);
   A.x = x; A.rej_count = rej_count; A.rej = rej; A.lse_t = lse_t; A.lse_d = lse_d; A.L = L;
   A.status = status;
+  A.feat_rows = feat_rows;
 #define DSPARK_RS(KS_, OV_) hipLaunchKernelGGL((k_resid_stats<KS_, OV_>), dim3(A.nslice), dim3(kPThreads), 0, st, A)
   if (overlap) {
     if (rank == 64) DSPARK_RS(4, true); else if (rank == 128) DSPARK_RS(8, true); else DSPARK_RS(16, true);
@@ -1206,7 +1215,7 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
                         const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
                         const int32_t* x0, int32_t* x, float* logp_d, float* lse_d, float* margin,
                         void* ws, hipStream_t st, hipEvent_t* ev_begin, hipEvent_t* ev_end,
-                        int* n_timed) {
+                        int* n_timed, const RnnArgs* rnn) {
   const WsLayout L = ws_layout(R, gamma, V);
   char* w = reinterpret_cast<char*>(ws);
   uint32_t* status = reinterpret_cast<uint32_t*>(w + L.header);
@@ -1224,7 +1233,11 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
   p.U = U; p.W1 = W1; p.W2t = W2t; p.x0 = x0; p.x = x; p.logp_d = logp_d; p.lse_d = lse_d;
   p.margin = margin; p.L = Lc; p.I = Ic; p.status = status;
 
-  const int grid = persistent_grid(gamma, V, rank, u_bf16, w_bf16, u_vec, W1, W2t, greedy);
+  // The RNN head's features e_k come from a recurrent cell launched before
+  // each step; its draft always takes the per-step schedule.
+  const void* feat = rnn ? rnn->feat : nullptr;
+  p.feat = feat;
+  const int grid = rnn ? 0 : persistent_grid(gamma, V, rank, u_bf16, w_bf16, u_vec, W1, W2t, greedy);
   if (grid > 0) {
     PersistArgs P{};
     P.p = p;
@@ -1249,8 +1262,13 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     return hipSuccess;
   }
 
+  if (rnn) {
+    const hipError_t e = launch_rnn_hproj(*rnn, st);
+    if (e != hipSuccess) return e;
+  }
   for (int k = 1; k <= gamma; ++k) {
     hipError_t e;
+    if (rnn && (e = launch_rnn_cell(*rnn, k, st)) != hipSuccess) return e;
     if (ev_begin && (e = hipEventRecord(ev_begin[k - 1], st)) != hipSuccess) return e;
     if (rank == 0) {
       RowStatsArgs a{};
@@ -1261,7 +1279,8 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     } else {
       MarkovArgs a{};
       a.R = R; a.gamma = gamma; a.k = k; a.V = V; a.rank = rank; a.nch = nch; a.nrows_cap = R;
-      a.U = U; a.W1v = W1; a.W2tv = W2t; a.x0 = x0; a.x = x; a.scale2 = scale2; a.u_vec_ok = u_vec;
+      a.U = U; a.W1v = feat ? feat : W1; a.W2tv = W2t; a.x0 = x0; a.x = x; a.feat_rows = feat != nullptr;
+      a.scale2 = scale2; a.u_vec_ok = u_vec;
       a.L = Lc; a.I = Ic; a.status = status;
       e = launch_markov_stats(a, u_bf16, w_bf16, greedy ? kModeGreedy : kModeSample, st);
     }

@@ -36,6 +36,7 @@ struct MarkovArgs {
   const uint16_t* W2t;
   const int32_t* x0;       // draft anchors
   const int32_t* x;        // [R][gamma+1]
+  bool feat_rows;          // W1 holds per-position features [R][gamma][rank] (RNN head)
   float scale2;
   bool u_vec_ok;
   float2* L;               // [row][nch] as RowStatsArgs; residual: (0, sum max(0, p_t - p_d))
@@ -113,6 +114,24 @@ struct StsArgs {
   float grid[kStsMaxGrid];   // candidate temperatures, in search order
 };
 
+// RNN draft head: the recurrent cell that produces the bias features e_k.
+struct RnnArgs {
+  int R, gamma, V, rank, d;
+  const void* W1;          // [V][rank] token embeddings (W dtype)
+  const void* Wr;          // [3 rank][2 rank + d] gate / candidate / output rows (W dtype)
+  const void* h;           // [R][gamma][d] backbone hidden states
+  bool w_bf16, h_bf16;
+  const int32_t* x0;       // [R] anchors
+  const int32_t* x;        // [R][gamma+1] drafted tokens (x[i][k-1] read at step k)
+  float* P;                // [R*gamma][3 rank] workspace: the h part of the projection
+  float* state;            // [R][gamma][rank] s_1 .. s_gamma
+  void* feat;              // [R][gamma][rank] e_1 .. e_gamma (W dtype)
+  uint32_t* status;
+};
+
+hipError_t launch_rnn_hproj(const RnnArgs& a, hipStream_t st);
+hipError_t launch_rnn_cell(const RnnArgs& a, int k, hipStream_t st);
+
 hipError_t launch_sts_fit(const StsArgs& a, hipStream_t st);
 hipError_t launch_row_stats(const RowStatsArgs& a, bool bf16, bool greedy, hipStream_t st);
 hipError_t launch_markov_stats(const MarkovArgs& a, bool u_bf16, bool w_bf16, int mode,
@@ -126,12 +145,13 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
                         const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
                         const int32_t* x0, int32_t* x, float* logp_d, float* lse_d, float* margin,
                         void* ws, hipStream_t st, hipEvent_t* ev_begin = nullptr,
-                        hipEvent_t* ev_end = nullptr, int* n_timed = nullptr);
+                        hipEvent_t* ev_end = nullptr, int* n_timed = nullptr,
+                        const RnnArgs* rnn = nullptr);
 bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void* U,
                          const void* W1, const void* W2t, const void* target, const int32_t* x,
                          const int32_t* rej_count, const int4* rej, const float2* lse_t,
                          const float* lse_d, float2* L, uint32_t* status, hipStream_t st,
-                         hipError_t* err, bool overlap = false);
+                         hipError_t* err, bool overlap = false, bool feat_rows = false);
 hipError_t launch_acceptance_rate(int R, int gamma, int V, int rank, float T, const void* target,
                                   const int32_t* x, const float* lse_d, const void* U, bool u_bf16,
                                   const void* W1, const void* W2t, bool w_bf16, float* c_star,
@@ -142,6 +162,6 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
                          const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
                          int32_t* m, int32_t* tau, int32_t* emitted, int32_t* next_anchor,
                          float* logp_t, void* ws, hipStream_t st, const int32_t* cap = nullptr,
-                         int32_t* m_full = nullptr);
+                         int32_t* m_full = nullptr, const void* feat = nullptr);
 
 }  // namespace dspark

@@ -30,6 +30,18 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// Row of the bias-feature table that multiplies W2 for (request req, block
+// position kk).  Markov head: W1[x_{kk-1}] (x_0 the anchor, read from x0 when
+// use_x0 is set and kk == 1; a token outside the vocabulary is flagged and
+// replaced by 0).  With feat_rows the table is the per-position feature tensor
+// [R][gamma][rank] of the RNN head and the row is req * gamma + kk - 1.
+__device__ __forceinline__ int bias_row_index(const MarkovArgs& a, int req, int kk, bool use_x0) {
+  if (a.feat_rows) return req * a.gamma + (kk - 1);
+  int prev = (use_x0 && kk == 1) ? a.x0[req] : a.x[(int64_t)req * (a.gamma + 1) + (kk - 1)];
+  if (prev < 0 || prev >= a.V) { set_flag(a.status, kFlagBadToken); prev = 0; }
+  return prev;
+}
+
 // ===================================================================== rows
 template <typename T>
 __device__ __forceinline__ void load_vec(const T* p, float* out);
@@ -309,11 +321,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma_reg(MarkovArgs a) {
       }
     }
     int prev = 0;
-    if (valid[nt]) {
-      prev = (MODE != kModeResid && kk == 1) ? a.x0[req]
-                                             : a.x[(int64_t)req * (a.gamma + 1) + (kk - 1)];
-      if (prev < 0 || prev >= a.V) { set_flag(a.status, kFlagBadToken); prev = 0; }
-    }
+    if (valid[nt]) prev = bias_row_index(a, req, kk, MODE != kModeResid);
     prevs[nt] = prev;
     urow[nt] = reinterpret_cast<const UT*>(a.U) + ((int64_t)req * a.gamma + (kk - 1)) * a.V;
     trow[nt] = reinterpret_cast<const UT*>(a.target) + (int64_t)tr * a.V;
@@ -586,11 +594,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
     int req, kk, tr, qr;
     row_info(row, req, kk, tr, qr);
     int prev = 0;
-    if (valid[nt]) {
-      prev = (MODE != kModeResid && kk == 1) ? a.x0[req]
-                                             : a.x[(int64_t)req * (a.gamma + 1) + (kk - 1)];
-      if (prev < 0 || prev >= a.V) { set_flag(a.status, kFlagBadToken); prev = 0; }
-    }
+    if (valid[nt]) prev = bias_row_index(a, req, kk, MODE != kModeResid);
     prevs[nt] = prev;
     trow[nt] = reinterpret_cast<const UT*>(a.target) + (int64_t)tr * a.V;
     mt[nt] = 0.f; lrt2[nt] = 0.f; lse_d[nt] = 0.f;
@@ -953,9 +957,7 @@ __global__ __launch_bounds__(256) void k_markov_valu(MarkovArgs a) {
       const int4 e = a.rej[row];
       req = e.x; kk = e.y; trow = e.z; qrow = e.w;
     }
-    int prev = (MODE != kModeResid && kk == 1) ? a.x0[req]
-                                               : a.x[(int64_t)req * (a.gamma + 1) + (kk - 1)];
-    if (prev < 0 || prev >= a.V) { set_flag(a.status, kFlagBadToken); prev = 0; }
+    const int prev = bias_row_index(a, req, kk, MODE != kModeResid);
     const UT* urow = reinterpret_cast<const UT*>(a.U) + ((int64_t)req * a.gamma + (kk - 1)) * a.V;
     const WT* erow = W1 + (int64_t)prev * a.rank;
     float sv[2];

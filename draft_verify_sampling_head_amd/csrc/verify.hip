@@ -44,6 +44,7 @@ struct VerifyArgs {
   const void* U;
   const void* W1;
   const void* W2t;
+  const void* feat;     // nullable: per-position bias features [R][gamma][rank] (RNN head)
   int32_t* m;
   int32_t* tau;
   int32_t* emitted;
@@ -203,7 +204,8 @@ __global__ __launch_bounds__(256) void k_resid_pick(VerifyArgs a) {
     const UT* urow = reinterpret_cast<const UT*>(a.U) + ((int64_t)i * a.gamma + (k - 1)) * a.V;
     int prev = a.x[(int64_t)i * (a.gamma + 1) + (k - 1)];
     if (prev < 0 || prev >= a.V) prev = 0;
-    const WT* erow = reinterpret_cast<const WT*>(a.W1) + (int64_t)prev * a.rank;
+    const WT* erow = a.feat ? reinterpret_cast<const WT*>(a.feat) + ((int64_t)i * a.gamma + (k - 1)) * a.rank
+                            : reinterpret_cast<const WT*>(a.W1) + (int64_t)prev * a.rank;
     const float lse_d = a.lse_d[(int64_t)i * a.gamma + (k - 1)];
     float b = 0.f;
     if (a.rank > 0 && v < a.V) b = markov_bias_half(erow, reinterpret_cast<const WT*>(a.W2t), a.rank, v, h);
@@ -370,7 +372,7 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
                          const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
                          int32_t* m, int32_t* tau, int32_t* emitted, int32_t* next_anchor,
                          float* logp_t, void* ws, hipStream_t st, const int32_t* cap,
-                         int32_t* m_full) {
+                         int32_t* m_full, const void* feat) {
   const WsLayout L = ws_layout(R, gamma, V);
   char* w = reinterpret_cast<char*>(ws);
   uint32_t* hdr = reinterpret_cast<uint32_t*>(w + L.header);
@@ -400,6 +402,7 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
   a.ell = ell; a.cu = cu; a.target = target; a.x = x; a.logp_d = logp_d; a.lse_d = lse_d;
   a.U = U; a.W1 = W1; a.W2t = W2t; a.m = m; a.tau = tau; a.emitted = emitted;
   a.next_anchor = next_anchor; a.logp_t = logp_t; a.cap = cap; a.m_full = m_full;
+  a.feat = feat;
   a.vl = rs.L; a.vi = rs.I;
   a.lse_t = reinterpret_cast<float2*>(w + L.lse_t);
   a.rej_count = reinterpret_cast<int32_t*>(hdr + 1);
@@ -416,15 +419,20 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
   e = hipGetLastError();
   if (e != hipSuccess || greedy) return e;
 
+  // rows of the bias features: W1[x_{k-1}] (Markov head) or the draft's own
+  // per-position features (RNN head)
+  const void* E = feat ? feat : W1;
   if (u_bf16 && w_bf16 && rank > 0 && u_vec && t_vec &&
-      launch_resid_slices(R, gamma, V, rank, T, U, W1, W2t, target, x, a.rej_count, a.rej,
-                          a.lse_t, lse_d, const_cast<float2*>(a.rl), hdr, st, &e)) {
+      launch_resid_slices(R, gamma, V, rank, T, U, E, W2t, target, x, a.rej_count, a.rej,
+                          a.lse_t, lse_d, const_cast<float2*>(a.rl), hdr, st, &e, false,
+                          feat != nullptr)) {
     if (e != hipSuccess) return e;
   } else {
     // per-tile kernel for the other shapes
     MarkovArgs ma{};
     ma.R = R; ma.gamma = gamma; ma.k = 0; ma.V = V; ma.rank = rank; ma.nch = nch; ma.nrows_cap = R;
-    ma.U = U; ma.W1v = W1; ma.W2tv = W2t; ma.x0 = nullptr; ma.x = x; ma.scale2 = kLog2e / T;
+    ma.U = U; ma.W1v = E; ma.W2tv = W2t; ma.x0 = nullptr; ma.x = x; ma.feat_rows = feat != nullptr;
+    ma.scale2 = kLog2e / T;
     ma.u_vec_ok = u_vec && t_vec;
     ma.L = const_cast<float2*>(a.rl); ma.I = nullptr;
     ma.rej_count = a.rej_count; ma.rej = a.rej; ma.target = target; ma.lse_t = a.lse_t;

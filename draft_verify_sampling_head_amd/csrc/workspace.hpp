@@ -41,4 +41,22 @@ inline WsLayout ws_layout(int R, int gamma, int V) {
   return L;
 }
 
+// RNN draft head: the shared layout, then the h part of the cell's projection
+// and the recurrent states (used when the caller passes no state buffer).
+struct RnnWsLayout {
+  size_t P;            // float [R*gamma][3 rank]
+  size_t state;        // float [R][gamma][rank]
+  size_t total;
+};
+
+inline RnnWsLayout rnn_ws_layout(int R, int gamma, int V, int rank) {
+  const size_t pos = (size_t)R * (size_t)gamma;
+  RnnWsLayout L;
+  size_t off = ws_layout(R, gamma, V).total;
+  L.P = off;     off += ws_align(pos * 3 * (size_t)rank * 4);
+  L.state = off; off += ws_align(pos * (size_t)rank * 4);
+  L.total = off;
+  return L;
+}
+
 }  // namespace dspark

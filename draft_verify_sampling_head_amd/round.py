@@ -1,6 +1,6 @@
 """One DSpark round on the GPU: the six C-ABI calls enqueued back to back.
 
-draft (Markov head) -> confidence -> prefix schedule (Algorithm 1, static, or
+draft (Markov head, or the RNN head) -> confidence -> prefix schedule (Algorithm 1, static, or
 the asynchronous form with a two-slot capacity ring) -> pack the verify batch
 (optionally padded to a graph tier) -> verify (compact: the scheduled window;
 cap-accept: the whole block, committed within the scheduled window) -> pack
@@ -18,7 +18,9 @@ from . import _lib as L
 class RoundBuffers:
     """Outputs and workspace of one round, allocated once and reused."""
 
-    def __init__(self, R, gamma, V, device="cuda", slots=None):
+    def __init__(self, R, gamma, V, device="cuda", slots=None, rnn=None):
+        """rnn: (rank, d, weight dtype) to hold the RNN head's features and
+        states (and its larger workspace)."""
         i32, f32 = torch.int32, torch.float32
         dev = torch.device(device)
         self.R, self.gamma, self.V = R, gamma, V
@@ -47,7 +49,14 @@ class RoundBuffers:
         self.cu_out = torch.empty(R + 1, dtype=i32, device=dev)
         self.flat_out = torch.empty(cap, dtype=i32, device=dev)
         self.N_out = torch.empty(1, dtype=i32, device=dev)
-        self.ws = L.workspace(R, gamma, V, device=dev)
+        self.feat = self.state = None
+        if rnn is not None:
+            rank, d, wdt = rnn
+            self.feat = torch.empty(R, gamma, rank, dtype=wdt, device=dev)
+            self.state = torch.empty(R, gamma, rank, dtype=f32, device=dev)
+            self.ws = L.rnn_workspace(R, gamma, V, rank, d, device=dev)
+        else:
+            self.ws = L.workspace(R, gamma, V, device=dev)
 
 
 class CapacityRing:
@@ -70,7 +79,7 @@ class CapacityRing:
 
 def run_round(inp, buf: RoundBuffers, T, seed, rnd, scheduler=True, layout=1, sts_T=None,
               stream=None, ring: CapacityRing = None, verify_mode="compact", tiers=None,
-              pad_token=0):
+              pad_token=0, head="markov"):
     """Enqueue one full round on `stream` (default: torch's current stream).
 
     `inp` holds U, W1, W2t, x0, h, w, sps and target (dense [R][gamma+1][V] for
@@ -79,9 +88,19 @@ def run_round(inp, buf: RoundBuffers, T, seed, rnd, scheduler=True, layout=1, st
     with capacities from `ring`.  `verify_mode` "cap-accept" packs and verifies
     the whole block and commits within the scheduled window.  `tiers` (host
     ints, ascending) pads the verify batch to the smallest tier that holds it
-    (`buf.N_pad`; the buffers need slots >= the largest tier)."""
-    L.draft_markov(inp["U"], inp["W1"], inp["W2t"], inp["x0"], T, seed, rnd, buf.x, buf.logp_d,
-                   buf.lse_d, buf.ws, stream=stream)
+    (`buf.N_pad`; the buffers need slots >= the largest tier).  `head` "rnn"
+    drafts with the RNN head (`inp["Wr"]`; buffers made with `rnn=`) and
+    verifies with its features."""
+    rnn = head == "rnn"
+    if rnn:
+        if verify_mode != "compact":
+            raise ValueError("the RNN head is verified in compact mode")
+        L.draft_rnn(inp["U"], inp["W1"], inp["W2t"], inp["Wr"], inp["h"], inp["x0"], T, seed, rnd,
+                    buf.x, buf.logp_d, buf.lse_d, buf.feat, buf.ws, state=buf.state,
+                    stream=stream)
+    else:
+        L.draft_markov(inp["U"], inp["W1"], inp["W2t"], inp["x0"], T, seed, rnd, buf.x,
+                       buf.logp_d, buf.lse_d, buf.ws, stream=stream)
     L.confidence(inp["h"], inp["W1"], inp["w"], buf.x, buf.c, sts_T=sts_T, V=buf.V, stream=stream)
     if scheduler == "async":
         kin, kplan = ring.slots(rnd)
@@ -102,6 +121,10 @@ def run_round(inp, buf: RoundBuffers, T, seed, rnd, scheduler=True, layout=1, st
                             buf.lse_d, inp["U"], inp["W1"], inp["W2t"], T, seed, rnd, buf.m,
                             buf.tau, buf.emitted, buf.next_anchor, buf.ws, m_full=buf.m_full,
                             logp_t=buf.logp_t, stream=stream)
+    elif rnn:
+        L.verify_features(buf.ell, buf.cu, inp["target"], layout, buf.x, buf.logp_d, buf.lse_d,
+                          inp["U"], buf.feat, inp["W2t"], T, seed, rnd, buf.m, buf.tau,
+                          buf.emitted, buf.next_anchor, buf.ws, logp_t=buf.logp_t, stream=stream)
     else:
         L.verify(buf.ell, buf.cu, inp["target"], layout, buf.x, buf.logp_d, buf.lse_d, inp["U"],
                  inp["W1"], inp["W2t"], T, seed, rnd, buf.m, buf.tau, buf.emitted, buf.next_anchor,

@@ -13,6 +13,9 @@ The backbone (base logits U_k, hidden states h_k) and the target model
   W1, W2  ~ N(0, 0.02^2)  (W2 stored transposed, [V][r])
   w       ~ N(0, 0.05^2), h ~ N(0, 1), anchors uniform in [0, V)
   SPS(B)  the engine cost table, dense for B = 0..N_max
+  Wr      (RNN head) ~ N(0, (gain / sqrt(2r + d))^2), so the cell's
+          pre-activations have a spread of about `gain`; drawn from a stream of
+          its own, so the other inputs do not change
 Sizes follow the pages' settings: block sizes 7-16, Qwen3 / DeepSeek
 vocabularies (151936 / 129280), up to 1024 concurrent requests.
 """
@@ -171,3 +174,12 @@ def make_inputs(cfg: Config, device="cpu", batch_rows: int = 2048) -> dict:
     out["sps"] = sps_table(cfg, N_max).to(device)
     out["hard"] = hard
     return out
+
+
+def rnn_weights(cfg: Config, device="cpu", gain: float = 1.0) -> torch.Tensor:
+    """Projection of the RNN head, Wr [3r][2r + d] in the config's dtype."""
+    r, d = cfg.rank, cfg.d
+    g = torch.Generator(device=device)
+    g.manual_seed(cfg.data_seed + 7919)
+    std = gain / math.sqrt(2 * r + d)
+    return (torch.randn(3 * r, 2 * r + d, generator=g, device=device) * std).to(cfg.dtype)

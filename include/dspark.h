@@ -369,6 +369,68 @@ dspark_status dspark_verify_cap_accept(int R, int gamma, int V, int r, float T, 
                                        int32_t* next_anchor, int32_t* m_full, float* logp_t,
                                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * (host) Bytes of workspace dspark_draft_rnn needs for these sizes: the
+ * shared workspace of dspark_workspace_bytes plus the h part of the cell's
+ * projection ([R gamma][3r] float32) and the states when `state` is NULL
+ * ([R][gamma][r] float32).  The first dspark_workspace_bytes bytes are laid
+ * out as for every other entry point, so the same buffer serves the round.
+ */
+size_t dspark_rnn_workspace_bytes(int R, int gamma, int V, int r, int d);
+
+/*
+ * RNN draft head over one block ([P3] Method details, RNN head: a gated
+ * recurrent state carries the whole in-block prefix, so the transition bias
+ * of position k depends on every earlier draft, not only on x_{k-1}).  With
+ * z_k = [s_{k-1} ; W1[x_{k-1}] ; h_k] (length 2r + d, s_0 = 0) and
+ * Wr = [Wr_g ; Wr_c ; Wr_o] (3r rows, no bias terms):
+ *   g_k = sigmoid(Wr_g z_k),  s_k = g_k * s_{k-1} + (1 - g_k) * tanh(Wr_c z_k),
+ *   e_k = tanh(Wr_o z_k),     bias_k = W2^T e_k (e_k rounded to W_dt),
+ * then x_k is drawn from softmax((U_k + bias_k) / T) by the same rule and
+ * random stream as dspark_draft_markov (T == 0: first argmax).
+ *   U, W1, W2t, x0, x, logp_d, lse_d, margin  as for dspark_draft_markov
+ *   Wr     [3r][2r + d]     (W_dt) rows 0..r-1 gate, r..2r-1 candidate,
+ *                           2r..3r-1 output; columns [s ; W1 row ; h]
+ *   h      [R][gamma][d]    backbone hidden states (h_dt)
+ *   feat   out [R][gamma][r]  e_1..e_gamma in W_dt (the bias features; pass
+ *                           them to dspark_verify_features)
+ *   state  out nullable [R][gamma][r] float32  s_1..s_gamma
+ *   ws     at least dspark_rnn_workspace_bytes(R, gamma, V, r, d) bytes
+ * r must be a multiple of 16 in [16, 512].  The h part of the projection is one
+ * contraction over all positions before the chain (MFMA when h and Wr are
+ * bf16 with d a multiple of 8 and 16-byte aligned tables); each step then
+ * runs the cell (fp32, vector ALU), the per-chunk statistics of U_k + bias_k
+ * (MFMA for bf16 weights) and the pick, three launches per step.
+ */
+dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, int d, float T,
+                               uint64_t seed, uint64_t round,
+                               const void* U, dspark_dtype U_dt,
+                               const void* W1, const void* W2t, dspark_dtype W_dt,
+                               const void* Wr, const void* h, dspark_dtype h_dt,
+                               const int32_t* x0, int32_t* x, float* logp_d, float* lse_d,
+                               float* margin, void* feat, float* state,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * dspark_verify for drafts whose bias is carried by per-position features
+ * (the RNN head above): identical accept tests and random streams; at a
+ * rejected position k the draft distribution is rebuilt as
+ * softmax((U_k + W2^T e_k) / T) from feat row i*gamma + k-1 instead of
+ * W1[x_{k-1}] W2 ([P1] 2.2: the residual needs the p_d actually sampled).
+ *   feat   [R][gamma][r] (W_dt) the draft's features; W1 is not read
+ *   other arguments as for dspark_verify (r >= 16)
+ */
+dspark_status dspark_verify_features(int R, int gamma, int V, int r, float T,
+                                     uint64_t seed, uint64_t round,
+                                     const int32_t* ell, const int32_t* cu,
+                                     const void* target, dspark_dtype t_dt, int target_layout,
+                                     const int32_t* x, const float* logp_d, const float* lse_d,
+                                     const void* U, dspark_dtype U_dt,
+                                     const void* feat, const void* W2t, dspark_dtype W_dt,
+                                     int32_t* m, int32_t* tau, int32_t* emitted,
+                                     int32_t* next_anchor, float* logp_t,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,6 +7,8 @@ own upstream outputs), so each stage is compared in isolation:
   draft       oracle re-runs the chain forced onto the GPU's tokens and reports
               its own choice at every position; a different choice is allowed
               only where the oracle's decision margin is below MARGIN (flagged)
+  rnn draft   as draft, after the states and the bf16 features of the RNN
+              head are checked (check_draft_rnn)
   confidence  float32 relative error <= TOL_REL
   schedule    ell, a, N, Theta bit-exact on the GPU's float32 confidences
   pack        bit-exact
@@ -58,7 +60,47 @@ def f32(a):
 def check_draft(rep, U, W1, W2t, x0, T, seed, rnd, dev_x, dev_lp, dev_lse, reqs):
     xo_f, lp, lse, mg, own = O.draft_markov(U, W1, W2t, x0, T, seed, rnd, req_ids=reqs,
                                             force_x=dev_x, own=True)
-    g = dev_x.shape[1] - 1
+    return _compare_draft(rep, x0, T, dev_x, dev_lp, dev_lse, reqs, lp, lse, mg, own)
+
+
+def check_draft_rnn(rep, U, W1, W2t, Wr, h, x0, T, seed, rnd, dev_x, dev_lp, dev_lse, dev_feat,
+                    dev_state, reqs, bf16_e):
+    """RNN head.  Pass 1 forces the oracle onto the GPU's tokens: its states
+    must agree within TOL_REL (absolute; states lie in (-1, 1)) and its
+    features bit for bit after rounding to bf16, except elements whose
+    rounding margin is below MARGIN (flagged; at most 0.1% of the elements),
+    or within TOL_REL for float32 features.  The features do not feed back
+    into the state, so pass 2 forces the GPU's features as well and compares
+    every token decision, log p_d and lse_d as for the Markov head."""
+    _, _, _, _, _, e, st, em = O.draft_rnn(U, W1, W2t, Wr, h, x0, T, seed, rnd, req_ids=reqs,
+                                           force_x=dev_x, bf16_e=bf16_e)
+    fe = dev_feat.astype(np.float64)
+    es = np.abs(dev_state.astype(np.float64) - st)
+    rep.note("rnn_state", es.max())
+    if es.max() > TOL_REL:
+        rep.err(f"rnn state max err {es.max():.3g}")
+    if bf16_e:
+        diff = fe != e
+        nflag = int((diff & (em < MARGIN)).sum())
+        nbad = int((diff & (em >= MARGIN)).sum())
+        rep.note("rnn_e_flagged", nflag)
+        if nbad:
+            i = np.argwhere(diff & (em >= MARGIN))[0]
+            rep.err(f"rnn features: {nbad} bf16 values differ away from a rounding tie "
+                    f"(first {tuple(i)}: gpu {fe[tuple(i)]!r} oracle {e[tuple(i)]!r})")
+        if nflag > 0.001 * e.size + 1:
+            rep.err(f"rnn features: {nflag} flagged of {e.size}")
+    else:
+        ee = np.abs(fe - e)
+        rep.note("rnn_e", ee.max())
+        if ee.max() > TOL_REL:
+            rep.err(f"rnn features max err {ee.max():.3g}")
+    _, lp, lse, mg, own, _, _, _ = O.draft_rnn(U, W1, W2t, Wr, h, x0, T, seed, rnd, req_ids=reqs,
+                                               force_x=dev_x, force_e=fe, bf16_e=bf16_e)
+    return _compare_draft(rep, x0, T, dev_x, dev_lp, dev_lse, reqs, lp, lse, mg, own)
+
+
+def _compare_draft(rep, x0, T, dev_x, dev_lp, dev_lse, reqs, lp, lse, mg, own):
     diff = own[:, 1:] != dev_x[:, 1:]
     rep.compared += diff.size
     bad = diff & (mg >= MARGIN)
@@ -118,12 +160,13 @@ def check_pack(rep, rows, lens, dev_cu, dev_flat, dev_mr, dev_mp, dev_N, what):
 
 
 def check_verify(rep, ell, cu, target, layout, x, dev_lp, dev_lse, U, W1, W2t, T, seed, rnd,
-                 dev_m, dev_tau, dev_em, dev_na, dev_lpt, reqs, full_R=None):
+                 dev_m, dev_tau, dev_em, dev_na, dev_lpt, reqs, full_R=None, feat=None):
     """reqs: request ids of the rows given (None: all); cu / target in the
-    layout the GPU consumed (for a subset, pass dense rows of the subset)."""
+    layout the GPU consumed (for a subset, pass dense rows of the subset).
+    feat: the draft's per-position bias features (RNN head)."""
     m, tau, em, na, lpt, mg = O.verify(ell, cu, target, layout, x, dev_lp.astype(np.float64),
                                        dev_lse.astype(np.float64), U, W1, W2t, T, seed, rnd,
-                                       req_ids=reqs)
+                                       req_ids=reqs, feat=feat)
     R = ell.size
     rep.compared += R
     for r in range(R):

@@ -66,6 +66,36 @@ def test_draft_argument_checks():
     assert _draft(R=0, U=None, x0=None, x=None, lp=None, lse=None, ws=None) == OK  # empty batch
 
 
+def _draft_rnn(R=4, g=7, V=100, r=16, d=32, T=1.0, U=FAKE, W1=FAKE, W2t=FAKE, Wr=FAKE, h=FAKE,
+               feat=FAKE, ws=FAKE, ws_bytes=1 << 30, wdt=1, hdt=1):
+    return L.load().dspark_draft_rnn(R, g, V, r, d, T, 0, 0, U, 1, W1, W2t, wdt, Wr, h, hdt, FAKE,
+                                     FAKE, FAKE, FAKE, None, feat, None, ws, ws_bytes, None)
+
+
+def test_rnn_argument_checks():
+    assert _draft_rnn(r=0) == UNSUPPORTED               # the RNN head needs a rank
+    assert _draft_rnn(r=8) == UNSUPPORTED
+    assert _draft_rnn(d=0) == INVALID
+    assert _draft_rnn(g=33) == UNSUPPORTED
+    assert _draft_rnn(T=-1.0) == INVALID
+    assert _draft_rnn(Wr=None) == INVALID
+    assert _draft_rnn(h=None) == INVALID
+    assert _draft_rnn(feat=None) == INVALID
+    assert _draft_rnn(hdt=5) == INVALID
+    assert _draft_rnn(feat=C.c_void_p(0x100004)) == UNSUPPORTED           # misaligned features
+    need = D.rnn_workspace_bytes(4, 7, 100, 16, 32)
+    assert need >= D.workspace_bytes(4, 7, 100) + 4 * 7 * 16 * 4 * 4
+    assert _draft_rnn(ws_bytes=need - 1) == WORKSPACE
+    assert _draft_rnn(R=0, U=None, W1=None, W2t=None, Wr=None, h=None, feat=None, ws=None) == OK
+    # the feature verify: a rank is required, and the features replace W1
+    lib = L.load()
+    args = lambda r, feat: (4, 7, 100, r, 1.0, 0, 0, FAKE, FAKE, FAKE, 1, 1, FAKE, FAKE, FAKE,
+                            FAKE, 1, feat, FAKE, 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
+                            None)
+    assert lib.dspark_verify_features(*args(0, FAKE)) == UNSUPPORTED
+    assert lib.dspark_verify_features(*args(16, None)) == INVALID
+
+
 def test_confidence_schedule_pack_verify_checks():
     lib = L.load()
     conf = lambda R=2, g=3, d=8, r=0, V=10, h=FAKE, w=FAKE, x=FAKE, c=FAKE: lib.dspark_confidence(
@@ -147,7 +177,8 @@ def test_synthetic_configs_shapes():
 
 @pytest.mark.parametrize("fn", ["draft_markov", "confidence", "prefix_schedule", "async_schedule",
                                 "pack", "pack_tiered", "verify", "verify_cap_accept",
-                                "acceptance_rate", "sts_fit", "confidence_logits"])
+                                "acceptance_rate", "sts_fit", "confidence_logits", "draft_rnn",
+                                "verify_features", "rnn_workspace_bytes"])
 def test_binding_names_match_abi(fn):
     assert callable(getattr(D, fn))
     assert f"dspark_{fn}" in declared()

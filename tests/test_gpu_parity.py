@@ -647,3 +647,100 @@ def test_full_config3_sampled():
 @pytest.mark.parametrize("R,gamma,rank", [(1, 16, 256), (32, 4, 64), (512, 8, 0)])
 def test_full_config4_cells_sampled(R, gamma, rank):
     _full(4, [0, R - 1] if R > 1 else [0], R=R, gamma=gamma, rank=rank)
+
+
+# ---------------------------------------------------------------- RNN head
+def run_and_check_rnn(cfg, inp_cpu=None, inp_dev=None, gain=3.0, reqs=None, rnd=0):
+    """A full round drafted by the RNN head (its features verified by
+    dspark_verify_features); every stage checked against the oracle."""
+    print(f"[case rnn] {cfg.name} R={cfg.R} g={cfg.gamma} V={cfg.V} r={cfg.rank} d={cfg.d} "
+          f"T={cfg.T} gain={gain} reqs={None if reqs is None else list(reqs)}", flush=True)
+    if inp_dev is None:
+        inp_dev = to_dev(inp_cpu)
+    g = dict(inp_dev)
+    g["Wr"] = synth.rnn_weights(cfg, device=DEV, gain=gain)
+    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV, rnn=(cfg.rank, cfg.d, cfg.dtype))
+    RD.run_round(g, buf, cfg.T, cfg.philox_seed, rnd, scheduler=cfg.scheduler, layout=1,
+                 head="rnn")
+    torch.cuda.synchronize()
+    status = D.get_status(buf.ws)
+    rep = PC.Report()
+    sel = slice(None) if reqs is None else np.asarray(reqs)
+
+    def host(key, rows=True):
+        t = inp_cpu[key] if inp_cpu is not None else g[key]
+        if rows and reqs is not None:
+            t = t[torch.as_tensor(np.asarray(reqs), device=t.device)]
+        return f(t) if t.is_floating_point() else n(t)
+
+    U, tgt, h = host("U"), host("target"), host("h")
+    W1, W2t, w = host("W1", False), host("W2t", False), host("w", False)
+    Wr = f(g["Wr"])
+    x0 = host("x0")
+    x = n(buf.x)[sel]
+    rq = None if reqs is None else np.asarray(reqs, np.int32)
+    feat = f(buf.feat)[sel]
+    bf16_e = cfg.dtype == torch.bfloat16
+    PC.check_draft_rnn(rep, U, W1, W2t, Wr, h, x0, cfg.T, cfg.philox_seed, rnd, x,
+                       n(buf.logp_d)[sel], n(buf.lse_d)[sel], feat, n(buf.state)[sel], rq, bf16_e)
+    PC.check_confidence(rep, h, W1, w, x, n(buf.c)[sel])
+    PC.check_schedule(rep, n(buf.c), n(g["sps"]), cfg.scheduler, n(buf.ell), n(buf.a),
+                      n(buf.N)[0], n(buf.theta)[0])
+    PC.check_pack(rep, n(buf.x), n(buf.ell) + 1, n(buf.cu), n(buf.flat), n(buf.marker_req),
+                  n(buf.marker_pos), n(buf.N)[0], "verify batch")
+    m, *_ = PC.check_verify(rep, n(buf.ell)[sel], None, tgt, 1, x, n(buf.logp_d)[sel],
+                            n(buf.lse_d)[sel], U, W1, W2t, cfg.T, cfg.philox_seed, rnd,
+                            n(buf.m)[sel], n(buf.tau)[sel], n(buf.emitted)[sel],
+                            n(buf.next_anchor)[sel], n(buf.logp_t)[sel], rq, feat=feat)
+    PC.check_pack(rep, n(buf.emitted), n(buf.tau), n(buf.cu_out), n(buf.flat_out), None, None,
+                  n(buf.N_out)[0], "emitted")
+    n_rej = int((n(buf.m) < n(buf.ell)).sum())
+    print(f"  {rep.summary()} status={status} sum_ell={int(n(buf.ell).sum())} "
+          f"sum_m={int(n(buf.m).sum())} rejected={n_rej}", flush=True)
+    assert status == 0, f"device flags {status}"
+    assert rep.ok(), rep.summary()
+    return buf, rep, n_rej
+
+
+RNN_SMALL = [
+    (0, {}),                                                            # float32 throughout
+    (2, dict(R=40, gamma=5, V=3000, d=256)),                             # bf16, rank 256, MFMA h part
+    (2, dict(R=33, gamma=4, V=2000, d=64, rank=64)),
+    (2, dict(R=9, gamma=3, V=1500, d=40, rank=16)),
+    (2, dict(R=6, gamma=4, V=1001, d=36, rank=32)),                      # d not a multiple of 8
+    (2, dict(R=35, gamma=4, V=2000, d=72, rank=512)),
+    (1, dict(R=20, gamma=5, V=3001, d=96, rank=32)),                     # greedy
+    (3, dict(R=70, gamma=6, V=2500, d=64)),                              # T = 0.7
+    (2, dict(R=24, gamma=4, V=1800, d=64, scheduler=False)),             # every position verified
+    (2, dict(R=1, gamma=1, V=700, d=16)),
+]
+
+
+@pytest.mark.parametrize("base,over", RNN_SMALL, ids=[f"rnn{i}" for i in range(len(RNN_SMALL))])
+def test_rnn_round_parity(base, over):
+    cfg = synth.scaled(synth.config(base), **over) if over else synth.config(base)
+    inp = synth.make_inputs(cfg, device="cpu")
+    run_and_check_rnn(cfg, inp)
+
+
+def test_rnn_feature_residuals_exercised():
+    """Static block, T = 1: many rejections, so the residual rows rebuilt from
+    the features are checked; the same drafts verified without the features
+    (as a Markov head) give other emitted tokens."""
+    cfg = synth.scaled(synth.config(2), R=48, gamma=6, V=2500, d=64, scheduler=False)
+    inp = synth.make_inputs(cfg, device="cpu")
+    buf, rep, n_rej = run_and_check_rnn(cfg, inp)
+    assert n_rej >= 10, n_rej
+    g = to_dev(inp)
+    alt = torch.empty_like(buf.emitted)
+    m2, t2, na2 = (torch.empty_like(buf.m) for _ in range(3))
+    D.verify(buf.ell, buf.cu, g["target"], 1, buf.x, buf.logp_d, buf.lse_d, g["U"], g["W1"],
+             g["W2t"], cfg.T, cfg.philox_seed, 0, m2, t2, alt, na2, buf.ws)
+    torch.cuda.synchronize()
+    assert not torch.equal(alt, buf.emitted)
+
+
+def test_rnn_full_config2_sampled():
+    cfg = synth.config(2)
+    inp = synth.make_inputs(cfg, device=DEV)
+    run_and_check_rnn(cfg, None, inp_dev=inp, gain=1.0, reqs=[0, 255])
