@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--verify-mode", choices=["compact", "cap-accept"], default="compact",
                    help="verify the scheduled window (default) or the whole block, committed "
                         "within the scheduled window")
+    p.add_argument("--head", choices=["markov", "rnn"], default="markov",
+                   help="draft head: the Markov head (default) or the RNN head (recurrent cell "
+                        "with per-position bias features; per-step schedule)")
     p.add_argument("--diagnostics", action="store_true",
                    help="also time the acceptance-rate (c*) pass on the last round and an STS "
                         "fit on synthetic held-out blocks")
@@ -85,14 +88,17 @@ class HipEvents:
             self.rt.hipEventDestroy(self.ev[i])
 
 
-def algorithmic_bytes(cfg, sum_tau, n_rej, N):
+def algorithmic_bytes(cfg, sum_tau, n_rej, N, head="markov"):
     """Bytes the round must move (per round): U once, the target rows up to
     the first rejection (or the bonus row), U rows of rejected positions, h,
-    W2 once and the gathered W1 rows, w, and the outputs."""
+    W2 once and the gathered W1 rows, w, and the outputs.  The RNN head adds
+    its projection Wr once and its features (written once, read back by the
+    statistics kernel)."""
     sU = sT = sh = sW = sw = 2 if cfg.dtype.itemsize == 2 else 4
     R, G, V, r, d = cfg.R, cfg.gamma, cfg.V, cfg.rank, cfg.d
+    extra = sW * (3 * r * (2 * r + d) + 2 * R * G * r) if head == "rnn" else 0
     return (sU * R * G * V + sT * V * sum_tau + sU * V * n_rej + sh * R * G * d
-            + sW * (r * V + R * G * r) + sw * (d + r) + R * G * 16 + N * 12)
+            + sW * (r * V + R * G * r) + sw * (d + r) + R * G * 16 + N * 12 + extra)
 
 
 def stats_kernel_bytes(cfg):
@@ -108,7 +114,7 @@ def stats_kernel_bytes(cfg):
 # kernel -> (sources it is built from, committed counter summary)
 KERNELS = {
     "k_markov_mfma": (("stats.hip", "launch.hpp", "device_common.hpp", "sampling.hpp", "workspace.hpp"),
-                      "k_markov_mfma_R256_g16_V129280_r256_counters.txt"),
+                      "k_markov_mfma_rnn_R256_g16_V129280_r256_counters.txt"),
     "k_draft_persistent": (("draft.hip", "launch.hpp", "device_common.hpp", "sampling.hpp",
                             "workspace.hpp"),
                            "k_draft_persistent_R256_g16_V129280_r256_counters.txt"),
@@ -183,7 +189,15 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] config {args.config} ({cfg.name}) inputs ready in {time.time() - t0:.1f}s")
     K, W = args.steps, args.warmup
-    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=dev)
+    rnn = args.head == "rnn"
+    if rnn:
+        if args.verify_mode != "compact":
+            print("bench.py: the RNN head is verified in compact mode", file=sys.stderr)
+            sys.exit(2)
+        inp["Wr"] = synth.rnn_weights(cfg, device=dev)
+        buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=dev, rnn=(cfg.rank, cfg.d, cfg.dtype))
+    else:
+        buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=dev)
     vmode = args.verify_mode
     ells = torch.empty(K + W, cfg.R, dtype=torch.int32, device=dev)
     ms = torch.empty(K + W, cfg.R, dtype=torch.int32, device=dev)
@@ -199,7 +213,17 @@ def main():
     def one_round(i, timed):
         buf.ell, buf.m = ells[i], ms[i]
         buf.N, buf.N_out = Ns[i:i + 1], Nouts[i:i + 1]
-        if timed:
+        if rnn:
+            j = (i - W) * 2 * cfg.gamma
+            args_ = (inp["U"], inp["W1"], inp["W2t"], inp["Wr"], inp["h"], inp["x0"], cfg.T,
+                     cfg.philox_seed, i, buf.x, buf.logp_d, buf.lse_d, buf.feat, buf.ws)
+            if timed:
+                n_timed[0] = L.draft_rnn_profiled(*args_, ev.array(j, cfg.gamma),
+                                                  ev.array(j + cfg.gamma, cfg.gamma),
+                                                  state=buf.state)
+            else:
+                L.draft_rnn(*args_, state=buf.state)
+        elif timed:
             j = (i - W) * 2 * cfg.gamma
             n_timed[0] = L.draft_markov_profiled(inp["U"], inp["W1"], inp["W2t"], inp["x0"], cfg.T,
                                                  cfg.philox_seed, i, buf.x, buf.logp_d, buf.lse_d,
@@ -224,6 +248,10 @@ def main():
                                 buf.lse_d, inp["U"], inp["W1"], inp["W2t"], cfg.T, cfg.philox_seed,
                                 i, buf.m, buf.tau, buf.emitted, buf.next_anchor, buf.ws,
                                 m_full=buf.m_full, logp_t=buf.logp_t)
+        elif rnn:
+            L.verify_features(buf.ell, buf.cu, inp["target"], 1, buf.x, buf.logp_d, buf.lse_d,
+                              inp["U"], buf.feat, inp["W2t"], cfg.T, cfg.philox_seed, i, buf.m,
+                              buf.tau, buf.emitted, buf.next_anchor, buf.ws, logp_t=buf.logp_t)
         else:
             L.verify(buf.ell, buf.cu, inp["target"], 1, buf.x, buf.logp_d, buf.lse_d, inp["U"],
                      inp["W1"], inp["W2t"], cfg.T, cfg.philox_seed, i, buf.m, buf.tau,
@@ -250,7 +278,7 @@ def main():
     N_avg = float(Ns[W:].cpu().numpy().mean())
     value = sum_ell / t_total
     bytes_round = sum(algorithmic_bytes(cfg, int((m_t[i] + 1).sum()), int((m_t[i] < ell_t[i]).sum()),
-                                        int(Ns[W + i].item())) for i in range(K)) / K
+                                        int(Ns[W + i].item()), args.head) for i in range(K)) / K
     hbm_frac_round = bytes_round / (t_total / K) / (HBM_PEAK_GBS * 1e9)
 
     # dominant kernel, timed with events on its launch stream: the persistent
@@ -270,7 +298,8 @@ def main():
         kflops = 2.0 * cfg.R * cfg.rank * cfg.V * cfg.gamma
     else:
         kernel = "k_markov_mfma"
-        kdesc = "k_markov_mfma (draft statistics, per step)"
+        kdesc = ("k_markov_mfma (draft statistics of U_k + W2^T e_k, per step; RNN head)" if rnn
+                 else "k_markov_mfma (draft statistics, per step)")
         kb = stats_kernel_bytes(cfg)
         kflops = 2.0 * cfg.R * cfg.rank * cfg.V
     achieved = kb / (avg_ms * 1e-3) / 1e9
@@ -285,7 +314,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, inp, buf, args.cpu_sample, sum_ell / K, torch, np, sched,
-                           int(Ns[W + K - 1].item()))
+                           int(Ns[W + K - 1].item()), args.head)
     out = {
         "metric": "verified draft tokens/s per round (B=256,γ=16,V=129280) + % peak HBM",
         "value": value,
@@ -301,7 +330,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"dspark-round config {args.config} ({cfg.name})", "R": cfg.R,
                    "gamma": cfg.gamma, "V": cfg.V, "rank": cfg.rank, "d": cfg.d, "T": cfg.T,
-                   "scheduler": sched, "verify_mode": vmode, "parallelism": "single-gpu"},
+                   "scheduler": sched, "verify_mode": vmode, "head": args.head,
+                   "parallelism": "single-gpu"},
         "hbm_frac_round": hbm_frac_round,
         "round_bytes_alg": bytes_round,
         "emitted_tokens_per_s": sum_tau / t_total,
@@ -359,7 +389,8 @@ def diagnostics(cfg, inp, buf, torch, np, D):
     return res
 
 
-def cpu_baseline(cfg, inp, buf, n_req, ell_per_round, torch, np, sched="greedy", K_in=0):
+def cpu_baseline(cfg, inp, buf, n_req, ell_per_round, torch, np, sched="greedy", K_in=0,
+                 head="markov"):
     """The oracle as it stands, on a bounded sample: draft + confidence +
     verify for n_req requests, the scheduler and both packs on the full batch;
     the per-request part is scaled to all R requests."""
@@ -374,7 +405,13 @@ def cpu_baseline(cfg, inp, buf, n_req, ell_per_round, torch, np, sched="greedy",
     c_all = buf.c.cpu().numpy()
     x_all = buf.x.cpu().numpy()
     t0 = time.perf_counter()
-    x, lp, lse, _ = O.draft_markov(U, W1, W2t, x0, cfg.T, cfg.philox_seed, 0, req_ids=reqs)
+    feat = None
+    if head == "rnn":
+        x, lp, lse, _, _, feat, _, _ = O.draft_rnn(U, W1, W2t, f(inp["Wr"]), h, x0, cfg.T,
+                                                   cfg.philox_seed, 0, req_ids=reqs,
+                                                   bf16_e=cfg.dtype == torch.bfloat16)
+    else:
+        x, lp, lse, _ = O.draft_markov(U, W1, W2t, x0, cfg.T, cfg.philox_seed, 0, req_ids=reqs)
     c, _ = O.confidence(h, W1, w, x)
     t1 = time.perf_counter()
     c_all = c_all.copy()
@@ -386,7 +423,7 @@ def cpu_baseline(cfg, inp, buf, n_req, ell_per_round, torch, np, sched="greedy",
     O.pack(x_all, ell + 1)
     t2 = time.perf_counter()
     O.verify(ell[reqs], None, tgt, 1, x, lp, lse, U, W1, W2t, cfg.T, cfg.philox_seed, 0,
-             req_ids=reqs)
+             req_ids=reqs, feat=feat)
     t3 = time.perf_counter()
     O.pack(x_all, ell + 1)
     t4 = time.perf_counter()

@@ -27,7 +27,7 @@ EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
            "dspark_draft_markov_profiled", "dspark_async_schedule", "dspark_pack_tiered",
            "dspark_verify_cap_accept", "dspark_acceptance_rate", "dspark_sts_fit",
            "dspark_sts_workspace_bytes", "dspark_confidence_logits", "dspark_rnn_workspace_bytes",
-           "dspark_draft_rnn", "dspark_verify_features")
+           "dspark_draft_rnn", "dspark_verify_features", "dspark_draft_rnn_profiled")
 
 
 class DsparkError(RuntimeError):
@@ -78,6 +78,7 @@ def load():
     L.dspark_rnn_workspace_bytes.restype = sz
     L.dspark_draft_rnn.argtypes = [i32, i32, i32, i32, i32, f32, u64, u64, P, i32, P, P, i32, P, P,
                                    i32, P, P, P, P, P, P, P, P, sz, P]
+    L.dspark_draft_rnn_profiled.argtypes = L.dspark_draft_rnn.argtypes + [P, P, P]
     L.dspark_verify_features.argtypes = L.dspark_verify.argtypes
     for fn in EXPORTS:
         getattr(L, fn).restype = getattr(L, fn).restype or i32
@@ -306,6 +307,24 @@ def draft_rnn(U, W1, W2t, Wr, h, x0, T, seed, rnd, x, logp_d, lse_d, feat, ws, s
                                    _ptr(x0), _ptr(x), _ptr(logp_d), _ptr(lse_d), _ptr(margin),
                                    _ptr(feat), _ptr(state), _ptr(ws), ws.numel(), _stream(stream))
     _check("dspark_draft_rnn", code)
+
+
+def draft_rnn_profiled(U, W1, W2t, Wr, h, x0, T, seed, rnd, x, logp_d, lse_d, feat, ws, ev_begin,
+                       ev_end, state=None, margin=None, stream=None):
+    """As draft_rnn, recording the caller's HIP events (ctypes arrays of gamma
+    hipEvent_t each) around each step's statistics kernel; returns gamma."""
+    R, gamma, V = U.shape
+    r = int(W1.shape[1])
+    d = int(h.shape[-1])
+    n_timed = C.c_int(0)
+    code = load().dspark_draft_rnn_profiled(R, gamma, V, r, d, float(T), seed, rnd, _ptr(U),
+                                            _dt(U), _ptr(W1), _ptr(W2t), _dt(W1), _ptr(Wr),
+                                            _ptr(h), _dt(h), _ptr(x0), _ptr(x), _ptr(logp_d),
+                                            _ptr(lse_d), _ptr(margin), _ptr(feat), _ptr(state),
+                                            _ptr(ws), ws.numel(), _stream(stream), ev_begin,
+                                            ev_end, C.byref(n_timed))
+    _check("dspark_draft_rnn_profiled", code)
+    return int(n_timed.value)
 
 
 def verify_features(ell, cu, target, layout, x, logp_d, lse_d, U, feat, W2t, T, seed, rnd, m, tau,

@@ -119,12 +119,14 @@ size_t dspark_rnn_workspace_bytes(int R, int gamma, int V, int r, int d) {
   return rnn_ws_layout(R, gamma, V, r).total;
 }
 
-dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, int d, float T, uint64_t seed,
-                               uint64_t round, const void* U, dspark_dtype U_dt, const void* W1,
-                               const void* W2t, dspark_dtype W_dt, const void* Wr, const void* h,
-                               dspark_dtype h_dt, const int32_t* x0, int32_t* x, float* logp_d,
-                               float* lse_d, float* margin, void* feat, float* state, void* ws,
-                               size_t ws_bytes, hipStream_t stream) {
+static dspark_status draft_rnn_impl(int R, int gamma, int V, int r, int d, float T,
+                                    uint64_t seed, uint64_t round, const void* U,
+                                    dspark_dtype U_dt, const void* W1, const void* W2t,
+                                    dspark_dtype W_dt, const void* Wr, const void* h,
+                                    dspark_dtype h_dt, const int32_t* x0, int32_t* x,
+                                    float* logp_d, float* lse_d, float* margin, void* feat,
+                                    float* state, void* ws, size_t ws_bytes, hipStream_t stream,
+                                    hipEvent_t* ev_begin, hipEvent_t* ev_end, int* n_timed) {
   dspark_status s = shape_check(R, gamma, V);
   if (s != DSPARK_OK) return s;
   if (d < 1) return DSPARK_E_INVALID;
@@ -150,7 +152,34 @@ dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, int d, float T, u
   a.status = reinterpret_cast<uint32_t*>(w + ws_layout(R, gamma, V).header);
   return hip_status(launch_draft(R, gamma, V, r, T, seed, round, U, U_dt == DSPARK_BF16, W1, W2t,
                                  W_dt == DSPARK_BF16, x0, x, logp_d, lse_d, margin, ws, stream,
-                                 nullptr, nullptr, nullptr, &a));
+                                 ev_begin, ev_end, n_timed, &a));
+}
+
+dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, int d, float T, uint64_t seed,
+                               uint64_t round, const void* U, dspark_dtype U_dt, const void* W1,
+                               const void* W2t, dspark_dtype W_dt, const void* Wr, const void* h,
+                               dspark_dtype h_dt, const int32_t* x0, int32_t* x, float* logp_d,
+                               float* lse_d, float* margin, void* feat, float* state, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  return draft_rnn_impl(R, gamma, V, r, d, T, seed, round, U, U_dt, W1, W2t, W_dt, Wr, h, h_dt,
+                        x0, x, logp_d, lse_d, margin, feat, state, ws, ws_bytes, stream, nullptr,
+                        nullptr, nullptr);
+}
+
+dspark_status dspark_draft_rnn_profiled(int R, int gamma, int V, int r, int d, float T,
+                                        uint64_t seed, uint64_t round, const void* U,
+                                        dspark_dtype U_dt, const void* W1, const void* W2t,
+                                        dspark_dtype W_dt, const void* Wr, const void* h,
+                                        dspark_dtype h_dt, const int32_t* x0, int32_t* x,
+                                        float* logp_d, float* lse_d, float* margin, void* feat,
+                                        float* state, void* ws, size_t ws_bytes,
+                                        hipStream_t stream, hipEvent_t* ev_begin,
+                                        hipEvent_t* ev_end, int* n_timed) {
+  if (!ev_begin || !ev_end) return DSPARK_E_INVALID;
+  if (n_timed) *n_timed = 0;
+  return draft_rnn_impl(R, gamma, V, r, d, T, seed, round, U, U_dt, W1, W2t, W_dt, Wr, h, h_dt,
+                        x0, x, logp_d, lse_d, margin, feat, state, ws, ws_bytes, stream, ev_begin,
+                        ev_end, n_timed);
 }
 
 static dspark_status confidence_impl(int R, int gamma, int d, int r, int V, const void* h,

@@ -14,14 +14,20 @@
 //   k_rnn_hproj_mfma : the h part for every block position at once (it does not
 //                      depend on the drafted tokens): P = h Wr_h^T, an
 //                      (R gamma) x d x 3r bf16 contraction on MFMA with fp32
-//                      accumulation (bf16 products are exact in fp32).
+//                      accumulation (bf16 products are exact in fp32),
+//                      LDS-staged 128 x 128 tiles.
 //   k_rnn_hproj_valu : the same for float32 operands or unaligned rows.
-//   k_rnn_cell       : per step, the recurrent part [s_{k-1} ; W1[x_{k-1}]]
-//                      (2r inputs) in fp32 on the VALU, plus P, then the gates,
-//                      s_k and e_k.  A workgroup owns 16 requests x 16 state
-//                      entries with their gate, candidate and output rows, so
-//                      the cell completes locally.
+//   k_rnn_cell_mfma  : per step, the recurrent part [s_{k-1} ; W1[x_{k-1}]]
+//                      (2r inputs) on MFMA with the fp32 state split into
+//                      three exact bf16 parts, plus P, then the gates, s_k and
+//                      e_k.  A workgroup owns 16 requests x 16 state entries
+//                      with their gate, candidate and output rows, so the cell
+//                      completes locally.
+//   k_rnn_cell       : the same cell in fp32 on the vector ALU (float32
+//                      weights, rows that are not 16-byte aligned).
 #include <algorithm>
+#include <cstdlib>
+#include <type_traits>
 
 #include "launch.hpp"
 
@@ -52,64 +58,103 @@ template <> __device__ __forceinline__ void st_f<uint16_t>(uint16_t* p, int64_t 
 
 // ------------------------------------------------------------- h projection
 // P[m][q] = sum_t h[m][t] Wr[q][2r + t], m < M = R gamma, q < N = 3r.
-// 256 threads, a 64 x 64 output tile; wave w computes the 32 x 32 quarter
-// (w >> 1, w & 1) as 2 x 2 tiles of v_mfma_f32_16x16x32_bf16.  Operand lane
-// (l & 15, l >> 4) holds row l & 15 of its 16-row tile, k-values 8 (l >> 4) +
-// [0, 8) of the 32-wide k-step; result lane (n, g) holds rows 4 g + [0, 4) of
-// column n.
-constexpr int kHT = 64;
+// Workgroup tile kBM x kBN (256 threads): per 32-wide k-step the tile's rows
+// of h and of Wr are staged through LDS (double buffered; the next k-step's
+// global loads are in flight while this one is computed), and wave w computes
+// the 64 x 64 quarter (w >> 1, w & 1) as 4 x 4 tiles of
+// v_mfma_f32_16x16x32_bf16.  Operand lane (l & 15, l >> 4) holds row l & 15
+// of its 16-row tile, k-values 8 (l >> 4) + [0, 8); result lane (n, g) holds
+// rows 4 g + [0, 4) of column n.  Workgroups b, b + 8, ... run on one XCD:
+// each XCD takes a contiguous run of tiles, N fastest, so tiles that share
+// rows of h share that XCD's L2.
+// 16 bytes at p (always a valid address), or zeros when !ok.  The zeroing is a
+// mask on the loaded value, so the load itself stays an unconditional global
+// load (a select between a load and a constant can otherwise become a load
+// from a selected address, through scratch).
+__device__ __forceinline__ uint4 ld16_or_zero(const uint16_t* p, bool ok) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+constexpr int kBM = 128, kBN = 128;
+constexpr int kLdsRow = 40;                 // bf16 per LDS row: 32 + 8 of padding (80 bytes)
+constexpr int kXcds = 8;                    // XCDs of an MI355X
 
 __global__ __launch_bounds__(256) void k_rnn_hproj_mfma(const uint16_t* __restrict__ h,
                                                          const uint16_t* __restrict__ Wr, int M,
                                                          int N, int d, int ldw, int wcol,
                                                          float* __restrict__ P) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int m0 = blockIdx.x * kHT + 32 * (wv >> 1);
-  const int n0 = blockIdx.y * kHT + 32 * (wv & 1);
-  const int rl = lane & 15, kg = lane >> 4;
-  const uint16_t* arow[2];
-  const uint16_t* brow[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    arow[t] = h + (int64_t)min(m0 + 16 * t + rl, M - 1) * d + 8 * kg;
-    brow[t] = Wr + (int64_t)min(n0 + 16 * t + rl, N - 1) * ldw + wcol + 8 * kg;
-  }
-  f32x4_t acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const bf16x8_t zero = {};
+  __shared__ uint4 As[2][kBM * kLdsRow / 8];
+  __shared__ uint4 Bs[2][kBN * kLdsRow / 8];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nN = (N + kBN - 1) / kBN, tiles = ((M + kBM - 1) / kBM) * nN;
+  const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  const int t = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (t >= tiles) return;
+  const int m0 = (t / nN) * kBM, n0 = (t % nN) * kBN;
+  // staging: thread t moves pieces t and t + 256 (row p >> 2, 16-byte column
+  // p & 3); both pieces share the column
+  const int kp = tid & 3;
+  const int row0 = tid >> 2, row1 = row0 + 64;
+  const uint16_t* ga0 = h + (int64_t)min(m0 + row0, M - 1) * d + 8 * kp;
+  const uint16_t* ga1 = h + (int64_t)min(m0 + row1, M - 1) * d + 8 * kp;
+  const uint16_t* gb0 = Wr + (int64_t)min(n0 + row0, N - 1) * ldw + wcol + 8 * kp;
+  const uint16_t* gb1 = Wr + (int64_t)min(n0 + row1, N - 1) * ldw + wcol + 8 * kp;
+  const int l0 = (row0 * kLdsRow + 8 * kp) / 8, l1 = (row1 * kLdsRow + 8 * kp) / 8;
   const int ksteps = (d + 31) / 32;
-  bf16x8_t A[2], B[2], An[2], Bn[2];
-  auto load = [&](bf16x8_t (&Ao)[2], bf16x8_t (&Bo)[2], int ks) __attribute__((always_inline)) {
-    const bool in = ks * 32 + 8 * kg < d;   // d is a multiple of 8: a group is all in or all out
+  f32x4_t acc[4][4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      Ao[t] = in ? *reinterpret_cast<const bf16x8_t*>(arow[t] + 32 * ks) : zero;
-      Bo[t] = in ? *reinterpret_cast<const bf16x8_t*>(brow[t] + 32 * ks) : zero;
-    }
-  };
-  load(A, B, 0);
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int rl = lane & 15, kg = lane >> 4;
+  const int wm = 64 * (wv >> 1), wn = 64 * (wv & 1);
+  {
+    const bool in = 8 * kp < d;                              // d % 8 == 0: all in or all out
+    As[0][l0] = ld16_or_zero(ga0, in);
+    As[0][l1] = ld16_or_zero(ga1, in);
+    Bs[0][l0] = ld16_or_zero(gb0, in);
+    Bs[0][l1] = ld16_or_zero(gb1, in);
+  }
+  __syncthreads();
   for (int ks = 0; ks < ksteps; ++ks) {
-    if (ks + 1 < ksteps) load(An, Bn, ks + 1);
+    const int buf = ks & 1;
+    // next k-step's pieces, in flight during this step's MFMAs
+    const bool nx = ks + 1 < ksteps && (ks + 1) * 32 + 8 * kp < d;
+    const int o = nx ? 32 * (ks + 1) : 0;
+    const uint4 ra0 = ld16_or_zero(ga0 + o, nx);
+    const uint4 ra1 = ld16_or_zero(ga1 + o, nx);
+    const uint4 rb0 = ld16_or_zero(gb0 + o, nx);
+    const uint4 rb1 = ld16_or_zero(gb1 + o, nx);
+    bf16x8_t Af[4], Bf[4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int i = 0; i < 4; ++i) {
+      Af[i] = __builtin_bit_cast(bf16x8_t, As[buf][((wm + 16 * i + rl) * kLdsRow + 8 * kg) / 8]);
+      Bf[i] = __builtin_bit_cast(bf16x8_t, Bs[buf][((wn + 16 * i + rl) * kLdsRow + 8 * kg) / 8]);
+    }
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[a], B[b], acc[a][b], 0, 0, 0);
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) { A[t] = An[t]; B[t] = Bn[t]; }
+      for (int b = 0; b < 4; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[a], Bf[b], acc[a][b], 0, 0, 0);
+    if (ks + 1 < ksteps) {
+      As[buf ^ 1][l0] = ra0;
+      As[buf ^ 1][l1] = ra1;
+      Bs[buf ^ 1][l0] = rb0;
+      Bs[buf ^ 1][l1] = rb1;
+    }
+    __syncthreads();
   }
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int n = n0 + 16 * b + rl;
+    for (int b = 0; b < 4; ++b) {
+      const int n = n0 + wn + 16 * b + rl;
       if (n >= N) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = m0 + 16 * a + 4 * kg + i;
+        const int m = m0 + wm + 16 * a + 4 * kg + i;
         if (m < M) P[(int64_t)m * N + n] = acc[a][b][i];
       }
     }
@@ -138,13 +183,19 @@ __global__ __launch_bounds__(256) void k_rnn_hproj_valu(const HT* __restrict__ h
 // Workgroup (request tile rt, state tile jt): requests 16 rt + [0, 16), state
 // entries j = 16 jt + [0, 16).  Thread t: request 16 rt + (t >> 4), entry
 // 16 jt + (t & 15); it accumulates the gate, candidate and output rows of its
-// entry against its request's recurrent input over the 2r columns, staged
-// through LDS in chunks of kKC columns (as fp32).
-constexpr int kKC = 64;
+// entry against its request's recurrent input over the 2r columns.  Those
+// columns go through LDS (as fp32) in chunks of kKC: every load of a chunk is
+// issued at once (16-byte weight pieces when the rows allow), and the next
+// chunk's loads are in flight while the current one is consumed.
+constexpr int kKC = 128;
 constexpr int kKP = kKC + 4;                 // padded LDS row (float4 reads stay conflict-light)
 
-template <typename WT>
+template <typename WT, bool VEC>
 __global__ __launch_bounds__(256) void k_rnn_cell(RnnArgs a, int k) {
+  constexpr int EPP = VEC ? 16 / (int)sizeof(WT) : 1;   // weight elements per load
+  constexpr int PPR = kKC / EPP;                         // loads per weight row and chunk
+  constexpr int NWP = 48 * PPR / 256;                    // weight loads per thread and chunk
+  constexpr int NZ = 16 * kKC / 256;                     // input values per thread and chunk
   __shared__ float Z[16 * kKP];
   __shared__ float W[48 * kKP];
   __shared__ int PV[16];
@@ -164,32 +215,61 @@ __global__ __launch_bounds__(256) void k_rnn_cell(RnnArgs a, int k) {
     PV[tid] = prev;
   }
   __syncthreads();
-  float pg = 0.f, pc = 0.f, po = 0.f;
-  for (int q0 = 0; q0 < nin; q0 += kKC) {
-    // stage z[16][kKC] and the 48 weight rows [gate | candidate | output] x 16
-    for (int idx = tid; idx < 16 * kKC; idx += 256) {
-      const int row = idx / kKC, col = idx % kKC, q = q0 + col;
+  using Raw = typename std::conditional<VEC, uint4, float>::type;
+  Raw wraw[NWP];
+  float zraw[NZ];
+  auto load = [&](int q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NWP; ++i) {
+      const int p = tid + 256 * i, row = p / PPR, q = q0 + (p % PPR) * EPP;
+      const WT* src = Wr + (int64_t)((row >> 4) * r + j0 + (row & 15)) * ldw + q;
+      if constexpr (VEC) wraw[i] = q < nin ? *reinterpret_cast<const uint4*>(src) : uint4{0u, 0u, 0u, 0u};
+      else wraw[i] = q < nin ? ld_f(src, 0) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NZ; ++i) {
+      const int idx = tid + 256 * i, row = idx / kKC, q = q0 + idx % kKC;
       const int req = req0 + row;
       float v = 0.f;
       if (req < a.R && q < nin) {
         if (q < r) v = (k == 1) ? 0.f : a.state[((int64_t)req * a.gamma + (k - 2)) * r + q];
         else v = ld_f(W1, (int64_t)PV[row] * r + (q - r));
       }
-      Z[row * kKP + col] = v;
+      zraw[i] = v;
     }
-    for (int idx = tid; idx < 48 * kKC; idx += 256) {
-      const int row = idx / kKC, col = idx % kKC, q = q0 + col;
-      const int part = row >> 4, j = j0 + (row & 15);
-      float v = 0.f;
-      if (j < r && q < nin) v = ld_f(Wr, (int64_t)(part * r + j) * ldw + q);
-      W[row * kKP + col] = v;
+  };
+  auto store = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NWP; ++i) {
+      const int p = tid + 256 * i, row = p / PPR, c = (p % PPR) * EPP;
+      float* dst = W + row * kKP + c;
+      if constexpr (VEC && sizeof(WT) == 2) {
+        const uint4 u = wraw[i];
+        *reinterpret_cast<float4*>(dst) = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w));
+      } else if constexpr (VEC) {
+        *reinterpret_cast<uint4*>(dst) = wraw[i];
+      } else {
+        dst[0] = wraw[i];
+      }
     }
+#pragma unroll
+    for (int i = 0; i < NZ; ++i) {
+      const int idx = tid + 256 * i;
+      Z[(idx / kKC) * kKP + idx % kKC] = zraw[i];
+    }
+  };
+  float pg = 0.f, pc = 0.f, po = 0.f;
+  load(0);
+  for (int q0 = 0; q0 < nin; q0 += kKC) {
+    store();
     __syncthreads();
+    if (q0 + kKC < nin) load(q0 + kKC);      // in flight while this chunk is consumed
     const float4* zr = reinterpret_cast<const float4*>(Z + rr * kKP);
     const float4* gr = reinterpret_cast<const float4*>(W + jj * kKP);
     const float4* cr = reinterpret_cast<const float4*>(W + (16 + jj) * kKP);
     const float4* orw = reinterpret_cast<const float4*>(W + (32 + jj) * kKP);
-#pragma unroll 4
+#pragma unroll 8
     for (int c = 0; c < kKC / 4; ++c) {
       const float4 z = zr[c], g = gr[c], cc = cr[c], o = orw[c];
       pg = fmaf(g.x, z.x, pg); pg = fmaf(g.y, z.y, pg); pg = fmaf(g.z, z.z, pg); pg = fmaf(g.w, z.w, pg);
@@ -214,6 +294,120 @@ __global__ __launch_bounds__(256) void k_rnn_cell(RnnArgs a, int k) {
   st_f(reinterpret_cast<WT*>(a.feat), pos * r + j, e);
 }
 
+// The cell on MFMA (bf16 weights with 16-byte aligned rows).  Workgroup
+// (rt, jt) owns requests 16 rt + [0, 16) and state entries 16 jt + [0, 16):
+// three 16 x 16 results (gate, candidate and output rows of those entries)
+// over the 2r recurrent columns, as v_mfma_f32_16x16x32_bf16 with the
+// requests as M and the weight rows as N.  The embedding half of z is bf16
+// already; the fp32 state is split into three bf16 parts s = hi + mid + lo
+// (together its 24 significant bits), so every product is exact in fp32 and
+// the accumulation is fp32, as on the vector ALU.  Wave w takes the k-steps
+// w, w + 4, ... of both halves (all its loads issued at once) and the four
+// partial results are added through LDS; wave w then finishes request row
+// 4 g + w of every lane group g.
+__device__ __forceinline__ void split3(const float4& a, const float4& b, bf16x8_t& hi,
+                                       bf16x8_t& mid, bf16x8_t& lo) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint16_t h[8], m[8], l[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    h[t] = f32_to_bf16(v[t]);
+    const float r1 = v[t] - __uint_as_float((uint32_t)h[t] << 16);
+    m[t] = f32_to_bf16(r1);
+    const float r2 = r1 - __uint_as_float((uint32_t)m[t] << 16);
+    l[t] = f32_to_bf16(r2);
+  }
+  hi = __builtin_bit_cast(bf16x8_t, h);
+  mid = __builtin_bit_cast(bf16x8_t, m);
+  lo = __builtin_bit_cast(bf16x8_t, l);
+}
+
+constexpr int kCellIt = 4;                   // k-steps per wave and half: r <= 4 * 4 * 32 = 512
+
+__global__ __launch_bounds__(256) void k_rnn_cell_mfma(RnnArgs a, int k) {
+  __shared__ float red[3][4][64][4];          // [part][wave][lane][row]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = a.rank, ldw = 2 * r + a.d, nks = (r + 31) / 32;
+  const int req0 = blockIdx.x * 16, j0 = blockIdx.y * 16;
+  const int m = lane & 15, kg = lane >> 4;
+  const uint16_t* W1 = reinterpret_cast<const uint16_t*>(a.W1);
+  const uint16_t* Wr = reinterpret_cast<const uint16_t*>(a.Wr);
+  // operand rows of this lane: request req0 + m (A), weight row j0 + m of each part (B)
+  const int reqA = req0 + m;
+  const bool okA = reqA < a.R;
+  int prev = 0;
+  if (okA) {
+    prev = (k == 1) ? a.x0[reqA] : a.x[(int64_t)reqA * (a.gamma + 1) + (k - 1)];
+    if (prev < 0 || prev >= a.V) { if (w == 0) set_flag(a.status, kFlagBadToken); prev = 0; }
+  }
+  const bool has_s = k >= 2;                  // s_0 = 0: no state half at the first step
+  const float* srow = a.state + ((int64_t)(okA ? reqA : 0) * a.gamma + (has_s ? k - 2 : 0)) * r;
+  const uint16_t* erow = W1 + (int64_t)prev * r;
+  const uint16_t* wrow[3];
+#pragma unroll
+  for (int p = 0; p < 3; ++p) wrow[p] = Wr + (int64_t)(p * r + j0 + m) * ldw;
+  const bf16x8_t zero = {};
+  const float4 fz = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 sv[kCellIt][2];
+  bf16x8_t ev[kCellIt], ws[kCellIt][3], we[kCellIt][3];
+#pragma unroll
+  for (int it = 0; it < kCellIt; ++it) {
+    const int c = 32 * (w + 4 * it) + 8 * kg;
+    const bool in = c < r;                     // r % 16 == 0: a group is all in or all out
+    const bool sin = in && has_s && okA;
+    sv[it][0] = sin ? *reinterpret_cast<const float4*>(srow + c) : fz;
+    sv[it][1] = sin ? *reinterpret_cast<const float4*>(srow + c + 4) : fz;
+    ev[it] = (in && okA) ? *reinterpret_cast<const bf16x8_t*>(erow + c) : zero;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      ws[it][p] = (in && has_s) ? *reinterpret_cast<const bf16x8_t*>(wrow[p] + c) : zero;
+      we[it][p] = in ? *reinterpret_cast<const bf16x8_t*>(wrow[p] + r + c) : zero;
+    }
+  }
+  f32x4_t acc[3];
+#pragma unroll
+  for (int p = 0; p < 3; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int it = 0; it < kCellIt; ++it) {
+    if (w + 4 * it >= nks) break;              // wave-uniform
+    if (has_s) {
+      bf16x8_t hi, mid, lo;
+      split3(sv[it][0], sv[it][1], hi, mid, lo);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, ws[it][p], acc[p], 0, 0, 0);
+        acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, ws[it][p], acc[p], 0, 0, 0);
+        acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, ws[it][p], acc[p], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ev[it], we[it][p], acc[p], 0, 0, 0);
+  }
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[p][w][lane][i] = acc[p][i];
+  __syncthreads();
+  // lane (n, g) of wave w: request req0 + 4 g + w, entry j0 + n
+  float pre[3];
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+    pre[p] = red[p][0][lane][w] + red[p][1][lane][w] + red[p][2][lane][w] + red[p][3][lane][w];
+  const int req = req0 + 4 * kg + w, j = j0 + m;
+  if (req >= a.R) return;
+  const int64_t pos = (int64_t)req * a.gamma + (k - 1);
+  const float* Pr = a.P + pos * 3 * r;
+  const float pg = pre[0] + Pr[j], pc = pre[1] + Pr[r + j], po = pre[2] + Pr[2 * r + j];
+  const float sp = has_s ? a.state[(pos - 1) * r + j] : 0.f;
+  const float g = 1.f / (1.f + expf(-pg));
+  const float s = g * sp + (1.f - g) * tanhf(pc);
+  const float e = tanhf(po);
+  if (!isfinite(pg) || !isfinite(pc) || !isfinite(po)) set_flag(a.status, kFlagNonFinite);
+  a.state[pos * r + j] = s;
+  reinterpret_cast<uint16_t*>(a.feat)[pos * r + j] = f32_to_bf16(e);
+}
+
 }  // namespace
 
 hipError_t launch_rnn_hproj(const RnnArgs& a, hipStream_t st) {
@@ -221,7 +415,8 @@ hipError_t launch_rnn_hproj(const RnnArgs& a, hipStream_t st) {
   if (M == 0) return hipSuccess;
   const bool aligned = ((reinterpret_cast<uintptr_t>(a.h) | reinterpret_cast<uintptr_t>(a.Wr)) & 15) == 0;
   if (a.h_bf16 && a.w_bf16 && aligned && (a.d % 8) == 0) {
-    hipLaunchKernelGGL(k_rnn_hproj_mfma, dim3((M + kHT - 1) / kHT, (N + kHT - 1) / kHT), dim3(256),
+    const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    hipLaunchKernelGGL(k_rnn_hproj_mfma, dim3(kXcds * ((tiles + kXcds - 1) / kXcds)), dim3(256),
                        0, st, reinterpret_cast<const uint16_t*>(a.h),
                        reinterpret_cast<const uint16_t*>(a.Wr), M, N, a.d, ldw, wcol, a.P);
     return hipGetLastError();
@@ -243,8 +438,21 @@ hipError_t launch_rnn_hproj(const RnnArgs& a, hipStream_t st) {
 hipError_t launch_rnn_cell(const RnnArgs& a, int k, hipStream_t st) {
   if (a.R == 0) return hipSuccess;
   const dim3 grid((a.R + 15) / 16, (a.rank + 15) / 16);
-  if (a.w_bf16) hipLaunchKernelGGL((k_rnn_cell<uint16_t>), grid, dim3(256), 0, st, a, k);
-  else hipLaunchKernelGGL((k_rnn_cell<float>), grid, dim3(256), 0, st, a, k);
+  const size_t es = a.w_bf16 ? 2 : 4;
+  const bool vec = (reinterpret_cast<uintptr_t>(a.Wr) & 15) == 0 &&
+                   ((size_t)(2 * a.rank + a.d) * es) % 16 == 0;
+  const bool mfma_ok = a.w_bf16 && vec && a.rank <= 4 * kCellIt * 32 &&
+                       (reinterpret_cast<uintptr_t>(a.W1) & 15) == 0 &&
+                       std::getenv("DSPARK_RNN_CELL_VALU") == nullptr;
+  if (mfma_ok) {
+    hipLaunchKernelGGL(k_rnn_cell_mfma, grid, dim3(256), 0, st, a, k);
+  } else if (a.w_bf16) {
+    if (vec) hipLaunchKernelGGL((k_rnn_cell<uint16_t, true>), grid, dim3(256), 0, st, a, k);
+    else hipLaunchKernelGGL((k_rnn_cell<uint16_t, false>), grid, dim3(256), 0, st, a, k);
+  } else {
+    if (vec) hipLaunchKernelGGL((k_rnn_cell<float, true>), grid, dim3(256), 0, st, a, k);
+    else hipLaunchKernelGGL((k_rnn_cell<float, false>), grid, dim3(256), 0, st, a, k);
+  }
   return hipGetLastError();
 }
 

@@ -412,6 +412,24 @@ dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, int d, float T,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Instrumented dspark_draft_rnn for performance measurement: identical
+ * results; additionally records ev_begin[k-1] / ev_end[k-1] on `stream`
+ * around the per-chunk statistics kernel of step k (the draft's dominant
+ * kernel) and sets *n_timed = gamma.
+ *   ev_begin, ev_end  (host) arrays of gamma events created by the caller
+ *   n_timed           (host, nullable) number of event pairs recorded
+ */
+dspark_status dspark_draft_rnn_profiled(int R, int gamma, int V, int r, int d, float T,
+                                        uint64_t seed, uint64_t round,
+                                        const void* U, dspark_dtype U_dt,
+                                        const void* W1, const void* W2t, dspark_dtype W_dt,
+                                        const void* Wr, const void* h, dspark_dtype h_dt,
+                                        const int32_t* x0, int32_t* x, float* logp_d,
+                                        float* lse_d, float* margin, void* feat, float* state,
+                                        void* ws, size_t ws_bytes, hipStream_t stream,
+                                        hipEvent_t* ev_begin, hipEvent_t* ev_end, int* n_timed);
+
+/*
  * dspark_verify for drafts whose bias is carried by per-position features
  * (the RNN head above): identical accept tests and random streams; at a
  * rejected position k the draft distribution is rebuilt as

@@ -744,3 +744,14 @@ def test_rnn_full_config2_sampled():
     cfg = synth.config(2)
     inp = synth.make_inputs(cfg, device=DEV)
     run_and_check_rnn(cfg, None, inp_dev=inp, gain=1.0, reqs=[0, 255])
+
+
+@pytest.mark.parametrize("over", [dict(R=40, gamma=5, V=3000, d=256),
+                                  dict(R=35, gamma=4, V=2000, d=72, rank=512)],
+                         ids=["r256", "r512"])
+def test_rnn_vector_alu_cell(monkeypatch, over):
+    """The fp32 vector-ALU cell (the path of float32 weights and unaligned
+    rows) on bf16 weights, forced by the environment switch."""
+    monkeypatch.setenv("DSPARK_RNN_CELL_VALU", "1")
+    cfg = synth.scaled(synth.config(2), **over)
+    run_and_check_rnn(cfg, synth.make_inputs(cfg, device="cpu"))
