@@ -15,7 +15,7 @@
 //                      depend on the drafted tokens): P = h Wr_h^T, an
 //                      (R gamma) x d x 3r bf16 contraction on MFMA with fp32
 //                      accumulation (bf16 products are exact in fp32),
-//                      LDS-staged 128 x 128 tiles.
+//                      LDS-staged 128 x 128 tiles, loads two stages ahead.
 //   k_rnn_hproj_valu : the same for float32 operands or unaligned rows.
 //   k_rnn_cell_mfma  : per step, the recurrent part [s_{k-1} ; W1[x_{k-1}]]
 //                      (2r inputs) on MFMA with the fp32 state split into
@@ -58,15 +58,16 @@ template <> __device__ __forceinline__ void st_f<uint16_t>(uint16_t* p, int64_t 
 
 // ------------------------------------------------------------- h projection
 // P[m][q] = sum_t h[m][t] Wr[q][2r + t], m < M = R gamma, q < N = 3r.
-// Workgroup tile kBM x kBN (256 threads): per 32-wide k-step the tile's rows
-// of h and of Wr are staged through LDS (double buffered; the next k-step's
-// global loads are in flight while this one is computed), and wave w computes
-// the 64 x 64 quarter (w >> 1, w & 1) as 4 x 4 tiles of
-// v_mfma_f32_16x16x32_bf16.  Operand lane (l & 15, l >> 4) holds row l & 15
-// of its 16-row tile, k-values 8 (l >> 4) + [0, 8); result lane (n, g) holds
-// rows 4 g + [0, 4) of column n.  Workgroups b, b + 8, ... run on one XCD:
-// each XCD takes a contiguous run of tiles, N fastest, so tiles that share
-// rows of h share that XCD's L2.
+// Workgroup tile kBM x kBN (256 threads).  The contraction runs in stages of
+// kBK columns: a stage's rows of h and of Wr are staged through LDS (double
+// buffered), and the global loads of stage s + 2 are issued before stage s is
+// computed, so two stages of MFMAs cover their latency.  Wave w computes the
+// 64 x 64 quarter (w >> 1, w & 1) as 4 x 4 tiles of v_mfma_f32_16x16x32_bf16,
+// two 32-wide k-steps per stage.  Operand lane (l & 15, l >> 4) holds row
+// l & 15 of its 16-row tile, k-values 8 (l >> 4) + [0, 8); result lane (n, g)
+// holds rows 4 g + [0, 4) of column n.  Workgroups b, b + 8, ... run on one
+// XCD: each XCD takes a contiguous run of tiles, N fastest, so tiles that
+// share rows of h share that XCD's L2.
 // 16 bytes at p (always a valid address), or zeros when !ok.  The zeroing is a
 // mask on the loaded value, so the load itself stays an unconditional global
 // load (a select between a load and a constant can otherwise become a load
@@ -77,9 +78,11 @@ __device__ __forceinline__ uint4 ld16_or_zero(const uint16_t* p, bool ok) {
   return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
-constexpr int kBM = 128, kBN = 128;
-constexpr int kLdsRow = 40;                 // bf16 per LDS row: 32 + 8 of padding (80 bytes)
-constexpr int kXcds = 8;                    // XCDs of an MI355X
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kLdsRow = kBK + 8;             // bf16 per LDS row (144 bytes: rows 4 banks apart)
+constexpr int kXcds = 8;                     // XCDs of an MI355X
+
+struct HStage { uint4 a[4], b[4]; };         // one stage's pieces of this thread
 
 __global__ __launch_bounds__(256) void k_rnn_hproj_mfma(const uint16_t* __restrict__ h,
                                                          const uint16_t* __restrict__ Wr, int M,
@@ -93,16 +96,33 @@ __global__ __launch_bounds__(256) void k_rnn_hproj_mfma(const uint16_t* __restri
   const int t = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (t >= tiles) return;
   const int m0 = (t / nN) * kBM, n0 = (t % nN) * kBN;
-  // staging: thread t moves pieces t and t + 256 (row p >> 2, 16-byte column
-  // p & 3); both pieces share the column
-  const int kp = tid & 3;
-  const int row0 = tid >> 2, row1 = row0 + 64;
-  const uint16_t* ga0 = h + (int64_t)min(m0 + row0, M - 1) * d + 8 * kp;
-  const uint16_t* ga1 = h + (int64_t)min(m0 + row1, M - 1) * d + 8 * kp;
-  const uint16_t* gb0 = Wr + (int64_t)min(n0 + row0, N - 1) * ldw + wcol + 8 * kp;
-  const uint16_t* gb1 = Wr + (int64_t)min(n0 + row1, N - 1) * ldw + wcol + 8 * kp;
-  const int l0 = (row0 * kLdsRow + 8 * kp) / 8, l1 = (row1 * kLdsRow + 8 * kp) / 8;
-  const int ksteps = (d + 31) / 32;
+  // staging: pieces tid + 256 i, i < 4: row (tid >> 3) + 32 i, 16-byte column tid & 7
+  const int kp = tid & 7, rbase = tid >> 3;
+  const uint16_t* ga[4];
+  const uint16_t* gb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ga[i] = h + (int64_t)min(m0 + rbase + 32 * i, M - 1) * d + 8 * kp;
+    gb[i] = Wr + (int64_t)min(n0 + rbase + 32 * i, N - 1) * ldw + wcol + 8 * kp;
+  }
+  const int nst = (d + kBK - 1) / kBK;
+  auto gload = [&](HStage& S, int st) __attribute__((always_inline)) {
+    const bool ok = st < nst && st * kBK + 8 * kp < d;     // d % 8 == 0: all in or all out
+    const int o = ok ? st * kBK : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      S.a[i] = ld16_or_zero(ga[i] + o, ok);
+      S.b[i] = ld16_or_zero(gb[i] + o, ok);
+    }
+  };
+  auto lstore = [&](const HStage& S, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int l = ((rbase + 32 * i) * kLdsRow + 8 * kp) / 8;
+      As[buf][l] = S.a[i];
+      Bs[buf][l] = S.b[i];
+    }
+  };
   f32x4_t acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -110,40 +130,38 @@ __global__ __launch_bounds__(256) void k_rnn_hproj_mfma(const uint16_t* __restri
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int rl = lane & 15, kg = lane >> 4;
   const int wm = 64 * (wv >> 1), wn = 64 * (wv & 1);
-  {
-    const bool in = 8 * kp < d;                              // d % 8 == 0: all in or all out
-    As[0][l0] = ld16_or_zero(ga0, in);
-    As[0][l1] = ld16_or_zero(ga1, in);
-    Bs[0][l0] = ld16_or_zero(gb0, in);
-    Bs[0][l1] = ld16_or_zero(gb1, in);
-  }
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sub = 0; sub < kBK / 32; ++sub) {
+      bf16x8_t Af[4], Bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Af[i] = __builtin_bit_cast(bf16x8_t, As[buf][((wm + 16 * i + rl) * kLdsRow + 32 * sub + 8 * kg) / 8]);
+        Bf[i] = __builtin_bit_cast(bf16x8_t, Bs[buf][((wn + 16 * i + rl) * kLdsRow + 32 * sub + 8 * kg) / 8]);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[a], Bf[b], acc[a][b], 0, 0, 0);
+    }
+  };
+  HStage S0, S1;
+  gload(S0, 0);
+  gload(S1, 1);
+  lstore(S0, 0);
   __syncthreads();
-  for (int ks = 0; ks < ksteps; ++ks) {
-    const int buf = ks & 1;
-    // next k-step's pieces, in flight during this step's MFMAs
-    const bool nx = ks + 1 < ksteps && (ks + 1) * 32 + 8 * kp < d;
-    const int o = nx ? 32 * (ks + 1) : 0;
-    const uint4 ra0 = ld16_or_zero(ga0 + o, nx);
-    const uint4 ra1 = ld16_or_zero(ga1 + o, nx);
-    const uint4 rb0 = ld16_or_zero(gb0 + o, nx);
-    const uint4 rb1 = ld16_or_zero(gb1 + o, nx);
-    bf16x8_t Af[4], Bf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      Af[i] = __builtin_bit_cast(bf16x8_t, As[buf][((wm + 16 * i + rl) * kLdsRow + 8 * kg) / 8]);
-      Bf[i] = __builtin_bit_cast(bf16x8_t, Bs[buf][((wn + 16 * i + rl) * kLdsRow + 8 * kg) / 8]);
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[a], Bf[b], acc[a][b], 0, 0, 0);
-    if (ks + 1 < ksteps) {
-      As[buf ^ 1][l0] = ra0;
-      As[buf ^ 1][l1] = ra1;
-      Bs[buf ^ 1][l0] = rb0;
-      Bs[buf ^ 1][l1] = rb1;
-    }
+  // two stages per trip so that the register sets keep fixed names: at stage
+  // s, the set for s + 1 is in flight and the set for s + 2 is issued
+  for (int st = 0; st < nst; st += 2) {
+    gload(S0, st + 2);
+    compute(0);
+    if (st + 1 < nst) lstore(S1, 1);
+    __syncthreads();
+    if (st + 1 >= nst) break;
+    gload(S1, st + 3);
+    compute(1);
+    if (st + 2 < nst) lstore(S0, 0);
     __syncthreads();
   }
 #pragma unroll
