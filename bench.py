@@ -293,7 +293,9 @@ def main():
     avg_ms = float(np.mean(durs))
     if nt == 1:
         kernel = "k_draft_persistent"
-        kdesc = "k_draft_persistent (whole draft: gamma steps, one cooperative launch)"
+        kdesc = ("k_draft_persistent (RNN head: cell, statistics and pick of all gamma steps, one "
+                 "cooperative launch)" if rnn else
+                 "k_draft_persistent (whole draft: gamma steps, one cooperative launch)")
         kb = draft_kernel_bytes(cfg)
         kflops = 2.0 * cfg.R * cfg.rank * cfg.V * cfg.gamma
     else:

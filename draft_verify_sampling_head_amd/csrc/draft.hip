@@ -155,6 +155,12 @@ struct PersistArgs {
   int nslice;                               // vocabulary slices = ceil(V / 512)
   uint32_t* bar;                            // grid-barrier counter, zero at launch
   uint32_t spin_limit;                      // bounded wait per barrier
+  // RNN head: the recurrent cell runs inside the launch before each step
+  const float* rP;                          // [R*gamma][3 rank] h part of the projection
+  float* rstate;                            // [R][gamma][rank] s_1 .. s_gamma
+  uint16_t* rfeat;                          // [R][gamma][rank] e_1 .. e_gamma (bf16)
+  const uint16_t* rWr;                      // [3 rank][2 rank + d]
+  int rd;                                   // d
 };
 
 // Values that cross workgroups inside the launch (chunk statistics, chunk
@@ -172,6 +178,14 @@ __device__ __forceinline__ float2 ld_coh2(const float2* p) {
   const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float2*>(p)),
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+}
+// 16 bytes written by another workgroup in this launch: two device-coherent
+// 64-bit loads (p 16-byte aligned).
+__device__ __forceinline__ uint4 ld_coh16(const void* p) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<void*>(p));
+  const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
 }
 __device__ __forceinline__ void st_coh2(float2* p, float2 v) {
   const uint64_t u = (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32);
@@ -702,7 +716,7 @@ struct PickLds {
 // winner writes the outputs.
 template <int KS, bool GREEDY>
 __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, float s2, BlockScratch& sh,
-                                           PickLds<2 * KS>& pl) {
+                                           PickLds<2 * KS>& pl, const uint16_t* feat) {
   constexpr int NT = kPThreads, TPE = NT / kChunk;
   constexpr int SEG = 2 * KS, NQ = SEG / TPE;   // 16-byte pieces of the rank per thread
   static_assert(kPMaxChunks <= 4 * NT, "four chunks per thread");
@@ -726,8 +740,9 @@ __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, float 
     }
   }
   if (!GREEDY && tid < SEG)
-    pl.E[tid] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.W1) +
-                                                (int64_t)prev * a.rank + 8 * tid);
+    pl.E[tid] = feat ? ld_coh16(feat + ((int64_t)i * a.gamma + (k - 1)) * a.rank + 8 * tid)
+                     : *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.W1) +
+                                                       (int64_t)prev * a.rank + 8 * tid);
   const int64_t o = (int64_t)i * a.gamma + (k - 1);
   if (GREEDY) {
     float v = -INFINITY;
@@ -848,7 +863,163 @@ __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, float 
   __syncthreads();                          // LDS slots and the W1 row are reused
 }
 
-template <int KS, bool GREEDY>
+// ---- RNN head inside the persistent launch
+// Feature rows e_k of requests row0 .. row0 + rows - 1 into LDS rows of ROWP
+// 16-byte pieces (the layout of gather_w1_rows).  They were written by other
+// workgroups in this launch, so they are read with device-coherent loads,
+// eight pieces per thread in flight at once.
+template <int SEG, int ROWP>
+__device__ __forceinline__ void gather_feat_rows(uint4* E, int row0, int rows, int k, int gamma,
+                                                 const uint16_t* feat, int rank) {
+  const int npieces = rows * ROWP;
+  for (int p0 = threadIdx.x; p0 < npieces; p0 += 8 * kPThreads) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = min(p0 + u * kPThreads, npieces - 1);
+      const int rl = p / ROWP, sp = p % ROWP;
+      v[u] = ld_coh16(feat + ((int64_t)(row0 + rl) * gamma + (k - 1)) * rank + 8 * (sp < SEG ? sp : 0));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (p0 + u * kPThreads < npieces) E[p0 + u * kPThreads] = v[u];
+  }
+}
+
+// float32 -> bf16 bits, round to nearest, ties to even (finite values)
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// bf16 parts hi + mid + lo of eight fp32 values (24 significant bits: the
+// products with bf16 weights are exact in fp32)
+__device__ __forceinline__ void split3_bf16(const float (&v)[8], bf16x8_t& hi, bf16x8_t& mid,
+                                            bf16x8_t& lo) {
+  uint16_t h[8], m[8], l[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    h[t] = (uint16_t)bf16_bits(v[t]);
+    const float r1 = v[t] - __uint_as_float((uint32_t)h[t] << 16);
+    m[t] = (uint16_t)bf16_bits(r1);
+    const float r2 = r1 - __uint_as_float((uint32_t)m[t] << 16);
+    l[t] = (uint16_t)bf16_bits(r2);
+  }
+  hi = __builtin_bit_cast(bf16x8_t, h);
+  mid = __builtin_bit_cast(bf16x8_t, m);
+  lo = __builtin_bit_cast(bf16x8_t, l);
+}
+
+// The cell of step k (DSpark summary page, Method details, RNN head):
+// g = sigmoid(Wr_g z), s_k = g s_{k-1} + (1 - g) tanh(Wr_c z), e_k = tanh(Wr_o z)
+// with z = [s_{k-1} ; W1[x_{k-1}] ; h_k], the h part precomputed in rP.  Tile
+// (rt, jt) = requests 16 rt + [0, 16) x state entries 16 jt + [0, 16) with
+// their gate, candidate and output rows; workgroup b takes tiles b, b + grid,
+// ...  Wave w computes k-step w (32 columns) of the recurrent product on
+// MFMA, the state half as three exact bf16 parts; red (LDS, 24 KB) adds the
+// eight waves' partial results, then waves 0-3 finish request rows 4 g + w.
+// s_{k-1} and the tokens x_{k-1} come from other workgroups (device-coherent
+// loads; tokens waited for), and s_k, e_k go out with device-coherent stores.
+__device__ __forceinline__ void rnn_cell_tiles_p(const PersistArgs& P, int k, float* red) {
+  const DraftPickArgs& a = P.p;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = a.rank, ldw = 2 * r + P.rd, nks = r / 32;   // r in {64, 128, 256}
+  const int ntj = r / 16, ntiles = ((a.R + 15) / 16) * ntj;
+  const int m = lane & 15, kg = lane >> 4;
+  const uint16_t* W1 = reinterpret_cast<const uint16_t*>(a.W1);
+  const bool has_s = k >= 2;
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int req0 = (tile / ntj) * 16, j0 = (tile % ntj) * 16;
+    f32x4_t acc[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (w < nks) {
+      const int reqA = req0 + m;
+      const bool okA = reqA < a.R;
+      int prev = 0;
+      if (okA) {
+        prev = (k == 1) ? a.x0[reqA]
+                        : wait_token(a.x + (int64_t)reqA * (a.gamma + 1) + (k - 1), P.spin_limit,
+                                     a.status);
+        if (prev >= a.V || (k == 1 && prev < 0)) set_flag(a.status, kFlagBadToken);
+        if (prev < 0 || prev >= a.V) prev = 0;
+      }
+      const int c = 32 * w + 8 * kg;
+      const bf16x8_t zero = {};
+      const bf16x8_t ev = okA ? *reinterpret_cast<const bf16x8_t*>(W1 + (int64_t)prev * r + c) : zero;
+      bf16x8_t ws[3], we[3];
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const uint16_t* wrow = P.rWr + (int64_t)(q * r + j0 + m) * ldw;
+        ws[q] = *reinterpret_cast<const bf16x8_t*>(wrow + c);
+        we[q] = *reinterpret_cast<const bf16x8_t*>(wrow + r + c);
+      }
+      if (has_s) {
+        float sv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (okA) {
+          const float* srow = P.rstate + ((int64_t)reqA * a.gamma + (k - 2)) * r + c;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float2 v = ld_coh2(reinterpret_cast<const float2*>(srow) + t);
+            sv[2 * t] = v.x;
+            sv[2 * t + 1] = v.y;
+          }
+        }
+        bf16x8_t hi, mid, lo;
+        split3_bf16(sv, hi, mid, lo);
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, ws[q], acc[q], 0, 0, 0);
+          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, ws[q], acc[q], 0, 0, 0);
+          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, ws[q], acc[q], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ev, we[q], acc[q], 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[((q * kPWaves + w) * 64 + lane) * 4 + i] = acc[q][i];
+    __syncthreads();
+    if (w < 4) {
+      float pre[3];
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        float t = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kPWaves; ++ww) t += red[((q * kPWaves + ww) * 64 + lane) * 4 + w];
+        pre[q] = t;
+      }
+      const int req = req0 + 4 * kg + w, j = j0 + m;
+      float e = 0.f;
+      if (req < a.R) {
+        const int64_t pos = (int64_t)req * a.gamma + (k - 1);
+        const float* Pr = P.rP + pos * 3 * r;
+        const float pg = pre[0] + Pr[j], pc = pre[1] + Pr[r + j], po = pre[2] + Pr[2 * r + j];
+        float sp = 0.f;
+        if (has_s)
+          sp = __hip_atomic_load(P.rstate + (pos - 1) * r + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float g = 1.f / (1.f + expf(-pg));
+        const float sn = g * sp + (1.f - g) * tanhf(pc);
+        e = tanhf(po);
+        if (!isfinite(pg) || !isfinite(pc) || !isfinite(po)) set_flag(a.status, kFlagNonFinite);
+        __hip_atomic_store(P.rstate + pos * r + j, sn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      // entries j, j + 1 share a 32-bit word of the feature row
+      const uint32_t eb = bf16_bits(e);
+      const uint32_t other = (uint32_t)__shfl_xor((int)eb, 1);
+      if (req < a.R && (m & 1) == 0) {
+        const int64_t pos = (int64_t)req * a.gamma + (k - 1);
+        st_coh(reinterpret_cast<int*>(P.rfeat + pos * r + j), (int)(eb | (other << 16)));
+      }
+    }
+    __syncthreads();                        // red is reused by the next tile
+  }
+}
+
+template <int KS, bool GREEDY, bool FEAT>
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_draft_persistent(PersistArgs P) {
   constexpr int SEG = 2 * KS;               // 16-byte segments per W1 row (rank / 8)
   static_assert(KS % 2 == 0, "rank must be a multiple of 32");
@@ -890,6 +1061,12 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int ngroups = (R + kPRows - 1) / kPRows;
   for (int k = 1; k <= a.gamma; ++k) {
     a.k = k;
+    if constexpr (FEAT) {
+      // ================= RNN cell of step k: e_k and s_k of every request,
+      // visible to every workgroup after the barrier
+      rnn_cell_tiles_p(P, k, reinterpret_cast<float*>(E));
+      grid_barrier(P.bar, ++epoch, P.spin_limit, a.status);
+    }
     // ================= phase A: chunk statistics of step k for every request
     for (int g = 0; g < ngroups; ++g) {
       const int row0 = g * kPRows;
@@ -907,17 +1084,22 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         // tokens x_{k-1} of the group (staged in LDS), then their W1 rows.
         // x_{k-1} is written by the picks of step k-1: waiting for each
         // token to appear is the only synchronisation with them
-        for (int rl = tid; rl < rows; rl += kPThreads) {
-          const int row = row0 + rl;
-          int prev = (k == 1) ? a.x0[row]
-                              : wait_token(a.x + (int64_t)row * (a.gamma + 1) + (k - 1), P.spin_limit,
-                                           a.status);
-          if (prev >= V || (k == 1 && prev < 0)) set_flag(a.status, kFlagBadToken);
-          if (prev < 0 || prev >= V) prev = 0;
-          PV[rl] = prev;
+        if constexpr (FEAT) {
+          // the group's feature rows e_k (written by the cell phase)
+          gather_feat_rows<SEG, ROWP>(E, row0, rows, k, a.gamma, P.rfeat, a.rank);
+        } else {
+          for (int rl = tid; rl < rows; rl += kPThreads) {
+            const int row = row0 + rl;
+            int prev = (k == 1) ? a.x0[row]
+                                : wait_token(a.x + (int64_t)row * (a.gamma + 1) + (k - 1), P.spin_limit,
+                                             a.status);
+            if (prev >= V || (k == 1 && prev < 0)) set_flag(a.status, kFlagBadToken);
+            if (prev < 0 || prev >= V) prev = 0;
+            PV[rl] = prev;
+          }
+          __syncthreads();
+          gather_w1_rows<SEG, ROWP>(E, PV, rows, W1, a.rank);
         }
-        __syncthreads();
-        gather_w1_rows<SEG, ROWP>(E, PV, rows, W1, a.rank);
       }
       wait_vm_zero();
       __syncthreads();
@@ -968,7 +1150,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     // No barrier follows: phase A of step k+1 waits for the tokens it reads,
     // and a token is written after its pick has read the chunk statistics
     // that phase A of step k+1 overwrites.
-    for (int i = b; i < R; i += gridDim.x) pick_row_p<KS, GREEDY>(a, i, s2, sh, pl);
+    for (int i = b; i < R; i += gridDim.x) pick_row_p<KS, GREEDY>(a, i, s2, sh, pl, FEAT ? P.rfeat : nullptr);
   }
 }
 
@@ -1139,26 +1321,26 @@ bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void*
 // workgroup of each instance fits per compute unit).
 struct PersistInfo {
   int cus = -1;
-  int fits[3][2] = {{-1, -1}, {-1, -1}, {-1, -1}};
+  int fits[3][2][2] = {{{-1, -1}, {-1, -1}}, {{-1, -1}, {-1, -1}}, {{-1, -1}, {-1, -1}}};
 };
 static PersistInfo g_pinfo[64];
 
-template <int KS, bool G>
+template <int KS, bool G, bool F>
 static bool persist_fits(PersistInfo& pi, int ki) {
-  if (pi.fits[ki][G] < 0) {
+  if (pi.fits[ki][G][F] < 0) {
     int nb = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &nb, reinterpret_cast<const void*>(k_draft_persistent<KS, G>), kPThreads, 0);
-    pi.fits[ki][G] = (e == hipSuccess && nb >= 1) ? 1 : 0;
+        &nb, reinterpret_cast<const void*>(k_draft_persistent<KS, G, F>), kPThreads, 0);
+    pi.fits[ki][G][F] = (e == hipSuccess && nb >= 1) ? 1 : 0;
     (void)hipGetLastError();
   }
-  return pi.fits[ki][G] == 1;
+  return pi.fits[ki][G][F] == 1;
 }
 
-template <int KS, bool G>
+template <int KS, bool G, bool F>
 static hipError_t launch_persist_ks(PersistArgs& P, int grid, hipStream_t st) {
   void* args[] = {&P};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_draft_persistent<KS, G>),
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_draft_persistent<KS, G, F>),
                                     dim3(grid), dim3(kPThreads), args, 0, st);
 }
 
@@ -1168,7 +1350,7 @@ static hipError_t launch_persist_ks(PersistArgs& P, int grid, hipStream_t st) {
 // U loads use 32-bit lane offsets).  DSPARK_DRAFT_KERNEL=steps in the
 // environment selects the per-step schedule for every shape.
 static int persistent_grid(int gamma, int V, int rank, bool u_bf16, bool w_bf16, bool u_vec,
-                           const void* W1, const void* W2t, bool greedy) {
+                           const void* W1, const void* W2t, bool greedy, bool feat) {
   const char* env = std::getenv("DSPARK_DRAFT_KERNEL");
   if (env && std::strcmp(env, "steps") == 0) return 0;
   if (!u_bf16 || !w_bf16 || !u_vec || (V % 8) != 0) return 0;
@@ -1187,9 +1369,18 @@ static int persistent_grid(int gamma, int V, int rank, bool u_bf16, bool w_bf16,
   if (pi.cus < 1 || pi.cus > kMaxGrid || nslice > pi.cus || (V + kChunk - 1) / kChunk > kPMaxChunks)
     return 0;
   bool fits;
-  if (rank == 64) fits = greedy ? persist_fits<4, true>(pi, 0) : persist_fits<4, false>(pi, 0);
-  else if (rank == 128) fits = greedy ? persist_fits<8, true>(pi, 1) : persist_fits<8, false>(pi, 1);
-  else fits = greedy ? persist_fits<16, true>(pi, 2) : persist_fits<16, false>(pi, 2);
+#define DSPARK_FITS(KS_, KI_, F_) \
+  (greedy ? persist_fits<KS_, true, F_>(pi, KI_) : persist_fits<KS_, false, F_>(pi, KI_))
+  if (feat) {
+    if (rank == 64) fits = DSPARK_FITS(4, 0, true);
+    else if (rank == 128) fits = DSPARK_FITS(8, 1, true);
+    else fits = DSPARK_FITS(16, 2, true);
+  } else {
+    if (rank == 64) fits = DSPARK_FITS(4, 0, false);
+    else if (rank == 128) fits = DSPARK_FITS(8, 1, false);
+    else fits = DSPARK_FITS(16, 2, false);
+  }
+#undef DSPARK_FITS
   return fits ? pi.cus : 0;
 }
 
@@ -1233,11 +1424,21 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
   p.U = U; p.W1 = W1; p.W2t = W2t; p.x0 = x0; p.x = x; p.logp_d = logp_d; p.lse_d = lse_d;
   p.margin = margin; p.L = Lc; p.I = Ic; p.status = status;
 
-  // The RNN head's features e_k come from a recurrent cell launched before
-  // each step; its draft always takes the per-step schedule.
+  // RNN head: the features e_k come from the recurrent cell, run inside the
+  // persistent launch before each step (its h part precomputed), or launched
+  // before each step of the per-step schedule.  The fused form also needs
+  // bf16 h / Wr with 16-byte aligned rows and a 16-byte aligned feature tensor.
   const void* feat = rnn ? rnn->feat : nullptr;
   p.feat = feat;
-  const int grid = rnn ? 0 : persistent_grid(gamma, V, rank, u_bf16, w_bf16, u_vec, W1, W2t, greedy);
+  const char* cell_env = std::getenv("DSPARK_RNN_CELL_VALU");
+  const bool rnn_fused_ok =
+      rnn && rnn->w_bf16 && rnn->h_bf16 && cell_env == nullptr &&
+      ((reinterpret_cast<uintptr_t>(rnn->Wr) | reinterpret_cast<uintptr_t>(rnn->feat)) & 15) == 0 &&
+      ((2 * rank + rnn->d) % 8) == 0;
+  const int grid = (rnn && !rnn_fused_ok)
+                       ? 0
+                       : persistent_grid(gamma, V, rank, u_bf16, w_bf16, u_vec, W1, W2t, greedy,
+                                         rnn != nullptr);
   if (grid > 0) {
     PersistArgs P{};
     P.p = p;
@@ -1248,14 +1449,32 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     P.spin_limit = sl ? (uint32_t)std::strtoul(sl, nullptr, 10) : kBarrierSpins;
     if (P.spin_limit == 0) P.spin_limit = 1;
     const int prep_blocks = (int)std::min<int64_t>(64, ((int64_t)R * (gamma + 1) + 255) / 256);
+    hipError_t e;
+    if (rnn) {
+      P.rP = rnn->P;
+      P.rstate = rnn->state;
+      P.rfeat = reinterpret_cast<uint16_t*>(rnn->feat);
+      P.rWr = reinterpret_cast<const uint16_t*>(rnn->Wr);
+      P.rd = rnn->d;
+      if ((e = launch_rnn_hproj(*rnn, st)) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(k_draft_prep, dim3(prep_blocks), dim3(256), 0, st, P.bar, kMaxGrid, x, x0, R,
                        gamma);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev_begin && (e = hipEventRecord(ev_begin[0], st)) != hipSuccess) return e;
-    if (rank == 64) e = greedy ? launch_persist_ks<4, true>(P, grid, st) : launch_persist_ks<4, false>(P, grid, st);
-    else if (rank == 128) e = greedy ? launch_persist_ks<8, true>(P, grid, st) : launch_persist_ks<8, false>(P, grid, st);
-    else e = greedy ? launch_persist_ks<16, true>(P, grid, st) : launch_persist_ks<16, false>(P, grid, st);
+#define DSPARK_LP(KS_, F_) \
+    (greedy ? launch_persist_ks<KS_, true, F_>(P, grid, st) : launch_persist_ks<KS_, false, F_>(P, grid, st))
+    if (rnn) {
+      if (rank == 64) e = DSPARK_LP(4, true);
+      else if (rank == 128) e = DSPARK_LP(8, true);
+      else e = DSPARK_LP(16, true);
+    } else {
+      if (rank == 64) e = DSPARK_LP(4, false);
+      else if (rank == 128) e = DSPARK_LP(8, false);
+      else e = DSPARK_LP(16, false);
+    }
+#undef DSPARK_LP
     if (e != hipSuccess) return e;
     if (ev_end && (e = hipEventRecord(ev_end[0], st)) != hipSuccess) return e;
     if (n_timed) *n_timed = 1;

@@ -650,7 +650,7 @@ def test_full_config4_cells_sampled(R, gamma, rank):
 
 
 # ---------------------------------------------------------------- RNN head
-def run_and_check_rnn(cfg, inp_cpu=None, inp_dev=None, gain=3.0, reqs=None, rnd=0):
+def run_and_check_rnn(cfg, inp_cpu=None, inp_dev=None, gain=3.0, reqs=None, rnd=0, buf=None):
     """A full round drafted by the RNN head (its features verified by
     dspark_verify_features); every stage checked against the oracle."""
     print(f"[case rnn] {cfg.name} R={cfg.R} g={cfg.gamma} V={cfg.V} r={cfg.rank} d={cfg.d} "
@@ -659,7 +659,8 @@ def run_and_check_rnn(cfg, inp_cpu=None, inp_dev=None, gain=3.0, reqs=None, rnd=
         inp_dev = to_dev(inp_cpu)
     g = dict(inp_dev)
     g["Wr"] = synth.rnn_weights(cfg, device=DEV, gain=gain)
-    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV, rnn=(cfg.rank, cfg.d, cfg.dtype))
+    if buf is None:
+        buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV, rnn=(cfg.rank, cfg.d, cfg.dtype))
     RD.run_round(g, buf, cfg.T, cfg.philox_seed, rnd, scheduler=cfg.scheduler, layout=1,
                  head="rnn")
     torch.cuda.synchronize()
@@ -713,7 +714,13 @@ RNN_SMALL = [
     (3, dict(R=70, gamma=6, V=2500, d=64)),                              # T = 0.7
     (2, dict(R=24, gamma=4, V=1800, d=64, scheduler=False)),             # every position verified
     (2, dict(R=1, gamma=1, V=700, d=16)),
+    # shapes the fused persistent launch takes (bf16, rank 64/128/256, V % 8 == 0)
+    (1, dict(R=33, gamma=7, V=4096, d=128, rank=128)),                   # greedy
+    (3, dict(R=70, gamma=6, V=2504, d=64)),                              # T = 0.7
+    (2, dict(R=300, gamma=3, V=2048, d=32)),                             # more cell tiles than CUs
+    (2, dict(R=17, gamma=16, V=1536, d=64, rank=64)),
 ]
+RNN_FUSED = [RNN_SMALL[i] for i in (1, 2, 8, 10, 11, 12, 13)]
 
 
 @pytest.mark.parametrize("base,over", RNN_SMALL, ids=[f"rnn{i}" for i in range(len(RNN_SMALL))])
@@ -721,6 +728,24 @@ def test_rnn_round_parity(base, over):
     cfg = synth.scaled(synth.config(base), **over) if over else synth.config(base)
     inp = synth.make_inputs(cfg, device="cpu")
     run_and_check_rnn(cfg, inp)
+
+
+@pytest.mark.parametrize("base,over", RNN_FUSED, ids=[f"steps{i}" for i in range(len(RNN_FUSED))])
+def test_rnn_per_step_schedule(monkeypatch, base, over):
+    """The shapes of the fused launch, forced onto the per-step schedule."""
+    monkeypatch.setenv("DSPARK_DRAFT_KERNEL", "steps")
+    cfg = synth.scaled(synth.config(base), **over)
+    run_and_check_rnn(cfg, synth.make_inputs(cfg, device="cpu"))
+
+
+def test_rnn_rounds_reuse_buffers():
+    """Several rounds on the same buffers (features and states rewritten in
+    place), each checked against the oracle."""
+    cfg = synth.scaled(synth.config(2), R=40, gamma=5, V=3000, d=256)
+    inp = synth.make_inputs(cfg, device="cpu")
+    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV, rnn=(cfg.rank, cfg.d, cfg.dtype))
+    for rnd in range(3):
+        run_and_check_rnn(cfg, inp, rnd=rnd, buf=buf)
 
 
 def test_rnn_feature_residuals_exercised():
