@@ -111,39 +111,42 @@ def stats_kernel_bytes(cfg):
             + (s * cfg.rank * cfg.V) / cfg.gamma)
 
 
-# kernel -> (sources it is built from, committed counter summary)
+# (kernel, head) -> (sources it is built from, committed counter summary of
+# the headline workload R=256, gamma=16, V=129280, r=256)
+_PERSIST_SRC = ("draft.hip", "launch.hpp", "device_common.hpp", "sampling.hpp", "workspace.hpp")
 KERNELS = {
-    "k_markov_mfma": (("stats.hip", "launch.hpp", "device_common.hpp", "sampling.hpp", "workspace.hpp"),
-                      "k_markov_mfma_rnn_R256_g16_V129280_r256_counters.txt"),
-    "k_draft_persistent": (("draft.hip", "launch.hpp", "device_common.hpp", "sampling.hpp",
-                            "workspace.hpp"),
-                           "k_draft_persistent_R256_g16_V129280_r256_counters.txt"),
+    ("k_draft_persistent", "markov"): (_PERSIST_SRC,
+                                       "k_draft_persistent_R256_g16_V129280_r256_counters.txt"),
+    ("k_draft_persistent", "rnn"): (_PERSIST_SRC,
+                                    "k_draft_persistent_rnn_R256_g16_V129280_r256_counters.txt"),
 }
 
 
-def source_sha(kernel):
+def source_sha(key):
     """sha256 over the sources a kernel is built from."""
     import hashlib
     h = hashlib.sha256()
-    for f in KERNELS[kernel][0]:
+    for f in KERNELS[key][0]:
         with open(os.path.join(ROOT, "draft_verify_sampling_head_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def counter_traffic(kernel):
-    """HBM bytes per launch of `kernel` from its committed FETCH_SIZE /
-    WRITE_SIZE summary, calibrated against a device copy of known size; None
-    when the file is missing or the kernel sources have changed since the
-    counters were taken."""
+def counter_traffic(key, cfg, config_idx):
+    """HBM bytes per launch of the kernel `key` = (name, head) from its
+    committed FETCH_SIZE / WRITE_SIZE summary, calibrated against a device copy
+    of known size; None for other workloads, when the file is missing, or when
+    the kernel sources have changed since the counters were taken."""
+    if key not in KERNELS or config_idx != 2:
+        return None
     try:
         kv = {}
-        with open(os.path.join(ROOT, "profiles", KERNELS[kernel][1])) as fh:
+        with open(os.path.join(ROOT, "profiles", KERNELS[key][1])) as fh:
             for line in fh:
                 if ":" in line and not line.startswith((" ", "#", "|")):
                     k, v = line.split(":", 1)
                     kv[k.strip()] = v.strip()
-        if kv.get("source_sha256") != source_sha(kernel):
+        if kv.get("source_sha256") != source_sha(key):
             return None
         return float(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -342,7 +345,8 @@ def main():
         "device_status": status,
         "roofline": {"bound": "hbm", "kernel": kdesc,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(kernel),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": counter_traffic((kernel, args.head), cfg, args.config),
                      "avg_launch_us": avg_ms * 1e3, "bytes_per_launch": kb,
                      "mfma_tflops": mfma_tf, "mfma_frac": mfma_tf / MFMA_BF16_PEAK_TFLOPS},
         "cpu_baseline": cpu,
