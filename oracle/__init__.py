@@ -62,7 +62,7 @@ def lib():
         L.orc_prefix_schedule.restype = i32
         L.orc_async_schedule.argtypes = [i32, i32, P, P, i32, i32, P, P, P, P, P, P]
         L.orc_async_schedule.restype = i32
-        L.orc_acceptance_rate.argtypes = [i32, i32, i64, i32, f64, P, P, P, P, P, P, P]
+        L.orc_acceptance_rate.argtypes = [i32, i32, i64, i32, f64, P, P, P, P, P, P, P, P]
         L.orc_acceptance_rate.restype = i32
         L.orc_sts_fit.argtypes = [i32, i32, P, P, P, i32, i32, P, P, P, P]
         L.orc_sts_fit.restype = i32
@@ -255,17 +255,21 @@ def pack(rows, lens):
     return cu, flat, mr, mp, int(N[0])
 
 
-def acceptance_rate(target, x, U, W1, W2t, T):
+def acceptance_rate(target, x, U, W1, W2t, T, feat=None):
     """c*_k = sum_v min(p_d^k, p_t^k) for every request and position (dense
-    target [R][gamma+1][V]).  Returns (c_star [R][gamma], margin)."""
+    target [R][gamma+1][V]); feat [R][gamma][rank]: the RNN head's bias
+    features in place of W1[x_{k-1}].  Returns (c_star [R][gamma], margin)."""
     target = _f32(target)
     R, g1, V = target.shape
     gamma = g1 - 1
     rank = 0 if W1 is None else int(W1.shape[1])
+    if feat is not None:
+        rank = int(np.shape(feat)[-1])
     cs = np.zeros((R, gamma))
     mg = np.zeros((R, gamma))
     rc = lib().orc_acceptance_rate(R, gamma, V, rank, float(T), _p(target), _p(_i32(x)),
-                                   _p(_f32(U)), _p(_f32(W1)), _p(_f32(W2t)), _p(cs), _p(mg))
+                                   _p(_f32(U)), _p(_f32(W1)), _p(_f32(W2t)), _p(cs), _p(mg),
+                                   _p(_f32(feat)))
     assert rc == 0, rc
     return cs, mg
 

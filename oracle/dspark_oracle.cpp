@@ -789,7 +789,7 @@ int orc_verify(int R, int gamma, int64_t V, int rank, double T, uint64_t seed, u
 // Out: c_star [R][gamma]; margin [R][gamma] (nullable; +inf when T > 0).
 int orc_acceptance_rate(int R, int gamma, int64_t V, int rank, double T, const float* target,
                         const int32_t* x, const float* U, const float* W1, const float* W2t,
-                        double* c_star, double* margin) {
+                        double* c_star, double* margin, const float* feat) {
     if (R < 0 || gamma < 1 || V < 1 || !(T >= 0.0)) return 1;
     std::vector<double> s(V), lt(V);
     for (int i = 0; i < R; ++i) {
@@ -798,8 +798,19 @@ int orc_acceptance_rate(int R, int gamma, int64_t V, int rank, double T, const f
             const float* t = target + ((int64_t)i * (gamma + 1) + (k - 1)) * V;
             double cs, mg = POS_INF;
             if (T > 0.0) {
-                markov_scores(V, rank, U + ((int64_t)i * gamma + (k - 1)) * V, W1, W2t, xi[k - 1],
-                              s.data());
+                if (feat) {
+                    // the draft's bias features of this position (RNN head)
+                    const float* e = feat + ((int64_t)i * gamma + (k - 1)) * rank;
+                    const float* Uk = U + ((int64_t)i * gamma + (k - 1)) * V;
+                    for (int64_t v = 0; v < V; ++v) {
+                        double b = 0.0;
+                        for (int j = 0; j < rank; ++j) b += (double)e[j] * (double)W2t[v * rank + j];
+                        s[v] = (double)Uk[v] + b;
+                    }
+                } else {
+                    markov_scores(V, rank, U + ((int64_t)i * gamma + (k - 1)) * V, W1, W2t,
+                                  xi[k - 1], s.data());
+                }
                 for (int64_t v = 0; v < V; ++v) { s[v] /= T; lt[v] = (double)t[v] / T; }
                 const double lse_d = logsumexp(s.data(), V);
                 const double lse_t = logsumexp(lt.data(), V);

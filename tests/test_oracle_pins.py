@@ -786,6 +786,31 @@ def test_acceptance_rate_closed_forms():
     assert (O.acceptance_rate(tgt3, x2, U, W1, W2t, 0.0)[0] == 1.0).all()
 
 
+def test_acceptance_rate_with_rnn_features():
+    """With per-position bias features e_k (RNN head), c*_k = 1 - TV between
+    softmax((U_k + W2^T e_k) / T) and the target row, both by scipy on an
+    independently computed bias; the features replace W1[x_{k-1}] (W1 is not
+    read: passing nonsense for it changes nothing)."""
+    rng = np.random.default_rng(31)
+    R, g, V, rank = 3, 4, 400, 16
+    U = rng.normal(0, 2, (R, g, V)).astype(np.float32)
+    x = np.concatenate([rng.integers(0, V, (R, 1)), rng.integers(0, V, (R, g))], 1)
+    W2t = rng.normal(0, 0.4, (V, rank)).astype(np.float32)
+    feat = np.tanh(rng.normal(0, 1, (R, g, rank))).astype(np.float32)
+    tgt = (np.concatenate([U, U[:, :1]], 1) + rng.normal(0, 1, (R, g + 1, V))).astype(np.float32)
+    junk = rng.normal(0, 5, (V, rank)).astype(np.float32)
+    for T in [1.0, 0.7]:
+        cs, _ = O.acceptance_rate(tgt, x, U, junk, W2t, T, feat=feat)
+        for i in range(R):
+            for k in range(1, g + 1):
+                bias = W2t.astype(np.float64) @ feat[i, k - 1].astype(np.float64)
+                pd = special.softmax((U[i, k - 1].astype(np.float64) + bias) / T)
+                pt = special.softmax(tgt[i, k - 1].astype(np.float64) / T)
+                assert abs(cs[i, k - 1] - (1 - 0.5 * np.abs(pd - pt).sum())) < 1e-12
+        cs2, _ = O.acceptance_rate(tgt, x, U, None, W2t, T, feat=feat)
+        np.testing.assert_array_equal(cs, cs2)
+
+
 def test_acceptance_rate_is_the_verify_acceptance_probability():
     """c*_1 is the probability that the oracle's rejection test accepts x_1."""
     rng = np.random.default_rng(31)
