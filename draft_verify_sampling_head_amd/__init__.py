@@ -7,14 +7,14 @@ synthetic inputs.  Importing the package loads the library and fails if it is
 missing; there is no other execution path.
 """
 from . import _lib
-from ._lib import (DsparkError, acceptance_rate, async_schedule, confidence, confidence_logits,
-                   draft_markov, draft_rnn, get_status, clear_status, pack, pack_tiered,
+from ._lib import (DsparkError, acceptance_rate, acceptance_rate_features, async_schedule,
+                   confidence, confidence_logits, draft_markov, draft_rnn, get_status, clear_status, pack, pack_tiered,
                    prefix_schedule, rnn_workspace, rnn_workspace_bytes, sts_fit, sts_workspace,
                    verify, verify_cap_accept, verify_features, workspace, workspace_bytes)
 
 _lib.load()
 
-__all__ = ["DsparkError", "acceptance_rate", "async_schedule", "confidence", "confidence_logits",
-           "draft_markov", "draft_rnn", "get_status", "clear_status", "pack", "pack_tiered",
+__all__ = ["DsparkError", "acceptance_rate", "acceptance_rate_features", "async_schedule",
+           "confidence", "confidence_logits", "draft_markov", "draft_rnn", "get_status", "clear_status", "pack", "pack_tiered",
            "prefix_schedule", "rnn_workspace", "rnn_workspace_bytes", "sts_fit", "sts_workspace",
            "verify", "verify_cap_accept", "verify_features", "workspace", "workspace_bytes"]

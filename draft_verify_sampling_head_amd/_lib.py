@@ -27,7 +27,8 @@ EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
            "dspark_draft_markov_profiled", "dspark_async_schedule", "dspark_pack_tiered",
            "dspark_verify_cap_accept", "dspark_acceptance_rate", "dspark_sts_fit",
            "dspark_sts_workspace_bytes", "dspark_confidence_logits", "dspark_rnn_workspace_bytes",
-           "dspark_draft_rnn", "dspark_verify_features", "dspark_draft_rnn_profiled")
+           "dspark_draft_rnn", "dspark_verify_features", "dspark_draft_rnn_profiled",
+           "dspark_acceptance_rate_features")
 
 
 class DsparkError(RuntimeError):
@@ -80,6 +81,7 @@ def load():
                                    i32, P, P, P, P, P, P, P, P, sz, P]
     L.dspark_draft_rnn_profiled.argtypes = L.dspark_draft_rnn.argtypes + [P, P, P]
     L.dspark_verify_features.argtypes = L.dspark_verify.argtypes
+    L.dspark_acceptance_rate_features.argtypes = L.dspark_acceptance_rate.argtypes
     for fn in EXPORTS:
         getattr(L, fn).restype = getattr(L, fn).restype or i32
     L.dspark_workspace_bytes.restype = sz
@@ -325,6 +327,18 @@ def draft_rnn_profiled(U, W1, W2t, Wr, h, x0, T, seed, rnd, x, logp_d, lse_d, fe
                                             ev_end, C.byref(n_timed))
     _check("dspark_draft_rnn_profiled", code)
     return int(n_timed.value)
+
+
+def acceptance_rate_features(target, x, lse_d, U, feat, W2t, T, c_star, ws, stream=None):
+    """c* of RNN-head drafts: target dense [R][gamma+1][V]; feat [R][gamma][r]."""
+    R, g1, V = target.shape
+    r = int(feat.shape[-1])
+    code = load().dspark_acceptance_rate_features(R, g1 - 1, V, r, float(T), _ptr(target),
+                                                  _dt(target), _ptr(x), _ptr(lse_d), _ptr(U),
+                                                  _dt(U), _ptr(feat), _ptr(W2t), _dt(feat),
+                                                  _ptr(c_star), _ptr(ws), ws.numel(),
+                                                  _stream(stream))
+    _check("dspark_acceptance_rate_features", code)
 
 
 def verify_features(ell, cu, target, layout, x, logp_d, lse_d, U, feat, W2t, T, seed, rnd, m, tau,

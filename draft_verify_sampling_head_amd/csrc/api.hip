@@ -357,11 +357,12 @@ dspark_status dspark_sts_fit(int n, int gamma, const float* z, const int32_t* m,
   return hip_status(launch_sts_fit(a, stream));
 }
 
-dspark_status dspark_acceptance_rate(int R, int gamma, int V, int r, float T, const void* target,
-                                     dspark_dtype t_dt, const int32_t* x, const float* lse_d,
-                                     const void* U, dspark_dtype U_dt, const void* W1,
-                                     const void* W2t, dspark_dtype W_dt, float* c_star, void* ws,
-                                     size_t ws_bytes, hipStream_t stream) {
+static dspark_status acceptance_rate_impl(int R, int gamma, int V, int r, float T,
+                                          const void* target, dspark_dtype t_dt, const int32_t* x,
+                                          const float* lse_d, const void* U, dspark_dtype U_dt,
+                                          const void* W1, const void* W2t, dspark_dtype W_dt,
+                                          float* c_star, void* ws, size_t ws_bytes,
+                                          hipStream_t stream, const void* feat) {
   dspark_status s = shape_check(R, gamma, V);
   if (s != DSPARK_OK) return s;
   if ((s = rank_check(r)) != DSPARK_OK) return s;
@@ -377,7 +378,29 @@ dspark_status dspark_acceptance_rate(int R, int gamma, int V, int r, float T, co
   if (ws_bytes < ws_layout(R, gamma, V).total) return DSPARK_E_WORKSPACE;
   return hip_status(launch_acceptance_rate(R, gamma, V, r, T, target, x, lse_d, U,
                                            U_dt == DSPARK_BF16, W1, W2t, W_dt == DSPARK_BF16,
-                                           c_star, ws, stream));
+                                           c_star, ws, stream, feat));
+}
+
+dspark_status dspark_acceptance_rate(int R, int gamma, int V, int r, float T, const void* target,
+                                     dspark_dtype t_dt, const int32_t* x, const float* lse_d,
+                                     const void* U, dspark_dtype U_dt, const void* W1,
+                                     const void* W2t, dspark_dtype W_dt, float* c_star, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  return acceptance_rate_impl(R, gamma, V, r, T, target, t_dt, x, lse_d, U, U_dt, W1, W2t, W_dt,
+                              c_star, ws, ws_bytes, stream, nullptr);
+}
+
+dspark_status dspark_acceptance_rate_features(int R, int gamma, int V, int r, float T,
+                                              const void* target, dspark_dtype t_dt,
+                                              const int32_t* x, const float* lse_d, const void* U,
+                                              dspark_dtype U_dt, const void* feat,
+                                              const void* W2t, dspark_dtype W_dt, float* c_star,
+                                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (r == 0 && R > 0) return DSPARK_E_UNSUPPORTED;
+  if (R > 0 && !feat) return DSPARK_E_INVALID;
+  // the features take W1's place in the argument checks
+  return acceptance_rate_impl(R, gamma, V, r, T, target, t_dt, x, lse_d, U, U_dt, feat, W2t, W_dt,
+                              c_star, ws, ws_bytes, stream, feat);
 }
 
 dspark_status dspark_verify(int R, int gamma, int V, int r, float T, uint64_t seed, uint64_t round,

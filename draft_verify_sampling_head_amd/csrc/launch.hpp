@@ -155,7 +155,7 @@ bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void*
 hipError_t launch_acceptance_rate(int R, int gamma, int V, int rank, float T, const void* target,
                                   const int32_t* x, const float* lse_d, const void* U, bool u_bf16,
                                   const void* W1, const void* W2t, bool w_bf16, float* c_star,
-                                  void* ws, hipStream_t st);
+                                  void* ws, hipStream_t st, const void* feat = nullptr);
 hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,
                          const int32_t* ell, const int32_t* cu, const void* target, int layout,
                          const int32_t* x, const float* logp_d, const float* lse_d,

@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256) void k_cstar_greedy(int R, int gamma, int V, c
 hipError_t launch_acceptance_rate(int R, int gamma, int V, int rank, float T, const void* target,
                                   const int32_t* x, const float* lse_d, const void* U, bool u_bf16,
                                   const void* W1, const void* W2t, bool w_bf16, float* c_star,
-                                  void* ws, hipStream_t st) {
+                                  void* ws, hipStream_t st, const void* feat) {
   const WsLayout L = ws_layout(R, gamma, V);
   char* w = reinterpret_cast<char*>(ws);
   uint32_t* hdr = reinterpret_cast<uint32_t*>(w + L.header);
@@ -340,19 +340,23 @@ hipError_t launch_acceptance_rate(int R, int gamma, int V, int rank, float T, co
   int4* list = reinterpret_cast<int4*>(w + L.ver_i);
   float2* rl = reinterpret_cast<float2*>(w + L.ver_l);
   const int cap = (int)std::min<size_t>((size_t)items, (L.lse_t - L.ver_i) / sizeof(int4));
+  // rows of the bias features: W1[x_{k-1}] (Markov head) or the draft's own
+  // per-position features (RNN head)
+  const void* E = feat ? feat : W1;
   for (int q0 = 0; q0 < items; q0 += cap) {
     const int n = std::min(cap, items - q0);
     hipLaunchKernelGGL(k_cstar_list, dim3((n + 255) / 256), dim3(256), 0, st, gamma, q0, n, list,
                        count);
     if (u_bf16 && w_bf16 && rank > 0 && u_vec && t_vec &&
-        launch_resid_slices(n, gamma, V, rank, T, U, W1, W2t, target, x, count, list, a.lse_t,
-                            lse_d, rl, hdr, st, &e, true)) {
+        launch_resid_slices(n, gamma, V, rank, T, U, E, W2t, target, x, count, list, a.lse_t,
+                            lse_d, rl, hdr, st, &e, true, feat != nullptr)) {
       if (e != hipSuccess) return e;
     } else {
       MarkovArgs ma{};
       ma.R = R; ma.gamma = gamma; ma.k = 0; ma.V = V; ma.rank = rank; ma.nch = nch;
       ma.nrows_cap = n;
-      ma.U = U; ma.W1v = W1; ma.W2tv = W2t; ma.x0 = nullptr; ma.x = x; ma.scale2 = kLog2e / T;
+      ma.U = U; ma.W1v = E; ma.W2tv = W2t; ma.x0 = nullptr; ma.x = x; ma.feat_rows = feat != nullptr;
+      ma.scale2 = kLog2e / T;
       ma.u_vec_ok = u_vec && t_vec;
       ma.L = rl; ma.I = nullptr;
       ma.rej_count = count; ma.rej = list; ma.target = target; ma.lse_t = a.lse_t;

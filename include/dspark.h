@@ -412,6 +412,22 @@ dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, int d, float T,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * dspark_acceptance_rate for drafts whose bias is carried by per-position
+ * features (the RNN head): p_d^k = softmax((U_k + W2^T e_k) / T) with e_k from
+ * feat row i*gamma + k-1 ([P3] Method details, confidence head: c*_k is the
+ * single-step acceptance rate of the draft actually sampled).
+ *   feat   [R][gamma][r] (W_dt) the draft's features; W1 is not read
+ *   other arguments as for dspark_acceptance_rate (r >= 16)
+ */
+dspark_status dspark_acceptance_rate_features(int R, int gamma, int V, int r, float T,
+                                              const void* target, dspark_dtype t_dt,
+                                              const int32_t* x, const float* lse_d,
+                                              const void* U, dspark_dtype U_dt,
+                                              const void* feat, const void* W2t, dspark_dtype W_dt,
+                                              float* c_star, void* ws, size_t ws_bytes,
+                                              hipStream_t stream);
+
+/*
  * Instrumented dspark_draft_rnn for performance measurement: identical
  * results; additionally records ev_begin[k-1] / ev_end[k-1] on `stream`
  * around the per-chunk statistics kernel of step k (the draft's dominant

@@ -178,7 +178,8 @@ def test_synthetic_configs_shapes():
 @pytest.mark.parametrize("fn", ["draft_markov", "confidence", "prefix_schedule", "async_schedule",
                                 "pack", "pack_tiered", "verify", "verify_cap_accept",
                                 "acceptance_rate", "sts_fit", "confidence_logits", "draft_rnn",
-                                "verify_features", "rnn_workspace_bytes"])
+                                "verify_features", "rnn_workspace_bytes",
+                                "acceptance_rate_features"])
 def test_binding_names_match_abi(fn):
     assert callable(getattr(D, fn))
     assert f"dspark_{fn}" in declared()

@@ -780,3 +780,43 @@ def test_rnn_vector_alu_cell(monkeypatch, over):
     monkeypatch.setenv("DSPARK_RNN_CELL_VALU", "1")
     cfg = synth.scaled(synth.config(2), **over)
     run_and_check_rnn(cfg, synth.make_inputs(cfg, device="cpu"))
+
+
+def test_rnn_full_config3_sampled():
+    """R=1024 requests (four 256-row groups, four cell tiles per workgroup),
+    gamma=15, V=151936, T=0.7, tabulated SPS: sampled requests one by one."""
+    cfg = synth.config(3)
+    inp = synth.make_inputs(cfg, device=DEV)
+    run_and_check_rnn(cfg, None, inp_dev=inp, gain=1.0, reqs=[3, 700, 1023])
+
+
+@pytest.mark.parametrize("base,over", [(2, dict(R=40, gamma=5, V=3000, d=256)),
+                                       (2, dict(R=33, gamma=4, V=2000, d=64, rank=64)),
+                                       (0, {}),
+                                       (1, dict(R=20, gamma=5, V=3001, d=96, rank=32))],
+                         ids=["r256", "r64", "fp32", "greedy"])
+def test_rnn_acceptance_rate_parity(base, over):
+    """c* of RNN-head drafts (features in place of W1[x_{k-1}]) against the oracle."""
+    import oracle as O
+    cfg = synth.scaled(synth.config(base), **over) if over else synth.config(base)
+    inp = synth.make_inputs(cfg, device="cpu")
+    g = to_dev(inp)
+    Wr = synth.rnn_weights(cfg, device=DEV, gain=3.0)
+    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV, rnn=(cfg.rank, cfg.d, cfg.dtype))
+    D.draft_rnn(g["U"], g["W1"], g["W2t"], Wr, g["h"], g["x0"], cfg.T, cfg.philox_seed, 2, buf.x,
+                buf.logp_d, buf.lse_d, buf.feat, buf.ws, state=buf.state)
+    cs = torch.empty(cfg.R, cfg.gamma, dtype=torch.float32, device=DEV)
+    D.acceptance_rate_features(g["target"], buf.x, buf.lse_d, g["U"], buf.feat, g["W2t"], cfg.T,
+                               cs, buf.ws)
+    torch.cuda.synchronize()
+    assert D.get_status(buf.ws) == 0
+    ref, mg = O.acceptance_rate(f(inp["target"]), n(buf.x), f(inp["U"]), None, f(inp["W2t"]),
+                                cfg.T, feat=f(buf.feat))
+    got = n(cs).astype(np.float64)
+    if cfg.T > 0:
+        rel = np.abs(got - ref) / np.maximum(ref, 1e-30)
+        print(f"  c* max rel err {rel.max():.3g}", flush=True)
+        assert rel.max() <= 1e-5
+    else:
+        bad = (got != ref) & (mg >= 1e-5)
+        assert not bad.any() and (got != ref).sum() <= 0.001 * got.size + 1
