@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=2)
+    p.add_argument("--R", type=int, default=None, help="config 4 (rank and length sweep): requests")
+    p.add_argument("--gamma", type=int, default=None, help="config 4: block size")
+    p.add_argument("--rank", type=int, default=None, help="config 4: Markov rank")
     p.add_argument("--scheduler", choices=["greedy", "async", "static"], default=None,
                    help="Algorithm 1, the asynchronous production form (capacity planned two "
                         "rounds earlier, top-K admission), or the static block; default: the "
@@ -186,7 +189,10 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy: 3 x {nb} bytes")
         del src, dst
-    cfg = synth.config(args.config)
+    if args.config == 4:
+        cfg = synth.config(4, R=args.R, gamma=args.gamma, rank=args.rank)
+    else:
+        cfg = synth.config(args.config)
     t0 = time.time()
     inp = synth.make_inputs(cfg, device=dev)
     torch.cuda.synchronize()
@@ -294,7 +300,13 @@ def main():
             durs.append(ev.elapsed_ms(j + k, j + cfg.gamma + k))
     ev.close()
     avg_ms = float(np.mean(durs))
-    if nt == 1:
+    if cfg.rank == 0 and not rnn:
+        kernel = "k_row_stats"
+        kdesc = "k_row_stats (rank 0: statistics of all R*gamma rows of U, one launch)"
+        s = cfg.dtype.itemsize
+        kb = s * cfg.R * cfg.gamma * cfg.V + 8 * cfg.R * cfg.gamma * ((cfg.V + 127) // 128)
+        kflops = 0.0
+    elif nt == 1:
         kernel = "k_draft_persistent"
         kdesc = ("k_draft_persistent (RNN head: cell, statistics and pick of all gamma steps, one "
                  "cooperative launch)" if rnn else
@@ -302,9 +314,9 @@ def main():
         kb = draft_kernel_bytes(cfg)
         kflops = 2.0 * cfg.R * cfg.rank * cfg.V * cfg.gamma
     else:
-        kernel = "k_markov_mfma"
-        kdesc = ("k_markov_mfma (draft statistics of U_k + W2^T e_k, per step; RNN head)" if rnn
-                 else "k_markov_mfma (draft statistics, per step)")
+        kernel = "k_markov_mfma" if cfg.dtype == torch.bfloat16 else "k_markov_valu"
+        kdesc = (f"{kernel} (draft statistics of U_k + W2^T e_k, per step; RNN head)" if rnn
+                 else f"{kernel} (draft statistics, per step)")
         kb = stats_kernel_bytes(cfg)
         kflops = 2.0 * cfg.R * cfg.rank * cfg.V
     achieved = kb / (avg_ms * 1e-3) / 1e9
@@ -343,7 +355,7 @@ def main():
         "mean_ell": sum_ell / (K * cfg.R),
         "mean_tau": sum_tau / (K * cfg.R),
         "device_status": status,
-        "roofline": {"bound": "hbm", "kernel": kdesc,
+        "roofline": {"bound": "hbm", "kernel": kdesc,  # MFMA is the co-bound at rank > 0
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": counter_traffic((kernel, args.head), cfg, args.config),
@@ -401,6 +413,7 @@ def cpu_baseline(cfg, inp, buf, n_req, ell_per_round, torch, np, sched="greedy",
     verify for n_req requests, the scheduler and both packs on the full batch;
     the per-request part is scaled to all R requests."""
     import oracle as O
+    n_req = max(1, min(n_req, cfg.R))
     reqs = np.linspace(0, cfg.R - 1, n_req).round().astype(np.int32)
     sel = torch.as_tensor(reqs, device=inp["U"].device).long()
     f = lambda t: t.float().cpu().numpy()

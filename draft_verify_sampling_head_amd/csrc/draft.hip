@@ -41,6 +41,8 @@ struct DraftPickArgs {
   const void* W1;
   const void* W2t;
   const void* feat;         // nullable: per-position bias features [R][gamma][rank] (RNN head)
+  bool all_pos;             // rank 0: block b picks position b % gamma + 1 of request b / gamma,
+                            // statistics row b (all positions in one launch)
   const int32_t* x0;
   int32_t* x;
   float* logp_d;
@@ -51,21 +53,22 @@ struct DraftPickArgs {
   uint32_t* status;
 };
 
-// Pick of step a.k for request i by an NT-thread block (NT in {256, 512}).
+// Pick of position k for request i by an NT-thread block (NT in {256, 512});
+// lrow is the row of the chunk statistics.
 template <typename UT, typename WT, bool GREEDY, int NT>
-__device__ __forceinline__ void pick_row(const DraftPickArgs& a, int i, BlockScratch& sh) {
+__device__ __forceinline__ void pick_row(const DraftPickArgs& a, int i, int k, int64_t lrow,
+                                         BlockScratch& sh) {
   constexpr int TPE = NT / kChunk;          // threads per rebuilt entry
   const int tid = threadIdx.x;
-  const int k = a.k;
   const int64_t xo = (int64_t)i * (a.gamma + 1);
-  const int prev = (k == 1) ? a.x0[i] : a.x[xo + k - 1];
-  const float2* Lr = a.L + (int64_t)i * a.nch;
+  const int prev = a.rank == 0 ? 0 : (k == 1) ? a.x0[i] : a.x[xo + k - 1];
+  const float2* Lr = a.L + lrow * a.nch;
   int xk;
   float logp, lse, gap = INFINITY;
   if (GREEDY) {
     float v = -INFINITY;
     int idx = 0x7FFFFFFF;
-    const int* Ir = a.I + (int64_t)i * a.nch;
+    const int* Ir = a.I + lrow * a.nch;
     for (int c = tid; c < a.nch; c += NT) argmax_merge(v, idx, Lr[c].x, Ir[c]);
     block_argmax<NT>(v, idx, sh);
     xk = idx;
@@ -123,11 +126,15 @@ __device__ __forceinline__ void pick_row(const DraftPickArgs& a, int i, BlockScr
   __syncthreads();                          // sh is reused by the next call
 }
 
-// One 256-thread block per request.
+// One 256-thread block per request (step a.k), or per (request, position)
+// when all positions are independent (rank 0, all_pos).
 template <typename UT, typename WT, bool GREEDY>
 __global__ __launch_bounds__(256) void k_draft_pick(DraftPickArgs a) {
   __shared__ BlockScratch sh;
-  pick_row<UT, WT, GREEDY, 256>(a, blockIdx.x, sh);
+  if (a.all_pos)
+    pick_row<UT, WT, GREEDY, 256>(a, blockIdx.x / a.gamma, blockIdx.x % a.gamma + 1, blockIdx.x, sh);
+  else
+    pick_row<UT, WT, GREEDY, 256>(a, blockIdx.x, a.k, blockIdx.x, sh);
 }
 
 // ============================================================= persistent
@@ -1481,6 +1488,33 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     return hipSuccess;
   }
 
+#define DSPARK_PICK(UT_, WT_, G_, NB_) \
+    hipLaunchKernelGGL((k_draft_pick<UT_, WT_, G_>), dim3(NB_), dim3(256), 0, st, p)
+#define DSPARK_PICK_ALL(NB_)                                                                          \
+    if (u_bf16 && w_bf16) { if (greedy) DSPARK_PICK(uint16_t, uint16_t, true, NB_); else DSPARK_PICK(uint16_t, uint16_t, false, NB_); } \
+    else if (u_bf16)      { if (greedy) DSPARK_PICK(uint16_t, float, true, NB_);    else DSPARK_PICK(uint16_t, float, false, NB_); }    \
+    else if (w_bf16)      { if (greedy) DSPARK_PICK(float, uint16_t, true, NB_);    else DSPARK_PICK(float, uint16_t, false, NB_); }    \
+    else                  { if (greedy) DSPARK_PICK(float, float, true, NB_);       else DSPARK_PICK(float, float, false, NB_); }
+  if (rank == 0 && !rnn) {
+    // rank 0 (no transition bias): the positions are independent, so the
+    // statistics of all R gamma rows of U are one launch (into the target-row
+    // statistics region, unused until the verify) and the picks another
+    RowStatsArgs a{};
+    a.base = U; a.kind = kRowsAll; a.R = R; a.gamma = gamma; a.k = 0; a.V = V; a.nch = nch;
+    a.nrows_cap = R * gamma; a.scale2 = scale2; a.vec_ok = u_vec;
+    a.L = reinterpret_cast<float2*>(w + L.ver_l); a.I = reinterpret_cast<int*>(w + L.ver_i);
+    a.status = status;
+    hipError_t e;
+    if (ev_begin && (e = hipEventRecord(ev_begin[0], st)) != hipSuccess) return e;
+    if ((e = launch_row_stats(a, u_bf16, greedy, st)) != hipSuccess) return e;
+    if (ev_end && (e = hipEventRecord(ev_end[0], st)) != hipSuccess) return e;
+    p.all_pos = true;
+    p.L = a.L;
+    p.I = a.I;
+    DSPARK_PICK_ALL(R * gamma)
+    if (n_timed) *n_timed = 1;
+    return hipGetLastError();
+  }
   if (rnn) {
     const hipError_t e = launch_rnn_hproj(*rnn, st);
     if (e != hipSuccess) return e;
@@ -1506,16 +1540,12 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     if (e != hipSuccess) return e;
     if (ev_end && (e = hipEventRecord(ev_end[k - 1], st)) != hipSuccess) return e;
     p.k = k;
-#define DSPARK_PICK(UT_, WT_, G_) \
-    hipLaunchKernelGGL((k_draft_pick<UT_, WT_, G_>), dim3(R), dim3(256), 0, st, p)
-    if (u_bf16 && w_bf16) { if (greedy) DSPARK_PICK(uint16_t, uint16_t, true); else DSPARK_PICK(uint16_t, uint16_t, false); }
-    else if (u_bf16)      { if (greedy) DSPARK_PICK(uint16_t, float, true);    else DSPARK_PICK(uint16_t, float, false); }
-    else if (w_bf16)      { if (greedy) DSPARK_PICK(float, uint16_t, true);    else DSPARK_PICK(float, uint16_t, false); }
-    else                  { if (greedy) DSPARK_PICK(float, float, true);       else DSPARK_PICK(float, float, false); }
-#undef DSPARK_PICK
+    DSPARK_PICK_ALL(R)
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+#undef DSPARK_PICK_ALL
+#undef DSPARK_PICK
   if (n_timed) *n_timed = gamma;
   return hipSuccess;
 }

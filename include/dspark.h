@@ -108,7 +108,8 @@ dspark_status dspark_get_status(const void* ws, size_t ws_bytes, uint32_t* flags
  * 512 vocabulary entries per compute unit, all gamma steps run as one
  * cooperative launch that keeps W2 on chip (grid barriers between steps;
  * DSPARK_FLAG_BARRIER reports a barrier that gave up waiting); other shapes
- * run two launches per step.  Both schedules give the same results.  The
+ * run two launches per step, and r == 0 (independent positions) two launches
+ * in all.  The schedules give the same results.  The
  * environment variable DSPARK_DRAFT_KERNEL=steps forces the per-step
  * schedule.
  */
@@ -125,7 +126,10 @@ dspark_status dspark_draft_markov(int R, int gamma, int V, int r, float T,
  * dominant kernel.  With the persistent schedule (one cooperative launch for
  * all gamma steps) that is ev_begin[0] / ev_end[0] around the launch and
  * *n_timed = 1; with the per-step schedule ev_begin[k-1] / ev_end[k-1] bracket
- * the per-chunk statistics kernel of step k and *n_timed = gamma.
+ * the per-chunk statistics kernel of step k and *n_timed = gamma; at r == 0
+ * (independent positions: one statistics launch over all R gamma rows, then
+ * one pick launch) ev_begin[0] / ev_end[0] bracket the statistics launch and
+ * *n_timed = 1.
  *   ev_begin, ev_end  (host) arrays of gamma events created by the caller
  *   n_timed           (host, nullable) number of event pairs recorded
  * Returns DSPARK_E_INVALID if either array is null.
