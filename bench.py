@@ -450,8 +450,17 @@ def cpu_baseline(cfg, inp, buf, n_req, ell_per_round, torch, np, sched="greedy",
     t_round = per_req * cfg.R + (t2 - t1) + (t4 - t3)
     log(f"[bench] oracle: {per_req:.2f} s/request (draft+conf+verify), schedule+pack "
         f"{(t2 - t1) + (t4 - t3):.3f} s, est. round {t_round:.1f} s")
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": ell_per_round / t_round, "unit": "verified draft tokens/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu": model, "host_nproc": os.cpu_count(),
             "sample": f"{n_req} of {cfg.R} requests (draft+confidence+verify, {t3 - t0:.1f} s of "
                       f"CPU) scaled to {cfg.R}; scheduler and packs on the full batch; tokens per "
                       f"round = the GPU rounds' mean sum of ell ({ell_per_round:.1f})",
