@@ -172,7 +172,8 @@ __global__ __launch_bounds__(256) void k_row_stats(RowStatsArgs a) {
     for (int t = threadIdx.x; t <= a.R; t += 256) cus[t] = a.cu[t];
     __syncthreads();
   }
-  const int* cu = lds_cu ? cus : a.cu;
+  // (the two offset arrays are read on separate paths: a pointer that may
+  // point at either LDS or global memory would turn every read into a flat load)
   const int64_t items = (int64_t)nrows * a.segs;
   for (int64_t it = wave; it < items; it += nwaves) {
     const int q = (int)(it / a.segs);
@@ -183,12 +184,21 @@ __global__ __launch_bounds__(256) void k_row_stats(RowStatsArgs a) {
     } else if (a.kind == kRowsVerifyPacked || a.kind == kRowsAll) {
       row = q;
     } else {
-      int lo = 0, hi = a.R - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu[mid] <= q) lo = mid; else hi = mid - 1;
+      int lo = 0, hi = a.R - 1, base;
+      if (lds_cu) {
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (cus[mid] <= q) lo = mid; else hi = mid - 1;
+        }
+        base = cus[lo];
+      } else {
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (a.cu[mid] <= q) lo = mid; else hi = mid - 1;
+        }
+        base = a.cu[lo];
       }
-      row = (int64_t)lo * (a.gamma + 1) + (q - cu[lo]);
+      row = (int64_t)lo * (a.gamma + 1) + (q - base);
     }
     const T* rp = reinterpret_cast<const T*>(a.base) + row * a.V;
     const int c0 = seg * a.cps, c1 = min(a.nch, c0 + a.cps);
