@@ -719,8 +719,11 @@ RNN_SMALL = [
     (3, dict(R=70, gamma=6, V=2504, d=64)),                              # T = 0.7
     (2, dict(R=300, gamma=3, V=2048, d=32)),                             # more cell tiles than CUs
     (2, dict(R=17, gamma=16, V=1536, d=64, rank=64)),
+    (2, dict(R=8, gamma=32, V=1024, d=64, rank=64)),                     # longest block, fused
+    (2, dict(R=12, gamma=32, V=900, d=32, rank=32)),                     # longest block, per step
+    (2, dict(R=24, gamma=4, V=1800, d=64, T=0.3)),                       # low temperature, fused
 ]
-RNN_FUSED = [RNN_SMALL[i] for i in (1, 2, 8, 10, 11, 12, 13)]
+RNN_FUSED = [RNN_SMALL[i] for i in (1, 2, 8, 10, 11, 12, 13, 14, 16)]
 
 
 @pytest.mark.parametrize("base,over", RNN_SMALL, ids=[f"rnn{i}" for i in range(len(RNN_SMALL))])
