@@ -402,9 +402,14 @@ size_t dspark_rnn_workspace_bytes(int R, int gamma, int V, int r, int d);
  *   ws     at least dspark_rnn_workspace_bytes(R, gamma, V, r, d) bytes
  * r must be a multiple of 16 in [16, 512].  The h part of the projection is one
  * contraction over all positions before the chain (MFMA when h and Wr are
- * bf16 with d a multiple of 8 and 16-byte aligned tables); each step then
- * runs the cell (fp32, vector ALU), the per-chunk statistics of U_k + bias_k
- * (MFMA for bf16 weights) and the pick, three launches per step.
+ * bf16 with d a multiple of 8 and 16-byte aligned tables).  With bf16 U,
+ * weights and h, r in {64, 128, 256}, 2r + d a multiple of 8 and the shape
+ * limits of dspark_draft_markov's persistent launch, all gamma steps (cell,
+ * statistics, pick) run in one cooperative launch with two grid barriers per
+ * step (DSPARK_FLAG_BARRIER as there).  Other shapes run three launches per
+ * step: the cell (MFMA with the fp32 state split into exact bf16 parts for
+ * bf16 weights, fp32 vector ALU otherwise), the per-chunk statistics and the
+ * pick.  The schedules give the same results.
  */
 dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, int d, float T,
                                uint64_t seed, uint64_t round,
