@@ -633,15 +633,15 @@ def _full(idx, reqs, **cell):
 
 
 def test_full_config2_sampled():
-    _full(2, [0, 131, 255])
+    _full(2, [0, 31, 64, 97, 131, 170, 222, 255])
 
 
 def test_full_config1_sampled():
-    _full(1, [0, 17, 63])
+    _full(1, [0, 9, 17, 26, 38, 45, 51, 63])
 
 
 def test_full_config3_sampled():
-    _full(3, [5, 600, 1023])
+    _full(3, [5, 200, 399, 600, 811, 1023])
 
 
 @pytest.mark.parametrize("R,gamma,rank", [(1, 16, 256), (32, 4, 64), (512, 8, 0)])
@@ -771,7 +771,7 @@ def test_rnn_feature_residuals_exercised():
 def test_rnn_full_config2_sampled():
     cfg = synth.config(2)
     inp = synth.make_inputs(cfg, device=DEV)
-    run_and_check_rnn(cfg, None, inp_dev=inp, gain=1.0, reqs=[0, 255])
+    run_and_check_rnn(cfg, None, inp_dev=inp, gain=1.0, reqs=[0, 77, 160, 255])
 
 
 @pytest.mark.parametrize("over", [dict(R=40, gamma=5, V=3000, d=256),
