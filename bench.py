@@ -326,6 +326,8 @@ def main():
         f"({achieved:.0f} GB/s, {mfma_tf:.0f} TFLOP/s), round HBM frac {hbm_frac_round:.3f}, "
         f"status={status}")
 
+    copy_gbs = copy_bandwidth(torch, dev)
+    log(f"[bench] device copy bandwidth {copy_gbs:.0f} GB/s (read + write, 1 GiB, median of 5)")
     diag = diagnostics(cfg, inp, buf, torch, np, D) if args.diagnostics else None
 
     cpu = None
@@ -360,12 +362,34 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": counter_traffic((kernel, args.head), cfg, args.config),
                      "avg_launch_us": avg_ms * 1e3, "bytes_per_launch": kb,
-                     "mfma_tflops": mfma_tf, "mfma_frac": mfma_tf / MFMA_BF16_PEAK_TFLOPS},
+                     "mfma_tflops": mfma_tf, "mfma_frac": mfma_tf / MFMA_BF16_PEAK_TFLOPS,
+                     "copy_gbps_measured": copy_gbs, "frac_of_copy": achieved / copy_gbs},
+        "hbm_frac_round_of_copy": bytes_round / (t_total / K) / (copy_gbs * 1e9),
         "cpu_baseline": cpu,
     }
     if diag is not None:
         out["diagnostics"] = diag
     print(json.dumps(out), flush=True)
+
+
+def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=5):
+    """HBM bandwidth a plain device-to-device copy reaches on this GPU (bytes
+    read + written per second, median of `reps` copies), measured after the
+    timed rounds."""
+    import statistics
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        dst.copy_(src)
+        e.record()
+        e.synchronize()
+        times.append(s.elapsed_time(e) * 1e-3)
+    del src, dst
+    return 2 * nbytes / statistics.median(times) / 1e9
 
 
 def diagnostics(cfg, inp, buf, torch, np, D):
