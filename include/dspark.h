@@ -409,7 +409,9 @@ size_t dspark_rnn_workspace_bytes(int R, int gamma, int V, int r, int d);
  * step (DSPARK_FLAG_BARRIER as there).  Other shapes run three launches per
  * step: the cell (MFMA with the fp32 state split into exact bf16 parts for
  * bf16 weights, fp32 vector ALU otherwise), the per-chunk statistics and the
- * pick.  The schedules give the same results.
+ * pick.  The schedules give the same results.  DSPARK_DRAFT_KERNEL=steps
+ * forces the per-step schedule, DSPARK_RNN_CELL_VALU (any value) the per-step
+ * schedule with the vector-ALU cell.
  */
 dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, int d, float T,
                                uint64_t seed, uint64_t round,
