@@ -25,6 +25,9 @@
 //                      completes locally.
 //   k_rnn_cell       : the same cell in fp32 on the vector ALU (float32
 //                      weights, rows that are not 16-byte aligned).
+// The cell kernels serve the per-step schedule.  When the shape fits the
+// persistent draft launch (draft.hip), that launch runs the same cell, tile by
+// tile, as a phase of every step, and only k_rnn_hproj_mfma runs before it.
 #include <algorithm>
 #include <cstdlib>
 #include <type_traits>
