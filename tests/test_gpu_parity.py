@@ -823,3 +823,48 @@ def test_rnn_acceptance_rate_parity(base, over):
     else:
         bad = (got != ref) & (mg >= 1e-5)
         assert not bad.any() and (got != ref).sum() <= 0.001 * got.size + 1
+
+
+def test_rnn_round_driver_async_tiers():
+    """The RNN head through the round driver with the asynchronous scheduler
+    (two-slot capacity ring) and a tier-padded verify batch, over several
+    rounds on the same buffers; draft, schedule, packs and verify against the
+    oracle."""
+    import oracle as O
+    cfg = synth.scaled(synth.config(2), R=48, gamma=5, V=2600, d=64)
+    inp = synth.make_inputs(cfg, device="cpu")
+    g = to_dev(inp)
+    g["Wr"] = synth.rnn_weights(cfg, device=DEV, gain=3.0)
+    tiers = [64, 128, 192, 256, 320]
+    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV, slots=320,
+                          rnn=(cfg.rank, cfg.d, cfg.dtype))
+    nmax = g["sps"].numel() - 1
+    ring = RD.CapacityRing(cfg.R, cfg.gamma, nmax, device=DEV)
+    hist = [min(cfg.R * (cfg.gamma + 1), nmax)] * 2
+    U, W1, W2t, h = f(inp["U"]), f(inp["W1"]), f(inp["W2t"]), f(inp["h"])
+    for rnd in range(3):
+        print(f"[case] rnn driver round {rnd}", flush=True)
+        D.clear_status(buf.ws)
+        RD.run_round(g, buf, cfg.T, cfg.philox_seed, rnd, scheduler="async", ring=ring,
+                     tiers=tiers, pad_token=7, head="rnn")
+        torch.cuda.synchronize()
+        assert D.get_status(buf.ws) == 0
+        rep = PC.Report()
+        feat = f(buf.feat)
+        PC.check_draft_rnn(rep, U, W1, W2t, f(g["Wr"]), h, n(inp["x0"]), cfg.T, cfg.philox_seed,
+                           rnd, n(buf.x), n(buf.logp_d), n(buf.lse_d), feat, n(buf.state), None,
+                           True)
+        e, _, Ne, _, Kp, _ = O.async_schedule(n(buf.c), n(g["sps"]), hist[rnd])
+        hist.append(Kp)
+        np.testing.assert_array_equal(n(buf.ell), e)
+        pk = O.pack_tiered(n(buf.x), e + 1, tiers, 7, slots=320)
+        np.testing.assert_array_equal(n(buf.flat), pk[1])
+        assert int(n(buf.N)[0]) == pk[4] and int(n(buf.N_pad)[0]) == pk[5]
+        PC.check_verify(rep, e, None, f(inp["target"]), 1, n(buf.x), n(buf.logp_d),
+                        n(buf.lse_d), U, W1, W2t, cfg.T, cfg.philox_seed, rnd, n(buf.m),
+                        n(buf.tau), n(buf.emitted), n(buf.next_anchor), n(buf.logp_t), None,
+                        feat=feat)
+        PC.check_pack(rep, n(buf.emitted), n(buf.tau), n(buf.cu_out), n(buf.flat_out), None, None,
+                      n(buf.N_out)[0], "emitted")
+        print(f"  {rep.summary()}", flush=True)
+        assert rep.ok(), rep.summary()
