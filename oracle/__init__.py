@@ -312,17 +312,18 @@ def pack_tiered(rows, lens, tiers, pad_token, slots=None):
 
 
 def verify_cap_accept(ell, cap, cu, target, layout, x, logp_d, lse_d, U, W1, W2t, T, seed=0,
-                      rnd=0, req_ids=None):
+                      rnd=0, req_ids=None, feat=None):
     """Cap-accept verification (bevisy.github.io DeepSpec analysis, section
     5.4, DSpark in SGLang, the verify modes: verify the whole window, commit
     only the scheduler's truncated window).  Request i is verified over its window ell[i] exactly
     as in `verify`; of the token sequence that produces (m accepted drafts,
     then the correction or bonus), the first min(m, c) + 1 tokens are
     committed, c = cap[i] clamped to [0, ell[i]].  When m > c the committed
-    token at position c + 1 is the accepted draft x_{c+1} itself.
+    token at position c + 1 is the accepted draft x_{c+1} itself.  feat: the
+    RNN head's per-position bias features, as for `verify`.
     Returns (m, tau, emitted, next_anchor, logp_t, margin, m_full)."""
     m_full, _, em_full, _, lpt, mg = verify(ell, cu, target, layout, x, logp_d, lse_d, U, W1, W2t,
-                                            T, seed, rnd, req_ids=req_ids)
+                                            T, seed, rnd, req_ids=req_ids, feat=feat)
     ell = _i32(ell)
     c = np.clip(_i32(cap), 0, ell)
     m = np.minimum(m_full, c).astype(np.int32)

@@ -190,13 +190,13 @@ def check_verify(rep, ell, cu, target, layout, x, dev_lp, dev_lse, U, W1, W2t, T
 
 
 def check_verify_cap_accept(rep, ell, cap, cu, target, layout, x, dev_lp, dev_lse, U, W1, W2t, T,
-                            seed, rnd, dev_m, dev_tau, dev_em, dev_na, dev_mfull, reqs):
+                            seed, rnd, dev_m, dev_tau, dev_em, dev_na, dev_mfull, reqs, feat=None):
     """Cap-accept verify: the committed result and the whole-window accepted
     count, bit-exact except requests whose oracle margin is below MARGIN."""
     m, tau, em, na, lpt, mg, mfull = O.verify_cap_accept(ell, cap, cu, target, layout, x,
                                                          dev_lp.astype(np.float64),
                                                          dev_lse.astype(np.float64), U, W1, W2t,
-                                                         T, seed, rnd, req_ids=reqs)
+                                                         T, seed, rnd, req_ids=reqs, feat=feat)
     R = ell.size
     rep.compared += R
     for r in range(R):

@@ -988,3 +988,35 @@ def test_rnn_bf16_features_and_memory():
     f1[:, 3:] = -1
     _, _, _, _, _, e2, _, _ = O.draft_rnn(U, W1, W2t, Wr, h, x0, 1.0, seed=6, force_x=f1)
     assert (np.abs(e2[:, 2] - e[:, 2]).max(axis=1) > 0).all()
+
+
+def test_cap_accept_with_rnn_features_is_a_prefix_of_the_feature_verify():
+    """Cap-accept of RNN drafts: the committed tokens are the first
+    min(m, C) + 1 of the feature verify's sequence, and differ from a
+    feature-less verify's where a residual was drawn."""
+    R, g, V, rank, d = 40, 4, 300, 16, 6
+    rng = np.random.default_rng(44)
+    U = rng.normal(0, 2, (R, g, V)).astype(np.float32)
+    W1 = rng.normal(0, 0.5, (V, rank)).astype(np.float32)
+    W2t = rng.normal(0, 0.5, (V, rank)).astype(np.float32)
+    Wr = rng.normal(0, 0.4, (3 * rank, 2 * rank + d)).astype(np.float32)
+    h = rng.normal(0, 1, (R, g, d)).astype(np.float32)
+    x0 = rng.integers(0, V, R)
+    x, lp, lse, _, _, e, _, _ = O.draft_rnn(U, W1, W2t, Wr, h, x0, 1.0, seed=8)
+    tgt = (np.concatenate([U, U[:, :1]], 1) + rng.normal(0, 1, (R, g + 1, V))).astype(np.float32)
+    ell = np.full(R, g, np.int32)
+    cap = rng.integers(0, g + 1, R).astype(np.int32)
+    m, tau, em, na, _, _ = O.verify(ell, None, tgt, 1, x, lp, lse, U, W1, W2t, 1.0, seed=8, feat=e)
+    mc, tc, ec, nc, _, _, mf = O.verify_cap_accept(ell, cap, None, tgt, 1, x, lp, lse, U, W1, W2t,
+                                                   1.0, seed=8, feat=e)
+    np.testing.assert_array_equal(mf, m)
+    np.testing.assert_array_equal(mc, np.minimum(m, cap))
+    for i in range(R):
+        np.testing.assert_array_equal(ec[i, :tc[i]], em[i, :tc[i]] if tc[i] <= tau[i]
+                                      else x[i, 1:tc[i] + 1])
+        if mc[i] < cap[i]:                    # not cut by the window: plain verification
+            assert tc[i] == tau[i] and nc[i] == na[i]
+        else:                                  # cut: the last committed token is the draft x_{C+1}
+            assert nc[i] == x[i, mc[i] + 1] if mc[i] < m[i] else nc[i] == na[i]
+    _, _, e2, *_ = O.verify_cap_accept(ell, cap, None, tgt, 1, x, lp, lse, U, W1, W2t, 1.0, seed=8)
+    assert (e2 != ec).any()
