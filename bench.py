@@ -200,9 +200,6 @@ def main():
     K, W = args.steps, args.warmup
     rnn = args.head == "rnn"
     if rnn:
-        if args.verify_mode != "compact":
-            print("bench.py: the RNN head is verified in compact mode", file=sys.stderr)
-            sys.exit(2)
         inp["Wr"] = synth.rnn_weights(cfg, device=dev)
         buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=dev, rnn=(cfg.rank, cfg.d, cfg.dtype))
     else:
@@ -252,7 +249,13 @@ def main():
         win = buf.full if vmode == "cap-accept" else buf.ell
         L.pack(buf.x, win, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N,
                ws=buf.ws)
-        if vmode == "cap-accept":
+        if vmode == "cap-accept" and rnn:
+            L.verify_cap_accept_features(buf.full, buf.ell, buf.cu, inp["target"], 1, buf.x,
+                                         buf.logp_d, buf.lse_d, inp["U"], buf.feat, inp["W2t"],
+                                         cfg.T, cfg.philox_seed, i, buf.m, buf.tau, buf.emitted,
+                                         buf.next_anchor, buf.ws, m_full=buf.m_full,
+                                         logp_t=buf.logp_t)
+        elif vmode == "cap-accept":
             L.verify_cap_accept(buf.full, buf.ell, buf.cu, inp["target"], 1, buf.x, buf.logp_d,
                                 buf.lse_d, inp["U"], inp["W1"], inp["W2t"], cfg.T, cfg.philox_seed,
                                 i, buf.m, buf.tau, buf.emitted, buf.next_anchor, buf.ws,

@@ -28,7 +28,7 @@ EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
            "dspark_verify_cap_accept", "dspark_acceptance_rate", "dspark_sts_fit",
            "dspark_sts_workspace_bytes", "dspark_confidence_logits", "dspark_rnn_workspace_bytes",
            "dspark_draft_rnn", "dspark_verify_features", "dspark_draft_rnn_profiled",
-           "dspark_acceptance_rate_features")
+           "dspark_acceptance_rate_features", "dspark_verify_cap_accept_features")
 
 
 class DsparkError(RuntimeError):
@@ -82,6 +82,7 @@ def load():
     L.dspark_draft_rnn_profiled.argtypes = L.dspark_draft_rnn.argtypes + [P, P, P]
     L.dspark_verify_features.argtypes = L.dspark_verify.argtypes
     L.dspark_acceptance_rate_features.argtypes = L.dspark_acceptance_rate.argtypes
+    L.dspark_verify_cap_accept_features.argtypes = L.dspark_verify_cap_accept.argtypes
     for fn in EXPORTS:
         getattr(L, fn).restype = getattr(L, fn).restype or i32
     L.dspark_workspace_bytes.restype = sz
@@ -339,6 +340,22 @@ def acceptance_rate_features(target, x, lse_d, U, feat, W2t, T, c_star, ws, stre
                                                   _ptr(c_star), _ptr(ws), ws.numel(),
                                                   _stream(stream))
     _check("dspark_acceptance_rate_features", code)
+
+
+def verify_cap_accept_features(ell, cap, cu, target, layout, x, logp_d, lse_d, U, feat, W2t, T,
+                               seed, rnd, m, tau, emitted, next_anchor, ws, m_full=None,
+                               logp_t=None, stream=None):
+    """dspark_verify_cap_accept with the draft's per-position features."""
+    R = ell.shape[0]
+    gamma = x.shape[1] - 1
+    V = target.shape[-1]
+    r = int(feat.shape[-1])
+    code = load().dspark_verify_cap_accept_features(
+        R, gamma, V, r, float(T), seed, rnd, _ptr(ell), _ptr(cap), _ptr(cu), _ptr(target),
+        _dt(target), int(layout), _ptr(x), _ptr(logp_d), _ptr(lse_d), _ptr(U), _dt(U), _ptr(feat),
+        _ptr(W2t), _dt(feat), _ptr(m), _ptr(tau), _ptr(emitted), _ptr(next_anchor), _ptr(m_full),
+        _ptr(logp_t), _ptr(ws), ws.numel(), _stream(stream))
+    _check("dspark_verify_cap_accept_features", code)
 
 
 def verify_features(ell, cu, target, layout, x, logp_d, lse_d, U, feat, W2t, T, seed, rnd, m, tau,

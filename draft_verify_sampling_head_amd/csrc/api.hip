@@ -431,6 +431,27 @@ dspark_status dspark_verify_features(int R, int gamma, int V, int r, float T, ui
                      logp_t, ws, ws_bytes, stream, nullptr, nullptr, feat);
 }
 
+dspark_status dspark_verify_cap_accept_features(int R, int gamma, int V, int r, float T,
+                                                uint64_t seed, uint64_t round, const int32_t* ell,
+                                                const int32_t* cap, const int32_t* cu,
+                                                const void* target, dspark_dtype t_dt,
+                                                int target_layout, const int32_t* x,
+                                                const float* logp_d, const float* lse_d,
+                                                const void* U, dspark_dtype U_dt, const void* feat,
+                                                const void* W2t, dspark_dtype W_dt, int32_t* m,
+                                                int32_t* tau, int32_t* emitted,
+                                                int32_t* next_anchor, int32_t* m_full,
+                                                float* logp_t, void* ws, size_t ws_bytes,
+                                                hipStream_t stream) {
+  if (R > 0 && !cap) return DSPARK_E_INVALID;
+  if (r == 0 && R > 0) return DSPARK_E_UNSUPPORTED;
+  if (R > 0 && !feat) return DSPARK_E_INVALID;
+  // the features take W1's place in the argument checks
+  return verify_impl(R, gamma, V, r, T, seed, round, ell, cu, target, t_dt, target_layout, x,
+                     logp_d, lse_d, U, U_dt, feat, W2t, W_dt, m, tau, emitted, next_anchor,
+                     logp_t, ws, ws_bytes, stream, cap, m_full, feat);
+}
+
 dspark_status dspark_verify_cap_accept(int R, int gamma, int V, int r, float T, uint64_t seed,
                                        uint64_t round, const int32_t* ell, const int32_t* cap,
                                        const int32_t* cu, const void* target, dspark_dtype t_dt,

@@ -93,8 +93,6 @@ def run_round(inp, buf: RoundBuffers, T, seed, rnd, scheduler=True, layout=1, st
     verifies with its features."""
     rnn = head == "rnn"
     if rnn:
-        if verify_mode != "compact":
-            raise ValueError("the RNN head is verified in compact mode")
         L.draft_rnn(inp["U"], inp["W1"], inp["W2t"], inp["Wr"], inp["h"], inp["x0"], T, seed, rnd,
                     buf.x, buf.logp_d, buf.lse_d, buf.feat, buf.ws, state=buf.state,
                     stream=stream)
@@ -116,7 +114,12 @@ def run_round(inp, buf: RoundBuffers, T, seed, rnd, scheduler=True, layout=1, st
     else:
         L.pack(buf.x, win, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N, ws=buf.ws,
                stream=stream)
-    if verify_mode == "cap-accept":
+    if verify_mode == "cap-accept" and rnn:
+        L.verify_cap_accept_features(buf.full, buf.ell, buf.cu, inp["target"], layout, buf.x,
+                                     buf.logp_d, buf.lse_d, inp["U"], buf.feat, inp["W2t"], T, seed,
+                                     rnd, buf.m, buf.tau, buf.emitted, buf.next_anchor, buf.ws,
+                                     m_full=buf.m_full, logp_t=buf.logp_t, stream=stream)
+    elif verify_mode == "cap-accept":
         L.verify_cap_accept(buf.full, buf.ell, buf.cu, inp["target"], layout, buf.x, buf.logp_d,
                             buf.lse_d, inp["U"], inp["W1"], inp["W2t"], T, seed, rnd, buf.m,
                             buf.tau, buf.emitted, buf.next_anchor, buf.ws, m_full=buf.m_full,

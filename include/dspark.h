@@ -439,6 +439,26 @@ dspark_status dspark_acceptance_rate_features(int R, int gamma, int V, int r, fl
                                               hipStream_t stream);
 
 /*
+ * dspark_verify_cap_accept for drafts whose bias is carried by per-position
+ * features (the RNN head): the whole-window verification rebuilds p_d of a
+ * rejected position from feat row i*gamma + k-1, as dspark_verify_features.
+ *   feat   [R][gamma][r] (W_dt) the draft's features; W1 is not read
+ *   other arguments as for dspark_verify_cap_accept (r >= 16)
+ */
+dspark_status dspark_verify_cap_accept_features(int R, int gamma, int V, int r, float T,
+                                                uint64_t seed, uint64_t round, const int32_t* ell,
+                                                const int32_t* cap, const int32_t* cu,
+                                                const void* target, dspark_dtype t_dt,
+                                                int target_layout, const int32_t* x,
+                                                const float* logp_d, const float* lse_d,
+                                                const void* U, dspark_dtype U_dt, const void* feat,
+                                                const void* W2t, dspark_dtype W_dt, int32_t* m,
+                                                int32_t* tau, int32_t* emitted,
+                                                int32_t* next_anchor, int32_t* m_full,
+                                                float* logp_t, void* ws, size_t ws_bytes,
+                                                hipStream_t stream);
+
+/*
  * Instrumented dspark_draft_rnn for performance measurement: identical
  * results; additionally records ev_begin[k-1] / ev_end[k-1] on `stream`
  * around the per-chunk statistics kernel of step k (the draft's dominant

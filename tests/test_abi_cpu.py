@@ -179,7 +179,7 @@ def test_synthetic_configs_shapes():
                                 "pack", "pack_tiered", "verify", "verify_cap_accept",
                                 "acceptance_rate", "sts_fit", "confidence_logits", "draft_rnn",
                                 "verify_features", "rnn_workspace_bytes",
-                                "acceptance_rate_features"])
+                                "acceptance_rate_features", "verify_cap_accept_features"])
 def test_binding_names_match_abi(fn):
     assert callable(getattr(D, fn))
     assert f"dspark_{fn}" in declared()

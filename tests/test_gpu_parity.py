@@ -868,3 +868,33 @@ def test_rnn_round_driver_async_tiers():
                       n(buf.N_out)[0], "emitted")
         print(f"  {rep.summary()}", flush=True)
         assert rep.ok(), rep.summary()
+
+
+@pytest.mark.parametrize("over", [dict(R=40, gamma=5, V=3000, d=256),
+                                  dict(R=33, gamma=4, V=2001, d=64, rank=32)],
+                         ids=["fused", "per-step"])
+def test_rnn_cap_accept_parity(over):
+    """Cap-accept verification of RNN drafts (the whole block verified with
+    the draft's features, committed within the scheduled window) through the
+    round driver, against the oracle."""
+    cfg = synth.scaled(synth.config(2), **over)
+    inp = synth.make_inputs(cfg, device="cpu")
+    g = to_dev(inp)
+    g["Wr"] = synth.rnn_weights(cfg, device=DEV, gain=3.0)
+    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV, rnn=(cfg.rank, cfg.d, cfg.dtype))
+    RD.run_round(g, buf, cfg.T, cfg.philox_seed, 4, scheduler=True, verify_mode="cap-accept",
+                 head="rnn")
+    torch.cuda.synchronize()
+    assert D.get_status(buf.ws) == 0
+    rep = PC.Report()
+    feat = f(buf.feat)
+    m, mfull = PC.check_verify_cap_accept(rep, n(buf.full), n(buf.ell), None, f(inp["target"]), 1,
+                                          n(buf.x), n(buf.logp_d), n(buf.lse_d), f(inp["U"]),
+                                          f(inp["W1"]), f(inp["W2t"]), cfg.T, cfg.philox_seed, 4,
+                                          n(buf.m), n(buf.tau), n(buf.emitted),
+                                          n(buf.next_anchor), n(buf.m_full), None, feat=feat)
+    PC.check_pack(rep, n(buf.emitted), n(buf.tau), n(buf.cu_out), n(buf.flat_out), None, None,
+                  n(buf.N_out)[0], "emitted")
+    print(f"  {rep.summary()} cut={int((mfull > n(buf.ell)).sum())}", flush=True)
+    assert rep.ok(), rep.summary()
+    assert (mfull > n(buf.ell)).any()           # the window cut some requests
