@@ -401,8 +401,12 @@ def diagnostics(cfg, inp, buf, torch, np, D):
     held-out blocks (n = 1024 rounds of R requests, 64 temperatures, 15 bins)."""
     dev = inp["U"].device
     cs = torch.empty(cfg.R, cfg.gamma, dtype=torch.float32, device=dev)
-    run_c = lambda: D.acceptance_rate(inp["target"], buf.x, buf.lse_d, inp["U"], inp["W1"],
-                                      inp["W2t"], cfg.T, cs, buf.ws)
+    if buf.feat is not None:          # RNN head: p_d from the draft's features
+        run_c = lambda: D.acceptance_rate_features(inp["target"], buf.x, buf.lse_d, inp["U"],
+                                                   buf.feat, inp["W2t"], cfg.T, cs, buf.ws)
+    else:
+        run_c = lambda: D.acceptance_rate(inp["target"], buf.x, buf.lse_d, inp["U"], inp["W1"],
+                                          inp["W2t"], cfg.T, cs, buf.ws)
     n = 1024 * cfg.R
     g = torch.Generator(device="cpu").manual_seed(7)
     z = (torch.randn(n, cfg.gamma, generator=g) * 2.0 + 1.5).to(dev)
