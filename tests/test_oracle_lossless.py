@@ -341,3 +341,83 @@ def test_monte_carlo_rnn_draft_lossless():
     # ignored) emit a different law
     m2, tau2, em2, *_ = O.verify(ell, None, tgt, 1, x, lp, lse, Ub, W1, W2t, T, seed=79, rnd=5)
     assert (em2 != em).any()
+
+
+def _rnn_setup(seed):
+    U, W1, W2t, h, w, tl = _setup(seed)
+    rng = np.random.default_rng(seed + 100)
+    Wr = rng.normal(0, 0.6, (3 * RANK, 2 * RANK + D)).astype(np.float32)
+    return U, W1, W2t, Wr, h, w, tl
+
+
+def _rnn_draft_conditionals(U, W1, W2t, Wr, h, anchor, T):
+    """p_d(. | x_1..x_{k-1}) of the oracle's RNN head for every in-block prefix,
+    from log p_d of every candidate token forced after every prefix (the
+    features, and so the distribution, depend on the whole prefix)."""
+    seqs = list(itertools.product(range(V), repeat=G))
+    X = np.array([(anchor,) + s for s in seqs], np.int32)
+    n = len(seqs)
+    out = O.draft_rnn(np.broadcast_to(U, (n, G, V)), W1, W2t, Wr, np.broadcast_to(h, (n, G, D)),
+                      X[:, 0], T, force_x=X)
+    lp = out[1]
+    cond = {}
+    for i, s in enumerate(seqs):
+        for k in range(1, G + 1):
+            cond.setdefault(s[:k - 1], np.zeros(V))[s[k - 1]] = np.exp(lp[i, k - 1])
+    for pre, p in cond.items():
+        assert abs(p.sum() - 1.0) < 1e-12, (pre, p.sum())
+    return cond
+
+
+def _enumerate_round_rnn(U, W1, W2t, Wr, h, w, tl, T, sps, anchor, scheduler_mode,
+                         residual_from_markov=False):
+    cond = _rnn_draft_conditionals(U, W1, W2t, Wr, h, anchor, T)
+    emitted_law = {}
+    for xs in itertools.product(range(V), repeat=G):
+        x = (anchor,) + xs
+        pd = [cond[xs[:k - 1]] for k in range(1, G + 1)]
+        p_draft = np.prod([pd[k - 1][x[k]] for k in range(1, G + 1)])
+        if scheduler_mode is None:
+            ell = G
+        else:
+            c, _ = O.confidence(h[None], W1, w, np.array([x]))
+            ell = int(O.prefix_schedule(c, sps, mode=scheduler_mode)[0][0])
+        outcomes = []
+        p_reach = 1.0
+        for k in range(1, ell + 1):
+            pt = _pt(tl, x[1:k], T)
+            alpha = min(1.0, pt[x[k]] / pd[k - 1][x[k]])
+            # the residual uses the distribution the draft sampled from; the
+            # negative control rebuilds it as a Markov head would (W1[x_{k-1}] only)
+            pr = O.draft_row(U[k - 1], np.tanh(W1), W2t, x[k - 1], T) if residual_from_markov \
+                else pd[k - 1]
+            q, _ = O.residual_row(tl[tuple(x[1:k])], np.log(pr), 0.0, T)
+            outcomes.append((k - 1, p_reach * (1.0 - alpha), q))
+            p_reach *= alpha
+        outcomes.append((ell, p_reach, _pt(tl, x[1:ell + 1], T)))
+        for m, pm, ydist in outcomes:
+            if pm == 0.0:
+                continue
+            for y in range(V):
+                e = tuple(int(t) for t in x[1:m + 1]) + (y,)
+                emitted_law[e] = emitted_law.get(e, 0.0) + p_draft * pm * ydist[y]
+    return _complete(tl, emitted_law, T)
+
+
+@pytest.mark.parametrize("T,mode", [(1.0, None), (1.0, 0), (0.7, 0)])
+def test_exact_enumeration_lossless_rnn_head(T, mode):
+    """RNN-head drafts (a distribution at each position that depends on the
+    whole prefix), verified with the residual of the sampled distribution and
+    scheduled by Algorithm 1 on x-dependent confidences: the emitted law is the
+    target's to 1e-12; rebuilding the residual without the features is not."""
+    U, W1, W2t, Wr, h, w, tl = _rnn_setup(31)
+    sps = _sps_dynamic()
+    law = _enumerate_round_rnn(U, W1, W2t, Wr, h, w, tl, T, sps, 5, mode)
+    ref = _target_law(tl, T)
+    assert abs(sum(law.values()) - 1.0) < 1e-12
+    tv = 0.5 * sum(abs(law.get(s, 0.0) - p) for s, p in ref.items())
+    assert tv < 1e-12, tv
+    bad = _enumerate_round_rnn(U, W1, W2t, Wr, h, w, tl, T, sps, 5, mode,
+                               residual_from_markov=True)
+    tv_bad = 0.5 * sum(abs(bad.get(s, 0.0) - p) for s, p in ref.items())
+    assert tv_bad > 1e-4, tv_bad
