@@ -153,7 +153,7 @@ constexpr int kPThreads = 512;
 constexpr int kPWaves = 8;
 constexpr int kPSlice = 512;                // vocabulary entries per workgroup
 constexpr int kPRows = 256;                 // requests per row group (LDS-resident W1 rows)
-constexpr int kPMaxChunks = 1024;           // chunk statistics staged per pick
+constexpr int kPMaxChunks = 2048;           // chunk statistics per pick (four per thread)
 constexpr uint32_t kBarrierSpins = 1u << 24;
 
 struct PersistArgs {
@@ -870,6 +870,16 @@ __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, float 
   __syncthreads();                          // LDS slots and the W1 row are reused
 }
 
+// The persistent launch's pick as a launch of its own for the per-step
+// schedule (bf16 data and weights, rank 64/128/256): one 512-thread workgroup
+// per request, step a.k.
+template <int KS, bool GREEDY>
+__global__ __launch_bounds__(kPThreads) void k_draft_pick_p(DraftPickArgs a, float s2) {
+  __shared__ BlockScratch sh;
+  __shared__ PickLds<2 * KS> pl;
+  pick_row_p<KS, GREEDY>(a, blockIdx.x, s2, sh, pl, reinterpret_cast<const uint16_t*>(a.feat));
+}
+
 // ---- RNN head inside the persistent launch
 // Feature rows e_k of requests row0 .. row0 + rows - 1 into LDS rows of ROWP
 // 16-byte pieces (the layout of gather_w1_rows).  They were written by other
@@ -1519,6 +1529,9 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     const hipError_t e = launch_rnn_hproj(*rnn, st);
     if (e != hipSuccess) return e;
   }
+  // the 512-thread pick of the persistent launch where its shape limits hold
+  const bool fast_pick = u_bf16 && w_bf16 && (rank == 64 || rank == 128 || rank == 256) &&
+                         nch <= kPMaxChunks;
   for (int k = 1; k <= gamma; ++k) {
     hipError_t e;
     if (rnn && (e = launch_rnn_cell(*rnn, k, st)) != hipSuccess) return e;
@@ -1540,7 +1553,17 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     if (e != hipSuccess) return e;
     if (ev_end && (e = hipEventRecord(ev_end[k - 1], st)) != hipSuccess) return e;
     p.k = k;
-    DSPARK_PICK_ALL(R)
+    if (fast_pick) {
+#define DSPARK_PICKP(KS_)                                                                     \
+      if (greedy) hipLaunchKernelGGL((k_draft_pick_p<KS_, true>), dim3(R), dim3(kPThreads), 0, st, p, scale2); \
+      else hipLaunchKernelGGL((k_draft_pick_p<KS_, false>), dim3(R), dim3(kPThreads), 0, st, p, scale2)
+      if (rank == 64) { DSPARK_PICKP(4); }
+      else if (rank == 128) { DSPARK_PICKP(8); }
+      else { DSPARK_PICKP(16); }
+#undef DSPARK_PICKP
+    } else {
+      DSPARK_PICK_ALL(R)
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
