@@ -81,6 +81,12 @@ def _p(a):
     return None if a is None else a.ctypes.data_as(C.c_void_p)
 
 
+def _T(T):
+    """The sampling temperature as the GPU library receives it: the C ABI takes
+    a float32, so the oracle computes with that value widened to double."""
+    return float(np.float32(T))
+
+
 def _f32(a):
     return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
 
@@ -133,7 +139,7 @@ def draft_row(Uk, W1, W2t, prev, T):
     Uk = _f32(Uk)
     rank = 0 if W1 is None else W1.shape[1]
     p = np.zeros(Uk.size)
-    lib().orc_draft_row(Uk.size, rank, float(T), _p(Uk), _p(_f32(W1)), _p(_f32(W2t)),
+    lib().orc_draft_row(Uk.size, rank, _T(T), _p(Uk), _p(_f32(W1)), _p(_f32(W2t)),
                         int(prev), _p(p))
     return p
 
@@ -142,7 +148,7 @@ def residual_row(t, s, lse_d, T):
     t = _f32(t)
     s = _f64(s)
     q = np.zeros(t.size)
-    tot = lib().orc_residual_row(t.size, float(T), _p(t), _p(s), float(lse_d), _p(q))
+    tot = lib().orc_residual_row(t.size, _T(T), _p(t), _p(s), float(lse_d), _p(q))
     return q, float(tot)
 
 
@@ -163,7 +169,7 @@ def draft_rnn(U, W1, W2t, Wr, h, x0, T, seed=0, rnd=0, req_ids=None, force_x=Non
     e = np.zeros((R, gamma, rank))
     s = np.zeros((R, gamma, rank))
     em = np.zeros((R, gamma, rank))
-    rc = lib().orc_draft_rnn(R, gamma, V, rank, d, float(T), seed, rnd, _p(U), _p(_f32(W1)),
+    rc = lib().orc_draft_rnn(R, gamma, V, rank, d, _T(T), seed, rnd, _p(U), _p(_f32(W1)),
                              _p(_f32(W2t)), _p(_f32(Wr)), _p(h), _p(_i32(x0)), _p(_i32(req_ids)),
                              _p(_i32(force_x)), _p(_f32(force_e)), int(bool(bf16_e)), _p(x),
                              _p(lp), _p(lse), _p(mg), _p(xo), _p(e), _p(s), _p(em))
@@ -184,7 +190,7 @@ def draft_markov(U, W1, W2t, x0, T, seed=0, rnd=0, req_ids=None, force_x=None, o
     lse = np.zeros((R, gamma))
     mg = np.zeros((R, gamma))
     xo = np.zeros((R, gamma + 1), np.int32) if own else None
-    rc = lib().orc_draft_markov(R, gamma, V, rank, float(T), seed, rnd, _p(U), _p(W1c),
+    rc = lib().orc_draft_markov(R, gamma, V, rank, _T(T), seed, rnd, _p(U), _p(W1c),
                                 _p(W2c), _p(x0), _p(_i32(req_ids)), _p(_i32(force_x)),
                                 _p(x), _p(lp), _p(lse), _p(mg), _p(xo))
     assert rc == 0, rc
@@ -267,7 +273,7 @@ def acceptance_rate(target, x, U, W1, W2t, T, feat=None):
         rank = int(np.shape(feat)[-1])
     cs = np.zeros((R, gamma))
     mg = np.zeros((R, gamma))
-    rc = lib().orc_acceptance_rate(R, gamma, V, rank, float(T), _p(target), _p(_i32(x)),
+    rc = lib().orc_acceptance_rate(R, gamma, V, rank, _T(T), _p(target), _p(_i32(x)),
                                    _p(_f32(U)), _p(_f32(W1)), _p(_f32(W2t)), _p(cs), _p(mg),
                                    _p(_f32(feat)))
     assert rc == 0, rc
@@ -350,7 +356,7 @@ def verify(ell, cu, target, layout, x, logp_d, lse_d, U, W1, W2t, T, seed=0, rnd
     na = np.zeros(R, np.int32)
     lpt = np.zeros((R, gamma))
     mg = np.zeros(R)
-    rc = lib().orc_verify(R, gamma, V, rank, float(T), seed, rnd, _p(ell), _p(_i32(cu)),
+    rc = lib().orc_verify(R, gamma, V, rank, _T(T), seed, rnd, _p(ell), _p(_i32(cu)),
                           _p(target), int(layout), _p(x), _p(_f64(logp_d)), _p(_f64(lse_d)),
                           _p(_f32(U)), _p(_f32(W1)), _p(_f32(W2t)), _p(_i32(req_ids)),
                           _p(_i32(force_m)), _p(m), _p(tau), _p(em), _p(na), _p(lpt), _p(mg),

@@ -30,6 +30,9 @@ import oracle as O
 
 V, G, RANK, D = 8, 3, 4, 6
 
+# the library takes the temperature as a float32; the pins use that value
+T07 = float(np.float32(0.7))
+
 
 def _setup(seed):
     rng = np.random.default_rng(seed)
@@ -115,7 +118,7 @@ def _sps_appendix_a_like():
     return np.array([0.0, 1.0, 0.5, 0.45, 0.44])
 
 
-@pytest.mark.parametrize("T,mode", [(1.0, None), (1.0, 0), (0.7, 0)])
+@pytest.mark.parametrize("T,mode", [(1.0, None), (1.0, 0), (T07, 0)])
 def test_exact_enumeration_lossless(T, mode):
     U, W1, W2t, h, w, tl = _setup(31)
     sps = _sps_dynamic()
@@ -147,7 +150,7 @@ def test_exact_enumeration_global_search_is_biased():
     assert tv0 < 1e-12
 
 
-@pytest.mark.parametrize("T", [1.0, 0.7])
+@pytest.mark.parametrize("T", [1.0, T07])
 def test_monte_carlo_sampled_path_lossless(T):
     U, W1, W2t, h, w, tl = _setup(31)
     n = 120_000
@@ -229,7 +232,7 @@ def _enumerate_cap_accept(U, W1, W2t, h, w, tl, T, sps, anchor):
     return _complete(tl, emitted_law, T)
 
 
-@pytest.mark.parametrize("T", [1.0, 0.7])
+@pytest.mark.parametrize("T", [1.0, T07])
 def test_exact_enumeration_cap_accept_lossless(T):
     U, W1, W2t, h, w, tl = _setup(31)
     law = _enumerate_cap_accept(U, W1, W2t, h, w, tl, T, _sps_dynamic(), anchor=5)
@@ -404,7 +407,7 @@ def _enumerate_round_rnn(U, W1, W2t, Wr, h, w, tl, T, sps, anchor, scheduler_mod
     return _complete(tl, emitted_law, T)
 
 
-@pytest.mark.parametrize("T,mode", [(1.0, None), (1.0, 0), (0.7, 0)])
+@pytest.mark.parametrize("T,mode", [(1.0, None), (1.0, 0), (T07, 0)])
 def test_exact_enumeration_lossless_rnn_head(T, mode):
     """RNN-head drafts (a distribution at each position that depends on the
     whole prefix), verified with the residual of the sampled distribution and

@@ -23,6 +23,9 @@ import oracle as O
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 
+# the library takes the temperature as a float32; the pins use that value
+T07 = float(np.float32(0.7))
+
 
 # ---------------------------------------------------------------- Philox --
 @pytest.fixture(scope="module")
@@ -140,7 +143,7 @@ def test_draft_row_uniform_logits():
 def test_draft_row_rank0_is_softmax():
     rng = np.random.default_rng(3)
     U = rng.normal(0, 3, 777).astype(np.float32)
-    for T in [1.0, 0.7, 2.5]:
+    for T in [1.0, T07, 2.5]:
         p = O.draft_row(U, None, None, 0, T)
         np.testing.assert_allclose(p, special.softmax(U.astype(np.float64) / T), rtol=1e-12,
                                    atol=1e-300)
@@ -155,8 +158,9 @@ def test_draft_row_onehot_embedding_selects_W2_row():
     W2t = rng.normal(0, 1, (V, rank)).astype(np.float32)
     prev, j = 42, 5
     W1[prev, j] = 1.0
-    p = O.draft_row(U, W1, W2t, prev, 0.9)
-    ref = special.softmax((U.astype(np.float64) + W2t[:, j]) / 0.9)
+    T = float(np.float32(0.9))
+    p = O.draft_row(U, W1, W2t, prev, T)
+    ref = special.softmax((U.astype(np.float64) + W2t[:, j]) / T)
     np.testing.assert_allclose(p, ref, rtol=1e-12)
 
 
@@ -734,7 +738,7 @@ def test_residual_row_closed_form():
     t = rng.normal(0, 1, V).astype(np.float32)
     s = rng.normal(0, 1, V)
     lse_d = special.logsumexp(s)
-    for T in [1.0, 0.6]:
+    for T in [1.0, float(np.float32(0.6))]:
         q, tot = O.residual_row(t, s, lse_d, T)
         pt = special.softmax(t.astype(np.float64) / T)
         pd = special.softmax(s)
@@ -769,7 +773,7 @@ def test_acceptance_rate_closed_forms():
     W1 = rng.normal(0, 0.4, (V, rank)).astype(np.float32)
     W2t = rng.normal(0, 0.4, (V, rank)).astype(np.float32)
     tgt3 = (np.concatenate([U, U[:, :1]], 1) + rng.normal(0, 1, (R, g + 1, V))).astype(np.float32)
-    for T in [1.0, 0.6]:
+    for T in [1.0, float(np.float32(0.6))]:
         cs, _ = O.acceptance_rate(tgt3, x, U, W1, W2t, T)
         for i in range(R):
             for k in range(1, g + 1):
@@ -799,7 +803,7 @@ def test_acceptance_rate_with_rnn_features():
     feat = np.tanh(rng.normal(0, 1, (R, g, rank))).astype(np.float32)
     tgt = (np.concatenate([U, U[:, :1]], 1) + rng.normal(0, 1, (R, g + 1, V))).astype(np.float32)
     junk = rng.normal(0, 5, (V, rank)).astype(np.float32)
-    for T in [1.0, 0.7]:
+    for T in [1.0, T07]:
         cs, _ = O.acceptance_rate(tgt, x, U, junk, W2t, T, feat=feat)
         for i in range(R):
             for k in range(1, g + 1):
@@ -934,7 +938,7 @@ def test_rnn_closed_gate_is_a_markov_head_on_tanh_embeddings():
     Wr[rank:2 * rank] = np.random.default_rng(1).normal(0, 1, (rank, 2 * rank + d))
     Wr[2 * rank:, rank:2 * rank] = np.eye(rank)        # output: the embedding part
     W1t = np.tanh(W1.astype(np.float64)).astype(np.float32)
-    for T in [1.0, 0.7, 0.0]:
+    for T in [1.0, T07, 0.0]:
         a = O.draft_rnn(U, W1, W2t, Wr, h, x0, T, seed=4, bf16_e=False)
         b = O.draft_markov(U, W1t, W2t, x0, T, seed=4, own=True)
         assert np.abs(a[6]).max() == 0.0               # the state never moves
