@@ -4,8 +4,10 @@ block size 16, vocabulary 129280, Markov rank 256, hidden 4096, bf16, T = 1,
 scheduler on (Algorithm 1; --scheduler async selects the asynchronous form).
 
 Prints ONE JSON line.  `value` = verified draft tokens per second
-(sum of scheduled lengths ell over the timed rounds / their wall time), inputs
-resident in HBM before the timed region.  The `roofline` object covers the
+(sum of scheduled lengths ell over the timed rounds / their device time, each
+round timed with events around its six stages on the launch stream), inputs
+resident in HBM before the timed region; a 512 MiB scratch buffer is written
+between rounds so that no round starts with W2 or U in the memory-side cache.  The `roofline` object covers the
 dominant kernel (the persistent draft kernel: all gamma steps in one
 cooperative launch; the per-step statistics kernel when the shape takes the
 per-step schedule), timed live with HIP events recorded on the launch stream
@@ -56,6 +58,9 @@ def parse():
                         "fit on synthetic held-out blocks")
     p.add_argument("--cpu-sample", type=int, default=48, help="requests in the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--flush-mib", type=int, default=512,
+                   help="scratch buffer written between timed rounds (MiB) so that no round "
+                        "starts with W2 or U warm in the memory-side cache; 0 disables")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="before the rounds, copy a buffer of this many MiB three times "
                         "(device to device), the known-size reference for HBM byte counters")
@@ -270,17 +275,32 @@ def main():
                      buf.emitted, buf.next_anchor, buf.ws, logp_t=buf.logp_t)
         L.pack(buf.emitted, buf.tau, 0, buf.cu_out, buf.flat_out, N_out=buf.N_out, ws=buf.ws)
 
+    # between rounds a scratch buffer is written, so every round reads W2 and
+    # U from HBM (the 256 MB memory-side cache holds nothing of them); each
+    # round is timed with events on the launch stream around its six stages
+    flush = (torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+             if args.flush_mib > 0 else None)
+    r_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(K)]
     for i in range(W):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
         one_round(i, False)
     torch.cuda.synchronize()
     log(f"[bench] {W} warmup rounds done")
     t_start = time.perf_counter()
     for i in range(W, W + K):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        r_ev[i - W][0].record(stream)
         one_round(i, True)
+        r_ev[i - W][1].record(stream)
     torch.cuda.synchronize()
-    t_total = time.perf_counter() - t_start
+    t_wall = time.perf_counter() - t_start
+    round_ms = np.array([a.elapsed_time(b) for a, b in r_ev])
+    t_total = float(round_ms.sum()) * 1e-3
     status = D.get_status(buf.ws)
-    ms_per_step = 1e3 * t_total / K
+    ms_per_step = float(round_ms.mean())
 
     ell_t = ells[W:].cpu().numpy().astype(np.int64)
     m_t = ms[W:].cpu().numpy().astype(np.int64)
@@ -324,6 +344,9 @@ def main():
         kflops = 2.0 * cfg.R * cfg.rank * cfg.V
     achieved = kb / (avg_ms * 1e-3) / 1e9
     mfma_tf = kflops / (avg_ms * 1e-3) / 1e12
+    log(f"[bench] round time (events, W2/U cold): median {np.median(round_ms):.3f} ms, p10 "
+        f"{np.percentile(round_ms, 10):.3f}, p90 {np.percentile(round_ms, 90):.3f}; wall clock "
+        f"{1e3 * t_wall / K:.3f} ms per round with the {args.flush_mib} MiB scratch write")
     log(f"[bench] {K} rounds: {ms_per_step:.3f} ms/round, sum_ell={sum_ell}, sum_tau={sum_tau}, "
         f"N_avg={N_avg:.1f}, n_rej={n_rej}, {kernel} {avg_ms * 1e3:.1f} us/launch "
         f"({achieved:.0f} GB/s, {mfma_tf:.0f} TFLOP/s), round HBM frac {hbm_frac_round:.3f}, "
@@ -354,6 +377,11 @@ def main():
                    "gamma": cfg.gamma, "V": cfg.V, "rank": cfg.rank, "d": cfg.d, "T": cfg.T,
                    "scheduler": sched, "verify_mode": vmode, "head": args.head,
                    "parallelism": "single-gpu"},
+        "round_ms_median": float(np.median(round_ms)),
+        "round_ms_p10": float(np.percentile(round_ms, 10)),
+        "round_ms_p90": float(np.percentile(round_ms, 90)),
+        "wall_ms_per_step_incl_flush": 1e3 * t_wall / K,
+        "flush_mib_between_rounds": args.flush_mib,
         "hbm_frac_round": hbm_frac_round,
         "round_bytes_alg": bytes_round,
         "emitted_tokens_per_s": sum_tau / t_total,
@@ -373,6 +401,12 @@ def main():
     if diag is not None:
         out["diagnostics"] = diag
     print(json.dumps(out), flush=True)
+    # orderly teardown while the runtime is fully alive: all work finished,
+    # every device buffer released before the interpreter exits
+    torch.cuda.synchronize()
+    del buf, inp, flush, ells, ms, Ns, Nouts
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
 
 
 def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=5):

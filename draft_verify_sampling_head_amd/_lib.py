@@ -28,7 +28,9 @@ EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
            "dspark_verify_cap_accept", "dspark_acceptance_rate", "dspark_sts_fit",
            "dspark_sts_workspace_bytes", "dspark_confidence_logits", "dspark_rnn_workspace_bytes",
            "dspark_draft_rnn", "dspark_verify_features", "dspark_draft_rnn_profiled",
-           "dspark_acceptance_rate_features", "dspark_verify_cap_accept_features")
+           "dspark_acceptance_rate_features", "dspark_verify_cap_accept_features",
+           "dspark_set_switch", "dspark_get_switch")
+SWITCH_FORCE_PER_STEP, SWITCH_RNN_CELL_VALU, SWITCH_BARRIER_SPINS, SWITCH_DRAFT_KERNEL = 1, 2, 3, 4
 
 
 class DsparkError(RuntimeError):
@@ -83,6 +85,9 @@ def load():
     L.dspark_verify_features.argtypes = L.dspark_verify.argtypes
     L.dspark_acceptance_rate_features.argtypes = L.dspark_acceptance_rate.argtypes
     L.dspark_verify_cap_accept_features.argtypes = L.dspark_verify_cap_accept.argtypes
+    L.dspark_set_switch.argtypes = [i32, C.c_int64]
+    L.dspark_get_switch.argtypes = [i32]
+    L.dspark_get_switch.restype = C.c_int64
     for fn in EXPORTS:
         getattr(L, fn).restype = getattr(L, fn).restype or i32
     L.dspark_workspace_bytes.restype = sz
@@ -92,6 +97,17 @@ def load():
     L.dspark_version.restype = C.c_char_p
     _lib = L
     return L
+
+
+def set_switch(key, value):
+    """Set a test / measurement switch (SWITCH_*); returns the previous value."""
+    prev = int(load().dspark_get_switch(key))
+    _check("dspark_set_switch", load().dspark_set_switch(key, int(value)))
+    return prev
+
+
+def get_switch(key):
+    return int(load().dspark_get_switch(key))
 
 
 def _ptr(t):

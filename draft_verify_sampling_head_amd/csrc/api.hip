@@ -5,11 +5,41 @@
 #include "dspark.h"
 
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
 
 #include "launch.hpp"
 #include "workspace.hpp"
 
 using namespace dspark;
+
+namespace dspark {
+
+namespace {
+std::mutex g_sw_mu;
+bool g_sw_init = false;
+Switches g_sw{};
+
+void init_switches_locked() {
+  if (g_sw_init) return;
+  const char* dk = std::getenv("DSPARK_DRAFT_KERNEL");
+  g_sw.force_per_step = (dk && std::strcmp(dk, "steps") == 0) ? 1 : 0;
+  g_sw.draft_kernel = (dk && std::strcmp(dk, "barrier") == 0) ? 1 : 0;
+  g_sw.rnn_cell_valu = std::getenv("DSPARK_RNN_CELL_VALU") ? 1 : 0;
+  const char* sl = std::getenv("DSPARK_BARRIER_SPINS");
+  g_sw.barrier_spins = sl ? (uint32_t)std::strtoul(sl, nullptr, 10) : 0u;
+  g_sw_init = true;
+}
+}  // namespace
+
+Switches switches() {
+  std::lock_guard<std::mutex> lk(g_sw_mu);
+  init_switches_locked();
+  return g_sw;
+}
+
+}  // namespace dspark
 
 namespace {
 
@@ -56,7 +86,43 @@ const char* dspark_status_string(dspark_status s) {
   return "DSPARK_E_UNKNOWN";
 }
 
-const char* dspark_version(void) { return "dspark-mi355x 0.1 (gfx950)"; }
+const char* dspark_version(void) { return "dspark-mi355x 0.2 (gfx950)"; }
+
+dspark_status dspark_set_switch(int key, int64_t value) {
+  std::lock_guard<std::mutex> lk(g_sw_mu);
+  init_switches_locked();
+  switch (key) {
+    case DSPARK_SWITCH_FORCE_PER_STEP:
+      if (value != 0 && value != 1) return DSPARK_E_INVALID;
+      g_sw.force_per_step = (int)value;
+      return DSPARK_OK;
+    case DSPARK_SWITCH_RNN_CELL_VALU:
+      if (value != 0 && value != 1) return DSPARK_E_INVALID;
+      g_sw.rnn_cell_valu = (int)value;
+      return DSPARK_OK;
+    case DSPARK_SWITCH_BARRIER_SPINS:
+      if (value < 0 || value > 0xFFFFFFFFll) return DSPARK_E_INVALID;
+      g_sw.barrier_spins = (uint32_t)value;
+      return DSPARK_OK;
+    case DSPARK_SWITCH_DRAFT_KERNEL:
+      if (value != 0 && value != 1) return DSPARK_E_INVALID;
+      g_sw.draft_kernel = (int)value;
+      return DSPARK_OK;
+  }
+  return DSPARK_E_INVALID;
+}
+
+int64_t dspark_get_switch(int key) {
+  std::lock_guard<std::mutex> lk(g_sw_mu);
+  init_switches_locked();
+  switch (key) {
+    case DSPARK_SWITCH_FORCE_PER_STEP: return g_sw.force_per_step;
+    case DSPARK_SWITCH_RNN_CELL_VALU: return g_sw.rnn_cell_valu;
+    case DSPARK_SWITCH_BARRIER_SPINS: return g_sw.barrier_spins;
+    case DSPARK_SWITCH_DRAFT_KERNEL: return g_sw.draft_kernel;
+  }
+  return -1;
+}
 
 dspark_status dspark_clear_status(void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!ws || ws_bytes < 256 || !aligned16(ws)) return DSPARK_E_INVALID;
@@ -230,6 +296,8 @@ dspark_status dspark_prefix_schedule(int R, int gamma, const float* c, const dou
   if (R == 0) return DSPARK_OK;
   if (!c || !sps || !ell) return DSPARK_E_INVALID;
   if (N_max < R) return DSPARK_E_INVALID;
+  // static verification sends the whole block: R (gamma + 1) tokens must fit
+  if (!enabled && (int64_t)N_max < (int64_t)R * (gamma + 1)) return DSPARK_E_INVALID;
   if ((int64_t)R * gamma > 16384) return DSPARK_E_UNSUPPORTED;
   SchedArgs sa{};
   sa.R = R; sa.gamma = gamma; sa.N_max = N_max; sa.enabled = enabled ? 1 : 0;

@@ -36,6 +36,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 struct DraftPickArgs {
   int R, gamma, k, V, rank, nch;
   float invT;               // 1/T (sampling)
+  float T;                  // T (sampling; 1 when greedy)
   uint64_t seed, round;
   const void* U;
   const void* W1;
@@ -85,7 +86,9 @@ __device__ __forceinline__ void pick_row(const DraftPickArgs& a, int i, int k, i
                                                kTagDraftChunk, (uint32_t)i, (uint32_t)k, want_gap,
                                                &srel, sh);
     const float lse_rel = logf(srel);
-    lse = m * a.invT + lse_rel;
+    // the absolute normaliser is assembled in double: m / T can be large at a
+    // low temperature, where a float product would cost several ulps
+    lse = (float)((double)m / (double)a.T + (double)lse_rel);
     int c = pc.idx;
     if (c < 0) { set_flag(a.status, kFlagNonFinite); c = 0; }
     const int base = c * kChunk;
@@ -103,7 +106,7 @@ __device__ __forceinline__ void pick_row(const DraftPickArgs& a, int i, int k, i
 #pragma unroll
     for (int o = 1; o < TPE; o *= 2) b += __shfl_xor(b, o);
     const UT* urow = reinterpret_cast<const UT*>(a.U) + ((int64_t)i * a.gamma + (k - 1)) * a.V;
-    const float s = in ? (Elem<UT>::get(urow, v) + b - m) * a.invT : -INFINITY;
+    const float s = in ? (Elem<UT>::get(urow, v) + b - m) / a.T : -INFINITY;
     const PickResult pe = block_pick_in_chunk<NT>(s, base, a.seed, a.round, kTagDraftElem,
                                                   (uint32_t)i, (uint32_t)k, want_gap, sh);
     xk = pe.idx;
@@ -785,7 +788,7 @@ __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, float 
     }
     const PickRed rr = block_pick_reduce(pr, pl.red);
     const float lse_rel = logf(rr.s);
-    const float lse = m * a.invT + lse_rel;
+    const float lse = (float)((double)m / (double)a.T + (double)lse_rel);
     int c = rr.key == -INFINITY ? -1 : rr.idx;
     if (c < 0) { if (tid == 0) set_flag(a.status, kFlagNonFinite); c = 0; }
     // in-chunk: entry base + tid / TPE, part tid % TPE of the rank
@@ -826,7 +829,7 @@ __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, float 
     static_assert(TPE == 4, "four threads per entry");
     bsum += dpp_f<kDppXor1>(bsum);
     bsum += dpp_f<kDppXor2>(bsum);
-    const float sv = in ? (u + bsum - m) * a.invT : -INFINITY;   // score of entry v, minus m/T
+    const float sv = in ? (u + bsum - m) / a.T : -INFINITY;      // score of entry v, minus m/T
     float key = -INFINITY;
     int kid = 0x7FFFFFFF;
     if (h == 0 && in) {
@@ -1307,8 +1310,7 @@ bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void*
                          const int32_t* rej_count, const int4* rej, const float2* lse_t,
                          const float* lse_d, float2* L, uint32_t* status, hipStream_t st,
                          hipError_t* err, bool overlap, bool feat_rows) {
-  const char* env = std::getenv("DSPARK_DRAFT_KERNEL");
-  if (env && std::strcmp(env, "steps") == 0) return false;
+  if (switches().force_per_step) return false;
   if ((V % 8) != 0 || (rank != 64 && rank != 128 && rank != 256)) return false;
   for (const void* p : {U, W1, W2t, target})
     if (reinterpret_cast<uintptr_t>(p) & 15) return false;
@@ -1368,8 +1370,7 @@ static hipError_t launch_persist_ks(PersistArgs& P, int grid, hipStream_t st) {
 // environment selects the per-step schedule for every shape.
 static int persistent_grid(int gamma, int V, int rank, bool u_bf16, bool w_bf16, bool u_vec,
                            const void* W1, const void* W2t, bool greedy, bool feat) {
-  const char* env = std::getenv("DSPARK_DRAFT_KERNEL");
-  if (env && std::strcmp(env, "steps") == 0) return 0;
+  if (switches().force_per_step) return 0;
   if (!u_bf16 || !w_bf16 || !u_vec || (V % 8) != 0) return 0;
   if ((int64_t)32 * gamma * V >= ((int64_t)1 << 31)) return 0;
   if (rank != 64 && rank != 128 && rank != 256) return 0;
@@ -1437,7 +1438,7 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
 
   DraftPickArgs p{};
   p.R = R; p.gamma = gamma; p.k = 1; p.V = V; p.rank = rank; p.nch = nch;
-  p.invT = greedy ? 1.f : 1.f / T; p.seed = seed; p.round = round;
+  p.invT = greedy ? 1.f : 1.f / T; p.T = greedy ? 1.f : T; p.seed = seed; p.round = round;
   p.U = U; p.W1 = W1; p.W2t = W2t; p.x0 = x0; p.x = x; p.logp_d = logp_d; p.lse_d = lse_d;
   p.margin = margin; p.L = Lc; p.I = Ic; p.status = status;
 
@@ -1447,9 +1448,9 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
   // bf16 h / Wr with 16-byte aligned rows and a 16-byte aligned feature tensor.
   const void* feat = rnn ? rnn->feat : nullptr;
   p.feat = feat;
-  const char* cell_env = std::getenv("DSPARK_RNN_CELL_VALU");
+  const Switches sw = switches();
   const bool rnn_fused_ok =
-      rnn && rnn->w_bf16 && rnn->h_bf16 && cell_env == nullptr &&
+      rnn && rnn->w_bf16 && rnn->h_bf16 && !sw.rnn_cell_valu &&
       ((reinterpret_cast<uintptr_t>(rnn->Wr) | reinterpret_cast<uintptr_t>(rnn->feat)) & 15) == 0 &&
       ((2 * rank + rnn->d) % 8) == 0;
   const int grid = (rnn && !rnn_fused_ok)
@@ -1462,9 +1463,7 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     P.scale2 = scale2;
     P.nslice = (V + kPSlice - 1) / kPSlice;
     P.bar = reinterpret_cast<uint32_t*>(w + L.bar);
-    const char* sl = std::getenv("DSPARK_BARRIER_SPINS");
-    P.spin_limit = sl ? (uint32_t)std::strtoul(sl, nullptr, 10) : kBarrierSpins;
-    if (P.spin_limit == 0) P.spin_limit = 1;
+    P.spin_limit = sw.barrier_spins ? sw.barrier_spins : kBarrierSpins;
     const int prep_blocks = (int)std::min<int64_t>(64, ((int64_t)R * (gamma + 1) + 255) / 256);
     hipError_t e;
     if (rnn) {

@@ -7,6 +7,18 @@
 
 namespace dspark {
 
+// Test and measurement switches of the library (dspark_set_switch): read
+// once from the environment (DSPARK_DRAFT_KERNEL=steps, DSPARK_RNN_CELL_VALU,
+// DSPARK_BARRIER_SPINS) the first time they are needed, replaced only by an
+// explicit dspark_set_switch call.
+struct Switches {
+  int force_per_step;      // 1: the per-step draft schedule for every shape
+  int rnn_cell_valu;       // 1: the RNN head's per-step schedule with the vector-ALU cell
+  uint32_t barrier_spins;  // polls before a cross-workgroup wait gives up
+  int draft_kernel;        // persistent draft: 0 pipelined, 1 one grid barrier per step
+};
+Switches switches();
+
 enum { kRowsDraft = 0, kRowsVerifyPacked = 1, kRowsVerifyDense = 2, kRowsAll = 3 };
 enum { kModeSample = 0, kModeGreedy = 1, kModeResid = 2 };
 

@@ -464,7 +464,7 @@ hipError_t launch_rnn_cell(const RnnArgs& a, int k, hipStream_t st) {
                    ((size_t)(2 * a.rank + a.d) * es) % 16 == 0;
   const bool mfma_ok = a.w_bf16 && vec && a.rank <= 4 * kCellIt * 32 &&
                        (reinterpret_cast<uintptr_t>(a.W1) & 15) == 0 &&
-                       std::getenv("DSPARK_RNN_CELL_VALU") == nullptr;
+                       !switches().rnn_cell_valu;
   if (mfma_ok) {
     hipLaunchKernelGGL(k_rnn_cell_mfma, grid, dim3(256), 0, st, a, k);
   } else if (a.w_bf16) {

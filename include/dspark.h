@@ -6,10 +6,10 @@
  *  [P3] papercache.org summary of "DSpark: Confidence-Scheduled Speculative
  *       Decoding with Semi-Autoregressive Generation" (arXiv 2607.05147).
  *  [P1] backyes.github.io "MTP algorithm survey", section 2.2 (rejection sampling).
- *  [P2] bevisy.github.io DeepSpec analysis, section 2.2 (DFlash = rank 0).
+ *  [P2] bevisy.github.io DeepSpec analysis, section 2.2 (DFlash = rank 0) and
+ *       section 5.4 (DSpark in SGLang): verify modes static / compact /
+ *       cap-accept, ragged verify padded to captured graph tiers.
  *  [P4] modelscope/CSDN DSpark article, section 3.3 (flatten + marker tensors).
- *       Section 5.4 of that page (DSpark in SGLang): verify modes static /
- *       compact / cap-accept, ragged verify padded to captured graph tiers.
  *
  * Conventions shared by every entry point
  *  - Every pointer is a DEVICE pointer unless marked (host).  The caller owns
@@ -20,8 +20,9 @@
  *    DSPARK_E_HIP means a kernel launch failed; the stream state is then the
  *    HIP runtime's.
  *  - The library keeps no state between calls other than a per-device cache
- *    of immutable device facts (compute-unit count, occupancy).  Calls that
- *    share a workspace must be ordered on one stream (or otherwise serialised).
+ *    of immutable device facts (compute-unit count, occupancy) and the test
+ *    switches of dspark_set_switch.  Calls that share a workspace must be
+ *    ordered on one stream (or otherwise serialised).
  *  - R = requests in the batch, gamma = block size (draft positions per
  *    request), V = vocabulary, r = Markov rank, d = backbone hidden size,
  *    T = sampling temperature (T == 0 selects greedy decoding).
@@ -67,6 +68,33 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 #define DSPARK_FLAG_TIER     16u   /* a tiered pack's total exceeded every tier
                                       (N_pad = N)                                 */
 
+/*
+ * (host) Test and measurement switches.  They select among schedules that give
+ * the same results (or bound a wait); they never change what is computed.
+ * Their start values are read once from the environment, the first time the
+ * library needs them: DSPARK_DRAFT_KERNEL=steps (FORCE_PER_STEP = 1),
+ * DSPARK_DRAFT_KERNEL=barrier (DRAFT_KERNEL = 1), DSPARK_RNN_CELL_VALU set
+ * (RNN_CELL_VALU = 1), DSPARK_BARRIER_SPINS=n (BARRIER_SPINS = n).  Apart from
+ * the per-device cache of device facts these switches are the library's only
+ * state; set them between rounds, not while calls are being enqueued on
+ * another thread.
+ *   FORCE_PER_STEP  1: the per-step draft schedule for every shape
+ *   RNN_CELL_VALU   1: the RNN head on the per-step schedule with the
+ *                   vector-ALU cell
+ *   BARRIER_SPINS   polls before a cross-workgroup wait of a persistent draft
+ *                   launch gives up (DSPARK_FLAG_BARRIER); 0 = the default 2^24
+ *   DRAFT_KERNEL    persistent Markov draft: 0 request groups pipelined across
+ *                   steps (default), 1 one grid barrier per step
+ * dspark_set_switch returns DSPARK_E_INVALID for an unknown key or value;
+ * dspark_get_switch returns -1 for an unknown key.
+ */
+#define DSPARK_SWITCH_FORCE_PER_STEP 1
+#define DSPARK_SWITCH_RNN_CELL_VALU  2
+#define DSPARK_SWITCH_BARRIER_SPINS  3
+#define DSPARK_SWITCH_DRAFT_KERNEL   4
+dspark_status dspark_set_switch(int key, int64_t value);
+int64_t dspark_get_switch(int key);
+
 /* (host) Bytes of workspace every entry point below needs for these sizes. */
 size_t dspark_workspace_bytes(int R, int gamma, int V, int r, int d);
 
@@ -109,9 +137,8 @@ dspark_status dspark_get_status(const void* ws, size_t ws_bytes, uint32_t* flags
  * cooperative launch that keeps W2 on chip (grid barriers between steps;
  * DSPARK_FLAG_BARRIER reports a barrier that gave up waiting); other shapes
  * run two launches per step, and r == 0 (independent positions) two launches
- * in all.  The schedules give the same results.  The
- * environment variable DSPARK_DRAFT_KERNEL=steps forces the per-step
- * schedule.
+ * in all.  The schedules give the same results.  DSPARK_SWITCH_FORCE_PER_STEP
+ * forces the per-step schedule.
  */
 dspark_status dspark_draft_markov(int R, int gamma, int V, int r, float T,
                                   uint64_t seed, uint64_t round,
@@ -171,7 +198,9 @@ dspark_status dspark_confidence(int R, int gamma, int d, int r, int V,
  * B > N_max counts as Theta = 0 (capacity exceeded).
  *   c          [R][gamma]   confidences
  *   sps        [N_max+1]    SPS(B), engine steps per second at batch B (double)
- *   enabled    0: ell = gamma for every request (static verification)
+ *   enabled    0: ell = gamma for every request (static verification; then
+ *              N_max must hold the whole block, N_max >= R (gamma + 1), else
+ *              DSPARK_E_INVALID)
  *   ell        out [R]      scheduled verify lengths in [0, gamma]
  *   a          out nullable [R][gamma]  survival products
  *   N_out      out nullable (device scalar)  sum_i (1 + ell_i)
@@ -409,8 +438,8 @@ size_t dspark_rnn_workspace_bytes(int R, int gamma, int V, int r, int d);
  * step (DSPARK_FLAG_BARRIER as there).  Other shapes run three launches per
  * step: the cell (MFMA with the fp32 state split into exact bf16 parts for
  * bf16 weights, fp32 vector ALU otherwise), the per-chunk statistics and the
- * pick.  The schedules give the same results.  DSPARK_DRAFT_KERNEL=steps
- * forces the per-step schedule, DSPARK_RNN_CELL_VALU (any value) the per-step
+ * pick.  The schedules give the same results.  DSPARK_SWITCH_FORCE_PER_STEP
+ * forces the per-step schedule, DSPARK_SWITCH_RNN_CELL_VALU the per-step
  * schedule with the vector-ALU cell.
  */
 dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, int d, float T,
@@ -460,11 +489,15 @@ dspark_status dspark_verify_cap_accept_features(int R, int gamma, int V, int r, 
 
 /*
  * Instrumented dspark_draft_rnn for performance measurement: identical
- * results; additionally records ev_begin[k-1] / ev_end[k-1] on `stream`
- * around the per-chunk statistics kernel of step k (the draft's dominant
- * kernel) and sets *n_timed = gamma.
+ * results; additionally records events on `stream` around the draft's
+ * dominant kernel.  With the persistent schedule (cell, statistics and pick
+ * of all gamma steps in one cooperative launch) that is ev_begin[0] /
+ * ev_end[0] around the launch and *n_timed = 1; with the per-step schedule
+ * ev_begin[k-1] / ev_end[k-1] bracket the per-chunk statistics kernel of
+ * step k and *n_timed = gamma.
  *   ev_begin, ev_end  (host) arrays of gamma events created by the caller
  *   n_timed           (host, nullable) number of event pairs recorded
+ * Returns DSPARK_E_INVALID if either array is null.
  */
 dspark_status dspark_draft_rnn_profiled(int R, int gamma, int V, int r, int d, float T,
                                         uint64_t seed, uint64_t round,

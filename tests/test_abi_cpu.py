@@ -111,6 +111,10 @@ def test_confidence_schedule_pack_verify_checks():
     assert sched(N_max=3) == INVALID                     # N_max < R
     assert sched(R=1024, g=17, N_max=10**6) == UNSUPPORTED   # R * gamma > 16384
     assert sched(c=None) == INVALID
+    # static verification needs the whole block within N_max
+    stat = lambda N_max: lib.dspark_prefix_schedule(4, 4, FAKE, FAKE, N_max, 0, FAKE, None, None,
+                                                     None, None)
+    assert stat(19) == INVALID and stat(4) == INVALID
     asch = lambda R=4, g=4, N_max=100, kin=FAKE, kp=FAKE, ell=FAKE: lib.dspark_async_schedule(
         R, g, FAKE, FAKE, N_max, kin, kp, ell, None, None, None, None, None)
     assert asch(R=-1) == INVALID
@@ -183,3 +187,28 @@ def test_synthetic_configs_shapes():
 def test_binding_names_match_abi(fn):
     assert callable(getattr(D, fn))
     assert f"dspark_{fn}" in declared()
+
+
+def test_switches_set_get_and_reject():
+    """The test switches: known keys round-trip, unknown keys and values are
+    rejected, and every switch is restored."""
+    keys = [L.SWITCH_FORCE_PER_STEP, L.SWITCH_RNN_CELL_VALU, L.SWITCH_BARRIER_SPINS,
+            L.SWITCH_DRAFT_KERNEL]
+    saved = [L.get_switch(k) for k in keys]
+    try:
+        for k in keys:
+            assert L.get_switch(k) >= 0
+        L.set_switch(L.SWITCH_FORCE_PER_STEP, 1)
+        assert L.get_switch(L.SWITCH_FORCE_PER_STEP) == 1
+        L.set_switch(L.SWITCH_BARRIER_SPINS, 12345)
+        assert L.get_switch(L.SWITCH_BARRIER_SPINS) == 12345
+        lib = L.load()
+        assert lib.dspark_set_switch(L.SWITCH_FORCE_PER_STEP, 2) == INVALID
+        assert lib.dspark_set_switch(L.SWITCH_DRAFT_KERNEL, -1) == INVALID
+        assert lib.dspark_set_switch(L.SWITCH_BARRIER_SPINS, -5) == INVALID
+        assert lib.dspark_set_switch(99, 0) == INVALID
+        assert lib.dspark_get_switch(99) == -1
+    finally:
+        for k, v in zip(keys, saved):
+            L.set_switch(k, v)
+    assert [L.get_switch(k) for k in keys] == saved
