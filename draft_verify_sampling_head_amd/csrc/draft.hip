@@ -430,12 +430,28 @@ __device__ __forceinline__ void merge_greedy(EpiState& st) {
   st.m = v0;
   st.bi = i0;
 }
+// U value e (0-7) of a 16-byte piece of eight bf16 entries
+__device__ __forceinline__ float u_piece(const uint4& q, int e) {
+  const uint32_t w = (e >> 1) == 0 ? q.x : (e >> 1) == 1 ? q.y : (e >> 1) == 2 ? q.z : q.w;
+  return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+// Units 0 and 1 first add the lane's U values to the accumulators: the bias
+// contraction accumulates from zero (its terms are small), and the base
+// logits join it in one rounding, x = fl(U + bias).  Seeding the
+// accumulators with U instead would round a large value after every k-step.
 template <bool GREEDY, bool MASK>
-__device__ __forceinline__ void epi_unit(int u, EpiState& st, const f32x4_t (&acc)[4],
+__device__ __forceinline__ void epi_unit(int u, EpiState& st, f32x4_t (&acc)[4], const uint4 (&un)[2],
                                          const bool (&uok)[2], float s2, int gbase) {
   auto xv = [&](int j) __attribute__((always_inline)) {
     return (!MASK || uok[j >> 3]) ? acc[j >> 2][j & 3] : -INFINITY;
   };
+  if (u == 0 || u == 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 8 * u + e;
+      acc[j >> 2][j & 3] += u_piece(un[u], e);
+    }
+  }
   if (u == 0) {
     float m = fmaxf(fmaxf(xv(0), xv(1)), xv(2));
     m = fmaxf(fmaxf(m, xv(3)), xv(4));
@@ -478,15 +494,24 @@ __device__ __forceinline__ void epi_unit(int u, EpiState& st, const f32x4_t (&ac
   }
 }
 
-// One pipelined tile step: the MFMA chain of the next tile (acc_next, already
-// seeded) interleaved k-step by k-step with the epilogue units of the current
-// tile (acc_cur).  B operands come through a three-deep register ring.
-template <int KT, bool GREEDY, bool MASK>
+__device__ __forceinline__ void zero_acc(f32x4_t (&acc)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// One pipelined tile step: the MFMA chain of the next tile (acc_next, zeroed)
+// interleaved k-step by k-step with the epilogue units of the current tile
+// (acc_cur, whose U values are in un).  Once units 0 and 1 have consumed un,
+// the U pieces of tile `reload` are loaded into it.  B operands come through
+// a three-deep register ring.
+template <int KT, bool GREEDY, bool MASK, typename US>
 __device__ __forceinline__ void mfma_with_epilogue(f32x4_t (&acc_next)[4], const bf16x8_t (&Af)[4][KT],
-                                                   const uint4* erow, const f32x4_t (&acc_cur)[4],
+                                                   const uint4* erow, f32x4_t (&acc_cur)[4],
+                                                   uint4 (&un)[2], const US& us, int reload,
                                                    const bool (&uok)[2], float s2, int gbase,
                                                    EpiState& st) {
   constexpr int NU = 8;                     // epilogue units
+  constexpr int KT_RELOAD = KT / NU;        // the k-step whose units include unit 1
   bf16x8_t Bq[3];
   Bq[0] = __builtin_bit_cast(bf16x8_t, erow[0]);
   if (KT > 1) Bq[1] = __builtin_bit_cast(bf16x8_t, erow[4]);
@@ -498,30 +523,19 @@ __device__ __forceinline__ void mfma_with_epilogue(f32x4_t (&acc_next)[4], const
     for (int mt = 0; mt < 4; ++mt)
       acc_next[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[mt][kt], Bq[kt % 3], acc_next[mt], 0, 0, 0);
 #pragma unroll
-    for (int u = kt * NU / KT; u < (kt + 1) * NU / KT; ++u) epi_unit<GREEDY, MASK>(u, st, acc_cur, uok, s2, gbase);
+    for (int u = kt * NU / KT; u < (kt + 1) * NU / KT; ++u)
+      epi_unit<GREEDY, MASK>(u, st, acc_cur, un, uok, s2, gbase);
+    if (kt == KT_RELOAD) us.load(un, reload);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // The whole epilogue of a tile without MFMAs (last tile of a group).
 template <bool GREEDY, bool MASK>
-__device__ __forceinline__ void epilogue_all(EpiState& st, const f32x4_t (&acc)[4], const bool (&uok)[2],
-                                             float s2, int gbase) {
+__device__ __forceinline__ void epilogue_all(EpiState& st, f32x4_t (&acc)[4], const uint4 (&un)[2],
+                                             const bool (&uok)[2], float s2, int gbase) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) epi_unit<GREEDY, MASK>(u, st, acc, uok, s2, gbase);
-}
-
-// Seed four 4-value accumulators with 16 bf16 values (two 16-byte pieces).
-__device__ __forceinline__ void seed_acc(f32x4_t (&acc)[4], const uint4 (&un)[2]) {
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const uint32_t wd[4] = {un[q].x, un[q].y, un[q].z, un[q].w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = 8 * q + e;
-      acc[j >> 2][j & 3] = (e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]);
-    }
-  }
+  for (int u = 0; u < 8; ++u) epi_unit<GREEDY, MASK>(u, st, acc, un, uok, s2, gbase);
 }
 
 // U pieces of one wave for one row group, tile by tile.  The lane's two 8-entry
@@ -560,10 +574,10 @@ struct UStream {
 
 // Phase A of one wave for one row group: 16-row tiles, software-pipelined so
 // that while the MFMAs of tile i+1 run, the vector ALU works on the epilogue
-// of tile i.  U is prefetched two tiles ahead; the caller has already issued
-// the loads of tiles 0 and 1 (ua, ub) and waited for them.  The statistics of
-// every tile row over the wave's 64 entries go to HS[row][wave] (rows past
-// `rows`, in the ragged last tile, are never read).
+// of tile i (which adds U to the bias).  U is prefetched about two tiles
+// ahead; the caller has already issued the loads of tiles 0 and 1 (ua, ub).
+// The statistics of every tile row over the wave's 64 entries go to
+// HS[row][wave] (rows past `rows`, in the ragged last tile, are never read).
 template <int KT, int ROWP, bool GREEDY, bool MASK>
 __device__ __forceinline__ void slice_tiles(const bf16x8_t (&Af)[4][KT], const uint4* E, float2* HS,
                                             const UStream& us, uint4 (&ua)[2], uint4 (&ub)[2], int wslice,
@@ -583,36 +597,34 @@ __device__ __forceinline__ void slice_tiles(const bf16x8_t (&Af)[4][KT], const u
     st.m = -INFINITY; st.s0 = 0.f; st.s1 = 0.f; st.m2 = -FLT_MAX; st.bi = 0x7FFFFFFF;
     return st;
   };
-  // epilogue of tile i (acc_cur) with the MFMAs of tile i+1 (acc_next, seeded
-  // from un, which is then refilled with tile i+3)
+  // epilogue of tile i (acc_cur, its U values in un, which is then refilled
+  // with tile i+2) with the MFMAs of tile i+1 (acc_next, from zero)
   auto step2 = [&](f32x4_t (&acc_cur)[4], f32x4_t (&acc_next)[4], uint4 (&un)[2], int i)
       __attribute__((always_inline)) {
-    seed_acc(acc_next, un);
-    us.load(un, i + 3);
+    zero_acc(acc_next);
     EpiState st = fresh();
-    mfma_with_epilogue<KT, GREEDY, MASK>(acc_next, Af, E + (16 * (i + 1) + ln) * ROWP + lg, acc_cur, uok,
-                                         s2, gbase, st);
+    mfma_with_epilogue<KT, GREEDY, MASK>(acc_next, Af, E + (16 * (i + 1) + ln) * ROWP + lg, acc_cur, un,
+                                         us, i + 2, uok, s2, gbase, st);
     store(i, st);
   };
-  auto last = [&](const f32x4_t (&acc)[4], int i) __attribute__((always_inline)) {
+  auto last = [&](f32x4_t (&acc)[4], const uint4 (&un)[2], int i) __attribute__((always_inline)) {
     EpiState st = fresh();
-    epilogue_all<GREEDY, MASK>(st, acc, uok, s2, gbase);
+    epilogue_all<GREEDY, MASK>(st, acc, un, uok, s2, gbase);
     store(i, st);
   };
   f32x4_t accA[4], accB[4];
-  seed_acc(accA, ua);                         // tile 0
-  us.load(ua, 2);
+  zero_acc(accA);                             // tile 0 (U(0) in ua, U(1) in ub)
   tile_mfma<KT>(accA, Af, E + ln * ROWP + lg);
   int i = 0;
   for (; i + 2 < ntiles; i += 2) {
-    step2(accA, accB, ub, i);                 // epilogue i, MFMA i+1 (seeded from ub)
-    step2(accB, accA, ua, i + 1);             // epilogue i+1, MFMA i+2 (seeded from ua)
+    step2(accA, accB, ua, i);                 // epilogue i (U in ua), MFMA i+1
+    step2(accB, accA, ub, i + 1);             // epilogue i+1 (U in ub), MFMA i+2
   }
   if (i + 1 < ntiles) {
-    step2(accA, accB, ub, i);
-    last(accB, i + 1);
+    step2(accA, accB, ua, i);
+    last(accB, ub, i + 1);
   } else {
-    last(accA, i);
+    last(accA, ua, i);
   }
 }
 
@@ -1264,9 +1276,12 @@ void k_resid_stats(ResidArgs A) {
         cur = nxt;
         if (i + 1 < ntiles) load_row(nxt, i + 1);
         f32x4_t acc[4];
-        seed_acc(acc, cur.u);
+        zero_acc(acc);
         const int rl = 16 * i + ln;
         tile_mfma<KT>(acc, Af, E + rl * ROWP + lg);
+        // x = fl(U + bias): the base logits join the bias in one rounding
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j >> 2][j & 3] += u_piece(cur.u[j >> 3], j & 7);
         const float lrt2 = cur.nt.y * kLog2e;
         float S = 0.f;
 #pragma unroll
