@@ -29,7 +29,7 @@ EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
            "dspark_sts_workspace_bytes", "dspark_confidence_logits", "dspark_rnn_workspace_bytes",
            "dspark_draft_rnn", "dspark_verify_features", "dspark_draft_rnn_profiled",
            "dspark_acceptance_rate_features", "dspark_verify_cap_accept_features",
-           "dspark_set_switch", "dspark_get_switch")
+           "dspark_set_switch", "dspark_get_switch", "dspark_draft_markov_noalloc")
 SWITCH_FORCE_PER_STEP, SWITCH_RNN_CELL_VALU, SWITCH_BARRIER_SPINS, SWITCH_DRAFT_KERNEL = 1, 2, 3, 4
 
 
@@ -85,6 +85,8 @@ def load():
     L.dspark_verify_features.argtypes = L.dspark_verify.argtypes
     L.dspark_acceptance_rate_features.argtypes = L.dspark_acceptance_rate.argtypes
     L.dspark_verify_cap_accept_features.argtypes = L.dspark_verify_cap_accept.argtypes
+    L.dspark_draft_markov_noalloc.argtypes = [i32, i32, i32, i32, f32, u64, u64, P, i32, P, P, i32,
+                                              P, P, P, P, P, P, P]
     L.dspark_set_switch.argtypes = [i32, C.c_int64]
     L.dspark_get_switch.argtypes = [i32]
     L.dspark_get_switch.restype = C.c_int64
@@ -166,6 +168,20 @@ def draft_markov(U, W1, W2t, x0, T, seed, rnd, x, logp_d, lse_d, ws, margin=None
                                       _ptr(logp_d), _ptr(lse_d), _ptr(margin), _ptr(ws),
                                       ws.numel(), _stream(stream))
     _check("dspark_draft_markov", code)
+
+
+def draft_markov_noalloc(U, W1, W2t, x0, T, seed, rnd, x, logp_d, lse_d, flags=None, margin=None,
+                         stream=None):
+    """dspark_draft_markov without a workspace: the library's static device
+    scratch holds the draft's intermediate state (calls on one GPU must not
+    overlap).  flags: nullable device uint32 tensor receiving the status word."""
+    R, gamma, V = U.shape
+    r = 0 if W1 is None else int(W1.shape[1])
+    code = load().dspark_draft_markov_noalloc(R, gamma, V, r, float(T), seed, rnd, _ptr(U), _dt(U),
+                                              _ptr(W1), _ptr(W2t), _dt(W1), _ptr(x0), _ptr(x),
+                                              _ptr(logp_d), _ptr(lse_d), _ptr(margin), _ptr(flags),
+                                              _stream(stream))
+    _check("dspark_draft_markov_noalloc", code)
 
 
 def draft_markov_profiled(U, W1, W2t, x0, T, seed, rnd, x, logp_d, lse_d, ws, ev_begin, ev_end,

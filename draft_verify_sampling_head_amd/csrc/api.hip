@@ -153,8 +153,8 @@ static dspark_status draft_impl(int R, int gamma, int V, int r, float T, uint64_
   if (!aligned16(ws)) return DSPARK_E_INVALID;
   if (ws_bytes < ws_layout(R, gamma, V).total) return DSPARK_E_WORKSPACE;
   return hip_status(launch_draft(R, gamma, V, r, T, seed, round, U, U_dt == DSPARK_BF16, W1, W2t,
-                                 W_dt == DSPARK_BF16, x0, x, logp_d, lse_d, margin, ws, stream,
-                                 ev_begin, ev_end, n_timed));
+                                 W_dt == DSPARK_BF16, x0, x, logp_d, lse_d, margin,
+                                 draft_ws(ws, R, gamma, V), stream, ev_begin, ev_end, n_timed));
 }
 
 dspark_status dspark_draft_markov(int R, int gamma, int V, int r, float T, uint64_t seed,
@@ -217,8 +217,8 @@ static dspark_status draft_rnn_impl(int R, int gamma, int V, int r, int d, float
   a.feat = feat;
   a.status = reinterpret_cast<uint32_t*>(w + ws_layout(R, gamma, V).header);
   return hip_status(launch_draft(R, gamma, V, r, T, seed, round, U, U_dt == DSPARK_BF16, W1, W2t,
-                                 W_dt == DSPARK_BF16, x0, x, logp_d, lse_d, margin, ws, stream,
-                                 ev_begin, ev_end, n_timed, &a));
+                                 W_dt == DSPARK_BF16, x0, x, logp_d, lse_d, margin,
+                                 draft_ws(ws, R, gamma, V), stream, ev_begin, ev_end, n_timed, &a));
 }
 
 dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, int d, float T, uint64_t seed,

@@ -1438,13 +1438,11 @@ __global__ void k_draft_prep(uint32_t* flags, int nflags, int32_t* x, const int3
 hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,
                         const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
                         const int32_t* x0, int32_t* x, float* logp_d, float* lse_d, float* margin,
-                        void* ws, hipStream_t st, hipEvent_t* ev_begin, hipEvent_t* ev_end,
+                        const DraftWs& ws, hipStream_t st, hipEvent_t* ev_begin, hipEvent_t* ev_end,
                         int* n_timed, const RnnArgs* rnn) {
-  const WsLayout L = ws_layout(R, gamma, V);
-  char* w = reinterpret_cast<char*>(ws);
-  uint32_t* status = reinterpret_cast<uint32_t*>(w + L.header);
-  float2* Lc = reinterpret_cast<float2*>(w + L.draft_l);
-  int* Ic = reinterpret_cast<int*>(w + L.draft_i);
+  uint32_t* status = ws.status;
+  float2* Lc = reinterpret_cast<float2*>(ws.draft_l);
+  int* Ic = reinterpret_cast<int*>(ws.draft_i);
   const int nch = (V + kChunk - 1) / kChunk;
   const bool greedy = (T == 0.f);
   const float scale2 = greedy ? 1.f : kLog2e / T;
@@ -1477,7 +1475,7 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     P.p = p;
     P.scale2 = scale2;
     P.nslice = (V + kPSlice - 1) / kPSlice;
-    P.bar = reinterpret_cast<uint32_t*>(w + L.bar);
+    P.bar = ws.bar;
     P.spin_limit = sw.barrier_spins ? sw.barrier_spins : kBarrierSpins;
     const int prep_blocks = (int)std::min<int64_t>(64, ((int64_t)R * (gamma + 1) + 255) / 256);
     hipError_t e;
@@ -1519,14 +1517,14 @@ hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t see
     else if (u_bf16)      { if (greedy) DSPARK_PICK(uint16_t, float, true, NB_);    else DSPARK_PICK(uint16_t, float, false, NB_); }    \
     else if (w_bf16)      { if (greedy) DSPARK_PICK(float, uint16_t, true, NB_);    else DSPARK_PICK(float, uint16_t, false, NB_); }    \
     else                  { if (greedy) DSPARK_PICK(float, float, true, NB_);       else DSPARK_PICK(float, float, false, NB_); }
-  if (rank == 0 && !rnn) {
+  if (rank == 0 && !rnn && ws.rows_l != nullptr) {
     // rank 0 (no transition bias): the positions are independent, so the
     // statistics of all R gamma rows of U are one launch (into the target-row
     // statistics region, unused until the verify) and the picks another
     RowStatsArgs a{};
     a.base = U; a.kind = kRowsAll; a.R = R; a.gamma = gamma; a.k = 0; a.V = V; a.nch = nch;
     a.nrows_cap = R * gamma; a.scale2 = scale2; a.vec_ok = u_vec;
-    a.L = reinterpret_cast<float2*>(w + L.ver_l); a.I = reinterpret_cast<int*>(w + L.ver_i);
+    a.L = reinterpret_cast<float2*>(ws.rows_l); a.I = reinterpret_cast<int*>(ws.rows_i);
     a.status = status;
     hipError_t e;
     if (ev_begin && (e = hipEventRecord(ev_begin[0], st)) != hipSuccess) return e;

@@ -153,10 +153,11 @@ hipError_t launch_confidence(const ConfArgs& a, bool h_bf16, bool w1_bf16, bool 
                              hipStream_t st);
 hipError_t launch_pack(const PackArgs& a, hipStream_t st);
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t st);
+struct DraftWs;
 hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,
                         const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
                         const int32_t* x0, int32_t* x, float* logp_d, float* lse_d, float* margin,
-                        void* ws, hipStream_t st, hipEvent_t* ev_begin = nullptr,
+                        const DraftWs& ws, hipStream_t st, hipEvent_t* ev_begin = nullptr,
                         hipEvent_t* ev_end = nullptr, int* n_timed = nullptr,
                         const RnnArgs* rnn = nullptr);
 bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void* U,

@@ -19,8 +19,12 @@ struct WsLayout {
   size_t lse_t;        // float2 [R*(gamma+1)]       target-row (max, log-normaliser above it)
   size_t rej;          // int32  [R][4]   residual work list: request, position, row, pad
   size_t bar;          // uint32 [1024] grid-barrier flags of the persistent draft, one per workgroup
+  size_t rec;          // 16-byte [2][R][ceil(V/512)] per-slice records of the pipelined draft
   size_t total;
 };
+
+// Number of 512-entry vocabulary slices (one per workgroup of the persistent draft).
+inline size_t ws_nslice(int V) { return ((size_t)V + 511) / 512; }
 
 inline size_t ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -37,8 +41,58 @@ inline WsLayout ws_layout(int R, int gamma, int V) {
   L.lse_t = off;   off += ws_align(rows_v * 8);
   L.rej = off;     off += ws_align((size_t)R * 16);
   L.bar = off;     off += ws_align(4 * 1024);
+  L.rec = off;     off += ws_align(2 * (size_t)R * ws_nslice(V) * 16);
   L.total = off;
   return L;
+}
+
+// The regions the draft uses, as pointers.  rows_l / rows_i (statistics of
+// all R gamma rows at rank 0, one launch) may be null: the rank-0 draft then
+// runs one statistics launch per position in draft_l / draft_i.
+struct DraftWs {
+  uint32_t* status;    // status word
+  void* draft_l;       // float2 [R][nch]
+  void* draft_i;       // int32  [R][nch]
+  uint32_t* bar;       // uint32 [1024] grid-barrier flags
+  void* rec;           // 16-byte [2][R][ceil(V/512)]
+  void* rows_l;        // nullable float2 [R*gamma][nch]
+  void* rows_i;        // nullable int32  [R*gamma][nch]
+};
+
+inline DraftWs draft_ws(void* ws, int R, int gamma, int V) {
+  const WsLayout L = ws_layout(R, gamma, V);
+  char* w = reinterpret_cast<char*>(ws);
+  DraftWs d;
+  d.status = reinterpret_cast<uint32_t*>(w + L.header);
+  d.draft_l = w + L.draft_l;
+  d.draft_i = w + L.draft_i;
+  d.bar = reinterpret_cast<uint32_t*>(w + L.bar);
+  d.rec = w + L.rec;
+  d.rows_l = w + L.ver_l;      // the target-row statistics, unused until the verify
+  d.rows_i = w + L.ver_i;
+  return d;
+}
+
+// The draft alone in a compact layout (no rank-0 all-rows region):
+// header, draft_l, draft_i, barrier flags, records.  Returns the bytes needed.
+inline size_t draft_ws_compact(char* base, int R, int V, DraftWs* d) {
+  const size_t nch = ((size_t)V + 127) / 128;
+  size_t off = 0;
+  const size_t h = off;  off += ws_align(256);
+  const size_t l = off;  off += ws_align((size_t)R * nch * 8);
+  const size_t i = off;  off += ws_align((size_t)R * nch * 4);
+  const size_t b = off;  off += ws_align(4 * 1024);
+  const size_t r = off;  off += ws_align(2 * (size_t)R * ws_nslice(V) * 16);
+  if (d) {
+    d->status = reinterpret_cast<uint32_t*>(base + h);
+    d->draft_l = base + l;
+    d->draft_i = base + i;
+    d->bar = reinterpret_cast<uint32_t*>(base + b);
+    d->rec = base + r;
+    d->rows_l = nullptr;
+    d->rows_i = nullptr;
+  }
+  return off;
 }
 
 // RNN draft head: the shared layout, then the h part of the cell's projection

@@ -148,6 +148,34 @@ dspark_status dspark_draft_markov(int R, int gamma, int V, int r, float T,
                                   float* margin, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * dspark_draft_markov for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument; the draft's scratch (status word, chunk statistics,
+ * barrier flags, per-slice records) lives in a static device array of
+ * DSPARK_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends.  The call allocates and frees nothing.  Same kernels and
+ * results as dspark_draft_markov; rank 0 takes one statistics launch per
+ * position (the all-rows region of the workspace is not there).
+ *   flags   out nullable (device uint32): the DSPARK_FLAG_* word of this call,
+ *           written when the stream reaches the end of the call
+ *   other arguments as for dspark_draft_markov
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller.  The array keeps the last call's contents; the call clears what has
+ * to start at zero.  Returns DSPARK_E_WORKSPACE when the shape needs more than
+ * the array: 256 + 12 R ceil(V/128) + 4096 + 32 R ceil(V/512) bytes, each term
+ * rounded up to 256.
+ */
+#define DSPARK_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+dspark_status dspark_draft_markov_noalloc(int R, int gamma, int V, int r, float T,
+                                          uint64_t seed, uint64_t round,
+                                          const void* U, dspark_dtype U_dt,
+                                          const void* W1, const void* W2t, dspark_dtype W_dt,
+                                          const int32_t* x0, int32_t* x, float* logp_d,
+                                          float* lse_d, float* margin, uint32_t* flags,
+                                          hipStream_t stream);
+
+/*
  * Instrumented dspark_draft_markov for performance measurement: identical
  * results; additionally records events on `stream` around the draft's
  * dominant kernel.  With the persistent schedule (one cooperative launch for
