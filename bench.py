@@ -121,7 +121,8 @@ def stats_kernel_bytes(cfg):
 
 # (kernel, head) -> (sources it is built from, committed counter summary of
 # the headline workload R=256, gamma=16, V=129280, r=256)
-_PERSIST_SRC = ("draft.hip", "launch.hpp", "device_common.hpp", "sampling.hpp", "workspace.hpp")
+_PERSIST_SRC = ("draft.hip", "persist_common.hpp", "launch.hpp", "device_common.hpp", "sampling.hpp",
+                "workspace.hpp")
 KERNELS = {
     ("k_draft_persistent", "markov"): (_PERSIST_SRC,
                                        "k_draft_persistent_R256_g16_V129280_r256_counters.txt"),

@@ -25,7 +25,7 @@ void init_switches_locked() {
   if (g_sw_init) return;
   const char* dk = std::getenv("DSPARK_DRAFT_KERNEL");
   g_sw.force_per_step = (dk && std::strcmp(dk, "steps") == 0) ? 1 : 0;
-  g_sw.draft_kernel = (dk && std::strcmp(dk, "barrier") == 0) ? 1 : 0;
+  g_sw.draft_kernel = (dk && std::strcmp(dk, "pipe") == 0) ? 1 : 0;
   g_sw.rnn_cell_valu = std::getenv("DSPARK_RNN_CELL_VALU") ? 1 : 0;
   const char* sl = std::getenv("DSPARK_BARRIER_SPINS");
   g_sw.barrier_spins = sl ? (uint32_t)std::strtoul(sl, nullptr, 10) : 0u;

@@ -15,7 +15,7 @@ struct Switches {
   int force_per_step;      // 1: the per-step draft schedule for every shape
   int rnn_cell_valu;       // 1: the RNN head's per-step schedule with the vector-ALU cell
   uint32_t barrier_spins;  // polls before a cross-workgroup wait gives up
-  int draft_kernel;        // persistent draft: 0 pipelined, 1 one grid barrier per step
+  int draft_kernel;        // persistent draft: 0 one grid barrier per step, 1 pipelined
 };
 Switches switches();
 
@@ -154,6 +154,10 @@ hipError_t launch_confidence(const ConfArgs& a, bool h_bf16, bool w1_bf16, bool 
 hipError_t launch_pack(const PackArgs& a, hipStream_t st);
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t st);
 struct DraftWs;
+struct DraftPickArgs;
+bool launch_draft_pipe(const DraftPickArgs& p, bool greedy, float scale2, int grid,
+                       uint32_t spin_limit, const DraftWs& ws, hipStream_t st, hipEvent_t* ev_begin,
+                       hipEvent_t* ev_end, int* n_timed, hipError_t* err);
 hipError_t launch_draft(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,
                         const void* U, bool u_bf16, const void* W1, const void* W2t, bool w_bf16,
                         const int32_t* x0, int32_t* x, float* logp_d, float* lse_d, float* margin,

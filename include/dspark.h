@@ -73,7 +73,7 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
  * the same results (or bound a wait); they never change what is computed.
  * Their start values are read once from the environment, the first time the
  * library needs them: DSPARK_DRAFT_KERNEL=steps (FORCE_PER_STEP = 1),
- * DSPARK_DRAFT_KERNEL=barrier (DRAFT_KERNEL = 1), DSPARK_RNN_CELL_VALU set
+ * DSPARK_DRAFT_KERNEL=pipe (DRAFT_KERNEL = 1), DSPARK_RNN_CELL_VALU set
  * (RNN_CELL_VALU = 1), DSPARK_BARRIER_SPINS=n (BARRIER_SPINS = n).  Apart from
  * the per-device cache of device facts these switches are the library's only
  * state; set them between rounds, not while calls are being enqueued on
@@ -83,8 +83,9 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
  *                   vector-ALU cell
  *   BARRIER_SPINS   polls before a cross-workgroup wait of a persistent draft
  *                   launch gives up (DSPARK_FLAG_BARRIER); 0 = the default 2^24
- *   DRAFT_KERNEL    persistent Markov draft: 0 request groups pipelined across
- *                   steps (default), 1 one grid barrier per step
+ *   DRAFT_KERNEL    persistent Markov draft: 0 one grid barrier per step
+ *                   (default), 1 request groups pipelined across steps (no
+ *                   grid barrier; slower on the measured shapes)
  * dspark_set_switch returns DSPARK_E_INVALID for an unknown key or value;
  * dspark_get_switch returns -1 for an unknown key.
  */

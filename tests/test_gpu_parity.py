@@ -191,29 +191,39 @@ def switch():
 
 @pytest.fixture
 def draft_schedule(switch):
+    """None: the default persistent kernel (one grid barrier per step);
+    "pipe": the pipelined persistent kernel; "steps": one launch per step."""
     def set_to(name):
         switch(D._lib.SWITCH_FORCE_PER_STEP, 1 if name == "steps" else 0)
+        switch(D._lib.SWITCH_DRAFT_KERNEL, 1 if name == "pipe" else 0)
     return set_to
 
 
-@pytest.mark.parametrize("base,rank", [(2, 256), (1, 128), (3, 64)])
-def test_draft_schedules_both_match_oracle(draft_schedule, base, rank):
-    # the persistent (one cooperative launch) and per-step schedules of the
-    # draft on the same inputs: both must match the oracle
-    cfg = synth.scaled(synth.config(base), R=45, gamma=4, V=3072, d=32, rank=rank)
+@pytest.mark.parametrize("base,rank,R", [(2, 256, 45), (1, 128, 45), (3, 64, 45), (2, 256, 200),
+                                         (3, 128, 300), (2, 64, 1)])
+def test_draft_schedules_all_match_oracle(draft_schedule, base, rank, R):
+    # the persistent kernels (grid barrier, pipelined) and the per-step
+    # schedule of the draft on the same inputs: each must match the oracle.
+    # R = 45, 200, 300: one, two and three request groups of 128 with ragged
+    # last groups (odd tile counts padded to even)
+    cfg = synth.scaled(synth.config(base), R=R, gamma=4, V=3072, d=32, rank=rank)
     inp = synth.make_inputs(cfg, device="cpu")
     xs = []
-    for name in (None, "steps"):
+    for name in (None, "pipe", "steps"):
         draft_schedule(name)
         buf, _ = run_and_check(cfg, inp)
         xs.append(n(buf.x))
     # decisions agree except where the oracle flags a near-tie
-    assert (xs[0] != xs[1]).mean() <= 0.01
+    for other in xs[1:]:
+        assert (xs[0] != other).mean() <= 0.01
 
 
-def test_barrier_wait_is_bounded(switch):
-    # a one-poll limit on the persistent draft's grid barriers: the launch must
-    # still finish; a barrier that gave up is reported through the status word
+@pytest.mark.parametrize("kernel", [0, 1], ids=["barrier", "pipe"])
+def test_barrier_wait_is_bounded(switch, kernel):
+    # a one-poll limit on the persistent draft's cross-workgroup waits: the
+    # launch must still finish; a wait that gave up is reported through the
+    # status word
+    switch(D._lib.SWITCH_DRAFT_KERNEL, kernel)
     switch(D._lib.SWITCH_BARRIER_SPINS, 1)
     cfg = synth.scaled(synth.config(2), R=64, gamma=4, V=4096, d=32)
     inp = to_dev(synth.make_inputs(cfg, device="cpu"))
@@ -657,6 +667,18 @@ def test_full_config2_all_requests():
 
 def test_full_config1_all_requests():
     _full(1, None)
+
+
+@pytest.mark.parametrize("idx,cell", [(2, {}), (1, {}), (4, dict(R=512, gamma=16, rank=64)),
+                                      (4, dict(R=32, gamma=8, rank=256))],
+                         ids=["config2", "config1", "R512-g16-r64", "R32-g8-r256"])
+def test_full_pipelined_kernel(draft_schedule, idx, cell):
+    """The pipelined persistent draft kernel at full sizes: the headline
+    workload and the greedy one on every request, two rank-sweep cells on the
+    requests _cell_reqs spreads over the batch."""
+    draft_schedule("pipe")
+    reqs = _cell_reqs(cell["R"]) if cell else None
+    _full(idx, reqs, **cell)
 
 
 def test_full_config3_sampled():
