@@ -141,16 +141,25 @@ struct PersistArgs {
 // four threads per entry (all W2t loads issued at once, the entry noise
 // computed while they are in flight), and the thread holding the in-chunk
 // winner writes the outputs.
+//
+// known_prev >= 0: x_{k-1} as the caller already holds it (the persistent
+// launch keeps each workgroup's last pick in LDS), with its W1 row already in
+// pl.E when e_loaded; the token then goes to *last_out too.  At the end only
+// LDS is synchronised: the stores need not have completed (other workgroups
+// poll for the token; a grid barrier waits for its workgroup's own stores).
 template <int KS, bool GREEDY>
 __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, float s2, BlockScratch& sh,
-                                           PickLds<2 * KS>& pl, const uint16_t* feat) {
+                                           PickLds<2 * KS>& pl, const uint16_t* feat,
+                                           int known_prev = -1, bool e_loaded = false,
+                                           int* last_out = nullptr) {
   constexpr int NT = kPThreads, TPE = NT / kChunk;
   constexpr int SEG = 2 * KS, NQ = SEG / TPE;   // 16-byte pieces of the rank per thread
   static_assert(kPMaxChunks <= 4 * NT, "four chunks per thread");
   const int tid = threadIdx.x;
   const int k = a.k;
   const int64_t xo = (int64_t)i * (a.gamma + 1);
-  int prev = (k == 1) ? a.x0[i] : ld_coh(a.x + xo + k - 1);
+  int prev = known_prev;
+  if (prev < 0 && !GREEDY) prev = (k == 1) ? a.x0[i] : ld_coh(a.x + xo + k - 1);
   if (prev < 0 || prev >= a.V) prev = 0;        // flagged when phase A read it
   const float2* Lr = a.L + (int64_t)i * a.nch;
   // chunk statistics of this thread's four chunks (all loads in flight)
@@ -166,7 +175,7 @@ __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, float 
       if (GREEDY) Iv[w] = ld_coh(a.I + (int64_t)i * a.nch + c);
     }
   }
-  if (!GREEDY && tid < SEG)
+  if (!GREEDY && tid < SEG && !e_loaded)
     pl.E[tid] = feat ? ld_coh16(feat + ((int64_t)i * a.gamma + (k - 1)) * a.rank + 8 * tid)
                      : *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.W1) +
                                                        (int64_t)prev * a.rank + 8 * tid);
@@ -185,6 +194,7 @@ __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, float 
       a.logp_d[o] = 0.f;
       a.lse_d[o] = v;
       if (a.margin) a.margin[o] = INFINITY;
+      if (last_out) *last_out = xk;
     }
   } else {
     // the chunk noise while the statistics are in flight
@@ -284,10 +294,10 @@ __device__ __forceinline__ void pick_row_p(const DraftPickArgs& a, int i, float 
       a.logp_d[o] = sv - lse_rel;
       a.lse_d[o] = lse;
       if (a.margin) a.margin[o] = gap;
+      if (last_out) *last_out = xk;
     }
   }
-  wait_vm_zero();
-  __syncthreads();                          // LDS slots and the W1 row are reused
+  lds_sync();                               // LDS slots and the W1 row are reused
 }
 
 // The persistent launch's pick as a launch of its own for the per-step
@@ -456,6 +466,10 @@ __device__ __forceinline__ void rnn_cell_tiles_p(const PersistArgs& P, int k, fl
   }
 }
 
+// Picks per workgroup whose last token stays in LDS (further picks, R above
+// this many times the grid, read it from x).
+constexpr int kLastPicks = 16;
+
 template <int KS, bool GREEDY, bool FEAT>
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_draft_persistent(PersistArgs P) {
   constexpr int SEG = 2 * KS;               // 16-byte segments per W1 row (rank / 8)
@@ -470,6 +484,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   __shared__ int PV[kPRows];
   __shared__ BlockScratch sh;
   __shared__ PickLds<SEG> pl;
+  __shared__ int lastx[kLastPicks];         // x_{k-1} of this workgroup's first picks
 
   DraftPickArgs a = P.p;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -494,6 +509,14 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   for (int q = 0; q < 2; ++q) uok[q] = wave_active && wslice + slice_entry(lg, 8 * q) + 8 <= V;
   const bool wave_full = wave_active && wslice + 64 <= V;
 
+  // the anchors of the requests this workgroup picks (i = b + j grid); its
+  // picks then keep them current, so a pick reads x_{k-1} from here
+  if (tid < kLastPicks) {
+    const int i = b + tid * (int)gridDim.x;
+    const int x0 = (i < R) ? a.x0[i] : 0;
+    lastx[tid] = (x0 < 0 || x0 >= V) ? 0 : x0;   // flagged when phase A reads it
+  }
+  __syncthreads();
   uint32_t epoch = 0;
   const int ngroups = (R + kPRows - 1) / kPRows;
   for (int k = 1; k <= a.gamma; ++k) {
@@ -582,12 +605,20 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       }
       __syncthreads();                      // E, PV and HS are rewritten by the next group
     }
+    // the W1 row of x_{k-1} for this workgroup's first pick: a direct-to-LDS
+    // load issued now completes with the barrier's own wait for the stores
+    const bool e_pre = !GREEDY && !FEAT && b < R;
+    if (e_pre && wv == 0 && lane < SEG) lds_dma16(W1 + (int64_t)lastx[0] * a.rank + 8 * lane, pl.E);
     grid_barrier(P.bar, ++epoch, P.spin_limit, a.status);
     // ================= phase B: the pick of step k, one request per workgroup.
     // No barrier follows: phase A of step k+1 waits for the tokens it reads,
     // and a token is written after its pick has read the chunk statistics
     // that phase A of step k+1 overwrites.
-    for (int i = b; i < R; i += gridDim.x) pick_row_p<KS, GREEDY>(a, i, s2, sh, pl, FEAT ? P.rfeat : nullptr);
+    for (int i = b, j = 0; i < R; i += gridDim.x, ++j) {
+      const bool known = !FEAT && j < kLastPicks;
+      pick_row_p<KS, GREEDY>(a, i, s2, sh, pl, FEAT ? P.rfeat : nullptr, known ? lastx[j] : -1,
+                             e_pre && j == 0, known ? &lastx[j] : nullptr);
+    }
   }
 }
 

@@ -644,8 +644,8 @@ struct PipeUStream {
     rt = min(rt, T - 1);
     const bool last = rt == T - 1;
     const char* p = base + kk * kbytes + rt * rbytes;
-    dst[0] = *reinterpret_cast<const uint4*>(p + (last ? l0 : v0));
-    dst[1] = *reinterpret_cast<const uint4*>(p + (last ? l1 : v1));
+    dst[0] = ld_stream16(p + (last ? l0 : v0));
+    dst[1] = ld_stream16(p + (last ? l1 : v1));
   }
 };
 

@@ -13,6 +13,15 @@ namespace dspark {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// A streamed 16-byte load (non-temporal: U is read once per step, so it is
+// not kept in the caches in place of W2t and W1 rows, which the picks and
+// gathers read again).
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 struct DraftPickArgs {
   int R, gamma, k, V, rank, nch;
@@ -450,8 +459,8 @@ struct UStream {
     const int t = min(i, ntiles - 1);
     const bool last = t == ntiles - 1;
     const char* p = tbase + t * tstep;
-    dst[0] = *reinterpret_cast<const uint4*>(p + (last ? l0 : v0));
-    dst[1] = *reinterpret_cast<const uint4*>(p + (last ? l1 : v1));
+    dst[0] = ld_stream16(p + (last ? l0 : v0));
+    dst[1] = ld_stream16(p + (last ? l1 : v1));
   }
 };
 
