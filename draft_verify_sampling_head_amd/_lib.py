@@ -14,7 +14,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdspark.so")
+# DSPARK_LIB_PATH: another build of this library (the CPU sanitizer tests load
+# a build with host-side AddressSanitizer/UBSan instrumentation)
+LIB_PATH = os.environ.get("DSPARK_LIB_PATH") or os.path.join(_PKG, "libdspark.so")
 
 F32, BF16 = 0, 1
 STATUS = {0: "DSPARK_OK", 1: "DSPARK_E_INVALID", 2: "DSPARK_E_UNSUPPORTED",

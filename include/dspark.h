@@ -57,7 +57,11 @@ typedef enum {
     DSPARK_E_HIP = 4           /* a kernel launch failed                           */
 } dspark_status;
 
-typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+/* Element type of a tensor argument: a plain 32-bit integer, so that any value
+ * a caller passes is well defined to receive and check (values other than
+ * these two are rejected with DSPARK_E_INVALID). */
+typedef int32_t dspark_dtype;
+enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 };
 
 /* Device-side condition flags, OR-ed into the workspace status word. */
 #define DSPARK_FLAG_NONFINITE 1u   /* a non-finite logit or score was seen        */

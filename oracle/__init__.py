@@ -16,6 +16,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dspark_oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# DSPARK_ORACLE_LIB: a prebuilt variant of the same source (the CPU sanitizer
+# test runs the oracle tests against an AddressSanitizer/UBSan build)
+_LIB_OVERRIDE = os.environ.get("DSPARK_ORACLE_LIB")
 
 TAG_DRAFT_CHUNK, TAG_DRAFT_ELEM, TAG_ACCEPT = 1, 2, 3
 TAG_RESID_CHUNK, TAG_RESID_ELEM, TAG_BONUS_CHUNK, TAG_BONUS_ELEM = 4, 5, 6, 7
@@ -37,9 +40,12 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        L = C.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = C.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            L = C.CDLL(_LIB)
         P = C.c_void_p
         i32, i64, u32, u64, f64 = C.c_int, C.c_int64, C.c_uint32, C.c_uint64, C.c_double
         L.orc_philox4x32_10.argtypes = [P, P, P]
