@@ -11,7 +11,7 @@ from ._lib import (DsparkError, acceptance_rate, acceptance_rate_features, async
                    confidence, confidence_logits, draft_markov, draft_rnn, get_status, clear_status, pack, pack_tiered,
                    prefix_schedule, rnn_workspace, rnn_workspace_bytes, sts_fit, sts_workspace,
                    verify, verify_cap_accept, verify_cap_accept_features, verify_features,
-                   workspace, workspace_bytes)
+                   w2_transpose, workspace, workspace_bytes)
 
 _lib.load()
 
@@ -19,4 +19,4 @@ __all__ = ["DsparkError", "acceptance_rate", "acceptance_rate_features", "async_
            "confidence", "confidence_logits", "draft_markov", "draft_rnn", "get_status", "clear_status", "pack", "pack_tiered",
            "prefix_schedule", "rnn_workspace", "rnn_workspace_bytes", "sts_fit", "sts_workspace",
            "verify", "verify_cap_accept", "verify_cap_accept_features", "verify_features",
-           "workspace", "workspace_bytes"]
+           "w2_transpose", "workspace", "workspace_bytes"]

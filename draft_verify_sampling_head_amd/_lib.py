@@ -31,7 +31,8 @@ EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
            "dspark_sts_workspace_bytes", "dspark_confidence_logits", "dspark_rnn_workspace_bytes",
            "dspark_draft_rnn", "dspark_verify_features", "dspark_draft_rnn_profiled",
            "dspark_acceptance_rate_features", "dspark_verify_cap_accept_features",
-           "dspark_set_switch", "dspark_get_switch", "dspark_draft_markov_noalloc")
+           "dspark_set_switch", "dspark_get_switch", "dspark_draft_markov_noalloc",
+           "dspark_w2_transpose")
 SWITCH_FORCE_PER_STEP, SWITCH_RNN_CELL_VALU, SWITCH_BARRIER_SPINS, SWITCH_DRAFT_KERNEL = 1, 2, 3, 4
 
 
@@ -87,6 +88,7 @@ def load():
     L.dspark_verify_features.argtypes = L.dspark_verify.argtypes
     L.dspark_acceptance_rate_features.argtypes = L.dspark_acceptance_rate.argtypes
     L.dspark_verify_cap_accept_features.argtypes = L.dspark_verify_cap_accept.argtypes
+    L.dspark_w2_transpose.argtypes = [i32, i32, P, P, i32, P]
     L.dspark_draft_markov_noalloc.argtypes = [i32, i32, i32, i32, f32, u64, u64, P, i32, P, P, i32,
                                               P, P, P, P, P, P, P]
     L.dspark_set_switch.argtypes = [i32, C.c_int64]
@@ -184,6 +186,13 @@ def draft_markov_noalloc(U, W1, W2t, x0, T, seed, rnd, x, logp_d, lse_d, flags=N
                                               _ptr(logp_d), _ptr(lse_d), _ptr(margin), _ptr(flags),
                                               _stream(stream))
     _check("dspark_draft_markov_noalloc", code)
+
+
+def w2_transpose(W2, W2t, stream=None):
+    """dspark_w2_transpose: W2 [r][V] (the method's layout) into W2t [V][r]."""
+    r, V = W2.shape
+    code = load().dspark_w2_transpose(r, V, _ptr(W2), _ptr(W2t), _dt(W2), _stream(stream))
+    _check("dspark_w2_transpose", code)
 
 
 def draft_markov_profiled(U, W1, W2t, x0, T, seed, rnd, x, logp_d, lse_d, ws, ev_begin, ev_end,

@@ -128,7 +128,8 @@ dspark_status dspark_get_status(const void* ws, size_t ws_bytes, uint32_t* flags
  *   U      [R][gamma][V]   base logits U_1..U_gamma (U_dt)
  *   W1     [V][r]          embedding table (W_dt); unused if r == 0
  *   W2t    [V][r]          W2 TRANSPOSED: W2t[v][i] = W2[i][v], the weight
- *                          layout of a linear layer r -> V (W_dt)
+ *                          layout of a linear layer r -> V (W_dt);
+ *                          dspark_w2_transpose converts W2 [r][V] into it
  *   x0     [R]             anchors
  *   x      out [R][gamma+1]  x[i][0] = x0[i], x[i][k] = drafted token k
  *   logp_d out [R][gamma]    log p_k(x_k) of the tempered draft (0 if T == 0)
@@ -151,6 +152,21 @@ dspark_status dspark_draft_markov(int R, int gamma, int V, int r, float T,
                                   const void* W1, const void* W2t, dspark_dtype W_dt,
                                   const int32_t* x0, int32_t* x, float* logp_d, float* lse_d,
                                   float* margin, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * W2 in the method's own layout ([P3] Method details: W2 in R^{r x V}) into
+ * the W2t layout every entry point here reads: W2t[v][i] = W2[i][v].  The
+ * draft keeps each compute unit's slice of vocabulary entries in registers
+ * with an entry's r values contiguous, and its picks read a chunk's 128
+ * entries as 128 contiguous rows, so W2t is the resident format; convert once
+ * per weight update.  Element bits are copied unchanged.
+ *   W2   [r][V]   (W_dt)
+ *   W2t  out [V][r] (W_dt); must not overlap W2
+ * r == 0 enqueues nothing.  DSPARK_E_INVALID for negative r, V < 1, a null
+ * or overlapping buffer or an unknown W_dt.
+ */
+dspark_status dspark_w2_transpose(int r, int V, const void* W2, void* W2t, dspark_dtype W_dt,
+                                  hipStream_t stream);
 
 /*
  * dspark_draft_markov for callers that cannot allocate device memory (code

@@ -19,7 +19,7 @@ FAKE = C.c_void_p(0x100000)      # never dereferenced: every call below fails va
 def declared():
     src = open(os.path.join(ROOT, "include", "dspark.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(dspark_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
@@ -212,3 +212,13 @@ def test_switches_set_get_and_reject():
         for k, v in zip(keys, saved):
             L.set_switch(k, v)
     assert [L.get_switch(k) for k in keys] == saved
+
+
+def test_w2_transpose_argument_checks():
+    lib = L.load()
+    assert lib.dspark_w2_transpose(-1, 10, FAKE, FAKE, 1, None) == INVALID
+    assert lib.dspark_w2_transpose(16, 0, FAKE, FAKE, 1, None) == INVALID
+    assert lib.dspark_w2_transpose(16, 10, FAKE, FAKE, 7, None) == INVALID     # unknown dtype
+    assert lib.dspark_w2_transpose(16, 10, None, FAKE, 1, None) == INVALID
+    assert lib.dspark_w2_transpose(16, 10, FAKE, FAKE, 1, None) == INVALID     # same buffer
+    assert lib.dspark_w2_transpose(0, 10, None, None, 1, None) == OK           # r == 0: nothing

@@ -1014,3 +1014,30 @@ def test_rnn_cap_accept_parity(over):
     print(f"  {rep.summary()} cut={int((mfull > n(buf.ell)).sum())}", flush=True)
     assert rep.ok(), rep.summary()
     assert (mfull > n(buf.ell)).any()           # the window cut some requests
+
+
+@pytest.mark.parametrize("r,V,dtype", [(64, 1000, torch.bfloat16), (256, 129280, torch.bfloat16),
+                                       (48, 77, torch.float32), (256, 151936, torch.bfloat16)])
+def test_w2_transpose_is_exact(r, V, dtype):
+    """dspark_w2_transpose moves bits: W2t equals W2.T element for element."""
+    g = torch.Generator(device="cpu").manual_seed(r * 7 + V)
+    W2 = torch.randn(r, V, generator=g).to(dtype).to(DEV)
+    W2t = torch.empty(V, r, dtype=dtype, device=DEV)
+    D.w2_transpose(W2, W2t)
+    torch.cuda.synchronize()
+    ref = W2.t().contiguous()
+    assert torch.equal(W2t.view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
+                       ref.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
+
+
+def test_draft_from_w2_in_method_layout():
+    """The draft fed W2 [r][V] through dspark_w2_transpose matches the oracle."""
+    cfg = synth.scaled(synth.config(2), R=45, gamma=4, V=3072, d=32, rank=128)
+    inp = synth.make_inputs(cfg, device="cpu")
+    W2 = inp["W2t"].t().contiguous()                 # the method's layout, r x V
+    W2t = torch.empty(cfg.V, cfg.rank, dtype=W2.dtype, device=DEV)
+    D.w2_transpose(W2.to(DEV), W2t)
+    torch.cuda.synchronize()
+    inp2 = dict(inp)
+    inp2["W2t"] = W2t.cpu()
+    run_and_check(cfg, inp2)
