@@ -573,7 +573,9 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const float2 empty = make_float2(-INFINITY, GREEDY ? __int_as_float(0x7FFFFFFF) : 0.f);
         for (int rl = lane; rl < rows; rl += 64) HS[rl * kPWaves + wv] = empty;
       }
-      __syncthreads();
+      // LDS-only barriers around the merge: the tile loop's last U prefetches
+      // may still be in flight and need not be waited for here
+      lds_sync();
       // merge the two halves (waves 2c, 2c+1) of each of the slice's four
       // chunks and store the chunk statistics: S relative to the raw maximum
       if (slice_active) {
@@ -603,7 +605,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
           }
         }
       }
-      __syncthreads();                      // E, PV and HS are rewritten by the next group
+      lds_sync();                           // E, PV and HS are rewritten by the next group
     }
     // the W1 row of x_{k-1} for this workgroup's first pick: a direct-to-LDS
     // load issued now completes with the barrier's own wait for the stores
