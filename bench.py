@@ -6,8 +6,9 @@ scheduler on (Algorithm 1; --scheduler async selects the asynchronous form).
 Prints ONE JSON line.  `value` = verified draft tokens per second
 (sum of scheduled lengths ell over the timed rounds / their device time, each
 round timed with events around its six stages on the launch stream), inputs
-resident in HBM before the timed region; a 512 MiB scratch buffer is written
-between rounds so that no round starts with W2 or U in the memory-side cache.  The `roofline` object covers the
+resident in HBM before the timed region; between rounds a 512 MiB scratch
+buffer is written and a second one read, so that no round starts with W2 or U
+in the memory-side cache (nor with the write's dirty lines in it).  The `roofline` object covers the
 dominant kernel (the persistent draft kernel: all gamma steps in one
 cooperative launch; the per-step statistics kernel when the shape takes the
 per-step schedule), timed live with HIP events recorded on the launch stream
@@ -59,8 +60,9 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=48, help="requests in the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush-mib", type=int, default=512,
-                   help="scratch buffer written between timed rounds (MiB) so that no round "
-                        "starts with W2 or U warm in the memory-side cache; 0 disables")
+                   help="between timed rounds a scratch buffer of this many MiB is written, "
+                        "then a second one read, so that no round starts with W2 or U warm in "
+                        "the memory-side cache nor with dirty lines in it; 0 disables")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="before the rounds, copy a buffer of this many MiB three times "
                         "(device to device), the known-size reference for HBM byte counters")
@@ -245,16 +247,24 @@ def main():
             L.draft_markov(inp["U"], inp["W1"], inp["W2t"], inp["x0"], cfg.T, cfg.philox_seed, i,
                            buf.x, buf.logp_d, buf.lse_d, buf.ws)
         L.confidence(inp["h"], inp["W1"], inp["w"], buf.x, buf.c, V=cfg.V)
+        kin = kplan = None
         if sched == "async":
             kin, kplan = ring.slots(i)
-            L.async_schedule(buf.c, inp["sps"], kin, kplan, buf.ell, a=buf.a, N_out=buf.N,
-                             theta=buf.theta)
+        if vmode == "compact":
+            # schedule and verify-batch pack in one launch
+            L.schedule_pack(buf.c, inp["sps"], buf.x, buf.ell, buf.cu, buf.flat,
+                            mode={"static": 0, "greedy": 1, "async": 2}[sched],
+                            marker_req=buf.marker_req, marker_pos=buf.marker_pos, K_in=kin,
+                            K_plan=kplan, a=buf.a, N_out=buf.N, theta=buf.theta)
         else:
-            L.prefix_schedule(buf.c, inp["sps"], buf.ell, enabled=(sched == "greedy"), a=buf.a,
-                              N_out=buf.N, theta_best=buf.theta)
-        win = buf.full if vmode == "cap-accept" else buf.ell
-        L.pack(buf.x, win, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N,
-               ws=buf.ws)
+            if sched == "async":
+                L.async_schedule(buf.c, inp["sps"], kin, kplan, buf.ell, a=buf.a, N_out=buf.N,
+                                 theta=buf.theta)
+            else:
+                L.prefix_schedule(buf.c, inp["sps"], buf.ell, enabled=(sched == "greedy"),
+                                  a=buf.a, N_out=buf.N, theta_best=buf.theta)
+            L.pack(buf.x, buf.full, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N,
+                   ws=buf.ws)
         if vmode == "cap-accept" and rnn:
             L.verify_cap_accept_features(buf.full, buf.ell, buf.cu, inp["target"], 1, buf.x,
                                          buf.logp_d, buf.lse_d, inp["U"], buf.feat, inp["W2t"],
@@ -277,22 +287,29 @@ def main():
         L.pack(buf.emitted, buf.tau, 0, buf.cu_out, buf.flat_out, N_out=buf.N_out, ws=buf.ws)
 
     # between rounds a scratch buffer is written, so every round reads W2 and
-    # U from HBM (the 256 MB memory-side cache holds nothing of them); each
-    # round is timed with events on the launch stream around its six stages
-    flush = (torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
-             if args.flush_mib > 0 else None)
+    # U from HBM (the 256 MB memory-side cache holds nothing of them), and then
+    # a second buffer is read: the write leaves the cache full of dirty lines,
+    # and the read makes them drain before the round instead of inside it.
+    # Each round is timed with events on the launch stream around its stages.
+    flush = flush_rd = None
+    if args.flush_mib > 0:
+        flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+        flush_rd = torch.ones((args.flush_mib << 20) // 8, dtype=torch.int64, device=dev)
+
+    def flush_caches(i):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+            flush_rd.amax()
     r_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(K)]
     for i in range(W):
-        if flush is not None:
-            flush.fill_(i & 0xFF)
+        flush_caches(i)
         one_round(i, False)
     torch.cuda.synchronize()
     log(f"[bench] {W} warmup rounds done")
     t_start = time.perf_counter()
     for i in range(W, W + K):
-        if flush is not None:
-            flush.fill_(i & 0xFF)
+        flush_caches(i)
         r_ev[i - W][0].record(stream)
         one_round(i, True)
         r_ev[i - W][1].record(stream)
@@ -347,7 +364,7 @@ def main():
     mfma_tf = kflops / (avg_ms * 1e-3) / 1e12
     log(f"[bench] round time (events, W2/U cold): median {np.median(round_ms):.3f} ms, p10 "
         f"{np.percentile(round_ms, 10):.3f}, p90 {np.percentile(round_ms, 90):.3f}; wall clock "
-        f"{1e3 * t_wall / K:.3f} ms per round with the {args.flush_mib} MiB scratch write")
+        f"{1e3 * t_wall / K:.3f} ms per round with the {args.flush_mib} MiB scratch write and read")
     log(f"[bench] {K} rounds: {ms_per_step:.3f} ms/round, sum_ell={sum_ell}, sum_tau={sum_tau}, "
         f"N_avg={N_avg:.1f}, n_rej={n_rej}, {kernel} {avg_ms * 1e3:.1f} us/launch "
         f"({achieved:.0f} GB/s, {mfma_tf:.0f} TFLOP/s), round HBM frac {hbm_frac_round:.3f}, "
@@ -405,7 +422,7 @@ def main():
     # orderly teardown while the runtime is fully alive: all work finished,
     # every device buffer released before the interpreter exits
     torch.cuda.synchronize()
-    del buf, inp, flush, ells, ms, Ns, Nouts
+    del buf, inp, flush, flush_rd, ells, ms, Ns, Nouts
     torch.cuda.empty_cache()
     torch.cuda.synchronize()
 

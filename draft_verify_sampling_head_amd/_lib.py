@@ -32,7 +32,7 @@ EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
            "dspark_draft_rnn", "dspark_verify_features", "dspark_draft_rnn_profiled",
            "dspark_acceptance_rate_features", "dspark_verify_cap_accept_features",
            "dspark_set_switch", "dspark_get_switch", "dspark_draft_markov_noalloc",
-           "dspark_w2_transpose")
+           "dspark_w2_transpose", "dspark_schedule_pack")
 SWITCH_FORCE_PER_STEP, SWITCH_RNN_CELL_VALU, SWITCH_BARRIER_SPINS, SWITCH_DRAFT_KERNEL = 1, 2, 3, 4
 
 
@@ -68,6 +68,8 @@ def load():
     L.dspark_prefix_schedule.argtypes = [i32, i32, P, P, i32, i32, P, P, P, P, P]
     L.dspark_async_schedule.argtypes = [i32, i32, P, P, i32, P, P, P, P, P, P, P, P]
     L.dspark_pack.argtypes = [i32, i32, P, P, i32, P, P, P, P, P, P, sz, P]
+    L.dspark_schedule_pack.argtypes = [i32, i32, i32, P, P, i32, P, P, P, P, P, P, P, P, P, P, P,
+                                       P, P]
     L.dspark_sts_workspace_bytes.argtypes = [i32]
     L.dspark_sts_workspace_bytes.restype = sz
     L.dspark_sts_fit.argtypes = [i32, i32, P, P, P, i32, i32, P, P, P, sz, P]
@@ -240,6 +242,21 @@ def async_schedule(c, sps, K_in, K_plan, ell, N_max=None, a=None, N_out=None, th
                                         _ptr(K_plan), _ptr(ell), _ptr(a), _ptr(N_out), _ptr(theta),
                                         _ptr(theta_plan), _stream(stream))
     _check("dspark_async_schedule", code)
+
+
+def schedule_pack(c, sps, x, ell, cu, flat, mode=1, marker_req=None, marker_pos=None, K_in=None,
+                  K_plan=None, N_max=None, a=None, N_out=None, theta=None, theta_plan=None,
+                  stream=None):
+    """mode 0 static, 1 greedy, 2 asynchronous; outputs as prefix_schedule /
+    async_schedule followed by pack(x, ell, 1, ...)."""
+    R, gamma = c.shape
+    N_max = sps.numel() - 1 if N_max is None else N_max
+    code = load().dspark_schedule_pack(R, gamma, int(mode), _ptr(c), _ptr(sps), int(N_max),
+                                       _ptr(K_in), _ptr(K_plan), _ptr(x), _ptr(ell), _ptr(a),
+                                       _ptr(N_out), _ptr(theta), _ptr(theta_plan), _ptr(cu),
+                                       _ptr(flat), _ptr(marker_req), _ptr(marker_pos),
+                                       _stream(stream))
+    _check("dspark_schedule_pack", code)
 
 
 def pack(rows, lens, len_offset, cu, flat, marker_req=None, marker_pos=None, N_out=None, ws=None,

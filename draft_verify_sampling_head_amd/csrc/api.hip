@@ -322,6 +322,32 @@ dspark_status dspark_async_schedule(int R, int gamma, const float* c, const doub
   return hip_status(launch_schedule(sa, stream));
 }
 
+dspark_status dspark_schedule_pack(int R, int gamma, int mode, const float* c, const double* sps,
+                                   int N_max, const int32_t* K_in, int32_t* K_plan,
+                                   const int32_t* x, int32_t* ell, float* a, int32_t* N_out,
+                                   double* theta, double* theta_plan, int32_t* cu, int32_t* flat,
+                                   int32_t* marker_req, int32_t* marker_pos, hipStream_t stream) {
+  if (R < 0 || gamma < 1) return DSPARK_E_INVALID;
+  if (mode < 0 || mode > 2) return DSPARK_E_INVALID;
+  if (gamma > 32) return DSPARK_E_UNSUPPORTED;
+  if (R == 0) return DSPARK_OK;
+  if (!c || !sps || !ell || !x || !cu || !flat) return DSPARK_E_INVALID;
+  if (mode == 2 && (!K_in || !K_plan)) return DSPARK_E_INVALID;
+  if (N_max < R) return DSPARK_E_INVALID;
+  if (mode == 0 && (int64_t)N_max < (int64_t)R * (gamma + 1)) return DSPARK_E_INVALID;
+  if ((int64_t)R * gamma > 16384) return DSPARK_E_UNSUPPORTED;
+  SchedArgs sa{};
+  sa.R = R; sa.gamma = gamma; sa.N_max = N_max; sa.enabled = mode != 0; sa.mode = mode == 2;
+  sa.c = c; sa.sps = sps; sa.ell = ell; sa.a = a; sa.N_out = N_out; sa.theta = theta;
+  sa.K_in = K_in; sa.K_plan = K_plan; sa.theta_plan = theta_plan;
+  sa.pack = true;
+  PackArgs& p = sa.pk;
+  p.R = R; p.width = gamma + 1; p.rows = x; p.cu = cu; p.flat = flat;
+  p.marker_req = marker_req; p.marker_pos = marker_pos;
+  p.slots = (int64_t)R * (gamma + 1);
+  return hip_status(launch_schedule(sa, stream));
+}
+
 dspark_status dspark_pack(int R, int width, const int32_t* rows, const int32_t* len,
                           int len_offset, int32_t* cu, int32_t* flat, int32_t* marker_req,
                           int32_t* marker_pos, int32_t* N_out, void* ws, size_t ws_bytes,

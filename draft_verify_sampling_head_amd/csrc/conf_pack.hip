@@ -11,6 +11,7 @@
 // scatters every request's tokens to their flattened slots, writing the
 // offsets and the (request, position) markers; slots past N are set to -1.
 #include "launch.hpp"
+#include "pack.hpp"
 
 namespace dspark {
 
@@ -40,7 +41,24 @@ __device__ __forceinline__ float lane_dot(const A* a, const B* b, int n, bool ve
   float acc = 0.f;
   if (vec && sizeof(A) == sizeof(B)) {
     constexpr int W = 16 / sizeof(A);
+    constexpr int UNR = 4;                  // 16-byte loads of each operand in flight per lane
     int j = lane * W;
+    // four independent accumulators: the loads of four steps are issued
+    // together instead of one dependent step at a time
+    float part[UNR] = {0.f, 0.f, 0.f, 0.f};
+    for (; j + (UNR - 1) * 64 * W + W <= n; j += UNR * 64 * W) {
+      float x[UNR][W], y[UNR][W];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        unpack<A>(a + j + u * 64 * W, x[u]);
+        unpack<B>(b + j + u * 64 * W, y[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+#pragma unroll
+        for (int e = 0; e < W; ++e) part[u] = fmaf(x[u][e], y[u][e], part[u]);
+    }
+    acc = (part[0] + part[1]) + (part[2] + part[3]);
     for (; j + W <= n; j += 64 * W) {
       float x[W], y[W];
       unpack<A>(a + j, x);
@@ -63,9 +81,11 @@ __global__ __launch_bounds__(256) void k_confidence(ConfArgs a) {
   const int i = item / a.gamma, k = item % a.gamma + 1;
   const HT* h = reinterpret_cast<const HT*>(a.h) + (int64_t)item * a.d;
   const VT* w = reinterpret_cast<const VT*>(a.w);
+  // the token x_{k-1} is loaded first: its W1 row's address is then ready
+  // when the h part is done
+  int prev = a.rank > 0 ? a.x[(int64_t)i * (a.gamma + 1) + (k - 1)] : 0;
   float z = lane_dot(h, w, a.d, a.vec_h);
   if (a.rank > 0) {
-    int prev = a.x[(int64_t)i * (a.gamma + 1) + (k - 1)];
     if (prev < 0 || prev >= a.V) { set_flag(a.status, kFlagBadToken); prev = 0; }
     const WT* e = reinterpret_cast<const WT*>(a.W1) + (int64_t)prev * a.rank;
     z += lane_dot(e, w + a.d, a.rank, a.vec_e);
@@ -94,89 +114,16 @@ hipError_t launch_confidence(const ConfArgs& a, bool h_bf16, bool w1_bf16, bool 
 }
 
 // ------------------------------------------------------------------- pack
-// Exclusive scan of one value per thread over a 1024-thread block; returns
-// the thread's prefix and writes the block total to *total.
-__device__ inline int block_exclusive_scan(int v, int* lds_waves, int* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  if (lane == 63) lds_waves[wv] = inc;
-  __syncthreads();
-  if (wv == 0) {
-    int t = (lane < 16) ? lds_waves[lane] : 0;
-    int ti = t;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int y = __shfl_up(ti, o);
-      if (lane >= o) ti += y;
-    }
-    if (lane < 16) lds_waves[16 + lane] = ti - t;
-    if (lane == 15) lds_waves[32] = ti;
-  }
-  __syncthreads();
-  const int res = lds_waves[16 + wv] + inc - v;
-  *total = lds_waves[32];
-  __syncthreads();
-  return res;
-}
+constexpr int kPackCuLds = 8192;            // offsets kept in LDS up to R = 8191
 
-__global__ __launch_bounds__(1024) void k_pack(PackArgs a) {
-  __shared__ int lds[40];
-  const int tid = threadIdx.x;
-  int carry = 0;
-  for (int base = 0; base < a.R; base += 1024) {
-    const int r = base + tid;
-    int l = 0;
-    if (r < a.R) {
-      l = a.len[r] + a.len_offset;
-      if (l < 0 || l > a.width) {
-        set_flag(a.status, kFlagBadLen);
-        l = l < 0 ? 0 : a.width;
-      }
-    }
-    int tot;
-    const int pos = carry + block_exclusive_scan(l, lds, &tot);
-    if (r < a.R) {
-      a.cu[r] = pos;
-      const int32_t* src = a.rows + (int64_t)r * a.width;
-      for (int j = 0; j < l; ++j) {
-        a.flat[pos + j] = src[j];
-        if (a.marker_req) a.marker_req[pos + j] = r;
-        if (a.marker_pos) a.marker_pos[pos + j] = j;
-      }
-    }
-    carry += tot;
-  }
-  // graph-tier padding: the smallest tier that holds the packed total
-  int npad = carry;
-  if (a.ntiers > 0) {
-    int t = -1;
-    for (int k = 0; k < a.ntiers; ++k)
-      if (a.tiers[k] >= carry) { t = a.tiers[k]; break; }
-    if (t < 0) {
-      if (tid == 0) set_flag(a.status, kFlagTier);
-      t = carry;
-    }
-    npad = t;
-  }
-  if (tid == 0) {
-    a.cu[a.R] = carry;
-    if (a.N_out) *a.N_out = carry;
-    if (a.N_pad) *a.N_pad = npad;
-  }
-  for (int64_t q = carry + tid; q < a.slots; q += 1024) {
-    a.flat[q] = q < npad ? a.pad_token : -1;
-    if (a.marker_req) a.marker_req[q] = -1;
-    if (a.marker_pos) a.marker_pos[q] = -1;
-  }
+__global__ __launch_bounds__(kPackThreads) void k_pack(PackArgs a) {
+  __shared__ int lds[kPackLds];
+  __shared__ int cu_l[kPackCuLds];
+  pack_rows_block(a, [&](int r) { return a.len[r] + a.len_offset; }, lds, cu_l, kPackCuLds);
 }
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_pack, dim3(1), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(k_pack, dim3(1), dim3(kPackThreads), 0, st, a);
   return hipGetLastError();
 }
 

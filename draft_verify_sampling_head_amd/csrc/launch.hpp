@@ -108,6 +108,8 @@ struct SchedArgs {
   const int32_t* K_in;      // mode 1: capacity planned two rounds earlier
   int32_t* K_plan;          // mode 1: capacity planned from this round
   double* theta_plan;       // mode 1 (nullable)
+  bool pack;                // also pack the verify batch: pk.rows with length ell + 1
+  PackArgs pk;              // (pk.len, pk.len_offset unused)
 };
 
 constexpr int kStsMaxBins = 64;

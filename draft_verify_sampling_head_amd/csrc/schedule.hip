@@ -29,7 +29,13 @@
 // maximiser of Theta_q over q = 0..|E| (global search: every thread keeps the
 // first maximum of its own positions, then one block-wide (max Theta, min q)
 // reduction).
+//
+// With pack set, the same workgroup then packs the verify batch (the drafted
+// rows x with lengths ell + 1, anchors included) as the stand-alone pack
+// kernel does, from the lengths it has just left in LDS: the scheduler's
+// decision and the batch it implies cost one launch.
 #include "launch.hpp"
+#include "pack.hpp"
 
 namespace dspark {
 
@@ -221,6 +227,22 @@ __device__ __forceinline__ void schedule_body(const SchedArgs& a, int G2, uint64
   // G2 > 0: request r's keys sit at r*G2 + j (runs padded to G2, a power of
   // two); G2 == 0: packed at r*G + j (bitonic only)
   const int stride = G2 > 0 ? G2 : G;
+  const int p0 = tid * EPT;
+
+  // SPS(B) for every batch size this thread's positions can reach
+  // (B = R + p0 .. R + p0 + EPT, clamped to N_max: Theta is 0 past it),
+  // fetched first so the admission pass after the sort reads registers (up
+  // to 8 positions per thread; the 16-position form, which has no registers
+  // to spare, reads them where they are used)
+  constexpr int NSV = EPT <= 8 ? EPT + 1 : 1;
+  double sv[NSV];
+#pragma unroll
+  for (int e = 0; e < NSV; ++e) sv[e] = a.sps[min(R + p0 + e, a.N_max)];
+  // Theta at B = R + p0 + e (e known at compile time after unrolling)
+  auto theta_here = [&](int64_t tau, int e) {
+    const int B = R + p0 + e;
+    return (B > a.N_max) ? 0.0 : ((double)tau * 0x1p-32) * (EPT <= 8 ? sv[e] : a.sps[B]);
+  };
 
   // survival products (left to right, float32) and sort keys
   int64_t part = 0;
@@ -262,7 +284,11 @@ __device__ __forceinline__ void schedule_body(const SchedArgs& a, int G2, uint64
 
   if (!a.enabled) {
     const int64_t tau = ((int64_t)R << 32) + block_sum_i64(part, red64);
-    for (int r = tid; r < R; r += kSchedThreads) a.ell[r] = G;
+    int* ell_l = reinterpret_cast<int*>(keys);        // (the keys are not read again)
+    for (int r = tid; r < R; r += kSchedThreads) {
+      a.ell[r] = G;
+      ell_l[r] = G;
+    }
     if (tid == 0) {
       const int B = R * (G + 1);
       if (a.N_out) *a.N_out = B;
@@ -285,7 +311,6 @@ __device__ __forceinline__ void schedule_body(const SchedArgs& a, int G2, uint64
 
   // fixed-point prefix sums over the sorted order; thread t owns positions
   // [t*EPT, t*EPT + EPT)
-  const int p0 = tid * EPT;
   int64_t local = 0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e)
@@ -296,7 +321,7 @@ __device__ __forceinline__ void schedule_body(const SchedArgs& a, int G2, uint64
   // (thread 0 also holds q = 0)
   double pbest = -__builtin_inf();
   int pq = 0x7FFFFFFF;
-  if (a.mode == 1 && tid == 0) { pbest = theta_of((int64_t)R << 32, R, a.N_max, a.sps); pq = 0; }
+  if (a.mode == 1 && tid == 0) { pbest = theta_here((int64_t)R << 32, 0); pq = 0; }
   bool stopped = false;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
@@ -304,9 +329,9 @@ __device__ __forceinline__ void schedule_body(const SchedArgs& a, int G2, uint64
     if (v[e] == ~0ull) { if (firstsent == 0x7FFFFFFF) firstsent = p; stopped = true; }
     if (!stopped) {
       const int64_t tau_next = tau + fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(v[e] >> 32)));
-      const double after = theta_of(tau_next, R + p + 1, a.N_max, a.sps);
+      const double after = theta_here(tau_next, e + 1);
       if (a.mode == 0) {
-        const double before = theta_of(tau, R + p, a.N_max, a.sps);
+        const double before = theta_here(tau, e);
         if (!(after > before)) { first_stop = p; stopped = true; }
       } else if (after > pbest) {
         pbest = after;
@@ -351,13 +376,24 @@ __device__ __forceinline__ void schedule_body(const SchedArgs& a, int G2, uint64
   // Theta of the admitted prefix (exact integer sum)
   const int64_t tau_adm = ((int64_t)R << 32) + block_sum_i64(mine, red64);   // (has barriers)
   for (int r = tid; r < R; r += kSchedThreads) a.ell[r] = ell_l[r];
-  if (tid == 0 && a.theta) *a.theta = theta_of(tau_adm, R + admitted, a.N_max, a.sps);
+  // Theta of the admitted prefix, from the thread whose SPS values reach
+  // B = R + admitted
+  const int owner = min(admitted / EPT, kSchedThreads - 1);
+  if (tid == owner && a.theta) {
+    double th = theta_here(tau_adm, 0);
+#pragma unroll
+    for (int e = 1; e <= EPT; ++e)
+      if (p0 + e == admitted) th = theta_here(tau_adm, e);
+    *a.theta = th;
+  }
 }
 
 __global__ __launch_bounds__(kSchedThreads) void k_schedule(SchedArgs a) {
+  static_assert(kSchedThreads == kPackThreads, "the pack runs on the scheduler's workgroup");
   __shared__ uint64_t keys[kSchedMaxKeys];
   __shared__ int64_t red64[kSchedThreads / 64];
   __shared__ int red32[kSchedThreads / 64];
+  __shared__ int pk_lds[kPackLds];
   __shared__ int kin_l;
   // K_in is read once, before K_plan (which may be the same address) is written
   if (threadIdx.x == 0) kin_l = (a.mode == 1) ? *a.K_in : 0;
@@ -371,6 +407,17 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(SchedArgs a) {
   else if (n <= 4 * kSchedThreads) schedule_body<4>(a, G2, keys, red64, red32, &kin_l);
   else if (n <= 8 * kSchedThreads) schedule_body<8>(a, G2, keys, red64, red32, &kin_l);
   else schedule_body<16>(a, G2, keys, red64, red32, &kin_l);
+  // verify-batch pack of x with the lengths ell + 1 just decided (every path
+  // of the body leaves ell in LDS at the start of the key buffer)
+  if (a.pack) {
+    __syncthreads();
+    // ell in the first R ints of the key buffer; the offsets after them
+    // (2 R + 1 <= 2 * 16384 ints of the 32768 the buffer holds, except at R = 16384)
+    int* kb = reinterpret_cast<int*>(keys);
+    const int* ell_l = kb;
+    pack_rows_block(a.pk, [&](int r) { return ell_l[r] + 1; }, pk_lds, kb + a.R,
+                    2 * kSchedMaxKeys - a.R);
+  }
 }
 
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t st) {

@@ -100,20 +100,29 @@ def run_round(inp, buf: RoundBuffers, T, seed, rnd, scheduler=True, layout=1, st
         L.draft_markov(inp["U"], inp["W1"], inp["W2t"], inp["x0"], T, seed, rnd, buf.x,
                        buf.logp_d, buf.lse_d, buf.ws, stream=stream)
     L.confidence(inp["h"], inp["W1"], inp["w"], buf.x, buf.c, sts_T=sts_T, V=buf.V, stream=stream)
+    kin = kplan = None
     if scheduler == "async":
         kin, kplan = ring.slots(rnd)
-        L.async_schedule(buf.c, inp["sps"], kin, kplan, buf.ell, a=buf.a, N_out=buf.N,
-                         theta=buf.theta, stream=stream)
+    if verify_mode != "cap-accept" and not tiers:
+        # the schedule and the verify batch it implies in one launch
+        mode = 2 if scheduler == "async" else (1 if scheduler else 0)
+        L.schedule_pack(buf.c, inp["sps"], buf.x, buf.ell, buf.cu, buf.flat, mode=mode,
+                        marker_req=buf.marker_req, marker_pos=buf.marker_pos, K_in=kin,
+                        K_plan=kplan, a=buf.a, N_out=buf.N, theta=buf.theta, stream=stream)
     else:
-        L.prefix_schedule(buf.c, inp["sps"], buf.ell, enabled=bool(scheduler), a=buf.a,
-                          N_out=buf.N, theta_best=buf.theta, stream=stream)
-    win = buf.full if verify_mode == "cap-accept" else buf.ell
-    if tiers:
-        L.pack_tiered(buf.x, win, 1, tiers, pad_token, buf.cu, buf.flat, buf.marker_req,
-                      buf.marker_pos, buf.N, buf.N_pad, ws=buf.ws, stream=stream)
-    else:
-        L.pack(buf.x, win, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N, ws=buf.ws,
-               stream=stream)
+        if scheduler == "async":
+            L.async_schedule(buf.c, inp["sps"], kin, kplan, buf.ell, a=buf.a, N_out=buf.N,
+                             theta=buf.theta, stream=stream)
+        else:
+            L.prefix_schedule(buf.c, inp["sps"], buf.ell, enabled=bool(scheduler), a=buf.a,
+                              N_out=buf.N, theta_best=buf.theta, stream=stream)
+        win = buf.full if verify_mode == "cap-accept" else buf.ell
+        if tiers:
+            L.pack_tiered(buf.x, win, 1, tiers, pad_token, buf.cu, buf.flat, buf.marker_req,
+                          buf.marker_pos, buf.N, buf.N_pad, ws=buf.ws, stream=stream)
+        else:
+            L.pack(buf.x, win, 1, buf.cu, buf.flat, buf.marker_req, buf.marker_pos, buf.N,
+                   ws=buf.ws, stream=stream)
     if verify_mode == "cap-accept" and rnn:
         L.verify_cap_accept_features(buf.full, buf.ell, buf.cu, inp["target"], layout, buf.x,
                                      buf.logp_d, buf.lse_d, inp["U"], buf.feat, inp["W2t"], T, seed,

@@ -245,7 +245,10 @@ dspark_status dspark_confidence(int R, int gamma, int d, int r, int V,
  * Theta = tau * SPS(B) must strictly improve or the scan stops (early stop).
  * tau is summed in 2^-32 fixed point (exact, order-free); Theta is a double.
  * B > N_max counts as Theta = 0 (capacity exceeded).
- *   c          [R][gamma]   confidences
+ *   c          [R][gamma]   confidences, in [0, 1] (the confidence head's
+ *                           sigmoid outputs; outside [0, 1] a request's
+ *                           admitted positions need not form a prefix and
+ *                           ell, N_out and Theta are unspecified)
  *   sps        [N_max+1]    SPS(B), engine steps per second at batch B (double)
  *   enabled    0: ell = gamma for every request (static verification; then
  *              N_max must hold the whole block, N_max >= R (gamma + 1), else
@@ -293,6 +296,29 @@ dspark_status dspark_async_schedule(int R, int gamma, const float* c, const doub
                                     int N_max, const int32_t* K_in, int32_t* K_plan, int32_t* ell,
                                     float* a, int32_t* N_out, double* theta, double* theta_plan,
                                     hipStream_t stream);
+
+/*
+ * Scheduler and verify-batch pack in one launch ([P3] Method details, the
+ * prefix scheduler, and Supplementary details, variable-length routing; [P4]
+ * 3.3): the schedule of dspark_prefix_schedule (mode 0: static, every
+ * request verifies its whole block; mode 1: greedy with early stop) or of
+ * dspark_async_schedule (mode 2), then the pack of dspark_pack with rows = x,
+ * len = the ell just decided, len_offset = 1, by the same workgroup.  Every
+ * output equals that of the two calls in sequence.
+ *   mode       0 static, 1 greedy, 2 asynchronous (K_in, K_plan required)
+ *   c, sps, N_max, K_in, K_plan, ell, a, theta, theta_plan
+ *              as for the schedulers (theta = theta_best in modes 0 and 1;
+ *              theta_plan is written in mode 2 only)
+ *   x          [R][gamma+1] anchor + drafted tokens
+ *   N_out      out nullable (device scalar) sum_i (1 + ell_i) = cu[R]
+ *   cu, flat, marker_req, marker_pos  as for dspark_pack with width gamma+1
+ * Needs R <= N_max and R * gamma <= 16384 (mode 0: N_max >= R (gamma + 1)).
+ */
+dspark_status dspark_schedule_pack(int R, int gamma, int mode, const float* c, const double* sps,
+                                   int N_max, const int32_t* K_in, int32_t* K_plan,
+                                   const int32_t* x, int32_t* ell, float* a, int32_t* N_out,
+                                   double* theta, double* theta_plan, int32_t* cu, int32_t* flat,
+                                   int32_t* marker_req, int32_t* marker_pos, hipStream_t stream);
 
 /*
  * Ragged pack ([P3] Supplementary details, variable-length routing; [P4] 3.3):

@@ -123,6 +123,17 @@ def test_confidence_schedule_pack_verify_checks():
     assert asch(g=33) == UNSUPPORTED
     assert asch(R=1024, g=17, N_max=10**6) == UNSUPPORTED
     assert asch(R=0, kin=None) == OK
+    sp = lambda R=4, g=4, mode=1, N_max=100, x=FAKE, kin=FAKE, kp=FAKE, cu=FAKE, flat=FAKE: \
+        lib.dspark_schedule_pack(R, g, mode, FAKE, FAKE, N_max, kin, kp, x, FAKE, None, None, None,
+                                 None, cu, flat, None, None, None)
+    assert sp(mode=3) == INVALID and sp(mode=-1) == INVALID
+    assert sp(x=None) == INVALID and sp(cu=None) == INVALID and sp(flat=None) == INVALID
+    assert sp(N_max=3) == INVALID
+    assert sp(mode=0, N_max=19) == INVALID                # static needs the whole block
+    assert sp(mode=2, kin=None) == INVALID and sp(mode=2, kp=None) == INVALID
+    assert sp(g=33) == UNSUPPORTED
+    assert sp(R=1024, g=17, N_max=10**6) == UNSUPPORTED
+    assert sp(R=0, x=None) == OK
     pack = lambda R=4, width=3, rows=FAKE, ln=FAKE, cu=FAKE, flat=FAKE: lib.dspark_pack(
         R, width, rows, ln, 0, cu, flat, None, None, None, None, 0, None)
     assert pack(width=0) == INVALID

@@ -597,6 +597,74 @@ def test_sts_fit_parity():
     np.testing.assert_array_equal(tg, grid[[3, 9, 17, 5, 12]])
 
 
+def _schedule_pack_case(c, sps, x, mode, N_max=None, K_in=None):
+    """dspark_schedule_pack against the oracle's scheduler followed by its pack
+    of x with lengths ell + 1."""
+    import oracle as O
+    R, g = c.shape
+    dev = lambda v: torch.as_tensor(v, device=DEV)
+    ell = torch.full((R,), -7, dtype=torch.int32, device=DEV)
+    a = torch.empty(R, g, dtype=torch.float32, device=DEV)
+    N = torch.empty(1, dtype=torch.int32, device=DEV)
+    th = torch.empty(1, dtype=torch.float64, device=DEV)
+    thp = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+    cu = torch.full((R + 1,), -7, dtype=torch.int32, device=DEV)
+    flat = torch.full((R * (g + 1),), -7, dtype=torch.int32, device=DEV)
+    mr, mp = torch.full_like(flat, -7), torch.full_like(flat, -7)
+    Kin = Kp = None
+    if mode == 2:
+        Kin = torch.full((1,), K_in, dtype=torch.int32, device=DEV)
+        Kp = torch.empty(1, dtype=torch.int32, device=DEV)
+    D.schedule_pack(dev(c), dev(sps), dev(x), ell, cu, flat, mode=mode, marker_req=mr,
+                    marker_pos=mp, K_in=Kin, K_plan=Kp, N_max=N_max, a=a, N_out=N, theta=th,
+                    theta_plan=thp)
+    torch.cuda.synchronize()
+    if mode == 2:
+        e, ao, No, tho, Ko, thpo = O.async_schedule(c, sps, K_in, N_max=N_max)
+        assert int(n(Kp)[0]) == Ko
+        assert float(n(thp)[0]) == thpo
+    else:
+        e, ao, No, tho, _ = O.prefix_schedule(c, sps, N_max=N_max, enabled=mode == 1)
+        assert float(n(thp)[0]) == -1.0                  # not written outside mode 2
+    np.testing.assert_array_equal(n(ell), e)
+    np.testing.assert_array_equal(n(a).view(np.uint32), ao.view(np.uint32))
+    assert int(n(N)[0]) == No
+    assert float(n(th)[0]) == tho
+    pe = O.pack(x, np.asarray(e) + 1)
+    np.testing.assert_array_equal(n(cu), pe[0])
+    np.testing.assert_array_equal(n(flat), pe[1])
+    np.testing.assert_array_equal(n(mr), pe[2])
+    np.testing.assert_array_equal(n(mp), pe[3])
+    assert pe[4] == No
+
+
+def test_schedule_pack_matches_oracle():
+    """The fused schedule + verify-batch pack: static, greedy and asynchronous
+    modes over random shapes (merge-sorted runs, and the bitonic network for
+    packed keys), ties, zeros inside a block and all-ones confidences."""
+    rng = np.random.default_rng(11)
+    cases = [(int(rng.integers(1, 300)), int(rng.integers(1, 33))) for _ in range(12)]
+    cases += [(256, 16), (1, 1), (1024, 16), (600, 17)]
+    for it, (R, g) in enumerate(cases):
+        if R * g > 16384:
+            continue
+        c = rng.uniform(0, 1, (R, g)).astype(np.float32)
+        if it % 3 == 0:
+            c = rng.choice(np.array([0, 0.25, 0.5, 0.75, 1.0], np.float32), (R, g))
+        if it % 5 == 4:
+            c[:, :] = 1.0
+        if it % 7 == 6:
+            c[rng.uniform(0, 1, (R, g)) < 0.2] = 0.0             # runs cut short by c = 0
+        x = rng.integers(0, 129280, (R, g + 1)).astype(np.int32)
+        B = np.arange(R * (g + 1) + 1, dtype=np.float64)
+        sps = [1.0 / (0.020 + 5e-5 * B), 1.0 / (0.015 + 4e-5 * B + 0.003 * (B // 7))][it % 2]
+        N_max = None if it % 4 else int(rng.integers(R, R * (g + 1) + 1))
+        _schedule_pack_case(c, sps, x, 1, N_max=N_max)
+        _schedule_pack_case(c, sps, x, 0)
+        for K_in in [int(rng.integers(R, R * (g + 1) + 1)), 0, R * (g + 1) + 5]:
+            _schedule_pack_case(c, sps, x, 2, N_max=N_max, K_in=K_in)
+
+
 # ------------------------------------------------------------- stage: pack
 def test_pack_tiered_bitexact():
     import oracle as O
