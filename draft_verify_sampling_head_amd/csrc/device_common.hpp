@@ -178,4 +178,34 @@ __device__ __forceinline__ void set_flag(uint32_t* status, uint32_t f) {
   if (status) atomicOr(status, f);
 }
 
+// Values that cross workgroups inside one launch (chunk statistics, chunk
+// argmaxes, drafted tokens, row normalisers) are stored and loaded with
+// device-scope relaxed atomics.  Those accesses are coherent across the
+// XCDs' L2 caches by themselves, so a grid barrier or a completion counter
+// only has to order them: no L2 write-back or invalidation (XCD-wide
+// operations) is needed.
+__device__ __forceinline__ int ld_coh(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_coh2(const float2* p) {
+  const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float2*>(p)),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+}
+// 16 bytes written by another workgroup in this launch: two device-coherent
+// 64-bit loads (p 16-byte aligned).
+__device__ __forceinline__ uint4 ld_coh16(const void* p) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<void*>(p));
+  const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+}
+__device__ __forceinline__ void st_coh2(float2* p, float2 v) {
+  const uint64_t u = (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace dspark

@@ -17,6 +17,8 @@ struct Switches {
   uint32_t barrier_spins;  // polls before a cross-workgroup wait gives up
   int draft_kernel;        // persistent draft: 0 one grid barrier per step, 1 pipelined
 };
+// Polls before a cross-workgroup wait gives up when barrier_spins is 0.
+constexpr uint32_t kBarrierSpins = 1u << 24;
 Switches switches();
 
 enum { kRowsDraft = 0, kRowsVerifyPacked = 1, kRowsVerifyDense = 2, kRowsAll = 3 };
@@ -170,7 +172,8 @@ bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void*
                          const void* W1, const void* W2t, const void* target, const int32_t* x,
                          const int32_t* rej_count, const int4* rej, const float2* lse_t,
                          const float* lse_d, float2* L, uint32_t* status, hipStream_t st,
-                         hipError_t* err, bool overlap = false, bool feat_rows = false);
+                         hipError_t* err, bool overlap = false, bool feat_rows = false,
+                         int* winners = nullptr, uint64_t seed = 0, uint64_t round = 0);
 hipError_t launch_acceptance_rate(int R, int gamma, int V, int rank, float T, const void* target,
                                   const int32_t* x, const float* lse_d, const void* U, bool u_bf16,
                                   const void* W1, const void* W2t, bool w_bf16, float* c_star,

@@ -18,6 +18,106 @@ struct PickResult {
   float gap;     // best minus second-best key (only when asked for)
 };
 
+// Reductions over one chunk's lanes when a wave-wide 16-byte load covers
+// 64 / LPC chunks (LPC = 16 lanes for bf16 rows, 32 for fp32).
+template <int LPC>
+__device__ __forceinline__ float chunk_max(float v) {
+  v = row16_max(v);
+  if (LPC == 32) v = fmaxf(v, __shfl_xor(v, 16));
+  return v;
+}
+template <int LPC>
+__device__ __forceinline__ float chunk_sum(float v) {
+  v = row16_sum(v);
+  if (LPC == 32) v += __shfl_xor(v, 16);
+  return v;
+}
+template <int LPC>
+__device__ __forceinline__ void chunk_argmax(float& v, int& i) {
+  row16_argmax(v, i);
+  if (LPC == 32) argmax_merge(v, i, __shfl_xor(v, 16), __shfl_xor(i, 16));
+}
+
+// One wave: chunks [c0, c1) of one row.  UNR 16-byte loads per lane are in
+// flight at once (64 UNR / LPC chunks per batch); the data stays as raw
+// words until it is used.
+template <typename T, bool GREEDY, int UNR = 8>
+__device__ __forceinline__ void row_segment(const T* row, int V, int c0, int c1, float scale2,
+                                            bool vec_ok, float2* L, int* I, uint32_t* status) {
+  constexpr int VPL = 16 / sizeof(T);       // values per lane per 16-byte load
+  constexpr int LPC = kChunk / VPL;         // lanes per chunk
+  constexpr int CPI = 64 / LPC;             // chunks per wave-wide load
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % LPC;
+  const int cl = lane / LPC;
+  for (int cb = c0; cb < c1; cb += CPI * UNR) {
+    uint4 raw[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int c = cb + u * CPI + cl;
+      const int v0 = c * kChunk + sub * VPL;
+      if (c < c1 && vec_ok && v0 + VPL <= V) {
+        raw[u] = *reinterpret_cast<const uint4*>(row + v0);
+      } else {
+        // ragged tail: element loads, -inf past the segment or the vocabulary
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (sizeof(T) == 2) {
+            const uint32_t lo = (c < c1 && v0 + 2 * q < V) ? reinterpret_cast<const uint16_t*>(row)[v0 + 2 * q] : 0xFF80u;
+            const uint32_t hi = (c < c1 && v0 + 2 * q + 1 < V) ? reinterpret_cast<const uint16_t*>(row)[v0 + 2 * q + 1] : 0xFF80u;
+            w[q] = lo | (hi << 16);
+          } else {
+            w[q] = (c < c1 && v0 + q < V) ? __float_as_uint(reinterpret_cast<const float*>(row)[v0 + q])
+                                          : __float_as_uint(-INFINITY);
+          }
+        }
+        raw[u] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int c = cb + u * CPI + cl;
+      const int v0 = c * kChunk + sub * VPL;
+      float x[VPL];
+      {
+        const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+        for (int e = 0; e < VPL; ++e)
+          x[e] = (sizeof(T) == 2) ? ((e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1])) : __uint_as_float(w[e]);
+      }
+      if (GREEDY) {
+        float bv = -INFINITY;
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int e = 0; e < VPL; ++e)
+          if (x[e] > bv) { bv = x[e]; bi = v0 + e; }
+        chunk_argmax<LPC>(bv, bi);
+        if (sub == 0 && c < c1) {
+          L[c] = make_float2(bv, 0.f);
+          I[c] = bi;
+          if (nonfinite(bv)) set_flag(status, kFlagNonFinite);
+        }
+      } else {
+        float m = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) m = fmaxf(m, x[e]);
+        m = chunk_max<LPC>(m);
+        float s = 0.f;
+        if (m != -INFINITY) {
+#pragma unroll
+          for (int e = 0; e < VPL; ++e) s += __builtin_amdgcn_exp2f((x[e] - m) * scale2);
+        }
+        s = chunk_sum<LPC>(s);
+        if (sub == 0 && c < c1) {
+          L[c] = make_float2(m, s);
+          if (nonfinite(s) || m == INFINITY) set_flag(status, kFlagNonFinite);
+        }
+      }
+    }
+  }
+}
+
 // Per-chunk statistics are (M_c, S_c): M_c the raw maximum of the row's scores
 // x over chunk c (before the temperature), S_c = sum_{v in c} exp((x_v - M_c)/T).
 // Chunk log-mass L_c = M_c/T + log S_c.  Everything below is kept relative to
@@ -197,16 +297,19 @@ __device__ inline float markov_bias(const float* e, const float* W2t, int rank, 
 }
 
 // ------------------------------------------------------------ block-level
-// Reductions across the NT/64 waves of an NT-thread block (NT <= 512) through
+// Reductions across the NT/64 waves of an NT-thread block (NT <= 1024) through
 // LDS; every thread of the block must call them (they contain barriers).
-struct BlockScratch {
-  float f[8];
-  int i[8];
-  float g[8];
+template <int NW>
+struct BlockScratchN {
+  float f[NW];
+  int i[NW];
+  float g[NW];
 };
+using BlockScratch = BlockScratchN<8>;       // blocks of up to 512 threads
+using BlockScratch16 = BlockScratchN<16>;    // blocks of up to 1024 threads
 
-template <int NT = 256>
-__device__ inline float block_max(float v, BlockScratch& sh) {
+template <int NT = 256, typename S = BlockScratch>
+__device__ inline float block_max(float v, S& sh) {
   constexpr int NWV = NT / 64;
   const int wv = threadIdx.x >> 6;
   v = wave_max(v);
@@ -218,8 +321,8 @@ __device__ inline float block_max(float v, BlockScratch& sh) {
   for (int q = 1; q < NWV; ++q) r = fmaxf(r, sh.f[q]);
   return r;
 }
-template <int NT = 256>
-__device__ inline float block_sum(float v, BlockScratch& sh) {
+template <int NT = 256, typename S = BlockScratch>
+__device__ inline float block_sum(float v, S& sh) {
   constexpr int NWV = NT / 64;
   const int wv = threadIdx.x >> 6;
   v = wave_sum(v);
@@ -236,8 +339,8 @@ __device__ inline float block_sum(float v, BlockScratch& sh) {
     for (int q = 0; q + w < NWV; q += 2 * w) r[q] += r[q + w];
   return r[0];
 }
-template <int NT = 256>
-__device__ inline void block_argmax(float& v, int& idx, BlockScratch& sh) {
+template <int NT = 256, typename S = BlockScratch>
+__device__ inline void block_argmax(float& v, int& idx, S& sh) {
   constexpr int NWV = NT / 64;
   const int wv = threadIdx.x >> 6;
   wave_argmax(v, idx);
@@ -252,12 +355,15 @@ __device__ inline void block_argmax(float& v, int& idx, BlockScratch& sh) {
 
 // Chunk-level Gumbel pick by an NT-thread block: thread t scans chunk blocks
 // t, t+NT, ... (four chunks per Philox block).  Returns the chunk and,
-// through *sum_rel, sum_c S_c exp((M_c - m)/T) (the row normaliser above m).
-template <int NT = 256>
+// through *sum_rel when it is not null, sum_c S_c exp((M_c - m)/T) (the row
+// normaliser above m).
+// COH: the statistics were written by other workgroups of the same launch
+// (device-coherent loads).
+template <int NT = 256, bool COH = false, typename S = BlockScratch>
 __device__ inline PickResult block_pick_chunk(const float2* st, int nch, float m, float invT,
                                               uint64_t seed, uint64_t round, uint32_t tag,
                                               uint32_t req, uint32_t k, bool want_gap,
-                                              float* sum_rel, BlockScratch& sh) {
+                                              float* sum_rel, S& sh) {
   float best = -INFINITY, ssum = 0.f;
   int bi = 0x7FFFFFFF;
   const bool draw = nch > 1;
@@ -268,7 +374,7 @@ __device__ inline PickResult block_pick_chunk(const float2* st, int nch, float m
     for (int w = 0; w < 4; ++w) {
       const int c = b * 4 + w;
       if (c < nch) {
-        const float2 v = st[c];
+        const float2 v = COH ? ld_coh2(st + c) : st[c];
         if (v.y > 0.f) {
           const float rel = (v.x - m) * invT;
           ssum += v.y * expf(rel);
@@ -278,7 +384,7 @@ __device__ inline PickResult block_pick_chunk(const float2* st, int nch, float m
       }
     }
   }
-  *sum_rel = block_sum<NT>(ssum, sh);
+  if (sum_rel) *sum_rel = block_sum<NT>(ssum, sh);
   block_argmax<NT>(best, bi, sh);
   PickResult r{best == -INFINITY ? -1 : bi, best, INFINITY};
   if (want_gap && r.idx >= 0 && draw) {
@@ -289,7 +395,7 @@ __device__ inline PickResult block_pick_chunk(const float2* st, int nch, float m
       for (int w = 0; w < 4; ++w) {
         const int c = b * 4 + w;
         if (c < nch && c != r.idx) {
-          const float2 v = st[c];
+          const float2 v = COH ? ld_coh2(st + c) : st[c];
           if (v.y > 0.f)
             second = fmaxf(second, (v.x - m) * invT + logf(v.y) + gumbel_of(word_of(blk, (uint32_t)w)));
         }
@@ -303,10 +409,10 @@ __device__ inline PickResult block_pick_chunk(const float2* st, int nch, float m
 // In-chunk Gumbel pick by an NT-thread block: NT/128 consecutive threads share
 // one entry; the first of them holds the score of entry base + t/(NT/128)
 // (-inf = excluded).
-template <int NT = 256>
+template <int NT = 256, typename S = BlockScratch>
 __device__ inline PickResult block_pick_in_chunk(float s, int base, uint64_t seed, uint64_t round,
                                                  uint32_t tag, uint32_t req, uint32_t k,
-                                                 bool want_gap, BlockScratch& sh) {
+                                                 bool want_gap, S& sh) {
   constexpr int TPE = NT / kChunk;
   const int t = threadIdx.x;
   const int v = base + t / TPE;

@@ -57,104 +57,6 @@ __device__ __forceinline__ void load_vec<float>(const float* p, float* out) {
   out[0] = u.x; out[1] = u.y; out[2] = u.z; out[3] = u.w;
 }
 
-template <int LPC>
-__device__ __forceinline__ float chunk_max(float v) {
-  v = row16_max(v);
-  if (LPC == 32) v = fmaxf(v, __shfl_xor(v, 16));
-  return v;
-}
-template <int LPC>
-__device__ __forceinline__ float chunk_sum(float v) {
-  v = row16_sum(v);
-  if (LPC == 32) v += __shfl_xor(v, 16);
-  return v;
-}
-template <int LPC>
-__device__ __forceinline__ void chunk_argmax(float& v, int& i) {
-  row16_argmax(v, i);
-  if (LPC == 32) argmax_merge(v, i, __shfl_xor(v, 16), __shfl_xor(i, 16));
-}
-
-// One wave: chunks [c0, c1) of one row.  UNR 16-byte loads per lane are in
-// flight at once; the data stays as raw words until it is used.
-template <typename T, bool GREEDY>
-__device__ __forceinline__ void row_segment(const T* row, int V, int c0, int c1, float scale2,
-                                            bool vec_ok, float2* L, int* I, uint32_t* status) {
-  constexpr int VPL = 16 / sizeof(T);       // values per lane per 16-byte load
-  constexpr int LPC = kChunk / VPL;         // lanes per chunk
-  constexpr int CPI = 64 / LPC;             // chunks per wave-wide load
-  constexpr int UNR = 8;                    // loads in flight per lane
-  const int lane = threadIdx.x & 63;
-  const int sub = lane % LPC;
-  const int cl = lane / LPC;
-  for (int cb = c0; cb < c1; cb += CPI * UNR) {
-    uint4 raw[UNR];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int c = cb + u * CPI + cl;
-      const int v0 = c * kChunk + sub * VPL;
-      if (c < c1 && vec_ok && v0 + VPL <= V) {
-        raw[u] = *reinterpret_cast<const uint4*>(row + v0);
-      } else {
-        // ragged tail: element loads, -inf past the segment or the vocabulary
-        uint32_t w[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (sizeof(T) == 2) {
-            const uint32_t lo = (c < c1 && v0 + 2 * q < V) ? reinterpret_cast<const uint16_t*>(row)[v0 + 2 * q] : 0xFF80u;
-            const uint32_t hi = (c < c1 && v0 + 2 * q + 1 < V) ? reinterpret_cast<const uint16_t*>(row)[v0 + 2 * q + 1] : 0xFF80u;
-            w[q] = lo | (hi << 16);
-          } else {
-            w[q] = (c < c1 && v0 + q < V) ? __float_as_uint(reinterpret_cast<const float*>(row)[v0 + q])
-                                          : __float_as_uint(-INFINITY);
-          }
-        }
-        raw[u] = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int c = cb + u * CPI + cl;
-      const int v0 = c * kChunk + sub * VPL;
-      float x[VPL];
-      {
-        const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-#pragma unroll
-        for (int e = 0; e < VPL; ++e)
-          x[e] = (sizeof(T) == 2) ? ((e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1])) : __uint_as_float(w[e]);
-      }
-      if (GREEDY) {
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
-#pragma unroll
-        for (int e = 0; e < VPL; ++e)
-          if (x[e] > bv) { bv = x[e]; bi = v0 + e; }
-        chunk_argmax<LPC>(bv, bi);
-        if (sub == 0 && c < c1) {
-          L[c] = make_float2(bv, 0.f);
-          I[c] = bi;
-          if (nonfinite(bv)) set_flag(status, kFlagNonFinite);
-        }
-      } else {
-        float m = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < VPL; ++e) m = fmaxf(m, x[e]);
-        m = chunk_max<LPC>(m);
-        float s = 0.f;
-        if (m != -INFINITY) {
-#pragma unroll
-          for (int e = 0; e < VPL; ++e) s += __builtin_amdgcn_exp2f((x[e] - m) * scale2);
-        }
-        s = chunk_sum<LPC>(s);
-        if (sub == 0 && c < c1) {
-          L[c] = make_float2(m, s);
-          if (nonfinite(s) || m == INFINITY) set_flag(status, kFlagNonFinite);
-        }
-      }
-    }
-  }
-}
-
 constexpr int kCuLds = 2048;               // verify offsets staged in LDS up to this many
 
 template <typename T, bool GREEDY>

@@ -6,23 +6,28 @@
 // norm(max(0, p_t - p_d)); after a fully accepted prefix draw the bonus token
 // from the next target distribution; tau = m + 1; greedy reduction).
 // Launches, all sized by capacity so N, m and the rejections stay on device:
-//   1. k_row_stats over the N verify rows: chunk log-masses of t/T (or chunk
-//      maxima at T = 0); also clears the residual work counter.
-//   2. k_row_norm, one wave per verify row: the row normaliser (raw maximum,
-//      log-sum above it) or, at T = 0, the row argmax.
-//   3. k_verify_scan, one workgroup per request: lane k-1 of the first wave
-//      evaluates position k (log p_t(x_k), its uniform, the accept test) for
-//      every k at once and a ballot finds the first rejection; then either the
-//      bonus draw (chunked Gumbel-max on the row after the accepted prefix)
-//      or a residual work item.  Cap-accept (DeepSpec analysis page, section
-//      5.4, DSpark in SGLang: the verify modes): with a commit window C below
-//      the accepted count m, the first C + 1 tokens of the sequence are
-//      committed, the last being the accepted draft x_{C+1}; no draw is made.
-//   4. residual chunk masses for the listed (request, position) rows: the
+//   1. k_verify_rows, one workgroup per verify row: the row's chunk
+//      log-masses of t/T (chunk maxima at T = 0) and normaliser, the accept
+//      test of the position it decides (log p_t(x_k), its uniform), the bonus
+//      draw from a request's last row; the workgroup that completes a request
+//      finds its first rejection by a ballot over the published outcomes and
+//      writes the outputs, or lists a residual work item.  Cap-accept
+//      (DeepSpec analysis page, section 5.4, DSpark in SGLang: the verify
+//      modes): with a commit window C below the accepted count m, the first
+//      C + 1 tokens of the sequence are committed, the last being the accepted
+//      draft x_{C+1}; no draw is made.  Rows of more than kVrMaxChunks chunks
+//      take three launches instead: k_row_stats, k_row_norm (one wave per
+//      row) and k_verify_scan (one workgroup per request).
+//   2. residual chunk masses for the listed (request, position) rows: the
 //      draft scores are rebuilt with the Markov bias (MFMA) and combined with
-//      the target row into max(0, p_t - p_d) per chunk.
-//   5. k_resid_pick, one workgroup per work item: chunk pick and in-chunk pick
-//      on log max(0, p_t - p_d); zero mass falls back to p_t.
+//      the target row into max(0, p_t - p_d) per chunk; on the W2-slice
+//      layout the same pass draws every chunk's in-chunk winner.
+//   3. k_resid_pick, one workgroup per work item: chunk pick on the residual
+//      masses, then the chunk's winner (or, without winners, the in-chunk
+//      pick on log max(0, p_t - p_d) rebuilt here); zero mass falls back to
+//      p_t.
+#include <atomic>
+
 #include "launch.hpp"
 #include "sampling.hpp"
 #include "workspace.hpp"
@@ -58,7 +63,18 @@ struct VerifyArgs {
   int32_t* rej_count;
   int4* rej;            // (request, position, target row, verify row q)
   const float2* rl;     // [slot][nch] residual chunk masses (0, sum)
+  const int* rw;        // nullable [slot][nch] in-chunk winners of the residual
   uint32_t* status;
+  // fused verify rows
+  float2* vl_out;       // = vl, written by the fused kernel
+  int* req_done;        // [R] rows finished per request
+  int* ybonus;          // [R] bonus token drawn from the request's last row
+  int* acc;             // [R][gamma] outcome of each tested position (1 = rejected)
+  uint32_t* epoch_word; // header word raised by workgroup 0 once the counters are clear
+  uint32_t epoch;       // this call's epoch
+  uint32_t spin_limit;  // polls before the wait for the epoch gives up
+  float scale2;         // log2(e) / T (chunk sums), 1 at T = 0
+  bool vec_ok;          // 16-byte loads of target rows
 };
 
 __device__ __forceinline__ int64_t target_row(const VerifyArgs& a, int i, int j) {
@@ -84,15 +100,15 @@ __global__ __launch_bounds__(256) void k_row_norm(VerifyArgs a) {
   }
 }
 
-template <typename TT>
-__global__ __launch_bounds__(256) void k_verify_scan(VerifyArgs a) {
-  __shared__ BlockScratch sh;
-  __shared__ int s_m, s_rej;
-  const int i = blockIdx.x;
+// The accept scan of request i and its outputs, by one workgroup of NT
+// threads, from the row normalisers and chunk statistics in memory (the
+// three-launch verify for rows too long to keep in LDS).
+template <int NT, typename TT>
+__device__ inline void scan_request(const VerifyArgs& a, int i, int q0, BlockScratch& sh,
+                                    int* s_m, int* s_rej) {
   const int tid = threadIdx.x, lane = tid & 63;
   int L = a.ell[i];
   if (L < 0 || L > a.gamma) { if (tid == 0) set_flag(a.status, kFlagBadLen); L = L < 0 ? 0 : a.gamma; }
-  const int q0 = a.cu[i];
   const int32_t* xi = a.x + (int64_t)i * (a.gamma + 1);
   const TT* tgt = reinterpret_cast<const TT*>(a.target);
   if (tid < 64) {
@@ -120,13 +136,13 @@ __global__ __launch_bounds__(256) void k_verify_scan(VerifyArgs a) {
     }
     const uint64_t bal = __ballot(rej);
     if (lane == 0) {
-      s_rej = bal != 0;
-      s_m = bal ? (__builtin_ctzll(bal)) : L;   // first rejected position k = m + 1
+      *s_rej = bal != 0;
+      *s_m = bal ? (__builtin_ctzll(bal)) : L;   // first rejected position k = m + 1
     }
   }
   __syncthreads();
-  int m = s_m;
-  bool rejected = s_rej != 0;
+  int m = *s_m;
+  bool rejected = *s_rej != 0;
   int y = -1;
   // cap-accept: when more drafts were accepted than the commit window holds,
   // the window closes on the accepted draft x_{C+1} (no correction, no bonus)
@@ -154,16 +170,16 @@ __global__ __launch_bounds__(256) void k_verify_scan(VerifyArgs a) {
     const int q = q0 + L;
     const float2 nt = a.lse_t[q];
     float srel;
-    const PickResult pc = block_pick_chunk<256>(a.vl + (int64_t)q * a.nch, a.nch, nt.x, a.invT,
-                                                a.seed, a.round, kTagBonusChunk, (uint32_t)i,
-                                                (uint32_t)(L + 1), false, &srel, sh);
+    const PickResult pc = block_pick_chunk<NT>(a.vl + (int64_t)q * a.nch, a.nch, nt.x, a.invT,
+                                               a.seed, a.round, kTagBonusChunk, (uint32_t)i,
+                                               (uint32_t)(L + 1), false, &srel, sh);
     const int c = pc.idx < 0 ? 0 : pc.idx;
     if (pc.idx < 0 && tid == 0) set_flag(a.status, kFlagNonFinite);
     const TT* trow = tgt + target_row(a, i, L) * a.V;
-    const int v = c * kChunk + (tid >> 1);
-    const float s = (v < a.V) ? (Elem<TT>::get(trow, v) - nt.x) * a.invT : -INFINITY;
-    const PickResult pe = block_pick_in_chunk<256>(s, c * kChunk, a.seed, a.round, kTagBonusElem,
-                                                   (uint32_t)i, (uint32_t)(L + 1), false, sh);
+    const int v = c * kChunk + tid / (NT / kChunk);
+    const float sc = (v < a.V) ? (Elem<TT>::get(trow, v) - nt.x) * a.invT : -INFINITY;
+    const PickResult pe = block_pick_in_chunk<NT>(sc, c * kChunk, a.seed, a.round, kTagBonusElem,
+                                                  (uint32_t)i, (uint32_t)(L + 1), false, sh);
     y = pe.idx < 0 ? c * kChunk : pe.idx;
   } else if (tid == 0) {
     const int slot = atomicAdd(a.rej_count, 1);
@@ -172,13 +188,249 @@ __global__ __launch_bounds__(256) void k_verify_scan(VerifyArgs a) {
   // outputs (a rejected sampled position gets its token from k_resid_pick)
   int32_t* em = a.emitted + (int64_t)i * (a.gamma + 1);
   const bool have_y = closed || a.greedy || !rejected;
-  for (int q = tid; q <= a.gamma; q += 256)
+  for (int q = tid; q <= a.gamma; q += NT)
     em[q] = (q < m) ? xi[q + 1] : ((q == m && have_y) ? y : -1);
   if (tid == 0) {
     a.m[i] = m;
     a.tau[i] = m + 1;
     if (have_y) a.next_anchor[i] = y;
   }
+}
+
+template <typename TT>
+__global__ __launch_bounds__(256) void k_verify_scan(VerifyArgs a) {
+  __shared__ BlockScratch sh;
+  __shared__ int s_m, s_rej;
+  const int i = blockIdx.x;
+  scan_request<256, TT>(a, i, a.cu[i], sh, &s_m, &s_rej);
+}
+
+// ------------------------------------------------------- fused verify rows
+// One launch for the verify rows: statistics of every verify row, its
+// normaliser, every position's accept test, and the accept scan of every
+// request.  One workgroup of kVrThreads per verify row q = cu[i] + j:
+//   1. finds its request i (the one whose offsets hold q) and streams the
+//      target row into per-chunk statistics in LDS (each wave one batch of
+//      kVrUnr loads per lane, the arithmetic of the stand-alone statistics
+//      kernel);
+//   2. writes them to memory (read later by the residual kernels), reduces
+//      them to the row normaliser and publishes it (device-coherent store);
+//   3. j < ell_i: tests position k = j + 1 (log p_t(x_k) is this row's) and
+//      publishes the outcome; j == ell_i at T > 0: draws the bonus token from
+//      its own statistics (used if the whole block is accepted);
+//   4. counts itself done for request i; the workgroup that completes the
+//      request finds the first rejection from the published outcomes and
+//      writes the request's outputs.
+// After step 3 only the first wave goes on (the counter update, the scan);
+// the others write the chunk statistics out and leave.
+// The completion counters and the residual count are cleared inside the
+// launch by workgroup 0, which then raises the launch's epoch in a header
+// word; a workgroup waits for that epoch (bounded) before its counter update.
+// Workgroup 0 is dispatched before every other, so the wait ends.  The epoch
+// is new for every call, so no state has to survive between calls.
+constexpr int kVrThreads = 512;
+constexpr int kVrWaves = kVrThreads / 64;
+constexpr int kVrUnr = 8;                   // 16-byte loads in flight per lane
+constexpr int kVrMaxChunks = 4096;          // per-row statistics held in LDS
+
+// The scan of request i from the outcomes its rows published in this launch,
+// by one wave: one round of device-coherent loads, a ballot, the outputs.
+template <bool GREEDY>
+__device__ inline void scan_published(const VerifyArgs& a, int i, int q0, int L) {
+  const int lane = threadIdx.x & 63;
+  const int32_t* xi = a.x + (int64_t)i * (a.gamma + 1);
+  const int k = lane + 1;
+  const bool rej_k = k <= L && ld_coh(a.acc + (int64_t)i * a.gamma + (k - 1)) != 0;
+  int yl = -1;
+  if (GREEDY && lane <= L) yl = __float_as_int(ld_coh2(a.lse_t + q0 + lane).y);   // argmax of row `lane`
+  if (!GREEDY && lane == 0) yl = ld_coh(a.ybonus + i);
+  if (k > L && k <= a.gamma && a.logp_t) a.logp_t[(int64_t)i * a.gamma + (k - 1)] = 0.f;
+  const uint64_t bal = __ballot(rej_k);
+  int m = bal ? __builtin_ctzll(bal) : L;       // first rejected position k = m + 1
+  int y = __shfl(yl, GREEDY ? m : 0);
+  bool rejected = bal != 0;
+  bool closed = false;
+  if (a.cap) {
+    int C = a.cap[i];
+    if (C < 0) { if (lane == 0) set_flag(a.status, kFlagBadLen); C = 0; }
+    if (C > L) C = L;
+    if (lane == 0 && a.m_full) a.m_full[i] = m;
+    if (m > C) {
+      closed = true;
+      m = C;
+      rejected = false;
+    }
+  }
+  if (closed) {
+    y = xi[m + 1];                      // the accepted draft that closes the window
+    if (y < 0 || y >= a.V) y = 0;       // (flagged by the position's test)
+  } else if (GREEDY || !rejected) {
+    // greedy: the argmax of row m; sampled: the bonus token drawn from row L
+    if (y < 0 || y >= a.V) { if (lane == 0) set_flag(a.status, kFlagNonFinite); y = 0; }
+  } else if (lane == 0) {
+    const int slot = atomicAdd(a.rej_count, 1);
+    a.rej[slot] = make_int4(i, m + 1, (int)target_row(a, i, m), q0 + m);
+  }
+  int32_t* em = a.emitted + (int64_t)i * (a.gamma + 1);
+  const bool have_y = closed || GREEDY || !rejected;
+  for (int q = lane; q <= a.gamma; q += 64)
+    em[q] = (q < m) ? xi[q + 1] : ((q == m && have_y) ? y : -1);
+  if (lane == 0) {
+    a.m[i] = m;
+    a.tau[i] = m + 1;
+    if (have_y) a.next_anchor[i] = y;
+  }
+}
+
+template <typename T, bool GREEDY>
+__global__ __launch_bounds__(kVrThreads) void k_verify_rows(VerifyArgs a) {
+  extern __shared__ __align__(16) unsigned char vr_lds[];
+  float2* sL = reinterpret_cast<float2*>(vr_lds);
+  int* sI = reinterpret_cast<int*>(vr_lds + (size_t)a.nch * sizeof(float2));
+  __shared__ BlockScratch sh;
+  __shared__ int s_i, s_lo, s_hi, s_ell;
+  const int tid = threadIdx.x, wv = tid >> 6;
+  const int q = blockIdx.x;
+  if (q == 0) {
+    for (int t = tid; t < a.R; t += kVrThreads) st_coh(a.req_done + t, 0);
+    if (tid == 0) st_coh(a.rej_count, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0): the clears have completed
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(a.epoch_word, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const int N = min(a.cu[a.R], a.R * (a.gamma + 1));
+  if (q >= N) return;
+  // the request whose offsets hold q, and its scheduled length
+  if (tid == 0) s_i = -1;
+  __syncthreads();
+  for (int t = tid; t < a.R; t += kVrThreads) {
+    const int lo = a.cu[t], hi = a.cu[t + 1], el = a.ell[t];
+    if (lo <= q && q < hi) { s_i = t; s_lo = lo; s_hi = hi; s_ell = el; }
+  }
+  __syncthreads();
+  const int i = s_i;
+  if (i < 0) {                                  // offsets not ascending
+    if (tid == 0) set_flag(a.status, kFlagBadLen);
+    return;
+  }
+  const int q0 = s_lo, nrows = s_hi - s_lo, j = q - q0;
+  if (nrows > a.gamma + 1) {                    // more rows than the block holds
+    if (tid == 0) set_flag(a.status, kFlagBadLen);
+    return;
+  }
+  int L = s_ell;
+  if (L < 0 || L > a.gamma || L > nrows - 1) {
+    if (tid == 0 && j == 0) set_flag(a.status, kFlagBadLen);
+    L = min(max(L, 0), min(a.gamma, nrows - 1));
+  }
+  const int64_t row = a.layout == 0 ? (int64_t)q : (int64_t)i * (a.gamma + 1) + j;
+  const T* rp = reinterpret_cast<const T*>(a.target) + row * a.V;
+  // the token this row tests and its draft log-probability, fetched ahead
+  int xk = 0;
+  float lpd = 0.f;
+  if (tid == 0 && j < L) {
+    xk = a.x[(int64_t)i * (a.gamma + 1) + j + 1];
+    if (!GREEDY) lpd = a.logp_d[(int64_t)i * a.gamma + j];
+  }
+
+  // 1. chunk statistics of the row into LDS: batches of CPB chunks per wave
+  constexpr int CPB = 64 * kVrUnr / (kChunk * (int)sizeof(T) / 16);
+  for (int c0 = wv * CPB; c0 < a.nch; c0 += kVrWaves * CPB)
+    row_segment<T, GREEDY, kVrUnr>(rp, a.V, c0, min(a.nch, c0 + CPB), a.scale2, a.vec_ok, sL, sI,
+                                   a.status);
+  // the tested token's score (its row was just streamed), in flight during
+  // the reductions below
+  float tk = 0.f;
+  if (!GREEDY && tid == 0 && j < L) tk = Elem<T>::get(rp, (xk < 0 || xk >= a.V) ? 0 : xk);
+  __syncthreads();
+
+  // 2. the row normaliser (raw maximum, log-sum above it), or at T = 0 the
+  // row maximum and its first argmax
+  float2 nt;
+  if (GREEDY) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int c = tid; c < a.nch; c += kVrThreads) argmax_merge(bv, bi, sL[c].x, sI[c]);
+    block_argmax<kVrThreads>(bv, bi, sh);
+    nt = make_float2(bv, __int_as_float(bi));
+  } else {
+    float mx = -INFINITY;
+    for (int c = tid; c < a.nch; c += kVrThreads) mx = fmaxf(mx, sL[c].x);
+    const float m = block_max<kVrThreads>(mx, sh);
+    float sum = 0.f;
+    if (m != -INFINITY) {
+      for (int c = tid; c < a.nch; c += kVrThreads) {
+        const float2 v = sL[c];
+        if (v.y > 0.f) sum += v.y * expf((v.x - m) * a.invT);
+      }
+    }
+    sum = block_sum<kVrThreads>(sum, sh);
+    nt = (m == -INFINITY) ? make_float2(-INFINITY, -INFINITY)
+                          : make_float2(m, sum > 0.f ? logf(sum) : -INFINITY);
+  }
+  if (tid == 0) st_coh2(a.lse_t + q, nt);
+
+  // 3. the test of position j + 1, or the bonus draw from the last row
+  if (tid == 0 && j < L) {
+    const int k = j + 1;
+    if (xk < 0 || xk >= a.V) { set_flag(a.status, kFlagBadToken); xk = 0; }
+    int rej;
+    if (GREEDY) {
+      rej = xk != __float_as_int(nt.y);
+      if (a.logp_t) a.logp_t[(int64_t)i * a.gamma + j] = 0.f;
+    } else {
+      const float lp = (tk - nt.x) * a.invT - nt.y;
+      if (a.logp_t) a.logp_t[(int64_t)i * a.gamma + j] = lp;
+      const uint4 blk = stream_block(a.seed, a.round, kTagAccept, (uint32_t)i, (uint32_t)k, 0u);
+      rej = !(log_uniform(blk.x) < lp - lpd);
+    }
+    st_coh(a.acc + (int64_t)i * a.gamma + j, rej);
+  }
+  if (!GREEDY && j == L) {
+    const PickResult pc = block_pick_chunk<kVrThreads>(sL, a.nch, nt.x, a.invT, a.seed, a.round,
+                                                       kTagBonusChunk, (uint32_t)i,
+                                                       (uint32_t)(L + 1), false, nullptr, sh);
+    const int c = pc.idx < 0 ? 0 : pc.idx;
+    if (pc.idx < 0 && tid == 0) set_flag(a.status, kFlagNonFinite);
+    const int v = c * kChunk + tid / (kVrThreads / kChunk);
+    const float sc = (v < a.V) ? (Elem<T>::get(rp, v) - nt.x) * a.invT : -INFINITY;
+    const PickResult pe = block_pick_in_chunk<kVrThreads>(sc, c * kChunk, a.seed, a.round,
+                                                          kTagBonusElem, (uint32_t)i,
+                                                          (uint32_t)(L + 1), false, sh);
+    if (tid == 0) st_coh(a.ybonus + i, pe.idx < 0 ? c * kChunk : pe.idx);
+  }
+  // the chunk statistics, read only by the residual kernels of later
+  // launches, are written by the other waves, which then leave
+  if (wv != 0) {
+    if (!GREEDY) {
+      float2* gL = a.vl_out + (int64_t)q * a.nch;
+      for (int c = tid - 64; c < a.nch; c += kVrThreads - 64) gL[c] = sL[c];
+    }
+    return;
+  }
+  const int lane = tid;
+
+  // 4. done with row q: the wave's stores have completed, then one counter
+  // update; the wave that completes request i scans it
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  int last = 0;
+  if (lane == 0) {
+    uint32_t spins = 0;
+    while (__hip_atomic_load(a.epoch_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
+      if (++spins >= a.spin_limit) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (spins >= a.spin_limit) {
+      atomicOr(a.status, kFlagBarrier);
+    } else {
+      const int done = __hip_atomic_fetch_add(a.req_done + i, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+      last = done + 1 == nrows;
+    }
+  }
+  if (!__shfl(last, 0)) return;
+  scan_published<GREEDY>(a, i, q0, L);
 }
 
 template <typename UT, typename WT>
@@ -198,7 +450,15 @@ __global__ __launch_bounds__(256) void k_resid_pick(VerifyArgs a) {
                                               (uint32_t)i, (uint32_t)k, false, &mass, sh);
   const int v_off = tid >> 1, h = tid & 1;
   int y;
-  if (mass > 0.f) {
+  if (mass > 0.f && a.rw) {
+    // the in-chunk winner was drawn with the masses
+    const int c = pr.idx < 0 ? 0 : pr.idx;
+    y = a.rw[(int64_t)slot * a.nch + c];
+    if (y < 0) {
+      if (tid == 0) set_flag(a.status, kFlagNonFinite);
+      y = c * kChunk;
+    }
+  } else if (mass > 0.f) {
     const int c = pr.idx < 0 ? 0 : pr.idx;
     const int v = c * kChunk + v_off;
     const UT* urow = reinterpret_cast<const UT*>(a.U) + ((int64_t)i * a.gamma + (k - 1)) * a.V;
@@ -370,6 +630,15 @@ hipError_t launch_acceptance_rate(int R, int gamma, int V, int rank, float T, co
   return hipGetLastError();
 }
 
+// A new epoch for every fused verify launch (never 0, the value a cleared
+// workspace holds).
+static uint32_t next_verify_epoch() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  if (e == 0) e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  return e;
+}
+
 hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,
                          const int32_t* ell, const int32_t* cu, const void* target, int layout,
                          const int32_t* x, const float* logp_d, const float* lse_d,
@@ -386,20 +655,6 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
   const bool t_vec = ((reinterpret_cast<uintptr_t>(target) & 15) == 0) && (((size_t)V * usz) % 16 == 0);
   const bool u_vec = ((reinterpret_cast<uintptr_t>(U) & 15) == 0) && (((size_t)V * usz) % 16 == 0);
 
-  RowStatsArgs rs{};
-  rs.base = target;
-  rs.kind = layout == 0 ? kRowsVerifyPacked : kRowsVerifyDense;
-  rs.R = R; rs.gamma = gamma; rs.k = 0; rs.V = V; rs.nch = nch; rs.cu = cu;
-  rs.nrows_cap = R * (gamma + 1);
-  rs.scale2 = greedy ? 1.f : kLog2e / T;
-  rs.vec_ok = t_vec;
-  rs.L = reinterpret_cast<float2*>(w + L.ver_l);
-  rs.I = reinterpret_cast<int*>(w + L.ver_i);
-  rs.status = hdr;
-  rs.zero_me = hdr + 1;
-  hipError_t e = launch_row_stats(rs, u_bf16, greedy, st);
-  if (e != hipSuccess) return e;
-
   VerifyArgs a{};
   a.R = R; a.gamma = gamma; a.V = V; a.rank = rank; a.nch = nch; a.layout = layout;
   a.invT = greedy ? 1.f : 1.f / T; a.greedy = greedy; a.seed = seed; a.round = round;
@@ -407,30 +662,63 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
   a.U = U; a.W1 = W1; a.W2t = W2t; a.m = m; a.tau = tau; a.emitted = emitted;
   a.next_anchor = next_anchor; a.logp_t = logp_t; a.cap = cap; a.m_full = m_full;
   a.feat = feat;
-  a.vl = rs.L; a.vi = rs.I;
+  a.vl = reinterpret_cast<const float2*>(w + L.ver_l);
+  a.vi = reinterpret_cast<const int*>(w + L.ver_i);
   a.lse_t = reinterpret_cast<float2*>(w + L.lse_t);
   a.rej_count = reinterpret_cast<int32_t*>(hdr + 1);
   a.rej = reinterpret_cast<int4*>(w + L.rej);
   a.rl = reinterpret_cast<float2*>(w + L.draft_l);
   a.status = hdr;
-  {
-    const int rows = R * (gamma + 1);
-    const int grid = min(4096, (rows + 3) / 4);
-    hipLaunchKernelGGL(k_row_norm, dim3(grid), dim3(256), 0, st, a);
+  a.scale2 = greedy ? 1.f : kLog2e / T;
+  a.vec_ok = t_vec;
+  const int rows = R * (gamma + 1);
+  hipError_t e;
+  if (nch <= kVrMaxChunks) {
+    // statistics, normalisers and the accept scan in one launch
+    a.vl_out = reinterpret_cast<float2*>(w + L.ver_l);
+    a.req_done = reinterpret_cast<int*>(w + L.vaux);
+    a.ybonus = a.req_done + R;
+    a.acc = a.ybonus + R;
+    a.epoch_word = hdr + 3;
+    a.epoch = next_verify_epoch();
+    a.spin_limit = switches().barrier_spins ? switches().barrier_spins : kBarrierSpins;
+    const size_t lds = (size_t)nch * (greedy ? 12 : 8);
+#define DSPARK_VR(T_, G_) hipLaunchKernelGGL((k_verify_rows<T_, G_>), dim3(rows), dim3(kVrThreads), lds, st, a)
+    if (u_bf16) { if (greedy) DSPARK_VR(uint16_t, true); else DSPARK_VR(uint16_t, false); }
+    else        { if (greedy) DSPARK_VR(float, true);    else DSPARK_VR(float, false); }
+#undef DSPARK_VR
+  } else {
+    // rows too long for the statistics to stay in LDS: three launches
+    RowStatsArgs rs{};
+    rs.base = target;
+    rs.kind = layout == 0 ? kRowsVerifyPacked : kRowsVerifyDense;
+    rs.R = R; rs.gamma = gamma; rs.k = 0; rs.V = V; rs.nch = nch; rs.cu = cu;
+    rs.nrows_cap = rows;
+    rs.scale2 = a.scale2;
+    rs.vec_ok = t_vec;
+    rs.L = reinterpret_cast<float2*>(w + L.ver_l);
+    rs.I = reinterpret_cast<int*>(w + L.ver_i);
+    rs.status = hdr;
+    rs.zero_me = hdr + 1;
+    e = launch_row_stats(rs, u_bf16, greedy, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_row_norm, dim3(min(4096, (rows + 3) / 4)), dim3(256), 0, st, a);
+    if (u_bf16) hipLaunchKernelGGL((k_verify_scan<uint16_t>), dim3(R), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_verify_scan<float>), dim3(R), dim3(256), 0, st, a);
   }
-  if (u_bf16) hipLaunchKernelGGL((k_verify_scan<uint16_t>), dim3(R), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_verify_scan<float>), dim3(R), dim3(256), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess || greedy) return e;
 
   // rows of the bias features: W1[x_{k-1}] (Markov head) or the draft's own
   // per-position features (RNN head)
   const void* E = feat ? feat : W1;
+  int* winners = reinterpret_cast<int*>(w + L.draft_i);
   if (u_bf16 && w_bf16 && rank > 0 && u_vec && t_vec &&
       launch_resid_slices(R, gamma, V, rank, T, U, E, W2t, target, x, a.rej_count, a.rej,
                           a.lse_t, lse_d, const_cast<float2*>(a.rl), hdr, st, &e, false,
-                          feat != nullptr)) {
+                          feat != nullptr, winners, seed, round)) {
     if (e != hipSuccess) return e;
+    a.rw = winners;
   } else {
     // per-tile kernel for the other shapes
     MarkovArgs ma{};

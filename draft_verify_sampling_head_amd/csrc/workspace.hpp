@@ -11,13 +11,16 @@
 namespace dspark {
 
 struct WsLayout {
-  size_t header;       // uint32 words: [0] status flags, [1] residual count
+  size_t header;       // uint32 words: [0] status flags, [1] residual count,
+                       // [2] pipelined-draft epoch, [3] verify epoch
   size_t draft_l;      // float2 [R][nch]   chunk (max, scaled sum) / residual masses
-  size_t draft_i;      // int32  [R][nch]   chunk argmax (greedy)
+  size_t draft_i;      // int32  [R][nch]   chunk argmax (greedy) / residual in-chunk winners
   size_t ver_l;        // float2 [R*(gamma+1)][nch]  target-row chunk (max, scaled sum)
   size_t ver_i;        // int32  [R*(gamma+1)][nch]  target-row chunk argmax (greedy)
   size_t lse_t;        // float2 [R*(gamma+1)]       target-row (max, log-normaliser above it)
   size_t rej;          // int32  [R][4]   residual work list: request, position, row, pad
+  size_t vaux;         // int32  [R][2 + gamma] verify: rows finished and bonus token per
+                       // request, outcome of every tested position
   size_t bar;          // uint32 [1024] grid-barrier flags of the persistent draft, one per workgroup
   size_t rec;          // 16-byte [2][R][ceil(V/512)] per-slice records of the pipelined draft
   size_t total;
@@ -40,6 +43,7 @@ inline WsLayout ws_layout(int R, int gamma, int V) {
   L.ver_i = off;   off += ws_align(rows_v * nch * 4);
   L.lse_t = off;   off += ws_align(rows_v * 8);
   L.rej = off;     off += ws_align((size_t)R * 16);
+  L.vaux = off;    off += ws_align((size_t)R * (gamma + 2) * 4);
   L.bar = off;     off += ws_align(4 * 1024);
   L.rec = off;     off += ws_align(2 * (size_t)R * ws_nslice(V) * 16);
   L.total = off;

@@ -117,6 +117,9 @@ SMALL = [
     (2, dict(R=24, gamma=4, V=1800, d=64, T=2.0, scheduler=False)),
     (2, dict(R=300, gamma=3, V=2048, d=32, rank=128)),                   # two 256-row groups
     (1, dict(R=260, gamma=3, V=4096, d=32, rank=64)),                    # greedy, two row groups
+    # rows of more than 4096 chunks: verify statistics outside LDS (three launches)
+    (2, dict(R=3, gamma=2, V=600_001, d=32, rank=16)),
+    (1, dict(R=2, gamma=2, V=530_000, d=32, rank=0)),
 ]
 
 
@@ -248,6 +251,31 @@ def test_barrier_wait_is_bounded(switch, kernel):
                         buf.logp_d, buf.lse_d, buf.ws)
     torch.cuda.synchronize()
     assert D.get_status(buf.ws) == 0
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0], ids=["sampled", "greedy"])
+def test_verify_epoch_wait_is_bounded(switch, T):
+    # a one-poll limit on the fused verify's wait for its cleared counters:
+    # the launch must still finish; a wait that gave up is reported through
+    # the status word, and otherwise the outputs equal those of a run with
+    # the default limit
+    cfg = synth.scaled(synth.config(2), R=64, gamma=4, V=4096, d=32, T=T)
+    inp = to_dev(synth.make_inputs(cfg, device="cpu"))
+    outs = []
+    for spins in (0, 1, 0):
+        switch(D._lib.SWITCH_BARRIER_SPINS, spins)
+        buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV)
+        D.clear_status(buf.ws)
+        RD.run_round(inp, buf, cfg.T, cfg.philox_seed, 0, scheduler=cfg.scheduler)
+        torch.cuda.synchronize()
+        st = D.get_status(buf.ws)
+        outs.append((st, n(buf.m), n(buf.tau), n(buf.emitted), n(buf.next_anchor)))
+    assert outs[0][0] == 0 and outs[2][0] == 0
+    for a, b in zip(outs[0][1:], outs[2][1:]):
+        np.testing.assert_array_equal(a, b)
+    if not outs[1][0] & D._lib.FLAG_BARRIER:
+        for a, b in zip(outs[0][1:], outs[1][1:]):
+            np.testing.assert_array_equal(a, b)
 
 
 # -------------------------------------------------------- stage: scheduler
