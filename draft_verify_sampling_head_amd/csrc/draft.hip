@@ -646,26 +646,16 @@ struct ResidArgs {
   const float2* lse_t;                      // [verify row] (raw max, log-normaliser above it)
   const float* lse_d;
   float2* L;                                // out [slot][nch] (0, residual mass)
-  int* W;                                   // out nullable [slot][nch] in-chunk winner (residual)
-  uint64_t seed, round;                     // sampler stream of the in-chunk winners
   uint32_t* status;
   bool feat_rows;                           // W1 holds per-position features [R][gamma][rank]
 };
 
-//
-// With W (residual mode) the kernel also draws, for every listed row and
-// chunk, the chunk's in-chunk Gumbel-max winner over log max(0, p_t - p_d)
-// with the sampler's in-chunk stream: the residual pick then only has to
-// choose the chunk (the two levels of the chunked sampler are independent).
 template <int KS, bool OVERLAP>
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_resid_stats(ResidArgs A) {
   constexpr int SEG = 2 * KS, ROWP = SEG + 1, KT = KS / 2;
   __shared__ uint4 E[kPRows * ROWP];
   __shared__ float HS[kPRows * kPWaves];
-  __shared__ float HK[OVERLAP ? 1 : kPRows * kPWaves];   // best in-chunk key per (row, wave)
-  __shared__ int HI[OVERLAP ? 1 : kPRows * kPWaves];     // and its entry
-  __shared__ int RK[OVERLAP ? 1 : kPRows];               // request << 6 | position, per row
   __shared__ int PV[kPRows];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int b = blockIdx.x;
@@ -698,7 +688,6 @@ void k_resid_stats(ResidArgs A) {
         if (prev < 0 || prev >= V) { set_flag(A.status, kFlagBadToken); prev = 0; }
       }
       PV[rl] = prev;
-      if (!OVERLAP) RK[rl] = (e.x << 6) | e.y;
     }
     __syncthreads();
     gather_w1_rows<SEG, ROWP>(E, PV, rows, A.W1, A.rank);
@@ -733,15 +722,8 @@ void k_resid_stats(ResidArgs A) {
         for (int j = 0; j < 16; ++j) acc[j >> 2][j & 3] += u_piece(cur.u[j >> 3], j & 7);
         const float lrt2 = cur.nt.y * kLog2e;
         float S = 0.f;
-        float bk = -INFINITY;                 // in-chunk winner of this lane's entries
-        int bv = 0x7FFFFFFF;
-        uint4 gb = make_uint4(0, 0, 0, 0);    // sampler block of entries 4 (j / 4) .. + 3
-        const int rkey = (!OVERLAP && A.W) ? RK[min(rl, rows - 1)] : 0;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          if (!OVERLAP && A.W && (j & 3) == 0)
-            gb = stream_block(A.seed, A.round, kTagResidElem, (uint32_t)(rkey >> 6),
-                              (uint32_t)(rkey & 63), (uint32_t)(uoff[j >> 3] + (j & 4)) >> 2);
           if (uok[j >> 3]) {
             const uint32_t w = (j & 8) ? ((j & 4) ? ((j & 2) ? cur.t[1].w : cur.t[1].z)
                                                   : ((j & 2) ? cur.t[1].y : cur.t[1].x))
@@ -751,29 +733,14 @@ void k_resid_stats(ResidArgs A) {
             const float pt = __builtin_amdgcn_exp2f((tv - cur.nt.x) * s2 - lrt2);
             const float pd = __builtin_amdgcn_exp2f((acc[j >> 2][j & 3] * invT - cur.ld) * kLog2e);
             S += OVERLAP ? fminf(pt, pd) : fmaxf(pt - pd, 0.f);
-            if (!OVERLAP && A.W) {
-              const float d = pt - pd;
-              if (d > 0.f) {
-                const int v = uoff[j >> 3] + (j & 7);
-                argmax_merge(bk, bv, logf(d) + gumbel_of(word_of(gb, (uint32_t)v & 3u)), v);
-              }
-            }
           }
         }
         S += __shfl_xor(S, 16);
         S += __shfl_xor(S, 32);
         if (lg == 0 && rl < rows) HS[rl * kPWaves + wv] = S;
-        if (!OVERLAP && A.W) {
-          argmax_merge(bk, bv, __shfl_xor(bk, 16), __shfl_xor(bv, 16));
-          argmax_merge(bk, bv, __shfl_xor(bk, 32), __shfl_xor(bv, 32));
-          if (lg == 0 && rl < rows) { HK[rl * kPWaves + wv] = bk; HI[rl * kPWaves + wv] = bv; }
-        }
       }
     } else {
-      for (int rl = lane; rl < rows; rl += 64) {
-        HS[rl * kPWaves + wv] = 0.f;
-        if (!OVERLAP && A.W) { HK[rl * kPWaves + wv] = -INFINITY; HI[rl * kPWaves + wv] = 0x7FFFFFFF; }
-      }
+      for (int rl = lane; rl < rows; rl += 64) HS[rl * kPWaves + wv] = 0.f;
     }
     __syncthreads();
     for (int t = tid; t < rows * 4; t += kPThreads) {
@@ -783,12 +750,6 @@ void k_resid_stats(ResidArgs A) {
       const float St = HS[rl * kPWaves + 2 * c] + HS[rl * kPWaves + 2 * c + 1];
       A.L[(int64_t)(row0 + rl) * A.nch + chunk] = make_float2(0.f, St);
       if (nonfinite(St)) set_flag(A.status, kFlagNonFinite);
-      if (!OVERLAP && A.W) {
-        float k0 = HK[rl * kPWaves + 2 * c];
-        int v0 = HI[rl * kPWaves + 2 * c];
-        argmax_merge(k0, v0, HK[rl * kPWaves + 2 * c + 1], HI[rl * kPWaves + 2 * c + 1]);
-        A.W[(int64_t)(row0 + rl) * A.nch + chunk] = k0 == -INFINITY ? -1 : v0;
-      }
     }
     __syncthreads();
   }
@@ -801,8 +762,7 @@ bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void*
                          const void* W1, const void* W2t, const void* target, const int32_t* x,
                          const int32_t* rej_count, const int4* rej, const float2* lse_t,
                          const float* lse_d, float2* L, uint32_t* status, hipStream_t st,
-                         hipError_t* err, bool overlap, bool feat_rows, int* winners,
-                         uint64_t seed, uint64_t round) {
+                         hipError_t* err, bool overlap, bool feat_rows) {
   if (switches().force_per_step) return false;
   if ((V % 8) != 0 || (rank != 64 && rank != 128 && rank != 256)) return false;
   for (const void* p : {U, W1, W2t, target})
@@ -816,8 +776,6 @@ bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void*
   A.W2t = reinterpret_cast<const uint16_t*>(W2t);
   A.target = reinterpret_cast<const uint16_t*>(target);
   A.x = x; A.rej_count = rej_count; A.rej = rej; A.lse_t = lse_t; A.lse_d = lse_d; A.L = L;
-  A.W = overlap ? nullptr : winners;
-  A.seed = seed; A.round = round;
   A.status = status;
   A.feat_rows = feat_rows;
 #define DSPARK_RS(KS_, OV_) hipLaunchKernelGGL((k_resid_stats<KS_, OV_>), dim3(A.nslice), dim3(kPThreads), 0, st, A)

@@ -172,8 +172,7 @@ bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void*
                          const void* W1, const void* W2t, const void* target, const int32_t* x,
                          const int32_t* rej_count, const int4* rej, const float2* lse_t,
                          const float* lse_d, float2* L, uint32_t* status, hipStream_t st,
-                         hipError_t* err, bool overlap = false, bool feat_rows = false,
-                         int* winners = nullptr, uint64_t seed = 0, uint64_t round = 0);
+                         hipError_t* err, bool overlap = false, bool feat_rows = false);
 hipError_t launch_acceptance_rate(int R, int gamma, int V, int rank, float T, const void* target,
                                   const int32_t* x, const float* lse_d, const void* U, bool u_bf16,
                                   const void* W1, const void* W2t, bool w_bf16, float* c_star,

@@ -20,12 +20,9 @@
 //      row) and k_verify_scan (one workgroup per request).
 //   2. residual chunk masses for the listed (request, position) rows: the
 //      draft scores are rebuilt with the Markov bias (MFMA) and combined with
-//      the target row into max(0, p_t - p_d) per chunk; on the W2-slice
-//      layout the same pass draws every chunk's in-chunk winner.
-//   3. k_resid_pick, one workgroup per work item: chunk pick on the residual
-//      masses, then the chunk's winner (or, without winners, the in-chunk
-//      pick on log max(0, p_t - p_d) rebuilt here); zero mass falls back to
-//      p_t.
+//      the target row into max(0, p_t - p_d) per chunk.
+//   3. k_resid_pick, one workgroup per work item: chunk pick and in-chunk pick
+//      on log max(0, p_t - p_d); zero mass falls back to p_t.
 #include <atomic>
 
 #include "launch.hpp"
@@ -63,7 +60,6 @@ struct VerifyArgs {
   int32_t* rej_count;
   int4* rej;            // (request, position, target row, verify row q)
   const float2* rl;     // [slot][nch] residual chunk masses (0, sum)
-  const int* rw;        // nullable [slot][nch] in-chunk winners of the residual
   uint32_t* status;
   // fused verify rows
   float2* vl_out;       // = vl, written by the fused kernel
@@ -450,15 +446,7 @@ __global__ __launch_bounds__(256) void k_resid_pick(VerifyArgs a) {
                                               (uint32_t)i, (uint32_t)k, false, &mass, sh);
   const int v_off = tid >> 1, h = tid & 1;
   int y;
-  if (mass > 0.f && a.rw) {
-    // the in-chunk winner was drawn with the masses
-    const int c = pr.idx < 0 ? 0 : pr.idx;
-    y = a.rw[(int64_t)slot * a.nch + c];
-    if (y < 0) {
-      if (tid == 0) set_flag(a.status, kFlagNonFinite);
-      y = c * kChunk;
-    }
-  } else if (mass > 0.f) {
+  if (mass > 0.f) {
     const int c = pr.idx < 0 ? 0 : pr.idx;
     const int v = c * kChunk + v_off;
     const UT* urow = reinterpret_cast<const UT*>(a.U) + ((int64_t)i * a.gamma + (k - 1)) * a.V;
@@ -712,13 +700,11 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
   // rows of the bias features: W1[x_{k-1}] (Markov head) or the draft's own
   // per-position features (RNN head)
   const void* E = feat ? feat : W1;
-  int* winners = reinterpret_cast<int*>(w + L.draft_i);
   if (u_bf16 && w_bf16 && rank > 0 && u_vec && t_vec &&
       launch_resid_slices(R, gamma, V, rank, T, U, E, W2t, target, x, a.rej_count, a.rej,
                           a.lse_t, lse_d, const_cast<float2*>(a.rl), hdr, st, &e, false,
-                          feat != nullptr, winners, seed, round)) {
+                          feat != nullptr)) {
     if (e != hipSuccess) return e;
-    a.rw = winners;
   } else {
     // per-tile kernel for the other shapes
     MarkovArgs ma{};

@@ -14,7 +14,7 @@ struct WsLayout {
   size_t header;       // uint32 words: [0] status flags, [1] residual count,
                        // [2] pipelined-draft epoch, [3] verify epoch
   size_t draft_l;      // float2 [R][nch]   chunk (max, scaled sum) / residual masses
-  size_t draft_i;      // int32  [R][nch]   chunk argmax (greedy) / residual in-chunk winners
+  size_t draft_i;      // int32  [R][nch]   chunk argmax (greedy)
   size_t ver_l;        // float2 [R*(gamma+1)][nch]  target-row chunk (max, scaled sum)
   size_t ver_i;        // int32  [R*(gamma+1)][nch]  target-row chunk argmax (greedy)
   size_t lse_t;        // float2 [R*(gamma+1)]       target-row (max, log-normaliser above it)
