@@ -5,15 +5,17 @@
 // float32 running product per request.  Candidates (r, j) with a > 0 are
 // ordered by a descending, then r, then j ascending -- a total order -- by
 // sorting 64-bit keys (~bits(a) << 32 | r*32 + j-1).  Since c <= 1 makes a
-// non-increasing in j, each request's keys are already an ascending run: the
-// sort is a bottom-up merge of the R runs (merge path: each thread finds its
-// output range by a binary search and merges it from LDS, keeping the result
-// in registers).  Runs that are not ascending (some c outside [0, 1]) and
-// shapes whose padded runs do not fit take a bitonic network instead (1024
-// threads holding runs of keys in registers; only exchanges wider than a
-// wave's span go through LDS).  Admitting the q first candidates gives
-// B = R + q and tau_q = R + sum of their a; in 2^-32 fixed point the sums are
-// exact, so a block-wide prefix sum yields every tau_q at once, and
+// non-increasing in j, each request's keys are already an ascending run: up
+// to four keys per thread the runs, padded to a power of two, are merged
+// bottom-up (merge path: each thread finds its output range by a binary
+// search and merges it from LDS into registers).  Larger shapes, and runs out
+// of order (some c outside [0, 1]), take a stable LSD radix sort of the keys'
+// high halves (four 8-bit passes; ranks among equal digits from wave
+// ballots, offsets from one block scan of per-wave digit counts per pass),
+// which leaves equal values of a in (r, j) order.  Admitting the q first
+// candidates gives B = R + q and tau_q = R + sum of their a; in 2^-32 fixed
+// point the sums are exact, so a block-wide prefix sum yields every tau_q at
+// once, and
 // Theta_q = (tau_q * 2^-32) * SPS(B) is one double product (0 past N_max).
 // The sequential rule "admit while Theta improves, stop at the first
 // non-improvement" admits exactly the candidates before the first q with
@@ -112,66 +114,77 @@ __device__ inline int block_min_i(int v, int* lds) {
   return t;
 }
 
-// Compare-exchange for the bitonic network: `lower` is the element with the
-// smaller index of the pair; ascending blocks keep the smaller key there.
-__device__ __forceinline__ uint64_t bitonic_keep(uint64_t mine, uint64_t other, bool lower, bool up) {
-  const bool take_min = (lower == up);
-  return take_min ? (mine < other ? mine : other) : (mine < other ? other : mine);
-}
-
-// Thread t holds the EPT consecutive positions [t EPT, t EPT + EPT) in
-// registers.  Pairs closer than EPT are exchanged inside the thread, pairs
-// closer than 64 EPT across the wave (64-bit lane shuffles), wider pairs
-// through LDS with a workgroup barrier per stage.
+// Stable LSD radix sort of keys[0, P) by their high 32 bits: four passes of
+// eight bits.  Wave w owns positions [w S, w S + S), S = 64 EPT, read in EPT
+// rounds of 64 consecutive positions.  In a round the lanes holding the same
+// digit are found by matching the digit's bits across the wave (eight
+// ballots); a key's rank among the equal digits of its wave before it is the
+// wave's count of that digit so far plus the matching lanes below it.  One
+// exclusive scan of the per-wave digit counts in (digit, wave) order gives
+// every key its place.  Keys whose high halves are equal keep their buffer
+// order, which the caller makes ascending in the low halves, so the result
+// is the order of the whole 64-bit keys.  Thread t ends with the sorted
+// positions [t EPT, t EPT + EPT) in v.
 template <int EPT>
-__device__ __forceinline__ void bitonic_sort_regs(uint64_t (&v)[EPT], uint64_t* keys, int P) {
-  const int tid = threadIdx.x;
-  constexpr int WSPAN = 64 * EPT;
-  for (int kk = 2; kk <= P; kk <<= 1) {
-    int j = kk >> 1;
-    if (j >= WSPAN) {
+__device__ __forceinline__ void radix_sort_hi32(uint64_t (&v)[EPT], uint64_t* keys,
+                                                uint32_t* whist, int* scan_lds) {
+  constexpr int S = 64 * EPT;
+  constexpr int NW = kSchedThreads / 64;
+  static_assert(NW * 256 == 4 * kSchedThreads, "four counts per thread in the scan");
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint64_t below = (1ull << lane) - 1;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 32 + 8 * pass;
+    for (int t = tid; t < NW * 256; t += kSchedThreads) whist[t] = 0;
+    uint64_t k[EPT];
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) keys[tid * EPT + e] = v[e];
-      __syncthreads();
-      for (; j >= WSPAN; j >>= 1) {
-        for (int pi = tid; pi < P / 2; pi += kSchedThreads) {
-          const int i = (pi / j) * 2 * j + (pi % j);
-          const uint64_t x = keys[i], y = keys[i + j];
-          const bool up = (i & kk) == 0;
-          if ((x > y) == up) { keys[i] = y; keys[i + j] = x; }
-        }
-        __syncthreads();
+    for (int e = 0; e < EPT; ++e) k[e] = keys[wv * S + e * 64 + lane];
+    __syncthreads();                          // counts cleared, every key read
+    uint32_t rank[EPT];
+    int dig[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int d = (int)(k[e] >> shift) & 255;
+      uint64_t peers = ~0ull;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const uint64_t bb = __ballot((d >> b) & 1);
+        peers &= ((d >> b) & 1) ? bb : ~bb;
       }
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) v[e] = keys[tid * EPT + e];
-      __syncthreads();
-    }
-    for (; j >= EPT; j >>= 1) {
-      const int lx = j / EPT;                       // partner lane offset
-      const bool lower = (tid & lx) == 0;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const int i = tid * EPT + e;
-        const uint64_t o = __shfl_xor(v[e], lx);
-        v[e] = bitonic_keep(v[e], o, lower, (i & kk) == 0);
+      const int leader = __builtin_ctzll(peers);
+      uint32_t base = 0;
+      if (lane == leader) {
+        base = whist[wv * 256 + d];
+        whist[wv * 256 + d] = base + (uint32_t)__popcll(peers);
       }
+      base = __shfl(base, leader);
+      rank[e] = base + (uint32_t)__popcll(peers & below);
+      dig[e] = d;
     }
-    // in-thread stages, unrolled over the compile-time distance jj (<= j)
+    __syncthreads();
+    // offsets: exclusive scan of the counts, entry d * NW + w for digit d of wave w
+    uint32_t c4[4], sum = 0;
 #pragma unroll
-    for (int jj = EPT / 2; jj >= 1; jj >>= 1) {
-      if (jj <= j) {
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-          if ((e & jj) == 0) {
-            const int i = tid * EPT + e;
-            const bool up = (i & kk) == 0;
-            const uint64_t x = v[e], y = v[e | jj];
-            if ((x > y) == up) { v[e] = y; v[e | jj] = x; }
-          }
-        }
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int idx = 4 * tid + q;
+      c4[q] = whist[(idx % NW) * 256 + idx / NW];
+      sum += c4[q];
     }
+    int total;
+    uint32_t pre = (uint32_t)block_exclusive_scan((int)sum, scan_lds, &total);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = 4 * tid + q;
+      whist[(idx % NW) * 256 + idx / NW] = pre;
+      pre += c4[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) keys[whist[wv * 256 + dig[e]] + rank[e]] = k[e];
+    __syncthreads();
   }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) v[e] = keys[tid * EPT + e];
 }
 
 // Bottom-up merge of the ascending runs of length run0 (a power of two) in
@@ -220,12 +233,13 @@ __device__ __forceinline__ void merge_sort_runs(uint64_t (&v)[EPT], uint64_t* ke
 
 template <int EPT>
 __device__ __forceinline__ void schedule_body(const SchedArgs& a, int G2, uint64_t* keys, int64_t* red64,
-                                              int* red32, const int* kin_l) {
+                                              int* red32, const int* kin_l, uint32_t* whist,
+                                              int* scan_lds) {
   const int tid = threadIdx.x;
   const int R = a.R, G = a.gamma;
   const int P = kSchedThreads * EPT;
   // G2 > 0: request r's keys sit at r*G2 + j (runs padded to G2, a power of
-  // two); G2 == 0: packed at r*G + j (bitonic only)
+  // two); G2 == 0: packed at r*G + j
   const int stride = G2 > 0 ? G2 : G;
   const int p0 = tid * EPT;
 
@@ -297,16 +311,19 @@ __device__ __forceinline__ void schedule_body(const SchedArgs& a, int G2, uint64
     return;
   }
 
-  // sort ascending: a descending, then r, then j
+  // sort ascending: a descending, then r, then j.  Up to four keys per
+  // thread with ascending padded runs: the run merge; otherwise (more keys,
+  // or runs out of order) the radix sort, which keeps equal values of a in
+  // the buffer's (r, j) order.
   uint64_t v[EPT];
-  if (G2 > 0 && !unsorted) {
-    merge_sort_runs<EPT>(v, keys, P, G2);
-  } else {
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) v[e] = keys[tid * EPT + e];
-    __syncthreads();
-    bitonic_sort_regs<EPT>(v, keys, P);
+  bool merged = false;
+  if constexpr (EPT <= 4) {
+    if (G2 > 0 && !unsorted) {
+      merge_sort_runs<EPT>(v, keys, P, G2);
+      merged = true;
+    }
   }
+  if (!merged) radix_sort_hi32<EPT>(v, keys, whist, scan_lds);
   __syncthreads();                            // keys is reused below
 
   // fixed-point prefix sums over the sorted order; thread t owns positions
@@ -394,19 +411,21 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(SchedArgs a) {
   __shared__ int64_t red64[kSchedThreads / 64];
   __shared__ int red32[kSchedThreads / 64];
   __shared__ int pk_lds[kPackLds];
+  __shared__ uint32_t whist[kSchedThreads / 64 * 256];   // per-wave digit counts of the sort
   __shared__ int kin_l;
   // K_in is read once, before K_plan (which may be the same address) is written
   if (threadIdx.x == 0) kin_l = (a.mode == 1) ? *a.K_in : 0;
-  // runs padded to a power of two when they fit, else packed keys
+  // runs padded to a power of two up to four keys per thread (the run
+  // merge), else packed keys (R gamma <= kSchedMaxKeys, checked by the host)
   int G2 = 1;
   while (G2 < a.gamma) G2 *= 2;
   int n = a.R * G2;
-  if (n > kSchedMaxKeys) { G2 = 0; n = a.R * a.gamma; }
-  if (n <= kSchedThreads) schedule_body<1>(a, G2, keys, red64, red32, &kin_l);
-  else if (n <= 2 * kSchedThreads) schedule_body<2>(a, G2, keys, red64, red32, &kin_l);
-  else if (n <= 4 * kSchedThreads) schedule_body<4>(a, G2, keys, red64, red32, &kin_l);
-  else if (n <= 8 * kSchedThreads) schedule_body<8>(a, G2, keys, red64, red32, &kin_l);
-  else schedule_body<16>(a, G2, keys, red64, red32, &kin_l);
+  if (n > 4 * kSchedThreads) { G2 = 0; n = a.R * a.gamma; }
+  if (n <= kSchedThreads) schedule_body<1>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds);
+  else if (n <= 2 * kSchedThreads) schedule_body<2>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds);
+  else if (n <= 4 * kSchedThreads) schedule_body<4>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds);
+  else if (n <= 8 * kSchedThreads) schedule_body<8>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds);
+  else schedule_body<16>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds);
   // verify-batch pack of x with the lengths ell + 1 just decided (every path
   // of the body leaves ell in LDS at the start of the key buffer)
   if (a.pack) {
