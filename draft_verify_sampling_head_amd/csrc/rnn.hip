@@ -61,16 +61,19 @@ template <> __device__ __forceinline__ void st_f<uint16_t>(uint16_t* p, int64_t 
 
 // ------------------------------------------------------------- h projection
 // P[m][q] = sum_t h[m][t] Wr[q][2r + t], m < M = R gamma, q < N = 3r.
-// Workgroup tile kBM x kBN (256 threads).  The contraction runs in stages of
-// kBK columns: a stage's rows of h and of Wr are staged through LDS (double
-// buffered), and the global loads of stage s + 2 are issued before stage s is
-// computed, so two stages of MFMAs cover their latency.  Wave w computes the
-// 64 x 64 quarter (w >> 1, w & 1) as 4 x 4 tiles of v_mfma_f32_16x16x32_bf16,
-// two 32-wide k-steps per stage.  Operand lane (l & 15, l >> 4) holds row
-// l & 15 of its 16-row tile, k-values 8 (l >> 4) + [0, 8); result lane (n, g)
-// holds rows 4 g + [0, 4) of column n.  Workgroups b, b + 8, ... run on one
-// XCD: each XCD takes a contiguous run of tiles, N fastest, so tiles that
-// share rows of h share that XCD's L2.
+// Workgroup tile kBM x kBN (256 threads, four waves of kWM x kWN).  The
+// tiles are small enough that two workgroups share a compute unit (eight
+// waves, so one workgroup's MFMAs cover the other's barriers and loads) and
+// that the grid fills the chip: at 4096 x 768 it is 512 workgroups.  The
+// contraction runs in stages of kBK columns: a stage's rows of h and of Wr are
+// staged through LDS (double buffered), and the global loads of stage s + 2
+// are issued before stage s is computed, so two stages of MFMAs cover their
+// latency.  Each wave computes its kWM x kWN part as 16 x 16 tiles of
+// v_mfma_f32_16x16x32_bf16, two 32-wide k-steps per stage.  Operand lane
+// (l & 15, l >> 4) holds row l & 15 of its 16-row tile, k-values 8 (l >> 4) +
+// [0, 8); result lane (n, g) holds rows 4 g + [0, 4) of column n.  Workgroups
+// b, b + 8, ... run on one XCD: each XCD takes a contiguous run of tiles, N
+// fastest, so tiles that share rows of h share that XCD's L2.
 // 16 bytes at p (always a valid address), or zeros when !ok.  The zeroing is a
 // mask on the loaded value, so the load itself stays an unconditional global
 // load (a select between a load and a constant can otherwise become a load
@@ -81,16 +84,21 @@ __device__ __forceinline__ uint4 ld16_or_zero(const uint16_t* p, bool ok) {
   return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kBM = 64, kBN = 96, kBK = 64;
+constexpr int kWM = 32, kWN = 48;            // wave tile: 2 x 3 MFMA tiles
+constexpr int kTM = kWM / 16, kTN = kWN / 16;
+constexpr int kPA = kBM * (kBK / 8) / 256;   // 16-byte pieces of h per thread and stage
+constexpr int kPB = kBN * (kBK / 8) / 256;   // and of Wr
+static_assert((kBM / kWM) * (kBN / kWN) == 4, "four waves");
 constexpr int kLdsRow = kBK + 8;             // bf16 per LDS row (144 bytes: rows 4 banks apart)
 constexpr int kXcds = 8;                     // XCDs of an MI355X
 
-struct HStage { uint4 a[4], b[4]; };         // one stage's pieces of this thread
+struct HStage { uint4 a[kPA], b[kPB]; };     // one stage's pieces of this thread
 
-__global__ __launch_bounds__(256) void k_rnn_hproj_mfma(const uint16_t* __restrict__ h,
-                                                         const uint16_t* __restrict__ Wr, int M,
-                                                         int N, int d, int ldw, int wcol,
-                                                         float* __restrict__ P) {
+__global__ __launch_bounds__(256, 2) void k_rnn_hproj_mfma(const uint16_t* __restrict__ h,
+                                                            const uint16_t* __restrict__ Wr, int M,
+                                                            int N, int d, int ldw, int wcol,
+                                                            float* __restrict__ P) {
   __shared__ uint4 As[2][kBM * kLdsRow / 8];
   __shared__ uint4 Bs[2][kBN * kLdsRow / 8];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -99,53 +107,51 @@ __global__ __launch_bounds__(256) void k_rnn_hproj_mfma(const uint16_t* __restri
   const int t = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (t >= tiles) return;
   const int m0 = (t / nN) * kBM, n0 = (t % nN) * kBN;
-  // staging: pieces tid + 256 i, i < 4: row (tid >> 3) + 32 i, 16-byte column tid & 7
+  // staging: piece tid + 256 i: row (tid >> 3) + 32 i, 16-byte column tid & 7
   const int kp = tid & 7, rbase = tid >> 3;
-  const uint16_t* ga[4];
-  const uint16_t* gb[4];
+  const uint16_t* ga[kPA];
+  const uint16_t* gb[kPB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ga[i] = h + (int64_t)min(m0 + rbase + 32 * i, M - 1) * d + 8 * kp;
+  for (int i = 0; i < kPA; ++i) ga[i] = h + (int64_t)min(m0 + rbase + 32 * i, M - 1) * d + 8 * kp;
+#pragma unroll
+  for (int i = 0; i < kPB; ++i)
     gb[i] = Wr + (int64_t)min(n0 + rbase + 32 * i, N - 1) * ldw + wcol + 8 * kp;
-  }
   const int nst = (d + kBK - 1) / kBK;
   auto gload = [&](HStage& S, int st) __attribute__((always_inline)) {
     const bool ok = st < nst && st * kBK + 8 * kp < d;     // d % 8 == 0: all in or all out
     const int o = ok ? st * kBK : 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      S.a[i] = ld16_or_zero(ga[i] + o, ok);
-      S.b[i] = ld16_or_zero(gb[i] + o, ok);
-    }
+    for (int i = 0; i < kPA; ++i) S.a[i] = ld16_or_zero(ga[i] + o, ok);
+#pragma unroll
+    for (int i = 0; i < kPB; ++i) S.b[i] = ld16_or_zero(gb[i] + o, ok);
   };
   auto lstore = [&](const HStage& S, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int l = ((rbase + 32 * i) * kLdsRow + 8 * kp) / 8;
-      As[buf][l] = S.a[i];
-      Bs[buf][l] = S.b[i];
-    }
+    for (int i = 0; i < kPA; ++i) As[buf][((rbase + 32 * i) * kLdsRow + 8 * kp) / 8] = S.a[i];
+#pragma unroll
+    for (int i = 0; i < kPB; ++i) Bs[buf][((rbase + 32 * i) * kLdsRow + 8 * kp) / 8] = S.b[i];
   };
-  f32x4_t acc[4][4];
+  f32x4_t acc[kTM][kTN];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kTM; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < kTN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int rl = lane & 15, kg = lane >> 4;
-  const int wm = 64 * (wv >> 1), wn = 64 * (wv & 1);
+  const int wm = kWM * (wv / (kBN / kWN)), wn = kWN * (wv % (kBN / kWN));
   auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int sub = 0; sub < kBK / 32; ++sub) {
-      bf16x8_t Af[4], Bf[4];
+      bf16x8_t Af[kTM], Bf[kTN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kTM; ++i)
         Af[i] = __builtin_bit_cast(bf16x8_t, As[buf][((wm + 16 * i + rl) * kLdsRow + 32 * sub + 8 * kg) / 8]);
+#pragma unroll
+      for (int i = 0; i < kTN; ++i)
         Bf[i] = __builtin_bit_cast(bf16x8_t, Bs[buf][((wn + 16 * i + rl) * kLdsRow + 32 * sub + 8 * kg) / 8]);
-      }
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < kTM; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < kTN; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[a], Bf[b], acc[a][b], 0, 0, 0);
     }
   };
@@ -168,9 +174,9 @@ __global__ __launch_bounds__(256) void k_rnn_hproj_mfma(const uint16_t* __restri
     __syncthreads();
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kTM; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < kTN; ++b) {
       const int n = n0 + wn + 16 * b + rl;
       if (n >= N) continue;
 #pragma unroll
