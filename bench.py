@@ -10,7 +10,7 @@ resident in HBM before the timed region; between rounds a 512 MiB scratch
 buffer is written and a second one read, so that no round starts with W2 or U
 in the memory-side cache (nor with the write's dirty lines in it).  The `roofline` object covers the
 dominant kernel (the persistent draft kernel: all gamma steps in one
-cooperative launch; the per-step statistics kernel when the shape takes the
+co-resident launch; the per-step statistics kernel when the shape takes the
 per-step schedule), timed live with HIP events recorded on the launch stream
 around each of its launches.  `cpu_baseline` is the single-threaded CPU oracle on a bounded
 sample of requests of the same workload, scaled to a full round.
@@ -350,8 +350,8 @@ def main():
     elif nt == 1:
         kernel = "k_draft_persistent"
         kdesc = ("k_draft_persistent (RNN head: cell, statistics and pick of all gamma steps, one "
-                 "cooperative launch)" if rnn else
-                 "k_draft_persistent (whole draft: gamma steps, one cooperative launch)")
+                 "co-resident launch)" if rnn else
+                 "k_draft_persistent (whole draft: gamma steps, one co-resident launch)")
         kb = draft_kernel_bytes(cfg)
         kflops = 2.0 * cfg.R * cfg.rank * cfg.V * cfg.gamma
     else:

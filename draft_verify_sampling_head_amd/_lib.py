@@ -34,6 +34,7 @@ EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
            "dspark_set_switch", "dspark_get_switch", "dspark_draft_markov_noalloc",
            "dspark_w2_transpose", "dspark_schedule_pack")
 SWITCH_FORCE_PER_STEP, SWITCH_RNN_CELL_VALU, SWITCH_BARRIER_SPINS, SWITCH_DRAFT_KERNEL = 1, 2, 3, 4
+SWITCH_PERSIST_LAUNCH = 5
 
 
 class DsparkError(RuntimeError):

@@ -9,7 +9,7 @@
 //      statistics, the chunk-level Gumbel pick, then the in-chunk pick after
 //      rebuilding the 128 scores of the chosen chunk (bias by FMA chain).
 // Two schedules of the same phases:
-//   persistent : one cooperative launch for all gamma steps (k_draft_persistent).
+//   persistent : one co-resident launch for all gamma steps (k_draft_persistent).
 //                Each workgroup owns a 512-entry vocabulary slice and keeps its
 //                W2 slice in registers as MFMA operands for the whole round, so
 //                W2 is read from memory once per round instead of once per
@@ -812,8 +812,8 @@ static bool persist_fits(PersistInfo& pi, int ki) {
 template <int KS, bool G, bool F>
 static hipError_t launch_persist_ks(PersistArgs& P, int grid, hipStream_t st) {
   void* args[] = {&P};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_draft_persistent<KS, G, F>),
-                                    dim3(grid), dim3(kPThreads), args, 0, st);
+  return launch_coresident(reinterpret_cast<const void*>(k_draft_persistent<KS, G, F>), dim3(grid),
+                           dim3(kPThreads), args, 0, st);
 }
 
 // The persistent schedule takes bf16 U and weights, rank 64/128/256, rows and

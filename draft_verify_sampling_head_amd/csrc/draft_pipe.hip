@@ -1,5 +1,5 @@
 // draft_pipe.hip -- the Markov draft head with request groups pipelined
-// across the gamma sequential steps (one cooperative launch for the block).
+// across the gamma sequential steps (one co-resident launch for the block).
 //
 // DSpark summary page, Method details (causal block distribution, Markov
 // head): p_k(v | x_0, x_<k) = softmax(U_k + W1[x_{k-1}] W2)(v), sampled left to
@@ -874,8 +874,8 @@ static bool pipe_fits(int dev, int ki) {
 template <int KS, bool G>
 static hipError_t launch_pipe_ks(PipeArgs& P, int grid, hipStream_t st) {
   void* args[] = {&P};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_draft_pipe<KS, G>), dim3(grid),
-                                    dim3(kPThreads), args, 0, st);
+  return launch_coresident(reinterpret_cast<const void*>(k_draft_pipe<KS, G>), dim3(grid),
+                           dim3(kPThreads), args, 0, st);
 }
 
 // Launches the pipelined draft (the caller has checked the persistent

@@ -16,10 +16,21 @@ struct Switches {
   int rnn_cell_valu;       // 1: the RNN head's per-step schedule with the vector-ALU cell
   uint32_t barrier_spins;  // polls before a cross-workgroup wait gives up
   int draft_kernel;        // persistent draft: 0 one grid barrier per step, 1 pipelined
+  int persist_launch;      // launches that need a co-resident grid: 0 plain, 1 cooperative
 };
 // Polls before a cross-workgroup wait gives up when barrier_spins is 0.
 constexpr uint32_t kBarrierSpins = 1u << 24;
 Switches switches();
+
+// Launch of a kernel whose workgroups wait for one another (grid
+// barriers): the grid (at most one workgroup per compute unit)
+// must be co-resident.  By the switch: a plain launch (resident at once when
+// nothing else occupies the device; while other work holds compute units the
+// waits last until it drains, and they are bounded: a wait that gives up
+// reports DSPARK_FLAG_BARRIER), or a cooperative launch (the runtime
+// guarantees residency or fails the launch).
+hipError_t launch_coresident(const void* fn, dim3 grid, dim3 block, void** args, size_t lds,
+                             hipStream_t st);
 
 enum { kRowsDraft = 0, kRowsVerifyPacked = 1, kRowsVerifyDense = 2, kRowsAll = 3 };
 enum { kModeSample = 0, kModeGreedy = 1, kModeResid = 2 };

@@ -78,10 +78,11 @@ enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 };
  * Their start values are read once from the environment, the first time the
  * library needs them: DSPARK_DRAFT_KERNEL=steps (FORCE_PER_STEP = 1),
  * DSPARK_DRAFT_KERNEL=pipe (DRAFT_KERNEL = 1), DSPARK_RNN_CELL_VALU set
- * (RNN_CELL_VALU = 1), DSPARK_BARRIER_SPINS=n (BARRIER_SPINS = n).  Apart from
- * the per-device cache of device facts these switches are the library's only
- * state; set them between rounds, not while calls are being enqueued on
- * another thread.
+ * (RNN_CELL_VALU = 1), DSPARK_BARRIER_SPINS=n (BARRIER_SPINS = n),
+ * DSPARK_PERSIST_LAUNCH=coop (PERSIST_LAUNCH = 1).  Apart from the
+ * per-device cache of device facts and a per-process call counter of the
+ * verify these switches are the library's only state; set them between
+ * rounds, not while calls are being enqueued on another thread.
  *   FORCE_PER_STEP  1: the per-step draft schedule for every shape
  *   RNN_CELL_VALU   1: the RNN head on the per-step schedule with the
  *                   vector-ALU cell
@@ -90,6 +91,14 @@ enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 };
  *   DRAFT_KERNEL    persistent Markov draft: 0 one grid barrier per step
  *                   (default), 1 request groups pipelined across steps (no
  *                   grid barrier; slower on the measured shapes)
+ *   PERSIST_LAUNCH  launches whose workgroups wait for one another (the
+ *                   persistent draft kernels, with grid barriers; grids of
+ *                   at most one workgroup per compute unit): 0 plain launch (default; resident at once while
+ *                   nothing else occupies the device, otherwise the waits
+ *                   last until the other work drains; a wait that gives up
+ *                   sets DSPARK_FLAG_BARRIER), 1 cooperative launch (the
+ *                   runtime guarantees residency; about 20 us more per
+ *                   launch from its synchronisation around the kernel)
  * dspark_set_switch returns DSPARK_E_INVALID for an unknown key or value;
  * dspark_get_switch returns -1 for an unknown key.
  */
@@ -97,6 +106,7 @@ enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 };
 #define DSPARK_SWITCH_RNN_CELL_VALU  2
 #define DSPARK_SWITCH_BARRIER_SPINS  3
 #define DSPARK_SWITCH_DRAFT_KERNEL   4
+#define DSPARK_SWITCH_PERSIST_LAUNCH 5
 dspark_status dspark_set_switch(int key, int64_t value);
 int64_t dspark_get_switch(int key);
 

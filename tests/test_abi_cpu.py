@@ -204,7 +204,7 @@ def test_switches_set_get_and_reject():
     """The test switches: known keys round-trip, unknown keys and values are
     rejected, and every switch is restored."""
     keys = [L.SWITCH_FORCE_PER_STEP, L.SWITCH_RNN_CELL_VALU, L.SWITCH_BARRIER_SPINS,
-            L.SWITCH_DRAFT_KERNEL]
+            L.SWITCH_DRAFT_KERNEL, L.SWITCH_PERSIST_LAUNCH]
     saved = [L.get_switch(k) for k in keys]
     try:
         for k in keys:
@@ -217,6 +217,9 @@ def test_switches_set_get_and_reject():
         assert lib.dspark_set_switch(L.SWITCH_FORCE_PER_STEP, 2) == INVALID
         assert lib.dspark_set_switch(L.SWITCH_DRAFT_KERNEL, -1) == INVALID
         assert lib.dspark_set_switch(L.SWITCH_BARRIER_SPINS, -5) == INVALID
+        assert lib.dspark_set_switch(L.SWITCH_PERSIST_LAUNCH, 2) == INVALID
+        L.set_switch(L.SWITCH_PERSIST_LAUNCH, 1)
+        assert L.get_switch(L.SWITCH_PERSIST_LAUNCH) == 1
         assert lib.dspark_set_switch(99, 0) == INVALID
         assert lib.dspark_get_switch(99) == -1
     finally:

@@ -194,11 +194,13 @@ def switch():
 
 @pytest.fixture
 def draft_schedule(switch):
-    """None: the default persistent kernel (one grid barrier per step);
-    "pipe": the pipelined persistent kernel; "steps": one launch per step."""
+    """None: the default persistent kernel (one grid barrier per step, plain
+    launch); "coop": the same kernel in a cooperative launch; "pipe": the
+    pipelined persistent kernel; "steps": one launch per step."""
     def set_to(name):
         switch(D._lib.SWITCH_FORCE_PER_STEP, 1 if name == "steps" else 0)
         switch(D._lib.SWITCH_DRAFT_KERNEL, 1 if name == "pipe" else 0)
+        switch(D._lib.SWITCH_PERSIST_LAUNCH, 1 if name == "coop" else 0)
     return set_to
 
 
@@ -212,7 +214,7 @@ def test_draft_schedules_all_match_oracle(draft_schedule, base, rank, R):
     cfg = synth.scaled(synth.config(base), R=R, gamma=4, V=3072, d=32, rank=rank)
     inp = synth.make_inputs(cfg, device="cpu")
     xs = []
-    for name in (None, "pipe", "steps"):
+    for name in (None, "coop", "pipe", "steps"):
         draft_schedule(name)
         buf, _ = run_and_check(cfg, inp)
         xs.append(n(buf.x))
@@ -251,6 +253,16 @@ def test_barrier_wait_is_bounded(switch, kernel):
                         buf.logp_d, buf.lse_d, buf.ws)
     torch.cuda.synchronize()
     assert D.get_status(buf.ws) == 0
+
+
+def test_rounds_with_more_slices_than_compute_units():
+    """V = 151936: 297 vocabulary slices of 512, more than the compute units
+    (the draft then takes the per-step schedule): several rounds in a row
+    finish with a clean status and match the oracle."""
+    cfg = synth.scaled(synth.config(3), R=24, gamma=4, d=64)
+    inp = synth.make_inputs(cfg, device="cpu")
+    for rnd in range(3):
+        run_and_check(cfg, inp, rnd=rnd)
 
 
 @pytest.mark.parametrize("T", [1.0, 0.0], ids=["sampled", "greedy"])
