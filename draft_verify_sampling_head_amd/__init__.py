@@ -9,7 +9,7 @@ missing; there is no other execution path.
 from . import _lib
 from ._lib import (DsparkError, acceptance_rate, acceptance_rate_features, async_schedule,
                    confidence, confidence_logits, draft_markov, draft_rnn, get_status, clear_status, pack, pack_tiered,
-                   prefix_schedule, schedule_pack, rnn_workspace, rnn_workspace_bytes, sts_fit, sts_workspace,
+                   prefix_schedule, round_markov, schedule_pack, rnn_workspace, rnn_workspace_bytes, sts_fit, sts_workspace,
                    verify, verify_cap_accept, verify_cap_accept_features, verify_features,
                    w2_transpose, workspace, workspace_bytes)
 
@@ -17,6 +17,6 @@ _lib.load()
 
 __all__ = ["DsparkError", "acceptance_rate", "acceptance_rate_features", "async_schedule",
            "confidence", "confidence_logits", "draft_markov", "draft_rnn", "get_status", "clear_status", "pack", "pack_tiered",
-           "prefix_schedule", "schedule_pack", "rnn_workspace", "rnn_workspace_bytes", "sts_fit", "sts_workspace",
+           "prefix_schedule", "round_markov", "schedule_pack", "rnn_workspace", "rnn_workspace_bytes", "sts_fit", "sts_workspace",
            "verify", "verify_cap_accept", "verify_cap_accept_features", "verify_features",
            "w2_transpose", "workspace", "workspace_bytes"]

@@ -32,9 +32,22 @@ EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_version",
            "dspark_draft_rnn", "dspark_verify_features", "dspark_draft_rnn_profiled",
            "dspark_acceptance_rate_features", "dspark_verify_cap_accept_features",
            "dspark_set_switch", "dspark_get_switch", "dspark_draft_markov_noalloc",
-           "dspark_w2_transpose", "dspark_schedule_pack")
+           "dspark_w2_transpose", "dspark_schedule_pack", "dspark_round_markov")
 SWITCH_FORCE_PER_STEP, SWITCH_RNN_CELL_VALU, SWITCH_BARRIER_SPINS, SWITCH_DRAFT_KERNEL = 1, 2, 3, 4
 SWITCH_PERSIST_LAUNCH = 5
+
+
+class RoundMarkovArgs(C.Structure):
+    """dspark_round_markov_args, field for field."""
+    _fields_ = ([(n, C.c_int) for n in ("R", "gamma", "V", "r", "d")] + [("T", C.c_float)]
+                + [("seed", C.c_uint64), ("round", C.c_uint64)]
+                + [(n, C.c_int) for n in ("sched_mode", "N_max", "target_layout", "U_dt", "W_dt",
+                                          "h_dt", "w_dt", "t_dt")]
+                + [(n, C.c_void_p) for n in (
+                    "U", "W1", "W2t", "x0", "h", "w", "sts_T", "sps", "target", "K_in", "K_plan",
+                    "x", "logp_d", "lse_d", "c", "ell", "a", "N", "theta", "theta_plan", "cu",
+                    "flat", "marker_req", "marker_pos", "m", "tau", "emitted", "next_anchor",
+                    "logp_t", "cu_out", "flat_out", "N_out")])
 
 
 class DsparkError(RuntimeError):
@@ -94,6 +107,7 @@ def load():
     L.dspark_w2_transpose.argtypes = [i32, i32, P, P, i32, P]
     L.dspark_draft_markov_noalloc.argtypes = [i32, i32, i32, i32, f32, u64, u64, P, i32, P, P, i32,
                                               P, P, P, P, P, P, P]
+    L.dspark_round_markov.argtypes = [C.POINTER(RoundMarkovArgs), P, sz, P]
     L.dspark_set_switch.argtypes = [i32, C.c_int64]
     L.dspark_get_switch.argtypes = [i32]
     L.dspark_get_switch.restype = C.c_int64
@@ -346,6 +360,37 @@ def verify(ell, cu, target, layout, x, logp_d, lse_d, U, W1, W2t, T, seed, rnd, 
                                 _ptr(m), _ptr(tau), _ptr(emitted), _ptr(next_anchor),
                                 _ptr(logp_t), _ptr(ws), ws.numel(), _stream(stream))
     _check("dspark_verify", code)
+
+
+def round_markov(U, W1, W2t, x0, h, w, sps, target, layout, T, seed, rnd, x, logp_d, lse_d, c,
+                 ell, cu, flat, m, tau, emitted, next_anchor, cu_out, flat_out, ws, mode=1,
+                 sts_T=None, K_in=None, K_plan=None, N_max=None, a=None, N=None, theta=None,
+                 theta_plan=None, marker_req=None, marker_pos=None, logp_t=None, N_out=None,
+                 stream=None):
+    """dspark_round_markov: draft, confidence, schedule + verify-batch pack
+    (mode 0 static, 1 Algorithm 1, 2 asynchronous), verify and the output pack
+    in one call."""
+    R, gamma, V = U.shape
+    r = 0 if W1 is None else int(W1.shape[1])
+    d = int(h.shape[2])
+    A = RoundMarkovArgs()
+    A.R, A.gamma, A.V, A.r, A.d, A.T = R, gamma, V, r, d, float(T)
+    A.seed, A.round = int(seed), int(rnd)
+    A.sched_mode = int(mode)
+    A.N_max = sps.numel() - 1 if N_max is None else int(N_max)
+    A.target_layout = int(layout)
+    A.U_dt, A.W_dt, A.h_dt, A.w_dt, A.t_dt = _dt(U), _dt(W1), _dt(h), _dt(w), _dt(target)
+    for name, t in (("U", U), ("W1", W1), ("W2t", W2t), ("x0", x0), ("h", h), ("w", w),
+                    ("sts_T", sts_T), ("sps", sps), ("target", target), ("K_in", K_in),
+                    ("K_plan", K_plan), ("x", x), ("logp_d", logp_d), ("lse_d", lse_d), ("c", c),
+                    ("ell", ell), ("a", a), ("N", N), ("theta", theta), ("theta_plan", theta_plan),
+                    ("cu", cu), ("flat", flat), ("marker_req", marker_req),
+                    ("marker_pos", marker_pos), ("m", m), ("tau", tau), ("emitted", emitted),
+                    ("next_anchor", next_anchor), ("logp_t", logp_t), ("cu_out", cu_out),
+                    ("flat_out", flat_out), ("N_out", N_out)):
+        setattr(A, name, None if t is None else t.data_ptr())
+    code = load().dspark_round_markov(C.byref(A), _ptr(ws), ws.numel(), _stream(stream))
+    _check("dspark_round_markov", code)
 
 
 def rnn_workspace_bytes(R, gamma, V, r, d):

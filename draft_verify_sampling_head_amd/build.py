@@ -29,11 +29,22 @@ FLAGS = [
 ]
 
 
+def rocm_lib() -> str:
+    """The ROCm library folder next to the hipcc in use."""
+    return os.path.join(os.path.dirname(os.path.dirname(hipcc())), "lib")
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
             return cand
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libdspark.so")
+
+
+# roctx (marker ranges around each C-ABI call)
+def _link_flags() -> list:
+    lib = rocm_lib()
+    return [f"-L{lib}", "-lrocprofiler-sdk-roctx", f"-Wl,-rpath,{lib}"]
 
 
 def _compile(src: str, objdir: str = OBJDIR, extra: tuple = ()) -> str:
@@ -56,7 +67,7 @@ def build(verbose: bool = False, lib_path: str = LIB, objdir: str = OBJDIR,
     with cf.ThreadPoolExecutor(workers) as ex:
         objs = list(ex.map(lambda s: _compile(s, objdir, tuple(extra_flags)), srcs))
     tmp = lib_path + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + _link_flags()
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

@@ -143,12 +143,14 @@ int64_t dspark_get_switch(int key) {
 }
 
 dspark_status dspark_clear_status(void* ws, size_t ws_bytes, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   if (!ws || ws_bytes < 256 || !aligned16(ws)) return DSPARK_E_INVALID;
   hipLaunchKernelGGL(k_store_u32, dim3(1), dim3(64), 0, stream, reinterpret_cast<uint32_t*>(ws), 0u);
   return hip_status(hipGetLastError());
 }
 
 dspark_status dspark_get_status(const void* ws, size_t ws_bytes, uint32_t* flags) {
+  DSPARK_ABI_RANGE();
   if (!ws || !flags || ws_bytes < 256) return DSPARK_E_INVALID;
   return hip_status(hipMemcpy(flags, ws, sizeof(uint32_t), hipMemcpyDeviceToHost));
 }
@@ -158,7 +160,7 @@ static dspark_status draft_impl(int R, int gamma, int V, int r, float T, uint64_
                                 const void* W2t, dspark_dtype W_dt, const int32_t* x0, int32_t* x,
                                 float* logp_d, float* lse_d, float* margin, void* ws,
                                 size_t ws_bytes, hipStream_t stream, hipEvent_t* ev_begin,
-                                hipEvent_t* ev_end, int* n_timed) {
+                                hipEvent_t* ev_end, int* n_timed, bool dry = false) {
   dspark_status s = shape_check(R, gamma, V);
   if (s != DSPARK_OK) return s;
   if ((s = rank_check(r)) != DSPARK_OK) return s;
@@ -170,6 +172,7 @@ static dspark_status draft_impl(int R, int gamma, int V, int r, float T, uint64_
   if (r > 0 && (!aligned16(W1) || !aligned16(W2t))) return DSPARK_E_UNSUPPORTED;
   if (!aligned16(ws)) return DSPARK_E_INVALID;
   if (ws_bytes < ws_layout(R, gamma, V).total) return DSPARK_E_WORKSPACE;
+  if (dry) return DSPARK_OK;
   return hip_status(launch_draft(R, gamma, V, r, T, seed, round, U, U_dt == DSPARK_BF16, W1, W2t,
                                  W_dt == DSPARK_BF16, x0, x, logp_d, lse_d, margin,
                                  draft_ws(ws, R, gamma, V), stream, ev_begin, ev_end, n_timed));
@@ -180,6 +183,7 @@ dspark_status dspark_draft_markov(int R, int gamma, int V, int r, float T, uint6
                                   const void* W2t, dspark_dtype W_dt, const int32_t* x0,
                                   int32_t* x, float* logp_d, float* lse_d, float* margin, void* ws,
                                   size_t ws_bytes, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   return draft_impl(R, gamma, V, r, T, seed, round, U, U_dt, W1, W2t, W_dt, x0, x, logp_d, lse_d,
                     margin, ws, ws_bytes, stream, nullptr, nullptr, nullptr);
 }
@@ -191,6 +195,7 @@ dspark_status dspark_draft_markov_profiled(int R, int gamma, int V, int r, float
                                            float* lse_d, float* margin, void* ws, size_t ws_bytes,
                                            hipStream_t stream, hipEvent_t* ev_begin,
                                            hipEvent_t* ev_end, int* n_timed) {
+  DSPARK_ABI_RANGE();
   if (!ev_begin || !ev_end) return DSPARK_E_INVALID;
   if (n_timed) *n_timed = 0;
   return draft_impl(R, gamma, V, r, T, seed, round, U, U_dt, W1, W2t, W_dt, x0, x, logp_d, lse_d,
@@ -245,6 +250,7 @@ dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, int d, float T, u
                                dspark_dtype h_dt, const int32_t* x0, int32_t* x, float* logp_d,
                                float* lse_d, float* margin, void* feat, float* state, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   return draft_rnn_impl(R, gamma, V, r, d, T, seed, round, U, U_dt, W1, W2t, W_dt, Wr, h, h_dt,
                         x0, x, logp_d, lse_d, margin, feat, state, ws, ws_bytes, stream, nullptr,
                         nullptr, nullptr);
@@ -259,6 +265,7 @@ dspark_status dspark_draft_rnn_profiled(int R, int gamma, int V, int r, int d, f
                                         float* state, void* ws, size_t ws_bytes,
                                         hipStream_t stream, hipEvent_t* ev_begin,
                                         hipEvent_t* ev_end, int* n_timed) {
+  DSPARK_ABI_RANGE();
   if (!ev_begin || !ev_end) return DSPARK_E_INVALID;
   if (n_timed) *n_timed = 0;
   return draft_rnn_impl(R, gamma, V, r, d, T, seed, round, U, U_dt, W1, W2t, W_dt, Wr, h, h_dt,
@@ -269,7 +276,7 @@ dspark_status dspark_draft_rnn_profiled(int R, int gamma, int V, int r, int d, f
 static dspark_status confidence_impl(int R, int gamma, int d, int r, int V, const void* h,
                                      dspark_dtype h_dt, const void* W1, dspark_dtype W_dt,
                                      const void* w, dspark_dtype w_dt, const float* sts_T,
-                                     const int32_t* x, float* c, bool logits, hipStream_t stream) {
+                                     const int32_t* x, float* c, bool logits, hipStream_t stream, bool dry = false) {
   if (R < 0 || gamma < 1 || d < 1) return DSPARK_E_INVALID;
   if (gamma > 32) return DSPARK_E_UNSUPPORTED;
   dspark_status s = rank_check(r);
@@ -286,6 +293,7 @@ static dspark_status confidence_impl(int R, int gamma, int d, int r, int V, cons
   a.vec_h = aligned16(h) && aligned16(w) && ((size_t)d * hs) % 16 == 0 && hs == ws_;
   a.vec_e = r > 0 && aligned16(W1) && aligned16(reinterpret_cast<const char*>(w) + (size_t)d * ws_) &&
             ((size_t)r * es) % 16 == 0 && es == ws_;
+  if (dry) return DSPARK_OK;
   return hip_status(launch_confidence(a, h_dt == DSPARK_BF16, W_dt == DSPARK_BF16,
                                       w_dt == DSPARK_BF16, stream));
 }
@@ -294,6 +302,7 @@ dspark_status dspark_confidence(int R, int gamma, int d, int r, int V, const voi
                                 dspark_dtype h_dt, const void* W1, dspark_dtype W_dt,
                                 const void* w, dspark_dtype w_dt, const float* sts_T,
                                 const int32_t* x, float* c, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   return confidence_impl(R, gamma, d, r, V, h, h_dt, W1, W_dt, w, w_dt, sts_T, x, c, false,
                          stream);
 }
@@ -302,6 +311,7 @@ dspark_status dspark_confidence_logits(int R, int gamma, int d, int r, int V, co
                                        dspark_dtype h_dt, const void* W1, dspark_dtype W_dt,
                                        const void* w, dspark_dtype w_dt, const int32_t* x,
                                        float* z, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   return confidence_impl(R, gamma, d, r, V, h, h_dt, W1, W_dt, w, w_dt, nullptr, x, z, true,
                          stream);
 }
@@ -309,6 +319,7 @@ dspark_status dspark_confidence_logits(int R, int gamma, int d, int r, int V, co
 dspark_status dspark_prefix_schedule(int R, int gamma, const float* c, const double* sps,
                                      int N_max, int enabled, int32_t* ell, float* a,
                                      int32_t* N_out, double* theta_best, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   if (R < 0 || gamma < 1) return DSPARK_E_INVALID;
   if (gamma > 32) return DSPARK_E_UNSUPPORTED;
   if (R == 0) return DSPARK_OK;
@@ -327,6 +338,7 @@ dspark_status dspark_async_schedule(int R, int gamma, const float* c, const doub
                                     int N_max, const int32_t* K_in, int32_t* K_plan, int32_t* ell,
                                     float* a, int32_t* N_out, double* theta, double* theta_plan,
                                     hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   if (R < 0 || gamma < 1) return DSPARK_E_INVALID;
   if (gamma > 32) return DSPARK_E_UNSUPPORTED;
   if (R == 0) return DSPARK_OK;
@@ -340,11 +352,12 @@ dspark_status dspark_async_schedule(int R, int gamma, const float* c, const doub
   return hip_status(launch_schedule(sa, stream));
 }
 
-dspark_status dspark_schedule_pack(int R, int gamma, int mode, const float* c, const double* sps,
-                                   int N_max, const int32_t* K_in, int32_t* K_plan,
-                                   const int32_t* x, int32_t* ell, float* a, int32_t* N_out,
-                                   double* theta, double* theta_plan, int32_t* cu, int32_t* flat,
-                                   int32_t* marker_req, int32_t* marker_pos, hipStream_t stream) {
+static dspark_status schedule_pack_impl(int R, int gamma, int mode, const float* c,
+                                        const double* sps, int N_max, const int32_t* K_in,
+                                        int32_t* K_plan, const int32_t* x, int32_t* ell, float* a,
+                                        int32_t* N_out, double* theta, double* theta_plan,
+                                        int32_t* cu, int32_t* flat, int32_t* marker_req,
+                                        int32_t* marker_pos, hipStream_t stream, bool dry) {
   if (R < 0 || gamma < 1) return DSPARK_E_INVALID;
   if (mode < 0 || mode > 2) return DSPARK_E_INVALID;
   if (gamma > 32) return DSPARK_E_UNSUPPORTED;
@@ -363,13 +376,24 @@ dspark_status dspark_schedule_pack(int R, int gamma, int mode, const float* c, c
   p.R = R; p.width = gamma + 1; p.rows = x; p.cu = cu; p.flat = flat;
   p.marker_req = marker_req; p.marker_pos = marker_pos;
   p.slots = (int64_t)R * (gamma + 1);
+  if (dry) return DSPARK_OK;
   return hip_status(launch_schedule(sa, stream));
 }
 
-dspark_status dspark_pack(int R, int width, const int32_t* rows, const int32_t* len,
-                          int len_offset, int32_t* cu, int32_t* flat, int32_t* marker_req,
-                          int32_t* marker_pos, int32_t* N_out, void* ws, size_t ws_bytes,
-                          hipStream_t stream) {
+dspark_status dspark_schedule_pack(int R, int gamma, int mode, const float* c, const double* sps,
+                                   int N_max, const int32_t* K_in, int32_t* K_plan,
+                                   const int32_t* x, int32_t* ell, float* a, int32_t* N_out,
+                                   double* theta, double* theta_plan, int32_t* cu, int32_t* flat,
+                                   int32_t* marker_req, int32_t* marker_pos, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
+  return schedule_pack_impl(R, gamma, mode, c, sps, N_max, K_in, K_plan, x, ell, a, N_out, theta,
+                            theta_plan, cu, flat, marker_req, marker_pos, stream, false);
+}
+
+static dspark_status pack_impl(int R, int width, const int32_t* rows, const int32_t* len,
+                               int len_offset, int32_t* cu, int32_t* flat, int32_t* marker_req,
+                               int32_t* marker_pos, int32_t* N_out, void* ws, size_t ws_bytes,
+                               hipStream_t stream, bool dry) {
   if (R < 0 || width < 1) return DSPARK_E_INVALID;
   if (R == 0) return DSPARK_OK;
   if (!rows || !len || !cu || !flat) return DSPARK_E_INVALID;
@@ -380,7 +404,17 @@ dspark_status dspark_pack(int R, int width, const int32_t* rows, const int32_t* 
   p.flat = flat; p.marker_req = marker_req; p.marker_pos = marker_pos; p.N_out = N_out;
   p.status = reinterpret_cast<uint32_t*>(ws);
   p.slots = (int64_t)R * width;
+  if (dry) return DSPARK_OK;
   return hip_status(launch_pack(p, stream));
+}
+
+dspark_status dspark_pack(int R, int width, const int32_t* rows, const int32_t* len,
+                          int len_offset, int32_t* cu, int32_t* flat, int32_t* marker_req,
+                          int32_t* marker_pos, int32_t* N_out, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  DSPARK_ABI_RANGE();
+  return pack_impl(R, width, rows, len, len_offset, cu, flat, marker_req, marker_pos, N_out, ws,
+                   ws_bytes, stream, false);
 }
 
 dspark_status dspark_pack_tiered(int R, int width, const int32_t* rows, const int32_t* len,
@@ -388,6 +422,7 @@ dspark_status dspark_pack_tiered(int R, int width, const int32_t* rows, const in
                                  int64_t slots, int32_t* cu, int32_t* flat, int32_t* marker_req,
                                  int32_t* marker_pos, int32_t* N_out, int32_t* N_pad, void* ws,
                                  size_t ws_bytes, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   if (R < 0 || width < 1) return DSPARK_E_INVALID;
   if (n_tiers < 0 || (n_tiers > 0 && !tiers)) return DSPARK_E_INVALID;
   if (n_tiers > kMaxTiers) return DSPARK_E_UNSUPPORTED;
@@ -417,7 +452,7 @@ static dspark_status verify_impl(int R, int gamma, int V, int r, float T, uint64
                                  dspark_dtype W_dt, int32_t* m, int32_t* tau, int32_t* emitted,
                                  int32_t* next_anchor, float* logp_t, void* ws, size_t ws_bytes,
                                  hipStream_t stream, const int32_t* cap, int32_t* m_full,
-                                 const void* feat = nullptr) {
+                                 const void* feat = nullptr, bool dry = false) {
   dspark_status s = shape_check(R, gamma, V);
   if (s != DSPARK_OK) return s;
   if ((s = rank_check(r)) != DSPARK_OK) return s;
@@ -433,6 +468,7 @@ static dspark_status verify_impl(int R, int gamma, int V, int r, float T, uint64
   if (r > 0 && T > 0.f && (!aligned16(W1) || !aligned16(W2t))) return DSPARK_E_UNSUPPORTED;
   if (!aligned16(ws)) return DSPARK_E_INVALID;
   if (ws_bytes < ws_layout(R, gamma, V).total) return DSPARK_E_WORKSPACE;
+  if (dry) return DSPARK_OK;
   return hip_status(launch_verify(R, gamma, V, r, T, seed, round, ell, cu, target, target_layout,
                                   x, logp_d, lse_d, U, U_dt == DSPARK_BF16, W1, W2t,
                                   W_dt == DSPARK_BF16, m, tau, emitted, next_anchor, logp_t, ws,
@@ -448,6 +484,7 @@ size_t dspark_sts_workspace_bytes(int n) {
 dspark_status dspark_sts_fit(int n, int gamma, const float* z, const int32_t* m, const float* grid,
                              int G, int nbins, float* t_out, double* ece_out, void* ws,
                              size_t ws_bytes, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   if (n < 0 || gamma < 1 || G < 1 || nbins < 1) return DSPARK_E_INVALID;
   if (G > kStsMaxGrid || nbins > kStsMaxBins) return DSPARK_E_UNSUPPORTED;
   if (!grid) return DSPARK_E_INVALID;
@@ -498,6 +535,7 @@ dspark_status dspark_acceptance_rate(int R, int gamma, int V, int r, float T, co
                                      const void* U, dspark_dtype U_dt, const void* W1,
                                      const void* W2t, dspark_dtype W_dt, float* c_star, void* ws,
                                      size_t ws_bytes, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   return acceptance_rate_impl(R, gamma, V, r, T, target, t_dt, x, lse_d, U, U_dt, W1, W2t, W_dt,
                               c_star, ws, ws_bytes, stream, nullptr);
 }
@@ -508,6 +546,7 @@ dspark_status dspark_acceptance_rate_features(int R, int gamma, int V, int r, fl
                                               dspark_dtype U_dt, const void* feat,
                                               const void* W2t, dspark_dtype W_dt, float* c_star,
                                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   if (r == 0 && R > 0) return DSPARK_E_UNSUPPORTED;
   if (R > 0 && !feat) return DSPARK_E_INVALID;
   // the features take W1's place in the argument checks
@@ -522,6 +561,7 @@ dspark_status dspark_verify(int R, int gamma, int V, int r, float T, uint64_t se
                             dspark_dtype U_dt, const void* W1, const void* W2t, dspark_dtype W_dt,
                             int32_t* m, int32_t* tau, int32_t* emitted, int32_t* next_anchor,
                             float* logp_t, void* ws, size_t ws_bytes, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   return verify_impl(R, gamma, V, r, T, seed, round, ell, cu, target, t_dt, target_layout, x,
                      logp_d, lse_d, U, U_dt, W1, W2t, W_dt, m, tau, emitted, next_anchor, logp_t,
                      ws, ws_bytes, stream, nullptr, nullptr);
@@ -535,6 +575,7 @@ dspark_status dspark_verify_features(int R, int gamma, int V, int r, float T, ui
                                      const void* W2t, dspark_dtype W_dt, int32_t* m, int32_t* tau,
                                      int32_t* emitted, int32_t* next_anchor, float* logp_t,
                                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   if (r == 0 && R > 0) return DSPARK_E_UNSUPPORTED;
   if (R > 0 && !feat) return DSPARK_E_INVALID;
   // the features take W1's place in the argument checks
@@ -555,6 +596,7 @@ dspark_status dspark_verify_cap_accept_features(int R, int gamma, int V, int r, 
                                                 int32_t* next_anchor, int32_t* m_full,
                                                 float* logp_t, void* ws, size_t ws_bytes,
                                                 hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   if (R > 0 && !cap) return DSPARK_E_INVALID;
   if (r == 0 && R > 0) return DSPARK_E_UNSUPPORTED;
   if (R > 0 && !feat) return DSPARK_E_INVALID;
@@ -573,10 +615,43 @@ dspark_status dspark_verify_cap_accept(int R, int gamma, int V, int r, float T, 
                                        int32_t* m, int32_t* tau, int32_t* emitted,
                                        int32_t* next_anchor, int32_t* m_full, float* logp_t,
                                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   if (R > 0 && !cap) return DSPARK_E_INVALID;
   return verify_impl(R, gamma, V, r, T, seed, round, ell, cu, target, t_dt, target_layout, x,
                      logp_d, lse_d, U, U_dt, W1, W2t, W_dt, m, tau, emitted, next_anchor, logp_t,
                      ws, ws_bytes, stream, cap, m_full);
+}
+
+dspark_status dspark_round_markov(const dspark_round_markov_args* a, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  DSPARK_ABI_RANGE();
+  if (!a) return DSPARK_E_INVALID;
+  if (a->sched_mode < 0 || a->sched_mode > 2) return DSPARK_E_INVALID;
+  // every call's checks first (nothing enqueued), then the five calls
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool dry = pass == 0;
+    dspark_status s = draft_impl(a->R, a->gamma, a->V, a->r, a->T, a->seed, a->round, a->U,
+                                 a->U_dt, a->W1, a->W2t, a->W_dt, a->x0, a->x, a->logp_d,
+                                 a->lse_d, nullptr, ws, ws_bytes, stream, nullptr, nullptr,
+                                 nullptr, dry);
+    if (s != DSPARK_OK) return s;
+    s = confidence_impl(a->R, a->gamma, a->d, a->r, a->V, a->h, a->h_dt, a->W1, a->W_dt, a->w,
+                        a->w_dt, a->sts_T, a->x, a->c, false, stream, dry);
+    if (s != DSPARK_OK) return s;
+    s = schedule_pack_impl(a->R, a->gamma, a->sched_mode, a->c, a->sps, a->N_max, a->K_in,
+                           a->K_plan, a->x, a->ell, a->a, a->N, a->theta, a->theta_plan, a->cu,
+                           a->flat, a->marker_req, a->marker_pos, stream, dry);
+    if (s != DSPARK_OK) return s;
+    s = verify_impl(a->R, a->gamma, a->V, a->r, a->T, a->seed, a->round, a->ell, a->cu, a->target,
+                    a->t_dt, a->target_layout, a->x, a->logp_d, a->lse_d, a->U, a->U_dt, a->W1,
+                    a->W2t, a->W_dt, a->m, a->tau, a->emitted, a->next_anchor, a->logp_t, ws,
+                    ws_bytes, stream, nullptr, nullptr, nullptr, dry);
+    if (s != DSPARK_OK) return s;
+    s = pack_impl(a->R, a->gamma + 1, a->emitted, a->tau, 0, a->cu_out, a->flat_out, nullptr,
+                  nullptr, a->N_out, ws, ws_bytes, stream, dry);
+    if (s != DSPARK_OK) return s;
+  }
+  return DSPARK_OK;
 }
 
 }  // extern "C"

@@ -4,8 +4,21 @@
 #include <stdint.h>
 
 #include "device_common.hpp"
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 namespace dspark {
+
+// A marker range over one C-ABI call, named after the entry point: a
+// profiler's marker trace (rocprofv3 --marker-trace) shows each call's host
+// span next to the kernels it enqueued.  Without a tool attached the two
+// calls return at once.
+struct AbiRange {
+  explicit AbiRange(const char* name) { roctxRangePush(name); }
+  ~AbiRange() { roctxRangePop(); }
+  AbiRange(const AbiRange&) = delete;
+  AbiRange& operator=(const AbiRange&) = delete;
+};
+#define DSPARK_ABI_RANGE() ::dspark::AbiRange dspark_abi_range_(__func__)
 
 // Test and measurement switches of the library (dspark_set_switch): read
 // once from the environment (DSPARK_DRAFT_KERNEL=steps, DSPARK_RNN_CELL_VALU,

@@ -15,6 +15,7 @@
 #include <cstdint>
 
 #include "dspark.h"
+#include "launch.hpp"
 
 namespace dspark {
 namespace {
@@ -45,6 +46,7 @@ __global__ __launch_bounds__(kTT) void k_transpose(const E* __restrict__ src, E*
 
 extern "C" dspark_status dspark_w2_transpose(int r, int V, const void* W2, void* W2t,
                                              dspark_dtype W_dt, hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   using namespace dspark;
   if (r < 0 || V < 1) return DSPARK_E_INVALID;
   if (W_dt != DSPARK_F32 && W_dt != DSPARK_BF16) return DSPARK_E_INVALID;

@@ -66,6 +66,7 @@ extern "C" dspark_status dspark_draft_markov_noalloc(int R, int gamma, int V, in
                                                      const int32_t* x0, int32_t* x, float* logp_d,
                                                      float* lse_d, float* margin, uint32_t* flags,
                                                      hipStream_t stream) {
+  DSPARK_ABI_RANGE();
   if (R < 0 || gamma < 1 || V < 1) return DSPARK_E_INVALID;
   if (gamma > 32) return DSPARK_E_UNSUPPORTED;
   if (r < 0) return DSPARK_E_INVALID;

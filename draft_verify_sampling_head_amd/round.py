@@ -1,4 +1,5 @@
-"""One DSpark round on the GPU: the six C-ABI calls enqueued back to back.
+"""One DSpark round on the GPU: the C-ABI calls enqueued back to back (or, for
+the Markov head with compact verify, the one call that enqueues them all).
 
 draft (Markov head, or the RNN head) -> confidence -> prefix schedule (Algorithm 1, static, or
 the asynchronous form with a two-slot capacity ring) -> pack the verify batch
@@ -79,7 +80,7 @@ class CapacityRing:
 
 def run_round(inp, buf: RoundBuffers, T, seed, rnd, scheduler=True, layout=1, sts_T=None,
               stream=None, ring: CapacityRing = None, verify_mode="compact", tiers=None,
-              pad_token=0, head="markov"):
+              pad_token=0, head="markov", single_call=False):
     """Enqueue one full round on `stream` (default: torch's current stream).
 
     `inp` holds U, W1, W2t, x0, h, w, sps and target (dense [R][gamma+1][V] for
@@ -90,8 +91,25 @@ def run_round(inp, buf: RoundBuffers, T, seed, rnd, scheduler=True, layout=1, st
     ints, ascending) pads the verify batch to the smallest tier that holds it
     (`buf.N_pad`; the buffers need slots >= the largest tier).  `head` "rnn"
     drafts with the RNN head (`inp["Wr"]`; buffers made with `rnn=`) and
-    verifies with its features."""
+    verifies with its features.  `single_call` enqueues the Markov-head round
+    with compact verify (no tiers) as one call, dspark_round_markov, with the
+    same results."""
     rnn = head == "rnn"
+    if single_call:
+        if rnn or verify_mode != "compact" or tiers:
+            raise ValueError("single_call covers the Markov head with compact verify, no tiers")
+        kin = kplan = None
+        if scheduler == "async":
+            kin, kplan = ring.slots(rnd)
+        mode = 2 if scheduler == "async" else (1 if scheduler else 0)
+        L.round_markov(inp["U"], inp["W1"], inp["W2t"], inp["x0"], inp["h"], inp["w"], inp["sps"],
+                       inp["target"], layout, T, seed, rnd, buf.x, buf.logp_d, buf.lse_d, buf.c,
+                       buf.ell, buf.cu, buf.flat, buf.m, buf.tau, buf.emitted, buf.next_anchor,
+                       buf.cu_out, buf.flat_out, buf.ws, mode=mode, sts_T=sts_T, K_in=kin,
+                       K_plan=kplan, a=buf.a, N=buf.N, theta=buf.theta,
+                       marker_req=buf.marker_req, marker_pos=buf.marker_pos, logp_t=buf.logp_t,
+                       N_out=buf.N_out, stream=stream)
+        return
     if rnn:
         L.draft_rnn(inp["U"], inp["W1"], inp["W2t"], inp["Wr"], inp["h"], inp["x0"], T, seed, rnd,
                     buf.x, buf.logp_d, buf.lse_d, buf.feat, buf.ws, state=buf.state,

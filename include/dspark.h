@@ -73,6 +73,13 @@ enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 };
                                       (N_pad = N)                                 */
 
 /*
+ * Tracing: every call in this header that takes a stream, and dspark_get_status, opens
+ * a roctx range named after itself for its host-side span (shown by
+ * `rocprofv3 --marker-trace`); without a profiler attached the ranges cost
+ * two calls that return at once.
+ */
+
+/*
  * (host) Test and measurement switches.  They select among schedules that give
  * the same results (or bound a wait); they never change what is computed.
  * Their start values are read once from the environment, the first time the
@@ -613,6 +620,71 @@ dspark_status dspark_verify_features(int R, int gamma, int V, int r, float T,
                                      int32_t* m, int32_t* tau, int32_t* emitted,
                                      int32_t* next_anchor, float* logp_t,
                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One whole round with the Markov head in one call ([P3] Method details: draft
+ * the block, score it with the confidence head, schedule the verify prefix,
+ * verify, emit): enqueues on `stream`, in this order and with the same
+ * results as the calls made one by one,
+ *   dspark_draft_markov      (margin not produced)
+ *   dspark_confidence
+ *   dspark_schedule_pack     (mode = sched_mode)
+ *   dspark_verify
+ *   dspark_pack              (emitted, tau, len_offset 0 -> cu_out, flat_out,
+ *                             N_out; no markers)
+ * with the fields of `a` as those calls' arguments of the same names (c, ell,
+ * N, theta, ... are the intermediate buffers they hand to one another; `a` is
+ * the score buffer of the scheduler).  (host) `a` is read during the call
+ * only.  Every call's argument checks run before anything is enqueued, so an
+ * error other than DSPARK_E_HIP leaves the stream untouched; the status is the
+ * first failing call's.  ws, ws_bytes: one workspace of
+ * dspark_workspace_bytes(R, gamma, V, r, d) bytes shared by the five calls.
+ */
+typedef struct dspark_round_markov_args {
+  int R, gamma, V, r, d;
+  float T;
+  uint64_t seed, round;
+  int sched_mode;                 /* 0 static block, 1 Algorithm 1, 2 asynchronous */
+  int N_max;
+  int target_layout;
+  dspark_dtype U_dt, W_dt, h_dt, w_dt, t_dt;
+  /* inputs */
+  const void* U;
+  const void* W1;
+  const void* W2t;
+  const int32_t* x0;
+  const void* h;
+  const void* w;
+  const float* sts_T;             /* nullable */
+  const double* sps;
+  const void* target;
+  const int32_t* K_in;            /* sched_mode 2 only */
+  int32_t* K_plan;                /* sched_mode 2 only */
+  /* intermediate buffers and outputs */
+  int32_t* x;
+  float* logp_d;
+  float* lse_d;
+  float* c;
+  int32_t* ell;
+  float* a;                       /* nullable */
+  int32_t* N;                     /* nullable */
+  double* theta;                  /* nullable */
+  double* theta_plan;             /* nullable */
+  int32_t* cu;
+  int32_t* flat;
+  int32_t* marker_req;            /* nullable */
+  int32_t* marker_pos;            /* nullable */
+  int32_t* m;
+  int32_t* tau;
+  int32_t* emitted;
+  int32_t* next_anchor;
+  float* logp_t;                  /* nullable */
+  int32_t* cu_out;
+  int32_t* flat_out;
+  int32_t* N_out;                 /* nullable */
+} dspark_round_markov_args;
+dspark_status dspark_round_markov(const dspark_round_markov_args* a, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
 
 #ifdef __cplusplus
 }

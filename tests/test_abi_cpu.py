@@ -194,7 +194,8 @@ def test_synthetic_configs_shapes():
                                 "pack", "pack_tiered", "verify", "verify_cap_accept",
                                 "acceptance_rate", "sts_fit", "confidence_logits", "draft_rnn",
                                 "verify_features", "rnn_workspace_bytes",
-                                "acceptance_rate_features", "verify_cap_accept_features"])
+                                "acceptance_rate_features", "verify_cap_accept_features",
+                                "schedule_pack", "round_markov"])
 def test_binding_names_match_abi(fn):
     assert callable(getattr(D, fn))
     assert f"dspark_{fn}" in declared()
@@ -236,3 +237,59 @@ def test_w2_transpose_argument_checks():
     assert lib.dspark_w2_transpose(16, 10, None, FAKE, 1, None) == INVALID
     assert lib.dspark_w2_transpose(16, 10, FAKE, FAKE, 1, None) == INVALID     # same buffer
     assert lib.dspark_w2_transpose(0, 10, None, None, 1, None) == OK           # r == 0: nothing
+
+
+def test_every_enqueueing_entry_point_has_a_marker_range():
+    """Each C-ABI call that takes a stream (and the blocking status read) opens
+    a roctx range named after itself, and the library links the roctx
+    runtime."""
+    csrc = os.path.join(ROOT, "draft_verify_sampling_head_amd", "csrc")
+    found = {}
+    for fn in sorted(os.listdir(csrc)):
+        if not fn.endswith(".hip"):
+            continue
+        src = open(os.path.join(csrc, fn)).read()
+        for m in re.finditer(r'^(?:extern "C" )?dspark_status (dspark_\w+)\(', src, re.M):
+            body = src.index(") {", m.end())
+            sig = src[m.start():body]
+            first = src[body + 3:].lstrip().split("\n", 1)[0]
+            if "hipStream_t" in sig or m.group(1) == "dspark_get_status":
+                found[m.group(1)] = first.strip() == "DSPARK_ABI_RANGE();"
+    assert "dspark_verify" in found and "dspark_draft_markov_noalloc" in found
+    assert all(found.values()), [k for k, v in found.items() if not v]
+    assert set(found) <= set(declared())
+    with open(L.LIB_PATH, "rb") as f:
+        assert b"librocprofiler-sdk-roctx.so" in f.read()
+
+
+def _round(**kw):
+    A = L.RoundMarkovArgs()
+    A.R, A.gamma, A.V, A.r, A.d, A.T = 4, 7, 100, 0, 32, 1.0
+    A.sched_mode, A.N_max, A.target_layout = 1, 4 * 8, 1
+    for n, _ in L.RoundMarkovArgs._fields_:
+        if n not in ("R", "gamma", "V", "r", "d", "T", "seed", "round", "sched_mode", "N_max",
+                     "target_layout") and not n.endswith("_dt"):
+            setattr(A, n, FAKE.value)
+    for n, v in kw.items():
+        setattr(A, n, v)
+    return L.load().dspark_round_markov(C.byref(A), FAKE, 1 << 30, None)
+
+
+def test_round_markov_checks_every_call_before_enqueueing():
+    """The one-call round rejects what any of its five calls would reject.
+    Errors found by the later calls' checks come back as those calls' codes:
+    had the draft been enqueued first, the launch (no GPU here) would have
+    failed with DSPARK_E_HIP instead."""
+    lib = L.load()
+    assert lib.dspark_round_markov(None, FAKE, 1 << 30, None) == INVALID
+    assert _round(sched_mode=3) == INVALID
+    assert _round(gamma=33) == UNSUPPORTED              # draft
+    assert _round(h=None) == INVALID                    # confidence
+    assert _round(N_max=3) == INVALID                   # schedule: N_max < R
+    assert _round(sched_mode=0, N_max=31) == INVALID    # static block needs R (gamma + 1)
+    assert _round(sched_mode=2, K_in=None) == INVALID   # asynchronous scheduler needs K_in
+    assert _round(t_dt=1) == UNSUPPORTED                # verify: target and U dtypes differ
+    assert _round(target_layout=2) == INVALID           # verify
+    assert _round(cu_out=None) == INVALID               # output pack
+    assert lib.dspark_round_markov(C.byref(L.RoundMarkovArgs()), FAKE, 1 << 30, None) == INVALID
+    assert _round(R=0) == OK                            # empty batch: nothing to do

@@ -136,6 +136,66 @@ def test_packed_target_layout():
     run_and_check(cfg, inp, layout=0)
 
 
+ROUND_ONE_CALL = [
+    (0, {}, True),
+    (2, dict(R=40, gamma=5, V=3000, d=256), True),
+    (1, dict(R=33, gamma=7, V=5000, d=128), False),                  # greedy, static block
+    (2, dict(R=37, gamma=6, V=2600, d=64, rank=0), "async"),
+    (2, dict(R=300, gamma=3, V=2048, d=32, rank=128), True),
+]
+
+
+@pytest.mark.parametrize("base,over,sched", ROUND_ONE_CALL,
+                         ids=[f"cfg{b}-{i}" for i, (b, _, _) in enumerate(ROUND_ONE_CALL)])
+def test_round_markov_one_call_matches_calls(base, over, sched):
+    """dspark_round_markov enqueues the same kernels in the same order as the
+    five calls made one by one: every output is bit-identical, over two rounds
+    (with the asynchronous scheduler each run keeps its own capacity ring),
+    and the first round also matches the oracle."""
+    cfg = synth.scaled(synth.config(base), **over)
+    print(f"[case] one-call round {cfg.name} R={cfg.R} g={cfg.gamma} V={cfg.V} r={cfg.rank} "
+          f"sched={sched}", flush=True)
+    inp = to_dev(synth.make_inputs(cfg, device="cpu"))
+    outs = []
+    for single in (False, True):
+        buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV)
+        ring = RD.CapacityRing(cfg.R, cfg.gamma, inp["sps"].numel() - 1, device=DEV)
+        per_round = []
+        for rnd in range(2):
+            D.clear_status(buf.ws)
+            RD.run_round(inp, buf, cfg.T, cfg.philox_seed, rnd, scheduler=sched, ring=ring,
+                         single_call=single)
+            torch.cuda.synchronize()
+            assert D.get_status(buf.ws) == 0
+            per_round.append({k: n(getattr(buf, k)).copy() for k in (
+                "x", "logp_d", "lse_d", "c", "ell", "a", "N", "theta", "cu", "flat",
+                "marker_req", "marker_pos", "m", "tau", "emitted", "next_anchor", "logp_t",
+                "cu_out", "flat_out", "N_out")})
+        outs.append(per_round)
+    for rnd in range(2):
+        for k, v in outs[0][rnd].items():
+            w = outs[1][rnd][k]
+            if k in ("flat", "marker_req", "marker_pos"):
+                N = int(outs[0][rnd]["N"][0])
+                v, w = v[:N], w[:N]
+            if k == "flat_out":
+                N = int(outs[0][rnd]["N_out"][0])
+                v, w = v[:N], w[:N]
+            assert np.array_equal(v.view(np.uint8), w.view(np.uint8)), (rnd, k)
+    if sched is not True:
+        return
+    rep = PC.Report()
+    inc = synth.make_inputs(cfg, device="cpu")
+    x, r0 = outs[1][0]["x"], outs[1][0]
+    lp, lse = PC.check_draft(rep, f(inc["U"]), f(inc["W1"]), f(inc["W2t"]), n(inc["x0"]), cfg.T,
+                             cfg.philox_seed, 0, x, r0["logp_d"], r0["lse_d"], None,
+                             threads=THREADS)
+    PC.check_verify(rep, r0["ell"], None, f(inc["target"]), 1, x, lp, lse, f(inc["U"]),
+                    f(inc["W1"]), f(inc["W2t"]), cfg.T, cfg.philox_seed, 0, r0["m"], r0["tau"],
+                    r0["emitted"], r0["next_anchor"], r0["logp_t"], None, threads=THREADS)
+    assert rep.ok(), rep.summary()
+
+
 def test_fp32_logits_bf16_weights():
     cfg = synth.scaled(synth.config(2), R=34, gamma=4, V=1900, d=64)
     inp = synth.make_inputs(cfg, device="cpu")
