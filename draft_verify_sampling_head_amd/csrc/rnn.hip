@@ -15,7 +15,8 @@
 //                      depend on the drafted tokens): P = h Wr_h^T, an
 //                      (R gamma) x d x 3r bf16 contraction on MFMA with fp32
 //                      accumulation (bf16 products are exact in fp32),
-//                      LDS-staged 128 x 128 tiles, loads two stages ahead.
+//                      128 x 96 tiles fed by direct-to-LDS loads three
+//                      stages ahead.
 //   k_rnn_hproj_valu : the same for float32 operands or unaligned rows.
 //   k_rnn_cell_mfma  : per step, the recurrent part [s_{k-1} ; W1[x_{k-1}]]
 //                      (2r inputs) on MFMA with the fp32 state split into
@@ -61,75 +62,114 @@ template <> __device__ __forceinline__ void st_f<uint16_t>(uint16_t* p, int64_t 
 
 // ------------------------------------------------------------- h projection
 // P[m][q] = sum_t h[m][t] Wr[q][2r + t], m < M = R gamma, q < N = 3r.
-// Workgroup tile kBM x kBN (256 threads, four waves of kWM x kWN).  The
-// tiles are small enough that two workgroups share a compute unit (eight
-// waves, so one workgroup's MFMAs cover the other's barriers and loads) and
-// that the grid fills the chip: at 4096 x 768 it is 512 workgroups.  The
-// contraction runs in stages of kBK columns: a stage's rows of h and of Wr are
-// staged through LDS (double buffered), and the global loads of stage s + 2
-// are issued before stage s is computed, so two stages of MFMAs cover their
-// latency.  Each wave computes its kWM x kWN part as 16 x 16 tiles of
-// v_mfma_f32_16x16x32_bf16, two 32-wide k-steps per stage.  Operand lane
-// (l & 15, l >> 4) holds row l & 15 of its 16-row tile, k-values 8 (l >> 4) +
-// [0, 8); result lane (n, g) holds rows 4 g + [0, 4) of column n.  Workgroups
-// b, b + 8, ... run on one XCD: each XCD takes a contiguous run of tiles, N
-// fastest, so tiles that share rows of h share that XCD's L2.
-// 16 bytes at p (always a valid address), or zeros when !ok.  The zeroing is a
-// mask on the loaded value, so the load itself stays an unconditional global
-// load (a select between a load and a constant can otherwise become a load
-// from a selected address, through scratch).
-__device__ __forceinline__ uint4 ld16_or_zero(const uint16_t* p, bool ok) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
-  const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
-  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+// Workgroup tile kBM x kBN = 128 x 96 (at 4096 x 768 that is 256 workgroups,
+// one per compute unit) with eight waves of 32 x 48 (2 x 3 tiles of
+// v_mfma_f32_16x16x32_bf16, fp32 accumulation), two waves per SIMD.  The
+// tile's rows of h and of Wr stream through a kNB-deep LDS ring in stages of
+// kBK columns, moved by direct-to-LDS loads (global_load_lds_dwordx4: no
+// registers, no LDS write instructions) issued three stages before they are
+// due, from a wave-uniform base plus 32-bit lane offsets.  LDS layout of a
+// stage: row-major 16-byte pieces, eight per row (64 bf16 columns), the piece
+// index XORed with the row's low three bits, so the rows one ds_read_b128
+// touches at one column spread over the banks (the bank-conflict counter reads
+// zero); a DMA instruction fills 64 consecutive pieces, each lane fetching
+// the global piece that belongs in its slot.  Workgroups b, b + 8, ... run on
+// one XCD: each XCD takes a contiguous run of tiles, N fastest, so tiles that
+// share rows of h share that XCD's L2.  Measured at 4096 x 768 x 4096: 39.6 us
+// (0.65 PFLOP/s) against 56 us for 64 x 96 tiles with register-staged loads;
+// four waves of 64 x 48 (fewer LDS bytes per MFMA, one wave per SIMD) took
+// 49 us, and reading h from L2 instead of HBM changed nothing.
+constexpr int kBM = 128, kBN = 96, kBK = 64;
+constexpr int kNB = 5;                       // LDS ring depth, in stages
+constexpr int kAPc = kBM * (kBK / 8);        // 16-byte pieces of h per stage (1024)
+constexpr int kBPc = kBN * (kBK / 8);        // and of Wr (768)
+constexpr int kSlotP = kAPc + kBPc;          // pieces per ring slot (28 KB)
+constexpr int kIA = kAPc / 64, kIB = kBPc / 64;   // DMA instructions per stage (16 + 12)
+constexpr int kXcds = 8;                     // XCDs of an MI355X
+constexpr int kHprojWaves = 8;
+
+typedef __attribute__((address_space(1))) void hp_gvoid_t;
+typedef __attribute__((address_space(3))) void hp_lvoid_t;
+
+__device__ __forceinline__ int hp_slot(int row, int p) { return row * 8 + (p ^ (row & 7)); }
+
+// s_waitcnt: at most N vector-memory operations of this wave outstanding, and
+// none of its LDS operations (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[15:14])
+template <int N>
+__device__ __forceinline__ void hp_wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
 }
 
-constexpr int kBM = 64, kBN = 96, kBK = 64;
-constexpr int kWM = 32, kWN = 48;            // wave tile: 2 x 3 MFMA tiles
-constexpr int kTM = kWM / 16, kTN = kWN / 16;
-constexpr int kPA = kBM * (kBK / 8) / 256;   // 16-byte pieces of h per thread and stage
-constexpr int kPB = kBN * (kBK / 8) / 256;   // and of Wr
-static_assert((kBM / kWM) * (kBN / kWN) == 4, "four waves");
-constexpr int kLdsRow = kBK + 8;             // bf16 per LDS row (144 bytes: rows 4 banks apart)
-constexpr int kXcds = 8;                     // XCDs of an MI355X
-
-struct HStage { uint4 a[kPA], b[kPB]; };     // one stage's pieces of this thread
-
-__global__ __launch_bounds__(256, 2) void k_rnn_hproj_mfma(const uint16_t* __restrict__ h,
-                                                            const uint16_t* __restrict__ Wr, int M,
-                                                            int N, int d, int ldw, int wcol,
-                                                            float* __restrict__ P) {
-  __shared__ uint4 As[2][kBM * kLdsRow / 8];
-  __shared__ uint4 Bs[2][kBN * kLdsRow / 8];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+// NW waves: 4 (wave tile 64 x 48, waves 2 x 2) or 8 (32 x 48, waves 4 x 2).
+// Wave wv issues the stage's h instructions wv + NW i and, if wv < kBW, the
+// Wr instructions wv + kBW i.
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_rnn_hproj_mfma(const uint16_t* __restrict__ h,
+                                                                const uint16_t* __restrict__ Wr,
+                                                                int M, int N, int d, int ldw,
+                                                                int wcol, float* __restrict__ P) {
+  constexpr int NT = 64 * NW;
+  constexpr int WNN = 2, WNM = NW / WNN;       // waves along N and along M
+  constexpr int kWM = kBM / WNM, kWN = kBN / WNN;
+  constexpr int kTM = kWM / 16, kTN = kWN / 16;
+  constexpr int NA = kIA / NW;                 // h instructions per wave and stage
+  constexpr int kBW = 4, NBI = kIB / kBW;      // waves that load Wr, and their instructions
+  static_assert(kIA % NW == 0 && kIB % kBW == 0 && kBW <= NW, "whole DMA instructions per wave");
+  __shared__ uint4 ring[kNB * kSlotP];
+  // the wave index as a scalar: the per-wave choice of loads and waits below
+  // is then a scalar branch, not two exec-masked paths
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nN = (N + kBN - 1) / kBN, tiles = ((M + kBM - 1) / kBM) * nN;
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
   const int t = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (t >= tiles) return;
   const int m0 = (t / nN) * kBM, n0 = (t % nN) * kBN;
-  // staging: piece tid + 256 i: row (tid >> 3) + 32 i, 16-byte column tid & 7
-  const int kp = tid & 7, rbase = tid >> 3;
-  const uint16_t* ga[kPA];
-  const uint16_t* gb[kPB];
-#pragma unroll
-  for (int i = 0; i < kPA; ++i) ga[i] = h + (int64_t)min(m0 + rbase + 32 * i, M - 1) * d + 8 * kp;
-#pragma unroll
-  for (int i = 0; i < kPB; ++i)
-    gb[i] = Wr + (int64_t)min(n0 + rbase + 32 * i, N - 1) * ldw + wcol + 8 * kp;
   const int nst = (d + kBK - 1) / kBK;
-  auto gload = [&](HStage& S, int st) __attribute__((always_inline)) {
-    const bool ok = st < nst && st * kBK + 8 * kp < d;     // d % 8 == 0: all in or all out
-    const int o = ok ? st * kBK : 0;
+  const bool bw = wv < kBW;
+  // this lane's DMA pieces: slot -> (row, piece) through the XOR swizzle,
+  // addressed as a wave-uniform stage base plus a 32-bit byte offset (the host
+  // checks that h and the Wr rows span less than 4 GiB), so a stage's loads
+  // need no per-lane address arithmetic.  The last stage has offsets of its
+  // own: its columns past d re-read column d - 8 (a valid address) and are
+  // zeroed in LDS once they have landed.
+  const int lastc = (nst - 1) * kBK;
+  uint32_t oa[NA], oal[NA], ob[NBI], obl[NBI];
 #pragma unroll
-    for (int i = 0; i < kPA; ++i) S.a[i] = ld16_or_zero(ga[i] + o, ok);
+  for (int i = 0; i < NA; ++i) {
+    const int q = (wv + NW * i) * 64 + lane, row = q >> 3, p = (q & 7) ^ (row & 7);
+    const uint32_t rb = (uint32_t)min(m0 + row, M - 1) * (uint32_t)d;
+    oa[i] = 2u * (rb + 8u * p);
+    oal[i] = 2u * (rb + (uint32_t)min(lastc + 8 * p, d - 8)) - 2u * lastc;
+  }
 #pragma unroll
-    for (int i = 0; i < kPB; ++i) S.b[i] = ld16_or_zero(gb[i] + o, ok);
-  };
-  auto lstore = [&](const HStage& S, int buf) __attribute__((always_inline)) {
+  for (int i = 0; i < NBI; ++i) {
+    const int q = ((bw ? wv : 0) + kBW * i) * 64 + lane, row = q >> 3, p = (q & 7) ^ (row & 7);
+    const uint32_t rb = (uint32_t)min(n0 + row, N - 1) * (uint32_t)ldw + (uint32_t)wcol;
+    ob[i] = 2u * (rb + 8u * p);
+    obl[i] = 2u * (rb + (uint32_t)min(lastc + 8 * p, d - 8)) - 2u * lastc;
+  }
+  const char* hb = reinterpret_cast<const char*>(h);
+  const char* wb = reinterpret_cast<const char*>(Wr);
+  // stage st into ring slot st % kNB; stages past the last re-read the last
+  // one into a slot that is not read again, so every wave always has the
+  // same number of loads in flight
+  auto issue = [&](int st) __attribute__((always_inline)) {
+    const bool last = st >= nst - 1;
+    const int64_t sb = 2 * (int64_t)(last ? lastc : st * kBK);
+    uint4* slot = ring + (st % kNB) * kSlotP;
 #pragma unroll
-    for (int i = 0; i < kPA; ++i) As[buf][((rbase + 32 * i) * kLdsRow + 8 * kp) / 8] = S.a[i];
+    for (int i = 0; i < NA; ++i)
+      __builtin_amdgcn_global_load_lds((hp_gvoid_t*)(hb + sb + (last ? oal[i] : oa[i])),
+                                       (hp_lvoid_t*)(slot + (wv + NW * i) * 64), 16, 0, 0);
+    if (bw) {
 #pragma unroll
-    for (int i = 0; i < kPB; ++i) Bs[buf][((rbase + 32 * i) * kLdsRow + 8 * kp) / 8] = S.b[i];
+      for (int i = 0; i < NBI; ++i)
+        __builtin_amdgcn_global_load_lds((hp_gvoid_t*)(wb + sb + (last ? obl[i] : ob[i])),
+                                         (hp_lvoid_t*)(slot + kAPc + (wv + kBW * i) * 64), 16, 0, 0);
+    }
   };
   f32x4_t acc[kTM][kTN];
 #pragma unroll
@@ -137,42 +177,66 @@ __global__ __launch_bounds__(256, 2) void k_rnn_hproj_mfma(const uint16_t* __res
 #pragma unroll
     for (int b = 0; b < kTN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int rl = lane & 15, kg = lane >> 4;
-  const int wm = kWM * (wv / (kBN / kWN)), wn = kWN * (wv % (kBN / kWN));
-  auto compute = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int sub = 0; sub < kBK / 32; ++sub) {
-      bf16x8_t Af[kTM], Bf[kTN];
-#pragma unroll
-      for (int i = 0; i < kTM; ++i)
-        Af[i] = __builtin_bit_cast(bf16x8_t, As[buf][((wm + 16 * i + rl) * kLdsRow + 32 * sub + 8 * kg) / 8]);
-#pragma unroll
-      for (int i = 0; i < kTN; ++i)
-        Bf[i] = __builtin_bit_cast(bf16x8_t, Bs[buf][((wn + 16 * i + rl) * kLdsRow + 32 * sub + 8 * kg) / 8]);
-#pragma unroll
-      for (int a = 0; a < kTM; ++a)
-#pragma unroll
-        for (int b = 0; b < kTN; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[a], Bf[b], acc[a][b], 0, 0, 0);
+  const int wm = kWM * (wv / WNN), wn = kWN * (wv % WNN);
+  // stage s is due: this wave's pieces of it have landed (the loads of the
+  // AHEAD stages issued after it may still be in flight), then every wave's
+  // (barrier); a partial last stage has its columns past d zeroed
+  auto arrive = [&](auto ahead, int s) __attribute__((always_inline)) {
+    constexpr int AH = decltype(ahead)::value;
+    if (bw) hp_wait_vm_lgkm0<AH * (NA + NBI)>();
+    else hp_wait_vm_lgkm0<AH * NA>();
+    __builtin_amdgcn_s_barrier();
+    if (s == nst - 1 && d - s * kBK < kBK) {
+      const int cols = d - s * kBK;
+      uint4* w = ring + (s % kNB) * kSlotP;
+      for (int q = tid; q < kSlotP; q += NT) {
+        const int row = (q < kAPc ? q : q - kAPc) >> 3, p = (q & 7) ^ (row & 7);
+        if (8 * p >= cols) w[q] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      hp_wait_vm_lgkm0<0>();
+      __builtin_amdgcn_s_barrier();
     }
   };
-  HStage S0, S1;
-  gload(S0, 0);
-  gload(S1, 1);
-  lstore(S0, 0);
-  __syncthreads();
-  // two stages per trip so that the register sets keep fixed names: at stage
-  // s, the set for s + 1 is in flight and the set for s + 2 is issued
-  for (int st = 0; st < nst; st += 2) {
-    gload(S0, st + 2);
-    compute(0);
-    if (st + 1 < nst) lstore(S1, 1);
-    __syncthreads();
-    if (st + 1 >= nst) break;
-    gload(S1, st + 3);
-    compute(1);
-    if (st + 2 < nst) lstore(S0, 0);
-    __syncthreads();
+  auto frags = [&](int s, int sub, bf16x8_t (&Af)[kTM], bf16x8_t (&Bf)[kTN])
+      __attribute__((always_inline)) {
+    const uint4* slot = ring + (s % kNB) * kSlotP;
+    const int p = 4 * sub + kg;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+      Af[i] = __builtin_bit_cast(bf16x8_t, slot[hp_slot(wm + 16 * i + rl, p)]);
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+      Bf[j] = __builtin_bit_cast(bf16x8_t, slot[kAPc + hp_slot(wn + 16 * j + rl, p)]);
+  };
+  auto mfmas = [&](const bf16x8_t (&Af)[kTM], const bf16x8_t (&Bf)[kTN])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int a = 0; a < kTM; ++a)
+#pragma unroll
+      for (int b = 0; b < kTN; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af[a], Bf[b], acc[a][b], 0, 0, 0);
+  };
+  // Software pipeline over the two 32-column halves of each stage: the LDS
+  // reads of one half are in flight during the other half's MFMAs, across
+  // stage boundaries too.  The DMA of stage s is issued three stages before
+  // s is due; the slot it fills was last read a full stage earlier, before
+  // the barrier of the stage that precedes the issue.
+  for (int s = 0; s < kNB - 1; ++s) issue(s);
+  arrive(std::integral_constant<int, kNB - 2>{}, 0);
+  bf16x8_t A0[kTM], B0[kTN], A1[kTM], B1[kTN];
+  frags(0, 0, A0, B0);
+  for (int st = 0; st < nst; ++st) {
+    frags(st, 1, A1, B1);
+    mfmas(A0, B0);
+    if (st + 1 < nst) {
+      arrive(std::integral_constant<int, kNB - 3>{}, st + 1);
+      issue(st + kNB - 1);
+      frags(st + 1, 0, A0, B0);
+    }
+    mfmas(A1, B1);
   }
+  // the trailing loads (of stages past the last) complete before the stores
+  hp_wait_vm_lgkm0<0>();
 #pragma unroll
   for (int a = 0; a < kTM; ++a)
 #pragma unroll
@@ -441,10 +505,13 @@ hipError_t launch_rnn_hproj(const RnnArgs& a, hipStream_t st) {
   const int M = a.R * a.gamma, N = 3 * a.rank, ldw = 2 * a.rank + a.d, wcol = 2 * a.rank;
   if (M == 0) return hipSuccess;
   const bool aligned = ((reinterpret_cast<uintptr_t>(a.h) | reinterpret_cast<uintptr_t>(a.Wr)) & 15) == 0;
-  if (a.h_bf16 && a.w_bf16 && aligned && (a.d % 8) == 0) {
+  // the MFMA kernel addresses h and Wr with 32-bit byte offsets
+  const bool span_ok = (int64_t)M * a.d * 2 < ((int64_t)1 << 32) &&
+                       (int64_t)N * ldw * 2 < ((int64_t)1 << 32);
+  if (a.h_bf16 && a.w_bf16 && aligned && (a.d % 8) == 0 && span_ok) {
     const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-    hipLaunchKernelGGL(k_rnn_hproj_mfma, dim3(kXcds * ((tiles + kXcds - 1) / kXcds)), dim3(256),
-                       0, st, reinterpret_cast<const uint16_t*>(a.h),
+    hipLaunchKernelGGL(k_rnn_hproj_mfma<kHprojWaves>, dim3(kXcds * ((tiles + kXcds - 1) / kXcds)),
+                       dim3(64 * kHprojWaves), 0, st, reinterpret_cast<const uint16_t*>(a.h),
                        reinterpret_cast<const uint16_t*>(a.Wr), M, N, a.d, ldw, wcol, a.P);
     return hipGetLastError();
   }
