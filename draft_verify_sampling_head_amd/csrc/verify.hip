@@ -23,6 +23,7 @@
 //      the target row into max(0, p_t - p_d) per chunk.
 //   3. k_resid_pick, one workgroup per work item: chunk pick and in-chunk pick
 //      on log max(0, p_t - p_d); zero mass falls back to p_t.
+
 #include <atomic>
 
 #include "launch.hpp"
@@ -67,7 +68,9 @@ struct VerifyArgs {
   int* ybonus;          // [R] bonus token drawn from the request's last row
   int* acc;             // [R][gamma] outcome of each tested position (1 = rejected)
   uint32_t* epoch_word; // header word raised by workgroup 0 once the counters are clear
-  uint32_t epoch;       // this call's epoch
+  uint32_t epoch;       // this call's epoch from the host (below 2^31), or 0: taken on the device
+  uint32_t* last_word;  // header word: device epochs used so far (the last call's, counted)
+  int* rows_done;       // header word: rows of this call finished (device epochs only)
   uint32_t spin_limit;  // polls before the wait for the epoch gives up
   float scale2;         // log2(e) / T (chunk sums), 1 at T = 0
   bool vec_ok;          // 16-byte loads of target rows
@@ -223,7 +226,10 @@ __global__ __launch_bounds__(256) void k_verify_scan(VerifyArgs a) {
 // launch by workgroup 0, which then raises the launch's epoch in a header
 // word; a workgroup waits for that epoch (bounded) before its counter update.
 // Workgroup 0 is dispatched before every other, so the wait ends.  The epoch
-// is new for every call, so no state has to survive between calls.
+// comes from a per-process host counter, or, for a call captured in a graph
+// (where a host value would be frozen into every replay), from the device: a
+// count of the device epochs used so far, kept in a second header word and
+// advanced by the row that completes the call's count.
 constexpr int kVrThreads = 512;
 constexpr int kVrWaves = kVrThreads / 64;
 constexpr int kVrUnr = 8;                   // 16-byte loads in flight per lane
@@ -287,16 +293,55 @@ __global__ __launch_bounds__(kVrThreads) void k_verify_rows(VerifyArgs a) {
   __shared__ int s_i, s_lo, s_hi, s_ell;
   const int tid = threadIdx.x, wv = tid >> 6;
   const int q = blockIdx.x;
+  const int N = min(a.cu[a.R], a.R * (a.gamma + 1));
+  // this call's epoch.  From the host when the call is enqueued directly;
+  // under graph capture a host value would be frozen into every replay, so
+  // then it is taken on the device: the count of device epochs used so far
+  // plus one, with the top bit set so that it never equals a host epoch.
+  // Every workgroup reads that count before any row of the call is counted
+  // (it moves only once every row has been), so all agree.
+  const bool dev_epoch = a.epoch == 0;
+  uint32_t E = a.epoch;
+  if (dev_epoch && tid == 0)
+    E = ((__hip_atomic_load(a.last_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u) & 0x7FFFFFFFu) |
+        0x80000000u;
   if (q == 0) {
     for (int t = tid; t < a.R; t += kVrThreads) st_coh(a.req_done + t, 0);
-    if (tid == 0) st_coh(a.rej_count, 0);
+    if (tid == 0) { st_coh(a.rej_count, 0); st_coh(a.rows_done, 0); }
     __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0): the clears have completed
     __syncthreads();
-    if (tid == 0)
-      __hip_atomic_store(a.epoch_word, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      __hip_atomic_store(a.epoch_word, E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (dev_epoch && N <= 0)
+        __hip_atomic_store(a.last_word, E & 0x7FFFFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
-  const int N = min(a.cu[a.R], a.R * (a.gamma + 1));
   if (q >= N) return;
+  // (thread 0) wait for this call's epoch, bounded; false if the wait gave up.
+  // A wait that gives up leaves its row uncounted, so it records the epoch as
+  // finished itself: the next call then starts from a new epoch.
+  auto epoch_ready = [&]() {
+    uint32_t spins = 0;
+    while (__hip_atomic_load(a.epoch_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != E) {
+      if (++spins >= a.spin_limit) {
+        atomicOr(a.status, kFlagBarrier);
+        if (dev_epoch)
+          __hip_atomic_store(a.last_word, E & 0x7FFFFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    return true;
+  };
+  // (thread 0, after epoch_ready) with a device epoch, count row q; the last
+  // row of the call records the epoch as used.  (One counter for the whole
+  // call: its updates serialise, which costs about 9 us at 462 rows, so
+  // directly enqueued calls use the host epoch and skip it.)
+  auto count_row = [&]() {
+    if (dev_epoch &&
+        __hip_atomic_fetch_add(a.rows_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == N)
+      __hip_atomic_store(a.last_word, E & 0x7FFFFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   // the request whose offsets hold q, and its scheduled length
   if (tid == 0) s_i = -1;
   __syncthreads();
@@ -307,12 +352,18 @@ __global__ __launch_bounds__(kVrThreads) void k_verify_rows(VerifyArgs a) {
   __syncthreads();
   const int i = s_i;
   if (i < 0) {                                  // offsets not ascending
-    if (tid == 0) set_flag(a.status, kFlagBadLen);
+    if (tid == 0) {
+      set_flag(a.status, kFlagBadLen);
+      if (epoch_ready()) count_row();
+    }
     return;
   }
   const int q0 = s_lo, nrows = s_hi - s_lo, j = q - q0;
   if (nrows > a.gamma + 1) {                    // more rows than the block holds
-    if (tid == 0) set_flag(a.status, kFlagBadLen);
+    if (tid == 0) {
+      set_flag(a.status, kFlagBadLen);
+      if (epoch_ready()) count_row();
+    }
     return;
   }
   int L = s_ell;
@@ -411,19 +462,11 @@ __global__ __launch_bounds__(kVrThreads) void k_verify_rows(VerifyArgs a) {
   // update; the wave that completes request i scans it
   __builtin_amdgcn_s_waitcnt(0x0F70);
   int last = 0;
-  if (lane == 0) {
-    uint32_t spins = 0;
-    while (__hip_atomic_load(a.epoch_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
-      if (++spins >= a.spin_limit) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-    if (spins >= a.spin_limit) {
-      atomicOr(a.status, kFlagBarrier);
-    } else {
-      const int done = __hip_atomic_fetch_add(a.req_done + i, 1, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-      last = done + 1 == nrows;
-    }
+  if (lane == 0 && epoch_ready()) {
+    const int done = __hip_atomic_fetch_add(a.req_done + i, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    last = done + 1 == nrows;
+    count_row();
   }
   if (!__shfl(last, 0)) return;
   scan_published<GREEDY>(a, i, q0, L);
@@ -618,13 +661,14 @@ hipError_t launch_acceptance_rate(int R, int gamma, int V, int rank, float T, co
   return hipGetLastError();
 }
 
-// A new epoch for every fused verify launch (never 0, the value a cleared
-// workspace holds).
+// A new host epoch for every directly enqueued fused verify launch: in
+// [1, 2^31) (0 and the top bit are the device epochs' marks).
 static uint32_t next_verify_epoch() {
   static std::atomic<uint32_t> counter{0};
-  uint32_t e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
-  if (e == 0) e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
-  return e;
+  for (;;) {
+    const uint32_t e = (counter.fetch_add(1, std::memory_order_relaxed) + 1) & 0x7FFFFFFFu;
+    if (e != 0) return e;
+  }
 }
 
 hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t seed, uint64_t round,
@@ -668,7 +712,13 @@ hipError_t launch_verify(int R, int gamma, int V, int rank, float T, uint64_t se
     a.ybonus = a.req_done + R;
     a.acc = a.ybonus + R;
     a.epoch_word = hdr + 3;
-    a.epoch = next_verify_epoch();
+    // a host epoch for a call enqueued directly; 0 (epoch taken on the device)
+    // for a call being captured into a graph
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if ((e = hipStreamIsCapturing(st, &cs)) != hipSuccess) return e;
+    a.epoch = cs == hipStreamCaptureStatusNone ? next_verify_epoch() : 0u;
+    a.last_word = hdr + 4;
+    a.rows_done = reinterpret_cast<int*>(hdr + 5);
     a.spin_limit = switches().barrier_spins ? switches().barrier_spins : kBarrierSpins;
     const size_t lds = (size_t)nch * (greedy ? 12 : 8);
 #define DSPARK_VR(T_, G_) hipLaunchKernelGGL((k_verify_rows<T_, G_>), dim3(rows), dim3(kVrThreads), lds, st, a)

@@ -12,7 +12,9 @@ namespace dspark {
 
 struct WsLayout {
   size_t header;       // uint32 words: [0] status flags, [1] residual count,
-                       // [2] pipelined-draft epoch, [3] verify epoch
+                       // [2] pipelined-draft epoch, [3] verify epoch, [4] epoch
+                       // of the last verify whose rows all finished, [5] verify
+                       // rows finished
   size_t draft_l;      // float2 [R][nch]   chunk (max, scaled sum) / residual masses
   size_t draft_i;      // int32  [R][nch]   chunk argmax (greedy)
   size_t ver_l;        // float2 [R*(gamma+1)][nch]  target-row chunk (max, scaled sum)

@@ -117,7 +117,11 @@ enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 };
 dspark_status dspark_set_switch(int key, int64_t value);
 int64_t dspark_get_switch(int key);
 
-/* (host) Bytes of workspace every entry point below needs for these sizes. */
+/* (host) Bytes of workspace every entry point below needs for these sizes.
+ * Its first 256 bytes (the header: status word, the verify's epoch words and
+ * counters) must be zero when a workspace is first used; the calls keep them
+ * consistent afterwards, also when a call is captured in a HIP graph and
+ * replayed. */
 size_t dspark_workspace_bytes(int R, int gamma, int V, int r, int d);
 
 /* (host) Human-readable name of a status code. */

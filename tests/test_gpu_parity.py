@@ -196,6 +196,49 @@ def test_round_markov_one_call_matches_calls(base, over, sched):
     assert rep.ok(), rep.summary()
 
 
+@pytest.mark.parametrize("single", [False, True], ids=["calls", "one_call"])
+def test_round_replays_in_a_hip_graph(single):
+    """A whole round captured in a HIP graph (torch.cuda.graph) and replayed
+    several times, with eager rounds on other buffers in between: every
+    replay rewrites every output bit-identically to the eager round.  The
+    verify's cross-workgroup epoch lives on the device, so each replay gets a
+    new one (an epoch frozen into the captured arguments would let replays
+    after the first count rows before their counters were cleared)."""
+    cfg = synth.scaled(synth.config(2), R=40, gamma=5, V=3000, d=64)
+    inp = to_dev(synth.make_inputs(cfg, device="cpu"))
+    keys = ("x", "logp_d", "lse_d", "c", "ell", "N", "m", "tau", "emitted", "next_anchor",
+            "cu_out", "N_out")
+    ref_buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV)
+    RD.run_round(inp, ref_buf, cfg.T, cfg.philox_seed, 3, scheduler=True)
+    torch.cuda.synchronize()
+    assert D.get_status(ref_buf.ws) == 0
+    ref = {k: n(getattr(ref_buf, k)).copy() for k in keys}
+    buf = RD.RoundBuffers(cfg.R, cfg.gamma, cfg.V, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):              # warm-up outside the capture
+        RD.run_round(inp, buf, cfg.T, cfg.philox_seed, 3, scheduler=True, single_call=single)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        RD.run_round(inp, buf, cfg.T, cfg.philox_seed, 3, scheduler=True, single_call=single)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for k in ("x", "m", "tau", "emitted", "next_anchor", "cu_out", "ell"):
+            getattr(buf, k).fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert D.get_status(buf.ws) == 0, rep
+        for k in keys:
+            assert np.array_equal(n(getattr(buf, k)).view(np.uint8), ref[k].view(np.uint8)), (rep, k)
+        N_out = int(ref["N_out"][0])
+        assert np.array_equal(n(buf.flat_out)[:N_out], n(ref_buf.flat_out)[:N_out]), rep
+        # eager work on other buffers between replays
+        RD.run_round(inp, ref_buf, cfg.T, cfg.philox_seed, 3, scheduler=True)
+        torch.cuda.synchronize()
+
+
 def test_fp32_logits_bf16_weights():
     cfg = synth.scaled(synth.config(2), R=34, gamma=4, V=1900, d=64)
     inp = synth.make_inputs(cfg, device="cpu")
