@@ -451,18 +451,21 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
 }
 
-template <typename UT, int KS, int MODE, int NBUF>
-__global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
+template <typename UT, int KS, int MODE, int NBUF, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_markov_mfma(MarkovArgs a) {
+  constexpr int NT = 64 * NWV;                            // threads
+  constexpr int NTW = 256 / (32 * NWV);                   // 32-row tiles per wave
   constexpr int SEGMAX = 2 * KS;                          // W2t row segments
   constexpr int EPL = 16 / (int)sizeof(UT);               // U elements per segment
   constexpr int SPR = 32 / EPL;                           // U segments per row of a tile
   constexpr int USEG = 16 / EPL;                          // U segments read per lane (16 values)
   constexpr int W2_SEGS = 32 * SEGMAX;
   constexpr int SLOT = W2_SEGS + 256 * SPR;               // 16-byte units per ring slot
-  constexpr int NW = KS / 4;                              // W2 DMA ops per wave per tile
-  constexpr int NU = SPR;                                 // U DMA ops per wave per tile
+  constexpr int NW = KS / NWV;                            // W2 DMA ops per wave per tile
+  constexpr int NU = 4 * SPR / NWV;                       // U DMA ops per wave per tile
   constexpr int OPS = NW + NU;
   static_assert(KS >= 4 && KS % 4 == 0, "DMA path needs rank >= 64");
+  static_assert((NWV == 4 || NWV == 8) && KS % NWV == 0 && (4 * SPR) % NWV == 0, "waves");
   static_assert(NBUF == 4, "ring depth");
   __shared__ u32x4_t ring[NBUF * SLOT];
 
@@ -480,14 +483,14 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
   const int vbase = c0 * kChunk;
   const int nseg = a.rank >> 3;
   const int smask = ((nseg & (nseg - 1)) == 0) ? min(nseg, 16) - 1 : 0;
-  const bool wave_active = rg * 256 + wv * 64 < nrows;
+  const bool wave_active = rg * 256 + wv * 32 * NTW < nrows;
 
   // ---- rows computed by this lane: column n of the wave's two 32-row tiles
   const int n = lane & 31, half = lane >> 5;
-  bool valid[2];
-  const UT* trow[2];
-  int prevs[2];
-  float mt[2], lrt2[2], lse_d[2];
+  bool valid[NTW];
+  const UT* trow[NTW];
+  int prevs[NTW];
+  float mt[NTW], lrt2[NTW], lse_d[NTW];
   auto row_info = [&](int row, int& req, int& kk, int& tr, int& qr) __attribute__((always_inline)) {
     req = 0; kk = a.k; tr = 0; qr = 0;
     if (row < nrows) {
@@ -500,8 +503,8 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
     }
   };
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int row = rg * 256 + wv * 64 + nt * 32 + n;
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int row = rg * 256 + wv * 32 * NTW + nt * 32 + n;
     valid[nt] = row < nrows;
     int req, kk, tr, qr;
     row_info(row, req, kk, tr, qr);
@@ -517,9 +520,9 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
       lse_d[nt] = a.lse_d[(int64_t)req * a.gamma + (kk - 1)];
     }
   }
-  bf16x8_t Bf[2][KS];
+  bf16x8_t Bf[NTW][KS];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NTW; ++nt) {
     const uint16_t* erow = a.W1 + (int64_t)prevs[nt] * a.rank + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -536,7 +539,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
   int w2_row[NW];
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
-    const int idx = (wv + 4 * i) * 64 + lane;
+    const int idx = (wv + NWV * i) * 64 + lane;
     const int r = idx / SEGMAX, p = idx - r * SEGMAX;
     w2_row[i] = r;
     w2_off[i] = (p < nseg) ? (p ^ (seg_swizzle(r) & smask)) * 8 : -1;
@@ -545,7 +548,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
   int u_seg[NU];
 #pragma unroll
   for (int i = 0; i < NU; ++i) {
-    const int idx = (wv + 4 * i) * 64 + lane;
+    const int idx = (wv + NWV * i) * 64 + lane;
     const int rr = idx / SPR, sp = idx - rr * SPR;
     u_seg[i] = (sp ^ (u_swizzle(rr) & (SPR - 1))) * EPL;
     int req, kk, tr, qr;
@@ -559,7 +562,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
     const int vb = vbase + min(t, T - 1) * 32;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      const int g = wv + 4 * i;
+      const int g = wv + NWV * i;
       if (w2_off[i] >= 0) {
         const int v = min(vb + w2_row[i], a.V - 1);
         __builtin_amdgcn_global_load_lds(
@@ -569,7 +572,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
-      const int g = wv + 4 * i;
+      const int g = wv + NWV * i;
       const int v = min(vb + u_seg[i], vmax_seg);
       __builtin_amdgcn_global_load_lds((gvoid_t*)(u_ptr[i] + v),
                                        (lvoid_t*)(ring + S * SLOT + W2_SEGS + g * 64), 16, 0, 0);
@@ -577,7 +580,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
   };
   if (nseg < SEGMAX) {
     const u32x4_t z = {0u, 0u, 0u, 0u};
-    for (int j = tid; j < NBUF * W2_SEGS; j += 256) {
+    for (int j = tid; j < NBUF * W2_SEGS; j += NT) {
       const int sl = j / W2_SEGS, u = j - sl * W2_SEGS;
       if (u % SEGMAX >= nseg) ring[sl * SLOT + u] = z;
     }
@@ -590,7 +593,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
     if (vb + 32 > a.V) {
       const uint32_t ninf = (EPL == 8) ? 0xFF80FF80u : 0xFF800000u;
       const u32x4_t w = {ninf, ninf, ninf, ninf};
-      for (int j = tid; j < 256 * SPR; j += 256) {
+      for (int j = tid; j < 256 * SPR; j += NT) {
         const int rr = j / SPR, sp = j - rr * SPR;
         const int seg = sp ^ (u_swizzle(rr) & (SPR - 1));
         if (vb + seg * EPL >= a.V) ring[S * SLOT + W2_SEGS + j] = w;
@@ -602,19 +605,19 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
   };
 
   // ---- epilogue state
-  float Mr[2], Sr[2], Ms2[2];
-  int Ir[2];
+  float Mr[NTW], Sr[NTW], Ms2[NTW];
+  int Ir[NTW];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) { Mr[nt] = -INFINITY; Sr[nt] = 0.f; Ms2[nt] = -INFINITY; Ir[nt] = 0x7FFFFFFF; }
+  for (int nt = 0; nt < NTW; ++nt) { Mr[nt] = -INFINITY; Sr[nt] = 0.f; Ms2[nt] = -INFINITY; Ir[nt] = 0x7FFFFFFF; }
   const float s2 = a.scale2;
   const float invT = s2 * kLn2;
 
   // straight-line part of the epilogue of one tile: x = acc + U, then the
   // running (max, sum) or argmax update, branch-free
-  auto epi_hot = [&](f32x16_t (&acc)[2], const u32x4_t (&uw)[2][USEG], int t) __attribute__((always_inline)) {
+  auto epi_hot = [&](f32x16_t (&acc)[NTW], const u32x4_t (&uw)[NTW][USEG], int t) __attribute__((always_inline)) {
     const int vt = vbase + t * 32 + 16 * half;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NTW; ++nt) {
       float x[16];
 #pragma unroll
       for (int e = 0; e < USEG; ++e) {
@@ -669,8 +672,8 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
     if ((t & 3) != 3) return;
     const int c = c0 + (t >> 2);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int row = rg * 256 + wv * 64 + nt * 32 + n;
+    for (int nt = 0; nt < NTW; ++nt) {
+      const int row = rg * 256 + wv * 32 * NTW + nt * 32 + n;
       const int64_t o = (int64_t)row * a.nch + c;
       if (MODE == kModeGreedy) {
         float bv = Mr[nt];
@@ -710,11 +713,11 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
       }
     }
   };
-  auto read_u = [&](auto Sc, u32x4_t (&uw)[2][USEG]) __attribute__((always_inline)) {
+  auto read_u = [&](auto Sc, u32x4_t (&uw)[NTW][USEG]) __attribute__((always_inline)) {
     constexpr int S = decltype(Sc)::value;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int rr = wv * 64 + nt * 32 + n;
+    for (int nt = 0; nt < NTW; ++nt) {
+      const int rr = wv * 32 * NTW + nt * 32 + n;
       const u32x4_t* ul = ring + S * SLOT + W2_SEGS + rr * SPR;
       const int usw = u_swizzle(rr) & (SPR - 1);
 #pragma unroll
@@ -722,7 +725,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
     }
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[2][NTW];
   // Schedule of tile t (ring slot t % 4, accumulator buffer t % 2):
   //   wait for tile t's DMA, barrier, DMA of tile t+2 into the slot of t-2,
   //   then the MFMAs of tile t interleaved with the epilogue of tile t-1
@@ -738,27 +741,34 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
     issue(std::integral_constant<int, SN>{}, t + 2);
     if (wave_active) {
       const u32x4_t* tile = ring + S * SLOT + arow * SEGMAX;
+      // A operands: all k-steps up front with two 32-row tiles per wave; with
+      // one (eight waves, two per SIMD, half the registers) a rolling window
+      // three k-steps deep, each loaded two MFMAs before its use
+      constexpr int AW_AHEAD = NTW == 1 ? 2 : KS;
       u32x4_t aw[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) aw[ks] = tile[(2 * ks + half) ^ aswz];
-      u32x4_t uw[2][USEG];
+      for (int ks = 0; ks < AW_AHEAD && ks < KS; ++ks) aw[ks] = tile[(2 * ks + half) ^ aswz];
+      u32x4_t uw[NTW][USEG];
       if (with_epi) read_u(std::integral_constant<int, SP>{}, uw);
       __builtin_amdgcn_sched_barrier(0);
       const f32x16_t zero = {};
       // the epilogue of tile t-1 is cut into 2*KS slices, one after each MFMA:
       // first half = x = acc + U with the running max (or argmax), second half
       // = the exp sums relative to the new maximum
-      constexpr int NSL = 2 * KS;
+      constexpr int NSL = NTW * KS;
       constexpr int HALF_SL = NSL / 2;
-      constexpr int PER_A = (32 + HALF_SL - 1) / HALF_SL;
-      float x[2][16];
-      float tmx[2] = {-INFINITY, -INFINITY};
-      float ssum[2] = {0.f, 0.f};
-      float nM[2], nMs2[2];
+      constexpr int PER_A = (16 * NTW + HALF_SL - 1) / HALF_SL;
+      float x[NTW][16];
+      float tmx[NTW], ssum[NTW];
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) { tmx[nt] = -INFINITY; ssum[nt] = 0.f; }
+      float nM[NTW], nMs2[NTW];
       const int vt = vbase + (t - 1) * 32 + 16 * half;
 #pragma unroll
       for (int i = 0; i < NSL; ++i) {
-        const int ks = i >> 1, ntm = i & 1;
+        const int ks = i / NTW, ntm = i % NTW;
+        if (NTW == 1 && ntm == 0 && ks + AW_AHEAD < KS)
+          aw[ks + AW_AHEAD] = tile[(2 * (ks + AW_AHEAD) + half) ^ aswz];
         const bf16x8_t A = __builtin_bit_cast(bf16x8_t, aw[ks]);
         acc[P][ntm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bf[ntm][ks], ks ? acc[P][ntm] : zero, 0, 0, 0);
         if (with_epi && MODE != kModeResid) {
@@ -766,7 +776,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
 #pragma unroll
             for (int q = 0; q < PER_A; ++q) {
               const int e = i * PER_A + q;
-              if (e < 32) {
+              if (e < 16 * NTW) {
                 const int nt = e >> 4, j = e & 15;
                 const uint32_t wd = uw[nt][j / EPL][(j % EPL) / (EPL / 4)];
                 const float u = (EPL == 8) ? ((j & 1) ? bf16_hi(wd) : bf16_lo(wd)) : __uint_as_float(wd);
@@ -786,7 +796,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
           } else if (MODE == kModeSample) {
             if (i == HALF_SL) {
 #pragma unroll
-              for (int nt = 0; nt < 2; ++nt) {
+              for (int nt = 0; nt < NTW; ++nt) {
                 nM[nt] = fmaxf(Mr[nt], tmx[nt]);
                 nMs2[nt] = nM[nt] * s2;
               }
@@ -794,7 +804,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
 #pragma unroll
             for (int q = 0; q < PER_A; ++q) {
               const int e = (i - HALF_SL) * PER_A + q;
-              if (e < 32) {
+              if (e < 16 * NTW) {
                 const int nt = e >> 4, j = e & 15;
                 ssum[nt] += __builtin_amdgcn_exp2f(fmaf(x[nt][j], s2, -nMs2[nt]));
                 asm volatile("" : "+v"(ssum[nt]));
@@ -807,7 +817,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
       if (with_epi) {
         if (MODE == kModeSample) {
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < NTW; ++nt) {
             // rescale the running sum to the new maximum; an all -inf tile
             // leaves the state unchanged; a NaN sum stays NaN
             const float newS = Sr[nt] * __builtin_amdgcn_exp2f(Ms2[nt] - nMs2[nt]) + ssum[nt];
@@ -841,7 +851,7 @@ __global__ __launch_bounds__(256) void k_markov_mfma(MarkovArgs a) {
   // epilogue of the last tile (T-1, slot 3, accumulator buffer 1)
   wait_vm_lgkm0<0>();
   if (wave_active) {
-    u32x4_t uw[2][USEG];
+    u32x4_t uw[NTW][USEG];
     read_u(std::integral_constant<int, 3>{}, uw);
     epi_hot(acc[1], uw, T - 1);
     epi_chunk(T - 1);
@@ -957,9 +967,14 @@ static void launch_mfma_ks(MarkovArgs& a, int grid, hipStream_t st, bool dma) {
 #define DSPARK_DMA(KS_)                                                                          \
     {                                                                                             \
       constexpr int SLOTB = (32 * 2 * KS_ + 256 * SPR) * 16;                                      \
+      constexpr int KSD = 4 * SLOTB <= 160 * 1024 ? KS_ : 4;                                      \
       if (4 * SLOTB <= 160 * 1024) {                                                              \
-        hipLaunchKernelGGL((k_markov_mfma<UT, (4 * SLOTB <= 160 * 1024 ? KS_ : 4), MODE, 4>),    \
-                           dim3(grid), dim3(256), 0, st, a);                                      \
+        if (KSD >= 8 && MODE != kModeResid)                                                       \
+          hipLaunchKernelGGL((k_markov_mfma<UT, KSD, MODE, 4, (KSD >= 8 ? 8 : 4)>), dim3(grid),   \
+                             dim3(512), 0, st, a);                                                \
+        else                                                                                      \
+          hipLaunchKernelGGL((k_markov_mfma<UT, KSD, MODE, 4, 4>), dim3(grid), dim3(256), 0, st,  \
+                             a);                                                                  \
         return;                                                                                   \
       }                                                                                           \
     }
