@@ -20,6 +20,7 @@
 //                persistent kernel does not take (float32 data, rank other than
 //                64/128/256, vocabularies beyond 512 entries per compute unit).
 // Nothing returns to the host in either schedule.
+#include <atomic>
 #include <cfloat>
 #include <cstdlib>
 #include <cstring>
@@ -792,21 +793,30 @@ bool launch_resid_slices(int R, int gamma, int V, int rank, float T, const void*
 // Per-device facts for the persistent schedule (compute units; whether one
 // workgroup of each instance fits per compute unit).
 struct PersistInfo {
-  int cus = -1;
-  int fits[3][2][2] = {{{-1, -1}, {-1, -1}}, {{-1, -1}, {-1, -1}}, {{-1, -1}, {-1, -1}}};
+  // filled on first use; calls from several host threads may race to fill
+  // an entry, all with the same value (atomic, relaxed)
+  std::atomic<int> cus{-1};
+  std::atomic<int> fits[3][2][2];
+  PersistInfo() {
+    for (auto& a : fits)
+      for (auto& b : a)
+        for (auto& c : b) c.store(-1, std::memory_order_relaxed);
+  }
 };
 static PersistInfo g_pinfo[64];
 
 template <int KS, bool G, bool F>
 static bool persist_fits(PersistInfo& pi, int ki) {
-  if (pi.fits[ki][G][F] < 0) {
+  int f = pi.fits[ki][G][F].load(std::memory_order_relaxed);
+  if (f < 0) {
     int nb = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
         &nb, reinterpret_cast<const void*>(k_draft_persistent<KS, G, F>), kPThreads, 0);
-    pi.fits[ki][G][F] = (e == hipSuccess && nb >= 1) ? 1 : 0;
+    f = (e == hipSuccess && nb >= 1) ? 1 : 0;
     (void)hipGetLastError();
+    pi.fits[ki][G][F].store(f, std::memory_order_relaxed);
   }
-  return pi.fits[ki][G][F] == 1;
+  return f == 1;
 }
 
 template <int KS, bool G, bool F>
@@ -831,13 +841,13 @@ static int persistent_grid(int gamma, int V, int rank, bool u_bf16, bool w_bf16,
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   PersistInfo& pi = g_pinfo[dev];
-  if (pi.cus < 0) {
-    int cus = 0;
+  int cus = pi.cus.load(std::memory_order_relaxed);
+  if (cus < 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
-    pi.cus = cus;
+    pi.cus.store(cus, std::memory_order_relaxed);
   }
   const int nslice = (V + kPSlice - 1) / kPSlice;
-  if (pi.cus < 1 || pi.cus > kMaxGrid || nslice > pi.cus || (V + kChunk - 1) / kChunk > kPMaxChunks)
+  if (cus < 1 || cus > kMaxGrid || nslice > cus || (V + kChunk - 1) / kChunk > kPMaxChunks)
     return 0;
   bool fits;
 #define DSPARK_FITS(KS_, KI_, F_) \
@@ -852,7 +862,7 @@ static int persistent_grid(int gamma, int V, int rank, bool u_bf16, bool w_bf16,
     else fits = DSPARK_FITS(16, 2, false);
   }
 #undef DSPARK_FITS
-  return fits ? pi.cus : 0;
+  return fits ? cus : 0;
 }
 
 __global__ void k_zero_words(uint32_t* p, int n) {

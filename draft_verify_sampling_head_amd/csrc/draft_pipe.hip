@@ -32,6 +32,7 @@
 // advancing its own pending pick, so the chains cannot deadlock: all tiles of
 // step k need only the tokens of step k-1, and every pick of step k needs only
 // the tiles of step k.
+#include <atomic>
 #include <cfloat>
 
 #include "launch.hpp"
@@ -854,19 +855,25 @@ __global__ void k_pipe_prep(uint32_t* epoch_word, int32_t* x, const int32_t* x0,
 }
 
 struct PipeInfo {
-  int fits[3][2] = {{-1, -1}, {-1, -1}, {-1, -1}};
+  // filled on first use (atomic, relaxed: racing fills store the same value)
+  std::atomic<int> fits[3][2];
+  PipeInfo() {
+    for (auto& a : fits)
+      for (auto& c : a) c.store(-1, std::memory_order_relaxed);
+  }
 };
 static PipeInfo g_pipe[64];
 
 template <int KS, bool G>
 static bool pipe_fits(int dev, int ki) {
-  int& f = g_pipe[dev].fits[ki][G];
+  int f = g_pipe[dev].fits[ki][G].load(std::memory_order_relaxed);
   if (f < 0) {
     int nb = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
         &nb, reinterpret_cast<const void*>(k_draft_pipe<KS, G>), kPThreads, 0);
     f = (e == hipSuccess && nb >= 1) ? 1 : 0;
     (void)hipGetLastError();
+    g_pipe[dev].fits[ki][G].store(f, std::memory_order_relaxed);
   }
   return f == 1;
 }
