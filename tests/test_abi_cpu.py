@@ -293,3 +293,34 @@ def test_round_markov_checks_every_call_before_enqueueing():
     assert _round(cu_out=None) == INVALID               # output pack
     assert lib.dspark_round_markov(C.byref(L.RoundMarkovArgs()), FAKE, 1 << 30, None) == INVALID
     assert _round(R=0) == OK                            # empty batch: nothing to do
+
+
+def test_round_markov_args_layout_matches_header(tmp_path):
+    """The binding's ctypes mirror of dspark_round_markov_args has the C
+    struct's size and every field at the C offset (a small C program compiled
+    against include/dspark.h prints them)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [n for n, _ in L.RoundMarkovArgs._fields_]
+    hip_stub = tmp_path / "hip" / "hip_runtime_api.h"
+    hip_stub.parent.mkdir()
+    hip_stub.write_text("typedef struct ihipStream_t* hipStream_t;\n"
+                        "typedef struct ihipEvent_t* hipEvent_t;\n")
+    src = tmp_path / "layout.c"
+    body = "\n".join(f'  printf("{n} %zu\\n", offsetof(dspark_round_markov_args, {n}));' for n in fields)
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"dspark.h\"\n"
+                   "int main(void) {\n"
+                   '  printf("sizeof %zu\\n", sizeof(dspark_round_markov_args));\n'
+                   f"{body}\n  return 0;\n}}\n")
+    exe = tmp_path / "layout"
+    r = subprocess.run([cc, "-std=c11", f"-I{tmp_path}", f"-I{os.path.join(ROOT, 'include')}",
+                        str(src), "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    assert int(out["sizeof"]) == C.sizeof(L.RoundMarkovArgs)
+    for n in fields:
+        assert int(out[n]) == getattr(L.RoundMarkovArgs, n).offset, n
