@@ -161,8 +161,10 @@ dspark_status dspark_get_status(const void* ws, size_t ws_bytes, uint32_t* flags
  * DSPARK_F32 weights run it on the vector ALU.  With bf16 U and weights,
  * r in {64, 128, 256}, 16-byte aligned tables, V a multiple of 8 and at most
  * 512 vocabulary entries per compute unit, all gamma steps run as one
- * cooperative launch that keeps W2 on chip (grid barriers between steps;
- * DSPARK_FLAG_BARRIER reports a barrier that gave up waiting); other shapes
+ * launch whose workgroups are all resident at once (at most one per compute
+ * unit; plain launch, or cooperative with DSPARK_SWITCH_PERSIST_LAUNCH) that
+ * keeps W2 on chip (grid barriers between steps; DSPARK_FLAG_BARRIER reports
+ * a barrier that gave up waiting); other shapes
  * run two launches per step, and r == 0 (independent positions) two launches
  * in all.  The schedules give the same results.  DSPARK_SWITCH_FORCE_PER_STEP
  * forces the per-step schedule.
@@ -220,8 +222,8 @@ dspark_status dspark_draft_markov_noalloc(int R, int gamma, int V, int r, float 
 /*
  * Instrumented dspark_draft_markov for performance measurement: identical
  * results; additionally records events on `stream` around the draft's
- * dominant kernel.  With the persistent schedule (one cooperative launch for
- * all gamma steps) that is ev_begin[0] / ev_end[0] around the launch and
+ * dominant kernel.  With the persistent schedule (one launch for all gamma
+ * steps) that is ev_begin[0] / ev_end[0] around the launch and
  * *n_timed = 1; with the per-step schedule ev_begin[k-1] / ev_end[k-1] bracket
  * the per-chunk statistics kernel of step k and *n_timed = gamma; at r == 0
  * (independent positions: one statistics launch over all R gamma rows, then
@@ -530,7 +532,7 @@ size_t dspark_rnn_workspace_bytes(int R, int gamma, int V, int r, int d);
  * bf16 with d a multiple of 8 and 16-byte aligned tables).  With bf16 U,
  * weights and h, r in {64, 128, 256}, 2r + d a multiple of 8 and the shape
  * limits of dspark_draft_markov's persistent launch, all gamma steps (cell,
- * statistics, pick) run in one cooperative launch with two grid barriers per
+ * statistics, pick) run in one co-resident launch with two grid barriers per
  * step (DSPARK_FLAG_BARRIER as there).  Other shapes run three launches per
  * step: the cell (MFMA with the fp32 state split into exact bf16 parts for
  * bf16 weights, fp32 vector ALU otherwise), the per-chunk statistics and the
@@ -587,7 +589,7 @@ dspark_status dspark_verify_cap_accept_features(int R, int gamma, int V, int r, 
  * Instrumented dspark_draft_rnn for performance measurement: identical
  * results; additionally records events on `stream` around the draft's
  * dominant kernel.  With the persistent schedule (cell, statistics and pick
- * of all gamma steps in one cooperative launch) that is ev_begin[0] /
+ * of all gamma steps in one launch) that is ev_begin[0] /
  * ev_end[0] around the launch and *n_timed = 1; with the per-step schedule
  * ev_begin[k-1] / ev_end[k-1] bracket the per-chunk statistics kernel of
  * step k and *n_timed = gamma.
