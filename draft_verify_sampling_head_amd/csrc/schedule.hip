@@ -23,6 +23,13 @@
 // largest admitted position of request r (admitted positions of a request are
 // always a prefix 1..ell_r, because a is non-increasing in j).
 //
+// The rule reads the order only up to its first stop, a few hundred
+// positions for real confidence curves.  So Algorithm 1 first orders only a
+// selected prefix of about 512 keys (histograms of the keys' high bits find
+// it; it is ranked bucket by bucket) and decides on it with one position per
+// thread; the whole sort above runs only when the stop is not inside that
+// prefix, or when too many equal keys make the prefix too long.
+//
 // The asynchronous form used in production (same page, Supplementary details,
 // the scheduler in production) sorts the same keys and takes two decisions
 // from the one sort: admission of the first min(K_in, N_max) - R candidates
@@ -231,10 +238,143 @@ __device__ __forceinline__ void merge_sort_runs(uint64_t (&v)[EPT], uint64_t* ke
   }
 }
 
+// Algorithm 1 reads the sorted order only up to its first stop, which for
+// real confidence curves lies a few hundred positions in, however many
+// candidates there are.  So before sorting everything, the kSelK smallest
+// keys (largest a) are selected: a histogram of 12 bits of the keys' high
+// halves (bits 19..30: exponent and four mantissa bits of a; bit 31 is the
+// same for every candidate) finds the bucket in which the count reaches
+// kSelK; if more than kSelMax keys lie up to that bucket, a second histogram
+// of the next 12 bits, over that bucket's keys alone, finds the crossing
+// there.  The selected set is every key whose prefix (12 or 24 bits) does not
+// exceed the crossing one, so it is a prefix of the full order: keys with
+// equal prefixes are all in or all out.  Ordering the set: with one level,
+// the exclusive scan of the bucket counts is each bucket's first position, so
+// every key is scattered into its bucket's range and ranked against the keys
+// of its own bucket only; after a second level the keys are ranked against
+// the whole set.  The keys are distinct, so the ranks are a permutation.
+// Thread t receives positions [t EPT, t EPT + EPT) in v, sentinels past the
+// set.  Returns the set's size n, or -1 when more than kSelMax keys tie on
+// the prefixes around the crossing; *total is the number of candidates.  The
+// caller sorts everything when -1 comes back, or when the admission scan over
+// the n positions finds no stop and n < *total.
+constexpr int kSelK = 512;
+constexpr int kSelMax = 1024;
+constexpr int kSelBins = 4 * kSchedThreads;
+
+template <int EPT>
+__device__ int select_sorted_prefix(uint64_t (&v)[EPT], const uint64_t* keys, int P,
+                                    uint32_t* whist, uint64_t* ssel, int* sel, int64_t* red64,
+                                    int* total) {
+  static_assert(kSelBins == (kSchedThreads / 64) * 256, "the bins fill the radix count buffer");
+  static_assert(kSelBins * 4 >= kSelMax * 8, "the ranked keys fit the bins' buffer");
+  static_assert(kSchedMaxKeys < 65536, "bucket offsets and counts fit 16 bits");
+  const int tid = threadIdx.x;
+  // one histogram level: bins (k >> shift) & 0xFFF over the candidates (only
+  // those of level-1 bucket b1 when inb); returns the crossing bin of `need`
+  // (the last bin when the count never reaches it), the count before it and
+  // the count through it; n_all = count of everything histogrammed.  Each
+  // thread then leaves, in its own four bins, the bin's first position in
+  // the high half and zero in the low half (the scatter's running count).
+  auto level = [&](int shift, bool inb, uint32_t b1, int need, int& b, int& before_b,
+                   int& through_b, int& n_all) {
+    for (int t = tid; t < kSelBins; t += kSchedThreads) whist[t] = 0;
+    if (tid == 0) { sel[0] = kSelBins - 1; sel[1] = 0; sel[2] = -1; sel[4] = 0; }
+    __syncthreads();
+    for (int q = tid; q < P; q += kSchedThreads) {
+      const uint64_t k = keys[q];
+      if (k != ~0ull && (!inb || (uint32_t)((k >> 51) & 0xFFFu) == b1))
+        atomicAdd(&whist[(uint32_t)(k >> shift) & 0xFFFu], 1u);
+    }
+    __syncthreads();
+    int c[4], s = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { c[q] = (int)whist[4 * tid + q]; s += c[q]; }
+    int cum = (int)block_exscan_i64(s, red64);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (cum < need && cum + c[q] >= need) { sel[0] = 4 * tid + q; sel[1] = cum; sel[2] = cum + c[q]; }
+      whist[4 * tid + q] = (uint32_t)cum << 16;
+      cum += c[q];
+    }
+    if (tid == kSchedThreads - 1) sel[3] = cum;
+    __syncthreads();
+    b = sel[0];
+    before_b = sel[1];
+    n_all = sel[3];
+    through_b = sel[2] < 0 ? n_all : sel[2];
+    __syncthreads();                           // sel is rewritten next
+  };
+  int b1, cb1, nb1, n_all;
+  level(51, false, 0u, kSelK, b1, cb1, nb1, n_all);
+  *total = n_all;
+  uint64_t* out = reinterpret_cast<uint64_t*>(whist);
+  int n = nb1;
+  int r = 0;
+  uint64_t x = 0;
+  if (nb1 <= kSelMax) {
+    // one level: scatter into the buckets, rank inside the bucket
+    for (int q = tid; q < P; q += kSchedThreads) {
+      const uint64_t k = keys[q];
+      const uint32_t d1 = (uint32_t)((k >> 51) & 0xFFFu);
+      if (k != ~0ull && (int)d1 <= b1) {
+        const uint32_t w = atomicAdd(&whist[d1], 1u);
+        ssel[(w >> 16) + (w & 0xFFFFu)] = k;
+      }
+    }
+    __syncthreads();
+    if (tid < n) {
+      x = ssel[tid];
+      const uint32_t w = whist[(uint32_t)((x >> 51) & 0xFFFu)];
+      const int s0 = (int)(w >> 16), cnt = (int)(w & 0xFFFFu);
+      r = s0;
+      int i = 0;
+      for (; i + 4 <= cnt; i += 4) {
+        const uint64_t y0 = ssel[s0 + i], y1 = ssel[s0 + i + 1], y2 = ssel[s0 + i + 2],
+                       y3 = ssel[s0 + i + 3];
+        r += (y0 < x ? 1 : 0) + (y1 < x ? 1 : 0) + (y2 < x ? 1 : 0) + (y3 < x ? 1 : 0);
+      }
+      for (; i < cnt; ++i) r += (ssel[s0 + i] < x) ? 1 : 0;
+    }
+  } else {
+    // second level inside the crossing bucket; the selected keys are ranked
+    // against all of them
+    int b2, cb2, nb2, n_b1;
+    level(39, true, (uint32_t)b1, kSelK - cb1, b2, cb2, nb2, n_b1);
+    n = cb1 + nb2;
+    if (n > kSelMax) return -1;
+    for (int q = tid; q < P; q += kSchedThreads) {
+      const uint64_t k = keys[q];
+      if (k == ~0ull) continue;
+      const int d1 = (int)((k >> 51) & 0xFFFu), d2 = (int)((k >> 39) & 0xFFFu);
+      if (d1 < b1 || (d1 == b1 && d2 <= b2)) ssel[atomicAdd(&sel[4], 1)] = k;
+    }
+    __syncthreads();
+    if (tid < n) {
+      x = ssel[tid];
+      int i = 0;
+      for (; i + 4 <= n; i += 4) {
+        const uint64_t y0 = ssel[i], y1 = ssel[i + 1], y2 = ssel[i + 2], y3 = ssel[i + 3];
+        r += (y0 < x ? 1 : 0) + (y1 < x ? 1 : 0) + (y2 < x ? 1 : 0) + (y3 < x ? 1 : 0);
+      }
+      for (; i < n; ++i) r += (ssel[i] < x) ? 1 : 0;
+    }
+  }
+  __syncthreads();                             // the bins are read; out overwrites them
+  if (tid < n) out[r] = x;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int p = tid * EPT + e;
+    v[e] = (p < n) ? out[p] : ~0ull;
+  }
+  return n;
+}
+
 template <int EPT>
 __device__ __forceinline__ void schedule_body(const SchedArgs& a, int G2, uint64_t* keys, int64_t* red64,
                                               int* red32, const int* kin_l, uint32_t* whist,
-                                              int* scan_lds) {
+                                              int* scan_lds, uint64_t* ssel, int* sel) {
   const int tid = threadIdx.x;
   const int R = a.R, G = a.gamma;
   const int P = kSchedThreads * EPT;
@@ -311,67 +451,108 @@ __device__ __forceinline__ void schedule_body(const SchedArgs& a, int G2, uint64
     return;
   }
 
-  // sort ascending: a descending, then r, then j.  Up to four keys per
-  // thread with ascending padded runs: the run merge; otherwise (more keys,
-  // or runs out of order) the radix sort, which keeps equal values of a in
-  // the buffer's (r, j) order.
+  // Admission over sorted positions in v: thread t owns [t*EPT, t*EPT + EPT),
+  // and the first sentinel ends the candidates.  Fixed-point prefix sums give
+  // tau at every position.  Returns the number of candidates admitted; mode 1
+  // also writes the plan, so it is decided once.
   uint64_t v[EPT];
-  bool merged = false;
-  if constexpr (EPT <= 4) {
-    if (G2 > 0 && !unsorted) {
-      merge_sort_runs<EPT>(v, keys, P, G2);
-      merged = true;
-    }
-  }
-  if (!merged) radix_sort_hi32<EPT>(v, keys, whist, scan_lds);
-  __syncthreads();                            // keys is reused below
-
-  // fixed-point prefix sums over the sorted order; thread t owns positions
-  // [t*EPT, t*EPT + EPT)
-  int64_t local = 0;
+  auto decide = [&]() -> int {
+    int64_t local = 0;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e)
-    if (v[e] != ~0ull) local += fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(v[e] >> 32)));
-  int64_t tau = ((int64_t)R << 32) + block_exscan_i64(local, red64);  // tau before p0
-  int first_stop = 0x7FFFFFFF, firstsent = 0x7FFFFFFF;
-  // asynchronous form: first maximum of Theta_q over this thread's q = p + 1
-  // (thread 0 also holds q = 0)
-  double pbest = -__builtin_inf();
-  int pq = 0x7FFFFFFF;
-  if (a.mode == 1 && tid == 0) { pbest = theta_here((int64_t)R << 32, 0); pq = 0; }
-  bool stopped = false;
+    for (int e = 0; e < EPT; ++e)
+      if (v[e] != ~0ull) local += fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(v[e] >> 32)));
+    int64_t tau = ((int64_t)R << 32) + block_exscan_i64(local, red64);  // tau before p0
+    int first_stop = 0x7FFFFFFF, firstsent = 0x7FFFFFFF;
+    // asynchronous form: first maximum of Theta_q over this thread's q = p + 1
+    // (thread 0 also holds q = 0)
+    double pbest = -__builtin_inf();
+    int pq = 0x7FFFFFFF;
+    if (a.mode == 1 && tid == 0) { pbest = theta_here((int64_t)R << 32, 0); pq = 0; }
+    bool stopped = false;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int p = p0 + e;
-    if (v[e] == ~0ull) { if (firstsent == 0x7FFFFFFF) firstsent = p; stopped = true; }
-    if (!stopped) {
-      const int64_t tau_next = tau + fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(v[e] >> 32)));
-      const double after = theta_here(tau_next, e + 1);
-      if (a.mode == 0) {
-        const double before = theta_here(tau, e);
-        if (!(after > before)) { first_stop = p; stopped = true; }
-      } else if (after > pbest) {
-        pbest = after;
-        pq = p + 1;
+    for (int e = 0; e < EPT; ++e) {
+      const int p = p0 + e;
+      if (v[e] == ~0ull) { if (firstsent == 0x7FFFFFFF) firstsent = p; stopped = true; }
+      if (!stopped) {
+        const int64_t tau_next = tau + fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(v[e] >> 32)));
+        const double after = theta_here(tau_next, e + 1);
+        if (a.mode == 0) {
+          const double before = theta_here(tau, e);
+          if (!(after > before)) { first_stop = p; stopped = true; }
+        } else if (after > pbest) {
+          pbest = after;
+          pq = p + 1;
+        }
+        tau = tau_next;
       }
-      tau = tau_next;
+    }
+    // number of candidates = position of the first sentinel key
+    int E = block_min_i(firstsent, red32);
+    if (E > P) E = P;
+    int adm;
+    if (a.mode == 0) {
+      adm = block_min_i(first_stop, red32);
+      if (adm > E) adm = E;
+    } else {
+      const int cap = min(*kin_l, a.N_max);
+      adm = max(0, min(cap - R, E));
+      block_argmax_first(pbest, pq, reinterpret_cast<double*>(red64), red32);
+      if (tid == 0) {
+        *a.K_plan = R + pq;
+        if (a.theta_plan) *a.theta_plan = pbest;
+      }
+    }
+    return adm;
+  };
+
+  // Algorithm 1 first tries the selected prefix of the order; the whole sort
+  // (ascending: a descending, then r, then j) runs when that cannot decide,
+  // and always for the asynchronous form, whose plan scans every position.
+  // Up to four keys per thread with ascending padded runs it is the run
+  // merge; otherwise (more keys, or runs out of order) the radix sort, which
+  // keeps equal values of a in the buffer's (r, j) order.
+  // Algorithm 1 over the selected prefix (at most kSelMax positions, in
+  // order in srt): one position per thread, p = tid, so each thread makes a
+  // single Theta comparison instead of scanning EPT positions in sequence.
+  // Same arithmetic as decide(): Theta before and after admitting p.
+  auto decide_prefix = [&](const uint64_t* srt, int n) -> int {
+    const int p = tid;
+    const bool valid = p < n;
+    const uint64_t k = valid ? srt[p] : ~0ull;
+    const int64_t fa = valid ? fixed32(__uint_as_float(0xFFFFFFFFu - (uint32_t)(k >> 32))) : 0;
+    const int B0 = R + p;
+    const double s0 = (valid && B0 <= a.N_max) ? a.sps[B0] : 0.0;
+    const double s1 = (valid && B0 + 1 <= a.N_max) ? a.sps[B0 + 1] : 0.0;
+    const int64_t tau = ((int64_t)R << 32) + block_exscan_i64(fa, red64);   // tau before p
+    int stop = 0x7FFFFFFF;
+    if (valid) {
+      const double before = (B0 > a.N_max) ? 0.0 : ((double)tau * 0x1p-32) * s0;
+      const double after = (B0 + 1 > a.N_max) ? 0.0 : ((double)(tau + fa) * 0x1p-32) * s1;
+      if (!(after > before)) stop = p;
+    }
+    return min(block_min_i(stop, red32), n);
+  };
+
+  int admitted = -1;
+  if (a.mode == 0) {
+    int total = 0;
+    const int n = select_sorted_prefix<EPT>(v, keys, P, whist, ssel, sel, red64, &total);
+    if (n >= 0) {
+      admitted = decide_prefix(reinterpret_cast<const uint64_t*>(whist), n);
+      if (admitted >= n && n < total) admitted = -1;   // no stop inside the prefix
     }
   }
-  // number of candidates = position of the first sentinel key
-  int E = block_min_i(firstsent, red32);
-  if (E > P) E = P;
-  int admitted;
-  if (a.mode == 0) {
-    admitted = block_min_i(first_stop, red32);
-    if (admitted > E) admitted = E;
-  } else {
-    const int cap = min(*kin_l, a.N_max);
-    admitted = max(0, min(cap - R, E));
-    block_argmax_first(pbest, pq, reinterpret_cast<double*>(red64), red32);
-    if (tid == 0) {
-      *a.K_plan = R + pq;
-      if (a.theta_plan) *a.theta_plan = pbest;
+  if (admitted < 0) {
+    bool merged = false;
+    if constexpr (EPT <= 4) {
+      if (G2 > 0 && !unsorted) {
+        merge_sort_runs<EPT>(v, keys, P, G2);
+        merged = true;
+      }
     }
+    if (!merged) radix_sort_hi32<EPT>(v, keys, whist, scan_lds);
+    __syncthreads();
+    admitted = decide();
   }
 
   // ell_r = largest admitted position of request r, by LDS atomics in the
@@ -411,7 +592,11 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(SchedArgs a) {
   __shared__ int64_t red64[kSchedThreads / 64];
   __shared__ int red32[kSchedThreads / 64];
   __shared__ int pk_lds[kPackLds];
-  __shared__ uint32_t whist[kSchedThreads / 64 * 256];   // per-wave digit counts of the sort
+  // per-wave digit counts of the radix sort; the selection's bins, then its
+  // selected and ranked keys
+  __shared__ __align__(16) uint32_t whist[kSchedThreads / 64 * 256];
+  __shared__ uint64_t ssel[kSelMax];                       // the selection's keys
+  __shared__ int sel[8];
   __shared__ int kin_l;
   // K_in is read once, before K_plan (which may be the same address) is written
   if (threadIdx.x == 0) kin_l = (a.mode == 1) ? *a.K_in : 0;
@@ -421,11 +606,11 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(SchedArgs a) {
   while (G2 < a.gamma) G2 *= 2;
   int n = a.R * G2;
   if (n > 4 * kSchedThreads) { G2 = 0; n = a.R * a.gamma; }
-  if (n <= kSchedThreads) schedule_body<1>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds);
-  else if (n <= 2 * kSchedThreads) schedule_body<2>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds);
-  else if (n <= 4 * kSchedThreads) schedule_body<4>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds);
-  else if (n <= 8 * kSchedThreads) schedule_body<8>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds);
-  else schedule_body<16>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds);
+  if (n <= kSchedThreads) schedule_body<1>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds, ssel, sel);
+  else if (n <= 2 * kSchedThreads) schedule_body<2>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds, ssel, sel);
+  else if (n <= 4 * kSchedThreads) schedule_body<4>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds, ssel, sel);
+  else if (n <= 8 * kSchedThreads) schedule_body<8>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds, ssel, sel);
+  else schedule_body<16>(a, G2, keys, red64, red32, &kin_l, whist, pk_lds, ssel, sel);
   // verify-batch pack of x with the lengths ell + 1 just decided (every path
   // of the body leaves ell in LDS at the start of the key buffer)
   if (a.pack) {

@@ -449,6 +449,50 @@ def test_scheduler_stress_size():
         _sched_case(c3, 1.0 / (0.020 + 5e-5 * B))
 
 
+def test_scheduler_prefix_selection_paths():
+    """Algorithm 1 first sorts only the ~512 largest a (selected by histograms of
+    the keys' high bits) and falls back to the whole sort when that cannot decide.
+    Every path against the oracle, bit for bit: the prefix decides (early stop),
+    the second histogram level (a packed into one bucket), ties too many for the
+    prefix (one value of a shared by 1100 requests), no stop inside the prefix
+    (SPS flat, so everything is admitted), and fewer candidates than the prefix."""
+    rng = np.random.default_rng(11)
+
+    def flat(R, g):
+        return np.ones(R * (g + 1) + 1)
+
+    def falling(R, g, k=5e-5):
+        return 1.0 / (0.020 + k * np.arange(R * (g + 1) + 1, dtype=np.float64))
+
+    # the prefix decides: configs 2 and 3 (run merge and radix shapes) with their
+    # synthetic SPS tables
+    for idx in (2, 3):
+        cfg = synth.config(idx)
+        z = rng.normal(0, 3.2, (cfg.R, cfg.gamma))
+        c = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+        _sched_case(c, synth.sps_table(cfg, cfg.R * (cfg.gamma + 1)).numpy())
+    # second level: every a within 1e-3 of 1, so one first-level bucket holds
+    # them all; the steep curve stops near position 270
+    c = (1.0 - rng.uniform(0, 6e-5, (1000, 16))).astype(np.float32)
+    _sched_case(c, falling(1000, 16, 1.0))
+    # ties: a = 1/2 for 1024 requests (the crossing bucket, ranked; the capacity
+    # stops it inside, so the (r, j) order of equal a decides) and for 1100
+    # (more than the prefix takes: the whole sort)
+    for R, g in [(1024, 15), (1100, 14)]:
+        c = np.full((R, g), 0.5, np.float32)
+        _sched_case(c, flat(R, g), N_max=R + 300)
+    # no stop inside the prefix: the flat curve admits every candidate
+    for R, g in [(256, 16), (700, 20)]:
+        c = rng.uniform(0.3, 1.0, (R, g)).astype(np.float32)
+        c[rng.uniform(size=(R, g)) < 0.05] = 0.0
+        _sched_case(c, flat(R, g))
+        _sched_case(c, flat(R, g), N_max=R + 600)        # the capacity stops it past 512
+    # fewer candidates than the prefix holds
+    c = rng.uniform(0, 1, (9, 5)).astype(np.float32)
+    _sched_case(c, flat(9, 5))
+    _sched_case(c, falling(9, 5, 0.01))
+
+
 def _async_case(c, sps, K_in, N_max=None, alias=False):
     import oracle as O
     R, g = c.shape
