@@ -472,7 +472,7 @@ def test_scheduler_prefix_selection_paths():
         c = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
         _sched_case(c, synth.sps_table(cfg, cfg.R * (cfg.gamma + 1)).numpy())
     # second level: every a within 1e-3 of 1, so one first-level bucket holds
-    # them all; the steep curve stops near position 270
+    # them all; the steep curve stops inside the prefix (about 340 of ~670 keys)
     c = (1.0 - rng.uniform(0, 6e-5, (1000, 16))).astype(np.float32)
     _sched_case(c, falling(1000, 16, 1.0))
     # ties: a = 1/2 for 1024 requests (the crossing bucket, ranked; the capacity
